@@ -1,0 +1,144 @@
+"""Seeded synthetic inputs for the RMSNorm workloads.
+
+This module only draws random numbers and stores them in the tensor dtype; it
+contains no RMSNorm arithmetic, so both the HIP path's tests/benchmark and the
+CPU oracle can take their inputs from here without sharing any of the method.
+
+Recipe (one ``numpy.random.default_rng(seed)`` stream per workload):
+  * draw order is x, then residual (fused workloads only), then weight;
+  * ``N(mu, sigma)`` means ``standard_normal(float32) * sigma + mu``
+    (sigma is a standard deviation), ``U(a, b)`` means ``uniform(a, b)``
+    cast to float32;
+  * outlier channels, where a workload has them, are scaled before storing;
+  * bf16 tensors are the float32 draws rounded once, to nearest-even, by
+    torch's CPU conversion.
+
+The shapes are the Llama-style activations the pages discuss: hidden 2048 at
+the Llama-3.2-1B size used by the gollamago project (README, "性能测量", bf16
+rows=4096 x columns=2048), a decode-sized batch, a large-hidden headline shape
+and a fused residual shape with an odd row count.  Synthetic normal rows stand
+in for real activations; no model weights or datasets are involved.
+"""
+from dataclasses import dataclass, field
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+import torch
+
+# Eight fixed columns, one in each of the eight bf16 positions of a 16-byte
+# vector (stride 1021), scaled x100 in the large-hidden workload.
+OUTLIER_COLUMNS: Tuple[int, ...] = (13, 1034, 2055, 3076, 4097, 5118, 6139, 7160)
+
+
+@dataclass(frozen=True)
+class Dist:
+    kind: str  # "normal" (a = mean, b = std) or "uniform" (a = low, b = high)
+    a: float
+    b: float
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str  # "f32" or "bf16"
+    rows: int
+    hidden: int
+    eps: float
+    fused: bool
+    x: Dist
+    weight: Dist
+    residual: Optional[Dist] = None
+    outlier_columns: Tuple[int, ...] = ()
+    outlier_scale: float = 1.0
+    note: str = field(default="", compare=False)
+
+    @property
+    def elem_size(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Each input read once, each output written once, weight once.
+
+        Byte ledger rule: TileLang tutorial ch. 02, section 2.1 (every input
+        stored tensor read once, every output written once, intermediates not
+        counted)."""
+        streams = 4 if self.fused else 2
+        return (streams * self.rows * self.hidden + self.hidden) * self.elem_size
+
+
+N01 = Dist("normal", 0.0, 1.0)
+W_N = Dist("normal", 1.0, 0.1)
+
+WORKLOADS: Dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("fp32_64x2048", "f32", 64, 2048, 1e-5, False, N01, W_N,
+                 note="small fp32 case"),
+        Workload("bf16_prefill_4096x2048", "bf16", 4096, 2048, 1e-5, False, N01, W_N,
+                 note="Llama-1B prefill shape"),
+        Workload("bf16_decode_256x4096", "bf16", 256, 4096, 1e-6, False,
+                 Dist("normal", 0.0, 2.0), Dist("uniform", 0.5, 1.5),
+                 note="decode shape; latency case"),
+        Workload("bf16_16384x8192", "bf16", 16384, 8192, 1e-5, False, N01, W_N,
+                 outlier_columns=OUTLIER_COLUMNS, outlier_scale=100.0,
+                 note="large hidden, 8 outlier channels x100; headline bandwidth case"),
+        Workload("bf16_residual_12289x5120", "bf16", 12289, 5120, 1e-5, True, N01, W_N,
+                 residual=N01, note="fused residual add; odd row count"),
+    ]
+}
+
+HEADLINE = "bf16_16384x8192"
+
+
+def _draw(rng: np.random.Generator, d: Dist, shape) -> np.ndarray:
+    if d.kind == "normal":
+        return rng.standard_normal(shape, dtype=np.float32) * np.float32(d.b) + np.float32(d.a)
+    if d.kind == "uniform":
+        return rng.uniform(d.a, d.b, shape).astype(np.float32)
+    raise ValueError("unknown distribution %r" % d.kind)
+
+
+def _store(a: np.ndarray, dtype: str) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    if dtype == "f32":
+        return t
+    if dtype == "bf16":
+        return t.to(torch.bfloat16)
+    raise ValueError("dtype must be 'f32' or 'bf16'")
+
+
+def make(w: Workload, seed: int = 0, rows: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """CPU tensors ``x``, ``weight`` (and ``residual`` when fused) for ``w``.
+
+    ``rows`` overrides the row count (same per-row distribution); the draws for
+    a smaller ``rows`` are not a prefix of the full-size draws."""
+    r = w.rows if rows is None else rows
+    rng = np.random.default_rng(seed)
+    x = _draw(rng, w.x, (r, w.hidden))
+    if w.outlier_columns:
+        cols = [c for c in w.outlier_columns if c < w.hidden]
+        x[:, cols] *= np.float32(w.outlier_scale)
+    out = {"x": _store(x, w.dtype)}
+    if w.fused:
+        out["residual"] = _store(_draw(rng, w.residual or N01, (r, w.hidden)), w.dtype)
+    out["weight"] = _store(_draw(rng, w.weight, (w.hidden,)), w.dtype)
+    return out
+
+
+def custom(rows: int, hidden: int, dtype: str, fused: bool = False, eps: float = 1e-5,
+           x: Dist = N01, weight: Dist = W_N, residual: Dist = N01) -> Workload:
+    """An ad-hoc workload (ragged widths, odd row counts, ...) with the same recipe."""
+    return Workload("custom_%s_%dx%d%s" % (dtype, rows, hidden, "_res" if fused else ""),
+                    dtype, rows, hidden, eps, fused, x, weight,
+                    residual if fused else None)
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """Raw storage of a CPU tensor as numpy: float32 values or bf16 bit patterns."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.float32:
+        return t.numpy()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    raise TypeError("unsupported dtype %s" % t.dtype)

@@ -1,0 +1,105 @@
+"""CPU reference oracle for RMSNorm -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product (``memory_bound_rmsnorm_amd``)
+never imports it and has no CPU fallback.
+
+The arithmetic lives in ``rmsnorm_oracle.c`` (fp64, one rounding per output);
+this module only moves numpy arrays in and out of it.  Arrays are row-major
+``[rows, hidden]``; float32 data is ``np.float32`` and bfloat16 data is the raw
+16-bit pattern in ``np.uint16``.
+
+Pinning status: every function here is checked in ``tests/test_oracle_pins.py``
+against closed forms, bit-exact special cases and an exact-rational brute force.
+The only unpinned choice is which bf16 neighbour is returned when the exact
+result lies within the fp64 evaluation error (about 1e-12 relative) of a
+rounding midpoint.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+F32 = 0
+BF16 = 1
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        lib = ctypes.CDLL(_build.LIB)
+        vp, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+        lib.oracle_rmsnorm_fwd.argtypes = [vp, vp, vp, i64, i64, f32, i32]
+        lib.oracle_rmsnorm_fwd.restype = i32
+        lib.oracle_rmsnorm_residual_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, i32]
+        lib.oracle_rmsnorm_residual_fwd.restype = i32
+        lib.oracle_round_bf16.argtypes = [ctypes.c_double]
+        lib.oracle_round_bf16.restype = ctypes.c_uint16
+        lib.oracle_round_f32.argtypes = [ctypes.c_double]
+        lib.oracle_round_f32.restype = ctypes.c_float
+        _lib = lib
+    return _lib
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError("oracle arrays must be float32 or uint16 (bf16 bits), got %s" % a.dtype)
+
+
+def _check(a: np.ndarray, name: str) -> np.ndarray:
+    if a.ndim != 2:
+        raise ValueError("%s must be 2-D [rows, hidden]" % name)
+    return np.ascontiguousarray(a)
+
+
+def rmsnorm_fwd(x: np.ndarray, weight: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm of every row of ``x`` (float32 or bf16-bits), same dtype out."""
+    x = _check(x, "x")
+    weight = np.ascontiguousarray(weight).reshape(-1)
+    code = _dtype_code(x)
+    if weight.dtype != x.dtype or weight.shape[0] != x.shape[1]:
+        raise ValueError("weight must be [hidden] with the dtype of x")
+    out = np.empty_like(x)
+    rc = _load().oracle_rmsnorm_fwd(x.ctypes.data, weight.ctypes.data, out.ctypes.data,
+                                    x.shape[0], x.shape[1], float(eps), code)
+    if rc != 0:
+        raise RuntimeError("oracle_rmsnorm_fwd failed")
+    return out
+
+
+def rmsnorm_residual_fwd(x: np.ndarray, residual: np.ndarray, weight: np.ndarray, eps: float):
+    """Returns ``(h, y)``: h = round(x + residual), y = RMSNorm(h)."""
+    x = _check(x, "x")
+    residual = _check(residual, "residual")
+    weight = np.ascontiguousarray(weight).reshape(-1)
+    code = _dtype_code(x)
+    if residual.dtype != x.dtype or residual.shape != x.shape:
+        raise ValueError("residual must match x")
+    if weight.dtype != x.dtype or weight.shape[0] != x.shape[1]:
+        raise ValueError("weight must be [hidden] with the dtype of x")
+    h = np.empty_like(x)
+    y = np.empty_like(x)
+    rc = _load().oracle_rmsnorm_residual_fwd(x.ctypes.data, residual.ctypes.data,
+                                             weight.ctypes.data, h.ctypes.data, y.ctypes.data,
+                                             x.shape[0], x.shape[1], float(eps), code)
+    if rc != 0:
+        raise RuntimeError("oracle_rmsnorm_residual_fwd failed")
+    return h, y
+
+
+def round_bf16(v: float) -> int:
+    """Nearest-even bf16 bit pattern of a Python float (fp64), one rounding."""
+    return int(_load().oracle_round_bf16(float(v)))
+
+
+def round_f32(v: float) -> float:
+    return float(_load().oracle_round_f32(float(v)))

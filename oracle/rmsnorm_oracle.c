@@ -1,0 +1,165 @@
+/*
+ * RMSNorm reference oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite (tests/), __graft_entry__.smoke() and the CPU-baseline
+ * leg of bench.py may load or call this code.  The product path (the HIP
+ * library under memory_bound_rmsnorm_amd/) never links, imports or falls back
+ * to it, and the two share no code, header, table or constant.
+ *
+ * What it computes (plain definition, fp64 throughout, one rounding per
+ * output element):
+ *
+ *   y_j = x_j * rsqrt(mean_j(x_j^2) + eps) * w_j
+ *
+ *   - formula, eps inside the root, mean = sum / hidden:
+ *       xserv "phase 4: transformer core kernels", csrc/normalization/rmsnorm.cu
+ *       (header comment) and docs/04-transformer-kernels.md, "Kernel 设计细节 /
+ *       RMSNorm" (rms = sqrt(sum(x^2)/hidden_size + eps); y = x / rms * gamma);
+ *       the CPU reference `cpu_rmsnorm` in crates/xserv-kernels/tests/ops_test.rs.
+ *   - accumulate and scale at high precision, round once at write-back, never
+ *       before the weight multiply: gollamago README, "RMSNorm 优化（TileLang）".
+ *   - eps arrives as a 32-bit float and gamma has the dtype of x:
+ *       xserv crates/xserv-kernels/src/rmsnorm.rs (the `eps: f32` argument and
+ *       the dtype-equality assertion).
+ *
+ *   Fused variant (residual add, then RMSNorm of the sum): the Add that precedes
+ *   RmsNorm is folded into the same pass to cut data movement -- TileLang
+ *   tutorial ch. 02 "从 PyTorch 到 kernel", section 4.2 (CANN
+ *   aclnnAddRmsNormDynamicQuant).  Reading taken here: h = round(x + residual)
+ *   is written back in the tensor dtype and the *rounded* h is what gets
+ *   normalised, i.e. the result equals an unfused add followed by RMSNorm.
+ *
+ * Readings of points the pages leave open:
+ *   - rounding is IEEE round-to-nearest, ties to even, directly from fp64 to
+ *     the output type (no intermediate fp32 for bf16);
+ *   - sum of squares runs over j = 0..hidden-1 in ascending order in fp64;
+ *   - NaN/Inf inputs propagate as IEEE arithmetic dictates.
+ *
+ * dtype codes (private to this file): 0 = float32, 1 = bfloat16 (stored as the
+ * upper 16 bits of the float32 pattern).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+
+/* Exact widening of one stored element to double. */
+static double load_elem(const void *base, int64_t i, int dtype) {
+    float f;
+    if (dtype == ORACLE_F32) {
+        memcpy(&f, (const char *)base + 4 * i, 4);
+    } else {
+        uint16_t b;
+        uint32_t u;
+        memcpy(&b, (const char *)base + 2 * i, 2);
+        u = (uint32_t)b << 16;
+        memcpy(&f, &u, 4);
+    }
+    return (double)f;
+}
+
+/*
+ * Round a double to bfloat16 (8 significant bits, exponent range of float32),
+ * nearest-even, in a single step.
+ *
+ * For finite non-zero v with |v| in [2^E, 2^(E+1)), the bf16 grid spacing is
+ * 2^(E-7); below the smallest normal (E < -126) the spacing stays 2^-133.
+ * |v| / spacing is computed exactly (division by a power of two), rounded to
+ * an integer with nearbyint() under the default round-to-nearest-even mode,
+ * and scaled back, which again is exact.  A result beyond the largest finite
+ * bf16 value overflows to infinity, as IEEE rounding to nearest does.
+ */
+uint16_t oracle_round_bf16(double v) {
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    double a, spacing, m;
+    int e2;
+    float f;
+    uint32_t u;
+    if (isnan(v)) return (uint16_t)(sign | 0x7FC0u);
+    if (isinf(v)) return (uint16_t)(sign | 0x7F80u);
+    if (v == 0.0) return sign;
+    a = fabs(v);
+    (void)frexp(a, &e2);          /* a = f * 2^e2, f in [0.5, 1) */
+    e2 -= 1;                      /* now a in [2^e2, 2^(e2+1)) */
+    if (e2 < -126) e2 = -126;
+    spacing = ldexp(1.0, e2 - 7);
+    m = nearbyint(a / spacing) * spacing;
+    /* largest finite bf16 is (2 - 2^-7) * 2^127 */
+    if (m > ldexp(255.0, 120)) return (uint16_t)(sign | 0x7F80u);
+    f = (float)m;                 /* exact: m has at most 8 significant bits */
+    memcpy(&u, &f, 4);
+    return (uint16_t)(sign | (uint16_t)((u >> 16) & 0x7FFFu));
+}
+
+/* Round a double to float32, nearest-even (the C conversion under the default
+ * floating-point environment). */
+float oracle_round_f32(double v) { return (float)v; }
+
+static void store_elem(void *base, int64_t i, double v, int dtype) {
+    if (dtype == ORACLE_F32) {
+        float f = oracle_round_f32(v);
+        memcpy((char *)base + 4 * i, &f, 4);
+    } else {
+        uint16_t b = oracle_round_bf16(v);
+        memcpy((char *)base + 2 * i, &b, 2);
+    }
+}
+
+/* Normalise one row already widened to double: v[0..hidden) -> out row. */
+static void normalise_row(const double *v, const void *w, void *out, int64_t out_off,
+                          int64_t hidden, float eps, int dtype) {
+    double s = 0.0, mean, r;
+    int64_t j;
+    for (j = 0; j < hidden; ++j) s += v[j] * v[j];
+    mean = s / (double)hidden;
+    r = 1.0 / sqrt(mean + (double)eps);
+    for (j = 0; j < hidden; ++j)
+        store_elem(out, out_off + j, v[j] * r * load_elem(w, j, dtype), dtype);
+}
+
+/*
+ * out[i, :] = RMSNorm(x[i, :]) for i < rows; row-major, contiguous.
+ * Returns 0 on success, -1 on a bad argument or allocation failure.
+ */
+int oracle_rmsnorm_fwd(const void *x, const void *w, void *out, int64_t rows, int64_t hidden,
+                       float eps, int dtype) {
+    double *v;
+    int64_t i, j;
+    if (rows < 0 || hidden <= 0 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16)) return -1;
+    v = (double *)malloc(sizeof(double) * (size_t)hidden);
+    if (!v) return -1;
+    for (i = 0; i < rows; ++i) {
+        for (j = 0; j < hidden; ++j) v[j] = load_elem(x, i * hidden + j, dtype);
+        normalise_row(v, w, out, i * hidden, hidden, eps, dtype);
+    }
+    free(v);
+    return 0;
+}
+
+/*
+ * h[i, :] = round(x[i, :] + residual[i, :]) and out[i, :] = RMSNorm(h[i, :]).
+ * The sum is formed in fp64, rounded once to the dtype and written to h_out;
+ * the rounded value is what the norm sees.
+ */
+int oracle_rmsnorm_residual_fwd(const void *x, const void *residual, const void *w, void *h_out,
+                                void *out, int64_t rows, int64_t hidden, float eps, int dtype) {
+    double *v;
+    int64_t i, j;
+    if (rows < 0 || hidden <= 0 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16)) return -1;
+    v = (double *)malloc(sizeof(double) * (size_t)hidden);
+    if (!v) return -1;
+    for (i = 0; i < rows; ++i) {
+        for (j = 0; j < hidden; ++j) {
+            int64_t k = i * hidden + j;
+            double sum = load_elem(x, k, dtype) + load_elem(residual, k, dtype);
+            store_elem(h_out, k, sum, dtype);
+            v[j] = load_elem(h_out, k, dtype);
+        }
+        normalise_row(v, w, out, i * hidden, hidden, eps, dtype);
+    }
+    free(v);
+    return 0;
+}

@@ -1,0 +1,126 @@
+"""The oracle pins must catch plausible mistakes.
+
+Each case plants one slip in a private copy of the oracle's C source, builds it
+with gcc into a temporary library, points the oracle module at it and runs the
+pin tests: at least one pin has to fail.  Everything here runs on the CPU; the
+real oracle library is restored afterwards.
+"""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+from oracle import build as oracle_build
+from tests import test_oracle_pins as pins
+
+MUTANTS = [
+    ("eps dropped", "sqrt(mean + (double)eps)", "sqrt(mean)"),
+    ("eps outside the root", "r = 1.0 / sqrt(mean + (double)eps);", "r = 1.0 / sqrt(mean) + (double)eps;"),
+    ("divisor hidden - 1", "mean = s / (double)hidden;", "mean = s / (double)(hidden > 1 ? hidden - 1 : 1);"),
+    ("no square root", "r = 1.0 / sqrt(mean + (double)eps);", "r = 1.0 / (mean + (double)eps);"),
+    ("sum of |x| instead of x^2", "s += v[j] * v[j];", "s += fabs(v[j]);"),
+    ("weight dropped", "v[j] * r * load_elem(w, j, dtype)", "v[j] * r"),
+    ("weight index shifted", "v[j] * r * load_elem(w, j, dtype)", "v[j] * r * load_elem(w, (j + 1) % hidden, dtype)"),
+    ("sign lost", "v[j] * r * load_elem(w, j, dtype)", "fabs(v[j]) * r * load_elem(w, j, dtype)"),
+    ("rows and columns transposed", "load_elem(x, i * hidden + j, dtype)", "load_elem(x, j * rows + i, dtype)"),
+    ("truncating rounding", "nearbyint(a / spacing)", "floor(a / spacing)"),
+    ("ties away from zero", "nearbyint(a / spacing)", "round(a / spacing)"),
+    ("bf16 rounded via float32", "a = fabs(v);", "a = fabs((double)(float)v);"),
+    ("subnormal spacing wrong", "if (e2 < -126) e2 = -126;", ""),
+    ("residual subtracted", "load_elem(x, k, dtype) + load_elem(residual, k, dtype)",
+     "load_elem(x, k, dtype) - load_elem(residual, k, dtype)"),
+    ("unrounded residual sum normalised", "v[j] = load_elem(h_out, k, dtype);", "v[j] = sum;"),
+    ("rounded before the weight multiply",
+     "store_elem(out, out_off + j, v[j] * r * load_elem(w, j, dtype), dtype);",
+     "store_elem(out, out_off + j, (dtype == ORACLE_BF16 ? "
+     "(double)oracle_bf16_back(oracle_round_bf16(v[j] * r)) : (double)(float)(v[j] * r)) "
+     "* load_elem(w, j, dtype), dtype);"),
+]
+
+HELPER = """
+static float oracle_bf16_back(uint16_t b) { uint32_t u = (uint32_t)b << 16; float f; memcpy(&f, &u, 4); return f; }
+"""
+
+PIN_TESTS = [
+    (pins.test_round_bf16_matches_exact_rational_rounding, {}),
+    (pins.test_round_bf16_ties_go_to_even, {}),
+    (pins.test_hand_computed_four_element_example, {}),
+    (pins.test_exact_example_every_dtype_bitwise, {}),
+    (pins.test_constant_row_closed_form, dict(c=1e-3, eps=pins.EPS6, dtype="f32")),
+    (pins.test_constant_row_closed_form, dict(c=3.0, eps=pins.EPS5, dtype="bf16")),
+    (pins.test_single_column_rows, {}),
+    (pins.test_power_of_two_scale_invariance_bitwise, dict(k=3)),
+    (pins.test_row_independence_and_layout, {}),
+    (pins.test_zero_row_and_signs, {}),
+    (pins.test_rms_identity, {}),
+    (pins.test_brute_force_tiny_rows, dict(dtype="bf16")),
+    (pins.test_brute_force_tiny_rows, dict(dtype="f32")),
+    (pins.test_residual_sum_rounded_once, dict(dtype="bf16")),
+    (pins.test_residual_normalises_the_rounded_sum, {}),
+    (pins.test_residual_special_cases_reduce_to_plain, {}),
+]
+
+
+def _build_mutant(src: str, tmpdir: str) -> str:
+    path = os.path.join(tmpdir, "mutant.c")
+    with open(path, "w") as f:
+        f.write(src)
+    lib = os.path.join(tmpdir, "libmutant.so")
+    subprocess.run(["gcc", "-std=c99", "-O2", "-fPIC", "-shared", "-ffp-contract=off",
+                    "-o", lib, path, "-lm"], check=True, capture_output=True)
+    return lib
+
+
+def _load_mutant(lib_path):
+    import ctypes
+    saved = oracle._lib
+    oracle._lib = None
+    real = oracle_build.LIB
+    oracle_build.LIB = lib_path
+    try:
+        lib = oracle._load()
+    finally:
+        oracle_build.LIB = real
+        oracle._lib = saved
+    assert isinstance(lib, ctypes.CDLL)
+    return lib
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(name, old, new):
+    with open(oracle_build.SRC) as f:
+        src = f.read()
+    assert old in src, "mutation anchor not found: %r" % old
+    mutated = src.replace(old, new, 1)
+    mutated = mutated.replace("#define ORACLE_BF16 1", "#define ORACLE_BF16 1\n" + HELPER, 1)
+    with tempfile.TemporaryDirectory() as d:
+        lib = _load_mutant(_build_mutant(mutated, d))
+        saved = oracle._lib
+        oracle._lib = lib
+        failed = []
+        try:
+            for fn, kw in PIN_TESTS:
+                try:
+                    fn(**kw)
+                except (AssertionError, RuntimeError, ValueError, OverflowError, ZeroDivisionError):
+                    failed.append(fn.__name__)
+        finally:
+            oracle._lib = saved
+    assert failed, "no pin caught the mutant %r" % name
+
+
+def test_unmodified_copy_passes_every_pin():
+    """Control for the harness: a rebuilt, unmodified copy fails no pin."""
+    with open(oracle_build.SRC) as f:
+        src = f.read()
+    with tempfile.TemporaryDirectory() as d:
+        lib = _load_mutant(_build_mutant(src, d))
+        saved = oracle._lib
+        oracle._lib = lib
+        try:
+            for fn, kw in PIN_TESTS:
+                fn(**kw)
+        finally:
+            oracle._lib = saved
