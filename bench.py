@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Throughput of the RMSNorm hot path on one MI355X.
+
+A step is one rmsnorm_fwd call (or rmsnorm_residual_fwd for the fused
+workload) over a whole [rows, hidden] batch: load rows, sum squares, inverse
+root, scale and store.  Default workload: bf16 [16384, 8192], the
+large-hidden configuration the headline bandwidth figure is quoted on.
+
+Byte accounting follows the TileLang tutorial ch. 02, section 2.1: every input
+read once, every output written once, the weight once; the figure reported is
+algorithmic bytes / time, and its roofline is HBM bandwidth (MI355X: 8 TB/s).
+
+Timing protocol: inputs are resident in HBM before the timed region; several
+copies of the input/output set are rotated so that the footprint of a pass
+(>= 2 GiB) exceeds the 256 MB last-level cache and every step reads from HBM;
+W untimed warm-up steps; then exactly K steps between a device synchronise and
+HIP events on the launch stream.  Parity of this launch configuration at this
+size with the CPU oracle is the job of the GPU test suite, not of this script.
+
+Prints ONE JSON line on stdout.  With --all, one JSON record per workload is
+also written to stderr (lines starting with '#').
+"""
+import argparse
+import concurrent.futures
+import json
+import os
+import platform
+import sys
+import time
+
+import torch
+
+import memory_bound_rmsnorm_amd as mbr
+from memory_bound_rmsnorm_amd import _build, inputs
+
+HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
+MIN_FOOTPRINT = 2 << 30
+PROFILE_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=inputs.HEADLINE, choices=sorted(inputs.WORKLOADS))
+    ap.add_argument("--all", action="store_true", help="also time every other workload (stderr)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline budget; 0 disables it")
+    ap.add_argument("--no-copy", action="store_true", help="skip the copy-ceiling measurement")
+    ap.add_argument("--seed", type=int, default=0)
+    return ap.parse_args()
+
+
+def host_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+class Sets:
+    """Rotating device copies of one workload's inputs and outputs."""
+
+    def __init__(self, w, t, n_sets):
+        dev = {k: v.cuda() for k, v in t.items()}
+        self.weight = dev["weight"]
+        self.sets = []
+        for i in range(n_sets):
+            s = {"x": dev["x"] if i == 0 else dev["x"].clone()}
+            if w.fused:
+                s["residual"] = dev["residual"] if i == 0 else dev["residual"].clone()
+                s["h"] = torch.empty_like(s["x"])
+            s["out"] = torch.empty_like(s["x"])
+            self.sets.append(s)
+        self.fused = w.fused
+        self.eps = w.eps
+
+    def launch(self, i):
+        s = self.sets[i % len(self.sets)]
+        if self.fused:
+            mbr.rmsnorm_residual_fwd(s["x"], s["residual"], self.weight, s["h"], s["out"], self.eps)
+        else:
+            mbr.rmsnorm_fwd(s["x"], self.weight, s["out"], self.eps)
+
+
+def n_sets_for(w) -> int:
+    per_set = (4 if w.fused else 2) * w.rows * w.hidden * w.elem_size
+    return max(2, -(-MIN_FOOTPRINT // per_set))
+
+
+def time_steps(fn, steps, warmup):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        fn(warmup + i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, start.elapsed_time(end) / 1e3
+
+
+def copy_ceiling(w, steps, warmup):
+    """hbm_copy of the same read/write byte count as one step, rotated the same way."""
+    nbytes = w.rows * w.hidden * w.elem_size * (2 if w.fused else 1)
+    n = max(2, -(-MIN_FOOTPRINT // (2 * nbytes)))
+    src = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(i % 251) for i in range(n)]
+    dst = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(n)]
+    wall, ev = time_steps(lambda i: mbr.hbm_copy(src[i % n], dst[i % n]), steps, warmup)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ev / steps) / 1e9
+
+
+def load_traffic(w):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources; else None."""
+    path = os.path.join(PROFILE_DIR, "pmc_traffic_%s.txt" % w.name)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if ":" in line:
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    try:
+        if vals.get("source_sha256") != _build.source_digest():
+            return None
+        fetch = float(vals["rmsnorm_fetch_kib_per_dispatch"]) * 1024 * float(vals["copy_fetch_scale"])
+        write = float(vals["rmsnorm_write_kib_per_dispatch"]) * 1024 * float(vals["copy_write_scale"])
+        return fetch + write
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, t, seconds):
+    """The oracle, as it stands, over a bounded sample of the workload's rows,
+    rows split across the host's threads; GB/s with the same byte ledger."""
+    import oracle  # the CPU checker; timed here as a reported baseline only
+    T = host_threads()
+    rows = min(w.rows, 512 if w.hidden >= 4096 else 2048)
+    xb = inputs.bits(t["x"])[:rows]
+    wb = inputs.bits(t["weight"])
+    rb = inputs.bits(t["residual"])[:rows] if w.fused else None
+    per_thread = [(i * rows // T, (i + 1) * rows // T) for i in range(T)]
+
+    def one_pass():
+        with concurrent.futures.ThreadPoolExecutor(T) as ex:
+            def job(r):
+                if r[0] == r[1]:
+                    return
+                if w.fused:
+                    oracle.rmsnorm_residual_fwd(xb[r[0]:r[1]], rb[r[0]:r[1]], wb, w.eps)
+                else:
+                    oracle.rmsnorm_fwd(xb[r[0]:r[1]], wb, w.eps)
+            list(ex.map(job, per_thread))
+
+    one_pass()  # warm-up
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        one_pass()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    sample_bytes = ((4 if w.fused else 2) * rows * w.hidden + w.hidden) * w.elem_size
+    return {"value": round(sample_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": T, "kind": "oracle",
+            "sample": "first %d of %d rows, %d passes in %.1f s on %d threads (%s)"
+                      % (rows, w.rows, reps, el, T, cpu_model())}
+
+
+def bench_workload(w, steps, warmup, seed, with_copy=True):
+    t = inputs.make(w, seed=seed)
+    n_sets = n_sets_for(w)
+    sets = Sets(w, t, n_sets)
+    wall, ev = time_steps(sets.launch, steps, warmup)
+    nbytes = w.algorithmic_bytes
+    kern_s = ev / steps
+    cfg = mbr.rmsnorm_select_config(w.rows, w.hidden, torch.float32 if w.dtype == "f32" else torch.bfloat16,
+                                    True, w.fused)
+    rec = {
+        "workload": w.name, "rows": w.rows, "hidden": w.hidden, "dtype": w.dtype, "fused": w.fused,
+        "eps": w.eps, "algorithmic_bytes": nbytes, "rotation_sets": n_sets,
+        "wall_s": wall, "event_s": ev, "us_per_call": kern_s * 1e6,
+        "gbps_wall": nbytes * steps / wall / 1e9, "gbps_kernel": nbytes / kern_s / 1e9,
+        "kernel_config": cfg.as_dict(),
+    }
+    if with_copy:
+        cc = copy_ceiling(w, max(20, steps // 2), max(2, warmup // 2))
+        rec["copy_ceiling_gbps"] = cc
+        rec["frac_of_copy_ceiling"] = rec["gbps_kernel"] / cc
+    return t, rec
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this RMSNorm path shards by rows with no communication, and "
+              "runs on more than one GPU are not part of this build (asked for --gpus %d, WORLD_SIZE %d)"
+              % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (HIP device); none is visible", file=sys.stderr)
+        sys.exit(1)
+    mbr.lib()  # fail loudly if the HIP library is not built
+    w = inputs.WORKLOADS[args.workload]
+    log("# device:", torch.cuda.get_device_name(0), "| workload:", w.name, "| steps", args.steps, "warmup", args.warmup)
+    t, rec = bench_workload(w, args.steps, args.warmup, args.seed, not args.no_copy)
+    log("# timed:", json.dumps(rec))
+
+    achieved = rec["gbps_kernel"]
+    line = {
+        "metric": "bf16 RMSNorm achieved HBM GB/s and % of peak at 16384×8192",
+        "value": round(rec["gbps_wall"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": rec["wall_s"] / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded; x ~ N(0,1) with 8 outlier channels x100, weight ~ N(1, 0.1))"
+                if w.name == inputs.HEADLINE else "synthetic (seeded)",
+        "config": {"workload": "RMSNorm %s [%d, %d]%s, eps %g" % (w.dtype, w.rows, w.hidden,
+                                                                  " fused residual" if w.fused else "", w.eps),
+                   "rows": w.rows, "hidden": w.hidden, "fused": w.fused,
+                   "algorithmic_bytes_per_step": w.algorithmic_bytes, "rotation_sets": rec["rotation_sets"],
+                   "launch": rec["kernel_config"]},
+        "pct_of_peak": round(100 * rec["gbps_wall"] / HBM_PEAK_GBPS, 2),
+        "us_per_call": round(rec["us_per_call"], 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic(w)},
+        "parity": "checked against the CPU oracle at this size and launch configuration by "
+                  "tests/test_parity_gpu.py::test_stated_workloads_full_size",
+    }
+    if "copy_ceiling_gbps" in rec:
+        line["copy_ceiling_gbps"] = round(rec["copy_ceiling_gbps"], 2)
+        line["frac_of_copy_ceiling"] = round(rec["frac_of_copy_ceiling"], 4)
+    if args.all:
+        for name, other in inputs.WORKLOADS.items():
+            if name == w.name:
+                continue
+            _, r = bench_workload(other, args.steps, args.warmup, args.seed)
+            log("# workload:", json.dumps(r))
+    if args.cpu_seconds > 0:
+        line["cpu_baseline"] = cpu_baseline(w, t, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,171 @@
+/*
+ * rmsnorm.h -- C ABI of librmsnorm.so, row-wise RMSNorm for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Operation (per row of a row-major [rows, hidden] tensor):
+ *
+ *     y_j = x_j * rsqrt(sum_k x_k^2 / hidden + eps) * weight_j
+ *
+ * eps sits inside the root and the mean divides by hidden (xserv "phase 4:
+ * transformer core kernels", csrc/normalization/rmsnorm.cu header comment and
+ * docs/04-transformer-kernels.md, "Kernel 设计细节 / RMSNorm").  The sum of
+ * squares, the inverse root and both products are evaluated in fp32 and each
+ * output is rounded to the tensor dtype exactly once, nearest-even, after the
+ * weight multiply (gollamago README, "RMSNorm 优化（TileLang）": one global
+ * read and one global write per row, fp32 accumulation and scaling, rounding
+ * only at write-back).
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are DEVICE pointers (HIP device memory, e.g. torch CUDA-tensor
+ *     storage).  The caller owns every buffer; the library allocates nothing,
+ *     needs no workspace and keeps no per-call state.
+ *   - Tensors are contiguous and row-major; weight is [hidden]; all tensors
+ *     share one dtype.  Any element-aligned address is accepted; 16-byte
+ *     vector accesses are used only when every pointer is 16-byte aligned and
+ *     hidden * dtype_size is a multiple of 16.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
+ *     work and return without synchronising; results are ready when the stream
+ *     reaches that point.
+ *   - Every INVALID_ARG / UNSUPPORTED_DTYPE return happens before any HIP call,
+ *     so nothing is enqueued on error.  rows == 0 returns RMSNORM_OK without
+ *     touching the GPU.
+ *   - An output may alias an input exactly (out == x, residual_out ==
+ *     residual, residual_out == x, ...): every element is read before it is
+ *     overwritten, and only by the thread that writes it.  Any other overlap
+ *     of an output with another buffer -- a partial overlap, weight, or the
+ *     other output -- is rejected with INVALID_ARG.
+ *   - For equal inputs, shapes and configuration the results are bitwise
+ *     reproducible (fixed reduction order, no atomics).
+ *
+ * Status codes and the export convention follow the Intro-ops operator
+ * runtime's public C header (include/operator_runtime/api.h: SUCCESS,
+ * INVALID_ARG, UNSUPPORTED_DTYPE, RUNTIME; default visibility + extern "C").
+ */
+#ifndef MBR_RMSNORM_H
+#define MBR_RMSNORM_H
+
+#include <stdint.h>
+
+#define RMSNORM_API __attribute__((visibility("default")))
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RMSNORM_OK = 0,
+    RMSNORM_ERR_INVALID_ARG = 1,       /* null pointer, bad size, bad eps, bad overlap, bad config */
+    RMSNORM_ERR_UNSUPPORTED_DTYPE = 2, /* dtype not one of rmsnorm_dtype_t */
+    RMSNORM_ERR_RUNTIME = 3            /* the HIP launch reported an error */
+} rmsnorm_status_t;
+
+typedef enum {
+    RMSNORM_DTYPE_F32 = 0, /* IEEE binary32 */
+    RMSNORM_DTYPE_BF16 = 1 /* bfloat16: upper 16 bits of a binary32 */
+} rmsnorm_dtype_t;
+
+/*
+ * rmsnorm_fwd: out[i, :] = RMSNorm(x[i, :]) * weight for 0 <= i < rows.
+ *
+ *   x       [rows, hidden] input, read once.
+ *   weight  [hidden] scale (gamma), same dtype as x.
+ *   out     [rows, hidden] output; may be x itself (in place).
+ *   rows    >= 0 (0: no-op).
+ *   hidden  >= 1, <= 2^31 - 1, and rows * hidden * dtype_size must fit in int64.
+ *   eps     finite and >= 0 (passed as a 32-bit float, as the xserv FFI
+ *           wrapper crates/xserv-kernels/src/rmsnorm.rs does).
+ *   dtype   RMSNORM_DTYPE_F32 or RMSNORM_DTYPE_BF16.
+ *   stream  hipStream_t or NULL.
+ * Returns RMSNORM_OK once the kernel is enqueued.
+ */
+RMSNORM_API rmsnorm_status_t rmsnorm_fwd(const void* x, const void* weight, void* out,
+                                         int64_t rows, int64_t hidden, float eps,
+                                         rmsnorm_dtype_t dtype, void* stream);
+
+/*
+ * rmsnorm_residual_fwd: fused residual add + RMSNorm, one pass over the rows.
+ *
+ *   residual_out[i, :] = round(x[i, :] + residual[i, :])      (h, stored)
+ *   out[i, :]          = RMSNorm(residual_out[i, :]) * weight  (norm of the ROUNDED h)
+ *
+ * Folding the Add that precedes RmsNorm into the same kernel to cut data
+ * movement follows the fusion example in the TileLang tutorial ch. 02
+ * "从 PyTorch 到 kernel", section 4.2 (CANN aclnnAddRmsNormDynamicQuant).
+ * The sum is formed in fp32 and rounded once (exact for bf16 operands), so h
+ * equals the unfused x + residual bit for bit and out equals rmsnorm_fwd(h).
+ *
+ *   x, residual   [rows, hidden] inputs, each read once.
+ *   weight        [hidden].
+ *   residual_out  [rows, hidden] h; may be x or residual itself.
+ *   out           [rows, hidden] normalised h; may be x or residual, never
+ *                 residual_out.
+ * Other arguments and errors as rmsnorm_fwd.
+ */
+RMSNORM_API rmsnorm_status_t rmsnorm_residual_fwd(const void* x, const void* residual,
+                                                  const void* weight, void* residual_out,
+                                                  void* out, int64_t rows, int64_t hidden,
+                                                  float eps, rmsnorm_dtype_t dtype,
+                                                  void* stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+RMSNORM_API const char* rmsnorm_status_string(rmsnorm_status_t status);
+
+/* ------------------------------------------------------------------------
+ * Launch configurations.  rmsnorm_fwd / rmsnorm_residual_fwd pick one from
+ * (rows, hidden, dtype, alignment) by a fixed rule; the calls below expose
+ * that choice and let a caller (tests, tuning sweeps) force another one.
+ * Every configuration computes the same function; different configurations
+ * may differ in the last bit through the fp32 reduction order.
+ * ---------------------------------------------------------------------- */
+
+typedef enum {
+    RMSNORM_PATH_AUTO = 0,     /* let the library choose (the other fields are ignored) */
+    RMSNORM_PATH_VECTOR = 1,   /* row in VGPRs, 16-byte loads/stores; needs 16-byte alignment */
+    RMSNORM_PATH_ELEMENT = 2,  /* row in VGPRs, one element per access; any alignment */
+    RMSNORM_PATH_TWO_PASS = 3  /* row too large for registers: second read of x (and residual) */
+} rmsnorm_path_t;
+
+typedef struct {
+    int32_t path;           /* rmsnorm_path_t */
+    int32_t waves_per_row;  /* 64-lane waves cooperating on one row: 1, 2, 4, 8 or 16 */
+    int32_t items_per_lane; /* VECTOR: 16-byte vectors per lane, one of 1-8, 10, 12, 14, 16;
+                               ELEMENT: elements per lane, one of 1, 2, 4, 8, 16;
+                               TWO_PASS: ignored (0) */
+    int32_t rows_per_block; /* rows per workgroup; 64 * waves_per_row * rows_per_block <= 512
+                               (1024 when waves_per_row == 16); TWO_PASS: must be 1 */
+    int32_t max_blocks;     /* >= 0; 0: one workgroup per group of rows_per_block rows;
+                               n > 0: at most n workgroups, each looping over row groups */
+} rmsnorm_config_t;
+
+/*
+ * Fill *cfg with the configuration rmsnorm_fwd / rmsnorm_residual_fwd would use
+ * for this shape.  vector_aligned != 0 states that every pointer will be
+ * 16-byte aligned.  INVALID_ARG for cfg == NULL or bad sizes; no HIP call.
+ */
+RMSNORM_API rmsnorm_status_t rmsnorm_select_config(int64_t rows, int64_t hidden,
+                                                   rmsnorm_dtype_t dtype,
+                                                   int32_t vector_aligned, int32_t fused,
+                                                   rmsnorm_config_t* cfg);
+
+/*
+ * As rmsnorm_fwd / rmsnorm_residual_fwd with an explicit configuration
+ * (cfg == NULL or cfg->path == RMSNORM_PATH_AUTO: automatic choice).
+ * INVALID_ARG if the configuration is not built, cannot cover hidden, or
+ * needs an alignment the pointers do not have.
+ */
+RMSNORM_API rmsnorm_status_t rmsnorm_fwd_ex(const void* x, const void* weight, void* out,
+                                            int64_t rows, int64_t hidden, float eps,
+                                            rmsnorm_dtype_t dtype, const rmsnorm_config_t* cfg,
+                                            void* stream);
+
+RMSNORM_API rmsnorm_status_t rmsnorm_residual_fwd_ex(const void* x, const void* residual,
+                                                     const void* weight, void* residual_out,
+                                                     void* out, int64_t rows, int64_t hidden,
+                                                     float eps, rmsnorm_dtype_t dtype,
+                                                     const rmsnorm_config_t* cfg, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MBR_RMSNORM_H */

@@ -1,0 +1,209 @@
+"""Python binding of librmsnorm.so, the gfx950 RMSNorm library.
+
+Argument marshalling only: every function takes torch CUDA (HIP) tensors,
+passes their device pointers, sizes, dtype code and the current HIP stream to
+the C ABI declared in include/rmsnorm.h, and turns a non-OK status into an
+exception.  All arithmetic runs in the HIP kernels; there is no CPU path and no
+fallback -- if the library is not built, every call raises.
+
+    rmsnorm_fwd(x, weight, out, eps)                          -> out
+    rmsnorm_residual_fwd(x, residual, weight, residual_out, out, eps) -> (residual_out, out)
+    rmsnorm_fwd_ex / rmsnorm_residual_fwd_ex(..., config)      forced launch configuration
+    rmsnorm_select_config(rows, hidden, dtype, vector_aligned, fused) -> Config
+    rmsnorm_status_string(status)                              -> str
+"""
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librmsnorm.so")
+COPY_LIB_PATH = os.path.join(_HERE, "libhbm_copy.so")
+
+RMSNORM_OK = 0
+RMSNORM_ERR_INVALID_ARG = 1
+RMSNORM_ERR_UNSUPPORTED_DTYPE = 2
+RMSNORM_ERR_RUNTIME = 3
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+
+PATH_AUTO = 0
+PATH_VECTOR = 1
+PATH_ELEMENT = 2
+PATH_TWO_PASS = 3
+PATH_NAMES = {PATH_AUTO: "auto", PATH_VECTOR: "vector", PATH_ELEMENT: "element", PATH_TWO_PASS: "two_pass"}
+
+
+class Config(ctypes.Structure):
+    """rmsnorm_config_t."""
+    _fields_ = [("path", ctypes.c_int32), ("waves_per_row", ctypes.c_int32),
+                ("items_per_lane", ctypes.c_int32), ("rows_per_block", ctypes.c_int32),
+                ("max_blocks", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {"path": PATH_NAMES.get(self.path, self.path), "waves_per_row": self.waves_per_row,
+                "items_per_lane": self.items_per_lane, "rows_per_block": self.rows_per_block,
+                "max_blocks": self.max_blocks}
+
+    def __repr__(self):
+        return "Config(%s)" % ", ".join("%s=%s" % kv for kv in self.as_dict().items())
+
+
+class RmsnormError(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        self.status = status
+        super().__init__("%s: %s" % (fn, rmsnorm_status_string(status)))
+
+
+_lib = None
+_copy_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded librmsnorm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("librmsnorm.so is not built (%s); run `python -m memory_bound_rmsnorm_amd._build` "
+                              "or __graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int32
+        cfgp = ctypes.POINTER(Config)
+        L.rmsnorm_fwd.argtypes = [vp, vp, vp, i64, i64, f32, i32, vp]
+        L.rmsnorm_residual_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, i32, vp]
+        L.rmsnorm_fwd_ex.argtypes = [vp, vp, vp, i64, i64, f32, i32, cfgp, vp]
+        L.rmsnorm_residual_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, i32, cfgp, vp]
+        L.rmsnorm_select_config.argtypes = [i64, i64, i32, i32, i32, cfgp]
+        L.rmsnorm_status_string.argtypes = [i32]
+        L.rmsnorm_status_string.restype = ctypes.c_char_p
+        for fn in (L.rmsnorm_fwd, L.rmsnorm_residual_fwd, L.rmsnorm_fwd_ex, L.rmsnorm_residual_fwd_ex,
+                   L.rmsnorm_select_config):
+            fn.restype = i32
+        _lib = L
+    return _lib
+
+
+def copy_lib() -> ctypes.CDLL:
+    """The loaded libhbm_copy.so (bandwidth ceiling and counter calibration)."""
+    global _copy_lib
+    if _copy_lib is None:
+        if not os.path.exists(COPY_LIB_PATH):
+            raise ImportError("libhbm_copy.so is not built (%s)" % COPY_LIB_PATH)
+        L = ctypes.CDLL(COPY_LIB_PATH)
+        L.hbm_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
+        L.hbm_copy.restype = ctypes.c_int
+        _copy_lib = L
+    return _copy_lib
+
+
+def rmsnorm_status_string(status: int) -> str:
+    return lib().rmsnorm_status_string(int(status)).decode()
+
+
+def dtype_code(dtype: torch.dtype) -> int:
+    if dtype == torch.float32:
+        return DTYPE_F32
+    if dtype == torch.bfloat16:
+        return DTYPE_BF16
+    raise TypeError("RMSNorm supports torch.float32 and torch.bfloat16, not %s" % dtype)
+
+
+def _device_tensor(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor; this library has no CPU path" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous (row-major)" % name)
+    return t
+
+
+def _stream(stream, device) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _shape(x: torch.Tensor, weight: torch.Tensor):
+    if x.dim() < 1:
+        raise ValueError("x must have at least one dimension")
+    hidden = x.shape[-1]
+    if weight.dim() != 1 or weight.shape[0] != hidden:
+        raise ValueError("weight must have shape [hidden] = [%d]" % hidden)
+    rows = x.numel() // hidden if hidden else 0
+    return rows, hidden
+
+
+def _check(status: int, fn: str):
+    if status != RMSNORM_OK:
+        raise RmsnormError(status, fn)
+
+
+def rmsnorm_fwd_ex(x, weight, out, eps: float = 1e-5, config: Optional[Config] = None, stream=None):
+    """out = RMSNorm(x) * weight over the last dimension, with a forced configuration."""
+    for t, n in ((x, "x"), (weight, "weight"), (out, "out")):
+        _device_tensor(t, n)
+    if out.shape != x.shape or out.dtype != x.dtype or weight.dtype != x.dtype:
+        raise ValueError("out must match x in shape and dtype; weight must match x in dtype")
+    rows, hidden = _shape(x, weight)
+    st = lib().rmsnorm_fwd_ex(x.data_ptr(), weight.data_ptr(), out.data_ptr(), rows, hidden, float(eps),
+                              dtype_code(x.dtype), ctypes.byref(config) if config is not None else None,
+                              _stream(stream, x.device))
+    _check(st, "rmsnorm_fwd")
+    return out
+
+
+def rmsnorm_fwd(x, weight, out, eps: float = 1e-5, stream=None):
+    """out = RMSNorm(x) * weight over the last dimension (C: rmsnorm_fwd)."""
+    return rmsnorm_fwd_ex(x, weight, out, eps, None, stream)
+
+
+def rmsnorm_residual_fwd_ex(x, residual, weight, residual_out, out, eps: float = 1e-5,
+                            config: Optional[Config] = None, stream=None):
+    for t, n in ((x, "x"), (residual, "residual"), (weight, "weight"), (residual_out, "residual_out"),
+                 (out, "out")):
+        _device_tensor(t, n)
+    for t in (residual, residual_out, out):
+        if t.shape != x.shape or t.dtype != x.dtype:
+            raise ValueError("residual, residual_out and out must match x in shape and dtype")
+    if weight.dtype != x.dtype:
+        raise ValueError("weight must match x in dtype")
+    rows, hidden = _shape(x, weight)
+    st = lib().rmsnorm_residual_fwd_ex(x.data_ptr(), residual.data_ptr(), weight.data_ptr(),
+                                       residual_out.data_ptr(), out.data_ptr(), rows, hidden, float(eps),
+                                       dtype_code(x.dtype), ctypes.byref(config) if config is not None else None,
+                                       _stream(stream, x.device))
+    _check(st, "rmsnorm_residual_fwd")
+    return residual_out, out
+
+
+def rmsnorm_residual_fwd(x, residual, weight, residual_out, out, eps: float = 1e-5, stream=None):
+    """residual_out = x + residual (rounded once); out = RMSNorm(residual_out) * weight
+    (C: rmsnorm_residual_fwd)."""
+    return rmsnorm_residual_fwd_ex(x, residual, weight, residual_out, out, eps, None, stream)
+
+
+def rmsnorm_select_config(rows: int, hidden: int, dtype, vector_aligned: bool = True,
+                          fused: bool = False) -> Config:
+    """The configuration the automatic choice uses for this shape."""
+    code = dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype)
+    cfg = Config()
+    _check(lib().rmsnorm_select_config(int(rows), int(hidden), code, int(bool(vector_aligned)),
+                                       int(bool(fused)), ctypes.byref(cfg)), "rmsnorm_select_config")
+    return cfg
+
+
+def hbm_copy(src: torch.Tensor, dst: torch.Tensor, max_blocks: int = 0, stream=None):
+    """Plain 16-byte-vector copy of src's bytes into dst (bandwidth ceiling)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst too small")
+    rc = copy_lib().hbm_copy(src.data_ptr(), dst.data_ptr(), nbytes, int(max_blocks), _stream(stream, src.device))
+    if rc != 0:
+        raise RuntimeError("hbm_copy failed with code %d" % rc)
+    return dst

@@ -1,0 +1,37 @@
+// Kernel tables shared by the instantiation units and the C-ABI layer.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mbr {
+
+// Built configurations.  Vector path: waves per row x 16-byte vectors per lane
+// (1-8 plus the multiples that make common hidden sizes exact: 640 vectors =
+// 64 x 10 for bf16 5120, 896 = 64 x 14 for 7168, 768 = 64 x 12 for 6144).
+constexpr int kWprList[] = {1, 2, 4, 8, 16};
+constexpr int kVplList[] = {1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16};
+constexpr int kEplList[] = {1, 2, 4, 8, 16};
+constexpr int kNumWpr = sizeof(kWprList) / sizeof(int);
+constexpr int kNumVpl = sizeof(kVplList) / sizeof(int);
+constexpr int kNumEpl = sizeof(kEplList) / sizeof(int);
+
+constexpr int max_threads_for(int wpr) { return wpr == 16 ? 1024 : 512; }
+
+// A 1024-lane workgroup leaves each lane 128 VGPRs; the configurations below
+// are the ones whose row fits that budget without scratch spills (the others
+// are not built).  Narrower workgroups have 256 VGPRs per lane and fit all.
+constexpr bool vec_built(int wpr, int vpl, bool fused) { return wpr < 16 || vpl <= (fused ? 6 : 10); }
+constexpr bool elem_built(int wpr, int epl) { return wpr < 16 || epl <= 8; }
+
+// Host-side kernel handles (addresses of the __global__ stubs), or nullptr.
+// dtype: 0 = f32, 1 = bf16.
+const void* vec_kernel(int dtype, bool fused, bool masked, int wpr_index, int vpl_index);
+const void* elem_kernel(int dtype, bool fused, int wpr_index, int epl_index);
+const void* twopass_kernel(int dtype, bool fused, bool vec);
+
+// Per-unit getters defined in the instantiation files.
+const void* vec_kernel_bf16(bool fused, bool masked, int wi, int vi);
+const void* vec_kernel_f32(bool fused, bool masked, int wi, int vi);
+
+}  // namespace mbr

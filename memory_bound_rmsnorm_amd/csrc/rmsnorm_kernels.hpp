@@ -1,0 +1,372 @@
+// Row-wise RMSNorm kernels for gfx950 (CDNA4, wave64).
+//
+//   y_j = x_j * rsqrt(sum_k x_k^2 / hidden + eps) * w_j
+//
+// (xserv "phase 4: transformer core kernels", csrc/normalization/rmsnorm.cu
+// and docs/04-transformer-kernels.md "RMSNorm"), fp32 accumulation and scaling
+// with a single rounding at write-back and exactly one global read and one
+// global write of every row (gollamago README, "RMSNorm 优化（TileLang）").
+//
+// Three kernel families, all one row per group of 64*WPR lanes:
+//   rms_vec_kernel      the row lives in VGPRs as packed 16-byte vectors
+//                       (bf16x8 / f32x4); coalesced 16-byte loads and stores.
+//   rms_elem_kernel     the row lives in VGPRs as fp32 scalars, one element per
+//                       access: any hidden, any element alignment.
+//   rms_twopass_kernel  rows larger than the register budget of a 1024-lane
+//                       workgroup: pass 1 sums squares, pass 2 re-reads x.
+//
+// The sum of squares is reduced lane -> wave (DPP within 16-lane rows, then
+// the gfx950 permlane16/permlane32 swaps) -> workgroup (one LDS slot per wave,
+// one barrier, every wave adds the slots in the same fixed order).  Every lane
+// ends with bit-identical totals, so the inverse root needs no broadcast and
+// results are reproducible run to run.  There is no contraction anywhere, so
+// no MFMA: the kernels are bound by HBM bandwidth.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mbr {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Everything a launch needs; passed by value as the kernel argument.
+struct RowArgs {
+    const void* x;
+    const void* res;  // fused only
+    const void* w;
+    void* h;          // fused only: residual_out
+    void* out;
+    int64_t rows;
+    int64_t n_groups;    // ceil(rows / rows_per_block)
+    int32_t units;       // per row: 16-byte vectors (vector path) or elements
+    int32_t rows_per_block;
+    float hidden_f;      // hidden as fp32, the mean's divisor
+    float eps;
+};
+
+// ---------------------------------------------------------------- dtypes
+
+struct Bf16 {
+    static constexpr int kVec = 8;  // elements per 16-byte vector
+    using scalar = uint16_t;
+};
+struct F32 {
+    static constexpr int kVec = 4;
+    using scalar = float;
+};
+
+__device__ __forceinline__ void widen(const u32x4 v, float (&f)[8], Bf16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(v[i] << 16);
+        f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void widen(const u32x4 v, float (&f)[4], F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
+}
+
+// fp32 -> bf16, nearest-even (v_cvt_pk_bf16_f32 on gfx950); low half = lo.
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ u32x4 narrow(const float (&f)[8], Bf16) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+    return r;
+}
+__device__ __forceinline__ u32x4 narrow(const float (&f)[4], F32) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = __float_as_uint(f[i]);
+    return r;
+}
+
+__device__ __forceinline__ float widen1(uint16_t b) { return __uint_as_float((unsigned)b << 16); }
+__device__ __forceinline__ float widen1(float f) { return f; }
+__device__ __forceinline__ uint16_t narrow1(float f, Bf16) {
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+__device__ __forceinline__ float narrow1(float f, F32) { return f; }
+
+// ---------------------------------------------------------------- memory
+
+// Streamed operands (x, residual, outputs) are touched once: non-temporal
+// hints keep them from displacing the weight, which every row re-reads.
+__device__ __forceinline__ u32x4 load_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void store_stream(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ u32x4 load_keep(const u32x4* p) { return *p; }
+
+// ---------------------------------------------------------------- reduction
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 64 lanes of a wave; every lane returns the same bits.  Each
+// step adds a lane's value to its partner's with the two operands in the same
+// order on both sides, so partners compute identical sums.
+//   quad_perm [1,0,3,2], quad_perm [2,3,0,1]: sums over quads
+//   row_half_mirror, row_mirror:              sums over 8 and 16 lanes
+//   permlane16_swap:                          rows 0+1 and 2+3
+//   permlane32_swap:                          lanes 0-31 + 32-63
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp_mov<0xB1>(v);
+    v += dpp_mov<0x4E>(v);
+    v += dpp_mov<0x141>(v);
+    v += dpp_mov<0x140>(v);
+    {
+        auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    }
+    {
+        auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    }
+    return v;
+}
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// ---------------------------------------------------------------- vector path
+
+template <int WPR>
+constexpr int max_threads() { return WPR == 16 ? 1024 : 512; }
+
+// WPR waves (64*WPR lanes) per row, VPL 16-byte vectors per lane.  Lane l of a
+// row owns vectors l, l + 64*WPR, ... so each load/store instruction of a wave
+// covers 1 KiB of contiguous memory.  MASKED: the row has fewer than
+// 64*WPR*VPL vectors; loads are clamped in bounds and zeroed, stores skipped.
+template <class E, int WPR, int VPL, bool MASKED, bool FUSED>
+__global__ void __launch_bounds__(max_threads<WPR>()) rms_vec_kernel(const RowArgs a) {
+    constexpr int LANES = 64 * WPR;
+    constexpr int V = E::kVec;
+    const int wave = wave_id();
+    const int slot = wave / WPR;  // row within the workgroup
+    const int lane_row = static_cast<int>(threadIdx.x) - slot * LANES;
+    const int nvec = a.units;
+    __shared__ float part[2][16];
+
+    int it = 0;
+    for (int64_t g = blockIdx.x; g < a.n_groups; g += gridDim.x, ++it) {
+        const int64_t row = g * a.rows_per_block + slot;
+        const bool valid = row < a.rows;
+        const int64_t base = row * nvec;
+        u32x4 d[VPL];
+        float ss = 0.f;
+        if (valid) {
+            const u32x4* xr = static_cast<const u32x4*>(a.x) + base;
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) {
+                int v = k * LANES + lane_row;
+                if (MASKED) v = v < nvec ? v : nvec - 1;
+                d[k] = load_stream(xr + v);
+            }
+            if constexpr (FUSED) {
+                const u32x4* rr = static_cast<const u32x4*>(a.res) + base;
+                u32x4* hr = static_cast<u32x4*>(a.h) + base;
+#pragma unroll
+                for (int k = 0; k < VPL; ++k) {
+                    int v = k * LANES + lane_row;
+                    const int vc = MASKED ? (v < nvec ? v : nvec - 1) : v;
+                    const u32x4 rv = load_stream(rr + vc);
+                    float fx[V], fr[V];
+                    widen(d[k], fx, E{});
+                    widen(rv, fr, E{});
+#pragma unroll
+                    for (int i = 0; i < V; ++i) fx[i] += fr[i];
+                    d[k] = narrow(fx, E{});  // h rounded once; the norm sees this value
+                    if (!MASKED || v < nvec) store_stream(hr + v, d[k]);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) {
+                float f[V];
+                widen(d[k], f, E{});
+                float s = 0.f;
+#pragma unroll
+                for (int i = 0; i < V; ++i) s += f[i] * f[i];
+                if (MASKED && k * LANES + lane_row >= nvec) s = 0.f;
+                ss += s;
+            }
+        }
+        ss = wave_sum(ss);
+        if constexpr (WPR > 1) {
+            if ((threadIdx.x & 63) == 0) part[it & 1][wave] = ss;
+            __syncthreads();
+            ss = 0.f;
+#pragma unroll
+            for (int i = 0; i < WPR; ++i) ss += part[it & 1][slot * WPR + i];
+        }
+        if (valid) {
+            const float r = rsqrtf(ss / a.hidden_f + a.eps);
+            const u32x4* wr = static_cast<const u32x4*>(a.w);
+            u32x4* outr = static_cast<u32x4*>(a.out) + base;
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) {
+                const int v = k * LANES + lane_row;
+                if (MASKED && v >= nvec) continue;
+                float f[V], fw[V];
+                widen(d[k], f, E{});
+                widen(load_keep(wr + v), fw, E{});
+#pragma unroll
+                for (int i = 0; i < V; ++i) f[i] = f[i] * r * fw[i];
+                store_stream(outr + v, narrow(f, E{}));
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- element path
+
+// One element per access; lane l of a row owns elements l, l + 64*WPR, ...
+// (each wave instruction covers 64 consecutive elements).  Always masked.
+template <class E, int WPR, int EPL, bool FUSED>
+__global__ void __launch_bounds__(max_threads<WPR>()) rms_elem_kernel(const RowArgs a) {
+    using S = typename E::scalar;
+    constexpr int LANES = 64 * WPR;
+    const int wave = wave_id();
+    const int slot = wave / WPR;
+    const int lane_row = static_cast<int>(threadIdx.x) - slot * LANES;
+    const int H = a.units;
+    __shared__ float part[2][16];
+
+    int it = 0;
+    for (int64_t g = blockIdx.x; g < a.n_groups; g += gridDim.x, ++it) {
+        const int64_t row = g * a.rows_per_block + slot;
+        const bool valid = row < a.rows;
+        const int64_t base = row * H;
+        float d[EPL];
+        float ss = 0.f;
+        if (valid) {
+            const S* xr = static_cast<const S*>(a.x) + base;
+#pragma unroll
+            for (int k = 0; k < EPL; ++k) {
+                const int j = k * LANES + lane_row;
+                d[k] = widen1(xr[j < H ? j : H - 1]);
+            }
+            if constexpr (FUSED) {
+                const S* rr = static_cast<const S*>(a.res) + base;
+                S* hr = static_cast<S*>(a.h) + base;
+#pragma unroll
+                for (int k = 0; k < EPL; ++k) {
+                    const int j = k * LANES + lane_row;
+                    const S hv = narrow1(d[k] + widen1(rr[j < H ? j : H - 1]), E{});
+                    d[k] = widen1(hv);
+                    if (j < H) hr[j] = hv;
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < EPL; ++k) {
+                const int j = k * LANES + lane_row;
+                ss += j < H ? d[k] * d[k] : 0.f;
+            }
+        }
+        ss = wave_sum(ss);
+        if constexpr (WPR > 1) {
+            if ((threadIdx.x & 63) == 0) part[it & 1][wave] = ss;
+            __syncthreads();
+            ss = 0.f;
+#pragma unroll
+            for (int i = 0; i < WPR; ++i) ss += part[it & 1][slot * WPR + i];
+        }
+        if (valid) {
+            const float r = rsqrtf(ss / a.hidden_f + a.eps);
+            const S* wr = static_cast<const S*>(a.w);
+            S* outr = static_cast<S*>(a.out) + base;
+#pragma unroll
+            for (int k = 0; k < EPL; ++k) {
+                const int j = k * LANES + lane_row;
+                if (j < H) outr[j] = narrow1(d[k] * r * widen1(wr[j]), E{});
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- two-pass path
+
+// One row per workgroup iteration, blockDim.x lanes striding over the row.
+// Pass 1 reads x (and residual) and sums squares of x (of the rounded h);
+// pass 2 reads them again, recomputes h, and writes h and y.  Pass 1 writes
+// nothing, so exact input/output aliasing stays safe: every element is read
+// and then written by the same thread.
+template <class E, bool VEC, bool FUSED>
+__global__ void __launch_bounds__(1024) rms_twopass_kernel(const RowArgs a) {
+    using S = typename E::scalar;
+    constexpr int V = E::kVec;
+    const int wave = wave_id();
+    const int nwaves = static_cast<int>(blockDim.x) >> 6;
+    const int n = a.units;
+    __shared__ float part[2][16];
+
+    int it = 0;
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x, ++it) {
+        const int64_t base = row * n;
+        float ss = 0.f;
+        for (int64_t j = threadIdx.x; j < n; j += blockDim.x) {
+            if constexpr (VEC) {
+                float f[V];
+                widen(load_stream(static_cast<const u32x4*>(a.x) + base + j), f, E{});
+                if constexpr (FUSED) {
+                    float fr[V];
+                    widen(load_stream(static_cast<const u32x4*>(a.res) + base + j), fr, E{});
+#pragma unroll
+                    for (int i = 0; i < V; ++i) f[i] += fr[i];
+                    widen(narrow(f, E{}), f, E{});
+                }
+                float s = 0.f;
+#pragma unroll
+                for (int i = 0; i < V; ++i) s += f[i] * f[i];
+                ss += s;
+            } else {
+                float f = widen1(static_cast<const S*>(a.x)[base + j]);
+                if constexpr (FUSED) f = widen1(narrow1(f + widen1(static_cast<const S*>(a.res)[base + j]), E{}));
+                ss += f * f;
+            }
+        }
+        ss = wave_sum(ss);
+        if ((threadIdx.x & 63) == 0) part[it & 1][wave] = ss;
+        __syncthreads();
+        ss = 0.f;
+        for (int i = 0; i < nwaves; ++i) ss += part[it & 1][i];
+        const float r = rsqrtf(ss / a.hidden_f + a.eps);
+        for (int64_t j = threadIdx.x; j < n; j += blockDim.x) {
+            if constexpr (VEC) {
+                float f[V], fw[V];
+                u32x4 xv = load_stream(static_cast<const u32x4*>(a.x) + base + j);
+                if constexpr (FUSED) {
+                    float fr[V];
+                    widen(xv, f, E{});
+                    widen(load_stream(static_cast<const u32x4*>(a.res) + base + j), fr, E{});
+#pragma unroll
+                    for (int i = 0; i < V; ++i) f[i] += fr[i];
+                    xv = narrow(f, E{});
+                    store_stream(static_cast<u32x4*>(a.h) + base + j, xv);
+                }
+                widen(xv, f, E{});
+                widen(load_keep(static_cast<const u32x4*>(a.w) + j), fw, E{});
+#pragma unroll
+                for (int i = 0; i < V; ++i) f[i] = f[i] * r * fw[i];
+                store_stream(static_cast<u32x4*>(a.out) + base + j, narrow(f, E{}));
+            } else {
+                float f = widen1(static_cast<const S*>(a.x)[base + j]);
+                if constexpr (FUSED) {
+                    const S hv = narrow1(f + widen1(static_cast<const S*>(a.res)[base + j]), E{});
+                    static_cast<S*>(a.h)[base + j] = hv;
+                    f = widen1(hv);
+                }
+                static_cast<S*>(a.out)[base + j] = narrow1(f * r * widen1(static_cast<const S*>(a.w)[j]), E{});
+            }
+        }
+    }
+}
+
+}  // namespace mbr

@@ -1,0 +1,210 @@
+"""C-ABI checks that need no GPU: the libraries load, export what the headers
+declare, reject bad arguments before touching HIP, and choose only built,
+spill-free configurations."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+import torch
+
+import memory_bound_rmsnorm_amd as mbr
+from memory_bound_rmsnorm_amd import _build, inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
+NO_GPU = not torch.cuda.is_available()
+# Fake addresses are only ever passed where validation must reject the call;
+# they are used only where no GPU is visible, so a validation bug cannot turn
+# into a kernel launch on bogus memory.
+fake_only = pytest.mark.skipif(not NO_GPU, reason="fake device addresses are only used without a GPU")
+
+
+def _built():
+    if not (os.path.exists(_build.LIB_RMSNORM) and os.path.exists(_build.LIB_COPY)
+            and os.path.exists(_build.RESOURCE_USAGE)):
+        _build.build()
+
+
+def _declared(header):
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"(?:RMSNORM_API|HBM_COPY_API)\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_headers_declare_the_boundary():
+    names = {n for h in HEADERS for n in _declared(h)}
+    for n in ("rmsnorm_fwd", "rmsnorm_residual_fwd", "rmsnorm_status_string", "rmsnorm_select_config",
+              "rmsnorm_fwd_ex", "rmsnorm_residual_fwd_ex", "hbm_copy"):
+        assert n in names
+
+
+def test_libraries_export_every_declared_symbol():
+    _built()
+    libs = {"rmsnorm.h": ctypes.CDLL(_build.LIB_RMSNORM), "hbm_copy.h": ctypes.CDLL(_build.LIB_COPY)}
+    for h in HEADERS:
+        L = libs[os.path.basename(h)]
+        for name in _declared(h):
+            assert hasattr(L, name), "%s does not export %s" % (os.path.basename(h), name)
+
+
+def test_no_internal_symbols_exported():
+    _built()
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", _build.LIB_RMSNORM], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    declared = {n for h in HEADERS for n in _declared(h)}
+    assert exported <= declared | {"_init", "_fini"}, exported - declared
+
+
+def test_every_built_kernel_is_spill_free():
+    _built()
+    lines = open(_build.RESOURCE_USAGE).read().strip().splitlines()
+    assert len(lines) > 400
+    for l in lines:
+        assert "| scratch 0 |" in l and "VGPR spill 0" in l and "SGPR spill 0" in l, l
+
+
+def test_status_strings():
+    for s in range(4):
+        assert mbr.rmsnorm_status_string(s).startswith(
+            ["RMSNORM_OK", "RMSNORM_ERR_INVALID_ARG", "RMSNORM_ERR_UNSUPPORTED_DTYPE", "RMSNORM_ERR_RUNTIME"][s])
+    assert mbr.rmsnorm_status_string(99) == "unknown rmsnorm status"
+
+
+def test_rows_zero_is_ok_without_pointers():
+    L = mbr.lib()
+    assert L.rmsnorm_fwd(None, None, None, 0, 16, 1e-5, 1, None) == mbr.RMSNORM_OK
+    assert L.rmsnorm_residual_fwd(None, None, None, None, None, 0, 16, 1e-5, 0, None) == mbr.RMSNORM_OK
+
+
+@pytest.mark.parametrize("rows,hidden,eps,dtype,want", [
+    (-1, 16, 1e-5, 1, mbr.RMSNORM_ERR_INVALID_ARG),
+    (4, 0, 1e-5, 1, mbr.RMSNORM_ERR_INVALID_ARG),
+    (4, -8, 1e-5, 1, mbr.RMSNORM_ERR_INVALID_ARG),
+    (4, 2 ** 31, 1e-5, 1, mbr.RMSNORM_ERR_INVALID_ARG),
+    (4, 16, -1e-5, 1, mbr.RMSNORM_ERR_INVALID_ARG),
+    (4, 16, float("nan"), 1, mbr.RMSNORM_ERR_INVALID_ARG),
+    (4, 16, float("inf"), 1, mbr.RMSNORM_ERR_INVALID_ARG),
+    (4, 16, 1e-5, 2, mbr.RMSNORM_ERR_UNSUPPORTED_DTYPE),
+    (4, 16, 1e-5, -1, mbr.RMSNORM_ERR_UNSUPPORTED_DTYPE),
+    (2 ** 62, 16, 1e-5, 1, mbr.RMSNORM_ERR_INVALID_ARG),
+])
+def test_bad_sizes_rejected_before_any_pointer_use(rows, hidden, eps, dtype, want):
+    L = mbr.lib()
+    assert L.rmsnorm_fwd(None, None, None, rows, hidden, eps, dtype, None) == want
+    assert L.rmsnorm_residual_fwd(None, None, None, None, None, rows, hidden, eps, dtype, None) == want
+
+
+@fake_only
+def test_null_and_misaligned_pointers_rejected():
+    L = mbr.lib()
+    A, W, O = 0x7F0000000000, 0x7F0010000000, 0x7F0020000000
+    INV = mbr.RMSNORM_ERR_INVALID_ARG
+    assert L.rmsnorm_fwd(None, W, O, 4, 16, 1e-5, 1, None) == INV
+    assert L.rmsnorm_fwd(A, None, O, 4, 16, 1e-5, 1, None) == INV
+    assert L.rmsnorm_fwd(A, W, None, 4, 16, 1e-5, 1, None) == INV
+    assert L.rmsnorm_fwd(A + 1, W, O, 4, 16, 1e-5, 1, None) == INV  # bf16 needs 2-byte alignment
+    assert L.rmsnorm_fwd(A + 2, W, O, 4, 16, 1e-5, 0, None) == INV  # f32 needs 4-byte alignment
+    R, H = 0x7F0030000000, 0x7F0040000000
+    assert L.rmsnorm_residual_fwd(A, None, W, H, O, 4, 16, 1e-5, 1, None) == INV
+    assert L.rmsnorm_residual_fwd(A, R, W, None, O, 4, 16, 1e-5, 1, None) == INV
+
+
+@fake_only
+def test_overlaps_rejected():
+    L = mbr.lib()
+    INV = mbr.RMSNORM_ERR_INVALID_ARG
+    A = 0x7F0000000000
+    nb = 4 * 16 * 2
+    W = 0x7F0010000000
+    assert L.rmsnorm_fwd(A, W, A + 32, 4, 16, 1e-5, 1, None) == INV       # out partially over x
+    assert L.rmsnorm_fwd(A, W, W - 64, 4, 16, 1e-5, 1, None) == INV       # out over weight
+    X, R, H, O = A, A + 0x100000, A + 0x200000, A + 0x300000
+    assert L.rmsnorm_residual_fwd(X, R, W, H, H, 4, 16, 1e-5, 1, None) == INV     # out == residual_out
+    assert L.rmsnorm_residual_fwd(X, R, W, H, H + 2, 4, 16, 1e-5, 1, None) == INV
+    assert L.rmsnorm_residual_fwd(X, R, W, R + 2, O, 4, 16, 1e-5, 1, None) == INV  # h partially over residual
+    assert L.rmsnorm_residual_fwd(X, R, W, H, X + nb - 2, 4, 16, 1e-5, 1, None) == INV
+    assert L.rmsnorm_residual_fwd(X, R, W, W, O, 4, 16, 1e-5, 1, None) == INV       # h over weight
+
+
+@fake_only
+def test_bad_forced_configs_rejected():
+    L = mbr.lib()
+    INV = mbr.RMSNORM_ERR_INVALID_ARG
+    A, W, O = 0x7F0000000000, 0x7F0010000000, 0x7F0020000000
+
+    def call(path, wpr, per, rpb, hidden=2048, x=A, mb=0):
+        cfg = mbr.Config(path, wpr, per, rpb, mb)
+        return L.rmsnorm_fwd_ex(x, W, O, 8, hidden, 1e-5, 1, ctypes.byref(cfg), None)
+
+    assert call(1, 3, 4, 1) == INV            # waves per row not built
+    assert call(1, 1, 9, 1) == INV            # vectors per lane not built
+    assert call(1, 1, 2, 1) == INV            # 64 lanes x 2 vectors do not cover 256 vectors
+    assert call(1, 1, 4, 16) == INV           # 1024 lanes with a 512-lane bound
+    assert call(1, 16, 16, 1, hidden=2048 * 64) == INV  # not built (would spill)
+    assert call(1, 1, 4, 1, x=A + 2) == INV   # vector path needs 16-byte alignment
+    assert call(1, 1, 4, 1, hidden=2044) == INV  # hidden * 2 not a multiple of 16
+    assert call(2, 1, 16, 1, hidden=2048) == INV  # 64 x 16 elements do not cover 2048
+    assert call(3, 16, 0, 2) == INV           # two-pass takes one row per workgroup
+    assert call(7, 1, 4, 1) == INV            # unknown path
+    assert call(1, 1, 4, 0) == INV            # zero rows per block
+    assert call(1, 1, 4, 1, mb=-1) == INV
+
+
+@pytest.mark.parametrize("name", list(inputs.WORKLOADS))
+def test_selection_for_the_workloads(name):
+    w = inputs.WORKLOADS[name]
+    cfg = mbr.rmsnorm_select_config(w.rows, w.hidden, torch.float32 if w.dtype == "f32" else torch.bfloat16,
+                                    True, w.fused)
+    assert cfg.path == mbr.PATH_VECTOR
+    vec = 4 if w.dtype == "f32" else 8
+    assert 64 * cfg.waves_per_row * cfg.items_per_lane >= w.hidden // vec
+    assert 64 * cfg.waves_per_row * cfg.rows_per_block <= (1024 if cfg.waves_per_row == 16 else 512)
+
+
+@pytest.mark.parametrize("hidden", [1, 3, 7, 8, 9, 127, 769, 2048, 4095, 5120, 5121, 8192, 8193, 16384,
+                                    65536, 81920, 131072, 1 << 20])
+@pytest.mark.parametrize("rows", [1, 5, 4096, 12289])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("aligned", [True, False])
+@pytest.mark.parametrize("fused", [False, True])
+def test_selection_is_always_a_built_covering_config(hidden, rows, dtype, aligned, fused):
+    cfg = mbr.rmsnorm_select_config(rows, hidden, dtype, aligned, fused)
+    vec = 4 if dtype == torch.float32 else 8
+    assert cfg.waves_per_row in (1, 2, 4, 8, 16) and cfg.rows_per_block >= 1
+    if cfg.path == mbr.PATH_VECTOR:
+        assert aligned and hidden % vec == 0
+        assert 64 * cfg.waves_per_row * cfg.items_per_lane >= hidden // vec
+        assert cfg.items_per_lane in (1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16)
+        if cfg.waves_per_row == 16:
+            assert cfg.items_per_lane <= (6 if fused else 10)
+    elif cfg.path == mbr.PATH_ELEMENT:
+        assert 64 * cfg.waves_per_row * cfg.items_per_lane >= hidden
+        assert cfg.items_per_lane in (1, 2, 4, 8, 16)
+    else:
+        assert cfg.path == mbr.PATH_TWO_PASS and cfg.rows_per_block == 1
+        assert hidden > 8192  # everything narrower fits a register-resident path
+    assert 64 * cfg.waves_per_row * cfg.rows_per_block <= (1024 if cfg.waves_per_row == 16 else 512)
+    assert cfg.rows_per_block <= max(rows, 1)
+
+
+def test_hbm_copy_rejects_bad_arguments():
+    L = mbr.copy_lib()
+    assert L.hbm_copy(None, None, 0, 0, None) == 0
+    assert L.hbm_copy(None, None, 64, 0, None) == 1
+    assert L.hbm_copy(None, None, -1, 0, None) == 1
+    if NO_GPU:
+        A = 0x7F0000000000
+        assert L.hbm_copy(A + 8, A + 0x1000000, 64, 0, None) == 1   # misaligned
+        assert L.hbm_copy(A, A + 32, 64, 0, None) == 1              # overlap
+        assert L.hbm_copy(A, A + 0x1000000, 64, -1, None) == 1
+
+
+def test_binding_refuses_cpu_tensors():
+    x = torch.zeros(4, 8)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        mbr.rmsnorm_fwd(x, torch.ones(8), torch.empty_like(x))
+    with pytest.raises(TypeError):
+        mbr.dtype_code(torch.float16)

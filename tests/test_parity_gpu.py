@@ -1,0 +1,379 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on the GPU.
+
+Every test compares element by element on seeded inputs: bf16 within 1 ulp,
+fp32 within 1e-5 relative, the fused residual sum h bitwise (tests/parity.py).
+Covered: the five stated workloads at full size in the automatically chosen
+launch configuration (the one bench.py times), every built kernel
+configuration on shapes that span several workgroups and a partial last one,
+ragged widths, odd row counts, misaligned and aliased buffers, the two-pass
+fallback, the in-kernel row loop, determinism and degenerate rows.
+"""
+import ctypes
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import memory_bound_rmsnorm_amd as mbr
+from memory_bound_rmsnorm_amd import inputs
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+BF16, F32 = torch.bfloat16, torch.float32
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def tdtype(w):
+    return F32 if w.dtype == "f32" else BF16
+
+
+def run_plain(x, w, eps, cfg=None, out=None):
+    out = torch.empty_like(x) if out is None else out
+    mbr.rmsnorm_fwd_ex(x, w, out, eps, cfg)
+    torch.cuda.synchronize()
+    return out
+
+
+def run_fused(x, r, w, eps, cfg=None, h=None, out=None):
+    h = torch.empty_like(x) if h is None else h
+    out = torch.empty_like(x) if out is None else out
+    mbr.rmsnorm_residual_fwd_ex(x, r, w, h, out, eps, cfg)
+    torch.cuda.synchronize()
+    return h, out
+
+
+def check_workload(w, t, cfg=None, eps=None):
+    """Run workload tensors t (CPU) on the GPU and compare with the oracle."""
+    eps = w.eps if eps is None else eps
+    dev = {k: v.cuda() for k, v in t.items()}
+    xb, wb = inputs.bits(t["x"]), inputs.bits(t["weight"])
+    if w.fused:
+        h, y = run_fused(dev["x"], dev["residual"], dev["weight"], eps, cfg)
+        h_want, y_want = parity.oracle_residual(xb, inputs.bits(t["residual"]), wb, eps)
+        assert np.array_equal(inputs.bits(h), h_want), "residual sum differs"
+        return parity.compare(inputs.bits(y), y_want)
+    y = run_plain(dev["x"], dev["weight"], eps, cfg)
+    return parity.compare(inputs.bits(y), parity.oracle_fwd(xb, wb, eps))
+
+
+# ---------------------------------------------------------------- stated workloads
+
+
+@pytest.mark.parametrize("name", list(inputs.WORKLOADS))
+def test_stated_workloads_full_size(name):
+    w = inputs.WORKLOADS[name]
+    say("workload", name, "seed 0", "config", mbr.rmsnorm_select_config(w.rows, w.hidden, tdtype(w), True, w.fused))
+    stats = check_workload(w, inputs.make(w, seed=0))
+    say(name, stats)
+
+
+@pytest.mark.parametrize("name", ["bf16_prefill_4096x2048", "bf16_residual_12289x5120"])
+@pytest.mark.parametrize("seed", [1, 2])
+def test_stated_workloads_other_seeds(name, seed):
+    w = inputs.WORKLOADS[name]
+    say("workload", name, "seed", seed)
+    check_workload(w, inputs.make(w, seed=seed))
+
+
+# ---------------------------------------------------------------- shapes
+
+
+RAGGED = [(1, 1), (3, 3), (5, 7), (2, 8), (5, 9), (67, 127), (12, 769), (5, 2048), (3, 4095), (7, 5120),
+          (5, 5121), (3, 8193), (9, 16384), (2, 20000), (3, 65536), (2, 81920), (2, 131080)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("rows,hidden", RAGGED)
+def test_ragged_shapes(rows, hidden, dtype, fused):
+    w = inputs.custom(rows, hidden, dtype, fused)
+    cfg = mbr.rmsnorm_select_config(rows, hidden, BF16 if dtype == "bf16" else F32, True, fused)
+    say("shape", rows, hidden, dtype, "fused" if fused else "plain", cfg)
+    check_workload(w, inputs.make(w, seed=rows * 7 + hidden))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("fused", [False, True])
+def test_odd_row_counts(dtype, fused):
+    for rows in (1, 2, 3, 5, 12289):
+        w = inputs.custom(rows, 2048, dtype, fused)
+        say("rows", rows, dtype, fused)
+        check_workload(w, inputs.make(w, seed=rows))
+
+
+def test_many_rows_in_kernel_loop():
+    """More row groups than the largest grid: workgroups loop over rows."""
+    rows = (1 << 20) * 4 + 3
+    w = inputs.custom(rows, 8, "bf16", False)
+    cfg = mbr.rmsnorm_select_config(rows, 8, BF16)
+    assert (rows + cfg.rows_per_block - 1) // cfg.rows_per_block > (1 << 20)
+    say("many rows", rows, cfg)
+    check_workload(w, inputs.make(w, seed=5))
+
+
+# ---------------------------------------------------------------- every built configuration
+
+
+def _configs(path, dtype, fused):
+    vec = path == mbr.PATH_VECTOR
+    per_list = (1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16) if vec else (1, 2, 4, 8, 16)
+    for wpr in (1, 2, 4, 8, 16):
+        for per in per_list:
+            if wpr == 16 and per > ((6 if fused else 10) if vec else 8):
+                continue
+            yield wpr, per
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("fused", [False, True])
+def test_every_vector_config(dtype, fused):
+    vecw = 8 if dtype == "bf16" else 4
+    n = 0
+    for wpr, vpl in _configs(mbr.PATH_VECTOR, dtype, fused):
+        lanes = 64 * wpr
+        max_rpb = (1024 if wpr == 16 else 512) // lanes
+        for nvec in sorted({lanes * vpl, max(1, lanes * vpl - 37), lanes * (vpl - 1) + 1}):
+            for rpb in sorted({1, max_rpb}):
+                rows = 2 * rpb + 1
+                cfg = mbr.Config(mbr.PATH_VECTOR, wpr, vpl, rpb, 0)
+                w = inputs.custom(rows, nvec * vecw, dtype, fused)
+                say("vector", dtype, fused, cfg, "hidden", nvec * vecw, "rows", rows)
+                check_workload(w, inputs.make(w, seed=n), cfg)
+                n += 1
+    assert n > 100
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("fused", [False, True])
+def test_every_element_config(dtype, fused):
+    n = 0
+    for wpr, epl in _configs(mbr.PATH_ELEMENT, dtype, fused):
+        lanes = 64 * wpr
+        max_rpb = (1024 if wpr == 16 else 512) // lanes
+        for hidden in sorted({lanes * epl, max(1, lanes * epl - 5), lanes * (epl - 1) + 1 if epl > 1 else 3}):
+            rpb = max_rpb if n % 2 else 1
+            rows = 2 * rpb + 1
+            cfg = mbr.Config(mbr.PATH_ELEMENT, wpr, epl, rpb, 0)
+            w = inputs.custom(rows, hidden, dtype, fused)
+            say("element", dtype, fused, cfg, "hidden", hidden, "rows", rows)
+            check_workload(w, inputs.make(w, seed=n), cfg)
+            n += 1
+    assert n > 40
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("fused", [False, True])
+def test_every_two_pass_config(dtype, fused):
+    for wpr in (1, 2, 4, 8, 16):
+        for hidden in (4096, 4099, 12288 + 8):
+            cfg = mbr.Config(mbr.PATH_TWO_PASS, wpr, 0, 1, 0)
+            w = inputs.custom(5, hidden, dtype, fused)
+            say("two-pass", dtype, fused, cfg, "hidden", hidden)
+            check_workload(w, inputs.make(w, seed=wpr + hidden), cfg)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_persistent_grid_matches_bitwise(fused):
+    """Capping the grid (workgroups loop over row groups) changes nothing."""
+    w = inputs.custom(1000, 4096, "bf16", fused)
+    t = {k: v.cuda() for k, v in inputs.make(w, seed=3).items()}
+    base = mbr.rmsnorm_select_config(1000, 4096, BF16, True, fused)
+    capped = mbr.Config(base.path, base.waves_per_row, base.items_per_lane, base.rows_per_block, 37)
+    if fused:
+        a = run_fused(t["x"], t["residual"], t["weight"], 1e-5, base)
+        b = run_fused(t["x"], t["residual"], t["weight"], 1e-5, capped)
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    else:
+        assert torch.equal(run_plain(t["x"], t["weight"], 1e-5, base), run_plain(t["x"], t["weight"], 1e-5, capped))
+    check_workload(w, inputs.make(w, seed=3), capped)
+
+
+# ---------------------------------------------------------------- pointers
+
+
+def _raw_plain(xp, wp, op, rows, hidden, eps, dt):
+    st = mbr.lib().rmsnorm_fwd(xp, wp, op, rows, hidden, eps, dt, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return st
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("which", ["x", "weight", "out"])
+def test_misaligned_pointers(dtype, which):
+    """Element-aligned but not 16-byte-aligned buffers take the element path."""
+    rows, hidden, eps = 33, 2048, 1e-5
+    w = inputs.custom(rows, hidden, dtype, False)
+    t = inputs.make(w, seed=11)
+    td = BF16 if dtype == "bf16" else F32
+    es = 2 if dtype == "bf16" else 4
+    pad = 8
+    xbuf = torch.zeros(rows * hidden + pad, dtype=td, device="cuda")
+    wbuf = torch.zeros(hidden + pad, dtype=td, device="cuda")
+    obuf = torch.zeros(rows * hidden + pad, dtype=td, device="cuda")
+    off = {k: (1 if k == which else 0) for k in ("x", "weight", "out")}
+    xbuf[off["x"]:off["x"] + rows * hidden] = t["x"].reshape(-1).cuda()
+    wbuf[off["weight"]:off["weight"] + hidden] = t["weight"].cuda()
+    st = _raw_plain(xbuf.data_ptr() + es * off["x"], wbuf.data_ptr() + es * off["weight"],
+                    obuf.data_ptr() + es * off["out"], rows, hidden, eps, mbr.dtype_code(td))
+    assert st == mbr.RMSNORM_OK
+    got = inputs.bits(obuf[off["out"]:off["out"] + rows * hidden].reshape(rows, hidden).cpu())
+    parity.compare(got, parity.oracle_fwd(inputs.bits(t["x"]), inputs.bits(t["weight"]), eps))
+    # nothing outside the output was written
+    assert torch.count_nonzero(obuf[:off["out"]]) == 0
+    assert torch.count_nonzero(obuf[off["out"] + rows * hidden:]) == 0
+
+
+def test_misaligned_fused():
+    rows, hidden, eps = 17, 1024, 1e-5
+    w = inputs.custom(rows, hidden, "bf16", True)
+    t = inputs.make(w, seed=12)
+    n = rows * hidden
+    buf = torch.zeros(4 * n + 64, dtype=BF16, device="cuda")
+    xo, ro, ho, oo = 1, n + 3, 2 * n + 5, 3 * n + 9
+    buf[xo:xo + n] = t["x"].reshape(-1).cuda()
+    buf[ro:ro + n] = t["residual"].reshape(-1).cuda()
+    wt = t["weight"].cuda()
+    p = buf.data_ptr()
+    st = mbr.lib().rmsnorm_residual_fwd(p + 2 * xo, p + 2 * ro, wt.data_ptr(), p + 2 * ho, p + 2 * oo, rows, hidden,
+                                        eps, 1, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == mbr.RMSNORM_OK
+    h_want, y_want = parity.oracle_residual(inputs.bits(t["x"]), inputs.bits(t["residual"]),
+                                            inputs.bits(t["weight"]), eps)
+    cpu = inputs.bits(buf.cpu())
+    assert np.array_equal(cpu[ho:ho + n].reshape(rows, hidden), h_want)
+    parity.compare(cpu[oo:oo + n].reshape(rows, hidden), y_want)
+
+
+@pytest.mark.parametrize("hidden", [4096, 4100])
+def test_in_place_plain(hidden):
+    w = inputs.custom(300, hidden, "bf16", False)
+    t = inputs.make(w, seed=13)
+    want = parity.oracle_fwd(inputs.bits(t["x"]), inputs.bits(t["weight"]), 1e-5)
+    x = t["x"].cuda()
+    run_plain(x, t["weight"].cuda(), 1e-5, out=x)
+    parity.compare(inputs.bits(x), want)
+
+
+@pytest.mark.parametrize("alias", ["h=residual", "h=x", "out=x", "out=residual", "h=x,out=residual"])
+def test_in_place_fused(alias):
+    w = inputs.custom(257, 5120, "bf16", True)
+    t = inputs.make(w, seed=14)
+    h_want, y_want = parity.oracle_residual(inputs.bits(t["x"]), inputs.bits(t["residual"]),
+                                            inputs.bits(t["weight"]), 1e-5)
+    x, r, wt = t["x"].cuda(), t["residual"].cuda(), t["weight"].cuda()
+    named = {"x": x, "residual": r}
+    h = torch.empty_like(x)
+    out = torch.empty_like(x)
+    for part in alias.split(","):
+        k, v = part.split("=")
+        if k == "h":
+            h = named[v]
+        else:
+            out = named[v]
+    run_fused(x, r, wt, 1e-5, h=h, out=out)
+    assert np.array_equal(inputs.bits(h), h_want)
+    parity.compare(inputs.bits(out), y_want)
+
+
+def test_overlap_rejected_on_device_buffers():
+    """Partial overlaps are refused (and nothing is launched) -- real buffers,
+    so even a validation slip could not touch memory outside this allocation."""
+    buf = torch.zeros(4 * 64 * 2, dtype=BF16, device="cuda")
+    wt = torch.ones(64, dtype=BF16, device="cuda")
+    p = buf.data_ptr()
+    st = _raw_plain(p, wt.data_ptr(), p + 32, 2, 64, 1e-5, 1)
+    assert st == mbr.RMSNORM_ERR_INVALID_ARG
+    assert torch.count_nonzero(buf) == 0
+
+
+def test_non_default_stream():
+    w = inputs.WORKLOADS["bf16_prefill_4096x2048"]
+    t = inputs.make(w, seed=15)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        x, wt = t["x"].cuda(), t["weight"].cuda()
+        out = torch.empty_like(x)
+        mbr.rmsnorm_fwd(x, wt, out, w.eps)
+    s.synchronize()
+    parity.compare(inputs.bits(out), parity.oracle_fwd(inputs.bits(t["x"]), inputs.bits(t["weight"]), w.eps))
+
+
+# ---------------------------------------------------------------- determinism and degenerate rows
+
+
+@pytest.mark.parametrize("name", [inputs.HEADLINE, "bf16_residual_12289x5120"])
+def test_bitwise_deterministic(name):
+    w = inputs.WORKLOADS[name]
+    t = {k: v.cuda() for k, v in inputs.make(w, seed=0, rows=2048).items()}
+    if w.fused:
+        a = run_fused(t["x"], t["residual"], t["weight"], w.eps)
+        b = run_fused(t["x"], t["residual"], t["weight"], w.eps)
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    else:
+        assert torch.equal(run_plain(t["x"], t["weight"], w.eps), run_plain(t["x"], t["weight"], w.eps))
+
+
+def test_row_batches_bitwise_equal_in_one_config():
+    w = inputs.custom(4096, 8192, "bf16", False)
+    t = {k: v.cuda() for k, v in inputs.make(w, seed=16).items()}
+    cfg = mbr.rmsnorm_select_config(4096, 8192, BF16)
+    full = run_plain(t["x"], t["weight"], 1e-5, cfg)
+    top = run_plain(t["x"][:1000].contiguous(), t["weight"], 1e-5, cfg)
+    bot = run_plain(t["x"][1000:].contiguous(), t["weight"], 1e-5, cfg)
+    assert torch.equal(full, torch.cat([top, bot]))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_degenerate_rows(dtype):
+    """A zero row gives zeros (eps > 0); NaN and Inf stay in their own rows;
+    constant rows give c / sqrt(c^2 + eps) * w; eps = 0 works on non-zero rows."""
+    td = BF16 if dtype == "bf16" else F32
+    H = 4096
+    x = torch.randn(6, H, generator=torch.Generator().manual_seed(0)).to(td)
+    x[0] = 0
+    x[1, 7] = float("nan")
+    x[2, 9] = float("inf")
+    x[3] = -3.0
+    wt = (1 + 0.1 * torch.randn(H, generator=torch.Generator().manual_seed(1))).to(td)
+    for eps in (1e-5, 0.0):
+        xs = x if eps > 0 else x[1:]
+        y = run_plain(xs.cuda(), wt.cuda(), eps)
+        want = parity.oracle_fwd(inputs.bits(xs), inputs.bits(wt), eps)
+        got = inputs.bits(y)
+        if eps > 0:
+            assert np.all(got[0].astype(np.float64) == 0) if dtype == "f32" else np.all(got[0] & 0x7FFF == 0)
+        parity.compare(got, want)
+
+
+def test_pages_rmsnorm_test_case_on_gpu():
+    """The xserv RMSNorm tests' data (rows 4, hidden 768, eps 1e-5) through the
+    HIP path: parity with the oracle, and within the pages' tolerances of their
+    f32 CPU reference computed from the unrounded inputs."""
+    rows, hidden, eps = 4, 768, 1e-5
+    i = np.arange(rows * hidden)
+    x = (((i % 17).astype(np.float32) - np.float32(8.0)) * np.float32(0.1)).reshape(rows, hidden)
+    g = (np.float32(0.5) + (np.arange(hidden) % 3).astype(np.float32) * np.float32(0.2)).astype(np.float32)
+    ref = x.astype(np.float64) / np.sqrt(np.mean(x.astype(np.float64) ** 2, axis=1, keepdims=True) + eps) * g
+    for td, tol in ((F32, 1e-4), (BF16, 0.05)):
+        xt, gt = torch.from_numpy(x).to(td), torch.from_numpy(g).to(td)
+        y = run_plain(xt.cuda(), gt.cuda(), eps)
+        parity.compare(inputs.bits(y), parity.oracle_fwd(inputs.bits(xt), inputs.bits(gt), eps))
+        err = float(np.max(np.abs(y.float().cpu().numpy() - ref)))
+        say("pages' test case", td, "max_err vs f32 reference on unrounded inputs", err)
+        assert err <= tol
+
+
+def test_hbm_copy_copies():
+    src = torch.randint(0, 255, (3 * (1 << 20) + 13,), dtype=torch.uint8, device="cuda")
+    dst = torch.zeros_like(src)
+    mbr.hbm_copy(src, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
