@@ -133,10 +133,13 @@ def copy_ceiling(w, steps, warmup):
     return 2 * nbytes / (ev / steps) / 1e9
 
 
-def load_traffic(w):
+KERNEL_FAMILY = {"vector": "rms_vec_kernel", "element": "rms_elem_kernel", "two_pass": "rms_twopass_kernel"}
+
+
+def load_traffic(w, launch):
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel sources; else None."""
-    path = os.path.join(PROFILE_DIR, "pmc_traffic_%s.txt" % w.name)
+    path = os.path.join(PROFILE_DIR, "pmc_traffic_%s_%s.txt" % (KERNEL_FAMILY[launch["path"]], w.name))
     if not os.path.exists(path):
         return None
     vals = {}
@@ -256,7 +259,8 @@ def main():
         "pct_of_peak": round(100 * rec["gbps_wall"] / HBM_PEAK_GBPS, 2),
         "us_per_call": round(rec["us_per_call"], 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic(w)},
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": load_traffic(w, rec["kernel_config"])},
         "parity": "checked against the CPU oracle at this size and launch configuration by "
                   "tests/test_parity_gpu.py::test_stated_workloads_full_size",
     }

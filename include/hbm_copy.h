@@ -23,7 +23,7 @@ extern "C" {
  * Copy `bytes` bytes from device pointer src to device pointer dst on `stream`
  * (hipStream_t, NULL = default), asynchronously.  Both pointers must be 16-byte
  * aligned and the ranges must not overlap.  max_blocks > 0 caps the grid
- * (grid-stride loop); 0 = one workgroup per 16 KiB.
+ * (grid-stride loop); 0 = one workgroup per 16 KiB of data.
  * Returns 0 on success, 1 on an invalid argument (nothing launched), 3 if the
  * launch failed.
  */

@@ -11,8 +11,9 @@ namespace {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+// 512 lanes x 2 vectors per lane: the fastest copy shape measured on MI355X.
+constexpr int kThreads = 512;
+constexpr int kUnroll = 2;
 
 __global__ void __launch_bounds__(kThreads) hbm_copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                                             int64_t nvec, const unsigned char* __restrict__ src_tail,

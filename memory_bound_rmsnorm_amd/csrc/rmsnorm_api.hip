@@ -97,18 +97,20 @@ bool vector_aligned(const Problem& p) {
     return true;
 }
 
-// The automatic choice.  A row is spread over the fewest waves that keep at
-// most 8 items (128 bytes on the vector path) of it per lane; when rows are
-// few, each row gets more waves so the whole GPU has work in flight; 256-lane
-// workgroups carry several rows when a row needs fewer lanes.  Rows that no
-// built register-resident configuration covers take the two-pass path.
+// The automatic choice, from launch-shape sweeps on MI355X.  Vector path:
+// spread a row over the fewest waves (one row per workgroup) that keep at most
+// two 16-byte vectors of it per lane -- many short waves keep more requests in
+// flight than a few long ones; e.g. bf16 hidden 8192 runs as 8 waves x 2
+// vectors.  Element path: at most 8 elements per lane.  When rows are few,
+// each row gets more waves so the whole GPU has work.  Rows that no built
+// register-resident configuration covers take the two-pass path.
 rmsnorm_config_t choose(int64_t rows, int64_t hidden, int dtype, bool aligned, bool fused) {
     rmsnorm_config_t c = {RMSNORM_PATH_TWO_PASS, 16, 0, 1, 0};
     const bool vec = aligned && hidden % vec_elems(dtype) == 0;
     const int64_t units = vec ? hidden / vec_elems(dtype) : hidden;
     const int* list = vec ? mbr::kVplList : mbr::kEplList;
     const int nlist = vec ? mbr::kNumVpl : mbr::kNumEpl;
-    const int cap = 8;
+    const int cap = vec ? 2 : 8;
     auto fit = [&](int wpr) {
         const int per = round_up_in(list, nlist, ceil_div(units, int64_t(64) * wpr));
         if (per < 0) return -1;
@@ -127,9 +129,7 @@ rmsnorm_config_t choose(int64_t rows, int64_t hidden, int dtype, bool aligned, b
     c.path = vec ? RMSNORM_PATH_VECTOR : RMSNORM_PATH_ELEMENT;
     c.waves_per_row = wpr;
     c.items_per_lane = per;
-    int64_t rpb = wpr >= 4 ? 1 : 4 / wpr;
-    if (rpb > rows && rows > 0) rpb = rows;
-    c.rows_per_block = static_cast<int32_t>(rpb);
+    c.rows_per_block = 1;
     c.max_blocks = 0;
     return c;
 }

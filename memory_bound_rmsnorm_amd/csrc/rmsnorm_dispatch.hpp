@@ -18,10 +18,12 @@ constexpr int kNumEpl = sizeof(kEplList) / sizeof(int);
 
 constexpr int max_threads_for(int wpr) { return wpr == 16 ? 1024 : 512; }
 
-// A 1024-lane workgroup leaves each lane 128 VGPRs; the configurations below
-// are the ones whose row fits that budget without scratch spills (the others
-// are not built).  Narrower workgroups have 256 VGPRs per lane and fit all.
-constexpr bool vec_built(int wpr, int vpl, bool fused) { return wpr < 16 || vpl <= (fused ? 6 : 10); }
+// A 1024-lane workgroup leaves each lane 128 VGPRs, narrower ones 256; the
+// configurations below are the ones whose registers fit without scratch
+// spills (the others are not built).
+constexpr bool vec_built(int wpr, int vpl, bool fused) {
+    return wpr < 16 ? !(fused && vpl == 16) : vpl <= (fused ? 6 : 10);
+}
 constexpr bool elem_built(int wpr, int epl) { return wpr < 16 || epl <= 8; }
 
 // Host-side kernel handles (addresses of the __global__ stubs), or nullptr.

@@ -141,50 +141,95 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 template <int WPR>
 constexpr int max_threads() { return WPR == 16 ? 1024 : 512; }
 
+// The weight slice a lane needs is the same for every row.  Where registers
+// allow, a workgroup loads it once, up front, so that no dependent L2 round
+// trip sits between a row's reduction and its stores.  Measured on MI355X this
+// pays when a lane holds three or more vectors of a row; with one or two the
+// up-front weight loads only delay the row's own loads (and cost occupancy),
+// so there the slice is loaded after the reduction instead.
+template <int WPR, int VPL, bool FUSED>
+constexpr bool weight_resident() { return VPL >= 3 && VPL <= (WPR == 16 ? 4 : 8) && (!FUSED || VPL <= 6); }
+// With a capped grid each workgroup walks several row groups; when the row
+// slice is small the next row's loads are issued before the current row is
+// reduced and stored, so memory stays busy across the reduction.
+template <int VPL, bool FUSED>
+constexpr bool row_pipelined() { return VPL * (FUSED ? 2 : 1) <= 4; }
+
 // WPR waves (64*WPR lanes) per row, VPL 16-byte vectors per lane.  Lane l of a
 // row owns vectors l, l + 64*WPR, ... so each load/store instruction of a wave
 // covers 1 KiB of contiguous memory.  MASKED: the row has fewer than
-// 64*WPR*VPL vectors; loads are clamped in bounds and zeroed, stores skipped.
+// 64*WPR*VPL vectors; loads are clamped in bounds (the extra values are
+// excluded from the sum) and stores skipped.
 template <class E, int WPR, int VPL, bool MASKED, bool FUSED>
 __global__ void __launch_bounds__(max_threads<WPR>()) rms_vec_kernel(const RowArgs a) {
     constexpr int LANES = 64 * WPR;
     constexpr int V = E::kVec;
+    constexpr int NR = FUSED ? VPL : 1;  // residual registers
+    constexpr bool WRES = weight_resident<WPR, VPL, FUSED>();
+    constexpr bool PIPE = row_pipelined<VPL, FUSED>();
     const int wave = wave_id();
     const int slot = wave / WPR;  // row within the workgroup
     const int lane_row = static_cast<int>(threadIdx.x) - slot * LANES;
     const int nvec = a.units;
+    const int64_t rpb = a.rows_per_block;
     __shared__ float part[2][16];
 
+    auto vidx = [&](int k) {
+        const int v = k * LANES + lane_row;
+        return MASKED ? (v < nvec ? v : nvec - 1) : v;
+    };
+    auto in_row = [&](int k) { return !MASKED || k * LANES + lane_row < nvec; };
+    auto load_row = [&](int64_t row, u32x4 (&xv)[VPL], u32x4 (&rv)[NR]) {
+        const u32x4* xr = static_cast<const u32x4*>(a.x) + row * nvec;
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) xv[k] = load_stream(xr + vidx(k));
+        if constexpr (FUSED) {
+            const u32x4* rr = static_cast<const u32x4*>(a.res) + row * nvec;
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) rv[k] = load_stream(rr + vidx(k));
+        }
+    };
+
+    const u32x4* wr = static_cast<const u32x4*>(a.w);
+    u32x4 wv[WRES ? VPL : 1];
+    if constexpr (WRES) {
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) wv[k] = load_keep(wr + vidx(k));
+    }
+
+    int64_t g = blockIdx.x;
+    u32x4 nx[PIPE ? VPL : 1], nr[PIPE ? NR : 1];  // prefetched next row
+    if constexpr (PIPE) {
+        if (g < a.n_groups && g * rpb + slot < a.rows) load_row(g * rpb + slot, nx, nr);
+    }
     int it = 0;
-    for (int64_t g = blockIdx.x; g < a.n_groups; g += gridDim.x, ++it) {
-        const int64_t row = g * a.rows_per_block + slot;
+    for (; g < a.n_groups; g += gridDim.x, ++it) {
+        const int64_t row = g * rpb + slot;
         const bool valid = row < a.rows;
-        const int64_t base = row * nvec;
-        u32x4 d[VPL];
+        u32x4 d[VPL], rv[NR];
+        if constexpr (PIPE) {
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) d[k] = nx[k];
+#pragma unroll
+            for (int k = 0; k < NR; ++k) rv[k] = nr[k];
+            const int64_t next = (g + gridDim.x) * rpb + slot;
+            if (g + gridDim.x < a.n_groups && next < a.rows) load_row(next, nx, nr);
+        } else {
+            if (valid) load_row(row, d, rv);
+        }
         float ss = 0.f;
         if (valid) {
-            const u32x4* xr = static_cast<const u32x4*>(a.x) + base;
-#pragma unroll
-            for (int k = 0; k < VPL; ++k) {
-                int v = k * LANES + lane_row;
-                if (MASKED) v = v < nvec ? v : nvec - 1;
-                d[k] = load_stream(xr + v);
-            }
             if constexpr (FUSED) {
-                const u32x4* rr = static_cast<const u32x4*>(a.res) + base;
-                u32x4* hr = static_cast<u32x4*>(a.h) + base;
+                u32x4* hr = static_cast<u32x4*>(a.h) + row * nvec;
 #pragma unroll
                 for (int k = 0; k < VPL; ++k) {
-                    int v = k * LANES + lane_row;
-                    const int vc = MASKED ? (v < nvec ? v : nvec - 1) : v;
-                    const u32x4 rv = load_stream(rr + vc);
                     float fx[V], fr[V];
                     widen(d[k], fx, E{});
-                    widen(rv, fr, E{});
+                    widen(rv[k], fr, E{});
 #pragma unroll
                     for (int i = 0; i < V; ++i) fx[i] += fr[i];
                     d[k] = narrow(fx, E{});  // h rounded once; the norm sees this value
-                    if (!MASKED || v < nvec) store_stream(hr + v, d[k]);
+                    if (in_row(k)) store_stream(hr + k * LANES + lane_row, d[k]);
                 }
             }
 #pragma unroll
@@ -194,8 +239,7 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_vec_kernel(const RowAr
                 float s = 0.f;
 #pragma unroll
                 for (int i = 0; i < V; ++i) s += f[i] * f[i];
-                if (MASKED && k * LANES + lane_row >= nvec) s = 0.f;
-                ss += s;
+                ss += in_row(k) ? s : 0.f;
             }
         }
         ss = wave_sum(ss);
@@ -208,18 +252,19 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_vec_kernel(const RowAr
         }
         if (valid) {
             const float r = rsqrtf(ss / a.hidden_f + a.eps);
-            const u32x4* wr = static_cast<const u32x4*>(a.w);
-            u32x4* outr = static_cast<u32x4*>(a.out) + base;
+            u32x4* outr = static_cast<u32x4*>(a.out) + row * nvec;
 #pragma unroll
             for (int k = 0; k < VPL; ++k) {
-                const int v = k * LANES + lane_row;
-                if (MASKED && v >= nvec) continue;
+                if (!in_row(k)) continue;
                 float f[V], fw[V];
                 widen(d[k], f, E{});
-                widen(load_keep(wr + v), fw, E{});
+                if constexpr (WRES)
+                    widen(wv[k], fw, E{});
+                else
+                    widen(load_keep(wr + k * LANES + lane_row), fw, E{});
 #pragma unroll
                 for (int i = 0; i < V; ++i) f[i] = f[i] * r * fw[i];
-                store_stream(outr + v, narrow(f, E{}));
+                store_stream(outr + k * LANES + lane_row, narrow(f, E{}));
             }
         }
     }

@@ -1,0 +1,163 @@
+"""Condense rocprofv3 CSV output into the short text summaries kept in profiles/.
+
+    python -m memory_bound_rmsnorm_amd.profile_summary stats --csv K_kernel_stats.csv \\
+        --workload bf16_16384x8192 --command "<the rocprofv3 command>"
+    python -m memory_bound_rmsnorm_amd.profile_summary pmc --fetch F_counter_collection.csv \\
+        --write W_counter_collection.csv --workload bf16_16384x8192 --command "<...>"
+
+`stats` lists per-kernel call counts and durations from --kernel-trace --stats
+and the bandwidth implied by the RMSNorm kernel's average duration.
+`pmc` averages FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the RMSNorm
+kernel and of the plain copy kernel run in the same process, scales the
+RMSNorm counters by the copy's known-bytes / counted-bytes ratio, and records
+the kernel-source digest so that bench.py quotes the traffic only while the
+kernels are unchanged.
+"""
+import argparse
+import csv
+import os
+import sys
+from collections import defaultdict
+
+from memory_bound_rmsnorm_amd import _build, inputs
+
+RMS_KERNEL_TAGS = ("rms_vec_kernel", "rms_elem_kernel", "rms_twopass_kernel")
+COPY_KERNEL_TAG = "hbm_copy_kernel"
+
+
+def _is_rms(name):
+    return any(t in name for t in RMS_KERNEL_TAGS)
+
+
+def stats(args):
+    w = inputs.WORKLOADS[args.workload]
+    with open(args.csv) as f:
+        rows = list(csv.DictReader(f))
+    out = ["# rocprofv3 --kernel-trace --stats summary: RMSNorm %s [%d, %d]%s"
+           % (w.dtype, w.rows, w.hidden, " fused residual" if w.fused else ""),
+           "# command: %s" % args.command,
+           "# algorithmic bytes per call: %d" % w.algorithmic_bytes,
+           "%-90s %6s %12s %12s %12s" % ("kernel", "calls", "avg_us", "min_us", "max_us")]
+    rms_avg = None
+    for r in rows:
+        name = r["Name"]
+        short = name if len(name) <= 90 else name[:87] + "..."
+        avg = float(r["AverageNs"]) / 1e3
+        out.append("%-90s %6s %12.3f %12.3f %12.3f" % (short, r["Calls"], avg, float(r["MinNs"]) / 1e3,
+                                                        float(r["MaxNs"]) / 1e3))
+        if _is_rms(name) and rms_avg is None:
+            rms_avg = avg
+    if rms_avg:
+        out.append("rmsnorm_kernel_avg_us: %.3f" % rms_avg)
+        out.append("rmsnorm_gbps_from_avg: %.1f" % (w.algorithmic_bytes / rms_avg / 1e3))
+        out.append("rmsnorm_frac_of_8TBps: %.4f" % (w.algorithmic_bytes / rms_avg / 1e3 / 8000.0))
+    print("\n".join(out))
+
+
+def _counter_means(path, counter):
+    per_kernel = defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") != counter:
+                continue
+            per_kernel[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in per_kernel.items()}, {k: len(v) for k, v in per_kernel.items()}
+
+
+def _pick(means, pred):
+    names = [k for k in means if pred(k)]
+    if not names:
+        raise SystemExit("no matching kernel in counter file")
+    return names[0], means[names[0]]
+
+
+def pmc(args):
+    w = inputs.WORKLOADS[args.workload]
+    fm, fn = _counter_means(args.fetch, "FETCH_SIZE")
+    wm, wn = _counter_means(args.write, "WRITE_SIZE")
+    rname, rfetch = _pick(fm, _is_rms)
+    _, rwrite = _pick(wm, _is_rms)
+    cname, cfetch = _pick(fm, lambda k: COPY_KERNEL_TAG in k)
+    _, cwrite = _pick(wm, lambda k: COPY_KERNEL_TAG in k)
+    copy_bytes = w.rows * w.hidden * w.elem_size * (2 if w.fused else 1)  # read == written per dispatch
+    fscale = copy_bytes / (cfetch * 1024.0)
+    wscale = copy_bytes / (cwrite * 1024.0)
+    read_alg = ((2 if w.fused else 1) * w.rows * w.hidden + w.hidden) * w.elem_size
+    write_alg = (2 if w.fused else 1) * w.rows * w.hidden * w.elem_size
+    traffic = rfetch * 1024 * fscale + rwrite * 1024 * wscale
+    out = ["# rocprofv3 --pmc summary: HBM traffic of RMSNorm %s [%d, %d]%s"
+           % (w.dtype, w.rows, w.hidden, " fused residual" if w.fused else ""),
+           "# fetch command: %s" % args.command_fetch,
+           "# write command: %s" % args.command_write,
+           "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch, averaged over dispatches; the copy kernel",
+           "# moves a known byte count in the same process and calibrates both counters.",
+           "rmsnorm_kernel: %s" % rname.replace(":", ";"),
+           "rmsnorm_dispatches_counted: %d" % fn[rname],
+           "rmsnorm_fetch_kib_per_dispatch: %.1f" % rfetch,
+           "rmsnorm_write_kib_per_dispatch: %.1f" % rwrite,
+           "copy_kernel: %s" % COPY_KERNEL_TAG,
+           "copy_bytes_read_and_written_per_dispatch: %d" % copy_bytes,
+           "copy_fetch_kib_per_dispatch: %.1f" % cfetch,
+           "copy_write_kib_per_dispatch: %.1f" % cwrite,
+           "copy_fetch_scale: %.5f" % fscale,
+           "copy_write_scale: %.5f" % wscale,
+           "algorithmic_read_bytes: %d" % read_alg,
+           "algorithmic_write_bytes: %d" % write_alg,
+           "scaled_read_bytes: %.0f" % (rfetch * 1024 * fscale),
+           "scaled_write_bytes: %.0f" % (rwrite * 1024 * wscale),
+           "traffic_bytes_per_launch: %.0f" % traffic,
+           "traffic_over_algorithmic: %.4f" % (traffic / w.algorithmic_bytes),
+           "source_sha256: %s" % _build.source_digest()]
+    print("\n".join(out))
+
+
+def resources(args):
+    """Compile-time register/scratch/occupancy report of the built kernels,
+    condensed: totals plus the kernels the stated workloads launch."""
+    import ctypes
+    import torch
+    import memory_bound_rmsnorm_amd as mbr
+    with open(_build.RESOURCE_USAGE) as f:
+        lines = [l.strip() for l in f if l.strip()]
+    spill = [l for l in lines if "| scratch 0 |" not in l or "VGPR spill 0" not in l or "SGPR spill 0" not in l]
+    out = ["# compile-time resource usage of librmsnorm.so (gfx950), from hipcc -Rpass-analysis=kernel-resource-usage",
+           "# command: %s" % args.command,
+           "kernels_built: %d" % len(lines),
+           "kernels_with_scratch_or_spills: %d" % len(spill)]
+    for name, w in inputs.WORKLOADS.items():
+        cfg = mbr.rmsnorm_select_config(w.rows, w.hidden, torch.float32 if w.dtype == "f32" else torch.bfloat16,
+                                        True, w.fused)
+        e = "F32" if w.dtype == "f32" else "Bf16"
+        fam = {1: "rms_vec_kernel", 2: "rms_elem_kernel", 3: "rms_twopass_kernel"}[cfg.path]
+        per = cfg.items_per_lane
+        units = w.hidden // (4 if w.dtype == "f32" else 8)
+        masked = 64 * cfg.waves_per_row * per != units
+        mangled = "%sINS_%d%sELi%dELi%dELb%dELb%dE" % (fam, len(e), e, cfg.waves_per_row, per, int(masked),
+                                                       int(w.fused))
+        hit = [l for l in lines if mangled in l]
+        out.append("%s -> %s | %s" % (name, cfg.as_dict(), hit[0].split("|", 1)[1].strip() if hit else "?"))
+    print("\n".join(out))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("--csv", required=True)
+    s.add_argument("--workload", default=inputs.HEADLINE)
+    s.add_argument("--command", required=True)
+    p = sub.add_parser("pmc")
+    p.add_argument("--fetch", required=True)
+    p.add_argument("--write", required=True)
+    p.add_argument("--workload", default=inputs.HEADLINE)
+    p.add_argument("--command-fetch", required=True)
+    p.add_argument("--command-write", required=True)
+    r = sub.add_parser("resources")
+    r.add_argument("--command", default="python -m memory_bound_rmsnorm_amd._build && "
+                                        "python -m memory_bound_rmsnorm_amd.profile_summary resources")
+    a = ap.parse_args(argv)
+    {"stats": stats, "pmc": pmc, "resources": resources}[a.cmd](a)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
