@@ -17,8 +17,10 @@ W untimed warm-up steps; then exactly K steps between a device synchronise and
 HIP events on the launch stream.  Parity of this launch configuration at this
 size with the CPU oracle is the job of the GPU test suite, not of this script.
 
-Prints ONE JSON line on stdout.  With --all, one JSON record per workload is
-also written to stderr (lines starting with '#').
+Prints ONE JSON line on stdout.  With --all, one JSON record per other
+workload is written to stderr (lines starting with '#'); those also carry the
+per-launch time with the launches replayed from a HIP graph, since the small
+workloads finish faster than Python can issue them.
 """
 import argparse
 import concurrent.futures
@@ -121,6 +123,28 @@ def time_steps(fn, steps, warmup):
     return wall, start.elapsed_time(end) / 1e3
 
 
+def graph_time(fn, n_sets, replays=10):
+    """Per-launch time with the launches captured once in a HIP graph and
+    replayed, which removes Python and launch-call overhead from the GPU
+    timeline (the kernels allocate nothing and memset nothing, so they capture
+    cleanly)."""
+    launches = min(4096, max(64, n_sets))  # one pass over every rotation set
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(launches):
+            fn(i % n_sets)
+    g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(replays):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3 / (launches * replays)
+
+
 def copy_ceiling(w, steps, warmup):
     """hbm_copy of the same read/write byte count as one step, rotated the same way."""
     nbytes = w.rows * w.hidden * w.elem_size * (2 if w.fused else 1)
@@ -196,7 +220,7 @@ def cpu_baseline(w, t, seconds):
                       % (rows, w.rows, reps, el, T, cpu_model())}
 
 
-def bench_workload(w, steps, warmup, seed, with_copy=True):
+def bench_workload(w, steps, warmup, seed, with_copy=True, graph=False):
     t = inputs.make(w, seed=seed)
     n_sets = n_sets_for(w)
     sets = Sets(w, t, n_sets)
@@ -212,6 +236,10 @@ def bench_workload(w, steps, warmup, seed, with_copy=True):
         "gbps_wall": nbytes * steps / wall / 1e9, "gbps_kernel": nbytes / kern_s / 1e9,
         "kernel_config": cfg.as_dict(),
     }
+    if graph:
+        gs = graph_time(sets.launch, n_sets)
+        rec["us_per_call_graph"] = gs * 1e6
+        rec["gbps_graph"] = nbytes / gs / 1e9
     if with_copy:
         cc = copy_ceiling(w, max(20, steps // 2), max(2, warmup // 2))
         rec["copy_ceiling_gbps"] = cc
@@ -271,7 +299,7 @@ def main():
         for name, other in inputs.WORKLOADS.items():
             if name == w.name:
                 continue
-            _, r = bench_workload(other, args.steps, args.warmup, args.seed)
+            _, r = bench_workload(other, args.steps, args.warmup, args.seed, graph=True)
             log("# workload:", json.dumps(r))
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(w, t, args.cpu_seconds)

@@ -376,6 +376,38 @@ def test_pages_rmsnorm_test_case_on_gpu():
         assert err <= tol
 
 
+@pytest.mark.parametrize("fused", [False, True])
+def test_graph_capture_replays_match_eager(fused):
+    """Both entry points captured in a HIP graph: every replay, with eager work
+    and synchronisations in between, equals the eager result bitwise."""
+    w = inputs.custom(3000, 5120, "bf16", fused)
+    t = {k: v.cuda() for k, v in inputs.make(w, seed=17).items()}
+    x, wt = t["x"], t["weight"]
+    if fused:
+        h_e, y_e = run_fused(x, t["residual"], wt, 1e-5)
+    else:
+        y_e = run_plain(x, wt, 1e-5)
+    h_g = torch.empty_like(x)
+    y_g = torch.empty_like(x)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        if fused:
+            mbr.rmsnorm_residual_fwd(x, t["residual"], wt, h_g, y_g, 1e-5)
+        else:
+            mbr.rmsnorm_fwd(x, wt, y_g, 1e-5)
+    for rep in range(3):
+        y_g.zero_()
+        h_g.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_g, y_e), "replay %d differs" % rep
+        if fused:
+            assert torch.equal(h_g, h_e), "replay %d differs (h)" % rep
+        # eager work between replays
+        run_plain(x, wt, 1e-5)
+
+
 def test_hbm_copy_copies():
     src = torch.randint(0, 255, (3 * (1 << 20) + 13,), dtype=torch.uint8, device="cuda")
     dst = torch.zeros_like(src)
