@@ -162,7 +162,7 @@ KERNEL_FAMILY = {"vector": "rms_vec_kernel", "element": "rms_elem_kernel", "two_
 
 def load_traffic(w, launch):
     """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel sources; else None."""
+    on the current kernel sources in the current launch configuration; else None."""
     path = os.path.join(PROFILE_DIR, "pmc_traffic_%s_%s.txt" % (KERNEL_FAMILY[launch["path"]], w.name))
     if not os.path.exists(path):
         return None
@@ -175,6 +175,8 @@ def load_traffic(w, launch):
                 vals[k.strip()] = v.strip()
     try:
         if vals.get("source_sha256") != _build.source_digest():
+            return None
+        if vals.get("launch_config") != " ".join("%s=%s" % kv for kv in launch.items()):
             return None
         fetch = float(vals["rmsnorm_fetch_kib_per_dispatch"]) * 1024 * float(vals["copy_fetch_scale"])
         write = float(vals["rmsnorm_write_kib_per_dispatch"]) * 1024 * float(vals["copy_write_scale"])

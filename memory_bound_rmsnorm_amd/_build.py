@@ -104,18 +104,23 @@ def build(verbose: bool = False) -> None:
 
 
 
+KERNEL_SOURCES = ["rmsnorm_kernels.hpp", "rmsnorm_dispatch.hpp", "rmsnorm_vec_bf16.hip", "rmsnorm_vec_f32.hip",
+                  "rmsnorm_misc.hip", "hbm_copy.hip"]
+
+
 def source_digest() -> str:
-    """sha256 over the HIP sources and headers that make up the kernels, so
-    that counter readings taken on one version are not quoted for another."""
+    """sha256 over the kernel sources (device code and its instantiation
+    tables, plus the copy kernel that calibrates the counters), so that counter
+    readings taken on one version of the kernels are not quoted for another.
+    Host-side selection is checked separately through the launch configuration
+    recorded next to the counters."""
     import hashlib
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".hpp")):
-            h.update(name.encode())
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(f.read())
+    for name in KERNEL_SOURCES:
+        h.update(name.encode())
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
-
 
 if __name__ == "__main__":
     build(verbose=True)

@@ -99,9 +99,10 @@ bool vector_aligned(const Problem& p) {
 
 // The automatic choice, from launch-shape sweeps on MI355X.  Vector path:
 // spread a row over the fewest waves (one row per workgroup) that keep at most
-// two 16-byte vectors of it per lane -- many short waves keep more requests in
+// two 16-byte vectors of it per lane (three for the fused form, whose lanes
+// then keep the weight resident) -- many short waves keep more requests in
 // flight than a few long ones; e.g. bf16 hidden 8192 runs as 8 waves x 2
-// vectors.  Element path: at most 8 elements per lane.  When rows are few,
+// vectors, the fused bf16 hidden 5120 as 4 waves x 3.  Element path: at most 8 elements per lane.  When rows are few,
 // each row gets more waves so the whole GPU has work.  Rows that no built
 // register-resident configuration covers take the two-pass path.
 rmsnorm_config_t choose(int64_t rows, int64_t hidden, int dtype, bool aligned, bool fused) {
@@ -110,7 +111,7 @@ rmsnorm_config_t choose(int64_t rows, int64_t hidden, int dtype, bool aligned, b
     const int64_t units = vec ? hidden / vec_elems(dtype) : hidden;
     const int* list = vec ? mbr::kVplList : mbr::kEplList;
     const int nlist = vec ? mbr::kNumVpl : mbr::kNumEpl;
-    const int cap = vec ? 2 : 8;
+    const int cap = vec ? (fused ? 3 : 2) : 8;
     auto fit = [&](int wpr) {
         const int per = round_up_in(list, nlist, ceil_div(units, int64_t(64) * wpr));
         if (per < 0) return -1;

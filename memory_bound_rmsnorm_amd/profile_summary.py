@@ -107,8 +107,17 @@ def pmc(args):
            "scaled_write_bytes: %.0f" % (rwrite * 1024 * wscale),
            "traffic_bytes_per_launch: %.0f" % traffic,
            "traffic_over_algorithmic: %.4f" % (traffic / w.algorithmic_bytes),
+           "launch_config: %s" % _launch_config(w),
            "source_sha256: %s" % _build.source_digest()]
     print("\n".join(out))
+
+
+def _launch_config(w):
+    import torch
+    import memory_bound_rmsnorm_amd as mbr
+    cfg = mbr.rmsnorm_select_config(w.rows, w.hidden, torch.float32 if w.dtype == "f32" else torch.bfloat16,
+                                    True, w.fused)
+    return " ".join("%s=%s" % kv for kv in cfg.as_dict().items())
 
 
 def resources(args):
