@@ -43,6 +43,10 @@ def _load():
         lib.oracle_round_bf16.restype = ctypes.c_uint16
         lib.oracle_round_f32.argtypes = [ctypes.c_double]
         lib.oracle_round_f32.restype = ctypes.c_float
+        lib.oracle_round_e4m3.argtypes = [ctypes.c_double]
+        lib.oracle_round_e4m3.restype = ctypes.c_uint8
+        lib.oracle_rmsnorm_dynamic_quant_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, i32]
+        lib.oracle_rmsnorm_dynamic_quant_fwd.restype = i32
         _lib = lib
     return _lib
 
@@ -94,6 +98,42 @@ def rmsnorm_residual_fwd(x: np.ndarray, residual: np.ndarray, weight: np.ndarray
     if rc != 0:
         raise RuntimeError("oracle_rmsnorm_residual_fwd failed")
     return h, y
+
+
+QUANT_INT8 = 0
+QUANT_FP8_E4M3 = 1
+
+
+def rmsnorm_dynamic_quant_fwd(x: np.ndarray, weight: np.ndarray, eps: float, qtype: int,
+                              residual: np.ndarray = None):
+    """Returns ``(h, q, scale)``: h = round(x + residual) (None without a
+    residual), q the int8 codes (``np.int8``) or e4m3fn codes (``np.uint8``) of
+    the RMSNorm output quantised per row, scale the per-row float32 scales."""
+    x = _check(x, "x")
+    weight = np.ascontiguousarray(weight).reshape(-1)
+    code = _dtype_code(x)
+    if weight.dtype != x.dtype or weight.shape[0] != x.shape[1]:
+        raise ValueError("weight must be [hidden] with the dtype of x")
+    h = None
+    if residual is not None:
+        residual = _check(residual, "residual")
+        if residual.dtype != x.dtype or residual.shape != x.shape:
+            raise ValueError("residual must match x")
+        h = np.empty_like(x)
+    q = np.empty(x.shape, dtype=np.int8 if qtype == QUANT_INT8 else np.uint8)
+    scale = np.empty(x.shape[0], dtype=np.float32)
+    rc = _load().oracle_rmsnorm_dynamic_quant_fwd(
+        x.ctypes.data, residual.ctypes.data if residual is not None else None, weight.ctypes.data,
+        h.ctypes.data if h is not None else None, q.ctypes.data, scale.ctypes.data,
+        x.shape[0], x.shape[1], float(eps), code, int(qtype))
+    if rc != 0:
+        raise RuntimeError("oracle_rmsnorm_dynamic_quant_fwd failed")
+    return h, q, scale
+
+
+def round_e4m3(v: float) -> int:
+    """Nearest-even fp8 e4m3fn code of a Python float, saturating at 448."""
+    return int(_load().oracle_round_e4m3(float(v)))
 
 
 def round_bf16(v: float) -> int:

@@ -45,6 +45,8 @@
 
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
+#define ORACLE_QUANT_INT8 0
+#define ORACLE_QUANT_FP8_E4M3 1
 
 /* Exact widening of one stored element to double. */
 static double load_elem(const void *base, int64_t i, int dtype) {
@@ -92,6 +94,37 @@ uint16_t oracle_round_bf16(double v) {
     f = (float)m;                 /* exact: m has at most 8 significant bits */
     memcpy(&u, &f, 4);
     return (uint16_t)(sign | (uint16_t)((u >> 16) & 0x7FFFu));
+}
+
+/*
+ * Round a double to fp8 e4m3fn (1 sign bit, 4 exponent bits with bias 7, 3
+ * mantissa bits, no infinities, largest finite value 448), nearest-even, with
+ * finite values beyond 448 saturating to +-448.  Same construction as the bf16
+ * rounding: spacing 2^(E-3) for |v| in [2^E, 2^(E+1)), 2^-9 below the
+ * smallest normal 2^-6.  Returns the 8-bit code (sign in bit 7).
+ */
+uint8_t oracle_round_e4m3(double v) {
+    uint8_t sign = signbit(v) ? 0x80u : 0u;
+    double a, spacing, m;
+    int e2, code;
+    if (isnan(v)) return (uint8_t)(sign | 0x7Fu);
+    a = fabs(v);
+    if (a == 0.0) return sign;
+    if (isinf(a)) a = 448.0;
+    (void)frexp(a, &e2);
+    e2 -= 1;
+    if (e2 < -6) e2 = -6;
+    spacing = ldexp(1.0, e2 - 3);
+    m = nearbyint(a / spacing) * spacing;
+    if (m > 448.0) m = 448.0;
+    if (m < ldexp(1.0, -6)) {
+        code = (int)(m * 512.0);            /* subnormal: m = code * 2^-9 */
+    } else {
+        (void)frexp(m, &e2);                /* m = f * 2^e2, f in [0.5, 1) */
+        e2 -= 1;                            /* m in [2^e2, 2^(e2+1)) */
+        code = ((e2 + 7) << 3) | (int)(ldexp(m, -e2) * 8.0 - 8.0);
+    }
+    return (uint8_t)(sign | code);
 }
 
 /* Round a double to float32, nearest-even (the C conversion under the default
@@ -161,5 +194,73 @@ int oracle_rmsnorm_residual_fwd(const void *x, const void *residual, const void 
         normalise_row(v, w, out, i * hidden, hidden, eps, dtype);
     }
     free(v);
+    return 0;
+}
+
+/*
+ * Dynamic per-row (per-token) symmetric quantisation of the RMSNorm output,
+ * optionally after the residual add -- the Add + RmsNorm + DynamicQuant fusion
+ * named in the TileLang tutorial ch. 02, section 4.2 (CANN
+ * aclnnAddRmsNormDynamicQuant).  The pages give no formula for DynamicQuant;
+ * the reading taken is the plain per-token absmax scheme:
+ *
+ *   y_j     = v_j * r * w_j               (fp64, never rounded to the dtype)
+ *   scale   = max_j |y_j| / Q             (Q = 127 for int8, 448 for e4m3fn)
+ *   q_j     = round(y_j / scale)          (nearest-even; int8 clamped to
+ *                                          [-127, 127], e4m3fn saturating)
+ *
+ * and a row whose y is all zero gets scale 0 and codes 0.  v is x, or the
+ * rounded h = x + residual when residual is given (h is then written to
+ * h_out as in oracle_rmsnorm_residual_fwd).  scale_out receives the scale
+ * rounded to float32; the codes use the fp64 scale.
+ */
+int oracle_rmsnorm_dynamic_quant_fwd(const void *x, const void *residual, const void *w, void *h_out,
+                                     void *q_out, float *scale_out, int64_t rows, int64_t hidden,
+                                     float eps, int dtype, int qtype) {
+    double *v, *y;
+    int64_t i, j;
+    if (rows < 0 || hidden <= 0 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16)) return -1;
+    if (qtype != ORACLE_QUANT_INT8 && qtype != ORACLE_QUANT_FP8_E4M3) return -1;
+    if ((residual == NULL) != (h_out == NULL)) return -1;
+    v = (double *)malloc(sizeof(double) * (size_t)hidden);
+    y = (double *)malloc(sizeof(double) * (size_t)hidden);
+    if (!v || !y) {
+        free(v);
+        free(y);
+        return -1;
+    }
+    for (i = 0; i < rows; ++i) {
+        double s = 0.0, r, amax = 0.0, scale, qmax = qtype == ORACLE_QUANT_INT8 ? 127.0 : 448.0;
+        for (j = 0; j < hidden; ++j) {
+            int64_t k = i * hidden + j;
+            if (residual) {
+                store_elem(h_out, k, load_elem(x, k, dtype) + load_elem(residual, k, dtype), dtype);
+                v[j] = load_elem(h_out, k, dtype);
+            } else {
+                v[j] = load_elem(x, k, dtype);
+            }
+        }
+        for (j = 0; j < hidden; ++j) s += v[j] * v[j];
+        r = 1.0 / sqrt(s / (double)hidden + (double)eps);
+        for (j = 0; j < hidden; ++j) {
+            y[j] = v[j] * r * load_elem(w, j, dtype);
+            if (fabs(y[j]) > amax) amax = fabs(y[j]);
+        }
+        scale = amax / qmax;
+        scale_out[i] = (float)scale;
+        for (j = 0; j < hidden; ++j) {
+            double t = amax > 0.0 ? y[j] / scale : 0.0;
+            if (qtype == ORACLE_QUANT_INT8) {
+                double c = nearbyint(t);
+                if (c > 127.0) c = 127.0;
+                if (c < -127.0) c = -127.0;
+                ((int8_t *)q_out)[i * hidden + j] = (int8_t)c;
+            } else {
+                ((uint8_t *)q_out)[i * hidden + j] = oracle_round_e4m3(t);
+            }
+        }
+    }
+    free(v);
+    free(y);
     return 0;
 }

@@ -86,3 +86,47 @@ def rmsnorm_decimal(v, w, eps32: float):
     s = sum(a * a for a in dv)
     r = 1 / (s / len(dv) + de).sqrt()
     return [a * r * b for a, b in zip(dv, dw)]
+
+
+def e4m3_value(code: int) -> Fraction:
+    """Exact value of an fp8 e4m3fn code (1 sign, 4 exponent bits bias 7, 3
+    mantissa bits; 0x7F / 0xFF are NaN and not valid here)."""
+    sign = -1 if code & 0x80 else 1
+    e = (code >> 3) & 0xF
+    m = code & 7
+    if e == 0:
+        return sign * Fraction(m, 8) * Fraction(1, 64)
+    return sign * (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+
+
+def round_e4m3_exact(q) -> int:
+    """Nearest-even e4m3fn code of an exact rational, saturating at +-448."""
+    q = Fraction(q)
+    neg = q < 0
+    a = -q if neg else q
+    if a >= 448:
+        p = 0x7E
+    else:
+        lo, hi = 0, 0x7E  # value(lo) <= a < value(hi)
+        while hi - lo > 1:
+            mid = (lo + hi) // 2
+            if e4m3_value(mid) <= a:
+                lo = mid
+            else:
+                hi = mid
+        p = lo
+        if e4m3_value(p) != a:
+            mid_val = (e4m3_value(p) + e4m3_value(p + 1)) / 2
+            if a > mid_val or (a == mid_val and (p & 1)):
+                p += 1
+    return (0x80 if neg else 0) | p
+
+
+def round_half_even(q) -> int:
+    """Nearest integer to an exact rational, ties to even."""
+    q = Fraction(q)
+    fl = q.numerator // q.denominator
+    frac = q - fl
+    if frac > Fraction(1, 2) or (frac == Fraction(1, 2) and fl % 2):
+        return fl + 1
+    return fl

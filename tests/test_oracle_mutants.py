@@ -14,6 +14,7 @@ import pytest
 import oracle
 from oracle import build as oracle_build
 from tests import test_oracle_pins as pins
+from tests import test_oracle_quant_pins as qpins
 
 MUTANTS = [
     ("eps dropped", "sqrt(mean + (double)eps)", "sqrt(mean)"),
@@ -39,6 +40,24 @@ MUTANTS = [
      "* load_elem(w, j, dtype), dtype);"),
 ]
 
+MUTANTS += [
+    ("int8 full scale 128", "qtype == ORACLE_QUANT_INT8 ? 127.0 : 448.0", "qtype == ORACLE_QUANT_INT8 ? 128.0 : 448.0"),
+    ("fp8 full scale 240", "qtype == ORACLE_QUANT_INT8 ? 127.0 : 448.0", "qtype == ORACLE_QUANT_INT8 ? 127.0 : 240.0"),
+    ("truncating quantisation", "double c = nearbyint(t);", "double c = trunc(t);"),
+    ("codes from the unscaled output", "double t = amax > 0.0 ? y[j] / scale : 0.0;",
+     "double t = amax > 0.0 ? y[j] * 100.0 : 0.0;"),
+    ("scale not divided by the full scale", "scale = amax / qmax;\n        scale_out[i] = (float)scale;",
+     "scale = amax / qmax;\n        scale_out[i] = (float)amax;"),
+    ("quantising the bf16-rounded output", "y[j] = v[j] * r * load_elem(w, j, dtype);",
+     "y[j] = (double)oracle_bf16_back(oracle_round_bf16(v[j] * r * load_elem(w, j, dtype)));"),
+    ("residual ignored by the quantiser", "            if (residual) {\n                store_elem(h_out, k, load_elem(x, k, dtype) + load_elem(residual, k, dtype), dtype);",
+     "            if (residual) {\n                store_elem(h_out, k, load_elem(x, k, dtype), dtype);"),
+    ("fp8 exponent bias 8", "code = ((e2 + 7) << 3)", "code = ((e2 + 8) << 3)"),
+    ("fp8 subnormal spacing wrong", "if (e2 < -6) e2 = -6;", "if (e2 < -7) e2 = -7;"),
+    ("fp8 ties away from zero", "m = nearbyint(a / spacing) * spacing;\n    if (m > 448.0) m = 448.0;",
+     "m = round(a / spacing) * spacing;\n    if (m > 448.0) m = 448.0;"),
+]
+
 HELPER = """
 static float oracle_bf16_back(uint16_t b) { uint32_t u = (uint32_t)b << 16; float f; memcpy(&f, &u, 4); return f; }
 """
@@ -60,6 +79,15 @@ PIN_TESTS = [
     (pins.test_residual_sum_rounded_once, dict(dtype="bf16")),
     (pins.test_residual_normalises_the_rounded_sum, {}),
     (pins.test_residual_special_cases_reduce_to_plain, {}),
+    (qpins.test_e4m3_rounding_matches_exact_rational, {}),
+    (qpins.test_e4m3_ties_go_to_even, {}),
+    (qpins.test_hand_worked_codes, dict(qtype=0)),
+    (qpins.test_hand_worked_codes, dict(qtype=1)),
+    (qpins.test_codes_are_the_exact_rational_closed_form, dict(qtype=0, dtype="bf16")),
+    (qpins.test_codes_are_the_exact_rational_closed_form, dict(qtype=1, dtype="bf16")),
+    (qpins.test_scale_closed_form_constant_row, dict(qtype=0)),
+    (qpins.test_row_max_maps_to_full_scale_and_zero_row, dict(qtype=1)),
+    (qpins.test_fused_quant_uses_the_rounded_sum, dict(qtype=0)),
 ]
 
 
