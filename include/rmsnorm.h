@@ -164,6 +164,66 @@ RMSNORM_API rmsnorm_status_t rmsnorm_residual_fwd_ex(const void* x, const void* 
                                                      float eps, rmsnorm_dtype_t dtype,
                                                      const rmsnorm_config_t* cfg, void* stream);
 
+/* ------------------------------------------------------------------------
+ * RMSNorm with dynamic per-row quantisation of its output.
+ * ---------------------------------------------------------------------- */
+
+typedef enum {
+    RMSNORM_QUANT_INT8 = 0,     /* signed 8-bit codes in [-127, 127], Q = 127 */
+    RMSNORM_QUANT_FP8_E4M3 = 1  /* OCP fp8 e4m3fn codes (bias 7, max 448, no inf), Q = 448 */
+} rmsnorm_quant_t;
+
+/*
+ * rmsnorm_dynamic_quant_fwd: (residual add +) RMSNorm + per-row symmetric
+ * dynamic quantisation, one pass over the rows -- the Add + RmsNorm +
+ * DynamicQuant fusion the TileLang tutorial ch. 02, section 4.2, cites from
+ * CANN (aclnnAddRmsNormDynamicQuant) as a way to cut data movement.  The pages
+ * give no quantiser formula; this library implements the plain per-token one:
+ *
+ *   v         = x, or h = round(x + residual) (written to residual_out)
+ *   y_j       = v_j * rsqrt(sum_k v_k^2 / hidden + eps) * weight_j   (fp32, never rounded)
+ *   scale_out[i] = max_j |y_j| / Q
+ *   q_out[i, j]  = round(y_j / scale_out[i])   nearest-even; int8 clamped to
+ *                                              [-127, 127], fp8 saturating at +-448
+ *
+ * A row with max_j |y_j| == 0 gets scale 0 and all-zero codes.  The root
+ * cancels from y_j / scale, so the codes are evaluated as
+ * (v_j * weight_j) * (Q / max_k |v_k * weight_k|); they can differ from a
+ * higher-precision evaluation only where y_j / scale lies within float32
+ * rounding of a tie between two codes.
+ *
+ *   x, weight      as rmsnorm_fwd (dtype bf16 or f32).
+ *   residual       [rows, hidden] or NULL (no add); residual_out is NULL exactly
+ *                  when residual is; it may alias x or residual exactly.
+ *   q_out          [rows, hidden] bytes: int8 or e4m3fn codes, row-major.
+ *   scale_out      [rows] float32, 4-byte aligned.
+ *   qtype          rmsnorm_quant_t; anything else -> RMSNORM_ERR_UNSUPPORTED_DTYPE.
+ * q_out and scale_out may not overlap any other buffer or each other.  The
+ * 16-byte vector path additionally needs q_out 16-byte aligned.  Other rules
+ * and errors as rmsnorm_fwd.
+ */
+RMSNORM_API rmsnorm_status_t rmsnorm_dynamic_quant_fwd(const void* x, const void* residual,
+                                                      const void* weight, void* residual_out,
+                                                      void* q_out, float* scale_out, int64_t rows,
+                                                      int64_t hidden, float eps, rmsnorm_dtype_t dtype,
+                                                      rmsnorm_quant_t qtype, void* stream);
+
+/* As rmsnorm_dynamic_quant_fwd with an explicit launch configuration; the
+ * quantised kernels are built for at most 8 vectors (or elements) per lane,
+ * 4 with 16 waves per row. */
+RMSNORM_API rmsnorm_status_t rmsnorm_dynamic_quant_fwd_ex(const void* x, const void* residual,
+                                                         const void* weight, void* residual_out,
+                                                         void* q_out, float* scale_out, int64_t rows,
+                                                         int64_t hidden, float eps,
+                                                         rmsnorm_dtype_t dtype, rmsnorm_quant_t qtype,
+                                                         const rmsnorm_config_t* cfg, void* stream);
+
+/* The configuration rmsnorm_dynamic_quant_fwd would use (as rmsnorm_select_config). */
+RMSNORM_API rmsnorm_status_t rmsnorm_select_quant_config(int64_t rows, int64_t hidden,
+                                                         rmsnorm_dtype_t dtype,
+                                                         int32_t vector_aligned, int32_t fused,
+                                                         rmsnorm_config_t* cfg);
+
 #ifdef __cplusplus
 }
 #endif

@@ -10,6 +10,9 @@ fallback -- if the library is not built, every call raises.
     rmsnorm_residual_fwd(x, residual, weight, residual_out, out, eps) -> (residual_out, out)
     rmsnorm_fwd_ex / rmsnorm_residual_fwd_ex(..., config)      forced launch configuration
     rmsnorm_select_config(rows, hidden, dtype, vector_aligned, fused) -> Config
+    rmsnorm_dynamic_quant_fwd(x, weight, q_out, scale_out, eps, qtype, residual, residual_out)
+    rmsnorm_dynamic_quant_fwd_ex(..., config)                   forced launch configuration
+    rmsnorm_select_quant_config(rows, hidden, dtype, vector_aligned, fused) -> Config
     rmsnorm_status_string(status)                              -> str
 """
 import ctypes
@@ -29,6 +32,9 @@ RMSNORM_ERR_RUNTIME = 3
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
+
+QUANT_INT8 = 0
+QUANT_FP8_E4M3 = 1
 
 PATH_AUTO = 0
 PATH_VECTOR = 1
@@ -77,10 +83,14 @@ def lib() -> ctypes.CDLL:
         L.rmsnorm_fwd_ex.argtypes = [vp, vp, vp, i64, i64, f32, i32, cfgp, vp]
         L.rmsnorm_residual_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, i32, cfgp, vp]
         L.rmsnorm_select_config.argtypes = [i64, i64, i32, i32, i32, cfgp]
+        L.rmsnorm_select_quant_config.argtypes = [i64, i64, i32, i32, i32, cfgp]
+        L.rmsnorm_dynamic_quant_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
+        L.rmsnorm_dynamic_quant_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, cfgp, vp]
         L.rmsnorm_status_string.argtypes = [i32]
         L.rmsnorm_status_string.restype = ctypes.c_char_p
         for fn in (L.rmsnorm_fwd, L.rmsnorm_residual_fwd, L.rmsnorm_fwd_ex, L.rmsnorm_residual_fwd_ex,
-                   L.rmsnorm_select_config):
+                   L.rmsnorm_select_config, L.rmsnorm_select_quant_config, L.rmsnorm_dynamic_quant_fwd,
+                   L.rmsnorm_dynamic_quant_fwd_ex):
             fn.restype = i32
         _lib = L
     return _lib
@@ -195,6 +205,51 @@ def rmsnorm_select_config(rows: int, hidden: int, dtype, vector_aligned: bool = 
     cfg = Config()
     _check(lib().rmsnorm_select_config(int(rows), int(hidden), code, int(bool(vector_aligned)),
                                        int(bool(fused)), ctypes.byref(cfg)), "rmsnorm_select_config")
+    return cfg
+
+
+def rmsnorm_dynamic_quant_fwd_ex(x, weight, q_out, scale_out, eps: float = 1e-5, qtype: int = QUANT_INT8,
+                                 residual=None, residual_out=None, config: Optional[Config] = None, stream=None):
+    """(residual add +) RMSNorm + per-row dynamic quantisation with a forced
+    configuration.  q_out: one-byte tensor shaped like x (int8, uint8 or an
+    fp8 dtype); scale_out: float32 tensor with one element per row."""
+    for t, n in ((x, "x"), (weight, "weight"), (q_out, "q_out"), (scale_out, "scale_out")):
+        _device_tensor(t, n)
+    if (residual is None) != (residual_out is None):
+        raise ValueError("residual and residual_out go together")
+    if residual is not None:
+        for t, n in ((residual, "residual"), (residual_out, "residual_out")):
+            _device_tensor(t, n)
+            if t.shape != x.shape or t.dtype != x.dtype:
+                raise ValueError("%s must match x in shape and dtype" % n)
+    if weight.dtype != x.dtype:
+        raise ValueError("weight must match x in dtype")
+    rows, hidden = _shape(x, weight)
+    if q_out.shape != x.shape or q_out.element_size() != 1:
+        raise ValueError("q_out must be a one-byte tensor shaped like x")
+    if scale_out.dtype != torch.float32 or scale_out.numel() != rows:
+        raise ValueError("scale_out must be float32 with one element per row")
+    st = lib().rmsnorm_dynamic_quant_fwd_ex(
+        x.data_ptr(), residual.data_ptr() if residual is not None else None, weight.data_ptr(),
+        residual_out.data_ptr() if residual_out is not None else None, q_out.data_ptr(), scale_out.data_ptr(),
+        rows, hidden, float(eps), dtype_code(x.dtype), int(qtype),
+        ctypes.byref(config) if config is not None else None, _stream(stream, x.device))
+    _check(st, "rmsnorm_dynamic_quant_fwd")
+    return q_out, scale_out
+
+
+def rmsnorm_dynamic_quant_fwd(x, weight, q_out, scale_out, eps: float = 1e-5, qtype: int = QUANT_INT8,
+                              residual=None, residual_out=None, stream=None):
+    """(residual add +) RMSNorm + per-row dynamic quantisation (C: rmsnorm_dynamic_quant_fwd)."""
+    return rmsnorm_dynamic_quant_fwd_ex(x, weight, q_out, scale_out, eps, qtype, residual, residual_out, None, stream)
+
+
+def rmsnorm_select_quant_config(rows: int, hidden: int, dtype, vector_aligned: bool = True,
+                                fused: bool = False) -> Config:
+    code = dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype)
+    cfg = Config()
+    _check(lib().rmsnorm_select_quant_config(int(rows), int(hidden), code, int(bool(vector_aligned)),
+                                             int(bool(fused)), ctypes.byref(cfg)), "rmsnorm_select_quant_config")
     return cfg
 
 

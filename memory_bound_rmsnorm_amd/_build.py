@@ -22,7 +22,8 @@ LIB_RMSNORM = os.path.join(HERE, "librmsnorm.so")
 LIB_COPY = os.path.join(HERE, "libhbm_copy.so")
 RESOURCE_USAGE = os.path.join(BUILD, "resource_usage.txt")
 
-RMSNORM_SOURCES = ["rmsnorm_api.hip", "rmsnorm_misc.hip", "rmsnorm_vec_bf16.hip", "rmsnorm_vec_f32.hip"]
+RMSNORM_SOURCES = ["rmsnorm_api.hip", "rmsnorm_misc.hip", "rmsnorm_vec_bf16.hip", "rmsnorm_vec_f32.hip",
+                   "rmsnorm_quant_bf16.hip", "rmsnorm_quant_f32.hip", "rmsnorm_quant_misc.hip"]
 COPY_SOURCES = ["hbm_copy.hip"]
 
 # Packed-fp32 VALU forms are disabled: hipcc emits them from plain float code
@@ -105,7 +106,8 @@ def build(verbose: bool = False) -> None:
 
 
 KERNEL_SOURCES = ["rmsnorm_kernels.hpp", "rmsnorm_dispatch.hpp", "rmsnorm_vec_bf16.hip", "rmsnorm_vec_f32.hip",
-                  "rmsnorm_misc.hip", "hbm_copy.hip"]
+                  "rmsnorm_misc.hip", "rmsnorm_quant_bf16.hip", "rmsnorm_quant_f32.hip", "rmsnorm_quant_misc.hip",
+                  "hbm_copy.hip"]
 
 
 def source_digest() -> str:

@@ -32,6 +32,8 @@ struct Problem {
     float eps;
     int dtype;  // 0 f32, 1 bf16
     bool fused;
+    int qt;        // 0: normalised output; 1: int8 codes; 2: fp8 e4m3fn codes
+    float* scale;  // quantised forms: per-row scales
 };
 
 int elem_size(int dtype) { return dtype == RMSNORM_DTYPE_F32 ? 4 : 2; }
@@ -72,11 +74,30 @@ rmsnorm_status_t validate_pointers(const Problem& p) {
     const int es = elem_size(p.dtype);
     if (!p.x || !p.w || !p.out) return RMSNORM_ERR_INVALID_ARG;
     if (p.fused && (!p.res || !p.h)) return RMSNORM_ERR_INVALID_ARG;
-    const void* ptrs[] = {p.x, p.w, p.out, p.res, p.h};
+    const void* ptrs[] = {p.x, p.w, p.res, p.h};
     for (const void* q : ptrs)
         if (q && reinterpret_cast<uintptr_t>(q) % es != 0) return RMSNORM_ERR_INVALID_ARG;
     const int64_t nb = p.rows * p.hidden * es;  // no overflow: checked in validate_sizes
     const int64_t wb = p.hidden * es;
+    if (p.qt != 0) {
+        // codes (one byte per element) and scales touch nothing else at all
+        const int64_t qb = p.rows * p.hidden, sb = p.rows * 4;
+        if (!p.scale || reinterpret_cast<uintptr_t>(p.scale) % 4 != 0) return RMSNORM_ERR_INVALID_ARG;
+        const void* others[] = {p.x, p.w, p.res, p.h};
+        const int64_t sizes[] = {nb, wb, nb, nb};
+        for (int i = 0; i < 4; ++i) {
+            if (!others[i]) continue;
+            if (ranges_overlap(p.out, qb, others[i], sizes[i]) || ranges_overlap(p.scale, sb, others[i], sizes[i]))
+                return RMSNORM_ERR_INVALID_ARG;
+        }
+        if (ranges_overlap(p.out, qb, p.scale, sb)) return RMSNORM_ERR_INVALID_ARG;
+        if (p.fused) {
+            if (ranges_overlap(p.h, nb, p.w, wb)) return RMSNORM_ERR_INVALID_ARG;
+            if (!output_vs_input_ok(p.h, p.x, nb) || !output_vs_input_ok(p.h, p.res, nb)) return RMSNORM_ERR_INVALID_ARG;
+        }
+        return RMSNORM_OK;
+    }
+    if (reinterpret_cast<uintptr_t>(p.out) % es != 0) return RMSNORM_ERR_INVALID_ARG;
     if (ranges_overlap(p.out, nb, p.w, wb)) return RMSNORM_ERR_INVALID_ARG;
     if (!output_vs_input_ok(p.out, p.x, nb)) return RMSNORM_ERR_INVALID_ARG;
     if (p.fused) {
@@ -94,7 +115,7 @@ bool vector_aligned(const Problem& p) {
     const void* ptrs[] = {p.x, p.w, p.out, p.res, p.h};
     for (const void* q : ptrs)
         if (q && reinterpret_cast<uintptr_t>(q) % kVectorBytes != 0) return false;
-    return true;
+    return true;  // codes: a 16-byte-aligned base keeps every row's 8- (4-) byte stores aligned
 }
 
 // The automatic choice, from launch-shape sweeps on MI355X.  Vector path:
@@ -105,7 +126,7 @@ bool vector_aligned(const Problem& p) {
 // vectors, the fused bf16 hidden 5120 as 4 waves x 3.  Element path: at most 8 elements per lane.  When rows are few,
 // each row gets more waves so the whole GPU has work.  Rows that no built
 // register-resident configuration covers take the two-pass path.
-rmsnorm_config_t choose(int64_t rows, int64_t hidden, int dtype, bool aligned, bool fused) {
+rmsnorm_config_t choose(int64_t rows, int64_t hidden, int dtype, bool aligned, bool fused, int qt) {
     rmsnorm_config_t c = {RMSNORM_PATH_TWO_PASS, 16, 0, 1, 0};
     const bool vec = aligned && hidden % vec_elems(dtype) == 0;
     const int64_t units = vec ? hidden / vec_elems(dtype) : hidden;
@@ -115,7 +136,8 @@ rmsnorm_config_t choose(int64_t rows, int64_t hidden, int dtype, bool aligned, b
     auto fit = [&](int wpr) {
         const int per = round_up_in(list, nlist, ceil_div(units, int64_t(64) * wpr));
         if (per < 0) return -1;
-        const bool built = vec ? mbr::vec_built(wpr, per, fused) : mbr::elem_built(wpr, per);
+        const bool built = qt ? (vec ? mbr::qvec_built(wpr, per) : mbr::qelem_built(wpr, per))
+                              : (vec ? mbr::vec_built(wpr, per, fused) : mbr::elem_built(wpr, per));
         return built ? per : -1;
     };
     int wpr = 1;
@@ -137,7 +159,7 @@ rmsnorm_config_t choose(int64_t rows, int64_t hidden, int dtype, bool aligned, b
 
 rmsnorm_status_t launch(const Problem& p, const rmsnorm_config_t* user, hipStream_t stream) {
     const bool aligned = vector_aligned(p);
-    const rmsnorm_config_t c = (user && user->path != RMSNORM_PATH_AUTO) ? *user : choose(p.rows, p.hidden, p.dtype, aligned, p.fused);
+    const rmsnorm_config_t c = (user && user->path != RMSNORM_PATH_AUTO) ? *user : choose(p.rows, p.hidden, p.dtype, aligned, p.fused, p.qt);
     const int wi = index_of(mbr::kWprList, mbr::kNumWpr, c.waves_per_row);
     if (wi < 0 || c.rows_per_block < 1 || c.max_blocks < 0) return RMSNORM_ERR_INVALID_ARG;
     const int64_t lanes_per_row = int64_t(64) * c.waves_per_row;
@@ -152,6 +174,7 @@ rmsnorm_status_t launch(const Problem& p, const rmsnorm_config_t* user, hipStrea
     a.rows_per_block = c.rows_per_block;
     a.hidden_f = static_cast<float>(p.hidden);
     a.eps = p.eps;
+    a.scale = p.scale;
 
     const void* fn = nullptr;
     int64_t threads = 0;
@@ -164,7 +187,8 @@ rmsnorm_status_t launch(const Problem& p, const rmsnorm_config_t* user, hipStrea
             threads = lanes_per_row * c.rows_per_block;
             if (threads > mbr::max_threads_for(c.waves_per_row)) return RMSNORM_ERR_INVALID_ARG;
             const bool masked = lanes_per_row * c.items_per_lane != nvec;
-            fn = mbr::vec_kernel(p.dtype, p.fused, masked, wi, vi);
+            fn = p.qt ? mbr::qvec_kernel(p.dtype, p.qt, p.fused, masked, wi, vi)
+                      : mbr::vec_kernel(p.dtype, p.fused, masked, wi, vi);
             a.units = static_cast<int32_t>(nvec);
             break;
         }
@@ -173,7 +197,7 @@ rmsnorm_status_t launch(const Problem& p, const rmsnorm_config_t* user, hipStrea
             if (ei < 0 || lanes_per_row * c.items_per_lane < p.hidden) return RMSNORM_ERR_INVALID_ARG;
             threads = lanes_per_row * c.rows_per_block;
             if (threads > mbr::max_threads_for(c.waves_per_row)) return RMSNORM_ERR_INVALID_ARG;
-            fn = mbr::elem_kernel(p.dtype, p.fused, wi, ei);
+            fn = p.qt ? mbr::qelem_kernel(p.dtype, p.qt, p.fused, wi, ei) : mbr::elem_kernel(p.dtype, p.fused, wi, ei);
             a.units = static_cast<int32_t>(p.hidden);
             break;
         }
@@ -181,7 +205,7 @@ rmsnorm_status_t launch(const Problem& p, const rmsnorm_config_t* user, hipStrea
             if (c.rows_per_block != 1) return RMSNORM_ERR_INVALID_ARG;
             const bool vec = aligned && p.hidden % vec_elems(p.dtype) == 0;
             threads = lanes_per_row;
-            fn = mbr::twopass_kernel(p.dtype, p.fused, vec);
+            fn = p.qt ? mbr::qtwopass_kernel(p.dtype, p.qt, p.fused, vec) : mbr::twopass_kernel(p.dtype, p.fused, vec);
             a.units = static_cast<int32_t>(vec ? p.hidden / vec_elems(p.dtype) : p.hidden);
             break;
         }
@@ -232,7 +256,7 @@ RMSNORM_API rmsnorm_status_t rmsnorm_residual_fwd(const void* x, const void* res
 RMSNORM_API rmsnorm_status_t rmsnorm_fwd_ex(const void* x, const void* weight, void* out, int64_t rows,
                                             int64_t hidden, float eps, rmsnorm_dtype_t dtype,
                                             const rmsnorm_config_t* cfg, void* stream) {
-    Problem p = {x, nullptr, weight, nullptr, out, rows, hidden, eps, static_cast<int>(dtype), false};
+    Problem p = {x, nullptr, weight, nullptr, out, rows, hidden, eps, static_cast<int>(dtype), false, 0, nullptr};
     return run(p, cfg, stream);
 }
 
@@ -240,7 +264,7 @@ RMSNORM_API rmsnorm_status_t rmsnorm_residual_fwd_ex(const void* x, const void* 
                                                      void* residual_out, void* out, int64_t rows, int64_t hidden,
                                                      float eps, rmsnorm_dtype_t dtype,
                                                      const rmsnorm_config_t* cfg, void* stream) {
-    Problem p = {x, residual, weight, residual_out, out, rows, hidden, eps, static_cast<int>(dtype), true};
+    Problem p = {x, residual, weight, residual_out, out, rows, hidden, eps, static_cast<int>(dtype), true, 0, nullptr};
     return run(p, cfg, stream);
 }
 
@@ -250,7 +274,41 @@ RMSNORM_API rmsnorm_status_t rmsnorm_select_config(int64_t rows, int64_t hidden,
     if (!cfg) return RMSNORM_ERR_INVALID_ARG;
     rmsnorm_status_t s = validate_sizes(rows, hidden, 0.0f, static_cast<int>(dtype));
     if (s != RMSNORM_OK) return s;
-    *cfg = choose(rows, hidden, static_cast<int>(dtype), vector_aligned_flag != 0, fused != 0);
+    *cfg = choose(rows, hidden, static_cast<int>(dtype), vector_aligned_flag != 0, fused != 0, 0);
+    return RMSNORM_OK;
+}
+
+RMSNORM_API rmsnorm_status_t rmsnorm_dynamic_quant_fwd_ex(const void* x, const void* residual, const void* weight,
+                                                         void* residual_out, void* q_out, float* scale_out,
+                                                         int64_t rows, int64_t hidden, float eps,
+                                                         rmsnorm_dtype_t dtype, rmsnorm_quant_t qtype,
+                                                         const rmsnorm_config_t* cfg, void* stream) {
+    if (qtype != RMSNORM_QUANT_INT8 && qtype != RMSNORM_QUANT_FP8_E4M3) {
+        const rmsnorm_status_t s = validate_sizes(rows, hidden, eps, static_cast<int>(dtype));
+        return s != RMSNORM_OK ? s : RMSNORM_ERR_UNSUPPORTED_DTYPE;
+    }
+    if ((residual == nullptr) != (residual_out == nullptr)) return RMSNORM_ERR_INVALID_ARG;
+    if (rows > INT64_MAX / 4) return RMSNORM_ERR_INVALID_ARG;  // the scale vector's byte size must fit
+    Problem p = {x, residual, weight, residual_out, q_out, rows, hidden, eps, static_cast<int>(dtype),
+                 residual != nullptr, qtype == RMSNORM_QUANT_INT8 ? 1 : 2, scale_out};
+    return run(p, cfg, stream);
+}
+
+RMSNORM_API rmsnorm_status_t rmsnorm_dynamic_quant_fwd(const void* x, const void* residual, const void* weight,
+                                                      void* residual_out, void* q_out, float* scale_out,
+                                                      int64_t rows, int64_t hidden, float eps, rmsnorm_dtype_t dtype,
+                                                      rmsnorm_quant_t qtype, void* stream) {
+    return rmsnorm_dynamic_quant_fwd_ex(x, residual, weight, residual_out, q_out, scale_out, rows, hidden, eps, dtype,
+                                        qtype, nullptr, stream);
+}
+
+RMSNORM_API rmsnorm_status_t rmsnorm_select_quant_config(int64_t rows, int64_t hidden, rmsnorm_dtype_t dtype,
+                                                         int32_t vector_aligned_flag, int32_t fused,
+                                                         rmsnorm_config_t* cfg) {
+    if (!cfg) return RMSNORM_ERR_INVALID_ARG;
+    rmsnorm_status_t s = validate_sizes(rows, hidden, 0.0f, static_cast<int>(dtype));
+    if (s != RMSNORM_OK) return s;
+    *cfg = choose(rows, hidden, static_cast<int>(dtype), vector_aligned_flag != 0, fused != 0, 1);
     return RMSNORM_OK;
 }
 

@@ -25,12 +25,23 @@ constexpr bool vec_built(int wpr, int vpl, bool fused) {
     return wpr < 16 ? !(fused && vpl == 16) : vpl <= (fused ? 6 : 10);
 }
 constexpr bool elem_built(int wpr, int epl) { return wpr < 16 || epl <= 8; }
+// Quantised forms (int8 / fp8 codes plus a per-row scale) also hold the weight
+// slice, so lanes carry at most 8 vectors (4 in a 1024-lane workgroup).
+constexpr bool qvec_built(int wpr, int vpl) { return vpl <= 8 && (wpr < 16 || vpl <= 4); }
+constexpr bool qelem_built(int wpr, int epl) { return epl <= 8 && (wpr < 16 || epl <= 4); }
 
 // Host-side kernel handles (addresses of the __global__ stubs), or nullptr.
 // dtype: 0 = f32, 1 = bf16.
 const void* vec_kernel(int dtype, bool fused, bool masked, int wpr_index, int vpl_index);
 const void* elem_kernel(int dtype, bool fused, int wpr_index, int epl_index);
 const void* twopass_kernel(int dtype, bool fused, bool vec);
+
+// Quantised forms; qt: 1 = int8, 2 = fp8 e4m3fn.
+const void* qvec_kernel(int dtype, int qt, bool fused, bool masked, int wpr_index, int vpl_index);
+const void* qelem_kernel(int dtype, int qt, bool fused, int wpr_index, int epl_index);
+const void* qtwopass_kernel(int dtype, int qt, bool fused, bool vec);
+const void* qvec_kernel_bf16(int qt, bool fused, bool masked, int wi, int vi);
+const void* qvec_kernel_f32(int qt, bool fused, bool masked, int wi, int vi);
 
 // Per-unit getters defined in the instantiation files.
 const void* vec_kernel_bf16(bool fused, bool masked, int wi, int vi);

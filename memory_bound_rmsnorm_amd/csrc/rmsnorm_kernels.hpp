@@ -15,6 +15,16 @@
 //   rms_twopass_kernel  rows larger than the register budget of a 1024-lane
 //                       workgroup: pass 1 sums squares, pass 2 re-reads x.
 //
+// QT != 0 selects the dynamic-quantisation form (the Add + RmsNorm +
+// DynamicQuant fusion the TileLang tutorial ch. 02, section 4.2, cites from
+// CANN): instead of the normalised row, each row is written as int8 (QT 1) or
+// fp8 e4m3fn (QT 2) codes with one fp32 scale, scale = max|y| / Q and
+// code_j = round(y_j / scale).  Because y_j = x_j * r * w_j with one r > 0 per
+// row, r cancels from the codes: they are computed as (x_j * w_j) * (Q / m)
+// with m = max_k |x_k * w_k|, which the lanes track in the same reduction pass
+// as the sum of squares (one barrier per row, as in the plain form), and the
+// scale is r * m / Q.
+//
 // The sum of squares is reduced lane -> wave (DPP within 16-lane rows, then
 // the gfx950 permlane16/permlane32 swaps) -> workgroup (one LDS slot per wave,
 // one barrier, every wave adds the slots in the same fixed order).  Every lane
@@ -45,6 +55,7 @@ struct RowArgs {
     int32_t rows_per_block;
     float hidden_f;      // hidden as fp32, the mean's divisor
     float eps;
+    float* scale;        // quantised forms: one fp32 scale per row
 };
 
 // ---------------------------------------------------------------- dtypes
@@ -134,6 +145,71 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// Maximum over the 64 lanes of a wave, same pattern as wave_sum (fmaxf is
+// commutative, so every lane returns the same bits).
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp_mov<0xB1>(v));
+    v = fmaxf(v, dpp_mov<0x4E>(v));
+    v = fmaxf(v, dpp_mov<0x141>(v));
+    v = fmaxf(v, dpp_mov<0x140>(v));
+    {
+        auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    }
+    {
+        auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    }
+    return v;
+}
+
+// ---------------------------------------------------------------- quantised output
+
+template <int QT>
+constexpr float quant_max() { return QT == 1 ? 127.0f : 448.0f; }
+
+// One code from t = y / scale: int8 nearest-even clamped to [-127, 127], or
+// fp8 e4m3fn nearest-even (v_cvt_pk_fp8_f32) after clamping to +-448.
+template <int QT>
+__device__ __forceinline__ unsigned quant_code(float t) {
+    if constexpr (QT == 1) {
+        const float c = fminf(fmaxf(__builtin_rintf(t), -127.0f), 127.0f);
+        return static_cast<unsigned>(static_cast<int>(c)) & 0xffu;
+    } else {
+        const float c = fminf(fmaxf(t, -448.0f), 448.0f);
+        return static_cast<unsigned>(__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false)) & 0xffu;
+    }
+}
+
+// Four codes packed little-endian into one dword.
+template <int QT>
+__device__ __forceinline__ unsigned quant_pack4(float t0, float t1, float t2, float t3) {
+    if constexpr (QT == 1) {
+        return quant_code<1>(t0) | (quant_code<1>(t1) << 8) | (quant_code<1>(t2) << 16) | (quant_code<1>(t3) << 24);
+    } else {
+        const float c0 = fminf(fmaxf(t0, -448.0f), 448.0f), c1 = fminf(fmaxf(t1, -448.0f), 448.0f);
+        const float c2 = fminf(fmaxf(t2, -448.0f), 448.0f), c3 = fminf(fmaxf(t3, -448.0f), 448.0f);
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(c0, c1, 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(c2, c3, w, true);
+        return static_cast<unsigned>(w);
+    }
+}
+
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+// Codes of one 16-byte input vector: 8 bytes for bf16 (u32x2), 4 for fp32.
+template <int QT>
+__device__ __forceinline__ void store_codes(void* q_row, int v, const float (&t)[8], Bf16) {
+    u32x2 c;
+    c[0] = quant_pack4<QT>(t[0], t[1], t[2], t[3]);
+    c[1] = quant_pack4<QT>(t[4], t[5], t[6], t[7]);
+    __builtin_nontemporal_store(c, static_cast<u32x2*>(q_row) + v);
+}
+template <int QT>
+__device__ __forceinline__ void store_codes(void* q_row, int v, const float (&t)[4], F32) {
+    __builtin_nontemporal_store(quant_pack4<QT>(t[0], t[1], t[2], t[3]), static_cast<unsigned*>(q_row) + v);
+}
+
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // ---------------------------------------------------------------- vector path
@@ -149,6 +225,8 @@ constexpr int max_threads() { return WPR == 16 ? 1024 : 512; }
 // so there the slice is loaded after the reduction instead.
 template <int WPR, int VPL, bool FUSED>
 constexpr bool weight_resident() { return VPL >= 3 && VPL <= (WPR == 16 ? 4 : 8) && (!FUSED || VPL <= 6); }
+// The quantised forms need x_j * w_j before the reduction (for the row max),
+// so they always hold the weight slice.
 // With a capped grid each workgroup walks several row groups; when the row
 // slice is small the next row's loads are issued before the current row is
 // reduced and stored, so memory stays busy across the reduction.
@@ -160,12 +238,12 @@ constexpr bool row_pipelined() { return VPL * (FUSED ? 2 : 1) <= 4; }
 // covers 1 KiB of contiguous memory.  MASKED: the row has fewer than
 // 64*WPR*VPL vectors; loads are clamped in bounds (the extra values are
 // excluded from the sum) and stores skipped.
-template <class E, int WPR, int VPL, bool MASKED, bool FUSED>
+template <class E, int WPR, int VPL, bool MASKED, bool FUSED, int QT = 0>
 __global__ void __launch_bounds__(max_threads<WPR>()) rms_vec_kernel(const RowArgs a) {
     constexpr int LANES = 64 * WPR;
     constexpr int V = E::kVec;
     constexpr int NR = FUSED ? VPL : 1;  // residual registers
-    constexpr bool WRES = weight_resident<WPR, VPL, FUSED>();
+    constexpr bool WRES = QT != 0 || weight_resident<WPR, VPL, FUSED>();
     constexpr bool PIPE = row_pipelined<VPL, FUSED>();
     const int wave = wave_id();
     const int slot = wave / WPR;  // row within the workgroup
@@ -173,6 +251,7 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_vec_kernel(const RowAr
     const int nvec = a.units;
     const int64_t rpb = a.rows_per_block;
     __shared__ float part[2][16];
+    __shared__ float mpart[QT ? 2 : 1][QT ? 16 : 1];
 
     auto vidx = [&](int k) {
         const int v = k * LANES + lane_row;
@@ -217,7 +296,7 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_vec_kernel(const RowAr
         } else {
             if (valid) load_row(row, d, rv);
         }
-        float ss = 0.f;
+        float ss = 0.f, mx = 0.f;
         if (valid) {
             if constexpr (FUSED) {
                 u32x4* hr = static_cast<u32x4*>(a.h) + row * nvec;
@@ -240,17 +319,49 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_vec_kernel(const RowAr
 #pragma unroll
                 for (int i = 0; i < V; ++i) s += f[i] * f[i];
                 ss += in_row(k) ? s : 0.f;
+                if constexpr (QT != 0) {
+                    float fw[V];
+                    widen(wv[k], fw, E{});
+                    float m = 0.f;
+#pragma unroll
+                    for (int i = 0; i < V; ++i) m = fmaxf(m, fabsf(f[i] * fw[i]));
+                    mx = in_row(k) ? fmaxf(mx, m) : mx;
+                }
             }
         }
         ss = wave_sum(ss);
+        if constexpr (QT != 0) mx = wave_max(mx);
         if constexpr (WPR > 1) {
-            if ((threadIdx.x & 63) == 0) part[it & 1][wave] = ss;
+            if ((threadIdx.x & 63) == 0) {
+                part[it & 1][wave] = ss;
+                if constexpr (QT != 0) mpart[it & 1][wave] = mx;
+            }
             __syncthreads();
             ss = 0.f;
 #pragma unroll
             for (int i = 0; i < WPR; ++i) ss += part[it & 1][slot * WPR + i];
+            if constexpr (QT != 0) {
+                mx = 0.f;
+#pragma unroll
+                for (int i = 0; i < WPR; ++i) mx = fmaxf(mx, mpart[it & 1][slot * WPR + i]);
+            }
         }
-        if (valid) {
+        if (valid && QT != 0) {
+            const float r = rsqrtf(ss / a.hidden_f + a.eps);
+            const float inv = mx > 0.f ? quant_max<QT>() / mx : 0.f;
+            if (lane_row == 0) a.scale[row] = r * mx / quant_max<QT>();
+            void* qr = static_cast<unsigned char*>(a.out) + row * static_cast<int64_t>(nvec) * V;
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) {
+                if (!in_row(k)) continue;
+                float f[V], fw[V];
+                widen(d[k], f, E{});
+                widen(wv[k], fw, E{});
+#pragma unroll
+                for (int i = 0; i < V; ++i) f[i] = (f[i] * fw[i]) * inv;
+                store_codes<QT>(qr, k * LANES + lane_row, f, E{});
+            }
+        } else if (valid) {
             const float r = rsqrtf(ss / a.hidden_f + a.eps);
             u32x4* outr = static_cast<u32x4*>(a.out) + row * nvec;
 #pragma unroll
@@ -274,7 +385,7 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_vec_kernel(const RowAr
 
 // One element per access; lane l of a row owns elements l, l + 64*WPR, ...
 // (each wave instruction covers 64 consecutive elements).  Always masked.
-template <class E, int WPR, int EPL, bool FUSED>
+template <class E, int WPR, int EPL, bool FUSED, int QT = 0>
 __global__ void __launch_bounds__(max_threads<WPR>()) rms_elem_kernel(const RowArgs a) {
     using S = typename E::scalar;
     constexpr int LANES = 64 * WPR;
@@ -283,6 +394,16 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_elem_kernel(const RowA
     const int lane_row = static_cast<int>(threadIdx.x) - slot * LANES;
     const int H = a.units;
     __shared__ float part[2][16];
+    __shared__ float mpart[QT ? 2 : 1][QT ? 16 : 1];
+    float wq[QT ? EPL : 1];  // quantised forms: this lane's weights, loaded once
+    if constexpr (QT != 0) {
+        const S* wr = static_cast<const S*>(a.w);
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) {
+            const int j = k * LANES + lane_row;
+            wq[k] = widen1(wr[j < H ? j : H - 1]);
+        }
+    }
 
     int it = 0;
     for (int64_t g = blockIdx.x; g < a.n_groups; g += gridDim.x, ++it) {
@@ -290,7 +411,7 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_elem_kernel(const RowA
         const bool valid = row < a.rows;
         const int64_t base = row * H;
         float d[EPL];
-        float ss = 0.f;
+        float ss = 0.f, mx = 0.f;
         if (valid) {
             const S* xr = static_cast<const S*>(a.x) + base;
 #pragma unroll
@@ -313,17 +434,37 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_elem_kernel(const RowA
             for (int k = 0; k < EPL; ++k) {
                 const int j = k * LANES + lane_row;
                 ss += j < H ? d[k] * d[k] : 0.f;
+                if constexpr (QT != 0) mx = j < H ? fmaxf(mx, fabsf(d[k] * wq[k])) : mx;
             }
         }
         ss = wave_sum(ss);
+        if constexpr (QT != 0) mx = wave_max(mx);
         if constexpr (WPR > 1) {
-            if ((threadIdx.x & 63) == 0) part[it & 1][wave] = ss;
+            if ((threadIdx.x & 63) == 0) {
+                part[it & 1][wave] = ss;
+                if constexpr (QT != 0) mpart[it & 1][wave] = mx;
+            }
             __syncthreads();
             ss = 0.f;
 #pragma unroll
             for (int i = 0; i < WPR; ++i) ss += part[it & 1][slot * WPR + i];
+            if constexpr (QT != 0) {
+                mx = 0.f;
+#pragma unroll
+                for (int i = 0; i < WPR; ++i) mx = fmaxf(mx, mpart[it & 1][slot * WPR + i]);
+            }
         }
-        if (valid) {
+        if (valid && QT != 0) {
+            const float r = rsqrtf(ss / a.hidden_f + a.eps);
+            const float inv = mx > 0.f ? quant_max<QT>() / mx : 0.f;
+            if (lane_row == 0) a.scale[row] = r * mx / quant_max<QT>();
+            unsigned char* qr = static_cast<unsigned char*>(a.out) + base;
+#pragma unroll
+            for (int k = 0; k < EPL; ++k) {
+                const int j = k * LANES + lane_row;
+                if (j < H) qr[j] = static_cast<unsigned char>(quant_code<QT>((d[k] * wq[k]) * inv));
+            }
+        } else if (valid) {
             const float r = rsqrtf(ss / a.hidden_f + a.eps);
             const S* wr = static_cast<const S*>(a.w);
             S* outr = static_cast<S*>(a.out) + base;
@@ -343,7 +484,7 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_elem_kernel(const RowA
 // pass 2 reads them again, recomputes h, and writes h and y.  Pass 1 writes
 // nothing, so exact input/output aliasing stays safe: every element is read
 // and then written by the same thread.
-template <class E, bool VEC, bool FUSED>
+template <class E, bool VEC, bool FUSED, int QT = 0>
 __global__ void __launch_bounds__(1024) rms_twopass_kernel(const RowArgs a) {
     using S = typename E::scalar;
     constexpr int V = E::kVec;
@@ -351,11 +492,12 @@ __global__ void __launch_bounds__(1024) rms_twopass_kernel(const RowArgs a) {
     const int nwaves = static_cast<int>(blockDim.x) >> 6;
     const int n = a.units;
     __shared__ float part[2][16];
+    __shared__ float mpart[QT ? 2 : 1][QT ? 16 : 1];
 
     int it = 0;
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x, ++it) {
         const int64_t base = row * n;
-        float ss = 0.f;
+        float ss = 0.f, mx = 0.f;
         for (int64_t j = threadIdx.x; j < n; j += blockDim.x) {
             if constexpr (VEC) {
                 float f[V];
@@ -371,18 +513,65 @@ __global__ void __launch_bounds__(1024) rms_twopass_kernel(const RowArgs a) {
 #pragma unroll
                 for (int i = 0; i < V; ++i) s += f[i] * f[i];
                 ss += s;
+                if constexpr (QT != 0) {
+                    float fw[V];
+                    widen(load_keep(static_cast<const u32x4*>(a.w) + j), fw, E{});
+#pragma unroll
+                    for (int i = 0; i < V; ++i) mx = fmaxf(mx, fabsf(f[i] * fw[i]));
+                }
             } else {
                 float f = widen1(static_cast<const S*>(a.x)[base + j]);
                 if constexpr (FUSED) f = widen1(narrow1(f + widen1(static_cast<const S*>(a.res)[base + j]), E{}));
                 ss += f * f;
+                if constexpr (QT != 0) mx = fmaxf(mx, fabsf(f * widen1(static_cast<const S*>(a.w)[j])));
             }
         }
         ss = wave_sum(ss);
-        if ((threadIdx.x & 63) == 0) part[it & 1][wave] = ss;
+        if constexpr (QT != 0) mx = wave_max(mx);
+        if ((threadIdx.x & 63) == 0) {
+            part[it & 1][wave] = ss;
+            if constexpr (QT != 0) mpart[it & 1][wave] = mx;
+        }
         __syncthreads();
         ss = 0.f;
         for (int i = 0; i < nwaves; ++i) ss += part[it & 1][i];
         const float r = rsqrtf(ss / a.hidden_f + a.eps);
+        if constexpr (QT != 0) {
+            mx = 0.f;
+            for (int i = 0; i < nwaves; ++i) mx = fmaxf(mx, mpart[it & 1][i]);
+            const float inv = mx > 0.f ? quant_max<QT>() / mx : 0.f;
+            if (threadIdx.x == 0) a.scale[row] = r * mx / quant_max<QT>();
+            for (int64_t j = threadIdx.x; j < n; j += blockDim.x) {
+                if constexpr (VEC) {
+                    float f[V], fw[V];
+                    u32x4 xv = load_stream(static_cast<const u32x4*>(a.x) + base + j);
+                    if constexpr (FUSED) {
+                        float fr[V];
+                        widen(xv, f, E{});
+                        widen(load_stream(static_cast<const u32x4*>(a.res) + base + j), fr, E{});
+#pragma unroll
+                        for (int i = 0; i < V; ++i) f[i] += fr[i];
+                        xv = narrow(f, E{});
+                        store_stream(static_cast<u32x4*>(a.h) + base + j, xv);
+                    }
+                    widen(xv, f, E{});
+                    widen(load_keep(static_cast<const u32x4*>(a.w) + j), fw, E{});
+#pragma unroll
+                    for (int i = 0; i < V; ++i) f[i] = (f[i] * fw[i]) * inv;
+                    store_codes<QT>(static_cast<unsigned char*>(a.out) + base * V, static_cast<int>(j), f, E{});
+                } else {
+                    float f = widen1(static_cast<const S*>(a.x)[base + j]);
+                    if constexpr (FUSED) {
+                        const S hv = narrow1(f + widen1(static_cast<const S*>(a.res)[base + j]), E{});
+                        static_cast<S*>(a.h)[base + j] = hv;
+                        f = widen1(hv);
+                    }
+                    static_cast<unsigned char*>(a.out)[base + j] =
+                        static_cast<unsigned char>(quant_code<QT>((f * widen1(static_cast<const S*>(a.w)[j])) * inv));
+                }
+            }
+            continue;
+        }
         for (int64_t j = threadIdx.x; j < n; j += blockDim.x) {
             if constexpr (VEC) {
                 float f[V], fw[V];

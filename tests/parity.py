@@ -112,3 +112,90 @@ def oracle_residual(x: np.ndarray, res: np.ndarray, w: np.ndarray, eps: float):
             h[r[0]:r[1]], y[r[0]:r[1]] = oracle.rmsnorm_residual_fwd(x[r[0]:r[1]], res[r[0]:r[1]], w, eps)
         list(ex.map(job, _chunks(x.shape[0], 4 * threads())))
     return h, y
+
+
+QMAX = {0: 127.0, 1: 448.0}
+
+
+def _e4m3_table() -> np.ndarray:
+    """Value of every e4m3fn code (NaN codes 0x7F/0xFF as NaN)."""
+    v = np.empty(256)
+    for c in range(256):
+        e, m = (c >> 3) & 0xF, c & 7
+        mag = (m / 8.0) * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+        v[c] = np.nan if (c & 0x7F) == 0x7F else (-mag if c & 0x80 else mag)
+    return v
+
+
+E4M3 = _e4m3_table()
+
+
+def quant_t(v_bits: np.ndarray, w_bits: np.ndarray, qtype: int) -> np.ndarray:
+    """Q * v_j * w_j / max_k |v_k * w_k| per row in fp64 (products of two bf16 or
+    fp32 values are exact in fp64): the quantity the codes round, with the
+    root cancelled."""
+    if v_bits.dtype == np.uint16:
+        v = bf16_to_f64(v_bits)
+        w = bf16_to_f64(w_bits)
+    else:
+        v = v_bits.astype(np.float64)
+        w = w_bits.astype(np.float64)
+    p = v * w[None, :]
+    m = np.max(np.abs(p), axis=1, keepdims=True)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        t = np.where(m > 0, QMAX[qtype] * p / m, 0.0)
+    return t
+
+
+def compare_quant(q_gpu, q_want, s_gpu, s_want, t, qtype, tie_tol=1e-5) -> dict:
+    """Codes equal except where t lies within tie_tol (relative, int8: of 1)
+    of the tie between the two codes involved; scales within 1e-5 relative."""
+    s_g = s_gpu.astype(np.float64)
+    s_w = s_want.astype(np.float64)
+    assert np.all(s_g[s_w == 0] == 0), "zero scale expected"
+    nz = s_w != 0
+    srel = np.abs(s_g[nz] - s_w[nz]) / s_w[nz] if nz.any() else np.zeros(1)
+    assert srel.max() <= F32_RTOL, "scale relative error %.3e" % srel.max()
+    g = q_gpu.reshape(q_want.shape)
+    diff = g != q_want
+    n_diff = int(diff.sum())
+    if n_diff:
+        gi = g[diff]
+        wi = q_want[diff]
+        ti = t[diff]
+        if qtype == 0:
+            gi = gi.astype(np.int64)
+            wi = wi.astype(np.int64)
+            assert np.all(np.abs(gi - wi) == 1), "int8 codes differ by more than one"
+            mid = (gi + wi) / 2.0
+            assert np.all(np.abs(ti - mid) <= tie_tol * 127), "int8 code differs away from a tie"
+        else:
+            gu = gi.astype(np.uint8)
+            wu = wi.astype(np.uint8)
+            gv, wv = E4M3[gu], E4M3[wu]
+            assert np.all(np.sign(gv) * np.sign(wv) >= 0), "fp8 codes differ in sign"
+            key = lambda c: np.where(c & 0x80, -(c & 0x7F).astype(np.int64), (c & 0x7F).astype(np.int64))
+            assert np.all(np.abs(key(gu) - key(wu)) == 1), "fp8 codes differ by more than one step"
+            mid = (gv + wv) / 2.0
+            assert np.all(np.abs(ti - mid) <= tie_tol * np.abs(ti) + 2.0 ** -12), "fp8 code differs away from a tie"
+    return {"n": int(q_want.size), "codes_differing_at_ties": n_diff,
+            "max_scale_rel_err": float(srel.max())}
+
+
+def oracle_quant(x, w, eps, qtype, residual=None):
+    """The oracle's dynamic-quant output over all rows, rows across threads."""
+    rows = x.shape[0]
+    h = np.empty_like(x) if residual is not None else None
+    q = np.empty(x.shape, np.int8 if qtype == 0 else np.uint8)
+    s = np.empty(rows, np.float32)
+    with concurrent.futures.ThreadPoolExecutor(threads()) as ex:
+        def job(r):
+            a, b = r
+            res = residual[a:b] if residual is not None else None
+            hh, qq, ss = oracle.rmsnorm_dynamic_quant_fwd(x[a:b], w, eps, qtype, residual=res)
+            if h is not None:
+                h[a:b] = hh
+            q[a:b] = qq
+            s[a:b] = ss
+        list(ex.map(job, _chunks(rows, 4 * threads())))
+    return h, q, s

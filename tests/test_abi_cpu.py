@@ -208,3 +208,52 @@ def test_binding_refuses_cpu_tensors():
         mbr.rmsnorm_fwd(x, torch.ones(8), torch.empty_like(x))
     with pytest.raises(TypeError):
         mbr.dtype_code(torch.float16)
+
+
+def test_quant_rows_zero_and_bad_qtype():
+    L = mbr.lib()
+    assert L.rmsnorm_dynamic_quant_fwd(None, None, None, None, None, None, 0, 16, 1e-5, 1, 0, None) == mbr.RMSNORM_OK
+    assert L.rmsnorm_dynamic_quant_fwd(None, None, None, None, None, None, 4, 16, 1e-5, 1, 2, None) == \
+        mbr.RMSNORM_ERR_UNSUPPORTED_DTYPE
+    assert L.rmsnorm_dynamic_quant_fwd(None, None, None, None, None, None, -1, 16, 1e-5, 1, 7, None) == \
+        mbr.RMSNORM_ERR_INVALID_ARG
+
+
+@fake_only
+def test_quant_argument_validation():
+    L = mbr.lib()
+    INV = mbr.RMSNORM_ERR_INVALID_ARG
+    X, W, Q, S, R, H = (0x7F0000000000, 0x7F0010000000, 0x7F0020000000, 0x7F0030000000, 0x7F0040000000,
+                        0x7F0050000000)
+
+    def call(x=X, r=None, w=W, h=None, q=Q, s=S, rows=4, hidden=64, dt=1, qt=0):
+        return L.rmsnorm_dynamic_quant_fwd(x, r, w, h, q, s, rows, hidden, 1e-5, dt, qt, None)
+
+    assert call(r=R) == INV                 # residual without residual_out
+    assert call(h=H) == INV                 # residual_out without residual
+    assert call(q=None) == INV
+    assert call(s=None) == INV
+    assert call(s=S + 2) == INV             # scale needs 4-byte alignment
+    assert call(q=X + 16) == INV            # codes over x
+    assert call(q=W) == INV                 # codes over weight
+    assert call(s=X + 8) == INV             # scales over x
+    assert call(s=Q + 100) == INV           # scales over codes
+    assert call(r=R, h=W) == INV            # h over weight
+    assert call(r=R, h=R + 2) == INV        # h partially over residual
+    assert call(r=R, h=Q) == INV            # h over codes
+
+
+@pytest.mark.parametrize("hidden", [1, 7, 8, 2048, 4095, 5120, 8192, 8193, 16384, 32768, 65536])
+@pytest.mark.parametrize("rows", [1, 5, 4096])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("fused", [False, True])
+def test_quant_selection_is_always_built(hidden, rows, dtype, fused):
+    cfg = mbr.rmsnorm_select_quant_config(rows, hidden, dtype, True, fused)
+    if cfg.path == mbr.PATH_VECTOR:
+        assert cfg.items_per_lane <= (4 if cfg.waves_per_row == 16 else 8)
+        assert 64 * cfg.waves_per_row * cfg.items_per_lane * (4 if dtype == torch.float32 else 8) >= hidden
+    elif cfg.path == mbr.PATH_ELEMENT:
+        assert cfg.items_per_lane <= (4 if cfg.waves_per_row == 16 else 8)
+        assert 64 * cfg.waves_per_row * cfg.items_per_lane >= hidden
+    else:
+        assert cfg.path == mbr.PATH_TWO_PASS

@@ -1,0 +1,177 @@
+"""Parity of the dynamic-quant HIP path (through the C ABI) with the oracle.
+
+Codes must equal the oracle's except where Q*v*w/max|v*w| lies within float32
+error of a tie between two codes (tests/parity.py::compare_quant); scales
+within 1e-5 relative; the residual sum h bitwise."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import memory_bound_rmsnorm_amd as mbr
+from memory_bound_rmsnorm_amd import inputs
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+BF16, F32 = torch.bfloat16, torch.float32
+QT = {"int8": mbr.QUANT_INT8, "fp8": mbr.QUANT_FP8_E4M3}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_quant(t, qtype, eps, cfg=None, residual=True, h=None):
+    x, w = t["x"].cuda(), t["weight"].cuda()
+    q = torch.empty(x.shape, dtype=torch.uint8, device="cuda")
+    s = torch.empty(x.shape[0], dtype=torch.float32, device="cuda")
+    r = t["residual"].cuda() if residual and "residual" in t else None
+    hh = (torch.empty_like(x) if h is None else h) if r is not None else None
+    mbr.rmsnorm_dynamic_quant_fwd_ex(x, w, q, s, eps, qtype, r, hh, cfg)
+    torch.cuda.synchronize()
+    return (hh.cpu() if hh is not None else None), q.cpu().numpy(), s.cpu().numpy()
+
+
+def check(w, t, qtype, cfg=None, eps=None):
+    eps = w.eps if eps is None else eps
+    xb, wb = inputs.bits(t["x"]), inputs.bits(t["weight"])
+    rb = inputs.bits(t["residual"]) if w.fused else None
+    h_g, q_g, s_g = run_quant(t, qtype, eps, cfg)
+    h_o, q_o, s_o = parity.oracle_quant(xb, wb, eps, qtype, residual=rb)
+    if w.fused:
+        assert np.array_equal(inputs.bits(h_g), h_o), "residual sum differs"
+    v = h_o if w.fused else xb
+    q_o_view = q_o.view(np.uint8) if qtype == 0 else q_o
+    q_g_view = q_g.view(np.int8) if qtype == 0 else q_g
+    return parity.compare_quant(q_g_view, q_o if qtype == 0 else q_o_view, s_g, s_o,
+                                parity.quant_t(v, wb, qtype), qtype)
+
+
+@pytest.mark.parametrize("q", ["int8", "fp8"])
+@pytest.mark.parametrize("name", ["bf16_residual_12289x5120", inputs.HEADLINE, "bf16_prefill_4096x2048",
+                                  "fp32_64x2048", "bf16_decode_256x4096"])
+def test_stated_shapes_full_size(name, q):
+    w = inputs.WORKLOADS[name]
+    cfg = mbr.rmsnorm_select_quant_config(w.rows, w.hidden, BF16 if w.dtype == "bf16" else F32, True, w.fused)
+    say("quant", q, name, cfg)
+    say(check(w, inputs.make(w, seed=0), QT[q]))
+
+
+RAGGED = [(1, 1), (3, 7), (5, 9), (67, 127), (12, 769), (5, 2048), (3, 4095), (7, 5120), (5, 5121), (3, 8193),
+          (2, 20000), (2, 65536), (2, 131080)]
+
+
+@pytest.mark.parametrize("q", ["int8", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("rows,hidden", RAGGED)
+def test_ragged_shapes(rows, hidden, dtype, fused, q):
+    w = inputs.custom(rows, hidden, dtype, fused)
+    say("quant", q, rows, hidden, dtype, fused)
+    check(w, inputs.make(w, seed=rows + hidden), QT[q])
+
+
+def _qconfigs(path):
+    vec = path == mbr.PATH_VECTOR
+    for wpr in (1, 2, 4, 8, 16):
+        for per in ((1, 2, 3, 4, 5, 6, 7, 8) if vec else (1, 2, 4, 8)):
+            if wpr == 16 and per > 4:
+                continue
+            yield wpr, per
+
+
+@pytest.mark.parametrize("q", ["int8", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("fused", [False, True])
+def test_every_quant_config(dtype, fused, q):
+    vecw = 8 if dtype == "bf16" else 4
+    n = 0
+    for wpr, vpl in _qconfigs(mbr.PATH_VECTOR):
+        lanes = 64 * wpr
+        max_rpb = (1024 if wpr == 16 else 512) // lanes
+        for nvec in sorted({lanes * vpl, max(1, lanes * vpl - 37)}):
+            for rpb, mb in ((1, 0), (max_rpb, 0), (1, 2)):
+                rows = 2 * rpb + 1
+                cfg = mbr.Config(mbr.PATH_VECTOR, wpr, vpl, rpb, mb)
+                w = inputs.custom(rows, nvec * vecw, dtype, fused)
+                say("quant vector", q, dtype, fused, cfg, "hidden", nvec * vecw)
+                check(w, inputs.make(w, seed=n), QT[q], cfg)
+                n += 1
+    for wpr, epl in _qconfigs(mbr.PATH_ELEMENT):
+        lanes = 64 * wpr
+        hidden = max(1, lanes * epl - 5)
+        cfg = mbr.Config(mbr.PATH_ELEMENT, wpr, epl, 1, 0)
+        w = inputs.custom(3, hidden, dtype, fused)
+        say("quant element", q, dtype, fused, cfg, "hidden", hidden)
+        check(w, inputs.make(w, seed=n), QT[q], cfg)
+        n += 1
+    for wpr in (1, 4, 16):
+        for hidden in (4096, 4099):
+            cfg = mbr.Config(mbr.PATH_TWO_PASS, wpr, 0, 1, 0)
+            w = inputs.custom(5, hidden, dtype, fused)
+            say("quant two-pass", q, dtype, fused, cfg, "hidden", hidden)
+            check(w, inputs.make(w, seed=n), QT[q], cfg)
+            n += 1
+    assert n > 100
+
+
+@pytest.mark.parametrize("q", ["int8", "fp8"])
+def test_zero_rows_and_degenerate(q):
+    """A zero row gets scale 0 and zero codes; a row with one non-zero element
+    maps it to full scale."""
+    H = 2048
+    x = torch.randn(4, H, generator=torch.Generator().manual_seed(3)).to(BF16)
+    x[1] = 0
+    x[2] = 0
+    x[2, 77] = -2.5
+    wt = (1 + 0.1 * torch.randn(H, generator=torch.Generator().manual_seed(4))).to(BF16)
+    t = {"x": x, "weight": wt}
+    w = inputs.custom(4, H, "bf16", False)
+    check(w, t, QT[q])
+    _, qq, ss = run_quant(t, QT[q], w.eps)
+    assert ss[1] == 0 and np.all(qq[1] == 0)
+    assert qq[2, 77] == (0x81 if q == "int8" else 0xFE) and np.sum(qq[2] != 0) == 1
+
+
+@pytest.mark.parametrize("alias", ["x", "residual"])
+def test_residual_out_aliases_an_input(alias):
+    w = inputs.custom(129, 5120, "bf16", True)
+    t = inputs.make(w, seed=9)
+    want = parity.oracle_quant(inputs.bits(t["x"]), inputs.bits(t["weight"]), w.eps, 0,
+                               residual=inputs.bits(t["residual"]))
+    x, r, wt = t["x"].cuda(), t["residual"].cuda(), t["weight"].cuda()
+    h = x if alias == "x" else r
+    q = torch.empty(x.shape, dtype=torch.int8, device="cuda")
+    s = torch.empty(129, dtype=torch.float32, device="cuda")
+    mbr.rmsnorm_dynamic_quant_fwd(x, wt, q, s, w.eps, mbr.QUANT_INT8, r, h)
+    torch.cuda.synchronize()
+    assert np.array_equal(inputs.bits(h), want[0])
+    parity.compare_quant(q.cpu().numpy(), want[1], s.cpu().numpy(), want[2],
+                         parity.quant_t(want[0], inputs.bits(t["weight"]), 0), 0)
+
+
+def test_quant_matches_plain_path_codes_are_deterministic():
+    w = inputs.WORKLOADS["bf16_residual_12289x5120"]
+    t = inputs.make(w, seed=0, rows=2000)
+    a = run_quant(t, mbr.QUANT_FP8_E4M3, w.eps)
+    b = run_quant(t, mbr.QUANT_FP8_E4M3, w.eps)
+    assert np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2])
+    # h of the quantised form equals h of the plain fused form bitwise
+    x, r, wt = t["x"].cuda(), t["residual"].cuda(), t["weight"].cuda()
+    h2, y2 = torch.empty_like(x), torch.empty_like(x)
+    mbr.rmsnorm_residual_fwd(x, r, wt, h2, y2, w.eps)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], h2.cpu())
+
+
+def test_quant_rejects_overlaps_on_device_buffers():
+    x = torch.zeros(4, 256, dtype=BF16, device="cuda")
+    wt = torch.ones(256, dtype=BF16, device="cuda")
+    s = torch.zeros(4, dtype=torch.float32, device="cuda")
+    L = mbr.lib()
+    st = L.rmsnorm_dynamic_quant_fwd(x.data_ptr(), None, wt.data_ptr(), None, x.data_ptr() + 64, s.data_ptr(),
+                                     4, 256, 1e-5, 1, 0, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == mbr.RMSNORM_ERR_INVALID_ARG and torch.count_nonzero(x) == 0
