@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=inputs.HEADLINE, choices=sorted(inputs.WORKLOADS))
+    ap.add_argument("--workload", default=inputs.HEADLINE, choices=sorted(inputs.ALL_WORKLOADS))
     ap.add_argument("--all", action="store_true", help="also time every other workload (stderr)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline budget; 0 disables it")
     ap.add_argument("--no-copy", action="store_true", help="skip the copy-ceiling measurement")
@@ -76,6 +76,9 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
+QUANT_CODE = {"int8": mbr.QUANT_INT8, "fp8": mbr.QUANT_FP8_E4M3}
+
+
 class Sets:
     """Rotating device copies of one workload's inputs and outputs."""
 
@@ -88,21 +91,29 @@ class Sets:
             if w.fused:
                 s["residual"] = dev["residual"] if i == 0 else dev["residual"].clone()
                 s["h"] = torch.empty_like(s["x"])
-            s["out"] = torch.empty_like(s["x"])
+            if w.quant:
+                s["q"] = torch.empty(s["x"].shape, dtype=torch.uint8, device="cuda")
+                s["scale"] = torch.empty(w.rows, dtype=torch.float32, device="cuda")
+            else:
+                s["out"] = torch.empty_like(s["x"])
             self.sets.append(s)
         self.fused = w.fused
+        self.quant = QUANT_CODE[w.quant] if w.quant else None
         self.eps = w.eps
 
     def launch(self, i):
         s = self.sets[i % len(self.sets)]
-        if self.fused:
+        if self.quant is not None:
+            mbr.rmsnorm_dynamic_quant_fwd(s["x"], self.weight, s["q"], s["scale"], self.eps, self.quant,
+                                          s.get("residual"), s.get("h"))
+        elif self.fused:
             mbr.rmsnorm_residual_fwd(s["x"], s["residual"], self.weight, s["h"], s["out"], self.eps)
         else:
             mbr.rmsnorm_fwd(s["x"], self.weight, s["out"], self.eps)
 
 
 def n_sets_for(w) -> int:
-    per_set = (4 if w.fused else 2) * w.rows * w.hidden * w.elem_size
+    per_set = w.algorithmic_bytes - w.hidden * w.elem_size
     return max(2, -(-MIN_FOOTPRINT // per_set))
 
 
@@ -147,7 +158,7 @@ def graph_time(fn, n_sets, replays=10):
 
 def copy_ceiling(w, steps, warmup):
     """hbm_copy of the same read/write byte count as one step, rotated the same way."""
-    nbytes = w.rows * w.hidden * w.elem_size * (2 if w.fused else 1)
+    nbytes = w.copy_bytes
     n = max(2, -(-MIN_FOOTPRINT // (2 * nbytes)))
     src = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(i % 251) for i in range(n)]
     dst = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(n)]
@@ -195,13 +206,17 @@ def cpu_baseline(w, t, seconds):
     wb = inputs.bits(t["weight"])
     rb = inputs.bits(t["residual"])[:rows] if w.fused else None
     per_thread = [(i * rows // T, (i + 1) * rows // T) for i in range(T)]
+    qt = {"int8": oracle.QUANT_INT8, "fp8": oracle.QUANT_FP8_E4M3}.get(w.quant)
 
     def one_pass():
         with concurrent.futures.ThreadPoolExecutor(T) as ex:
             def job(r):
                 if r[0] == r[1]:
                     return
-                if w.fused:
+                if qt is not None:
+                    oracle.rmsnorm_dynamic_quant_fwd(xb[r[0]:r[1]], wb, w.eps, qt,
+                                                     residual=rb[r[0]:r[1]] if w.fused else None)
+                elif w.fused:
                     oracle.rmsnorm_residual_fwd(xb[r[0]:r[1]], rb[r[0]:r[1]], wb, w.eps)
                 else:
                     oracle.rmsnorm_fwd(xb[r[0]:r[1]], wb, w.eps)
@@ -216,7 +231,8 @@ def cpu_baseline(w, t, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    sample_bytes = ((4 if w.fused else 2) * rows * w.hidden + w.hidden) * w.elem_size
+    sample_bytes = inputs.Workload(w.name, w.dtype, rows, w.hidden, w.eps, w.fused, w.x, w.weight, w.residual,
+                                   quant=w.quant).algorithmic_bytes
     return {"value": round(sample_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": T, "kind": "oracle",
             "sample": "first %d of %d rows, %d passes in %.1f s on %d threads (%s)"
                       % (rows, w.rows, reps, el, T, cpu_model())}
@@ -229,10 +245,11 @@ def bench_workload(w, steps, warmup, seed, with_copy=True, graph=False):
     wall, ev = time_steps(sets.launch, steps, warmup)
     nbytes = w.algorithmic_bytes
     kern_s = ev / steps
-    cfg = mbr.rmsnorm_select_config(w.rows, w.hidden, torch.float32 if w.dtype == "f32" else torch.bfloat16,
-                                    True, w.fused)
+    select = mbr.rmsnorm_select_quant_config if w.quant else mbr.rmsnorm_select_config
+    cfg = select(w.rows, w.hidden, torch.float32 if w.dtype == "f32" else torch.bfloat16, True, w.fused)
     rec = {
         "workload": w.name, "rows": w.rows, "hidden": w.hidden, "dtype": w.dtype, "fused": w.fused,
+        "quant": w.quant,
         "eps": w.eps, "algorithmic_bytes": nbytes, "rotation_sets": n_sets,
         "wall_s": wall, "event_s": ev, "us_per_call": kern_s * 1e6,
         "gbps_wall": nbytes * steps / wall / 1e9, "gbps_kernel": nbytes / kern_s / 1e9,
@@ -261,14 +278,15 @@ def main():
         print("bench.py needs a GPU (HIP device); none is visible", file=sys.stderr)
         sys.exit(1)
     mbr.lib()  # fail loudly if the HIP library is not built
-    w = inputs.WORKLOADS[args.workload]
+    w = inputs.ALL_WORKLOADS[args.workload]
     log("# device:", torch.cuda.get_device_name(0), "| workload:", w.name, "| steps", args.steps, "warmup", args.warmup)
     t, rec = bench_workload(w, args.steps, args.warmup, args.seed, not args.no_copy)
     log("# timed:", json.dumps(rec))
 
     achieved = rec["gbps_kernel"]
     line = {
-        "metric": "bf16 RMSNorm achieved HBM GB/s and % of peak at 16384×8192",
+        "metric": "bf16 RMSNorm achieved HBM GB/s and % of peak at 16384×8192" if w.name == inputs.HEADLINE
+                  else "RMSNorm achieved HBM GB/s (%s)" % w.name,
         "value": round(rec["gbps_wall"], 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -281,9 +299,10 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded; x ~ N(0,1) with 8 outlier channels x100, weight ~ N(1, 0.1))"
                 if w.name == inputs.HEADLINE else "synthetic (seeded)",
-        "config": {"workload": "RMSNorm %s [%d, %d]%s, eps %g" % (w.dtype, w.rows, w.hidden,
-                                                                  " fused residual" if w.fused else "", w.eps),
-                   "rows": w.rows, "hidden": w.hidden, "fused": w.fused,
+        "config": {"workload": "RMSNorm %s [%d, %d]%s%s, eps %g" % (
+                       w.dtype, w.rows, w.hidden, " fused residual" if w.fused else "",
+                       " with %s dynamic quantisation" % w.quant if w.quant else "", w.eps),
+                   "rows": w.rows, "hidden": w.hidden, "fused": w.fused, "quant": w.quant,
                    "algorithmic_bytes_per_step": w.algorithmic_bytes, "rotation_sets": rec["rotation_sets"],
                    "launch": rec["kernel_config"]},
         "pct_of_peak": round(100 * rec["gbps_wall"] / HBM_PEAK_GBPS, 2),
@@ -298,7 +317,7 @@ def main():
         line["copy_ceiling_gbps"] = round(rec["copy_ceiling_gbps"], 2)
         line["frac_of_copy_ceiling"] = round(rec["frac_of_copy_ceiling"], 4)
     if args.all:
-        for name, other in inputs.WORKLOADS.items():
+        for name, other in inputs.ALL_WORKLOADS.items():
             if name == w.name:
                 continue
             _, r = bench_workload(other, args.steps, args.warmup, args.seed, graph=True)

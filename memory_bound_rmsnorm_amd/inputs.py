@@ -50,11 +50,32 @@ class Workload:
     residual: Optional[Dist] = None
     outlier_columns: Tuple[int, ...] = ()
     outlier_scale: float = 1.0
+    quant: Optional[str] = None  # None: normalised output; "int8" / "fp8": codes + per-row scale
     note: str = field(default="", compare=False)
 
     @property
     def elem_size(self) -> int:
         return 4 if self.dtype == "f32" else 2
+
+    @property
+    def read_bytes(self) -> int:
+        return ((2 if self.fused else 1) * self.rows * self.hidden + self.hidden) * self.elem_size
+
+    @property
+    def write_bytes(self) -> int:
+        h = self.rows * self.hidden * self.elem_size if self.fused else 0
+        if self.quant:
+            return h + self.rows * self.hidden + 4 * self.rows
+        return h + self.rows * self.hidden * self.elem_size
+
+    @property
+    def copy_bytes(self) -> int:
+        """Size of the plain copy that moves the same traffic (read == written):
+        the output bytes for the normalised forms, half the ledger (rounded
+        down to 16 bytes) for the quantised ones."""
+        if self.quant:
+            return (self.algorithmic_bytes // 2) & ~15
+        return self.write_bytes
 
     @property
     def algorithmic_bytes(self) -> int:
@@ -63,8 +84,7 @@ class Workload:
         Byte ledger rule: TileLang tutorial ch. 02, section 2.1 (every input
         stored tensor read once, every output written once, intermediates not
         counted)."""
-        streams = 4 if self.fused else 2
-        return (streams * self.rows * self.hidden + self.hidden) * self.elem_size
+        return self.read_bytes + self.write_bytes
 
 
 N01 = Dist("normal", 0.0, 1.0)
@@ -89,6 +109,18 @@ WORKLOADS: Dict[str, Workload] = {
 }
 
 HEADLINE = "bf16_16384x8192"
+
+# The same inputs with the output quantised per row (int8 or fp8 e4m3fn codes
+# plus one fp32 scale per row): the Add + RmsNorm + DynamicQuant fusion.
+QUANT_WORKLOADS: Dict[str, Workload] = {}
+for _base in ("bf16_16384x8192", "bf16_residual_12289x5120"):
+    for _q in ("int8", "fp8"):
+        _w = WORKLOADS[_base]
+        _name = _base.replace("bf16_", "bf16_%s_" % _q, 1)
+        QUANT_WORKLOADS[_name] = Workload(_name, _w.dtype, _w.rows, _w.hidden, _w.eps, _w.fused, _w.x, _w.weight,
+                                          _w.residual, _w.outlier_columns, _w.outlier_scale, quant=_q,
+                                          note=_w.note + "; %s output" % _q)
+ALL_WORKLOADS: Dict[str, Workload] = dict(WORKLOADS, **QUANT_WORKLOADS)
 
 
 def _draw(rng: np.random.Generator, d: Dist, shape) -> np.ndarray:

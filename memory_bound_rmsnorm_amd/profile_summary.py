@@ -30,7 +30,7 @@ def _is_rms(name):
 
 
 def stats(args):
-    w = inputs.WORKLOADS[args.workload]
+    w = inputs.ALL_WORKLOADS[args.workload]
     with open(args.csv) as f:
         rows = list(csv.DictReader(f))
     out = ["# rocprofv3 --kernel-trace --stats summary: RMSNorm %s [%d, %d]%s"
@@ -72,18 +72,18 @@ def _pick(means, pred):
 
 
 def pmc(args):
-    w = inputs.WORKLOADS[args.workload]
+    w = inputs.ALL_WORKLOADS[args.workload]
     fm, fn = _counter_means(args.fetch, "FETCH_SIZE")
     wm, wn = _counter_means(args.write, "WRITE_SIZE")
     rname, rfetch = _pick(fm, _is_rms)
     _, rwrite = _pick(wm, _is_rms)
     cname, cfetch = _pick(fm, lambda k: COPY_KERNEL_TAG in k)
     _, cwrite = _pick(wm, lambda k: COPY_KERNEL_TAG in k)
-    copy_bytes = w.rows * w.hidden * w.elem_size * (2 if w.fused else 1)  # read == written per dispatch
+    copy_bytes = w.copy_bytes  # read == written per dispatch, as bench.py's copy ceiling
     fscale = copy_bytes / (cfetch * 1024.0)
     wscale = copy_bytes / (cwrite * 1024.0)
-    read_alg = ((2 if w.fused else 1) * w.rows * w.hidden + w.hidden) * w.elem_size
-    write_alg = (2 if w.fused else 1) * w.rows * w.hidden * w.elem_size
+    read_alg = w.read_bytes
+    write_alg = w.write_bytes
     traffic = rfetch * 1024 * fscale + rwrite * 1024 * wscale
     out = ["# rocprofv3 --pmc summary: HBM traffic of RMSNorm %s [%d, %d]%s"
            % (w.dtype, w.rows, w.hidden, " fused residual" if w.fused else ""),
@@ -115,8 +115,8 @@ def pmc(args):
 def _launch_config(w):
     import torch
     import memory_bound_rmsnorm_amd as mbr
-    cfg = mbr.rmsnorm_select_config(w.rows, w.hidden, torch.float32 if w.dtype == "f32" else torch.bfloat16,
-                                    True, w.fused)
+    select = mbr.rmsnorm_select_quant_config if w.quant else mbr.rmsnorm_select_config
+    cfg = select(w.rows, w.hidden, torch.float32 if w.dtype == "f32" else torch.bfloat16, True, w.fused)
     return " ".join("%s=%s" % kv for kv in cfg.as_dict().items())
 
 
@@ -133,16 +133,17 @@ def resources(args):
            "# command: %s" % args.command,
            "kernels_built: %d" % len(lines),
            "kernels_with_scratch_or_spills: %d" % len(spill)]
-    for name, w in inputs.WORKLOADS.items():
-        cfg = mbr.rmsnorm_select_config(w.rows, w.hidden, torch.float32 if w.dtype == "f32" else torch.bfloat16,
-                                        True, w.fused)
+    for name, w in inputs.ALL_WORKLOADS.items():
+        select = mbr.rmsnorm_select_quant_config if w.quant else mbr.rmsnorm_select_config
+        cfg = select(w.rows, w.hidden, torch.float32 if w.dtype == "f32" else torch.bfloat16, True, w.fused)
         e = "F32" if w.dtype == "f32" else "Bf16"
         fam = {1: "rms_vec_kernel", 2: "rms_elem_kernel", 3: "rms_twopass_kernel"}[cfg.path]
         per = cfg.items_per_lane
         units = w.hidden // (4 if w.dtype == "f32" else 8)
         masked = 64 * cfg.waves_per_row * per != units
-        mangled = "%sINS_%d%sELi%dELi%dELb%dELb%dE" % (fam, len(e), e, cfg.waves_per_row, per, int(masked),
-                                                       int(w.fused))
+        qt = {None: 0, "int8": 1, "fp8": 2}[w.quant]
+        mangled = "%sINS_%d%sELi%dELi%dELb%dELb%dELi%dEEEv" % (fam, len(e), e, cfg.waves_per_row, per, int(masked),
+                                                               int(w.fused), qt)
         hit = [l for l in lines if mangled in l]
         out.append("%s -> %s | %s" % (name, cfg.as_dict(), hit[0].split("|", 1)[1].strip() if hit else "?"))
     print("\n".join(out))

@@ -32,6 +32,14 @@ def test_algorithmic_bytes():
     assert w["bf16_residual_12289x5120"].algorithmic_bytes == 503_367_680
 
 
+def test_quant_workload_bytes():
+    q = inputs.QUANT_WORKLOADS
+    assert q["bf16_int8_16384x8192"].algorithmic_bytes == (16384 * 8192 + 8192) * 2 + 16384 * 8192 + 4 * 16384
+    r, h = 12289, 5120
+    assert q["bf16_fp8_residual_12289x5120"].algorithmic_bytes == (2 * r * h + h) * 2 + r * h * 2 + r * h + 4 * r
+    assert all(w.quant in ("int8", "fp8") for w in q.values())
+
+
 def test_reproducible_and_seed_dependent():
     w = inputs.WORKLOADS["bf16_prefill_4096x2048"]
     a = inputs.make(w, seed=0, rows=64)
