@@ -123,7 +123,10 @@ bool vector_aligned(const Problem& p) {
 // two 16-byte vectors of it per lane (three for the fused form, whose lanes
 // then keep the weight resident) -- many short waves keep more requests in
 // flight than a few long ones; e.g. bf16 hidden 8192 runs as 8 waves x 2
-// vectors, the fused bf16 hidden 5120 as 4 waves x 3.  Element path: at most 8 elements per lane.  When rows are few,
+// vectors, the fused bf16 hidden 5120 as 4 waves x 3.  The quantised forms
+// store half as many bytes per vector and hold the weight anyway; they run
+// fastest with up to four (five fused) vectors per lane: 4 x 4 for hidden
+// 8192, 2 x 5 for the fused 5120.  Element path: at most 8 elements per lane.  When rows are few,
 // each row gets more waves so the whole GPU has work.  Rows that no built
 // register-resident configuration covers take the two-pass path.
 rmsnorm_config_t choose(int64_t rows, int64_t hidden, int dtype, bool aligned, bool fused, int qt) {
@@ -132,7 +135,7 @@ rmsnorm_config_t choose(int64_t rows, int64_t hidden, int dtype, bool aligned, b
     const int64_t units = vec ? hidden / vec_elems(dtype) : hidden;
     const int* list = vec ? mbr::kVplList : mbr::kEplList;
     const int nlist = vec ? mbr::kNumVpl : mbr::kNumEpl;
-    const int cap = vec ? (fused ? 3 : 2) : 8;
+    const int cap = vec ? (qt ? (fused ? 5 : 4) : (fused ? 3 : 2)) : 8;
     auto fit = [&](int wpr) {
         const int per = round_up_in(list, nlist, ceil_div(units, int64_t(64) * wpr));
         if (per < 0) return -1;
