@@ -9,8 +9,12 @@ this module only moves numpy arrays in and out of it.  Arrays are row-major
 ``[rows, hidden]``; float32 data is ``np.float32`` and bfloat16 data is the raw
 16-bit pattern in ``np.uint16``.
 
-Pinning status: every function here is checked in ``tests/test_oracle_pins.py``
-against closed forms, bit-exact special cases and an exact-rational brute force.
+Pinning status: every function here is checked against closed forms,
+bit-exact special cases and an exact-rational brute force --
+``tests/test_oracle_pins.py`` (forward, fused residual),
+``tests/test_oracle_quant_pins.py`` (dynamic quantisation) and
+``tests/test_oracle_bwd_pins.py`` (backward: 80-digit central differences of
+the forward, closed forms, invariants).
 The only unpinned choice is which bf16 neighbour is returned when the exact
 result lies within the fp64 evaluation error (about 1e-12 relative) of a
 rounding midpoint.
@@ -47,6 +51,8 @@ def _load():
         lib.oracle_round_e4m3.restype = ctypes.c_uint8
         lib.oracle_rmsnorm_dynamic_quant_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, i32]
         lib.oracle_rmsnorm_dynamic_quant_fwd.restype = i32
+        lib.oracle_rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, i32]
+        lib.oracle_rmsnorm_bwd.restype = i32
         _lib = lib
     return _lib
 
@@ -129,6 +135,27 @@ def rmsnorm_dynamic_quant_fwd(x: np.ndarray, weight: np.ndarray, eps: float, qty
     if rc != 0:
         raise RuntimeError("oracle_rmsnorm_dynamic_quant_fwd failed")
     return h, q, scale
+
+
+def rmsnorm_bwd(x: np.ndarray, weight: np.ndarray, dy: np.ndarray, eps: float, want_dw: bool = True):
+    """Returns ``(dx, dw)`` of y = RMSNorm(x) * weight for upstream gradient dy
+    (dw is None when not wanted)."""
+    x = _check(x, "x")
+    dy = _check(dy, "dy")
+    weight = np.ascontiguousarray(weight).reshape(-1)
+    code = _dtype_code(x)
+    if dy.dtype != x.dtype or dy.shape != x.shape:
+        raise ValueError("dy must match x")
+    if weight.dtype != x.dtype or weight.shape[0] != x.shape[1]:
+        raise ValueError("weight must be [hidden] with the dtype of x")
+    dx = np.empty_like(x)
+    dw = np.empty_like(weight) if want_dw else None
+    rc = _load().oracle_rmsnorm_bwd(x.ctypes.data, weight.ctypes.data, dy.ctypes.data, dx.ctypes.data,
+                                    dw.ctypes.data if dw is not None else None, x.shape[0], x.shape[1],
+                                    float(eps), code)
+    if rc != 0:
+        raise RuntimeError("oracle_rmsnorm_bwd failed")
+    return dx, dw
 
 
 def round_e4m3(v: float) -> int:

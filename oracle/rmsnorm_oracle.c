@@ -29,6 +29,10 @@
  *   is written back in the tensor dtype and the *rounded* h is what gets
  *   normalised, i.e. the result equals an unfused add followed by RMSNorm.
  *
+ *   Backward (dx and dweight for an upstream gradient dy): the plain
+ *   derivative of the forward above, in fp64, each output rounded once; dweight
+ *   sums over all rows in ascending row order.  See oracle_rmsnorm_bwd.
+ *
  * Readings of points the pages leave open:
  *   - rounding is IEEE round-to-nearest, ties to even, directly from fp64 to
  *     the output type (no intermediate fp32 for bf16);
@@ -262,5 +266,50 @@ int oracle_rmsnorm_dynamic_quant_fwd(const void *x, const void *residual, const 
     }
     free(v);
     free(y);
+    return 0;
+}
+
+/*
+ * Backward of y = x * r * w (r = 1/sqrt(sum_k x_k^2 / H + eps)) for an
+ * upstream gradient dy -- the norm backward of a training step, which the
+ * TileLang tutorial ch. 02, section 1.1(b), describes as mirroring the
+ * forward layer by layer.  The pages give no formula; this is the plain
+ * derivative, written out in fp64:
+ *
+ *   dr/dx_k = -r^3 x_k / H, so with c = sum_j dy_j w_j x_j
+ *   dx_k    = r dy_k w_k - x_k r^3 c / H
+ *   dw_j    = sum_i dy_ij x_ij r_i        (over all rows, fp64)
+ *
+ * dx and dw are each rounded once to the dtype.  dw may be NULL (not wanted).
+ */
+int oracle_rmsnorm_bwd(const void *x, const void *w, const void *dy, void *dx, void *dw, int64_t rows,
+                       int64_t hidden, float eps, int dtype) {
+    double *acc = NULL;
+    int64_t i, j;
+    if (rows < 0 || hidden <= 0 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16)) return -1;
+    if (dw) {
+        acc = (double *)calloc((size_t)hidden, sizeof(double));
+        if (!acc) return -1;
+    }
+    for (i = 0; i < rows; ++i) {
+        double s = 0.0, c = 0.0, r;
+        for (j = 0; j < hidden; ++j) {
+            double v = load_elem(x, i * hidden + j, dtype);
+            s += v * v;
+            c += load_elem(dy, i * hidden + j, dtype) * load_elem(w, j, dtype) * v;
+        }
+        r = 1.0 / sqrt(s / (double)hidden + (double)eps);
+        for (j = 0; j < hidden; ++j) {
+            double v = load_elem(x, i * hidden + j, dtype);
+            double g = load_elem(dy, i * hidden + j, dtype);
+            store_elem(dx, i * hidden + j, r * g * load_elem(w, j, dtype) - v * r * r * r * c / (double)hidden,
+                       dtype);
+            if (acc) acc[j] += g * v * r;
+        }
+    }
+    if (acc) {
+        for (j = 0; j < hidden; ++j) store_elem(dw, j, acc[j], dtype);
+        free(acc);
+    }
     return 0;
 }

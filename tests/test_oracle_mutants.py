@@ -15,6 +15,7 @@ import oracle
 from oracle import build as oracle_build
 from tests import test_oracle_pins as pins
 from tests import test_oracle_quant_pins as qpins
+from tests import test_oracle_bwd_pins as bpins
 
 MUTANTS = [
     ("eps dropped", "sqrt(mean + (double)eps)", "sqrt(mean)"),
@@ -58,6 +59,22 @@ MUTANTS += [
      "m = round(a / spacing) * spacing;\n    if (m > 448.0) m = 448.0;"),
 ]
 
+MUTANTS += [
+    ("bwd r squared in the radial term", "v * r * r * r * c / (double)hidden", "v * r * r * c / (double)hidden"),
+    ("bwd radial term without 1/H", "v * r * r * r * c / (double)hidden", "v * r * r * r * c"),
+    ("bwd radial term added", "r * g * load_elem(w, j, dtype) - v * r", "r * g * load_elem(w, j, dtype) + v * r"),
+    ("bwd weight missing from c", "c += load_elem(dy, i * hidden + j, dtype) * load_elem(w, j, dtype) * v;",
+     "c += load_elem(dy, i * hidden + j, dtype) * v;"),
+    ("bwd weight missing from the direct term", "store_elem(dx, i * hidden + j, r * g * load_elem(w, j, dtype)",
+     "store_elem(dx, i * hidden + j, r * g"),
+    ("bwd eps dropped", "r = 1.0 / sqrt(s / (double)hidden + (double)eps);", "r = 1.0 / sqrt(s / (double)hidden);"),
+    ("bwd dw without r", "acc[j] += g * v * r;", "acc[j] += g * v;"),
+    ("bwd dw times the weight", "acc[j] += g * v * r;", "acc[j] += g * v * r * load_elem(w, j, dtype);"),
+    ("bwd dw keeps only the last row", "acc[j] += g * v * r;", "acc[j] = g * v * r;"),
+    ("bwd dy read transposed", "double g = load_elem(dy, i * hidden + j, dtype);",
+     "double g = load_elem(dy, j * rows + i, dtype);"),
+]
+
 HELPER = """
 static float oracle_bf16_back(uint16_t b) { uint32_t u = (uint32_t)b << 16; float f; memcpy(&f, &u, 4); return f; }
 """
@@ -88,6 +105,15 @@ PIN_TESTS = [
     (qpins.test_scale_closed_form_constant_row, dict(qtype=0)),
     (qpins.test_row_max_maps_to_full_scale_and_zero_row, dict(qtype=1)),
     (qpins.test_fused_quant_uses_the_rounded_sum, dict(qtype=0)),
+    (bpins.test_matches_decimal_central_differences, dict(dtype="f32", hidden=5)),
+    (bpins.test_matches_decimal_central_differences, dict(dtype="bf16", hidden=8)),
+    (bpins.test_single_column_closed_form, dict(dtype="f32")),
+    (bpins.test_orthogonal_to_x_without_eps, {}),
+    (bpins.test_eps_component_along_x, {}),
+    (bpins.test_power_of_two_scaling_without_eps, dict(k=5)),
+    (bpins.test_weight_gradient_identity, {}),
+    (bpins.test_linear_in_dy_and_zero_gradient, {}),
+    (bpins.test_rows_independent_and_dw_sums_rows, {}),
 ]
 
 
