@@ -4,7 +4,9 @@
 A step is one rmsnorm_fwd call (or rmsnorm_residual_fwd for the fused
 workload) over a whole [rows, hidden] batch: load rows, sum squares, inverse
 root, scale and store.  Default workload: bf16 [16384, 8192], the
-large-hidden configuration the headline bandwidth figure is quoted on.
+large-hidden configuration the headline bandwidth figure is quoted on.  The
+quantised workloads time rmsnorm_dynamic_quant_fwd, the backward ones
+rmsnorm_bwd (dx and dweight: the row kernel plus the dweight reduction).
 
 Byte accounting follows the TileLang tutorial ch. 02, section 2.1: every input
 read once, every output written once, the weight once; the figure reported is
@@ -34,6 +36,7 @@ import torch
 
 import memory_bound_rmsnorm_amd as mbr
 from memory_bound_rmsnorm_amd import _build, inputs
+from memory_bound_rmsnorm_amd.profile_summary import launch_config
 
 HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 MIN_FOOTPRINT = 2 << 30
@@ -86,8 +89,18 @@ class Sets:
         dev = {k: v.cuda() for k, v in t.items()}
         self.weight = dev["weight"]
         self.sets = []
+        self.backward = w.backward
+        if w.backward:
+            nbytes = mbr.rmsnorm_bwd_workspace_size(w.rows, w.hidden, self.weight.dtype)
+            self.workspace = torch.empty(max(1, nbytes), dtype=torch.uint8, device="cuda")
         for i in range(n_sets):
             s = {"x": dev["x"] if i == 0 else dev["x"].clone()}
+            if w.backward:
+                s["dy"] = dev["dy"] if i == 0 else dev["dy"].clone()
+                s["dx"] = torch.empty_like(s["x"])
+                s["dw"] = torch.empty_like(self.weight)
+                self.sets.append(s)
+                continue
             if w.fused:
                 s["residual"] = dev["residual"] if i == 0 else dev["residual"].clone()
                 s["h"] = torch.empty_like(s["x"])
@@ -103,7 +116,9 @@ class Sets:
 
     def launch(self, i):
         s = self.sets[i % len(self.sets)]
-        if self.quant is not None:
+        if self.backward:
+            mbr.rmsnorm_bwd(s["x"], self.weight, s["dy"], s["dx"], s["dw"], self.eps, self.workspace)
+        elif self.quant is not None:
             mbr.rmsnorm_dynamic_quant_fwd(s["x"], self.weight, s["q"], s["scale"], self.eps, self.quant,
                                           s.get("residual"), s.get("h"))
         elif self.fused:
@@ -169,12 +184,15 @@ def copy_ceiling(w, steps, warmup):
 
 
 KERNEL_FAMILY = {"vector": "rms_vec_kernel", "element": "rms_elem_kernel", "two_pass": "rms_twopass_kernel"}
+BWD_KERNEL_FAMILY = {"vector": "rms_bwd_vec_kernel", "element": "rms_bwd_elem_kernel",
+                     "two_pass": "rms_bwd_twopass_kernel"}
 
 
 def load_traffic(w, launch):
-    """HBM bytes per launch from the committed counter summary, if it was taken
+    """HBM bytes per step from the committed counter summary, if it was taken
     on the current kernel sources in the current launch configuration; else None."""
-    path = os.path.join(PROFILE_DIR, "pmc_traffic_%s_%s.txt" % (KERNEL_FAMILY[launch["path"]], w.name))
+    fam = (BWD_KERNEL_FAMILY if w.backward else KERNEL_FAMILY)[launch["path"]]
+    path = os.path.join(PROFILE_DIR, "pmc_traffic_%s_%s.txt" % (fam, w.name))
     if not os.path.exists(path):
         return None
     vals = {}
@@ -185,7 +203,7 @@ def load_traffic(w, launch):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
     try:
-        if vals.get("source_sha256") != _build.source_digest():
+        if vals.get("source_sha256") != _build.source_digest("bwd" if w.backward else "fwd"):
             return None
         if vals.get("launch_config") != " ".join("%s=%s" % kv for kv in launch.items()):
             return None
@@ -205,6 +223,7 @@ def cpu_baseline(w, t, seconds):
     xb = inputs.bits(t["x"])[:rows]
     wb = inputs.bits(t["weight"])
     rb = inputs.bits(t["residual"])[:rows] if w.fused else None
+    gb = inputs.bits(t["dy"])[:rows] if w.backward else None
     per_thread = [(i * rows // T, (i + 1) * rows // T) for i in range(T)]
     qt = {"int8": oracle.QUANT_INT8, "fp8": oracle.QUANT_FP8_E4M3}.get(w.quant)
 
@@ -213,7 +232,9 @@ def cpu_baseline(w, t, seconds):
             def job(r):
                 if r[0] == r[1]:
                     return
-                if qt is not None:
+                if w.backward:  # each thread: dx and its rows' dweight
+                    oracle.rmsnorm_bwd(xb[r[0]:r[1]], wb, gb[r[0]:r[1]], w.eps)
+                elif qt is not None:
                     oracle.rmsnorm_dynamic_quant_fwd(xb[r[0]:r[1]], wb, w.eps, qt,
                                                      residual=rb[r[0]:r[1]] if w.fused else None)
                 elif w.fused:
@@ -232,7 +253,7 @@ def cpu_baseline(w, t, seconds):
         if el >= seconds:
             break
     sample_bytes = inputs.Workload(w.name, w.dtype, rows, w.hidden, w.eps, w.fused, w.x, w.weight, w.residual,
-                                   quant=w.quant).algorithmic_bytes
+                                   quant=w.quant, grad=w.grad).algorithmic_bytes
     return {"value": round(sample_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": T, "kind": "oracle",
             "sample": "first %d of %d rows, %d passes in %.1f s on %d threads (%s)"
                       % (rows, w.rows, reps, el, T, cpu_model())}
@@ -245,11 +266,10 @@ def bench_workload(w, steps, warmup, seed, with_copy=True, graph=False):
     wall, ev = time_steps(sets.launch, steps, warmup)
     nbytes = w.algorithmic_bytes
     kern_s = ev / steps
-    select = mbr.rmsnorm_select_quant_config if w.quant else mbr.rmsnorm_select_config
-    cfg = select(w.rows, w.hidden, torch.float32 if w.dtype == "f32" else torch.bfloat16, True, w.fused)
+    cfg = launch_config(w)
     rec = {
         "workload": w.name, "rows": w.rows, "hidden": w.hidden, "dtype": w.dtype, "fused": w.fused,
-        "quant": w.quant,
+        "quant": w.quant, "backward": w.backward,
         "eps": w.eps, "algorithmic_bytes": nbytes, "rotation_sets": n_sets,
         "wall_s": wall, "event_s": ev, "us_per_call": kern_s * 1e6,
         "gbps_wall": nbytes * steps / wall / 1e9, "gbps_kernel": nbytes / kern_s / 1e9,
@@ -286,7 +306,7 @@ def main():
     achieved = rec["gbps_kernel"]
     line = {
         "metric": "bf16 RMSNorm achieved HBM GB/s and % of peak at 16384×8192" if w.name == inputs.HEADLINE
-                  else "RMSNorm achieved HBM GB/s (%s)" % w.name,
+                  else "RMSNorm%s achieved HBM GB/s (%s)" % (" backward" if w.backward else "", w.name),
         "value": round(rec["gbps_wall"], 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -299,10 +319,11 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded; x ~ N(0,1) with 8 outlier channels x100, weight ~ N(1, 0.1))"
                 if w.name == inputs.HEADLINE else "synthetic (seeded)",
-        "config": {"workload": "RMSNorm %s [%d, %d]%s%s, eps %g" % (
-                       w.dtype, w.rows, w.hidden, " fused residual" if w.fused else "",
+        "config": {"workload": "RMSNorm %s%s [%d, %d]%s%s, eps %g" % (
+                       "backward (dx, dweight) " if w.backward else "", w.dtype, w.rows, w.hidden,
+                       " fused residual" if w.fused else "",
                        " with %s dynamic quantisation" % w.quant if w.quant else "", w.eps),
-                   "rows": w.rows, "hidden": w.hidden, "fused": w.fused, "quant": w.quant,
+                   "rows": w.rows, "hidden": w.hidden, "fused": w.fused, "quant": w.quant, "backward": w.backward,
                    "algorithmic_bytes_per_step": w.algorithmic_bytes, "rotation_sets": rec["rotation_sets"],
                    "launch": rec["kernel_config"]},
         "pct_of_peak": round(100 * rec["gbps_wall"] / HBM_PEAK_GBPS, 2),
@@ -311,7 +332,9 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": load_traffic(w, rec["kernel_config"])},
         "parity": "checked against the CPU oracle at this size and launch configuration by "
-                  "tests/test_parity_gpu.py::test_stated_workloads_full_size",
+                  + ("tests/test_bwd_gpu.py::test_bwd_workloads_full_size" if w.backward else
+                     "tests/test_quant_gpu.py" if w.quant else
+                     "tests/test_parity_gpu.py::test_stated_workloads_full_size"),
     }
     if "copy_ceiling_gbps" in rec:
         line["copy_ceiling_gbps"] = round(rec["copy_ceiling_gbps"], 2)

@@ -17,8 +17,9 @@
  *
  * Conventions shared by every entry point:
  *   - Pointers are DEVICE pointers (HIP device memory, e.g. torch CUDA-tensor
- *     storage).  The caller owns every buffer; the library allocates nothing,
- *     needs no workspace and keeps no per-call state.
+ *     storage).  The caller owns every buffer; the library allocates nothing
+ *     and keeps no per-call state.  Only the backward's weight gradient needs
+ *     scratch memory, which the caller passes in as a workspace.
  *   - Tensors are contiguous and row-major; weight is [hidden]; all tensors
  *     share one dtype.  Any element-aligned address is accepted; 16-byte
  *     vector accesses are used only when every pointer is 16-byte aligned and
@@ -44,6 +45,7 @@
 #ifndef MBR_RMSNORM_H
 #define MBR_RMSNORM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #define RMSNORM_API __attribute__((visibility("default")))
@@ -223,6 +225,65 @@ RMSNORM_API rmsnorm_status_t rmsnorm_select_quant_config(int64_t rows, int64_t h
                                                          rmsnorm_dtype_t dtype,
                                                          int32_t vector_aligned, int32_t fused,
                                                          rmsnorm_config_t* cfg);
+
+/*
+ * Backward.  For y = RMSNorm(x) * weight and an upstream gradient dy, the
+ * norm backward of a training step's backward stage (TileLang tutorial ch. 02,
+ * "从 PyTorch 到 kernel", section 1.1(b); the pages give no formula, this is
+ * the plain derivative), per row with r = rsqrt(sum_k x_k^2 / hidden + eps):
+ *
+ *     dx_k      = r * (dy_k * weight_k - x_k * r^2 * c / hidden),
+ *                 c = sum_j dy_j * weight_j * x_j
+ *     dweight_j = sum_i dy_ij * x_ij * r_i          (over all rows)
+ *
+ * evaluated in fp32 and rounded once to the tensor dtype.  dweight is reduced
+ * across rows in two fixed-order stages (per-workgroup fp32 partial rows in
+ * the workspace, then a column sum), so results are bitwise reproducible for
+ * equal inputs, shape and configuration; no atomics.  Workspace handling
+ * follows the create / query-workspace / execute pattern of the Intro-ops
+ * operator runtime's public C header (include/operator_runtime/api.h).
+ *
+ * rmsnorm_bwd:
+ *   x, weight  the forward's inputs ([rows, hidden], [hidden]).
+ *   dy         [rows, hidden] upstream gradient, same dtype.
+ *   dx         [rows, hidden] output; may be x or dy itself (exactly), must
+ *              not touch weight or partially overlap x or dy.
+ *   dweight    [hidden] output, or NULL when the weight gradient is not
+ *              wanted (then workspace is ignored).  Overwritten, not
+ *              accumulated into.  Overlaps nothing.  With rows == 0 it is
+ *              set to zero and the other pointers are not used.
+ *   workspace  device memory of at least rmsnorm_bwd_workspace_size() bytes,
+ *              16-byte aligned, overlapping nothing; contents on entry are
+ *              irrelevant and are clobbered.  May be NULL when the size is 0.
+ *              The same workspace must not be in use by another call that
+ *              may run concurrently (another stream).
+ *   workspace_bytes  its size; smaller than needed is INVALID_ARG.
+ *   rows, hidden, eps, dtype, stream: as rmsnorm_fwd.
+ * Enqueues one kernel for dx (and the partial rows), plus one for dweight.
+ */
+RMSNORM_API rmsnorm_status_t rmsnorm_bwd(const void* x, const void* weight, const void* dy, void* dx,
+                                         void* dweight, int64_t rows, int64_t hidden, float eps,
+                                         rmsnorm_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                         void* stream);
+
+/* rmsnorm_bwd with a launch configuration (NULL or path AUTO = automatic).
+ * rows_per_block must be 1; max_blocks caps the grid and is the number of
+ * partial dweight rows (0 = no cap). */
+RMSNORM_API rmsnorm_status_t rmsnorm_bwd_ex(const void* x, const void* weight, const void* dy, void* dx,
+                                            void* dweight, int64_t rows, int64_t hidden, float eps,
+                                            rmsnorm_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                            const rmsnorm_config_t* cfg, void* stream);
+
+/* Bytes of workspace rmsnorm_bwd (cfg NULL or AUTO: any pointer alignment) or
+ * rmsnorm_bwd_ex with cfg needs to produce dweight:
+ * min(rows, partial rows) * round_up(hidden, 64) * 4.  No HIP call. */
+RMSNORM_API rmsnorm_status_t rmsnorm_bwd_workspace_size(int64_t rows, int64_t hidden, rmsnorm_dtype_t dtype,
+                                                        const rmsnorm_config_t* cfg, size_t* bytes);
+
+/* The configuration rmsnorm_bwd would choose (max_blocks = its partial-row
+ * cap).  No HIP call. */
+RMSNORM_API rmsnorm_status_t rmsnorm_select_bwd_config(int64_t rows, int64_t hidden, rmsnorm_dtype_t dtype,
+                                                       int32_t vector_aligned, rmsnorm_config_t* cfg);
 
 #ifdef __cplusplus
 }

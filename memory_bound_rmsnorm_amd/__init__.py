@@ -13,7 +13,15 @@ fallback -- if the library is not built, every call raises.
     rmsnorm_dynamic_quant_fwd(x, weight, q_out, scale_out, eps, qtype, residual, residual_out)
     rmsnorm_dynamic_quant_fwd_ex(..., config)                   forced launch configuration
     rmsnorm_select_quant_config(rows, hidden, dtype, vector_aligned, fused) -> Config
+    rmsnorm_bwd(x, weight, dy, dx, dweight, eps, workspace)    -> (dx, dweight)
+    rmsnorm_bwd_ex(..., config)                                forced launch configuration
+    rmsnorm_bwd_workspace_size(rows, hidden, dtype, config)    -> bytes
+    rmsnorm_select_bwd_config(rows, hidden, dtype, vector_aligned) -> Config
     rmsnorm_status_string(status)                              -> str
+
+The backward's weight gradient needs a workspace; when none is passed, a
+torch byte tensor of the queried size is allocated for the call (device
+memory is the only thing torch provides here).
 """
 import ctypes
 import os
@@ -86,11 +94,16 @@ def lib() -> ctypes.CDLL:
         L.rmsnorm_select_quant_config.argtypes = [i64, i64, i32, i32, i32, cfgp]
         L.rmsnorm_dynamic_quant_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, vp]
         L.rmsnorm_dynamic_quant_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, cfgp, vp]
+        L.rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, i32, vp, ctypes.c_size_t, vp]
+        L.rmsnorm_bwd_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, i32, vp, ctypes.c_size_t, cfgp, vp]
+        L.rmsnorm_bwd_workspace_size.argtypes = [i64, i64, i32, cfgp, ctypes.POINTER(ctypes.c_size_t)]
+        L.rmsnorm_select_bwd_config.argtypes = [i64, i64, i32, i32, cfgp]
         L.rmsnorm_status_string.argtypes = [i32]
         L.rmsnorm_status_string.restype = ctypes.c_char_p
         for fn in (L.rmsnorm_fwd, L.rmsnorm_residual_fwd, L.rmsnorm_fwd_ex, L.rmsnorm_residual_fwd_ex,
                    L.rmsnorm_select_config, L.rmsnorm_select_quant_config, L.rmsnorm_dynamic_quant_fwd,
-                   L.rmsnorm_dynamic_quant_fwd_ex):
+                   L.rmsnorm_dynamic_quant_fwd_ex, L.rmsnorm_bwd, L.rmsnorm_bwd_ex, L.rmsnorm_bwd_workspace_size,
+                   L.rmsnorm_select_bwd_config):
             fn.restype = i32
         _lib = L
     return _lib
@@ -251,6 +264,63 @@ def rmsnorm_select_quant_config(rows: int, hidden: int, dtype, vector_aligned: b
     _check(lib().rmsnorm_select_quant_config(int(rows), int(hidden), code, int(bool(vector_aligned)),
                                              int(bool(fused)), ctypes.byref(cfg)), "rmsnorm_select_quant_config")
     return cfg
+
+
+def rmsnorm_bwd_workspace_size(rows: int, hidden: int, dtype, config: Optional[Config] = None) -> int:
+    """Workspace bytes the backward needs for dweight (C: rmsnorm_bwd_workspace_size)."""
+    code = dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype)
+    n = ctypes.c_size_t()
+    _check(lib().rmsnorm_bwd_workspace_size(int(rows), int(hidden), code,
+                                            ctypes.byref(config) if config is not None else None,
+                                            ctypes.byref(n)), "rmsnorm_bwd_workspace_size")
+    return int(n.value)
+
+
+def rmsnorm_select_bwd_config(rows: int, hidden: int, dtype, vector_aligned: bool = True) -> Config:
+    code = dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype)
+    cfg = Config()
+    _check(lib().rmsnorm_select_bwd_config(int(rows), int(hidden), code, int(bool(vector_aligned)),
+                                           ctypes.byref(cfg)), "rmsnorm_select_bwd_config")
+    return cfg
+
+
+def rmsnorm_bwd_ex(x, weight, dy, dx, dweight=None, eps: float = 1e-5, workspace=None,
+                   config: Optional[Config] = None, stream=None):
+    """dx (and dweight unless None) of y = RMSNorm(x) * weight for the upstream
+    gradient dy, with a forced configuration.  workspace: a contiguous GPU
+    tensor of at least rmsnorm_bwd_workspace_size bytes, or None."""
+    for t, n in ((x, "x"), (weight, "weight"), (dy, "dy"), (dx, "dx")):
+        _device_tensor(t, n)
+    for t, n in ((dy, "dy"), (dx, "dx")):
+        if t.shape != x.shape or t.dtype != x.dtype:
+            raise ValueError("%s must match x in shape and dtype" % n)
+    if weight.dtype != x.dtype:
+        raise ValueError("weight must match x in dtype")
+    rows, hidden = _shape(x, weight)
+    ws_ptr, ws_bytes = None, 0
+    if dweight is not None:
+        _device_tensor(dweight, "dweight")
+        if dweight.shape != weight.shape or dweight.dtype != x.dtype:
+            raise ValueError("dweight must match weight in shape and dtype")
+        if workspace is None:
+            need = rmsnorm_bwd_workspace_size(rows, hidden, x.dtype, config)
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+            if stream is not None:  # freed on return: keep it from reuse until that stream has run
+                workspace.record_stream(stream if isinstance(stream, torch.cuda.Stream)
+                                        else torch.cuda.ExternalStream(int(stream)))
+        _device_tensor(workspace, "workspace")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    st = lib().rmsnorm_bwd_ex(x.data_ptr(), weight.data_ptr(), dy.data_ptr(), dx.data_ptr(),
+                              dweight.data_ptr() if dweight is not None else None, rows, hidden, float(eps),
+                              dtype_code(x.dtype), ws_ptr, ws_bytes,
+                              ctypes.byref(config) if config is not None else None, _stream(stream, x.device))
+    _check(st, "rmsnorm_bwd")
+    return dx, dweight
+
+
+def rmsnorm_bwd(x, weight, dy, dx, dweight=None, eps: float = 1e-5, workspace=None, stream=None):
+    """RMSNorm backward (C: rmsnorm_bwd)."""
+    return rmsnorm_bwd_ex(x, weight, dy, dx, dweight, eps, workspace, None, stream)
 
 
 def hbm_copy(src: torch.Tensor, dst: torch.Tensor, max_blocks: int = 0, stream=None):

@@ -23,7 +23,8 @@ LIB_COPY = os.path.join(HERE, "libhbm_copy.so")
 RESOURCE_USAGE = os.path.join(BUILD, "resource_usage.txt")
 
 RMSNORM_SOURCES = ["rmsnorm_api.hip", "rmsnorm_misc.hip", "rmsnorm_vec_bf16.hip", "rmsnorm_vec_f32.hip",
-                   "rmsnorm_quant_bf16.hip", "rmsnorm_quant_f32.hip", "rmsnorm_quant_misc.hip"]
+                   "rmsnorm_quant_bf16.hip", "rmsnorm_quant_f32.hip", "rmsnorm_quant_misc.hip",
+                   "rmsnorm_bwd.hip"]
 COPY_SOURCES = ["hbm_copy.hip"]
 
 # Packed-fp32 VALU forms are disabled: hipcc emits them from plain float code
@@ -105,24 +106,28 @@ def build(verbose: bool = False) -> None:
 
 
 
-KERNEL_SOURCES = ["rmsnorm_kernels.hpp", "rmsnorm_dispatch.hpp", "rmsnorm_vec_bf16.hip", "rmsnorm_vec_f32.hip",
-                  "rmsnorm_misc.hip", "rmsnorm_quant_bf16.hip", "rmsnorm_quant_f32.hip", "rmsnorm_quant_misc.hip",
-                  "hbm_copy.hip"]
+# Device sources of each kernel family (plus the copy kernel that calibrates
+# the counters).
+KERNEL_SOURCES = {
+    "fwd": ["rmsnorm_kernels.hpp", "rmsnorm_vec_bf16.hip", "rmsnorm_vec_f32.hip", "rmsnorm_misc.hip",
+            "rmsnorm_quant_bf16.hip", "rmsnorm_quant_f32.hip", "rmsnorm_quant_misc.hip", "hbm_copy.hip"],
+    "bwd": ["rmsnorm_kernels.hpp", "rmsnorm_bwd_kernels.hpp", "rmsnorm_bwd.hip", "hbm_copy.hip"],
+}
 
 
-def source_digest() -> str:
-    """sha256 over the kernel sources (device code and its instantiation
-    tables, plus the copy kernel that calibrates the counters), so that counter
-    readings taken on one version of the kernels are not quoted for another.
-    Host-side selection is checked separately through the launch configuration
-    recorded next to the counters."""
+def source_digest(family: str = "fwd") -> str:
+    """sha256 over one kernel family's device sources, so that counter readings
+    taken on one version of the kernels are not quoted for another.  Host-side
+    selection is checked separately through the launch configuration recorded
+    next to the counters."""
     import hashlib
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in KERNEL_SOURCES[family]:
         h.update(name.encode())
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
 
 if __name__ == "__main__":
     build(verbose=True)

@@ -12,6 +12,7 @@
 #include <stdint.h>
 
 #include "../../include/rmsnorm.h"
+#include "rmsnorm_bwd_kernels.hpp"
 #include "rmsnorm_dispatch.hpp"
 #include "rmsnorm_kernels.hpp"
 
@@ -240,6 +241,196 @@ rmsnorm_status_t run(const Problem& p, const rmsnorm_config_t* cfg, void* stream
     return launch(p, cfg, static_cast<hipStream_t>(stream));
 }
 
+// ---------------------------------------------------------------- backward
+
+struct BwdProblem {
+    const void* x;
+    const void* w;
+    const void* dy;
+    void* dx;
+    void* dw;  // nullptr: dweight not wanted
+    int64_t rows;
+    int64_t hidden;
+    float eps;
+    int dtype;
+    void* ws;
+    size_t ws_bytes;
+};
+
+// Floats per partial dweight row: hidden rounded up to 64 (256-byte rows).
+int64_t bwd_ld(int64_t hidden) { return (hidden + 63) / 64 * 64; }
+
+// Default grid of the backward walk: 512 workgroups (two per CU on MI355X),
+// the best of the sweeps on MI355X for every measured shape.  Fixed, not read
+// from the device, so that a shape's results (and its workspace size) are the
+// same on any GPU.
+constexpr int64_t kBwdGrid = 512;
+
+// Partial dweight rows (= workgroups of the walk) for a configuration.
+int64_t bwd_partials(int64_t rows, const rmsnorm_config_t& c) {
+    const int64_t cap = c.max_blocks > 0 ? c.max_blocks : kMaxGrid;
+    return rows < cap ? rows : cap;
+}
+
+bool bwd_vector_aligned(const BwdProblem& p) {
+    if ((p.hidden * elem_size(p.dtype)) % kVectorBytes != 0) return false;
+    const void* ptrs[] = {p.x, p.w, p.dy, p.dx};
+    for (const void* q : ptrs)
+        if (reinterpret_cast<uintptr_t>(q) % kVectorBytes != 0) return false;
+    return true;
+}
+
+// With a capped grid the waves in flight are grid x waves per row, so a row
+// gets at least four waves (when it has two vectors or elements per lane to
+// spread) and lanes hold up to four 16-byte vectors (eight elements), more
+// waves when rows are few.  Sweeps on MI355X: bf16 hidden 8192 runs fastest as
+// 4 waves x 4 vectors, hidden 2048 as 4 x 1, both on 512 workgroups.
+rmsnorm_config_t choose_bwd(int64_t rows, int64_t hidden, int dtype, bool aligned) {
+    rmsnorm_config_t c = {RMSNORM_PATH_TWO_PASS, 16, 0, 1, static_cast<int32_t>(kBwdGrid)};
+    const bool vec = aligned && hidden % vec_elems(dtype) == 0;
+    const int64_t units = vec ? hidden / vec_elems(dtype) : hidden;
+    const int* list = vec ? mbr::kBwdVplList : mbr::kBwdEplList;
+    const int nlist = vec ? mbr::kNumBwdVpl : mbr::kNumBwdEpl;
+    const int cap = vec ? 4 : 8;
+    auto fit = [&](int wpr) {
+        const int per = round_up_in(list, nlist, ceil_div(units, int64_t(64) * wpr));
+        if (per < 0) return -1;
+        return (!vec || mbr::bwd_vec_built(wpr, per)) ? per : -1;
+    };
+    int wpr = 1;
+    while (wpr < 16 && ceil_div(units, int64_t(64) * wpr) > cap) wpr *= 2;
+    while (wpr < 4 && units >= int64_t(64) * wpr * 2) wpr *= 2;
+    while (wpr < 16 && rows < 2048 / wpr && units >= int64_t(64) * wpr * 2) wpr *= 2;
+    int per = fit(wpr);
+    while (per < 0 && wpr < 16) {
+        wpr *= 2;
+        per = fit(wpr);
+    }
+    if (per < 0) return c;
+    c.path = vec ? RMSNORM_PATH_VECTOR : RMSNORM_PATH_ELEMENT;
+    c.waves_per_row = wpr;
+    c.items_per_lane = per;
+    return c;
+}
+
+// Workspace bytes a configuration needs (0 without dweight or rows).
+int64_t bwd_workspace_need(int64_t rows, int64_t hidden, const rmsnorm_config_t& c) {
+    return bwd_partials(rows, c) * bwd_ld(hidden) * 4;
+}
+
+rmsnorm_status_t validate_bwd_pointers(const BwdProblem& p, int64_t ws_need) {
+    const int es = elem_size(p.dtype);
+    if (!p.x || !p.w || !p.dy || !p.dx) return RMSNORM_ERR_INVALID_ARG;
+    const void* ptrs[] = {p.x, p.w, p.dy, p.dx, p.dw};
+    for (const void* q : ptrs)
+        if (q && reinterpret_cast<uintptr_t>(q) % es != 0) return RMSNORM_ERR_INVALID_ARG;
+    const int64_t nb = p.rows * p.hidden * es;
+    const int64_t wb = p.hidden * es;
+    if (!output_vs_input_ok(p.dx, p.x, nb) || !output_vs_input_ok(p.dx, p.dy, nb)) return RMSNORM_ERR_INVALID_ARG;
+    if (ranges_overlap(p.dx, nb, p.w, wb)) return RMSNORM_ERR_INVALID_ARG;
+    if (!p.dw) return RMSNORM_OK;
+    const void* others[] = {p.x, p.w, p.dy, p.dx};
+    const int64_t sizes[] = {nb, wb, nb, nb};
+    for (int i = 0; i < 4; ++i)
+        if (ranges_overlap(p.dw, wb, others[i], sizes[i])) return RMSNORM_ERR_INVALID_ARG;
+    if (ws_need == 0) return RMSNORM_OK;
+    if (!p.ws || reinterpret_cast<uintptr_t>(p.ws) % kVectorBytes != 0) return RMSNORM_ERR_INVALID_ARG;
+    if (p.ws_bytes < static_cast<uint64_t>(ws_need)) return RMSNORM_ERR_INVALID_ARG;
+    for (int i = 0; i < 4; ++i)
+        if (ranges_overlap(p.ws, ws_need, others[i], sizes[i])) return RMSNORM_ERR_INVALID_ARG;
+    if (ranges_overlap(p.ws, ws_need, p.dw, wb)) return RMSNORM_ERR_INVALID_ARG;
+    return RMSNORM_OK;
+}
+
+rmsnorm_status_t launch_checked(const void* fn, int64_t grid, int64_t threads, void* arg, hipStream_t stream) {
+    void* args[] = {arg};
+    const hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(grid)), dim3(static_cast<unsigned>(threads)),
+                                         args, 0, stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return RMSNORM_ERR_RUNTIME;
+    }
+    return RMSNORM_OK;
+}
+
+rmsnorm_status_t run_bwd(const BwdProblem& p, const rmsnorm_config_t* user, void* stream_arg) {
+    rmsnorm_status_t s = validate_sizes(p.rows, p.hidden, p.eps, p.dtype);
+    if (s != RMSNORM_OK) return s;
+    const bool aligned = p.x && p.w && p.dy && p.dx && bwd_vector_aligned(p);
+    const rmsnorm_config_t c =
+        (user && user->path != RMSNORM_PATH_AUTO) ? *user : choose_bwd(p.rows, p.hidden, p.dtype, aligned);
+    const int wi = index_of(mbr::kWprList, mbr::kNumWpr, c.waves_per_row);
+    if (wi < 0 || c.rows_per_block != 1 || c.max_blocks < 0) return RMSNORM_ERR_INVALID_ARG;
+    const bool dw = p.dw != nullptr;
+    const int64_t ws_need = dw ? bwd_workspace_need(p.rows, p.hidden, c) : 0;
+    const hipStream_t stream = static_cast<hipStream_t>(stream_arg);
+    if (p.rows == 0) {
+        // nothing to differentiate: dx is empty and dweight is zero
+        if (!dw) return RMSNORM_OK;
+        if (reinterpret_cast<uintptr_t>(p.dw) % elem_size(p.dtype) != 0) return RMSNORM_ERR_INVALID_ARG;
+        mbr::DwArgs d = {nullptr, p.dw, bwd_ld(p.hidden), 0, static_cast<int32_t>(p.hidden)};
+        return launch_checked(mbr::bwd_dw_kernel(p.dtype), ceil_div(d.ld, mbr::kDwCols), 1024, &d, stream);
+    }
+    s = validate_bwd_pointers(p, ws_need);
+    if (s != RMSNORM_OK) return s;
+
+    const int64_t lanes = int64_t(64) * c.waves_per_row;
+    mbr::BwdArgs a;
+    a.x = p.x;
+    a.w = p.w;
+    a.dy = p.dy;
+    a.dx = p.dx;
+    a.part = static_cast<float*>(p.ws);
+    a.rows = p.rows;
+    a.ld = bwd_ld(p.hidden);
+    a.hidden_f = static_cast<float>(p.hidden);
+    a.eps = p.eps;
+    const void* fn = nullptr;
+    int64_t threads = lanes;
+    switch (c.path) {
+        case RMSNORM_PATH_VECTOR: {
+            if (!aligned || p.hidden % vec_elems(p.dtype) != 0) return RMSNORM_ERR_INVALID_ARG;
+            const int vi = index_of(mbr::kBwdVplList, mbr::kNumBwdVpl, c.items_per_lane);
+            const int64_t nvec = p.hidden / vec_elems(p.dtype);
+            if (vi < 0 || lanes * c.items_per_lane < nvec) return RMSNORM_ERR_INVALID_ARG;
+            if (threads > mbr::max_threads_for(c.waves_per_row)) return RMSNORM_ERR_INVALID_ARG;
+            fn = mbr::bwd_vec_kernel(p.dtype, dw, lanes * c.items_per_lane != nvec, wi, vi);
+            a.units = static_cast<int32_t>(nvec);
+            break;
+        }
+        case RMSNORM_PATH_ELEMENT: {
+            const int ei = index_of(mbr::kBwdEplList, mbr::kNumBwdEpl, c.items_per_lane);
+            if (ei < 0 || lanes * c.items_per_lane < p.hidden) return RMSNORM_ERR_INVALID_ARG;
+            if (threads > mbr::max_threads_for(c.waves_per_row)) return RMSNORM_ERR_INVALID_ARG;
+            fn = mbr::bwd_elem_kernel(p.dtype, dw, wi, ei);
+            a.units = static_cast<int32_t>(p.hidden);
+            break;
+        }
+        case RMSNORM_PATH_TWO_PASS: {
+            const bool vec = aligned && p.hidden % vec_elems(p.dtype) == 0;
+            fn = mbr::bwd_twopass_kernel(p.dtype, dw, vec);
+            a.units = static_cast<int32_t>(vec ? p.hidden / vec_elems(p.dtype) : p.hidden);
+            break;
+        }
+        default:
+            return RMSNORM_ERR_INVALID_ARG;
+    }
+    if (!fn) return RMSNORM_ERR_INVALID_ARG;
+    const int64_t grid = bwd_partials(p.rows, c);
+    s = launch_checked(fn, grid, threads, &a, stream);
+    if (s != RMSNORM_OK) return s;
+    if (dw) {
+        mbr::DwArgs d;
+        d.part = static_cast<const float*>(p.ws);
+        d.dw = p.dw;
+        d.ld = a.ld;
+        d.n_part = static_cast<int32_t>(grid);
+        d.hidden = static_cast<int32_t>(p.hidden);
+        s = launch_checked(mbr::bwd_dw_kernel(p.dtype), ceil_div(a.ld, mbr::kDwCols), 1024, &d, stream);
+    }
+    return s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -312,6 +503,50 @@ RMSNORM_API rmsnorm_status_t rmsnorm_select_quant_config(int64_t rows, int64_t h
     rmsnorm_status_t s = validate_sizes(rows, hidden, 0.0f, static_cast<int>(dtype));
     if (s != RMSNORM_OK) return s;
     *cfg = choose(rows, hidden, static_cast<int>(dtype), vector_aligned_flag != 0, fused != 0, 1);
+    return RMSNORM_OK;
+}
+
+RMSNORM_API rmsnorm_status_t rmsnorm_bwd_ex(const void* x, const void* weight, const void* dy, void* dx,
+                                            void* dweight, int64_t rows, int64_t hidden, float eps,
+                                            rmsnorm_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                            const rmsnorm_config_t* cfg, void* stream) {
+    const BwdProblem p = {x, weight, dy, dx, dweight, rows, hidden, eps, static_cast<int>(dtype), workspace,
+                          workspace_bytes};
+    return run_bwd(p, cfg, stream);
+}
+
+RMSNORM_API rmsnorm_status_t rmsnorm_bwd(const void* x, const void* weight, const void* dy, void* dx, void* dweight,
+                                         int64_t rows, int64_t hidden, float eps, rmsnorm_dtype_t dtype,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+    return rmsnorm_bwd_ex(x, weight, dy, dx, dweight, rows, hidden, eps, dtype, workspace, workspace_bytes, nullptr,
+                          stream);
+}
+
+RMSNORM_API rmsnorm_status_t rmsnorm_bwd_workspace_size(int64_t rows, int64_t hidden, rmsnorm_dtype_t dtype,
+                                                        const rmsnorm_config_t* cfg, size_t* bytes) {
+    if (!bytes) return RMSNORM_ERR_INVALID_ARG;
+    const rmsnorm_status_t s = validate_sizes(rows, hidden, 0.0f, static_cast<int>(dtype));
+    if (s != RMSNORM_OK) return s;
+    int64_t need;
+    if (cfg && cfg->path != RMSNORM_PATH_AUTO) {
+        if (cfg->max_blocks < 0) return RMSNORM_ERR_INVALID_ARG;
+        need = bwd_workspace_need(rows, hidden, *cfg);
+    } else {
+        const int d = static_cast<int>(dtype);
+        const int64_t a = bwd_workspace_need(rows, hidden, choose_bwd(rows, hidden, d, true));
+        const int64_t b = bwd_workspace_need(rows, hidden, choose_bwd(rows, hidden, d, false));
+        need = a > b ? a : b;
+    }
+    *bytes = static_cast<size_t>(need);
+    return RMSNORM_OK;
+}
+
+RMSNORM_API rmsnorm_status_t rmsnorm_select_bwd_config(int64_t rows, int64_t hidden, rmsnorm_dtype_t dtype,
+                                                       int32_t vector_aligned_flag, rmsnorm_config_t* cfg) {
+    if (!cfg) return RMSNORM_ERR_INVALID_ARG;
+    const rmsnorm_status_t s = validate_sizes(rows, hidden, 0.0f, static_cast<int>(dtype));
+    if (s != RMSNORM_OK) return s;
+    *cfg = choose_bwd(rows, hidden, static_cast<int>(dtype), vector_aligned_flag != 0);
     return RMSNORM_OK;
 }
 

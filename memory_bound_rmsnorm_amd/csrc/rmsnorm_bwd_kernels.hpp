@@ -1,0 +1,384 @@
+// RMSNorm backward kernels for gfx950 (CDNA4, wave64).
+//
+// For y = x * r * w with r = rsqrt(sum_k x_k^2 / H + eps) and an upstream
+// gradient dy, the derivative (the norm backward of a training step's backward
+// stage, TileLang tutorial ch. 02, section 1.1(b); the pages give no formula,
+// this is the plain one) is
+//
+//   dx_k = r * (dy_k * w_k - x_k * r^2 * c / H),   c = sum_j dy_j * w_j * x_j
+//   dw_j = sum_i dy_ij * x_ij * r_i
+//
+// dx is another row pass: the row of x and dy lives in registers, the two row
+// sums (x^2 and dy*w*x) go through the same lane -> wave -> workgroup
+// reduction as the forward (one barrier per row), and dx is written once.
+//
+// dw is the first reduction across rows.  It is done in two deterministic
+// stages without atomics: a capped grid walks the rows (workgroup b takes rows
+// b, b + G, b + 2G, ...) and every lane keeps fp32 sums for its own columns,
+// which stay fixed from row to row; at the end each workgroup writes one
+// partial row of fp32 sums into a caller-provided workspace, and
+// rms_bwd_dw_kernel adds the G partial rows per column in a fixed order and
+// rounds once.  Both stages are HBM-bound streams; nothing is a contraction.
+#pragma once
+
+#include "rmsnorm_kernels.hpp"
+
+namespace mbr {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct BwdArgs {
+    const void* x;
+    const void* w;
+    const void* dy;
+    void* dx;
+    float* part;     // DW: [gridDim.x][ld] fp32 partial dweight rows
+    int64_t rows;
+    int64_t ld;      // floats per partial row (a multiple of 64, >= hidden)
+    int32_t units;   // per row: 16-byte vectors (vector path) or elements
+    float hidden_f;
+    float eps;
+};
+
+struct DwArgs {
+    const float* part;  // [n_part][ld]
+    void* dw;           // [hidden], tensor dtype
+    int64_t ld;
+    int32_t n_part;
+    int32_t hidden;
+};
+
+// Row totals of both sums, identical bits in every lane of the row.
+template <int WPR>
+__device__ __forceinline__ void row_sums(float& ss, float& cc, float (&ps)[2][16], float (&pc)[2][16], int it,
+                                         int wave) {
+    ss = wave_sum(ss);
+    cc = wave_sum(cc);
+    if constexpr (WPR > 1) {
+        if ((threadIdx.x & 63) == 0) {
+            ps[it & 1][wave] = ss;
+            pc[it & 1][wave] = cc;
+        }
+        __syncthreads();
+        ss = 0.f;
+        cc = 0.f;
+#pragma unroll
+        for (int i = 0; i < WPR; ++i) {
+            ss += ps[it & 1][i];
+            cc += pc[it & 1][i];
+        }
+    }
+}
+
+// Makes the compiler treat a packed vector as redefined here (no instruction
+// is emitted), so values widened from it before this point are recomputed
+// after it instead of being held: a row's x, dy and w then stay packed across
+// the reduction (12 VGPRs per bf16 vector instead of 24 widened fp32 ones).
+__device__ __forceinline__ void repack(u32x4& v) { asm volatile("" : "+v"(v)); }
+
+// One partial row: V consecutive fp32 sums per 16-byte input vector.
+__device__ __forceinline__ void store_partial(float* p, const float* acc, Bf16) {
+    f32x4 a = {acc[0], acc[1], acc[2], acc[3]}, b = {acc[4], acc[5], acc[6], acc[7]};
+    reinterpret_cast<f32x4*>(p)[0] = a;
+    reinterpret_cast<f32x4*>(p)[1] = b;
+}
+__device__ __forceinline__ void store_partial(float* p, const float* acc, F32) {
+    f32x4 a = {acc[0], acc[1], acc[2], acc[3]};
+    reinterpret_cast<f32x4*>(p)[0] = a;
+}
+
+// Vector path: WPR waves per row (one row per workgroup at a time), VPL
+// 16-byte vectors per lane, lane l owning vectors l, l + 64*WPR, ... of both
+// x and dy; the weight slice stays in registers for the whole walk.  When the
+// row slice is small the next row's x and dy are loaded before the current
+// row is reduced, so memory stays busy across the barrier.
+template <class E, int WPR, int VPL, bool MASKED, bool DW>
+__global__ void __launch_bounds__(max_threads<WPR>()) rms_bwd_vec_kernel(const BwdArgs a) {
+    constexpr int LANES = 64 * WPR;
+    constexpr int V = E::kVec;
+    constexpr bool PIPE = VPL <= 2;
+    const int wave = wave_id();
+    const int lane = static_cast<int>(threadIdx.x);
+    const int nvec = a.units;
+    __shared__ float ps[2][16], pc[2][16];
+
+    // Byte offset of a lane's k-th vector within a row: unsigned 32-bit, so
+    // that accesses take a wave-uniform 64-bit row base in SGPRs plus one
+    // VGPR offset instead of a 64-bit VGPR address per vector.
+    auto voff = [&](int k) {
+        const int v = k * LANES + lane;
+        return static_cast<unsigned>(MASKED ? (v < nvec ? v : nvec - 1) : v) * 16u;
+    };
+    auto at = [](const void* base, unsigned off) {
+        return reinterpret_cast<const u32x4*>(static_cast<const char*>(base) + off);
+    };
+    auto in_row = [&](int k) { return !MASKED || k * LANES + lane < nvec; };
+    const int64_t row_bytes = static_cast<int64_t>(nvec) * 16;
+    auto load_row = [&](int64_t row, u32x4 (&xv)[VPL], u32x4 (&gv)[VPL]) {
+        const char* xr = static_cast<const char*>(a.x) + row * row_bytes;
+        const char* gr = static_cast<const char*>(a.dy) + row * row_bytes;
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) xv[k] = load_stream(at(xr, voff(k)));
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) gv[k] = load_stream(at(gr, voff(k)));
+    };
+
+    u32x4 wv[VPL];
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) wv[k] = load_keep(at(a.w, voff(k)));
+    float acc[DW ? VPL * V : 1];
+    if constexpr (DW) {
+#pragma unroll
+        for (int i = 0; i < VPL * V; ++i) acc[i] = 0.f;
+    }
+
+    int64_t row = blockIdx.x;
+    u32x4 nx[PIPE ? VPL : 1], ng[PIPE ? VPL : 1];
+    if constexpr (PIPE) {
+        if (row < a.rows) load_row(row, nx, ng);
+    }
+    for (int it = 0; row < a.rows; row += gridDim.x, ++it) {
+        u32x4 xv[VPL], gv[VPL];
+        if constexpr (PIPE) {
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) {
+                xv[k] = nx[k];
+                gv[k] = ng[k];
+            }
+            if (row + gridDim.x < a.rows) load_row(row + gridDim.x, nx, ng);
+        } else {
+            load_row(row, xv, gv);
+        }
+        float ss = 0.f, cc = 0.f;
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            float fx[V], fg[V], fw[V];
+            widen(xv[k], fx, E{});
+            widen(gv[k], fg, E{});
+            widen(wv[k], fw, E{});
+            float s = 0.f, c = 0.f;
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                s += fx[i] * fx[i];
+                c += (fg[i] * fw[i]) * fx[i];
+            }
+            ss += in_row(k) ? s : 0.f;
+            cc += in_row(k) ? c : 0.f;
+        }
+        row_sums<WPR>(ss, cc, ps, pc, it, wave);
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            repack(xv[k]);
+            repack(gv[k]);
+            repack(wv[k]);
+        }
+        const float r = rsqrtf(ss / a.hidden_f + a.eps);
+        const float k2 = r * r * cc / a.hidden_f;
+        char* dxr = static_cast<char*>(a.dx) + row * row_bytes;
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            if (!in_row(k)) continue;
+            float fx[V], fg[V], fw[V], d[V];
+            widen(xv[k], fx, E{});
+            widen(gv[k], fg, E{});
+            widen(wv[k], fw, E{});
+#pragma unroll
+            for (int i = 0; i < V; ++i) d[i] = r * (fg[i] * fw[i] - fx[i] * k2);
+            store_stream(reinterpret_cast<u32x4*>(dxr + voff(k)), narrow(d, E{}));
+            if constexpr (DW) {
+#pragma unroll
+                for (int i = 0; i < V; ++i) acc[k * V + i] += (fg[i] * fx[i]) * r;
+            }
+        }
+    }
+    if constexpr (DW) {
+        float* pr = a.part + static_cast<int64_t>(blockIdx.x) * a.ld;
+#pragma unroll
+        for (int k = 0; k < VPL; ++k)
+            if (in_row(k)) store_partial(pr + static_cast<int64_t>(k * LANES + lane) * V, acc + k * V, E{});
+    }
+}
+
+// Element path: any hidden, any element alignment; lane l owns elements
+// l, l + 64*WPR, ... (EPL of them).
+template <class E, int WPR, int EPL, bool DW>
+__global__ void __launch_bounds__(max_threads<WPR>()) rms_bwd_elem_kernel(const BwdArgs a) {
+    using S = typename E::scalar;
+    constexpr int LANES = 64 * WPR;
+    const int wave = wave_id();
+    const int lane = static_cast<int>(threadIdx.x);
+    const int H = a.units;
+    __shared__ float ps[2][16], pc[2][16];
+    auto jdx = [&](int k) {
+        const int j = k * LANES + lane;
+        return j < H ? j : H - 1;
+    };
+    auto in_row = [&](int k) { return k * LANES + lane < H; };
+
+    float fw[EPL], acc[DW ? EPL : 1];
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) {
+        fw[k] = widen1(static_cast<const S*>(a.w)[jdx(k)]);
+        if constexpr (DW) acc[k] = 0.f;
+    }
+    int it = 0;
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x, ++it) {
+        const S* xr = static_cast<const S*>(a.x) + row * H;
+        const S* gr = static_cast<const S*>(a.dy) + row * H;
+        float fx[EPL], fg[EPL];
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) fx[k] = widen1(xr[jdx(k)]);
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) fg[k] = widen1(gr[jdx(k)]);
+        float ss = 0.f, cc = 0.f;
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) {
+            ss += in_row(k) ? fx[k] * fx[k] : 0.f;
+            cc += in_row(k) ? (fg[k] * fw[k]) * fx[k] : 0.f;
+        }
+        row_sums<WPR>(ss, cc, ps, pc, it, wave);
+        const float r = rsqrtf(ss / a.hidden_f + a.eps);
+        const float k2 = r * r * cc / a.hidden_f;
+        S* dxr = static_cast<S*>(a.dx) + row * H;
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) {
+            if (!in_row(k)) continue;
+            dxr[k * LANES + lane] = narrow1(r * (fg[k] * fw[k] - fx[k] * k2), E{});
+            if constexpr (DW) acc[k] += (fg[k] * fx[k]) * r;
+        }
+    }
+    if constexpr (DW) {
+        float* pr = a.part + static_cast<int64_t>(blockIdx.x) * a.ld;
+#pragma unroll
+        for (int k = 0; k < EPL; ++k)
+            if (in_row(k)) pr[k * LANES + lane] = acc[k];
+    }
+}
+
+// Rows too wide for registers: 1024 lanes stride over the row twice.  Pass 1
+// reads x, dy and w for the two sums; pass 2 reads them again and writes dx.
+// A thread's columns are the same in every row, so its dweight sums live in
+// its own slots of the workgroup's partial row (written on the first row,
+// read-modify-written after; no other thread touches them).  Exact aliasing of
+// dx with x or dy stays safe: each element is read and then written by the
+// same thread.
+template <class E, bool VEC, bool DW>
+__global__ void __launch_bounds__(1024) rms_bwd_twopass_kernel(const BwdArgs a) {
+    using S = typename E::scalar;
+    constexpr int V = E::kVec;
+    const int wave = wave_id();
+    const int nwaves = static_cast<int>(blockDim.x) >> 6;
+    const int n = a.units;
+    __shared__ float ps[2][16], pc[2][16];
+    float* const pr = DW ? a.part + static_cast<int64_t>(blockIdx.x) * a.ld : nullptr;
+
+    int it = 0;
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x, ++it) {
+        const int64_t base = row * n;
+        float ss = 0.f, cc = 0.f;
+        for (int j = threadIdx.x; j < n; j += blockDim.x) {
+            if constexpr (VEC) {
+                float fx[V], fg[V], fw[V];
+                widen(load_stream(static_cast<const u32x4*>(a.x) + base + j), fx, E{});
+                widen(load_stream(static_cast<const u32x4*>(a.dy) + base + j), fg, E{});
+                widen(load_keep(static_cast<const u32x4*>(a.w) + j), fw, E{});
+#pragma unroll
+                for (int i = 0; i < V; ++i) {
+                    ss += fx[i] * fx[i];
+                    cc += (fg[i] * fw[i]) * fx[i];
+                }
+            } else {
+                const float fx = widen1(static_cast<const S*>(a.x)[base + j]);
+                const float fg = widen1(static_cast<const S*>(a.dy)[base + j]);
+                ss += fx * fx;
+                cc += (fg * widen1(static_cast<const S*>(a.w)[j])) * fx;
+            }
+        }
+        ss = wave_sum(ss);
+        cc = wave_sum(cc);
+        if ((threadIdx.x & 63) == 0) {
+            ps[it & 1][wave] = ss;
+            pc[it & 1][wave] = cc;
+        }
+        __syncthreads();
+        ss = 0.f;
+        cc = 0.f;
+        for (int i = 0; i < nwaves; ++i) {
+            ss += ps[it & 1][i];
+            cc += pc[it & 1][i];
+        }
+        const float r = rsqrtf(ss / a.hidden_f + a.eps);
+        const float k2 = r * r * cc / a.hidden_f;
+        for (int j = threadIdx.x; j < n; j += blockDim.x) {
+            if constexpr (VEC) {
+                float fx[V], fg[V], fw[V], d[V];
+                widen(load_stream(static_cast<const u32x4*>(a.x) + base + j), fx, E{});
+                widen(load_stream(static_cast<const u32x4*>(a.dy) + base + j), fg, E{});
+                widen(load_keep(static_cast<const u32x4*>(a.w) + j), fw, E{});
+#pragma unroll
+                for (int i = 0; i < V; ++i) d[i] = r * (fg[i] * fw[i] - fx[i] * k2);
+                store_stream(static_cast<u32x4*>(a.dx) + base + j, narrow(d, E{}));
+                if constexpr (DW) {
+                    f32x4* p = reinterpret_cast<f32x4*>(pr + static_cast<int64_t>(j) * V);
+#pragma unroll
+                    for (int q = 0; q < V / 4; ++q) {
+                        f32x4 t = {(fg[4 * q] * fx[4 * q]) * r, (fg[4 * q + 1] * fx[4 * q + 1]) * r,
+                                   (fg[4 * q + 2] * fx[4 * q + 2]) * r, (fg[4 * q + 3] * fx[4 * q + 3]) * r};
+                        p[q] = it == 0 ? t : p[q] + t;
+                    }
+                }
+            } else {
+                const float fx = widen1(static_cast<const S*>(a.x)[base + j]);
+                const float fg = widen1(static_cast<const S*>(a.dy)[base + j]);
+                const float fw = widen1(static_cast<const S*>(a.w)[j]);
+                static_cast<S*>(a.dx)[base + j] = narrow1(r * (fg * fw - fx * k2), E{});
+                if constexpr (DW) {
+                    const float t = (fg * fx) * r;
+                    pr[j] = it == 0 ? t : pr[j] + t;
+                }
+            }
+        }
+    }
+}
+
+// Second stage of dweight: workgroup b sums the columns of kDwQuads column
+// quads (4 fp32 columns each) over the n_part partial rows.  Thread (s, q),
+// s = tid / kDwQuads, q = tid % kDwQuads, adds partial rows s, s + S, s + 2S,
+// ... (S = 1024 / kDwQuads slices) of its quad in that order; the S slice sums
+// are then combined by a fixed pairwise tree in LDS, and the total is rounded
+// once to the tensor dtype.  n_part == 0 writes zeros.
+constexpr int kDwQuads = 8;
+constexpr int kDwSlices = 1024 / kDwQuads;
+constexpr int kDwCols = 4 * kDwQuads;  // columns per workgroup
+static_assert(64 % kDwCols == 0, "a workgroup's columns must not cross the end of a 64-float partial row");
+
+template <class E>
+__global__ void __launch_bounds__(1024) rms_bwd_dw_kernel(const DwArgs a) {
+    using S = typename E::scalar;
+    const int q = threadIdx.x % kDwQuads;
+    const int s = threadIdx.x / kDwQuads;
+    const int64_t quad = static_cast<int64_t>(blockIdx.x) * kDwQuads + q;
+    const f32x4* col = reinterpret_cast<const f32x4*>(a.part) + quad;
+    const int64_t stride = a.ld / 4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int p = s; p < a.n_part; p += kDwSlices) acc += col[p * stride];
+    __shared__ f32x4 sm[kDwSlices][kDwQuads];
+    sm[s][q] = acc;
+    __syncthreads();
+#pragma unroll
+    for (int st = kDwSlices / 2; st >= 1; st >>= 1) {
+        if (s < st) sm[s][q] += sm[s + st][q];
+        __syncthreads();
+    }
+    if (s == 0) {
+        const f32x4 t = sm[0][q];
+        S* out = static_cast<S*>(a.dw);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t c = quad * 4 + i;
+            if (c < a.hidden) out[c] = narrow1(t[i], E{});
+        }
+    }
+}
+
+}  // namespace mbr

@@ -43,6 +43,21 @@ const void* qtwopass_kernel(int dtype, int qt, bool fused, bool vec);
 const void* qvec_kernel_bf16(int qt, bool fused, bool masked, int wi, int vi);
 const void* qvec_kernel_f32(int qt, bool fused, bool masked, int wi, int vi);
 
+// Backward (dx, and dweight through per-workgroup partial rows): the lane
+// holds x, dy and the weight slice (plus fp32 column sums when dweight is
+// wanted), so the vector path carries at most 8 vectors per lane (4 in a
+// 1024-lane workgroup) and the element path at most 8 elements.
+constexpr int kBwdVplList[] = {1, 2, 3, 4, 5, 6, 7, 8};
+constexpr int kBwdEplList[] = {1, 2, 4, 8};
+constexpr int kNumBwdVpl = sizeof(kBwdVplList) / sizeof(int);
+constexpr int kNumBwdEpl = sizeof(kBwdEplList) / sizeof(int);
+constexpr bool bwd_vec_built(int wpr, int vpl) { return wpr < 16 || vpl <= 4; }
+
+const void* bwd_vec_kernel(int dtype, bool dw, bool masked, int wpr_index, int vpl_index);
+const void* bwd_elem_kernel(int dtype, bool dw, int wpr_index, int epl_index);
+const void* bwd_twopass_kernel(int dtype, bool dw, bool vec);
+const void* bwd_dw_kernel(int dtype);
+
 // Per-unit getters defined in the instantiation files.
 const void* vec_kernel_bf16(bool fused, bool masked, int wi, int vi);
 const void* vec_kernel_f32(bool fused, bool masked, int wi, int vi);

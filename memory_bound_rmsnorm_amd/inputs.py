@@ -5,7 +5,8 @@ contains no RMSNorm arithmetic, so both the HIP path's tests/benchmark and the
 CPU oracle can take their inputs from here without sharing any of the method.
 
 Recipe (one ``numpy.random.default_rng(seed)`` stream per workload):
-  * draw order is x, then residual (fused workloads only), then weight;
+  * draw order is x, then residual (fused workloads only) or the upstream
+    gradient dy (backward workloads only), then weight;
   * ``N(mu, sigma)`` means ``standard_normal(float32) * sigma + mu``
     (sigma is a standard deviation), ``U(a, b)`` means ``uniform(a, b)``
     cast to float32;
@@ -51,7 +52,12 @@ class Workload:
     outlier_columns: Tuple[int, ...] = ()
     outlier_scale: float = 1.0
     quant: Optional[str] = None  # None: normalised output; "int8" / "fp8": codes + per-row scale
+    grad: Optional[Dist] = None  # backward workloads: distribution of the upstream gradient dy
     note: str = field(default="", compare=False)
+
+    @property
+    def backward(self) -> bool:
+        return self.grad is not None
 
     @property
     def elem_size(self) -> int:
@@ -59,10 +65,13 @@ class Workload:
 
     @property
     def read_bytes(self) -> int:
-        return ((2 if self.fused else 1) * self.rows * self.hidden + self.hidden) * self.elem_size
+        # forward: x (and residual) plus weight; backward: x and dy plus weight
+        return ((2 if self.fused or self.backward else 1) * self.rows * self.hidden + self.hidden) * self.elem_size
 
     @property
     def write_bytes(self) -> int:
+        if self.backward:  # dx and dweight
+            return (self.rows * self.hidden + self.hidden) * self.elem_size
         h = self.rows * self.hidden * self.elem_size if self.fused else 0
         if self.quant:
             return h + self.rows * self.hidden + 4 * self.rows
@@ -72,8 +81,8 @@ class Workload:
     def copy_bytes(self) -> int:
         """Size of the plain copy that moves the same traffic (read == written):
         the output bytes for the normalised forms, half the ledger (rounded
-        down to 16 bytes) for the quantised ones."""
-        if self.quant:
+        down to 16 bytes) for the quantised and backward ones."""
+        if self.quant or self.backward:
             return (self.algorithmic_bytes // 2) & ~15
         return self.write_bytes
 
@@ -120,7 +129,17 @@ for _base in ("bf16_16384x8192", "bf16_residual_12289x5120"):
         QUANT_WORKLOADS[_name] = Workload(_name, _w.dtype, _w.rows, _w.hidden, _w.eps, _w.fused, _w.x, _w.weight,
                                           _w.residual, _w.outlier_columns, _w.outlier_scale, quant=_q,
                                           note=_w.note + "; %s output" % _q)
-ALL_WORKLOADS: Dict[str, Workload] = dict(WORKLOADS, **QUANT_WORKLOADS)
+# Backward (dx and dweight) for an upstream gradient dy ~ N(0, 1): the
+# large-hidden shape (same x recipe, outlier channels included), the Llama-1B
+# prefill shape, and the small fp32 case.
+BWD_WORKLOADS: Dict[str, Workload] = {}
+for _base in ("bf16_16384x8192", "bf16_prefill_4096x2048", "fp32_64x2048"):
+    _w = WORKLOADS[_base]
+    _name = _base.replace("bf16_", "bf16_bwd_", 1).replace("fp32_", "fp32_bwd_", 1).replace("prefill_", "")
+    BWD_WORKLOADS[_name] = Workload(_name, _w.dtype, _w.rows, _w.hidden, _w.eps, False, _w.x, _w.weight,
+                                    outlier_columns=_w.outlier_columns, outlier_scale=_w.outlier_scale,
+                                    grad=N01, note=_w.note + "; backward")
+ALL_WORKLOADS: Dict[str, Workload] = dict(WORKLOADS, **QUANT_WORKLOADS, **BWD_WORKLOADS)
 
 
 def _draw(rng: np.random.Generator, d: Dist, shape) -> np.ndarray:
@@ -154,16 +173,19 @@ def make(w: Workload, seed: int = 0, rows: Optional[int] = None) -> Dict[str, to
     out = {"x": _store(x, w.dtype)}
     if w.fused:
         out["residual"] = _store(_draw(rng, w.residual or N01, (r, w.hidden)), w.dtype)
+    if w.backward:
+        out["dy"] = _store(_draw(rng, w.grad, (r, w.hidden)), w.dtype)
     out["weight"] = _store(_draw(rng, w.weight, (w.hidden,)), w.dtype)
     return out
 
 
 def custom(rows: int, hidden: int, dtype: str, fused: bool = False, eps: float = 1e-5,
-           x: Dist = N01, weight: Dist = W_N, residual: Dist = N01) -> Workload:
+           x: Dist = N01, weight: Dist = W_N, residual: Dist = N01, backward: bool = False,
+           grad: Dist = N01) -> Workload:
     """An ad-hoc workload (ragged widths, odd row counts, ...) with the same recipe."""
-    return Workload("custom_%s_%dx%d%s" % (dtype, rows, hidden, "_res" if fused else ""),
+    return Workload("custom_%s_%dx%d%s%s" % (dtype, rows, hidden, "_res" if fused else "", "_bwd" if backward else ""),
                     dtype, rows, hidden, eps, fused, x, weight,
-                    residual if fused else None)
+                    residual if fused else None, grad=grad if backward else None)
 
 
 def bits(t: torch.Tensor) -> np.ndarray:

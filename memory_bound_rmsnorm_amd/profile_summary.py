@@ -22,6 +22,8 @@ from collections import defaultdict
 from memory_bound_rmsnorm_amd import _build, inputs
 
 RMS_KERNEL_TAGS = ("rms_vec_kernel", "rms_elem_kernel", "rms_twopass_kernel")
+BWD_KERNEL_TAGS = ("rms_bwd_vec_kernel", "rms_bwd_elem_kernel", "rms_bwd_twopass_kernel")
+BWD_DW_TAG = "rms_bwd_dw_kernel"
 COPY_KERNEL_TAG = "hbm_copy_kernel"
 
 
@@ -29,28 +31,50 @@ def _is_rms(name):
     return any(t in name for t in RMS_KERNEL_TAGS)
 
 
+def _step_kernels(w):
+    """Predicates for the kernels one step of workload w launches, once each:
+    the forward kernel, or the backward row kernel plus the dweight reduction."""
+    if w.backward:
+        return [lambda k: any(t in k for t in BWD_KERNEL_TAGS), lambda k: BWD_DW_TAG in k]
+    return [_is_rms]
+
+
+def _family(w):
+    return "bwd" if w.backward else "fwd"
+
+
 def stats(args):
     w = inputs.ALL_WORKLOADS[args.workload]
     with open(args.csv) as f:
         rows = list(csv.DictReader(f))
     out = ["# rocprofv3 --kernel-trace --stats summary: RMSNorm %s [%d, %d]%s"
-           % (w.dtype, w.rows, w.hidden, " fused residual" if w.fused else ""),
+           % (w.dtype, w.rows, w.hidden, " fused residual" if w.fused else " backward" if w.backward else ""),
            "# command: %s" % args.command,
            "# algorithmic bytes per call: %d" % w.algorithmic_bytes,
            "%-90s %6s %12s %12s %12s" % ("kernel", "calls", "avg_us", "min_us", "max_us")]
-    rms_avg = None
+    step_avg = []
+    preds = _step_kernels(w)
     for r in rows:
         name = r["Name"]
         short = name if len(name) <= 90 else name[:87] + "..."
         avg = float(r["AverageNs"]) / 1e3
         out.append("%-90s %6s %12.3f %12.3f %12.3f" % (short, r["Calls"], avg, float(r["MinNs"]) / 1e3,
                                                         float(r["MaxNs"]) / 1e3))
-        if _is_rms(name) and rms_avg is None:
-            rms_avg = avg
-    if rms_avg:
-        out.append("rmsnorm_kernel_avg_us: %.3f" % rms_avg)
-        out.append("rmsnorm_gbps_from_avg: %.1f" % (w.algorithmic_bytes / rms_avg / 1e3))
-        out.append("rmsnorm_frac_of_8TBps: %.4f" % (w.algorithmic_bytes / rms_avg / 1e3 / 8000.0))
+    for pred in preds:
+        hit = [r for r in rows if pred(r["Name"])]
+        if hit:
+            step_avg.append(float(hit[0]["AverageNs"]) / 1e3)
+    if len(step_avg) == len(preds):
+        t = sum(step_avg)
+        if w.backward:
+            out.append("bwd_row_kernel_avg_us: %.3f" % step_avg[0])
+            out.append("bwd_dw_kernel_avg_us: %.3f" % step_avg[1])
+            out.append("step_avg_us: %.3f" % t)
+            out.append("row_kernel_gbps_from_avg: %.1f" % (w.algorithmic_bytes / step_avg[0] / 1e3))
+        else:
+            out.append("rmsnorm_kernel_avg_us: %.3f" % t)
+        out.append("rmsnorm_gbps_from_avg: %.1f" % (w.algorithmic_bytes / t / 1e3))
+        out.append("rmsnorm_frac_of_8TBps: %.4f" % (w.algorithmic_bytes / t / 1e3 / 8000.0))
     print("\n".join(out))
 
 
@@ -75,8 +99,15 @@ def pmc(args):
     w = inputs.ALL_WORKLOADS[args.workload]
     fm, fn = _counter_means(args.fetch, "FETCH_SIZE")
     wm, wn = _counter_means(args.write, "WRITE_SIZE")
-    rname, rfetch = _pick(fm, _is_rms)
-    _, rwrite = _pick(wm, _is_rms)
+    rname, rfetch, rwrite, ndisp = [], 0.0, 0.0, []
+    for pred in _step_kernels(w):
+        n, f = _pick(fm, pred)
+        _, wr = _pick(wm, pred)
+        rname.append(n)
+        ndisp.append(fn[n])
+        rfetch += f
+        rwrite += wr
+    rname = " + ".join(rname)
     cname, cfetch = _pick(fm, lambda k: COPY_KERNEL_TAG in k)
     _, cwrite = _pick(wm, lambda k: COPY_KERNEL_TAG in k)
     copy_bytes = w.copy_bytes  # read == written per dispatch, as bench.py's copy ceiling
@@ -86,13 +117,13 @@ def pmc(args):
     write_alg = w.write_bytes
     traffic = rfetch * 1024 * fscale + rwrite * 1024 * wscale
     out = ["# rocprofv3 --pmc summary: HBM traffic of RMSNorm %s [%d, %d]%s"
-           % (w.dtype, w.rows, w.hidden, " fused residual" if w.fused else ""),
+           % (w.dtype, w.rows, w.hidden, " fused residual" if w.fused else " backward" if w.backward else ""),
            "# fetch command: %s" % args.command_fetch,
            "# write command: %s" % args.command_write,
            "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch, averaged over dispatches; the copy kernel",
            "# moves a known byte count in the same process and calibrates both counters.",
            "rmsnorm_kernel: %s" % rname.replace(":", ";"),
-           "rmsnorm_dispatches_counted: %d" % fn[rname],
+           "rmsnorm_dispatches_counted: %d" % min(ndisp),
            "rmsnorm_fetch_kib_per_dispatch: %.1f" % rfetch,
            "rmsnorm_write_kib_per_dispatch: %.1f" % rwrite,
            "copy_kernel: %s" % COPY_KERNEL_TAG,
@@ -108,24 +139,28 @@ def pmc(args):
            "traffic_bytes_per_launch: %.0f" % traffic,
            "traffic_over_algorithmic: %.4f" % (traffic / w.algorithmic_bytes),
            "launch_config: %s" % _launch_config(w),
-           "source_sha256: %s" % _build.source_digest()]
+           "source_sha256: %s" % _build.source_digest(_family(w))]
     print("\n".join(out))
 
 
-def _launch_config(w):
+def launch_config(w):
+    """The automatic configuration for workload w on 16-byte-aligned buffers."""
     import torch
     import memory_bound_rmsnorm_amd as mbr
+    dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    if w.backward:
+        return mbr.rmsnorm_select_bwd_config(w.rows, w.hidden, dt, True)
     select = mbr.rmsnorm_select_quant_config if w.quant else mbr.rmsnorm_select_config
-    cfg = select(w.rows, w.hidden, torch.float32 if w.dtype == "f32" else torch.bfloat16, True, w.fused)
-    return " ".join("%s=%s" % kv for kv in cfg.as_dict().items())
+    return select(w.rows, w.hidden, dt, True, w.fused)
+
+
+def _launch_config(w):
+    return " ".join("%s=%s" % kv for kv in launch_config(w).as_dict().items())
 
 
 def resources(args):
     """Compile-time register/scratch/occupancy report of the built kernels,
     condensed: totals plus the kernels the stated workloads launch."""
-    import ctypes
-    import torch
-    import memory_bound_rmsnorm_amd as mbr
     with open(_build.RESOURCE_USAGE) as f:
         lines = [l.strip() for l in f if l.strip()]
     spill = [l for l in lines if "| scratch 0 |" not in l or "VGPR spill 0" not in l or "SGPR spill 0" not in l]
@@ -134,16 +169,19 @@ def resources(args):
            "kernels_built: %d" % len(lines),
            "kernels_with_scratch_or_spills: %d" % len(spill)]
     for name, w in inputs.ALL_WORKLOADS.items():
-        select = mbr.rmsnorm_select_quant_config if w.quant else mbr.rmsnorm_select_config
-        cfg = select(w.rows, w.hidden, torch.float32 if w.dtype == "f32" else torch.bfloat16, True, w.fused)
+        cfg = launch_config(w)
         e = "F32" if w.dtype == "f32" else "Bf16"
-        fam = {1: "rms_vec_kernel", 2: "rms_elem_kernel", 3: "rms_twopass_kernel"}[cfg.path]
         per = cfg.items_per_lane
         units = w.hidden // (4 if w.dtype == "f32" else 8)
         masked = 64 * cfg.waves_per_row * per != units
-        qt = {None: 0, "int8": 1, "fp8": 2}[w.quant]
-        mangled = "%sINS_%d%sELi%dELi%dELb%dELb%dELi%dEEEv" % (fam, len(e), e, cfg.waves_per_row, per, int(masked),
-                                                               int(w.fused), qt)
+        if w.backward:
+            fam = {1: "rms_bwd_vec_kernel", 2: "rms_bwd_elem_kernel", 3: "rms_bwd_twopass_kernel"}[cfg.path]
+            mangled = "%sINS_%d%sELi%dELi%dELb%dELb1EEEv" % (fam, len(e), e, cfg.waves_per_row, per, int(masked))
+        else:
+            fam = {1: "rms_vec_kernel", 2: "rms_elem_kernel", 3: "rms_twopass_kernel"}[cfg.path]
+            qt = {None: 0, "int8": 1, "fp8": 2}[w.quant]
+            mangled = "%sINS_%d%sELi%dELi%dELb%dELb%dELi%dEEEv" % (fam, len(e), e, cfg.waves_per_row, per,
+                                                                   int(masked), int(w.fused), qt)
         hit = [l for l in lines if mangled in l]
         out.append("%s -> %s | %s" % (name, cfg.as_dict(), hit[0].split("|", 1)[1].strip() if hit else "?"))
     print("\n".join(out))

@@ -137,9 +137,10 @@ def rmsnorm_dynamic_quant_fwd(x: np.ndarray, weight: np.ndarray, eps: float, qty
     return h, q, scale
 
 
-def rmsnorm_bwd(x: np.ndarray, weight: np.ndarray, dy: np.ndarray, eps: float, want_dw: bool = True):
+def rmsnorm_bwd(x: np.ndarray, weight: np.ndarray, dy: np.ndarray, eps: float, want_dw: bool = True,
+                want_dx: bool = True):
     """Returns ``(dx, dw)`` of y = RMSNorm(x) * weight for upstream gradient dy
-    (dw is None when not wanted)."""
+    (either is None when not wanted)."""
     x = _check(x, "x")
     dy = _check(dy, "dy")
     weight = np.ascontiguousarray(weight).reshape(-1)
@@ -148,9 +149,10 @@ def rmsnorm_bwd(x: np.ndarray, weight: np.ndarray, dy: np.ndarray, eps: float, w
         raise ValueError("dy must match x")
     if weight.dtype != x.dtype or weight.shape[0] != x.shape[1]:
         raise ValueError("weight must be [hidden] with the dtype of x")
-    dx = np.empty_like(x)
+    dx = np.empty_like(x) if want_dx else None
     dw = np.empty_like(weight) if want_dw else None
-    rc = _load().oracle_rmsnorm_bwd(x.ctypes.data, weight.ctypes.data, dy.ctypes.data, dx.ctypes.data,
+    rc = _load().oracle_rmsnorm_bwd(x.ctypes.data, weight.ctypes.data, dy.ctypes.data,
+                                    dx.ctypes.data if dx is not None else None,
                                     dw.ctypes.data if dw is not None else None, x.shape[0], x.shape[1],
                                     float(eps), code)
     if rc != 0:

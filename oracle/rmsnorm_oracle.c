@@ -280,7 +280,8 @@ int oracle_rmsnorm_dynamic_quant_fwd(const void *x, const void *residual, const 
  *   dx_k    = r dy_k w_k - x_k r^3 c / H
  *   dw_j    = sum_i dy_ij x_ij r_i        (over all rows, fp64)
  *
- * dx and dw are each rounded once to the dtype.  dw may be NULL (not wanted).
+ * dx and dw are each rounded once to the dtype.  Either may be NULL (not
+ * wanted); the other is unaffected.
  */
 int oracle_rmsnorm_bwd(const void *x, const void *w, const void *dy, void *dx, void *dw, int64_t rows,
                        int64_t hidden, float eps, int dtype) {
@@ -302,8 +303,9 @@ int oracle_rmsnorm_bwd(const void *x, const void *w, const void *dy, void *dx, v
         for (j = 0; j < hidden; ++j) {
             double v = load_elem(x, i * hidden + j, dtype);
             double g = load_elem(dy, i * hidden + j, dtype);
-            store_elem(dx, i * hidden + j, r * g * load_elem(w, j, dtype) - v * r * r * r * c / (double)hidden,
-                       dtype);
+            if (dx)
+                store_elem(dx, i * hidden + j, r * g * load_elem(w, j, dtype) - v * r * r * r * c / (double)hidden,
+                           dtype);
             if (acc) acc[j] += g * v * r;
         }
     }

@@ -199,3 +199,118 @@ def oracle_quant(x, w, eps, qtype, residual=None):
             s[a:b] = ss
         list(ex.map(job, _chunks(rows, 4 * threads())))
     return h, q, s
+
+
+# ---------------------------------------------------------------- backward
+#
+# Tolerance derivation.  Let u = 2^-24 and L the longest fp32 chain of a row
+# sum on the GPU (terms per lane + 6 wave levels + one add per wave slot).
+#   * r = rsqrt(s/H + eps): s has all-positive terms, so its relative error is
+#     <= L*u; r's is about half of that plus the rsqrt's and the divide's, below
+#     (L/2 + 4)*u.
+#   * c = sum(dy*w*x) has error <= (L + 2)*u * C_abs, C_abs = sum|dy*w*x|.
+#   * dx_k = r*(dy_k*w_k - x_k*r^2*c/H) therefore has absolute error below
+#     gamma * M_k with M_k = r*|dy_k*w_k| + |x_k|*r^3*C_abs/H and
+#     gamma = (2L + 16)*u.  The two terms can cancel, so the bound is on M_k,
+#     not on |dx_k|; both sides then round once, which adds at most one unit
+#     in the last place of the dtype.
+#   * dw_j = sum_i dy_ij*x_ij*r_i is summed per lane over ceil(rows/G) rows (G
+#     partial rows), then over ceil(G/64) partial rows per slice and a 6-level
+#     tree: absolute error below gamma_w * A_j, A_j = sum_i |dy_ij*x_ij|*r_i,
+#     gamma_w = 2*(ceil(rows/G) + ceil(G/64) + L/2 + 12)*u (factor 2 for the
+#     per-term errors and margin); plus one unit in the last place.
+# M and A are magnitudes computed here in fp64 for the bound only; the values
+# compared against are the oracle's.
+
+U = 2.0 ** -24
+
+
+def _values(a: np.ndarray) -> np.ndarray:
+    return bf16_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def _ulp(vals: np.ndarray, bf16: bool) -> np.ndarray:
+    sp = np.spacing(np.abs(vals).astype(np.float32)).astype(np.float64)
+    return sp * 65536.0 if bf16 else sp
+
+
+def bwd_chain(cfg, hidden: int, bf16: bool) -> int:
+    """Longest fp32 chain of a row sum for a launch configuration (see above)."""
+    v = 8 if bf16 else 4
+    wpr = cfg.waves_per_row
+    if cfg.path == 1:      # vector
+        per_lane = cfg.items_per_lane * v
+    elif cfg.path == 2:    # element
+        per_lane = cfg.items_per_lane
+    else:                  # two-pass: every lane strides over the row
+        vec = hidden % v == 0
+        units = hidden // v if vec else hidden
+        per_lane = -(-units // (64 * wpr)) * (v if vec else 1)
+    return per_lane + 6 + wpr
+
+
+def _bwd_magnitudes(x, w, dy, eps, rows_chunk=2048):
+    """(M, A): per-element dx magnitudes and per-column dw magnitudes, fp64."""
+    rows, hidden = x.shape
+    M = np.empty((rows, hidden))
+    A = np.zeros(hidden)
+    wd = _values(w)
+    for a in range(0, rows, rows_chunk):
+        xd = _values(x[a:a + rows_chunk])
+        gd = _values(dy[a:a + rows_chunk])
+        r = 1.0 / np.sqrt((xd * xd).mean(axis=1) + float(np.float32(eps)))
+        gw = np.abs(gd * wd[None, :])
+        cabs = (gw * np.abs(xd)).sum(axis=1)
+        M[a:a + rows_chunk] = r[:, None] * gw + np.abs(xd) * (r ** 3 * cabs / hidden)[:, None]
+        A += (np.abs(gd * xd) * r[:, None]).sum(axis=0)
+    return M, A
+
+
+def compare_bwd(dx_gpu, dw_gpu, dx_want, dw_want, x, w, dy, eps, cfg, n_part) -> dict:
+    """dx (and dw unless dw_want is None) against the oracle with the bounds above."""
+    bf16 = x.dtype == np.uint16
+    rows, hidden = x.shape
+    L = bwd_chain(cfg, hidden, bf16)
+    M, A = _bwd_magnitudes(x, w, dy, eps)
+    stats = {"chain": L}
+
+    def check(got, want, mag, gamma, what):
+        gv, wv = _values(got), _values(want)
+        gn, wn = ~np.isfinite(gv), ~np.isfinite(wv)
+        assert np.array_equal(gn, wn), "%s: non-finite positions differ" % what
+        assert np.array_equal(np.isnan(gv), np.isnan(wv)), "%s: NaN positions differ" % what
+        inf = np.isinf(wv)
+        assert np.array_equal(gv[inf], wv[inf]), "%s: infinities differ" % what
+        ok = ~wn
+        g = _values(got)[ok]
+        o = _values(want)[ok]
+        tol = gamma * mag[ok] + np.maximum(_ulp(o, bf16), _ulp(g, bf16))
+        err = np.abs(g - o)
+        ratio = err / tol if err.size else np.zeros(1)
+        if err.size and not np.all(err <= tol):
+            i = int(np.argmax(ratio))
+            flat = np.flatnonzero(ok)[i]
+            raise AssertionError("%s mismatch at flat index %d: got %r want %r (|err| %.3e > tol %.3e)"
+                                 % (what, flat, g[i], o[i], err[i], tol[i]))
+        stats[what] = {"n": int(ok.sum()), "max_err_over_tol": float(ratio.max()) if err.size else 0.0,
+                       "frac_bitwise_equal": float(np.mean(got[ok] == want[ok])) if err.size else 1.0}
+
+    check(dx_gpu, dx_want, M, (2 * L + 16) * U, "dx")
+    if dw_want is not None:
+        g = max(1, n_part)
+        gamma_w = 2 * (-(-rows // g) + -(-g // 64) + L / 2 + 12) * U
+        check(dw_gpu, dw_want, A, gamma_w, "dw")
+    return stats
+
+
+def oracle_bwd(x: np.ndarray, w: np.ndarray, dy: np.ndarray, eps: float, want_dw: bool = True):
+    """The oracle's dx over all rows (rows across host threads) and dw (one
+    serial fp64 pass over all rows, as the oracle defines it)."""
+    dx = np.empty_like(x)
+    with concurrent.futures.ThreadPoolExecutor(threads()) as ex:
+        def job(r):
+            dx[r[0]:r[1]] = oracle.rmsnorm_bwd(x[r[0]:r[1]], w, dy[r[0]:r[1]], eps, want_dw=False)[0]
+        fut = ex.submit(lambda: oracle.rmsnorm_bwd(x, w, dy, eps, want_dx=False)[1]) if want_dw else None
+        list(ex.map(job, _chunks(x.shape[0], 4 * threads())))
+        dw = fut.result() if fut is not None else None
+    return dx, dw

@@ -1,0 +1,300 @@
+"""Parity of the HIP RMSNorm backward (through the C ABI) with the CPU oracle.
+
+dx and dweight are compared element by element with the bounds derived in
+tests/parity.py (fp32 evaluation error scaled by the magnitudes of the terms,
+plus one unit in the last place).  Covered: the stated backward workloads at
+full size in the automatic launch configuration (the one bench.py times),
+every built vector / element / two-pass configuration on shapes with a partial
+last vector or lane, grid caps that make workgroups walk many rows, ragged
+widths, rows == 0, dx-only calls, in-place dx, misaligned buffers, workspace
+checks, determinism, non-finite rows and HIP-graph replays.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import memory_bound_rmsnorm_amd as mbr
+from memory_bound_rmsnorm_amd import inputs
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+BF16, F32 = torch.bfloat16, torch.float32
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def tdt(dtype):
+    return BF16 if dtype == "bf16" else F32
+
+
+def run_bwd(x, w, dy, eps, cfg=None, want_dw=True, dx=None, ws=None):
+    dx = torch.empty_like(x) if dx is None else dx
+    dw = torch.empty_like(w) if want_dw else None
+    mbr.rmsnorm_bwd_ex(x, w, dy, dx, dw, eps, ws, cfg)
+    torch.cuda.synchronize()
+    return dx, dw
+
+
+def effective_config(rows, hidden, dtype, cfg=None, aligned=True):
+    return cfg if cfg is not None else mbr.rmsnorm_select_bwd_config(rows, hidden, tdt(dtype), aligned)
+
+
+def n_partials(rows, cfg):
+    cap = cfg.max_blocks if cfg.max_blocks > 0 else 1 << 20
+    return min(rows, cap)
+
+
+def check(w, t, cfg=None, eps=None, want_dw=True):
+    eps = w.eps if eps is None else eps
+    dev = {k: v.cuda() for k, v in t.items()}
+    dx, dw = run_bwd(dev["x"], dev["weight"], dev["dy"], eps, cfg, want_dw)
+    xb, wb, gb = inputs.bits(t["x"]), inputs.bits(t["weight"]), inputs.bits(t["dy"])
+    dx_want, dw_want = parity.oracle_bwd(xb, wb, gb, eps, want_dw)
+    c = effective_config(w.rows, w.hidden, w.dtype, cfg)
+    return parity.compare_bwd(inputs.bits(dx), inputs.bits(dw) if want_dw else None, dx_want, dw_want,
+                              xb, wb, gb, eps, c, n_partials(w.rows, c))
+
+
+# ---------------------------------------------------------------- stated workloads
+
+
+@pytest.mark.parametrize("name", list(inputs.BWD_WORKLOADS))
+def test_bwd_workloads_full_size(name):
+    w = inputs.BWD_WORKLOADS[name]
+    say("bwd workload", name, "seed 0", mbr.rmsnorm_select_bwd_config(w.rows, w.hidden, tdt(w.dtype), True))
+    say(name, check(w, inputs.make(w, seed=0)))
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_bwd_prefill_other_seeds(seed):
+    w = inputs.BWD_WORKLOADS["bf16_bwd_4096x2048"]
+    say("bwd prefill seed", seed)
+    check(w, inputs.make(w, seed=seed))
+
+
+# ---------------------------------------------------------------- shapes and configurations
+
+
+RAGGED = [(1, 1), (3, 3), (5, 7), (2, 8), (5, 9), (67, 127), (12, 769), (5, 2048), (3, 4095), (7, 5120),
+          (5, 5121), (3, 8193), (9, 16384), (2, 20000), (3, 65536), (2, 81920), (2, 131080), (5000, 96)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,hidden", RAGGED)
+def test_bwd_ragged_shapes(rows, hidden, dtype):
+    w = inputs.custom(rows, hidden, dtype, backward=True)
+    say("bwd shape", rows, hidden, dtype, effective_config(rows, hidden, dtype))
+    check(w, inputs.make(w, seed=rows * 5 + hidden))
+
+
+def test_bwd_many_rows_per_workgroup():
+    """Far more rows than partial rows: every workgroup walks ~100 rows."""
+    w = inputs.custom(40000, 1024, "bf16", backward=True)
+    cfg = effective_config(40000, 1024, "bf16")
+    say("bwd many rows", cfg)
+    assert n_partials(40000, cfg) < 40000 // 8
+    check(w, inputs.make(w, seed=5))
+
+
+def _built_vec():
+    return [(wpr, vpl) for wpr in (1, 2, 4, 8, 16) for vpl in range(1, 9) if wpr < 16 or vpl <= 4]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_every_vector_config(dtype):
+    vecw = 8 if dtype == "bf16" else 4
+    n = 0
+    for wpr, vpl in _built_vec():
+        lanes = 64 * wpr
+        for nvec in sorted({lanes * vpl, max(1, lanes * vpl - 37), lanes * (vpl - 1) + 1}):
+            for mb, rows in ((0, 3), (2, 5)):
+                cfg = mbr.Config(mbr.PATH_VECTOR, wpr, vpl, 1, mb)
+                w = inputs.custom(rows, nvec * vecw, dtype, backward=True)
+                say("bwd vector", dtype, cfg, "hidden", nvec * vecw, "rows", rows)
+                check(w, inputs.make(w, seed=n), cfg, want_dw=(n % 3 != 2))
+                n += 1
+    assert n > 150
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_every_element_config(dtype):
+    n = 0
+    for wpr in (1, 2, 4, 8, 16):
+        for epl in (1, 2, 4, 8):
+            lanes = 64 * wpr
+            for hidden in sorted({lanes * epl, max(1, lanes * epl - 5), lanes * (epl - 1) + 1 if epl > 1 else 3}):
+                cfg = mbr.Config(mbr.PATH_ELEMENT, wpr, epl, 1, 2 if n % 2 else 0)
+                w = inputs.custom(5, hidden, dtype, backward=True)
+                say("bwd element", dtype, cfg, "hidden", hidden)
+                check(w, inputs.make(w, seed=n), cfg, want_dw=(n % 4 != 3))
+                n += 1
+    assert n > 40
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_every_two_pass_config(dtype):
+    for wpr in (1, 2, 4, 8, 16):
+        for hidden in (4096, 4099, 12288 + 8):
+            for mb in (0, 2):
+                cfg = mbr.Config(mbr.PATH_TWO_PASS, wpr, 0, 1, mb)
+                w = inputs.custom(5, hidden, dtype, backward=True)
+                say("bwd two-pass", dtype, cfg, "hidden", hidden)
+                check(w, inputs.make(w, seed=wpr + hidden + mb), cfg)
+
+
+def test_bwd_large_eps_and_small_rows():
+    """eps comparable to mean(x^2): a misplaced eps would show."""
+    w = inputs.custom(300, 2048, "f32", eps=0.5, x=inputs.Dist("normal", 0.0, 0.5), backward=True)
+    say("bwd eps 0.5")
+    check(w, inputs.make(w, seed=9))
+
+
+# ---------------------------------------------------------------- semantics
+
+
+def test_bwd_dx_only_matches_and_grid_cap_changes_no_dx_bit():
+    w = inputs.custom(3000, 4096, "bf16", backward=True)
+    t = {k: v.cuda() for k, v in inputs.make(w, seed=3).items()}
+    dx_a, dw_a = run_bwd(t["x"], t["weight"], t["dy"], 1e-5)
+    dx_b, _ = run_bwd(t["x"], t["weight"], t["dy"], 1e-5, want_dw=False)
+    assert torch.equal(dx_a, dx_b)
+    base = effective_config(3000, 4096, "bf16")
+    for mb in (1, 7, 3000):
+        cfg = mbr.Config(base.path, base.waves_per_row, base.items_per_lane, 1, mb)
+        dx_c, dw_c = run_bwd(t["x"], t["weight"], t["dy"], 1e-5, cfg)
+        assert torch.equal(dx_a, dx_c), mb
+        say("bwd grid cap", mb)
+        xb, wb, gb = (inputs.bits(t[k].cpu()) for k in ("x", "weight", "dy"))
+        dx_want, dw_want = parity.oracle_bwd(xb, wb, gb, 1e-5)
+        parity.compare_bwd(inputs.bits(dx_c.cpu()), inputs.bits(dw_c.cpu()), dx_want, dw_want, xb, wb, gb, 1e-5,
+                           cfg, n_partials(3000, cfg))
+
+
+@pytest.mark.parametrize("alias", ["dx=dy", "dx=x"])
+@pytest.mark.parametrize("hidden", [4096, 4100, 81920])
+def test_bwd_in_place(alias, hidden):
+    w = inputs.custom(37, hidden, "bf16", backward=True)
+    t = {k: v.cuda() for k, v in inputs.make(w, seed=4).items()}
+    dx_e, dw_e = run_bwd(t["x"], t["weight"], t["dy"], 1e-5)
+    x, dy = t["x"].clone(), t["dy"].clone()
+    dst = dy if alias == "dx=dy" else x
+    dx_i, dw_i = run_bwd(x, t["weight"], dy, 1e-5, dx=dst)
+    assert dx_i.data_ptr() == dst.data_ptr()
+    assert torch.equal(dx_i, dx_e) and torch.equal(dw_i, dw_e)
+
+
+def test_bwd_rows_zero_zeroes_dweight():
+    wt = torch.randn(1000, device="cuda").to(BF16)
+    x = torch.empty(0, 1000, dtype=BF16, device="cuda")
+    dw = torch.full_like(wt, float("nan"))
+    mbr.rmsnorm_bwd(x, wt, torch.empty_like(x), torch.empty_like(x), dw, 1e-5)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dw) == 0 and not torch.isnan(dw).any()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_misaligned_pointers(dtype):
+    rows, hidden, eps = 33, 2048, 1e-5
+    td = tdt(dtype)
+    es = 2 if dtype == "bf16" else 4
+    w = inputs.custom(rows, hidden, dtype, backward=True)
+    t = inputs.make(w, seed=11)
+    bufs = {k: torch.zeros(rows * hidden + 8, dtype=td, device="cuda") for k in ("x", "dy", "dx")}
+    wbuf = torch.zeros(hidden + 8, dtype=td, device="cuda")
+    dwbuf = torch.zeros(hidden + 8, dtype=td, device="cuda")
+    bufs["x"][1:1 + rows * hidden] = t["x"].reshape(-1).cuda()
+    bufs["dy"][1:1 + rows * hidden] = t["dy"].reshape(-1).cuda()
+    wbuf[1:1 + hidden] = t["weight"].cuda()
+    nbytes = mbr.rmsnorm_bwd_workspace_size(rows, hidden, td)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    st = mbr.lib().rmsnorm_bwd(bufs["x"].data_ptr() + es, wbuf.data_ptr() + es, bufs["dy"].data_ptr() + es,
+                               bufs["dx"].data_ptr() + es, dwbuf.data_ptr() + es, rows, hidden, eps,
+                               mbr.dtype_code(td), ws.data_ptr(), nbytes, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == mbr.RMSNORM_OK
+    dx = inputs.bits(bufs["dx"][1:1 + rows * hidden].reshape(rows, hidden).cpu())
+    dw = inputs.bits(dwbuf[1:1 + hidden].cpu())
+    xb, wb, gb = inputs.bits(t["x"]), inputs.bits(t["weight"]), inputs.bits(t["dy"])
+    dx_want, dw_want = parity.oracle_bwd(xb, wb, gb, eps)
+    cfg = effective_config(rows, hidden, dtype, aligned=False)
+    assert cfg.path == mbr.PATH_ELEMENT
+    parity.compare_bwd(dx, dw, dx_want, dw_want, xb, wb, gb, eps, cfg, n_partials(rows, cfg))
+    assert bufs["dx"][0].item() == 0 and torch.count_nonzero(bufs["dx"][1 + rows * hidden:]) == 0
+    assert dwbuf[0].item() == 0 and torch.count_nonzero(dwbuf[1 + hidden:]) == 0
+
+
+def test_bwd_workspace_checked_on_device_buffers():
+    rows, hidden = 100, 1024
+    x = torch.randn(rows, hidden, device="cuda").to(BF16)
+    dy, dx = torch.randn_like(x), torch.empty_like(x)
+    wt = torch.ones(hidden, dtype=BF16, device="cuda")
+    dw = torch.empty_like(wt)
+    need = mbr.rmsnorm_bwd_workspace_size(rows, hidden, BF16)
+    cfg = effective_config(rows, hidden, "bf16")
+    assert need == min(rows, cfg.max_blocks) * 1024 * 4
+    ws = torch.empty(need + 64, dtype=torch.uint8, device="cuda")
+    L, s = mbr.lib(), torch.cuda.current_stream().cuda_stream
+    args = (x.data_ptr(), wt.data_ptr(), dy.data_ptr(), dx.data_ptr(), dw.data_ptr(), rows, hidden, 1e-5, 1)
+    INV = mbr.RMSNORM_ERR_INVALID_ARG
+    assert L.rmsnorm_bwd(*args, ws.data_ptr(), need - 1, s) == INV
+    assert L.rmsnorm_bwd(*args, None, need, s) == INV
+    assert L.rmsnorm_bwd(*args, ws.data_ptr() + 8, need, s) == INV          # not 16-byte aligned
+    assert L.rmsnorm_bwd(*args[:4], dx.data_ptr() + 64, *args[5:], ws.data_ptr(), need, s) == INV  # dw inside dx
+    assert L.rmsnorm_bwd(*args, dx.data_ptr(), need, s) == INV              # workspace over dx
+    assert L.rmsnorm_bwd(*args[:3], x.data_ptr() + 2, *args[4:], ws.data_ptr(), need, s) == INV  # partial overlap
+    assert L.rmsnorm_bwd(*args[:3], wt.data_ptr(), *args[4:], ws.data_ptr(), need, s) == INV     # dx over weight
+    assert L.rmsnorm_bwd(*args, ws.data_ptr(), need, s) == mbr.RMSNORM_OK
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name", ["bf16_bwd_16384x8192", "fp32_bwd_64x2048"])
+def test_bwd_bitwise_deterministic(name):
+    w = inputs.BWD_WORKLOADS[name]
+    t = {k: v.cuda() for k, v in inputs.make(w, seed=0).items()}
+    a = run_bwd(t["x"], t["weight"], t["dy"], w.eps)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        dx, dw = torch.empty_like(t["x"]), torch.empty_like(t["weight"])
+        mbr.rmsnorm_bwd(t["x"], t["weight"], t["dy"], dx, dw, w.eps, stream=s)
+    s.synchronize()
+    assert torch.equal(a[0], dx) and torch.equal(a[1], dw)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_non_finite_rows(dtype):
+    """A NaN or Inf in one row of x makes that row's dx and every dweight NaN,
+    as in the oracle; other rows' dx are untouched."""
+    w = inputs.custom(9, 1024, dtype, backward=True)
+    t = inputs.make(w, seed=2)
+    t["x"][3, 17] = float("nan")
+    say("bwd non-finite", dtype)
+    check(w, t)
+    t = inputs.make(w, seed=2)
+    t["dy"][5, 3] = float("inf")
+    check(w, t)
+
+
+def test_bwd_graph_capture_replays_match_eager():
+    w = inputs.custom(3000, 5120, "bf16", backward=True)
+    t = {k: v.cuda() for k, v in inputs.make(w, seed=17).items()}
+    dx_e, dw_e = run_bwd(t["x"], t["weight"], t["dy"], 1e-5)
+    dx_g, dw_g = torch.empty_like(t["x"]), torch.empty_like(t["weight"])
+    ws = torch.empty(mbr.rmsnorm_bwd_workspace_size(3000, 5120, BF16), dtype=torch.uint8, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mbr.rmsnorm_bwd(t["x"], t["weight"], t["dy"], dx_g, dw_g, 1e-5, ws)
+    for rep in range(3):
+        dx_g.zero_()
+        dw_g.zero_()
+        ws.fill_(0x7F)  # the workspace's contents on entry must not matter
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dx_g, dx_e) and torch.equal(dw_g, dw_e), "replay %d differs" % rep
+        run_bwd(t["x"], t["weight"], t["dy"], 1e-5)
