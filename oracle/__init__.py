@@ -14,7 +14,8 @@ bit-exact special cases and an exact-rational brute force --
 ``tests/test_oracle_pins.py`` (forward, fused residual),
 ``tests/test_oracle_quant_pins.py`` (dynamic quantisation) and
 ``tests/test_oracle_bwd_pins.py`` (backward: 80-digit central differences of
-the forward, closed forms, invariants).
+the forward, closed forms, invariants) and ``tests/test_oracle_ln_pins.py``
+(LayerNorm: torch's float64 layer_norm, closed forms, exact invariances).
 The only unpinned choice is which bf16 neighbour is returned when the exact
 result lies within the fp64 evaluation error (about 1e-12 relative) of a
 rounding midpoint.
@@ -53,6 +54,8 @@ def _load():
         lib.oracle_rmsnorm_dynamic_quant_fwd.restype = i32
         lib.oracle_rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, i32]
         lib.oracle_rmsnorm_bwd.restype = i32
+        lib.oracle_layernorm_fwd.argtypes = [vp, vp, vp, vp, i64, i64, f32, i32]
+        lib.oracle_layernorm_fwd.restype = i32
         _lib = lib
     return _lib
 
@@ -158,6 +161,27 @@ def rmsnorm_bwd(x: np.ndarray, weight: np.ndarray, dy: np.ndarray, eps: float, w
     if rc != 0:
         raise RuntimeError("oracle_rmsnorm_bwd failed")
     return dx, dw
+
+
+def layernorm_fwd(x: np.ndarray, gamma: np.ndarray, beta, eps: float) -> np.ndarray:
+    """LayerNorm of every row of ``x``: gamma * (x - mean) / sqrt(var + eps) + beta
+    (beta None: no bias), same dtype out."""
+    x = _check(x, "x")
+    gamma = np.ascontiguousarray(gamma).reshape(-1)
+    code = _dtype_code(x)
+    if gamma.dtype != x.dtype or gamma.shape[0] != x.shape[1]:
+        raise ValueError("gamma must be [hidden] with the dtype of x")
+    if beta is not None:
+        beta = np.ascontiguousarray(beta).reshape(-1)
+        if beta.dtype != x.dtype or beta.shape[0] != x.shape[1]:
+            raise ValueError("beta must be [hidden] with the dtype of x")
+    out = np.empty_like(x)
+    rc = _load().oracle_layernorm_fwd(x.ctypes.data, gamma.ctypes.data,
+                                      beta.ctypes.data if beta is not None else None, out.ctypes.data,
+                                      x.shape[0], x.shape[1], float(eps), code)
+    if rc != 0:
+        raise RuntimeError("oracle_layernorm_fwd failed")
+    return out
 
 
 def round_e4m3(v: float) -> int:

@@ -29,6 +29,8 @@
  *   is written back in the tensor dtype and the *rounded* h is what gets
  *   normalised, i.e. the result equals an unfused add followed by RMSNorm.
  *
+ *   LayerNorm (oracle_layernorm_fwd): mean, centred variance, one rounding.
+ *
  *   Backward (dx and dweight for an upstream gradient dy): the plain
  *   derivative of the forward above, in fp64, each output rounded once; dweight
  *   sums over all rows in ascending row order.  See oracle_rmsnorm_bwd.
@@ -312,6 +314,41 @@ int oracle_rmsnorm_bwd(const void *x, const void *w, const void *dy, void *dx, v
     if (acc) {
         for (j = 0; j < hidden; ++j) store_elem(dw, j, acc[j], dtype);
         free(acc);
+    }
+    return 0;
+}
+
+/*
+ * LayerNorm, the sibling norm on the same pages: per row,
+ *
+ *   y_j = gamma_j * (x_j - mu) / sqrt(var + eps) + beta_j,
+ *   mu = sum_j x_j / H,  var = sum_j (x_j - mu)^2 / H   (biased, divisor H)
+ *
+ * (xserv "phase 4: transformer core kernels", csrc/normalization/layernorm.cu
+ * header comment and docs/04-transformer-kernels.md "LayerNorm"; the CPU
+ * reference cpu_layernorm in crates/xserv-kernels/tests/ops_test.rs divides the
+ * centred sum of squares by hidden).  Plain two-pass definition in fp64: the
+ * mean first, then the centred squares, then one rounding per output.
+ * beta may be NULL (no bias).
+ */
+int oracle_layernorm_fwd(const void *x, const void *gamma, const void *beta, void *out, int64_t rows,
+                         int64_t hidden, float eps, int dtype) {
+    int64_t i, j;
+    if (rows < 0 || hidden <= 0 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16)) return -1;
+    for (i = 0; i < rows; ++i) {
+        double s = 0.0, q = 0.0, mu, inv;
+        for (j = 0; j < hidden; ++j) s += load_elem(x, i * hidden + j, dtype);
+        mu = s / (double)hidden;
+        for (j = 0; j < hidden; ++j) {
+            double d = load_elem(x, i * hidden + j, dtype) - mu;
+            q += d * d;
+        }
+        inv = 1.0 / sqrt(q / (double)hidden + (double)eps);
+        for (j = 0; j < hidden; ++j) {
+            double v = load_elem(gamma, j, dtype) * (load_elem(x, i * hidden + j, dtype) - mu) * inv;
+            if (beta) v += load_elem(beta, j, dtype);
+            store_elem(out, i * hidden + j, v, dtype);
+        }
     }
     return 0;
 }

@@ -16,6 +16,7 @@ from oracle import build as oracle_build
 from tests import test_oracle_pins as pins
 from tests import test_oracle_quant_pins as qpins
 from tests import test_oracle_bwd_pins as bpins
+from tests import test_oracle_ln_pins as lpins
 
 MUTANTS = [
     ("eps dropped", "sqrt(mean + (double)eps)", "sqrt(mean)"),
@@ -75,6 +76,24 @@ MUTANTS += [
      "double g = load_elem(dy, j * rows + i, dtype);"),
 ]
 
+MUTANTS += [
+    ("ln variance divisor H - 1", "inv = 1.0 / sqrt(q / (double)hidden + (double)eps);",
+     "inv = 1.0 / sqrt(q / (double)(hidden > 1 ? hidden - 1 : 1) + (double)eps);"),
+    ("ln eps outside the root", "inv = 1.0 / sqrt(q / (double)hidden + (double)eps);",
+     "inv = 1.0 / sqrt(q / (double)hidden) + (double)eps;"),
+    ("ln mean not subtracted", "double v = load_elem(gamma, j, dtype) * (load_elem(x, i * hidden + j, dtype) - mu) * inv;",
+     "double v = load_elem(gamma, j, dtype) * load_elem(x, i * hidden + j, dtype) * inv;"),
+    ("ln beta dropped", "if (beta) v += load_elem(beta, j, dtype);", "if (beta) v += 0.0;"),
+    ("ln gamma added as the bias", "if (beta) v += load_elem(beta, j, dtype);", "if (beta) v += load_elem(gamma, j, dtype);"),
+    ("ln uncentred fp32 variance",
+     "            double d = load_elem(x, i * hidden + j, dtype) - mu;\n            q += d * d;\n        }\n"
+     "        inv = 1.0 / sqrt(q / (double)hidden + (double)eps);",
+     "            float d = (float)load_elem(x, i * hidden + j, dtype);\n            q += (double)(d * d);\n        }\n"
+     "        inv = 1.0 / sqrt((double)((float)(q / (double)hidden) - (float)(mu * mu)) + (double)eps);"),
+    ("ln mean read transposed", "for (j = 0; j < hidden; ++j) s += load_elem(x, i * hidden + j, dtype);",
+     "for (j = 0; j < hidden; ++j) s += load_elem(x, j * rows + i, dtype);"),
+]
+
 HELPER = """
 static float oracle_bf16_back(uint16_t b) { uint32_t u = (uint32_t)b << 16; float f; memcpy(&f, &u, 4); return f; }
 """
@@ -114,6 +133,14 @@ PIN_TESTS = [
     (bpins.test_weight_gradient_identity, {}),
     (bpins.test_linear_in_dy_and_zero_gradient, {}),
     (bpins.test_rows_independent_and_dw_sums_rows, {}),
+    (lpins.test_matches_torch_layer_norm_in_float64, dict(dtype="f32", with_beta=True)),
+    (lpins.test_two_columns_closed_form, dict(dtype="f32")),
+    (lpins.test_constant_rows_and_single_column_give_beta, dict(dtype="bf16")),
+    (lpins.test_shift_invariance_bitwise, {}),
+    (lpins.test_scale_and_sign_invariance_bitwise, {}),
+    (lpins.test_standardised_moments, {}),
+    (lpins.test_rows_independent_and_layout, {}),
+    (lpins.test_pages_layernorm_test_case, {}),
 ]
 
 
