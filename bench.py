@@ -6,7 +6,8 @@ workload) over a whole [rows, hidden] batch: load rows, sum squares, inverse
 root, scale and store.  Default workload: bf16 [16384, 8192], the
 large-hidden configuration the headline bandwidth figure is quoted on.  The
 quantised workloads time rmsnorm_dynamic_quant_fwd, the backward ones
-rmsnorm_bwd (dx and dweight: the row kernel plus the dweight reduction).
+rmsnorm_bwd (dx and dweight: the row kernel plus the dweight reduction), the
+LayerNorm ones layernorm_fwd.
 
 Byte accounting follows the TileLang tutorial ch. 02, section 2.1: every input
 read once, every output written once, the weight once; the figure reported is
@@ -90,6 +91,8 @@ class Sets:
         self.weight = dev["weight"]
         self.sets = []
         self.backward = w.backward
+        self.layernorm = w.layernorm
+        self.beta = dev.get("beta")
         if w.backward:
             nbytes = mbr.rmsnorm_bwd_workspace_size(w.rows, w.hidden, self.weight.dtype)
             self.workspace = torch.empty(max(1, nbytes), dtype=torch.uint8, device="cuda")
@@ -118,6 +121,8 @@ class Sets:
         s = self.sets[i % len(self.sets)]
         if self.backward:
             mbr.rmsnorm_bwd(s["x"], self.weight, s["dy"], s["dx"], s["dw"], self.eps, self.workspace)
+        elif self.layernorm:
+            mbr.layernorm_fwd(s["x"], self.weight, self.beta, s["out"], self.eps)
         elif self.quant is not None:
             mbr.rmsnorm_dynamic_quant_fwd(s["x"], self.weight, s["q"], s["scale"], self.eps, self.quant,
                                           s.get("residual"), s.get("h"))
@@ -186,12 +191,13 @@ def copy_ceiling(w, steps, warmup):
 KERNEL_FAMILY = {"vector": "rms_vec_kernel", "element": "rms_elem_kernel", "two_pass": "rms_twopass_kernel"}
 BWD_KERNEL_FAMILY = {"vector": "rms_bwd_vec_kernel", "element": "rms_bwd_elem_kernel",
                      "two_pass": "rms_bwd_twopass_kernel"}
+LN_KERNEL_FAMILY = {"vector": "ln_vec_kernel", "element": "ln_elem_kernel", "two_pass": "ln_multipass_kernel"}
 
 
 def load_traffic(w, launch):
     """HBM bytes per step from the committed counter summary, if it was taken
     on the current kernel sources in the current launch configuration; else None."""
-    fam = (BWD_KERNEL_FAMILY if w.backward else KERNEL_FAMILY)[launch["path"]]
+    fam = (BWD_KERNEL_FAMILY if w.backward else LN_KERNEL_FAMILY if w.layernorm else KERNEL_FAMILY)[launch["path"]]
     path = os.path.join(PROFILE_DIR, "pmc_traffic_%s_%s.txt" % (fam, w.name))
     if not os.path.exists(path):
         return None
@@ -203,7 +209,7 @@ def load_traffic(w, launch):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
     try:
-        if vals.get("source_sha256") != _build.source_digest("bwd" if w.backward else "fwd"):
+        if vals.get("source_sha256") != _build.source_digest("bwd" if w.backward else "ln" if w.layernorm else "fwd"):
             return None
         if vals.get("launch_config") != " ".join("%s=%s" % kv for kv in launch.items()):
             return None
@@ -224,6 +230,7 @@ def cpu_baseline(w, t, seconds):
     wb = inputs.bits(t["weight"])
     rb = inputs.bits(t["residual"])[:rows] if w.fused else None
     gb = inputs.bits(t["dy"])[:rows] if w.backward else None
+    bb = inputs.bits(t["beta"]) if w.layernorm else None
     per_thread = [(i * rows // T, (i + 1) * rows // T) for i in range(T)]
     qt = {"int8": oracle.QUANT_INT8, "fp8": oracle.QUANT_FP8_E4M3}.get(w.quant)
 
@@ -234,6 +241,8 @@ def cpu_baseline(w, t, seconds):
                     return
                 if w.backward:  # each thread: dx and its rows' dweight
                     oracle.rmsnorm_bwd(xb[r[0]:r[1]], wb, gb[r[0]:r[1]], w.eps)
+                elif w.layernorm:
+                    oracle.layernorm_fwd(xb[r[0]:r[1]], wb, bb, w.eps)
                 elif qt is not None:
                     oracle.rmsnorm_dynamic_quant_fwd(xb[r[0]:r[1]], wb, w.eps, qt,
                                                      residual=rb[r[0]:r[1]] if w.fused else None)
@@ -253,7 +262,7 @@ def cpu_baseline(w, t, seconds):
         if el >= seconds:
             break
     sample_bytes = inputs.Workload(w.name, w.dtype, rows, w.hidden, w.eps, w.fused, w.x, w.weight, w.residual,
-                                   quant=w.quant, grad=w.grad).algorithmic_bytes
+                                   quant=w.quant, grad=w.grad, beta=w.beta).algorithmic_bytes
     return {"value": round(sample_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": T, "kind": "oracle",
             "sample": "first %d of %d rows, %d passes in %.1f s on %d threads (%s)"
                       % (rows, w.rows, reps, el, T, cpu_model())}
@@ -306,7 +315,8 @@ def main():
     achieved = rec["gbps_kernel"]
     line = {
         "metric": "bf16 RMSNorm achieved HBM GB/s and % of peak at 16384×8192" if w.name == inputs.HEADLINE
-                  else "RMSNorm%s achieved HBM GB/s (%s)" % (" backward" if w.backward else "", w.name),
+                  else "%s achieved HBM GB/s (%s)" % ("LayerNorm" if w.layernorm else
+                                                      "RMSNorm backward" if w.backward else "RMSNorm", w.name),
         "value": round(rec["gbps_wall"], 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -319,11 +329,13 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded; x ~ N(0,1) with 8 outlier channels x100, weight ~ N(1, 0.1))"
                 if w.name == inputs.HEADLINE else "synthetic (seeded)",
-        "config": {"workload": "RMSNorm %s%s [%d, %d]%s%s, eps %g" % (
+        "config": {"workload": "%s %s%s [%d, %d]%s%s, eps %g" % (
+                       "LayerNorm" if w.layernorm else "RMSNorm",
                        "backward (dx, dweight) " if w.backward else "", w.dtype, w.rows, w.hidden,
                        " fused residual" if w.fused else "",
                        " with %s dynamic quantisation" % w.quant if w.quant else "", w.eps),
                    "rows": w.rows, "hidden": w.hidden, "fused": w.fused, "quant": w.quant, "backward": w.backward,
+                   "layernorm": w.layernorm,
                    "algorithmic_bytes_per_step": w.algorithmic_bytes, "rotation_sets": rec["rotation_sets"],
                    "launch": rec["kernel_config"]},
         "pct_of_peak": round(100 * rec["gbps_wall"] / HBM_PEAK_GBPS, 2),
@@ -333,6 +345,7 @@ def main():
                      "traffic": load_traffic(w, rec["kernel_config"])},
         "parity": "checked against the CPU oracle at this size and launch configuration by "
                   + ("tests/test_bwd_gpu.py::test_bwd_workloads_full_size" if w.backward else
+                     "tests/test_ln_gpu.py::test_ln_workloads_full_size" if w.layernorm else
                      "tests/test_quant_gpu.py" if w.quant else
                      "tests/test_parity_gpu.py::test_stated_workloads_full_size"),
     }

@@ -285,6 +285,41 @@ RMSNORM_API rmsnorm_status_t rmsnorm_bwd_workspace_size(int64_t rows, int64_t hi
 RMSNORM_API rmsnorm_status_t rmsnorm_select_bwd_config(int64_t rows, int64_t hidden, rmsnorm_dtype_t dtype,
                                                        int32_t vector_aligned, rmsnorm_config_t* cfg);
 
+/*
+ * LayerNorm, the sibling norm on the same pages (xserv "phase 4: transformer
+ * core kernels", csrc/normalization/layernorm.cu header comment and
+ * docs/04-transformer-kernels.md "LayerNorm"), per row:
+ *
+ *     y_j = gamma_j * (x_j - mu) * rsqrt(var + eps) + beta_j,
+ *     mu = sum_j x_j / hidden,  var = sum_j (x_j - mu)^2 / hidden
+ *
+ * (biased variance, as the pages' CPU reference).  The mean is reduced first
+ * and the centred squares after it, from the row held in registers (no
+ * E[x^2] - mu^2 cancellation, no extra memory pass), in fp32; each output is
+ * rounded once after the affine step.
+ *
+ *   x       [rows, hidden] input, read once (three times for rows wider than
+ *           the register path covers).
+ *   gamma   [hidden], same dtype.
+ *   beta    [hidden], same dtype, or NULL for no bias.
+ *   out     [rows, hidden]; may be x itself, must not touch gamma or beta.
+ *   rows, hidden, eps, dtype, stream: as rmsnorm_fwd.
+ */
+RMSNORM_API rmsnorm_status_t layernorm_fwd(const void* x, const void* gamma, const void* beta, void* out,
+                                           int64_t rows, int64_t hidden, float eps, rmsnorm_dtype_t dtype,
+                                           void* stream);
+
+/* layernorm_fwd with a launch configuration (NULL or path AUTO = automatic;
+ * path TWO_PASS selects the three-pass wide-row kernel); rows_per_block must
+ * be 1. */
+RMSNORM_API rmsnorm_status_t layernorm_fwd_ex(const void* x, const void* gamma, const void* beta, void* out,
+                                              int64_t rows, int64_t hidden, float eps, rmsnorm_dtype_t dtype,
+                                              const rmsnorm_config_t* cfg, void* stream);
+
+/* The configuration layernorm_fwd would choose.  No HIP call. */
+RMSNORM_API rmsnorm_status_t layernorm_select_config(int64_t rows, int64_t hidden, rmsnorm_dtype_t dtype,
+                                                     int32_t vector_aligned, rmsnorm_config_t* cfg);
+
 #ifdef __cplusplus
 }
 #endif

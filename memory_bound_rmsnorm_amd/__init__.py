@@ -17,6 +17,9 @@ fallback -- if the library is not built, every call raises.
     rmsnorm_bwd_ex(..., config)                                forced launch configuration
     rmsnorm_bwd_workspace_size(rows, hidden, dtype, config)    -> bytes
     rmsnorm_select_bwd_config(rows, hidden, dtype, vector_aligned) -> Config
+    layernorm_fwd(x, gamma, beta, out, eps)                    -> out (beta may be None)
+    layernorm_fwd_ex(..., config)                              forced launch configuration
+    layernorm_select_config(rows, hidden, dtype, vector_aligned) -> Config
     rmsnorm_status_string(status)                              -> str
 
 The backward's weight gradient needs a workspace; when none is passed, a
@@ -98,12 +101,15 @@ def lib() -> ctypes.CDLL:
         L.rmsnorm_bwd_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, i32, vp, ctypes.c_size_t, cfgp, vp]
         L.rmsnorm_bwd_workspace_size.argtypes = [i64, i64, i32, cfgp, ctypes.POINTER(ctypes.c_size_t)]
         L.rmsnorm_select_bwd_config.argtypes = [i64, i64, i32, i32, cfgp]
+        L.layernorm_fwd.argtypes = [vp, vp, vp, vp, i64, i64, f32, i32, vp]
+        L.layernorm_fwd_ex.argtypes = [vp, vp, vp, vp, i64, i64, f32, i32, cfgp, vp]
+        L.layernorm_select_config.argtypes = [i64, i64, i32, i32, cfgp]
         L.rmsnorm_status_string.argtypes = [i32]
         L.rmsnorm_status_string.restype = ctypes.c_char_p
         for fn in (L.rmsnorm_fwd, L.rmsnorm_residual_fwd, L.rmsnorm_fwd_ex, L.rmsnorm_residual_fwd_ex,
                    L.rmsnorm_select_config, L.rmsnorm_select_quant_config, L.rmsnorm_dynamic_quant_fwd,
                    L.rmsnorm_dynamic_quant_fwd_ex, L.rmsnorm_bwd, L.rmsnorm_bwd_ex, L.rmsnorm_bwd_workspace_size,
-                   L.rmsnorm_select_bwd_config):
+                   L.rmsnorm_select_bwd_config, L.layernorm_fwd, L.layernorm_fwd_ex, L.layernorm_select_config):
             fn.restype = i32
         _lib = L
     return _lib
@@ -321,6 +327,38 @@ def rmsnorm_bwd_ex(x, weight, dy, dx, dweight=None, eps: float = 1e-5, workspace
 def rmsnorm_bwd(x, weight, dy, dx, dweight=None, eps: float = 1e-5, workspace=None, stream=None):
     """RMSNorm backward (C: rmsnorm_bwd)."""
     return rmsnorm_bwd_ex(x, weight, dy, dx, dweight, eps, workspace, None, stream)
+
+
+def layernorm_fwd_ex(x, gamma, beta, out, eps: float = 1e-5, config: Optional[Config] = None, stream=None):
+    """out = LayerNorm(x) * gamma + beta over the last dimension (beta None: no
+    bias), with a forced configuration."""
+    for t, n in ((x, "x"), (gamma, "gamma"), (out, "out")):
+        _device_tensor(t, n)
+    if out.shape != x.shape or out.dtype != x.dtype or gamma.dtype != x.dtype:
+        raise ValueError("out must match x in shape and dtype; gamma must match x in dtype")
+    rows, hidden = _shape(x, gamma)
+    if beta is not None:
+        _device_tensor(beta, "beta")
+        if beta.shape != gamma.shape or beta.dtype != x.dtype:
+            raise ValueError("beta must match gamma in shape and dtype")
+    st = lib().layernorm_fwd_ex(x.data_ptr(), gamma.data_ptr(), beta.data_ptr() if beta is not None else None,
+                                out.data_ptr(), rows, hidden, float(eps), dtype_code(x.dtype),
+                                ctypes.byref(config) if config is not None else None, _stream(stream, x.device))
+    _check(st, "layernorm_fwd")
+    return out
+
+
+def layernorm_fwd(x, gamma, beta, out, eps: float = 1e-5, stream=None):
+    """LayerNorm over the last dimension (C: layernorm_fwd)."""
+    return layernorm_fwd_ex(x, gamma, beta, out, eps, None, stream)
+
+
+def layernorm_select_config(rows: int, hidden: int, dtype, vector_aligned: bool = True) -> Config:
+    code = dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype)
+    cfg = Config()
+    _check(lib().layernorm_select_config(int(rows), int(hidden), code, int(bool(vector_aligned)),
+                                         ctypes.byref(cfg)), "layernorm_select_config")
+    return cfg
 
 
 def hbm_copy(src: torch.Tensor, dst: torch.Tensor, max_blocks: int = 0, stream=None):

@@ -1,0 +1,59 @@
+// Instantiations of the LayerNorm kernels and their lookup functions.
+#include <utility>
+
+#include "layernorm_kernels.hpp"
+#include "rmsnorm_dispatch.hpp"
+
+namespace mbr {
+namespace {
+
+template <class E, int WPR, int VPL, bool MASKED>
+const void* lvec_ptr() {
+    if constexpr (ln_vec_built(WPR, VPL))
+        return reinterpret_cast<const void*>(&ln_vec_kernel<E, WPR, VPL, MASKED>);
+    else
+        return nullptr;
+}
+
+template <class E, bool MASKED, size_t... I>
+const void* const* lvec_table(std::index_sequence<I...>) {
+    static const void* const table[] = {lvec_ptr<E, kWprList[I / kNumLnVpl], kLnVplList[I % kNumLnVpl], MASKED>()...};
+    return table;
+}
+
+template <class E, size_t... I>
+const void* const* lelem_table(std::index_sequence<I...>) {
+    static const void* const table[] = {
+        reinterpret_cast<const void*>(&ln_elem_kernel<E, kWprList[I / kNumLnEpl], kLnEplList[I % kNumLnEpl]>)...};
+    return table;
+}
+
+}  // namespace
+
+const void* ln_vec_kernel_ptr(int dtype, bool masked, int wi, int vi) {
+    using Seq = std::make_index_sequence<kNumWpr * kNumLnVpl>;
+    if (wi < 0 || wi >= kNumWpr || vi < 0 || vi >= kNumLnVpl) return nullptr;
+    const void* const* t;
+    if (dtype == 1)
+        t = masked ? lvec_table<Bf16, true>(Seq{}) : lvec_table<Bf16, false>(Seq{});
+    else
+        t = masked ? lvec_table<F32, true>(Seq{}) : lvec_table<F32, false>(Seq{});
+    return t[wi * kNumLnVpl + vi];
+}
+
+const void* ln_elem_kernel_ptr(int dtype, int wi, int ei) {
+    using Seq = std::make_index_sequence<kNumWpr * kNumLnEpl>;
+    if (wi < 0 || wi >= kNumWpr || ei < 0 || ei >= kNumLnEpl) return nullptr;
+    const void* const* t = dtype == 1 ? lelem_table<Bf16>(Seq{}) : lelem_table<F32>(Seq{});
+    return t[wi * kNumLnEpl + ei];
+}
+
+const void* ln_multipass_kernel_ptr(int dtype, bool vec) {
+    if (dtype == 1)
+        return vec ? reinterpret_cast<const void*>(&ln_multipass_kernel<Bf16, true>)
+                   : reinterpret_cast<const void*>(&ln_multipass_kernel<Bf16, false>);
+    return vec ? reinterpret_cast<const void*>(&ln_multipass_kernel<F32, true>)
+               : reinterpret_cast<const void*>(&ln_multipass_kernel<F32, false>);
+}
+
+}  // namespace mbr

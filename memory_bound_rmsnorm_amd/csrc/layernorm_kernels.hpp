@@ -1,0 +1,281 @@
+// LayerNorm kernels for gfx950 (CDNA4, wave64), the sibling of the RMSNorm
+// path:
+//
+//   y_j = gamma_j * (x_j - mu) * rsqrt(var + eps) + beta_j,
+//   mu = sum_j x_j / H,  var = sum_j (x_j - mu)^2 / H
+//
+// (xserv "phase 4: transformer core kernels", csrc/normalization/layernorm.cu
+// header comment and docs/04-transformer-kernels.md "LayerNorm"; biased
+// variance as in the pages' CPU reference).  The pages' kernel takes the
+// variance as E[x^2] - mu^2 from one pass of sums, which cancels when |mu| is
+// large against the spread.  Here the row stays in registers and the moments
+// come from the corrected two-pass scheme (Chan, Golub and LeVeque, "Algorithms
+// for computing the sample variance", 1983): a first reduction gives the fp32
+// mean m0; a second one, from the same registers, sums both (x - m0) and
+// (x - m0)^2, so that c = sum(x - m0)/H corrects m0's rounding error and
+// var = sum(x - m0)^2/H - c^2 (c^2 is tiny).  The output uses (x - m0) - c.
+// The error then scales with the spread of the row, not with |mu|.  The
+// gamma / beta loads are issued between the two reductions so that they are in
+// flight during the second one.  fp32 throughout, one rounding at write-back.
+//
+// Same lane -> wave (DPP + permlane) -> workgroup (one LDS slot per wave,
+// fixed order) reduction as the RMSNorm kernels: bitwise identical totals in
+// every lane, reproducible run to run.  HBM-bound; no contraction.
+#pragma once
+
+#include "rmsnorm_kernels.hpp"
+
+namespace mbr {
+
+struct LnArgs {
+    const void* x;
+    const void* g;  // gamma
+    const void* b;  // beta, or nullptr (no bias)
+    void* out;
+    int64_t rows;
+    int32_t units;  // per row: 16-byte vectors (vector path) or elements
+    float hidden_f;
+    float eps;
+};
+
+// Workgroup totals of N per-lane values: wave sums, one LDS slot per wave
+// and value, one barrier, fixed-order sums of the slots.  The first call of a
+// row uses slot set 0 and the second set 1; a set is written again only after
+// the other set's barrier, so single buffers suffice.
+template <int NWAVES, int N>
+__device__ __forceinline__ void block_sums(float (&v)[N], float (&slots)[N][16], int wave, int nwaves_rt = NWAVES) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) v[k] = wave_sum(v[k]);
+    if (NWAVES == 1 || nwaves_rt == 1) return;
+    if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+        for (int k = 0; k < N; ++k) slots[k][wave] = v[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        float t = 0.f;
+        if constexpr (NWAVES > 0) {
+#pragma unroll
+            for (int i = 0; i < NWAVES; ++i) t += slots[k][i];
+        } else {
+            for (int i = 0; i < nwaves_rt; ++i) t += slots[k][i];
+        }
+        v[k] = t;
+    }
+}
+
+// Moments of a row from the two reductions: the corrected shift c and inv.
+struct LnMoments {
+    float m0;   // first-pass mean
+    float c;    // sum(x - m0) / H
+    float inv;  // rsqrt(var + eps)
+};
+
+__device__ __forceinline__ LnMoments ln_moments(float m0, const float (&tq)[2], const LnArgs& a) {
+    const float c = tq[0] / a.hidden_f;
+    const float var = fmaxf(tq[1] / a.hidden_f - c * c, 0.f);
+    return {m0, c, rsqrtf(var + a.eps)};
+}
+
+// Vector path: WPR waves per row, one row per workgroup at a time, lane l
+// owning 16-byte vectors l, l + 64*WPR, ... (VPL of them).  MASKED: the row
+// has fewer than 64*WPR*VPL vectors; loads are clamped in bounds, the extra
+// values excluded from both sums, stores skipped.
+template <class E, int WPR, int VPL, bool MASKED>
+__global__ void __launch_bounds__(max_threads<WPR>()) ln_vec_kernel(const LnArgs a) {
+    constexpr int LANES = 64 * WPR;
+    constexpr int V = E::kVec;
+    const int wave = wave_id();
+    const int lane = static_cast<int>(threadIdx.x);
+    const int nvec = a.units;
+    const bool bias = a.b != nullptr;
+    __shared__ float s1[1][16], s2[2][16];
+
+    auto vidx = [&](int k) {
+        const int v = k * LANES + lane;
+        return MASKED ? (v < nvec ? v : nvec - 1) : v;
+    };
+    auto in_row = [&](int k) { return !MASKED || k * LANES + lane < nvec; };
+
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+        const u32x4* xr = static_cast<const u32x4*>(a.x) + row * nvec;
+        u32x4 d[VPL];
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) d[k] = load_stream(xr + vidx(k));
+        float s[1] = {0.f};
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            float f[V];
+            widen(d[k], f, E{});
+            float t = 0.f;
+#pragma unroll
+            for (int i = 0; i < V; ++i) t += f[i];
+            s[0] += in_row(k) ? t : 0.f;
+        }
+        block_sums<WPR>(s, s1, wave);
+        const float m0 = s[0] / a.hidden_f;
+        u32x4 gv[VPL], bv[VPL];
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            gv[k] = load_keep(static_cast<const u32x4*>(a.g) + vidx(k));
+            if (bias) bv[k] = load_keep(static_cast<const u32x4*>(a.b) + vidx(k));
+        }
+        float tq[2] = {0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            float f[V];
+            widen(d[k], f, E{});
+            float t = 0.f, q = 0.f;
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                const float e = f[i] - m0;
+                t += e;
+                q += e * e;
+            }
+            tq[0] += in_row(k) ? t : 0.f;
+            tq[1] += in_row(k) ? q : 0.f;
+        }
+        block_sums<WPR>(tq, s2, wave);
+        const LnMoments m = ln_moments(m0, tq, a);
+        u32x4* outr = static_cast<u32x4*>(a.out) + row * nvec;
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            if (!in_row(k)) continue;
+            float f[V], fg[V], fb[V];
+            widen(d[k], f, E{});
+            widen(gv[k], fg, E{});
+            if (bias) {
+                widen(bv[k], fb, E{});
+            } else {
+#pragma unroll
+                for (int i = 0; i < V; ++i) fb[i] = 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < V; ++i) f[i] = fg[i] * (((f[i] - m.m0) - m.c) * m.inv) + fb[i];
+            store_stream(outr + k * LANES + lane, narrow(f, E{}));
+        }
+    }
+}
+
+// Element path: any hidden, any element alignment; lane l owns elements
+// l, l + 64*WPR, ... (EPL of them).
+template <class E, int WPR, int EPL>
+__global__ void __launch_bounds__(max_threads<WPR>()) ln_elem_kernel(const LnArgs a) {
+    using S = typename E::scalar;
+    constexpr int LANES = 64 * WPR;
+    const int wave = wave_id();
+    const int lane = static_cast<int>(threadIdx.x);
+    const int H = a.units;
+    const bool bias = a.b != nullptr;
+    __shared__ float s1[1][16], s2[2][16];
+    auto jdx = [&](int k) {
+        const int j = k * LANES + lane;
+        return j < H ? j : H - 1;
+    };
+    auto in_row = [&](int k) { return k * LANES + lane < H; };
+
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+        const S* xr = static_cast<const S*>(a.x) + row * H;
+        float f[EPL];
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) f[k] = widen1(xr[jdx(k)]);
+        float s[1] = {0.f};
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) s[0] += in_row(k) ? f[k] : 0.f;
+        block_sums<WPR>(s, s1, wave);
+        const float m0 = s[0] / a.hidden_f;
+        float fg[EPL], fb[EPL];
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) {
+            fg[k] = widen1(static_cast<const S*>(a.g)[jdx(k)]);
+            fb[k] = bias ? widen1(static_cast<const S*>(a.b)[jdx(k)]) : 0.f;
+        }
+        float tq[2] = {0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) {
+            const float e = f[k] - m0;
+            tq[0] += in_row(k) ? e : 0.f;
+            tq[1] += in_row(k) ? e * e : 0.f;
+        }
+        block_sums<WPR>(tq, s2, wave);
+        const LnMoments m = ln_moments(m0, tq, a);
+        S* outr = static_cast<S*>(a.out) + row * H;
+#pragma unroll
+        for (int k = 0; k < EPL; ++k)
+            if (in_row(k)) outr[k * LANES + lane] = narrow1(fg[k] * (((f[k] - m.m0) - m.c) * m.inv) + fb[k], E{});
+    }
+}
+
+// Rows too wide for registers: blockDim.x lanes stride over the row three
+// times (sum; centred squares; output), one row per workgroup iteration.  The
+// first two passes write nothing, so exact aliasing of out with x stays safe.
+template <class E, bool VEC>
+__global__ void __launch_bounds__(1024) ln_multipass_kernel(const LnArgs a) {
+    using S = typename E::scalar;
+    constexpr int V = E::kVec;
+    const int wave = wave_id();
+    const int nwaves = static_cast<int>(blockDim.x) >> 6;
+    const int n = a.units;
+    const bool bias = a.b != nullptr;
+    __shared__ float s1[1][16], s2[2][16];
+
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+        const int64_t base = row * n;
+        float s[1] = {0.f};
+        for (int j = threadIdx.x; j < n; j += blockDim.x) {
+            if constexpr (VEC) {
+                float f[V];
+                widen(load_stream(static_cast<const u32x4*>(a.x) + base + j), f, E{});
+#pragma unroll
+                for (int i = 0; i < V; ++i) s[0] += f[i];
+            } else {
+                s[0] += widen1(static_cast<const S*>(a.x)[base + j]);
+            }
+        }
+        block_sums<0>(s, s1, wave, nwaves);
+        const float m0 = s[0] / a.hidden_f;
+        float tq[2] = {0.f, 0.f};
+        for (int j = threadIdx.x; j < n; j += blockDim.x) {
+            if constexpr (VEC) {
+                float f[V];
+                widen(load_stream(static_cast<const u32x4*>(a.x) + base + j), f, E{});
+#pragma unroll
+                for (int i = 0; i < V; ++i) {
+                    const float e = f[i] - m0;
+                    tq[0] += e;
+                    tq[1] += e * e;
+                }
+            } else {
+                const float e = widen1(static_cast<const S*>(a.x)[base + j]) - m0;
+                tq[0] += e;
+                tq[1] += e * e;
+            }
+        }
+        block_sums<0>(tq, s2, wave, nwaves);
+        const LnMoments m = ln_moments(m0, tq, a);
+        for (int j = threadIdx.x; j < n; j += blockDim.x) {
+            if constexpr (VEC) {
+                float f[V], fg[V], fb[V];
+                widen(load_stream(static_cast<const u32x4*>(a.x) + base + j), f, E{});
+                widen(load_keep(static_cast<const u32x4*>(a.g) + j), fg, E{});
+                if (bias) {
+                    widen(load_keep(static_cast<const u32x4*>(a.b) + j), fb, E{});
+                } else {
+#pragma unroll
+                    for (int i = 0; i < V; ++i) fb[i] = 0.f;
+                }
+#pragma unroll
+                for (int i = 0; i < V; ++i) f[i] = fg[i] * (((f[i] - m.m0) - m.c) * m.inv) + fb[i];
+                store_stream(static_cast<u32x4*>(a.out) + base + j, narrow(f, E{}));
+            } else {
+                const float f = widen1(static_cast<const S*>(a.x)[base + j]);
+                const float fg = widen1(static_cast<const S*>(a.g)[j]);
+                const float fb = bias ? widen1(static_cast<const S*>(a.b)[j]) : 0.f;
+                static_cast<S*>(a.out)[base + j] = narrow1(fg * (((f - m.m0) - m.c) * m.inv) + fb, E{});
+            }
+        }
+    }
+}
+
+}  // namespace mbr

@@ -12,6 +12,7 @@
 #include <stdint.h>
 
 #include "../../include/rmsnorm.h"
+#include "layernorm_kernels.hpp"
 #include "rmsnorm_bwd_kernels.hpp"
 #include "rmsnorm_dispatch.hpp"
 #include "rmsnorm_kernels.hpp"
@@ -431,6 +432,129 @@ rmsnorm_status_t run_bwd(const BwdProblem& p, const rmsnorm_config_t* user, void
     return s;
 }
 
+// ---------------------------------------------------------------- LayerNorm
+
+struct LnProblem {
+    const void* x;
+    const void* g;
+    const void* b;  // nullptr: no bias
+    void* out;
+    int64_t rows;
+    int64_t hidden;
+    float eps;
+    int dtype;
+};
+
+bool ln_vector_aligned(const LnProblem& p) {
+    if ((p.hidden * elem_size(p.dtype)) % kVectorBytes != 0) return false;
+    const void* ptrs[] = {p.x, p.g, p.b, p.out};
+    for (const void* q : ptrs)
+        if (q && reinterpret_cast<uintptr_t>(q) % kVectorBytes != 0) return false;
+    return true;
+}
+
+// Each LayerNorm row needs two workgroup reductions, so rows take as few
+// waves as registers allow: up to eight 16-byte vectors (or elements) per lane,
+// more waves per row only when rows are few; one row per workgroup, uncapped
+// grid.  Sweeps on MI355X, bf16 [8192, 4096]: 1 wave x 8 vectors 25.9 us,
+// 2 x 4 26.1, 4 x 2 28.3, 8 x 1 31.8.  Rows beyond every built register
+// configuration take the multi-pass path.
+rmsnorm_config_t choose_ln(int64_t rows, int64_t hidden, int dtype, bool aligned) {
+    rmsnorm_config_t c = {RMSNORM_PATH_TWO_PASS, 16, 0, 1, 0};
+    const bool vec = aligned && hidden % vec_elems(dtype) == 0;
+    const int64_t units = vec ? hidden / vec_elems(dtype) : hidden;
+    const int* list = vec ? mbr::kLnVplList : mbr::kLnEplList;
+    const int nlist = vec ? mbr::kNumLnVpl : mbr::kNumLnEpl;
+    const int cap = 8;
+    auto fit = [&](int wpr) {
+        const int per = round_up_in(list, nlist, ceil_div(units, int64_t(64) * wpr));
+        if (per < 0) return -1;
+        return (!vec || mbr::ln_vec_built(wpr, per)) ? per : -1;
+    };
+    int wpr = 1;
+    while (wpr < 16 && ceil_div(units, int64_t(64) * wpr) > cap) wpr *= 2;
+    while (wpr < 16 && rows < 4096 / wpr && units >= int64_t(64) * wpr * 2) wpr *= 2;
+    int per = fit(wpr);
+    while (per < 0 && wpr < 16) {
+        wpr *= 2;
+        per = fit(wpr);
+    }
+    if (per < 0) return c;
+    c.path = vec ? RMSNORM_PATH_VECTOR : RMSNORM_PATH_ELEMENT;
+    c.waves_per_row = wpr;
+    c.items_per_lane = per;
+    return c;
+}
+
+rmsnorm_status_t validate_ln_pointers(const LnProblem& p) {
+    const int es = elem_size(p.dtype);
+    if (!p.x || !p.g || !p.out) return RMSNORM_ERR_INVALID_ARG;
+    const void* ptrs[] = {p.x, p.g, p.b, p.out};
+    for (const void* q : ptrs)
+        if (q && reinterpret_cast<uintptr_t>(q) % es != 0) return RMSNORM_ERR_INVALID_ARG;
+    const int64_t nb = p.rows * p.hidden * es;
+    const int64_t wb = p.hidden * es;
+    if (!output_vs_input_ok(p.out, p.x, nb)) return RMSNORM_ERR_INVALID_ARG;
+    if (ranges_overlap(p.out, nb, p.g, wb)) return RMSNORM_ERR_INVALID_ARG;
+    if (p.b && ranges_overlap(p.out, nb, p.b, wb)) return RMSNORM_ERR_INVALID_ARG;
+    return RMSNORM_OK;
+}
+
+rmsnorm_status_t run_ln(const LnProblem& p, const rmsnorm_config_t* user, void* stream) {
+    rmsnorm_status_t s = validate_sizes(p.rows, p.hidden, p.eps, p.dtype);
+    if (s != RMSNORM_OK) return s;
+    if (p.rows == 0) return RMSNORM_OK;
+    s = validate_ln_pointers(p);
+    if (s != RMSNORM_OK) return s;
+    const bool aligned = ln_vector_aligned(p);
+    const rmsnorm_config_t c =
+        (user && user->path != RMSNORM_PATH_AUTO) ? *user : choose_ln(p.rows, p.hidden, p.dtype, aligned);
+    const int wi = index_of(mbr::kWprList, mbr::kNumWpr, c.waves_per_row);
+    if (wi < 0 || c.rows_per_block != 1 || c.max_blocks < 0) return RMSNORM_ERR_INVALID_ARG;
+    const int64_t lanes = int64_t(64) * c.waves_per_row;
+    mbr::LnArgs a;
+    a.x = p.x;
+    a.g = p.g;
+    a.b = p.b;
+    a.out = p.out;
+    a.rows = p.rows;
+    a.hidden_f = static_cast<float>(p.hidden);
+    a.eps = p.eps;
+    const void* fn = nullptr;
+    switch (c.path) {
+        case RMSNORM_PATH_VECTOR: {
+            if (!aligned || p.hidden % vec_elems(p.dtype) != 0) return RMSNORM_ERR_INVALID_ARG;
+            const int vi = index_of(mbr::kLnVplList, mbr::kNumLnVpl, c.items_per_lane);
+            const int64_t nvec = p.hidden / vec_elems(p.dtype);
+            if (vi < 0 || lanes * c.items_per_lane < nvec) return RMSNORM_ERR_INVALID_ARG;
+            if (lanes > mbr::max_threads_for(c.waves_per_row)) return RMSNORM_ERR_INVALID_ARG;
+            fn = mbr::ln_vec_kernel_ptr(p.dtype, lanes * c.items_per_lane != nvec, wi, vi);
+            a.units = static_cast<int32_t>(nvec);
+            break;
+        }
+        case RMSNORM_PATH_ELEMENT: {
+            const int ei = index_of(mbr::kLnEplList, mbr::kNumLnEpl, c.items_per_lane);
+            if (ei < 0 || lanes * c.items_per_lane < p.hidden) return RMSNORM_ERR_INVALID_ARG;
+            if (lanes > mbr::max_threads_for(c.waves_per_row)) return RMSNORM_ERR_INVALID_ARG;
+            fn = mbr::ln_elem_kernel_ptr(p.dtype, wi, ei);
+            a.units = static_cast<int32_t>(p.hidden);
+            break;
+        }
+        case RMSNORM_PATH_TWO_PASS: {
+            const bool vec = aligned && p.hidden % vec_elems(p.dtype) == 0;
+            fn = mbr::ln_multipass_kernel_ptr(p.dtype, vec);
+            a.units = static_cast<int32_t>(vec ? p.hidden / vec_elems(p.dtype) : p.hidden);
+            break;
+        }
+        default:
+            return RMSNORM_ERR_INVALID_ARG;
+    }
+    if (!fn) return RMSNORM_ERR_INVALID_ARG;
+    int64_t grid = p.rows < kMaxGrid ? p.rows : kMaxGrid;
+    if (c.max_blocks > 0 && grid > c.max_blocks) grid = c.max_blocks;
+    return launch_checked(fn, grid, lanes, &a, static_cast<hipStream_t>(stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -547,6 +671,28 @@ RMSNORM_API rmsnorm_status_t rmsnorm_select_bwd_config(int64_t rows, int64_t hid
     const rmsnorm_status_t s = validate_sizes(rows, hidden, 0.0f, static_cast<int>(dtype));
     if (s != RMSNORM_OK) return s;
     *cfg = choose_bwd(rows, hidden, static_cast<int>(dtype), vector_aligned_flag != 0);
+    return RMSNORM_OK;
+}
+
+RMSNORM_API rmsnorm_status_t layernorm_fwd_ex(const void* x, const void* gamma, const void* beta, void* out,
+                                              int64_t rows, int64_t hidden, float eps, rmsnorm_dtype_t dtype,
+                                              const rmsnorm_config_t* cfg, void* stream) {
+    const LnProblem p = {x, gamma, beta, out, rows, hidden, eps, static_cast<int>(dtype)};
+    return run_ln(p, cfg, stream);
+}
+
+RMSNORM_API rmsnorm_status_t layernorm_fwd(const void* x, const void* gamma, const void* beta, void* out,
+                                           int64_t rows, int64_t hidden, float eps, rmsnorm_dtype_t dtype,
+                                           void* stream) {
+    return layernorm_fwd_ex(x, gamma, beta, out, rows, hidden, eps, dtype, nullptr, stream);
+}
+
+RMSNORM_API rmsnorm_status_t layernorm_select_config(int64_t rows, int64_t hidden, rmsnorm_dtype_t dtype,
+                                                     int32_t vector_aligned_flag, rmsnorm_config_t* cfg) {
+    if (!cfg) return RMSNORM_ERR_INVALID_ARG;
+    const rmsnorm_status_t s = validate_sizes(rows, hidden, 0.0f, static_cast<int>(dtype));
+    if (s != RMSNORM_OK) return s;
+    *cfg = choose_ln(rows, hidden, static_cast<int>(dtype), vector_aligned_flag != 0);
     return RMSNORM_OK;
 }
 

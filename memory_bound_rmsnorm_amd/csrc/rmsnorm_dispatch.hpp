@@ -58,6 +58,20 @@ const void* bwd_elem_kernel(int dtype, bool dw, int wpr_index, int epl_index);
 const void* bwd_twopass_kernel(int dtype, bool dw, bool vec);
 const void* bwd_dw_kernel(int dtype);
 
+// LayerNorm: the row and the per-vector gamma / beta live in registers; up to
+// 8 vectors per lane (4 in a 1024-lane workgroup, whose lanes have 128 VGPRs)
+// are built spill-free, elements up to 8 per lane; wider rows take the
+// multi-pass path.
+constexpr int kLnVplList[] = {1, 2, 3, 4, 5, 6, 7, 8};
+constexpr bool ln_vec_built(int wpr, int vpl) { return wpr < 16 || vpl <= 4; }
+constexpr int kLnEplList[] = {1, 2, 4, 8};
+constexpr int kNumLnVpl = sizeof(kLnVplList) / sizeof(int);
+constexpr int kNumLnEpl = sizeof(kLnEplList) / sizeof(int);
+
+const void* ln_vec_kernel_ptr(int dtype, bool masked, int wpr_index, int vpl_index);
+const void* ln_elem_kernel_ptr(int dtype, int wpr_index, int epl_index);
+const void* ln_multipass_kernel_ptr(int dtype, bool vec);
+
 // Per-unit getters defined in the instantiation files.
 const void* vec_kernel_bf16(bool fused, bool masked, int wi, int vi);
 const void* vec_kernel_f32(bool fused, bool masked, int wi, int vi);

@@ -6,7 +6,8 @@ CPU oracle can take their inputs from here without sharing any of the method.
 
 Recipe (one ``numpy.random.default_rng(seed)`` stream per workload):
   * draw order is x, then residual (fused workloads only) or the upstream
-    gradient dy (backward workloads only), then weight;
+    gradient dy (backward workloads only), then weight (gamma), then beta
+    (LayerNorm workloads only);
   * ``N(mu, sigma)`` means ``standard_normal(float32) * sigma + mu``
     (sigma is a standard deviation), ``U(a, b)`` means ``uniform(a, b)``
     cast to float32;
@@ -53,7 +54,12 @@ class Workload:
     outlier_scale: float = 1.0
     quant: Optional[str] = None  # None: normalised output; "int8" / "fp8": codes + per-row scale
     grad: Optional[Dist] = None  # backward workloads: distribution of the upstream gradient dy
+    beta: Optional[Dist] = None  # LayerNorm workloads: distribution of beta (weight is gamma)
     note: str = field(default="", compare=False)
+
+    @property
+    def layernorm(self) -> bool:
+        return self.beta is not None
 
     @property
     def backward(self) -> bool:
@@ -65,8 +71,11 @@ class Workload:
 
     @property
     def read_bytes(self) -> int:
-        # forward: x (and residual) plus weight; backward: x and dy plus weight
-        return ((2 if self.fused or self.backward else 1) * self.rows * self.hidden + self.hidden) * self.elem_size
+        # forward: x (and residual) plus weight; backward: x and dy plus weight;
+        # LayerNorm: x plus gamma and beta
+        params = 2 if self.layernorm else 1
+        return ((2 if self.fused or self.backward else 1) * self.rows * self.hidden
+                + params * self.hidden) * self.elem_size
 
     @property
     def write_bytes(self) -> int:
@@ -139,7 +148,21 @@ for _base in ("bf16_16384x8192", "bf16_prefill_4096x2048", "fp32_64x2048"):
     BWD_WORKLOADS[_name] = Workload(_name, _w.dtype, _w.rows, _w.hidden, _w.eps, False, _w.x, _w.weight,
                                     outlier_columns=_w.outlier_columns, outlier_scale=_w.outlier_scale,
                                     grad=N01, note=_w.note + "; backward")
-ALL_WORKLOADS: Dict[str, Workload] = dict(WORKLOADS, **QUANT_WORKLOADS, **BWD_WORKLOADS)
+# LayerNorm: the pages' worked ledger example ([8192, 4096], fp16 there; bf16
+# moves the same bytes), their exercise shape [4096, 4096], and a small fp32
+# case at GPT-2's hidden size 768.
+LN_WORKLOADS: Dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("bf16_ln_8192x4096", "bf16", 8192, 4096, 1e-5, False, N01, W_N, beta=Dist("normal", 0.0, 0.1),
+                 note="LayerNorm, the pages' ledger example shape"),
+        Workload("bf16_ln_4096x4096", "bf16", 4096, 4096, 1e-5, False, N01, W_N, beta=Dist("normal", 0.0, 0.1),
+                 note="LayerNorm, the pages' exercise shape"),
+        Workload("fp32_ln_64x768", "f32", 64, 768, 1e-5, False, N01, W_N, beta=Dist("normal", 0.0, 0.1),
+                 note="LayerNorm, small fp32 case at hidden 768"),
+    ]
+}
+ALL_WORKLOADS: Dict[str, Workload] = dict(WORKLOADS, **QUANT_WORKLOADS, **BWD_WORKLOADS, **LN_WORKLOADS)
 
 
 def _draw(rng: np.random.Generator, d: Dist, shape) -> np.ndarray:
@@ -176,16 +199,20 @@ def make(w: Workload, seed: int = 0, rows: Optional[int] = None) -> Dict[str, to
     if w.backward:
         out["dy"] = _store(_draw(rng, w.grad, (r, w.hidden)), w.dtype)
     out["weight"] = _store(_draw(rng, w.weight, (w.hidden,)), w.dtype)
+    if w.layernorm:
+        out["beta"] = _store(_draw(rng, w.beta, (w.hidden,)), w.dtype)
     return out
 
 
 def custom(rows: int, hidden: int, dtype: str, fused: bool = False, eps: float = 1e-5,
            x: Dist = N01, weight: Dist = W_N, residual: Dist = N01, backward: bool = False,
-           grad: Dist = N01) -> Workload:
+           grad: Dist = N01, layernorm: bool = False, beta: Dist = Dist("normal", 0.0, 0.1)) -> Workload:
     """An ad-hoc workload (ragged widths, odd row counts, ...) with the same recipe."""
-    return Workload("custom_%s_%dx%d%s%s" % (dtype, rows, hidden, "_res" if fused else "", "_bwd" if backward else ""),
+    return Workload("custom_%s_%dx%d%s%s%s" % (dtype, rows, hidden, "_res" if fused else "", "_bwd" if backward else "",
+                                               "_ln" if layernorm else ""),
                     dtype, rows, hidden, eps, fused, x, weight,
-                    residual if fused else None, grad=grad if backward else None)
+                    residual if fused else None, grad=grad if backward else None,
+                    beta=beta if layernorm else None)
 
 
 def bits(t: torch.Tensor) -> np.ndarray:

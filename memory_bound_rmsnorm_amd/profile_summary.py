@@ -24,6 +24,7 @@ from memory_bound_rmsnorm_amd import _build, inputs
 RMS_KERNEL_TAGS = ("rms_vec_kernel", "rms_elem_kernel", "rms_twopass_kernel")
 BWD_KERNEL_TAGS = ("rms_bwd_vec_kernel", "rms_bwd_elem_kernel", "rms_bwd_twopass_kernel")
 BWD_DW_TAG = "rms_bwd_dw_kernel"
+LN_KERNEL_TAGS = ("ln_vec_kernel", "ln_elem_kernel", "ln_multipass_kernel")
 COPY_KERNEL_TAG = "hbm_copy_kernel"
 
 
@@ -36,19 +37,25 @@ def _step_kernels(w):
     the forward kernel, or the backward row kernel plus the dweight reduction."""
     if w.backward:
         return [lambda k: any(t in k for t in BWD_KERNEL_TAGS), lambda k: BWD_DW_TAG in k]
+    if w.layernorm:
+        return [lambda k: any(t in k for t in LN_KERNEL_TAGS)]
     return [_is_rms]
 
 
 def _family(w):
-    return "bwd" if w.backward else "fwd"
+    return "bwd" if w.backward else "ln" if w.layernorm else "fwd"
+
+
+def _title(w):
+    return "%s %s [%d, %d]%s" % ("LayerNorm" if w.layernorm else "RMSNorm", w.dtype, w.rows, w.hidden,
+                                 " fused residual" if w.fused else " backward" if w.backward else "")
 
 
 def stats(args):
     w = inputs.ALL_WORKLOADS[args.workload]
     with open(args.csv) as f:
         rows = list(csv.DictReader(f))
-    out = ["# rocprofv3 --kernel-trace --stats summary: RMSNorm %s [%d, %d]%s"
-           % (w.dtype, w.rows, w.hidden, " fused residual" if w.fused else " backward" if w.backward else ""),
+    out = ["# rocprofv3 --kernel-trace --stats summary: %s" % _title(w),
            "# command: %s" % args.command,
            "# algorithmic bytes per call: %d" % w.algorithmic_bytes,
            "%-90s %6s %12s %12s %12s" % ("kernel", "calls", "avg_us", "min_us", "max_us")]
@@ -116,8 +123,7 @@ def pmc(args):
     read_alg = w.read_bytes
     write_alg = w.write_bytes
     traffic = rfetch * 1024 * fscale + rwrite * 1024 * wscale
-    out = ["# rocprofv3 --pmc summary: HBM traffic of RMSNorm %s [%d, %d]%s"
-           % (w.dtype, w.rows, w.hidden, " fused residual" if w.fused else " backward" if w.backward else ""),
+    out = ["# rocprofv3 --pmc summary: HBM traffic of %s" % _title(w),
            "# fetch command: %s" % args.command_fetch,
            "# write command: %s" % args.command_write,
            "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch, averaged over dispatches; the copy kernel",
@@ -150,6 +156,8 @@ def launch_config(w):
     dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
     if w.backward:
         return mbr.rmsnorm_select_bwd_config(w.rows, w.hidden, dt, True)
+    if w.layernorm:
+        return mbr.layernorm_select_config(w.rows, w.hidden, dt, True)
     select = mbr.rmsnorm_select_quant_config if w.quant else mbr.rmsnorm_select_config
     return select(w.rows, w.hidden, dt, True, w.fused)
 
@@ -177,6 +185,8 @@ def resources(args):
         if w.backward:
             fam = {1: "rms_bwd_vec_kernel", 2: "rms_bwd_elem_kernel", 3: "rms_bwd_twopass_kernel"}[cfg.path]
             mangled = "%sINS_%d%sELi%dELi%dELb%dELb1EEEv" % (fam, len(e), e, cfg.waves_per_row, per, int(masked))
+        elif w.layernorm:
+            mangled = "ln_vec_kernelINS_%d%sELi%dELi%dELb%dEEEv" % (len(e), e, cfg.waves_per_row, per, int(masked))
         else:
             fam = {1: "rms_vec_kernel", 2: "rms_elem_kernel", 3: "rms_twopass_kernel"}[cfg.path]
             qt = {None: 0, "int8": 1, "fp8": 2}[w.quant]

@@ -266,6 +266,30 @@ def _bwd_magnitudes(x, w, dy, eps, rows_chunk=2048):
     return M, A
 
 
+def check_magnitude(got, want, mag, gamma, bf16: bool, what: str, stats: dict):
+    """|got - want| <= gamma * mag + one unit in the last place, elementwise;
+    non-finite values must match exactly."""
+    gv, wv = _values(got), _values(want)
+    gn, wn = ~np.isfinite(gv), ~np.isfinite(wv)
+    assert np.array_equal(gn, wn), "%s: non-finite positions differ" % what
+    assert np.array_equal(np.isnan(gv), np.isnan(wv)), "%s: NaN positions differ" % what
+    inf = np.isinf(wv)
+    assert np.array_equal(gv[inf], wv[inf]), "%s: infinities differ" % what
+    ok = ~wn
+    g = gv[ok]
+    o = wv[ok]
+    tol = gamma * mag[ok] + np.maximum(_ulp(o, bf16), _ulp(g, bf16))
+    err = np.abs(g - o)
+    ratio = err / tol if err.size else np.zeros(1)
+    if err.size and not np.all(err <= tol):
+        i = int(np.argmax(ratio))
+        flat = np.flatnonzero(ok)[i]
+        raise AssertionError("%s mismatch at flat index %d: got %r want %r (|err| %.3e > tol %.3e)"
+                             % (what, flat, g[i], o[i], err[i], tol[i]))
+    stats[what] = {"n": int(ok.sum()), "max_err_over_tol": float(ratio.max()) if err.size else 0.0,
+                   "frac_bitwise_equal": float(np.mean(got[ok] == want[ok])) if err.size else 1.0}
+
+
 def compare_bwd(dx_gpu, dw_gpu, dx_want, dw_want, x, w, dy, eps, cfg, n_part) -> dict:
     """dx (and dw unless dw_want is None) against the oracle with the bounds above."""
     bf16 = x.dtype == np.uint16
@@ -273,33 +297,11 @@ def compare_bwd(dx_gpu, dw_gpu, dx_want, dw_want, x, w, dy, eps, cfg, n_part) ->
     L = bwd_chain(cfg, hidden, bf16)
     M, A = _bwd_magnitudes(x, w, dy, eps)
     stats = {"chain": L}
-
-    def check(got, want, mag, gamma, what):
-        gv, wv = _values(got), _values(want)
-        gn, wn = ~np.isfinite(gv), ~np.isfinite(wv)
-        assert np.array_equal(gn, wn), "%s: non-finite positions differ" % what
-        assert np.array_equal(np.isnan(gv), np.isnan(wv)), "%s: NaN positions differ" % what
-        inf = np.isinf(wv)
-        assert np.array_equal(gv[inf], wv[inf]), "%s: infinities differ" % what
-        ok = ~wn
-        g = _values(got)[ok]
-        o = _values(want)[ok]
-        tol = gamma * mag[ok] + np.maximum(_ulp(o, bf16), _ulp(g, bf16))
-        err = np.abs(g - o)
-        ratio = err / tol if err.size else np.zeros(1)
-        if err.size and not np.all(err <= tol):
-            i = int(np.argmax(ratio))
-            flat = np.flatnonzero(ok)[i]
-            raise AssertionError("%s mismatch at flat index %d: got %r want %r (|err| %.3e > tol %.3e)"
-                                 % (what, flat, g[i], o[i], err[i], tol[i]))
-        stats[what] = {"n": int(ok.sum()), "max_err_over_tol": float(ratio.max()) if err.size else 0.0,
-                       "frac_bitwise_equal": float(np.mean(got[ok] == want[ok])) if err.size else 1.0}
-
-    check(dx_gpu, dx_want, M, (2 * L + 16) * U, "dx")
+    check_magnitude(dx_gpu, dx_want, M, (2 * L + 16) * U, bf16, "dx", stats)
     if dw_want is not None:
         g = max(1, n_part)
         gamma_w = 2 * (-(-rows // g) + -(-g // 64) + L / 2 + 12) * U
-        check(dw_gpu, dw_want, A, gamma_w, "dw")
+        check_magnitude(dw_gpu, dw_want, A, gamma_w, bf16, "dw", stats)
     return stats
 
 
@@ -314,3 +316,50 @@ def oracle_bwd(x: np.ndarray, w: np.ndarray, dy: np.ndarray, eps: float, want_dw
         list(ex.map(job, _chunks(x.shape[0], 4 * threads())))
         dw = fut.result() if fut is not None else None
     return dx, dw
+
+
+# ---------------------------------------------------------------- LayerNorm
+#
+# y = gamma*(x - mu)*inv + beta on the GPU in fp32 with the same reduction as
+# the RMSNorm kernels (chain length L as in bwd_chain), moments by the
+# corrected two-pass scheme: m0 = fp32 mean, then c = sum(x - m0)/H and
+# q = sum(x - m0)^2/H from the same values, output from (x - m0) - c.  The
+# correction leaves a mean error below about L*u*sum|x - mu|/H (m0's own error
+# cancels to first order), the differences add u*|x - mu|, inv's relative
+# error is below (L/2 + 4)*u, and the affine step adds two roundings; so
+# |y_gpu - y| <= (2L + 16)*u * M with M = |gamma|*inv*(|x - mu| + sum|x - mu|/H)
+# + |beta|, plus one unit in the last place for the final rounding on either
+# side.  gamma*(x - mu)*inv and beta can cancel, hence the bound on M; it does
+# not grow with |mu|.
+
+
+def _ln_magnitudes(x, g, b, eps, rows_chunk=2048):
+    rows, hidden = x.shape
+    M = np.empty((rows, hidden))
+    gd = np.abs(_values(g))
+    bd = np.abs(_values(b)) if b is not None else np.zeros(hidden)
+    for a in range(0, rows, rows_chunk):
+        xd = _values(x[a:a + rows_chunk])
+        mu = xd.mean(axis=1, keepdims=True)
+        var = ((xd - mu) ** 2).mean(axis=1, keepdims=True)
+        inv = 1.0 / np.sqrt(var + float(np.float32(eps)))
+        sabs = np.abs(xd - mu).mean(axis=1, keepdims=True)
+        M[a:a + rows_chunk] = gd[None, :] * inv * (np.abs(xd - mu) + sabs) + bd[None, :]
+    return M
+
+
+def compare_ln(y_gpu, y_want, x, g, b, eps, cfg) -> dict:
+    bf16 = x.dtype == np.uint16
+    L = bwd_chain(cfg, x.shape[1], bf16)
+    stats = {"chain": L}
+    check_magnitude(y_gpu, y_want, _ln_magnitudes(x, g, b, eps), (2 * L + 16) * U, bf16, "y", stats)
+    return stats
+
+
+def oracle_ln(x, g, b, eps):
+    out = np.empty_like(x)
+    with concurrent.futures.ThreadPoolExecutor(threads()) as ex:
+        def job(r):
+            out[r[0]:r[1]] = oracle.layernorm_fwd(x[r[0]:r[1]], g, b, eps)
+        list(ex.map(job, _chunks(x.shape[0], 4 * threads())))
+    return out

@@ -1,0 +1,66 @@
+"""C-ABI checks of the LayerNorm entry points that need no GPU."""
+import pytest
+import torch
+
+import memory_bound_rmsnorm_amd as mbr
+from tests.test_abi_cpu import HEADERS, _declared, fake_only
+
+INV = mbr.RMSNORM_ERR_INVALID_ARG
+
+
+def test_layernorm_declared():
+    names = {n for h in HEADERS for n in _declared(h)}
+    for n in ("layernorm_fwd", "layernorm_fwd_ex", "layernorm_select_config"):
+        assert n in names
+
+
+def test_rows_zero_needs_no_pointers():
+    assert mbr.lib().layernorm_fwd(None, None, None, None, 0, 64, 1e-5, 1, None) == mbr.RMSNORM_OK
+
+
+@pytest.mark.parametrize("rows,hidden,eps,dtype,want", [
+    (-1, 16, 1e-5, 1, INV), (4, 0, 1e-5, 1, INV), (4, 2 ** 31, 1e-5, 1, INV), (4, 16, -1.0, 1, INV),
+    (4, 16, float("nan"), 0, INV), (4, 16, 1e-5, 5, mbr.RMSNORM_ERR_UNSUPPORTED_DTYPE), (2 ** 62, 16, 1e-5, 1, INV),
+])
+def test_bad_sizes_rejected(rows, hidden, eps, dtype, want):
+    assert mbr.lib().layernorm_fwd(None, None, None, None, rows, hidden, eps, dtype, None) == want
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("aligned", [True, False])
+@pytest.mark.parametrize("rows", [1, 100, 100000])
+def test_choice_is_built_and_covering(dtype, aligned, rows):
+    v = 8 if dtype == torch.bfloat16 else 4
+    for hidden in [1, 7, 8, 64, 100, 768, 1000, 2048, 4095, 4096, 5120, 8192, 16384, 32768, 32776, 65536, 131080]:
+        c = mbr.layernorm_select_config(rows, hidden, dtype, aligned)
+        lanes = 64 * c.waves_per_row
+        assert c.rows_per_block == 1 and c.max_blocks == 0 and c.waves_per_row in (1, 2, 4, 8, 16)
+        if c.path == mbr.PATH_VECTOR:
+            assert aligned and hidden % v == 0 and lanes * c.items_per_lane >= hidden // v
+            assert c.items_per_lane in range(1, 9) and (c.waves_per_row < 16 or c.items_per_lane <= 4)
+        elif c.path == mbr.PATH_ELEMENT:
+            assert c.items_per_lane in (1, 2, 4, 8) and lanes * c.items_per_lane >= hidden
+        else:
+            assert c.path == mbr.PATH_TWO_PASS and hidden > 8 * 1024
+
+
+def test_stated_choices():
+    c = mbr.layernorm_select_config(8192, 4096, torch.bfloat16, True)
+    assert (c.path, c.waves_per_row, c.items_per_lane) == (mbr.PATH_VECTOR, 1, 8)
+    c = mbr.layernorm_select_config(64, 768, torch.float32, True)
+    assert (c.path, c.waves_per_row, c.items_per_lane) == (mbr.PATH_VECTOR, 2, 2)  # few rows: spread
+
+
+@fake_only
+def test_pointer_validation_and_forced_configs():
+    L = mbr.lib()
+    X, G, B, O = (0x7F0000000000 + i * 0x10000000 for i in range(4))
+    for args in [(None, G, B, O), (X, None, B, O), (X, G, B, None), (X + 1, G, B, O), (X, G, B + 1, O),
+                 (X, G, B, X + 2), (X, G, B, G), (X, G, B, B - 16)]:
+        assert L.layernorm_fwd(*args, 4, 256, 1e-5, 1, None) == INV, args
+    for cfg in [mbr.Config(mbr.PATH_VECTOR, 3, 2, 1, 0), mbr.Config(mbr.PATH_VECTOR, 4, 2, 2, 0),
+                mbr.Config(mbr.PATH_VECTOR, 16, 5, 1, 0), mbr.Config(mbr.PATH_VECTOR, 1, 2, 1, 0),
+                mbr.Config(mbr.PATH_ELEMENT, 4, 3, 1, 0), mbr.Config(mbr.PATH_VECTOR, 4, 2, 1, -1),
+                mbr.Config(9, 4, 2, 1, 0)]:
+        import ctypes
+        assert L.layernorm_fwd_ex(X, G, B, O, 4, 4096, 1e-5, 1, ctypes.byref(cfg), None) == INV, cfg

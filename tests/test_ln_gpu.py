@@ -1,0 +1,205 @@
+"""Parity of the HIP LayerNorm (through the C ABI) with the CPU oracle.
+
+Outputs are compared element by element with the bound derived in
+tests/parity.py (fp32 evaluation error scaled by the magnitude of the terms,
+plus one unit in the last place).  Covered: the stated LayerNorm workloads at
+full size in the automatic launch configuration (the one bench.py times),
+every built vector / element / multi-pass configuration with partial last
+vectors or lanes, ragged widths, rows with a large common offset (where
+E[x^2] - mean^2 would cancel), no-bias calls, in-place output, misaligned
+buffers, degenerate rows, determinism, streams, graph replays and the pages'
+own LayerNorm test case.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import memory_bound_rmsnorm_amd as mbr
+from memory_bound_rmsnorm_amd import inputs
+from tests import parity
+from tests.test_oracle_pins import _read_golden
+
+pytestmark = pytest.mark.gpu
+
+BF16, F32 = torch.bfloat16, torch.float32
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def tdt(dtype):
+    return BF16 if dtype == "bf16" else F32
+
+
+def run_ln(x, g, b, eps, cfg=None, out=None):
+    out = torch.empty_like(x) if out is None else out
+    mbr.layernorm_fwd_ex(x, g, b, out, eps, cfg)
+    torch.cuda.synchronize()
+    return out
+
+
+def check(w, t, cfg=None, eps=None, bias=True):
+    eps = w.eps if eps is None else eps
+    dev = {k: v.cuda() for k, v in t.items()}
+    y = run_ln(dev["x"], dev["weight"], dev["beta"] if bias else None, eps, cfg)
+    xb, gb = inputs.bits(t["x"]), inputs.bits(t["weight"])
+    bb = inputs.bits(t["beta"]) if bias else None
+    c = cfg if cfg is not None else mbr.layernorm_select_config(w.rows, w.hidden, tdt(w.dtype), True)
+    return parity.compare_ln(inputs.bits(y.cpu()), parity.oracle_ln(xb, gb, bb, eps), xb, gb, bb, eps, c)
+
+
+@pytest.mark.parametrize("name", list(inputs.LN_WORKLOADS))
+def test_ln_workloads_full_size(name):
+    w = inputs.LN_WORKLOADS[name]
+    say("ln workload", name, mbr.layernorm_select_config(w.rows, w.hidden, tdt(w.dtype), True))
+    say(name, check(w, inputs.make(w, seed=0)))
+
+
+RAGGED = [(1, 1), (3, 3), (5, 7), (2, 8), (5, 9), (67, 127), (12, 769), (5, 2048), (3, 4095), (7, 5120),
+          (5, 5121), (3, 8193), (9, 16384), (2, 20000), (3, 65536), (2, 81920), (2, 131080)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,hidden", RAGGED)
+def test_ln_ragged_shapes(rows, hidden, dtype):
+    w = inputs.custom(rows, hidden, dtype, layernorm=True)
+    say("ln shape", rows, hidden, dtype, mbr.layernorm_select_config(rows, hidden, tdt(dtype), True))
+    check(w, inputs.make(w, seed=rows * 3 + hidden), bias=(hidden % 2 == 0))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ln_every_vector_config(dtype):
+    vecw = 8 if dtype == "bf16" else 4
+    n = 0
+    for wpr in (1, 2, 4, 8, 16):
+        for vpl in range(1, 9):
+            if wpr == 16 and vpl > 4:
+                continue
+            lanes = 64 * wpr
+            for nvec in sorted({lanes * vpl, max(1, lanes * vpl - 37), lanes * (vpl - 1) + 1}):
+                cfg = mbr.Config(mbr.PATH_VECTOR, wpr, vpl, 1, 2 if n % 3 == 0 else 0)
+                w = inputs.custom(5, nvec * vecw, dtype, layernorm=True)
+                say("ln vector", dtype, cfg, "hidden", nvec * vecw)
+                check(w, inputs.make(w, seed=n), cfg, bias=(n % 2 == 0))
+                n += 1
+    assert n > 100
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ln_every_element_and_multipass_config(dtype):
+    n = 0
+    for wpr in (1, 2, 4, 8, 16):
+        lanes = 64 * wpr
+        for epl in (1, 2, 4, 8):
+            for hidden in sorted({lanes * epl, max(1, lanes * epl - 5), lanes * (epl - 1) + 1 if epl > 1 else 3}):
+                cfg = mbr.Config(mbr.PATH_ELEMENT, wpr, epl, 1, 2 if n % 2 else 0)
+                w = inputs.custom(5, hidden, dtype, layernorm=True)
+                say("ln element", dtype, cfg, "hidden", hidden)
+                check(w, inputs.make(w, seed=n), cfg, bias=(n % 3 != 0))
+                n += 1
+        for hidden in (4096, 4099, 12288 + 8):
+            cfg = mbr.Config(mbr.PATH_TWO_PASS, wpr, 0, 1, 2)
+            w = inputs.custom(5, hidden, dtype, layernorm=True)
+            say("ln multipass", dtype, cfg, "hidden", hidden)
+            check(w, inputs.make(w, seed=wpr + hidden), cfg)
+
+
+@pytest.mark.parametrize("dtype,offset", [("f32", 1000.0), ("f32", -3.0e4), ("bf16", 100.0)])
+def test_ln_large_common_offset(dtype, offset):
+    """Rows far from zero mean: the centred variance keeps full accuracy (a
+    variance from E[x^2] - mean^2 in fp32 would lose it entirely here)."""
+    for hidden in (4096, 5121, 81920):
+        w = inputs.custom(6, hidden, dtype, layernorm=True, x=inputs.Dist("normal", offset, 1.0))
+        st = check(w, inputs.make(w, seed=hidden))
+        say("ln offset", dtype, offset, hidden, st)
+
+
+def test_ln_in_place_and_degenerate_rows():
+    w = inputs.custom(40, 4096, "bf16", layernorm=True)
+    t = {k: v.cuda() for k, v in inputs.make(w, seed=8).items()}
+    y = run_ln(t["x"], t["weight"], t["beta"], 1e-5)
+    x2 = t["x"].clone()
+    assert torch.equal(run_ln(x2, t["weight"], t["beta"], 1e-5, out=x2), y)
+    # constant rows and hidden = 1 give beta exactly
+    const = torch.full((3, 4096), 2.5, dtype=BF16, device="cuda")
+    assert torch.equal(run_ln(const, t["weight"], t["beta"], 1e-5), t["beta"].expand(3, 4096))
+    one = torch.randn(5, 1, device="cuda").to(BF16)
+    assert torch.equal(run_ln(one, t["weight"][:1], t["beta"][:1], 1e-5), t["beta"][:1].expand(5, 1))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ln_misaligned_pointers(dtype):
+    rows, hidden, eps = 33, 2048, 1e-5
+    td = tdt(dtype)
+    es = 2 if dtype == "bf16" else 4
+    w = inputs.custom(rows, hidden, dtype, layernorm=True)
+    t = inputs.make(w, seed=11)
+    xbuf = torch.zeros(rows * hidden + 8, dtype=td, device="cuda")
+    obuf = torch.zeros(rows * hidden + 8, dtype=td, device="cuda")
+    gbuf = torch.zeros(hidden + 8, dtype=td, device="cuda")
+    bbuf = torch.zeros(hidden + 8, dtype=td, device="cuda")
+    xbuf[1:1 + rows * hidden] = t["x"].reshape(-1).cuda()
+    gbuf[1:1 + hidden] = t["weight"].cuda()
+    bbuf[1:1 + hidden] = t["beta"].cuda()
+    st = mbr.lib().layernorm_fwd(xbuf.data_ptr() + es, gbuf.data_ptr() + es, bbuf.data_ptr() + es,
+                                 obuf.data_ptr() + es, rows, hidden, eps, mbr.dtype_code(td),
+                                 torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == mbr.RMSNORM_OK
+    y = inputs.bits(obuf[1:1 + rows * hidden].reshape(rows, hidden).cpu())
+    xb, gb, bb = inputs.bits(t["x"]), inputs.bits(t["weight"]), inputs.bits(t["beta"])
+    cfg = mbr.layernorm_select_config(rows, hidden, td, False)
+    assert cfg.path == mbr.PATH_ELEMENT
+    parity.compare_ln(y, parity.oracle_ln(xb, gb, bb, eps), xb, gb, bb, eps, cfg)
+    assert obuf[0].item() == 0 and torch.count_nonzero(obuf[1 + rows * hidden:]) == 0
+
+
+def test_ln_overlap_rejected_on_device_buffers():
+    x = torch.randn(8, 256, device="cuda")
+    g, b = torch.ones(256, device="cuda"), torch.zeros(256, device="cuda")
+    L, s = mbr.lib(), torch.cuda.current_stream().cuda_stream
+    INV = mbr.RMSNORM_ERR_INVALID_ARG
+    assert L.layernorm_fwd(x.data_ptr(), g.data_ptr(), b.data_ptr(), x.data_ptr() + 4, 8, 256, 1e-5, 0, s) == INV
+    assert L.layernorm_fwd(x.data_ptr(), g.data_ptr(), b.data_ptr(), g.data_ptr(), 1, 256, 1e-5, 0, s) == INV
+    assert L.layernorm_fwd(x.data_ptr(), g.data_ptr(), b.data_ptr(), b.data_ptr(), 1, 256, 1e-5, 0, s) == INV
+
+
+def test_ln_deterministic_streams_and_graph_replays():
+    w = inputs.LN_WORKLOADS["bf16_ln_8192x4096"]
+    t = {k: v.cuda() for k, v in inputs.make(w, seed=0).items()}
+    y = run_ln(t["x"], t["weight"], t["beta"], w.eps)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        y2 = torch.empty_like(y)
+        mbr.layernorm_fwd(t["x"], t["weight"], t["beta"], y2, w.eps, stream=st)
+    st.synchronize()
+    assert torch.equal(y, y2)
+    yg = torch.empty_like(y)
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        mbr.layernorm_fwd(t["x"], t["weight"], t["beta"], yg, w.eps)
+    for rep in range(3):
+        yg.zero_()
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(yg, y), rep
+        run_ln(t["x"], t["weight"], None, w.eps)
+
+
+def test_pages_layernorm_test_case_on_gpu():
+    gd = _read_golden("xserv_layernorm_test.txt")
+    rows, hidden, eps = int(gd["rows"]), int(gd["hidden"]), float(gd["eps"])
+    i = np.arange(rows * hidden)
+    x = (((i % 17).astype(np.float32) - np.float32(8.0)) * np.float32(0.1)).reshape(rows, hidden)
+    j = np.arange(hidden)
+    g = (np.float32(0.8) + (j % 5).astype(np.float32) * np.float32(0.1)).astype(np.float32)
+    b = (((j % 7).astype(np.float32) - np.float32(3.0)) * np.float32(0.01)).astype(np.float32)
+    y = run_ln(torch.from_numpy(x).cuda(), torch.from_numpy(g).cuda(), torch.from_numpy(b).cuda(), eps).cpu().numpy()
+    want = oracle_y = parity.oracle_ln(x, g, b, eps)
+    parity.compare_ln(y, oracle_y, x, g, b, eps, mbr.layernorm_select_config(rows, hidden, F32, True))
+    assert float(np.max(np.abs(y - want))) <= float(gd["f32_atol"])
