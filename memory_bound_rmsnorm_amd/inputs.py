@@ -223,3 +223,131 @@ def bits(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
     raise TypeError("unsupported dtype %s" % t.dtype)
+
+
+# ---------------------------------------------------------------- KV RMSNorm + RoPE + cache scatter
+#
+# kv rows [tokens, heads, norm_dim + rope_dim] drawn like x above; gamma like
+# the weight; cos / sin tables [max_pos, rope_dim / 2] from the xserv rope
+# cache formula (phase 4, csrc/embedding/rope.cu: angle = pos * theta^(-2i /
+# rope_dim)), evaluated in float64 and stored as float32; a paged cache of
+# num_blocks blocks of block_size rows, each sequence owning a random set of
+# blocks listed in its block table (the block_table / cache_seqlens interface
+# of the paged MLA decode kernel the TileLang tutorial ch. 02, section 1.2,
+# points to); every token's slot is block_table[seq][pos // block_size] *
+# block_size + pos % block_size.  The caches start filled with seeded values,
+# so that rows a call must not touch can be checked.  The 512 + 64 split is the
+# latent + rotary width of the MLA KV cache in that kernel's DeepSeek model
+# family; the pages do not print it.
+
+
+@dataclass(frozen=True)
+class KvWorkload:
+    name: str
+    dtype: str
+    seqs: int
+    new_tokens: int        # tokens per sequence written by one call
+    max_len: int           # cache length per sequence (decode: lengths drawn up to this)
+    heads: int
+    norm_dim: int
+    rope_dim: int
+    eps: float
+    rope_style: int        # 1: adjacent pairs (xserv), 0: two halves
+    decode: bool           # True: one new token per sequence at a random length
+    block_size: int = 64
+    theta: float = 10000.0
+    note: str = field(default="", compare=False)
+
+    @property
+    def elem_size(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def tokens(self) -> int:
+        return self.seqs * self.new_tokens
+
+    @property
+    def blocks_per_seq(self) -> int:
+        return -(-self.max_len // self.block_size)
+
+    @property
+    def num_blocks(self) -> int:
+        return 2 * self.seqs * self.blocks_per_seq  # half of the blocks stay free
+
+    @property
+    def num_slots(self) -> int:
+        return self.num_blocks * self.block_size
+
+    @property
+    def max_pos(self) -> int:
+        return self.max_len
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """kv, the token's two table rows, its position and slot read; both cache
+        rows written; gamma once."""
+        d = self.norm_dim + self.rope_dim
+        per_token = (2 * self.heads * d * self.elem_size + self.rope_dim * 4 + 4 + 8)
+        return self.tokens * per_token + self.norm_dim * self.elem_size
+
+
+KV_WORKLOADS: Dict[str, KvWorkload] = {
+    w.name: w
+    for w in [
+        KvWorkload("bf16_kv_prefill_4x4096_576", "bf16", 4, 4096, 4096, 1, 512, 64, 1e-6, 1, False,
+                   note="prefill: 4 sequences x 4096 new tokens, MLA-style 512 + 64 split"),
+        KvWorkload("bf16_kv_decode_256_576", "bf16", 256, 1, 4096, 1, 512, 64, 1e-6, 1, True,
+                   note="decode: 256 sequences, one new token each at a random length"),
+    ]
+}
+
+
+def rope_tables(max_pos: int, rope_dim: int, theta: float = 10000.0):
+    """cos / sin tables [max_pos, rope_dim / 2], float32."""
+    i = np.arange(rope_dim // 2, dtype=np.float64)
+    freq = theta ** (-2.0 * i / rope_dim)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * freq[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def make_kv(w: KvWorkload, seed: int = 0) -> Dict[str, torch.Tensor]:
+    """CPU tensors for one call: kv, gamma, cos, sin, positions (int32), slots
+    (int64), block_table (int32) and cache_seqlens (int32).  The caches come
+    from kv_caches()."""
+    rng = np.random.default_rng(seed)
+    d = w.norm_dim + w.rope_dim
+    kv = _draw(rng, N01, (w.tokens, w.heads * d))
+    gamma = _draw(rng, W_N, (w.norm_dim,))
+    perm = rng.permutation(w.num_blocks)
+    table = perm[: w.seqs * w.blocks_per_seq].reshape(w.seqs, w.blocks_per_seq).astype(np.int32)
+    if w.decode:
+        lens = rng.integers(1, w.max_len + 1, size=w.seqs).astype(np.int32)
+        pos = (lens - 1).astype(np.int64)[:, None]
+    else:
+        lens = np.full(w.seqs, w.new_tokens, dtype=np.int32)
+        pos = np.tile(np.arange(w.new_tokens, dtype=np.int64), (w.seqs, 1))
+    seq = np.repeat(np.arange(w.seqs), w.new_tokens).reshape(w.seqs, w.new_tokens)
+    slots = table[seq, pos // w.block_size].astype(np.int64) * w.block_size + pos % w.block_size
+    cos_t, sin_t = rope_tables(w.max_pos, w.rope_dim, w.theta)
+    return {
+        "kv": _store(kv, w.dtype).reshape(w.tokens, w.heads, d),
+        "gamma": _store(gamma, w.dtype),
+        "cos": torch.from_numpy(cos_t), "sin": torch.from_numpy(sin_t),
+        "positions": torch.from_numpy(pos.reshape(-1).astype(np.int32)),
+        "slots": torch.from_numpy(slots.reshape(-1)),
+        "block_table": torch.from_numpy(table), "cache_seqlens": torch.from_numpy(lens),
+    }
+
+
+def cache_pattern(rows: int, heads: int, dim: int, dtype: str, device="cpu", salt: int = 0) -> torch.Tensor:
+    """Initial cache contents [rows, heads, dim]: a fixed pattern of small
+    multiples of 1/64 (exact in bf16), so that untouched rows can be checked."""
+    i = torch.arange(rows * heads * dim, device=device, dtype=torch.int64)
+    v = (((i * 7 + salt) % 251) - 125).to(torch.float32) / 64.0
+    return v.to(torch.float32 if dtype == "f32" else torch.bfloat16).reshape(rows, heads, dim)
+
+
+def kv_caches(w: KvWorkload, device="cpu"):
+    """(norm_cache, rope_cache) with their initial pattern."""
+    return (cache_pattern(w.num_slots, w.heads, w.norm_dim, w.dtype, device, 1),
+            cache_pattern(w.num_slots, w.heads, w.rope_dim, w.dtype, device, 2))

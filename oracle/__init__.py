@@ -15,7 +15,8 @@ bit-exact special cases and an exact-rational brute force --
 ``tests/test_oracle_quant_pins.py`` (dynamic quantisation) and
 ``tests/test_oracle_bwd_pins.py`` (backward: 80-digit central differences of
 the forward, closed forms, invariants) and ``tests/test_oracle_ln_pins.py``
-(LayerNorm: torch's float64 layer_norm, closed forms, exact invariances).
+(LayerNorm: torch's float64 layer_norm, closed forms, exact invariances) and
+``tests/test_oracle_kv_pins.py`` (KV RMSNorm + RoPE + cache scatter).
 The only unpinned choice is which bf16 neighbour is returned when the exact
 result lies within the fp64 evaluation error (about 1e-12 relative) of a
 rounding midpoint.
@@ -56,6 +57,9 @@ def _load():
         lib.oracle_rmsnorm_bwd.restype = i32
         lib.oracle_layernorm_fwd.argtypes = [vp, vp, vp, vp, i64, i64, f32, i32]
         lib.oracle_layernorm_fwd.restype = i32
+        lib.oracle_kv_rmsnorm_rope_cache.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                                     f32, i32, i32]
+        lib.oracle_kv_rmsnorm_rope_cache.restype = i32
         _lib = lib
     return _lib
 
@@ -182,6 +186,50 @@ def layernorm_fwd(x: np.ndarray, gamma: np.ndarray, beta, eps: float) -> np.ndar
     if rc != 0:
         raise RuntimeError("oracle_layernorm_fwd failed")
     return out
+
+
+ROPE_HALVES = 0
+ROPE_PAIRS = 1
+
+
+def kv_rmsnorm_rope_cache(kv: np.ndarray, gamma: np.ndarray, cos_t: np.ndarray, sin_t: np.ndarray,
+                          positions: np.ndarray, slots: np.ndarray, norm_cache: np.ndarray, rope_cache: np.ndarray,
+                          eps: float, rope_style: int) -> None:
+    """Writes RMSNorm(kv[..., :Dn]) * gamma into norm_cache[slot] and the RoPE of
+    kv[..., Dn:] into rope_cache[slot], in place.  kv [tokens, heads, Dn + Dr];
+    caches [num_slots, heads, Dn] and [num_slots, heads, Dr] (same dtype as kv);
+    cos_t / sin_t float32 [max_pos, Dr / 2]; positions int32 [tokens]; slots
+    int64 [tokens]."""
+    if kv.ndim != 3 or norm_cache.ndim != 3 or rope_cache.ndim != 3:
+        raise ValueError("kv and the caches must be 3-D")
+    tokens, heads, d = kv.shape
+    norm_dim, rope_dim = norm_cache.shape[2], rope_cache.shape[2]
+    code = _dtype_code(kv)
+    if norm_dim + rope_dim != d or norm_cache.shape[1] != heads or rope_cache.shape[1] != heads:
+        raise ValueError("cache shapes do not match kv")
+    if norm_cache.shape[0] != rope_cache.shape[0]:
+        raise ValueError("the two caches must have the same number of slots")
+    for a in (kv, norm_cache, rope_cache):
+        if a.dtype != kv.dtype or not a.flags.c_contiguous:
+            raise ValueError("kv and the caches must be contiguous with one dtype")
+    gamma = np.ascontiguousarray(gamma).reshape(-1)
+    if gamma.dtype != kv.dtype or gamma.shape[0] != norm_dim:
+        raise ValueError("gamma must be [norm_dim] with the dtype of kv")
+    cos_t = np.ascontiguousarray(cos_t, dtype=np.float32)
+    sin_t = np.ascontiguousarray(sin_t, dtype=np.float32)
+    if cos_t.shape != sin_t.shape or cos_t.ndim != 2 or cos_t.shape[1] != rope_dim // 2:
+        raise ValueError("tables must be [max_pos, rope_dim / 2]")
+    positions = np.ascontiguousarray(positions, dtype=np.int32)
+    slots = np.ascontiguousarray(slots, dtype=np.int64)
+    if positions.shape != (tokens,) or slots.shape != (tokens,):
+        raise ValueError("positions and slots must have one entry per token")
+    kv = np.ascontiguousarray(kv)
+    rc = _load().oracle_kv_rmsnorm_rope_cache(
+        kv.ctypes.data, gamma.ctypes.data, cos_t.ctypes.data, sin_t.ctypes.data, positions.ctypes.data,
+        slots.ctypes.data, norm_cache.ctypes.data, rope_cache.ctypes.data, tokens, heads, norm_dim, rope_dim,
+        cos_t.shape[0], norm_cache.shape[0], float(eps), int(rope_style), code)
+    if rc != 0:
+        raise RuntimeError("oracle_kv_rmsnorm_rope_cache failed")
 
 
 def round_e4m3(v: float) -> int:

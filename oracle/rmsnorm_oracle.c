@@ -352,3 +352,60 @@ int oracle_layernorm_fwd(const void *x, const void *gamma, const void *beta, voi
     }
     return 0;
 }
+
+/*
+ * KV RMSNorm + RoPE + cache scatter: the fused KV-cache maintenance operator
+ * the TileLang tutorial ch. 02 (sections 1.2 and 4.2) cites from CANN
+ * (aclnnKvRmsNormRopeCache): the tail axis of kv is split, the left part goes
+ * through RMSNorm, the right part through RoPE, and the two results are
+ * scattered into two caches.  Readings (the pages give no more):
+ *   kv [tokens, heads, norm_dim + rope_dim]; left part norm_dim wide, right
+ *   part rope_dim wide (even);
+ *   left: y = x * rsqrt(mean(x^2) + eps) * gamma, gamma [norm_dim];
+ *   right: RoPE as the xserv rope.cu kernel (phase 4): each pair (a, b) at
+ *   position p becomes (a*cos - b*sin, a*sin + b*cos) with cos/sin read from
+ *   fp32 tables [max_pos, rope_dim/2] at row p; pairs are adjacent elements
+ *   (2i, 2i+1) when rope_style is 1 (xserv) or the two halves (i, i + rope/2)
+ *   when it is 0 (the split-head form of the gollamago README, "RoPE");
+ *   scatter: token t writes both results at cache row slots[t] (caches
+ *   [num_slots, heads, norm_dim] and [num_slots, heads, rope_dim]); a token
+ *   whose slot or position is out of range (negative included) writes nothing.
+ * fp64 arithmetic, one rounding per output element.
+ */
+int oracle_kv_rmsnorm_rope_cache(const void *kv, const void *gamma, const float *cos_t, const float *sin_t,
+                                 const int32_t *positions, const int64_t *slots, void *norm_cache,
+                                 void *rope_cache, int64_t tokens, int64_t heads, int64_t norm_dim,
+                                 int64_t rope_dim, int64_t max_pos, int64_t num_slots, float eps, int rope_style,
+                                 int dtype) {
+    int64_t t, h, j, d = norm_dim + rope_dim, half = rope_dim / 2;
+    if (tokens < 0 || heads <= 0 || norm_dim <= 0 || rope_dim < 0 || rope_dim % 2 != 0 || max_pos < 0 ||
+        num_slots < 0 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16) || (rope_style != 0 && rope_style != 1))
+        return -1;
+    for (t = 0; t < tokens; ++t) {
+        const int64_t slot = slots[t];
+        const int64_t pos = positions[t];
+        if (slot < 0 || slot >= num_slots || pos < 0 || pos >= max_pos) continue;
+        for (h = 0; h < heads; ++h) {
+            const int64_t in = (t * heads + h) * d;
+            double s = 0.0, r;
+            for (j = 0; j < norm_dim; ++j) {
+                double v = load_elem(kv, in + j, dtype);
+                s += v * v;
+            }
+            r = 1.0 / sqrt(s / (double)norm_dim + (double)eps);
+            for (j = 0; j < norm_dim; ++j)
+                store_elem(norm_cache, (slot * heads + h) * norm_dim + j,
+                           load_elem(kv, in + j, dtype) * r * load_elem(gamma, j, dtype), dtype);
+            for (j = 0; j < half; ++j) {
+                const int64_t ia = rope_style ? 2 * j : j, ib = rope_style ? 2 * j + 1 : j + half;
+                const double a = load_elem(kv, in + norm_dim + ia, dtype);
+                const double b = load_elem(kv, in + norm_dim + ib, dtype);
+                const double c = (double)cos_t[pos * half + j], sn = (double)sin_t[pos * half + j];
+                const int64_t out = (slot * heads + h) * rope_dim;
+                store_elem(rope_cache, out + ia, a * c - b * sn, dtype);
+                store_elem(rope_cache, out + ib, a * sn + b * c, dtype);
+            }
+        }
+    }
+    return 0;
+}

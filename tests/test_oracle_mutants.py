@@ -17,6 +17,7 @@ from tests import test_oracle_pins as pins
 from tests import test_oracle_quant_pins as qpins
 from tests import test_oracle_bwd_pins as bpins
 from tests import test_oracle_ln_pins as lpins
+from tests import test_oracle_kv_pins as kpins
 
 MUTANTS = [
     ("eps dropped", "sqrt(mean + (double)eps)", "sqrt(mean)"),
@@ -94,6 +95,25 @@ MUTANTS += [
      "for (j = 0; j < hidden; ++j) s += load_elem(x, j * rows + i, dtype);"),
 ]
 
+MUTANTS += [
+    ("kv rotation sign", "store_elem(rope_cache, out + ia, a * c - b * sn, dtype);",
+     "store_elem(rope_cache, out + ia, a * c + b * sn, dtype);"),
+    ("kv cos and sin swapped", "const double c = (double)cos_t[pos * half + j], sn = (double)sin_t[pos * half + j];",
+     "const double c = (double)sin_t[pos * half + j], sn = (double)cos_t[pos * half + j];"),
+    ("kv halves paired as adjacent elements",
+     "const int64_t ia = rope_style ? 2 * j : j, ib = rope_style ? 2 * j + 1 : j + half;",
+     "const int64_t ia = 2 * j, ib = 2 * j + 1;"),
+    ("kv table row off by one", "const double c = (double)cos_t[pos * half + j], sn = (double)sin_t[pos * half + j];",
+     "const int64_t p1 = pos + 1 < max_pos ? pos + 1 : pos;\n"
+     "                const double c = (double)cos_t[p1 * half + j], sn = (double)sin_t[p1 * half + j];"),
+    ("kv slot ignored", "store_elem(norm_cache, (slot * heads + h) * norm_dim + j,",
+     "store_elem(norm_cache, (t * heads + h) * norm_dim + j,"),
+    ("kv eps dropped", "r = 1.0 / sqrt(s / (double)norm_dim + (double)eps);", "r = 1.0 / sqrt(s / (double)norm_dim);"),
+    ("kv gamma dropped", "load_elem(kv, in + j, dtype) * r * load_elem(gamma, j, dtype), dtype);",
+     "load_elem(kv, in + j, dtype) * r, dtype);"),
+    ("kv every head read from head 0", "const int64_t in = (t * heads + h) * d;", "const int64_t in = t * heads * d;"),
+]
+
 HELPER = """
 static float oracle_bf16_back(uint16_t b) { uint32_t u = (uint32_t)b << 16; float f; memcpy(&f, &u, 4); return f; }
 """
@@ -141,6 +161,14 @@ PIN_TESTS = [
     (lpins.test_standardised_moments, {}),
     (lpins.test_rows_independent_and_layout, {}),
     (lpins.test_pages_layernorm_test_case, {}),
+    (kpins.test_norm_part_is_the_rmsnorm_oracle, dict(dtype="f32", style=1)),
+    (kpins.test_rope_part_is_a_complex_multiplication, dict(dtype="f32", style=0)),
+    (kpins.test_rope_part_is_a_complex_multiplication, dict(dtype="bf16", style=1)),
+    (kpins.test_position_zero_is_the_identity, dict(style=1)),
+    (kpins.test_quarter_turn_moves_exactly_one_pair, dict(style=0)),
+    (kpins.test_quarter_turn_moves_exactly_one_pair, dict(style=1)),
+    (kpins.test_rotation_preserves_pair_lengths, {}),
+    (kpins.test_scatter_rows_and_skips, dict(dtype="bf16")),
 ]
 
 
