@@ -7,7 +7,8 @@ root, scale and store.  Default workload: bf16 [16384, 8192], the
 large-hidden configuration the headline bandwidth figure is quoted on.  The
 quantised workloads time rmsnorm_dynamic_quant_fwd, the backward ones
 rmsnorm_bwd (dx and dweight: the row kernel plus the dweight reduction), the
-LayerNorm ones layernorm_fwd.
+LayerNorm ones layernorm_fwd, the KV ones kv_rmsnorm_rope_cache (one call
+writes every token's two cache rows; whole input-and-cache sets rotate).
 
 Byte accounting follows the TileLang tutorial ch. 02, section 2.1: every input
 read once, every output written once, the weight once; the figure reported is
@@ -37,7 +38,7 @@ import torch
 
 import memory_bound_rmsnorm_amd as mbr
 from memory_bound_rmsnorm_amd import _build, inputs
-from memory_bound_rmsnorm_amd.profile_summary import launch_config
+from memory_bound_rmsnorm_amd.profile_summary import kv_launch, launch_dict
 
 HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 MIN_FOOTPRINT = 2 << 30
@@ -53,7 +54,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=inputs.HEADLINE, choices=sorted(inputs.ALL_WORKLOADS))
+    ap.add_argument("--workload", default=inputs.HEADLINE, choices=sorted(inputs.EVERY_WORKLOAD))
     ap.add_argument("--all", action="store_true", help="also time every other workload (stderr)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline budget; 0 disables it")
     ap.add_argument("--no-copy", action="store_true", help="skip the copy-ceiling measurement")
@@ -132,8 +133,34 @@ class Sets:
             mbr.rmsnorm_fwd(s["x"], self.weight, s["out"], self.eps)
 
 
+class KvSets:
+    """Rotating device copies of a KV workload's kv input and both caches."""
+
+    def __init__(self, w, t, n_sets):
+        dev = {k: v.cuda() for k, v in t.items()}
+        self.w = w
+        self.gamma, self.cos, self.sin = dev["gamma"], dev["cos"], dev["sin"]
+        self.positions, self.slots = dev["positions"], dev["slots"]
+        self.sets = []
+        for i in range(n_sets):
+            nc, rc = inputs.kv_caches(w, "cuda")
+            self.sets.append({"kv": dev["kv"] if i == 0 else dev["kv"].clone(), "nc": nc, "rc": rc})
+
+    def launch(self, i):
+        s = self.sets[i % len(self.sets)]
+        mbr.kv_rmsnorm_rope_cache(s["kv"], self.gamma, self.cos, self.sin, self.positions, self.slots, s["nc"],
+                                  s["rc"], self.w.eps, self.w.rope_style)
+
+
+def is_kv(w) -> bool:
+    return isinstance(w, inputs.KvWorkload)
+
+
 def n_sets_for(w) -> int:
-    per_set = w.algorithmic_bytes - w.hidden * w.elem_size
+    if is_kv(w):
+        per_set = w.tokens * w.heads * (w.norm_dim + w.rope_dim) * w.elem_size + w.cache_bytes
+    else:
+        per_set = w.algorithmic_bytes - w.hidden * w.elem_size
     return max(2, -(-MIN_FOOTPRINT // per_set))
 
 
@@ -197,7 +224,10 @@ LN_KERNEL_FAMILY = {"vector": "ln_vec_kernel", "element": "ln_elem_kernel", "two
 def load_traffic(w, launch):
     """HBM bytes per step from the committed counter summary, if it was taken
     on the current kernel sources in the current launch configuration; else None."""
-    fam = (BWD_KERNEL_FAMILY if w.backward else LN_KERNEL_FAMILY if w.layernorm else KERNEL_FAMILY)[launch["path"]]
+    if is_kv(w):
+        fam = {"vector": "kv_vec_kernel", "element": "kv_elem_kernel"}[launch["path"]]
+    else:
+        fam = (BWD_KERNEL_FAMILY if w.backward else LN_KERNEL_FAMILY if w.layernorm else KERNEL_FAMILY)[launch["path"]]
     path = os.path.join(PROFILE_DIR, "pmc_traffic_%s_%s.txt" % (fam, w.name))
     if not os.path.exists(path):
         return None
@@ -209,7 +239,8 @@ def load_traffic(w, launch):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
     try:
-        if vals.get("source_sha256") != _build.source_digest("bwd" if w.backward else "ln" if w.layernorm else "fwd"):
+        family = "kv" if is_kv(w) else "bwd" if w.backward else "ln" if w.layernorm else "fwd"
+        if vals.get("source_sha256") != _build.source_digest(family):
             return None
         if vals.get("launch_config") != " ".join("%s=%s" % kv for kv in launch.items()):
             return None
@@ -220,9 +251,52 @@ def load_traffic(w, launch):
         return None
 
 
+def cpu_baseline_kv(w, t, seconds):
+    """The oracle over the first tokens of a KV workload, tokens split across
+    the host's threads, each thread writing compact caches of its own."""
+    import numpy as np
+    import oracle  # the CPU checker; timed here as a reported baseline only
+    T = host_threads()
+    tokens = min(w.tokens, 2048)
+    kvb = inputs.bits(t["kv"])[:tokens]
+    gb = inputs.bits(t["gamma"])
+    cos_t, sin_t = t["cos"].numpy(), t["sin"].numpy()
+    pos = t["positions"].numpy()[:tokens]
+    np_dtype = np.uint16 if w.dtype == "bf16" else np.float32
+    per_thread = [(i * tokens // T, (i + 1) * tokens // T) for i in range(T)]
+
+    def one_pass():
+        with concurrent.futures.ThreadPoolExecutor(T) as ex:
+            def job(r):
+                n = r[1] - r[0]
+                if n == 0:
+                    return
+                nc = np.empty((n, w.heads, w.norm_dim), np_dtype)
+                rc = np.empty((n, w.heads, w.rope_dim), np_dtype)
+                oracle.kv_rmsnorm_rope_cache(kvb[r[0]:r[1]], gb, cos_t, sin_t, pos[r[0]:r[1]],
+                                             np.arange(n, dtype=np.int64), nc, rc, w.eps, w.rope_style)
+            list(ex.map(job, per_thread))
+
+    one_pass()
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        one_pass()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    sample_bytes = w.algorithmic_bytes * tokens // w.tokens
+    return {"value": round(sample_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": T, "kind": "oracle",
+            "sample": "first %d of %d tokens, %d passes in %.1f s on %d threads (%s)"
+                      % (tokens, w.tokens, reps, el, T, cpu_model())}
+
+
 def cpu_baseline(w, t, seconds):
     """The oracle, as it stands, over a bounded sample of the workload's rows,
     rows split across the host's threads; GB/s with the same byte ledger."""
+    if is_kv(w):
+        return cpu_baseline_kv(w, t, seconds)
     import oracle  # the CPU checker; timed here as a reported baseline only
     T = host_threads()
     rows = min(w.rows, 512 if w.hidden >= 4096 else 2048)
@@ -269,21 +343,27 @@ def cpu_baseline(w, t, seconds):
 
 
 def bench_workload(w, steps, warmup, seed, with_copy=True, graph=False):
-    t = inputs.make(w, seed=seed)
-    n_sets = n_sets_for(w)
-    sets = Sets(w, t, n_sets)
+    if is_kv(w):
+        t = inputs.make_kv(w, seed=seed)
+        n_sets = n_sets_for(w)
+        sets = KvSets(w, t, n_sets)
+        shape = {"tokens": w.tokens, "heads": w.heads, "norm_dim": w.norm_dim, "rope_dim": w.rope_dim,
+                 "num_slots": w.num_slots}
+    else:
+        t = inputs.make(w, seed=seed)
+        n_sets = n_sets_for(w)
+        sets = Sets(w, t, n_sets)
+        shape = {"rows": w.rows, "hidden": w.hidden, "fused": w.fused, "quant": w.quant, "backward": w.backward}
     wall, ev = time_steps(sets.launch, steps, warmup)
     nbytes = w.algorithmic_bytes
     kern_s = ev / steps
-    cfg = launch_config(w)
-    rec = {
-        "workload": w.name, "rows": w.rows, "hidden": w.hidden, "dtype": w.dtype, "fused": w.fused,
-        "quant": w.quant, "backward": w.backward,
+    rec = dict({"workload": w.name, "dtype": w.dtype}, **shape)
+    rec.update({
         "eps": w.eps, "algorithmic_bytes": nbytes, "rotation_sets": n_sets,
         "wall_s": wall, "event_s": ev, "us_per_call": kern_s * 1e6,
         "gbps_wall": nbytes * steps / wall / 1e9, "gbps_kernel": nbytes / kern_s / 1e9,
-        "kernel_config": cfg.as_dict(),
-    }
+        "kernel_config": launch_dict(w),
+    })
     if graph:
         gs = graph_time(sets.launch, n_sets)
         rec["us_per_call_graph"] = gs * 1e6
@@ -293,6 +373,35 @@ def bench_workload(w, steps, warmup, seed, with_copy=True, graph=False):
         rec["copy_ceiling_gbps"] = cc
         rec["frac_of_copy_ceiling"] = rec["gbps_kernel"] / cc
     return t, rec
+
+
+def describe(w):
+    """(metric, workload description, config fields, parity test) of a workload."""
+    if is_kv(w):
+        desc = "KV RMSNorm + RoPE (%s) + paged cache scatter %s, %d tokens (%s) x %d heads x (%d norm + %d rope), " \
+               "%d cache slots, eps %g" % ("adjacent pairs" if w.rope_style == 1 else "halves", w.dtype, w.tokens,
+                                           "decode" if w.decode else "prefill", w.heads, w.norm_dim, w.rope_dim,
+                                           w.num_slots, w.eps)
+        fields = {"tokens": w.tokens, "heads": w.heads, "norm_dim": w.norm_dim, "rope_dim": w.rope_dim,
+                  "num_slots": w.num_slots, "rope_style": w.rope_style}
+        return ("KV RMSNorm+RoPE+cache achieved HBM GB/s (%s)" % w.name, desc, fields,
+                "tests/test_kv_gpu.py::test_kv_workloads_full_size")
+    if w.name == inputs.HEADLINE:
+        metric = "bf16 RMSNorm achieved HBM GB/s and % of peak at 16384×8192"
+    else:
+        metric = "%s achieved HBM GB/s (%s)" % ("LayerNorm" if w.layernorm else
+                                               "RMSNorm backward" if w.backward else "RMSNorm", w.name)
+    desc = "%s %s%s [%d, %d]%s%s, eps %g" % (
+        "LayerNorm" if w.layernorm else "RMSNorm", "backward (dx, dweight) " if w.backward else "", w.dtype,
+        w.rows, w.hidden, " fused residual" if w.fused else "",
+        " with %s dynamic quantisation" % w.quant if w.quant else "", w.eps)
+    fields = {"rows": w.rows, "hidden": w.hidden, "fused": w.fused, "quant": w.quant, "backward": w.backward,
+              "layernorm": w.layernorm}
+    parity = ("tests/test_bwd_gpu.py::test_bwd_workloads_full_size" if w.backward else
+              "tests/test_ln_gpu.py::test_ln_workloads_full_size" if w.layernorm else
+              "tests/test_quant_gpu.py" if w.quant else
+              "tests/test_parity_gpu.py::test_stated_workloads_full_size")
+    return metric, desc, fields, parity
 
 
 def main():
@@ -307,16 +416,15 @@ def main():
         print("bench.py needs a GPU (HIP device); none is visible", file=sys.stderr)
         sys.exit(1)
     mbr.lib()  # fail loudly if the HIP library is not built
-    w = inputs.ALL_WORKLOADS[args.workload]
+    w = inputs.EVERY_WORKLOAD[args.workload]
     log("# device:", torch.cuda.get_device_name(0), "| workload:", w.name, "| steps", args.steps, "warmup", args.warmup)
     t, rec = bench_workload(w, args.steps, args.warmup, args.seed, not args.no_copy)
     log("# timed:", json.dumps(rec))
 
     achieved = rec["gbps_kernel"]
+    metric, desc, fields, parity = describe(w)
     line = {
-        "metric": "bf16 RMSNorm achieved HBM GB/s and % of peak at 16384×8192" if w.name == inputs.HEADLINE
-                  else "%s achieved HBM GB/s (%s)" % ("LayerNorm" if w.layernorm else
-                                                      "RMSNorm backward" if w.backward else "RMSNorm", w.name),
+        "metric": metric,
         "value": round(rec["gbps_wall"], 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -329,31 +437,20 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded; x ~ N(0,1) with 8 outlier channels x100, weight ~ N(1, 0.1))"
                 if w.name == inputs.HEADLINE else "synthetic (seeded)",
-        "config": {"workload": "%s %s%s [%d, %d]%s%s, eps %g" % (
-                       "LayerNorm" if w.layernorm else "RMSNorm",
-                       "backward (dx, dweight) " if w.backward else "", w.dtype, w.rows, w.hidden,
-                       " fused residual" if w.fused else "",
-                       " with %s dynamic quantisation" % w.quant if w.quant else "", w.eps),
-                   "rows": w.rows, "hidden": w.hidden, "fused": w.fused, "quant": w.quant, "backward": w.backward,
-                   "layernorm": w.layernorm,
-                   "algorithmic_bytes_per_step": w.algorithmic_bytes, "rotation_sets": rec["rotation_sets"],
-                   "launch": rec["kernel_config"]},
+        "config": dict({"workload": desc}, **fields, algorithmic_bytes_per_step=w.algorithmic_bytes,
+                       rotation_sets=rec["rotation_sets"], launch=rec["kernel_config"]),
         "pct_of_peak": round(100 * rec["gbps_wall"] / HBM_PEAK_GBPS, 2),
         "us_per_call": round(rec["us_per_call"], 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": load_traffic(w, rec["kernel_config"])},
-        "parity": "checked against the CPU oracle at this size and launch configuration by "
-                  + ("tests/test_bwd_gpu.py::test_bwd_workloads_full_size" if w.backward else
-                     "tests/test_ln_gpu.py::test_ln_workloads_full_size" if w.layernorm else
-                     "tests/test_quant_gpu.py" if w.quant else
-                     "tests/test_parity_gpu.py::test_stated_workloads_full_size"),
+        "parity": "checked against the CPU oracle at this size and launch configuration by " + parity,
     }
     if "copy_ceiling_gbps" in rec:
         line["copy_ceiling_gbps"] = round(rec["copy_ceiling_gbps"], 2)
         line["frac_of_copy_ceiling"] = round(rec["frac_of_copy_ceiling"], 4)
     if args.all:
-        for name, other in inputs.ALL_WORKLOADS.items():
+        for name, other in inputs.EVERY_WORKLOAD.items():
             if name == w.name:
                 continue
             _, r = bench_workload(other, args.steps, args.warmup, args.seed, graph=True)

@@ -320,6 +320,52 @@ RMSNORM_API rmsnorm_status_t layernorm_fwd_ex(const void* x, const void* gamma, 
 RMSNORM_API rmsnorm_status_t layernorm_select_config(int64_t rows, int64_t hidden, rmsnorm_dtype_t dtype,
                                                      int32_t vector_aligned, rmsnorm_config_t* cfg);
 
+/*
+ * KV RMSNorm + RoPE + cache scatter: the fused KV-cache maintenance operator
+ * the TileLang tutorial ch. 02 ("从 PyTorch 到 kernel", sections 1.2 and 4.2)
+ * cites from CANN (aclnnKvRmsNormRopeCache).  For every token t and head h,
+ * the row kv[t, h, :] is split along its tail axis:
+ *
+ *   kv[t, h, 0 : norm_dim]             -> RMSNorm (eps, gamma, as rmsnorm_fwd)
+ *                                          -> norm_cache[slots[t], h, :]
+ *   kv[t, h, norm_dim : norm_dim+rope] -> RoPE at position positions[t]
+ *                                          -> rope_cache[slots[t], h, :]
+ *
+ * RoPE as xserv's rope.cu (phase 4): a pair (a, b) becomes
+ * (a*cos - b*sin, a*sin + b*cos) with cos = cos_table[p, i], sin =
+ * sin_table[p, i]; the pairs are adjacent elements (2i, 2i+1) with rope_style 1
+ * or the two halves (i, i + rope_dim/2) with rope_style 0.  fp32 math, one
+ * rounding per output element.
+ *
+ *   kv          [tokens, heads, norm_dim + rope_dim], dtype.
+ *   gamma       [norm_dim], dtype.
+ *   cos_table, sin_table  [max_pos, rope_dim/2] float32 (may be NULL when
+ *               rope_dim is 0).
+ *   positions   [tokens] int32;  slots [tokens] int64: the cache row of each
+ *               token (for a paged cache, block_table[seq][pos / block_size] *
+ *               block_size + pos % block_size).  A token whose slot is not in
+ *               [0, num_slots) or whose position is not in [0, max_pos)
+ *               writes nothing (padding); slots must be distinct within a call
+ *               (two tokens with one slot race).
+ *   norm_cache  [num_slots, heads, norm_dim], dtype; only the rows named by
+ *               valid slots are written.
+ *   rope_cache  [num_slots, heads, rope_dim], dtype; same (may be NULL when
+ *               rope_dim is 0).
+ *   heads >= 1, norm_dim >= 1, rope_dim >= 0 and even; eps as rmsnorm_fwd;
+ *   rope_style 0 or 1.  The caches must not overlap each other or any input.
+ * 16-byte vector accesses are used when every buffer is 16-byte aligned,
+ * norm_dim is a multiple of the vector width, rope_dim a multiple of it
+ * (pairs) or of twice it (halves), and the rotated part fits in 64 lanes;
+ * otherwise an element kernel runs.  tokens == 0 returns RMSNORM_OK without
+ * touching the GPU.
+ */
+RMSNORM_API rmsnorm_status_t kv_rmsnorm_rope_cache(const void* kv, const void* gamma, const float* cos_table,
+                                                   const float* sin_table, const int32_t* positions,
+                                                   const int64_t* slots, void* norm_cache, void* rope_cache,
+                                                   int64_t tokens, int64_t heads, int64_t norm_dim,
+                                                   int64_t rope_dim, int64_t max_pos, int64_t num_slots, float eps,
+                                                   int32_t rope_style, rmsnorm_dtype_t dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,6 +20,7 @@ fallback -- if the library is not built, every call raises.
     layernorm_fwd(x, gamma, beta, out, eps)                    -> out (beta may be None)
     layernorm_fwd_ex(..., config)                              forced launch configuration
     layernorm_select_config(rows, hidden, dtype, vector_aligned) -> Config
+    kv_rmsnorm_rope_cache(kv, gamma, cos, sin, positions, slots, norm_cache, rope_cache, eps, rope_style)
     rmsnorm_status_string(status)                              -> str
 
 The backward's weight gradient needs a workspace; when none is passed, a
@@ -104,12 +105,15 @@ def lib() -> ctypes.CDLL:
         L.layernorm_fwd.argtypes = [vp, vp, vp, vp, i64, i64, f32, i32, vp]
         L.layernorm_fwd_ex.argtypes = [vp, vp, vp, vp, i64, i64, f32, i32, cfgp, vp]
         L.layernorm_select_config.argtypes = [i64, i64, i32, i32, cfgp]
+        L.kv_rmsnorm_rope_cache.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32,
+                                            i32, vp]
         L.rmsnorm_status_string.argtypes = [i32]
         L.rmsnorm_status_string.restype = ctypes.c_char_p
         for fn in (L.rmsnorm_fwd, L.rmsnorm_residual_fwd, L.rmsnorm_fwd_ex, L.rmsnorm_residual_fwd_ex,
                    L.rmsnorm_select_config, L.rmsnorm_select_quant_config, L.rmsnorm_dynamic_quant_fwd,
                    L.rmsnorm_dynamic_quant_fwd_ex, L.rmsnorm_bwd, L.rmsnorm_bwd_ex, L.rmsnorm_bwd_workspace_size,
-                   L.rmsnorm_select_bwd_config, L.layernorm_fwd, L.layernorm_fwd_ex, L.layernorm_select_config):
+                   L.rmsnorm_select_bwd_config, L.layernorm_fwd, L.layernorm_fwd_ex, L.layernorm_select_config,
+                   L.kv_rmsnorm_rope_cache):
             fn.restype = i32
         _lib = L
     return _lib
@@ -359,6 +363,47 @@ def layernorm_select_config(rows: int, hidden: int, dtype, vector_aligned: bool 
     _check(lib().layernorm_select_config(int(rows), int(hidden), code, int(bool(vector_aligned)),
                                          ctypes.byref(cfg)), "layernorm_select_config")
     return cfg
+
+
+ROPE_HALVES = 0
+ROPE_PAIRS = 1
+
+
+def kv_rmsnorm_rope_cache(kv, gamma, cos_table, sin_table, positions, slots, norm_cache, rope_cache,
+                          eps: float = 1e-6, rope_style: int = ROPE_PAIRS, stream=None):
+    """RMSNorm of kv[..., :norm_dim] into norm_cache[slot] and RoPE of
+    kv[..., norm_dim:] into rope_cache[slot] (C: kv_rmsnorm_rope_cache).
+    kv [tokens, heads, norm_dim + rope_dim]; caches [num_slots, heads, dim];
+    tables float32 [max_pos, rope_dim / 2]; positions int32, slots int64."""
+    for t, n in ((kv, "kv"), (gamma, "gamma"), (positions, "positions"), (slots, "slots"),
+                 (norm_cache, "norm_cache"), (rope_cache, "rope_cache"), (cos_table, "cos_table"),
+                 (sin_table, "sin_table")):
+        _device_tensor(t, n)
+    if kv.dim() != 3 or norm_cache.dim() != 3 or rope_cache.dim() != 3:
+        raise ValueError("kv and the caches must be 3-D")
+    tokens, heads, d = kv.shape
+    norm_dim, rope_dim = norm_cache.shape[2], rope_cache.shape[2]
+    if norm_dim + rope_dim != d or norm_cache.shape[1] != heads or rope_cache.shape[1] != heads or \
+            norm_cache.shape[0] != rope_cache.shape[0]:
+        raise ValueError("cache shapes do not match kv")
+    for t, n in ((gamma, "gamma"), (norm_cache, "norm_cache"), (rope_cache, "rope_cache")):
+        if t.dtype != kv.dtype:
+            raise ValueError("%s must have the dtype of kv" % n)
+    if gamma.dim() != 1 or gamma.shape[0] != norm_dim:
+        raise ValueError("gamma must be [norm_dim]")
+    if cos_table.dtype != torch.float32 or sin_table.dtype != torch.float32 or cos_table.shape != sin_table.shape \
+            or cos_table.dim() != 2 or cos_table.shape[1] != rope_dim // 2:
+        raise ValueError("tables must be float32 [max_pos, rope_dim / 2]")
+    if positions.dtype != torch.int32 or slots.dtype != torch.int64 or positions.numel() != tokens or \
+            slots.numel() != tokens:
+        raise ValueError("positions (int32) and slots (int64) need one entry per token")
+    st = lib().kv_rmsnorm_rope_cache(kv.data_ptr(), gamma.data_ptr(), cos_table.data_ptr(), sin_table.data_ptr(),
+                                     positions.data_ptr(), slots.data_ptr(), norm_cache.data_ptr(),
+                                     rope_cache.data_ptr(), tokens, heads, norm_dim, rope_dim, cos_table.shape[0],
+                                     norm_cache.shape[0], float(eps), int(rope_style), dtype_code(kv.dtype),
+                                     _stream(stream, kv.device))
+    _check(st, "kv_rmsnorm_rope_cache")
+    return norm_cache, rope_cache
 
 
 def hbm_copy(src: torch.Tensor, dst: torch.Tensor, max_blocks: int = 0, stream=None):

@@ -12,6 +12,7 @@
 #include <stdint.h>
 
 #include "../../include/rmsnorm.h"
+#include "kv_kernels.hpp"
 #include "layernorm_kernels.hpp"
 #include "rmsnorm_bwd_kernels.hpp"
 #include "rmsnorm_dispatch.hpp"
@@ -555,6 +556,131 @@ rmsnorm_status_t run_ln(const LnProblem& p, const rmsnorm_config_t* user, void* 
     return launch_checked(fn, grid, lanes, &a, static_cast<hipStream_t>(stream));
 }
 
+// ---------------------------------------------------------------- KV RMSNorm + RoPE + cache
+
+struct KvProblem {
+    const void* kv;
+    const void* gamma;
+    const float* cos_t;
+    const float* sin_t;
+    const int32_t* pos;
+    const int64_t* slots;
+    void* nc;
+    void* rc;
+    int64_t tokens;
+    int64_t heads;
+    int64_t dn;
+    int64_t dr;
+    int64_t max_pos;
+    int64_t num_slots;
+    float eps;
+    int style;
+    int dtype;
+};
+
+bool fits(int64_t a, int64_t b, int64_t c, int64_t d) {  // a * b * c * d <= INT64_MAX, all >= 0
+    if (a == 0 || b == 0 || c == 0 || d == 0) return true;
+    return a <= INT64_MAX / b && a * b <= INT64_MAX / c && a * b * c <= INT64_MAX / d;
+}
+
+rmsnorm_status_t validate_kv(const KvProblem& p) {
+    if (p.tokens < 0 || p.heads < 1 || p.heads > INT32_MAX || p.dn < 1 || p.dr < 0 || p.dr % 2 != 0 ||
+        p.dn + p.dr > INT32_MAX || p.max_pos < 0 || p.num_slots < 0)
+        return RMSNORM_ERR_INVALID_ARG;
+    if (!(p.eps >= 0.0f) || isinf(p.eps) || (p.style != 0 && p.style != 1)) return RMSNORM_ERR_INVALID_ARG;
+    if (p.dtype != RMSNORM_DTYPE_F32 && p.dtype != RMSNORM_DTYPE_BF16) return RMSNORM_ERR_UNSUPPORTED_DTYPE;
+    const int64_t es = elem_size(p.dtype);
+    if (!fits(p.tokens, p.heads, p.dn + p.dr, es) || !fits(p.num_slots, p.heads, p.dn + p.dr, es) ||
+        !fits(p.max_pos, p.dr, 4, 1))
+        return RMSNORM_ERR_INVALID_ARG;
+    return RMSNORM_OK;
+}
+
+rmsnorm_status_t validate_kv_pointers(const KvProblem& p) {
+    const int es = elem_size(p.dtype);
+    if (!p.kv || !p.gamma || !p.pos || !p.slots || !p.nc) return RMSNORM_ERR_INVALID_ARG;
+    if (p.dr > 0 && (!p.cos_t || !p.sin_t || !p.rc)) return RMSNORM_ERR_INVALID_ARG;
+    const void* ptrs[] = {p.kv, p.gamma, p.nc, p.rc};
+    for (const void* q : ptrs)
+        if (q && reinterpret_cast<uintptr_t>(q) % es != 0) return RMSNORM_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(p.pos) % 4 || reinterpret_cast<uintptr_t>(p.slots) % 8 ||
+        reinterpret_cast<uintptr_t>(p.cos_t) % 4 || reinterpret_cast<uintptr_t>(p.sin_t) % 4)
+        return RMSNORM_ERR_INVALID_ARG;
+    const int64_t d = p.dn + p.dr;
+    const int64_t ncb = p.num_slots * p.heads * p.dn * es, rcb = p.num_slots * p.heads * p.dr * es;
+    const int64_t tb = p.max_pos * (p.dr / 2) * 4;
+    const void* in[] = {p.kv, p.gamma, p.cos_t, p.sin_t, p.pos, p.slots};
+    const int64_t insz[] = {p.tokens * p.heads * d * es, p.dn * es, tb, tb, p.tokens * 4, p.tokens * 8};
+    for (int i = 0; i < 6; ++i) {
+        if (!in[i]) continue;
+        if (ranges_overlap(p.nc, ncb, in[i], insz[i]) || ranges_overlap(p.rc, rcb, in[i], insz[i]))
+            return RMSNORM_ERR_INVALID_ARG;
+    }
+    if (p.rc && ranges_overlap(p.nc, ncb, p.rc, rcb)) return RMSNORM_ERR_INVALID_ARG;
+    return RMSNORM_OK;
+}
+
+// The vector kernel needs 16-byte vectors that never straddle the split or a
+// rope pair group, table rows whose per-lane entries are 16-byte (8-byte for
+// fp32 adjacent pairs) aligned, a rotated part no wider than 64 lane slots and
+// a norm part of at most 8 vectors per lane.  Returns the NVPL index or -1.
+int kv_vec_choice(const KvProblem& p, bool* masked) {
+    const int v = vec_elems(p.dtype);
+    const int64_t unit = p.style == 1 ? v : 2 * v;
+    if (p.dn % v != 0 || p.dr % unit != 0) return -1;
+    const void* ptrs[] = {p.kv, p.gamma, p.nc, p.rc, p.cos_t, p.sin_t};
+    for (const void* q : ptrs)
+        if (q && reinterpret_cast<uintptr_t>(q) % kVectorBytes != 0) return -1;
+    const int64_t rope_lanes = p.style == 1 ? p.dr / v : p.dr / (2 * v);
+    if (rope_lanes > 64) return -1;
+    const int64_t nv = p.dn / v;
+    for (int i = 0; i < mbr::kNumKvVpl; ++i) {
+        if (int64_t(64) * mbr::kKvVplList[i] >= nv) {
+            *masked = int64_t(64) * mbr::kKvVplList[i] != nv;
+            return i;
+        }
+    }
+    return -1;
+}
+
+rmsnorm_status_t run_kv(const KvProblem& p, void* stream) {
+    rmsnorm_status_t s = validate_kv(p);
+    if (s != RMSNORM_OK) return s;
+    if (p.tokens == 0) return RMSNORM_OK;
+    s = validate_kv_pointers(p);
+    if (s != RMSNORM_OK) return s;
+    mbr::KvArgs a;
+    a.kv = p.kv;
+    a.gamma = p.gamma;
+    a.cos_t = p.cos_t;
+    a.sin_t = p.sin_t;
+    a.pos = p.pos;
+    a.slots = p.slots;
+    a.nc = p.nc;
+    a.rc = p.rc;
+    a.rows = p.tokens * p.heads;
+    a.max_pos = p.max_pos;
+    a.num_slots = p.num_slots;
+    a.heads = static_cast<int32_t>(p.heads);
+    a.norm_dim = static_cast<int32_t>(p.dn);
+    a.rope_dim = static_cast<int32_t>(p.dr);
+    a.norm_dim_f = static_cast<float>(p.dn);
+    a.eps = p.eps;
+    bool masked = false;
+    const int vi = kv_vec_choice(p, &masked);
+    const void* fn = vi >= 0 ? mbr::kv_vec_kernel_ptr(p.dtype, p.style, masked, vi)
+                             : mbr::kv_elem_kernel_ptr(p.dtype, p.style);
+    if (!fn) return RMSNORM_ERR_INVALID_ARG;
+    // One row per wave, four waves per workgroup.  Sweeps on MI355X (bf16
+    // prefill, 16384 rows of 512 + 64): two or eight waves per workgroup within
+    // noise; two or four rows per wave, all loaded before any is reduced,
+    // slower (13.4 us against 12.1), since fewer waves are in flight.
+    constexpr int64_t kWavesPerBlock = 4;
+    int64_t grid = ceil_div(a.rows, kWavesPerBlock);
+    if (grid > kMaxGrid) grid = kMaxGrid;
+    return launch_checked(fn, grid, 64 * kWavesPerBlock, &a, static_cast<hipStream_t>(stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -694,6 +820,18 @@ RMSNORM_API rmsnorm_status_t layernorm_select_config(int64_t rows, int64_t hidde
     if (s != RMSNORM_OK) return s;
     *cfg = choose_ln(rows, hidden, static_cast<int>(dtype), vector_aligned_flag != 0);
     return RMSNORM_OK;
+}
+
+RMSNORM_API rmsnorm_status_t kv_rmsnorm_rope_cache(const void* kv, const void* gamma, const float* cos_table,
+                                                   const float* sin_table, const int32_t* positions,
+                                                   const int64_t* slots, void* norm_cache, void* rope_cache,
+                                                   int64_t tokens, int64_t heads, int64_t norm_dim,
+                                                   int64_t rope_dim, int64_t max_pos, int64_t num_slots, float eps,
+                                                   int32_t rope_style, rmsnorm_dtype_t dtype, void* stream) {
+    const KvProblem p = {kv,       gamma,     cos_table, sin_table, positions, slots,
+                         norm_cache, rope_cache, tokens, heads,     norm_dim,  rope_dim,
+                         max_pos,  num_slots, eps,       rope_style, static_cast<int>(dtype)};
+    return run_kv(p, stream);
 }
 
 RMSNORM_API const char* rmsnorm_status_string(rmsnorm_status_t status) {

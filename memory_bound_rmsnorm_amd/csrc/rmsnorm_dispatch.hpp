@@ -72,6 +72,13 @@ const void* ln_vec_kernel_ptr(int dtype, bool masked, int wpr_index, int vpl_ind
 const void* ln_elem_kernel_ptr(int dtype, int wpr_index, int epl_index);
 const void* ln_multipass_kernel_ptr(int dtype, bool vec);
 
+// KV RMSNorm + RoPE + cache: one wave per row; the norm part in 1, 2, 4 or 8
+// 16-byte vectors per lane (index 0..3), rope style 0 (halves) or 1 (pairs).
+constexpr int kKvVplList[] = {1, 2, 4, 8};
+constexpr int kNumKvVpl = sizeof(kKvVplList) / sizeof(int);
+const void* kv_vec_kernel_ptr(int dtype, int style, bool masked, int vpl_index);
+const void* kv_elem_kernel_ptr(int dtype, int style);
+
 // Per-unit getters defined in the instantiation files.
 const void* vec_kernel_bf16(bool fused, bool masked, int wi, int vi);
 const void* vec_kernel_f32(bool fused, bool masked, int wi, int vi);

@@ -283,12 +283,28 @@ class KvWorkload:
         return self.max_len
 
     @property
-    def algorithmic_bytes(self) -> int:
-        """kv, the token's two table rows, its position and slot read; both cache
-        rows written; gamma once."""
+    def read_bytes(self) -> int:
+        """kv, the token's two table rows, its position and slot; gamma once."""
         d = self.norm_dim + self.rope_dim
-        per_token = (2 * self.heads * d * self.elem_size + self.rope_dim * 4 + 4 + 8)
-        return self.tokens * per_token + self.norm_dim * self.elem_size
+        return self.tokens * (self.heads * d * self.elem_size + self.rope_dim * 4 + 4 + 8) + \
+            self.norm_dim * self.elem_size
+
+    @property
+    def write_bytes(self) -> int:
+        """Both cache rows of every token."""
+        return self.tokens * self.heads * (self.norm_dim + self.rope_dim) * self.elem_size
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        return self.read_bytes + self.write_bytes
+
+    @property
+    def copy_bytes(self) -> int:
+        return (self.algorithmic_bytes // 2) & ~15
+
+    @property
+    def cache_bytes(self) -> int:
+        return self.num_slots * self.heads * (self.norm_dim + self.rope_dim) * self.elem_size
 
 
 KV_WORKLOADS: Dict[str, KvWorkload] = {
@@ -351,3 +367,7 @@ def kv_caches(w: KvWorkload, device="cpu"):
     """(norm_cache, rope_cache) with their initial pattern."""
     return (cache_pattern(w.num_slots, w.heads, w.norm_dim, w.dtype, device, 1),
             cache_pattern(w.num_slots, w.heads, w.rope_dim, w.dtype, device, 2))
+
+
+# Every workload bench.py can time, by name.
+EVERY_WORKLOAD = dict(ALL_WORKLOADS, **KV_WORKLOADS)

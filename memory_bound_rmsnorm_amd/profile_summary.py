@@ -25,6 +25,11 @@ RMS_KERNEL_TAGS = ("rms_vec_kernel", "rms_elem_kernel", "rms_twopass_kernel")
 BWD_KERNEL_TAGS = ("rms_bwd_vec_kernel", "rms_bwd_elem_kernel", "rms_bwd_twopass_kernel")
 BWD_DW_TAG = "rms_bwd_dw_kernel"
 LN_KERNEL_TAGS = ("ln_vec_kernel", "ln_elem_kernel", "ln_multipass_kernel")
+KV_KERNEL_TAGS = ("kv_vec_kernel", "kv_elem_kernel")
+
+
+def _is_kv(w):
+    return isinstance(w, inputs.KvWorkload)
 COPY_KERNEL_TAG = "hbm_copy_kernel"
 
 
@@ -35,6 +40,8 @@ def _is_rms(name):
 def _step_kernels(w):
     """Predicates for the kernels one step of workload w launches, once each:
     the forward kernel, or the backward row kernel plus the dweight reduction."""
+    if _is_kv(w):
+        return [lambda k: any(t in k for t in KV_KERNEL_TAGS)]
     if w.backward:
         return [lambda k: any(t in k for t in BWD_KERNEL_TAGS), lambda k: BWD_DW_TAG in k]
     if w.layernorm:
@@ -43,16 +50,21 @@ def _step_kernels(w):
 
 
 def _family(w):
+    if _is_kv(w):
+        return "kv"
     return "bwd" if w.backward else "ln" if w.layernorm else "fwd"
 
 
 def _title(w):
+    if _is_kv(w):
+        return "KV RMSNorm + RoPE + cache %s, %d tokens x %d heads x (%d + %d)" % (
+            w.dtype, w.tokens, w.heads, w.norm_dim, w.rope_dim)
     return "%s %s [%d, %d]%s" % ("LayerNorm" if w.layernorm else "RMSNorm", w.dtype, w.rows, w.hidden,
                                  " fused residual" if w.fused else " backward" if w.backward else "")
 
 
 def stats(args):
-    w = inputs.ALL_WORKLOADS[args.workload]
+    w = inputs.EVERY_WORKLOAD[args.workload]
     with open(args.csv) as f:
         rows = list(csv.DictReader(f))
     out = ["# rocprofv3 --kernel-trace --stats summary: %s" % _title(w),
@@ -73,7 +85,7 @@ def stats(args):
             step_avg.append(float(hit[0]["AverageNs"]) / 1e3)
     if len(step_avg) == len(preds):
         t = sum(step_avg)
-        if w.backward:
+        if getattr(w, "backward", False):
             out.append("bwd_row_kernel_avg_us: %.3f" % step_avg[0])
             out.append("bwd_dw_kernel_avg_us: %.3f" % step_avg[1])
             out.append("step_avg_us: %.3f" % t)
@@ -103,7 +115,7 @@ def _pick(means, pred):
 
 
 def pmc(args):
-    w = inputs.ALL_WORKLOADS[args.workload]
+    w = inputs.EVERY_WORKLOAD[args.workload]
     fm, fn = _counter_means(args.fetch, "FETCH_SIZE")
     wm, wn = _counter_means(args.write, "WRITE_SIZE")
     rname, rfetch, rwrite, ndisp = [], 0.0, 0.0, []
@@ -149,6 +161,19 @@ def pmc(args):
     print("\n".join(out))
 
 
+def kv_launch(w):
+    """The kernel kv_rmsnorm_rope_cache runs for workload w on 16-byte-aligned
+    buffers (its host-side choice, restated for reporting)."""
+    v = 4 if w.dtype == "f32" else 8
+    unit = v if w.rope_style == 1 else 2 * v
+    rope_lanes = w.rope_dim // unit if w.rope_style == 1 else w.rope_dim // (2 * v)
+    nv = w.norm_dim // v
+    per = next((k for k in (1, 2, 4, 8) if 64 * k >= nv), None)
+    vec = w.norm_dim % v == 0 and w.rope_dim % unit == 0 and rope_lanes <= 64 and per is not None
+    return {"path": "vector" if vec else "element", "norm_vectors_per_lane": per if vec else 0,
+            "rope_style": "pairs" if w.rope_style == 1 else "halves", "rows_per_workgroup": 4}
+
+
 def launch_config(w):
     """The automatic configuration for workload w on 16-byte-aligned buffers."""
     import torch
@@ -162,8 +187,12 @@ def launch_config(w):
     return select(w.rows, w.hidden, dt, True, w.fused)
 
 
+def launch_dict(w):
+    return kv_launch(w) if _is_kv(w) else launch_config(w).as_dict()
+
+
 def _launch_config(w):
-    return " ".join("%s=%s" % kv for kv in launch_config(w).as_dict().items())
+    return " ".join("%s=%s" % kv for kv in launch_dict(w).items())
 
 
 def resources(args):
@@ -194,6 +223,17 @@ def resources(args):
                                                                    int(masked), int(w.fused), qt)
         hit = [l for l in lines if mangled in l]
         out.append("%s -> %s | %s" % (name, cfg.as_dict(), hit[0].split("|", 1)[1].strip() if hit else "?"))
+    for name, w in inputs.KV_WORKLOADS.items():
+        k = kv_launch(w)
+        e = "F32" if w.dtype == "f32" else "Bf16"
+        if k["path"] == "vector":
+            masked = 64 * k["norm_vectors_per_lane"] != w.norm_dim // (4 if w.dtype == "f32" else 8)
+            mangled = "kv_vec_kernelINS_%d%sELi%dELb%dELi%dEEEv" % (len(e), e, k["norm_vectors_per_lane"],
+                                                                   int(masked), w.rope_style)
+        else:
+            mangled = "kv_elem_kernelINS_%d%sELi%dEEEv" % (len(e), e, w.rope_style)
+        hit = [l for l in lines if mangled in l]
+        out.append("%s -> %s | %s" % (name, k, hit[0].split("|", 1)[1].strip() if hit else "?"))
     print("\n".join(out))
 
 
@@ -202,7 +242,7 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
     s.add_argument("--csv", required=True)
-    s.add_argument("--workload", default=inputs.HEADLINE)
+    s.add_argument("--workload", default=inputs.HEADLINE, choices=sorted(inputs.EVERY_WORKLOAD))
     s.add_argument("--command", required=True)
     p = sub.add_parser("pmc")
     p.add_argument("--fetch", required=True)
