@@ -137,6 +137,11 @@ typedef struct {
                                (1024 when waves_per_row == 16); TWO_PASS: must be 1 */
     int32_t max_blocks;     /* >= 0; 0: one workgroup per group of rows_per_block rows;
                                n > 0: at most n workgroups, each looping over row groups */
+    int32_t lanes_per_row;  /* 0: 64 * waves_per_row (whole waves).  VECTOR path of the
+                               forward entry points only: 8, 16 or 32 lanes per row with
+                               waves_per_row 1 and items_per_lane 1 or 2, several rows
+                               sharing a wave; lanes_per_row * rows_per_block must then be
+                               a multiple of 64 and at most 512 */
 } rmsnorm_config_t;
 
 /*

@@ -59,12 +59,15 @@ class Config(ctypes.Structure):
     """rmsnorm_config_t."""
     _fields_ = [("path", ctypes.c_int32), ("waves_per_row", ctypes.c_int32),
                 ("items_per_lane", ctypes.c_int32), ("rows_per_block", ctypes.c_int32),
-                ("max_blocks", ctypes.c_int32)]
+                ("max_blocks", ctypes.c_int32), ("lanes_per_row", ctypes.c_int32)]
 
     def as_dict(self):
-        return {"path": PATH_NAMES.get(self.path, self.path), "waves_per_row": self.waves_per_row,
-                "items_per_lane": self.items_per_lane, "rows_per_block": self.rows_per_block,
-                "max_blocks": self.max_blocks}
+        d = {"path": PATH_NAMES.get(self.path, self.path), "waves_per_row": self.waves_per_row,
+             "items_per_lane": self.items_per_lane, "rows_per_block": self.rows_per_block,
+             "max_blocks": self.max_blocks}
+        if self.lanes_per_row:
+            d["lanes_per_row"] = self.lanes_per_row
+        return d
 
     def __repr__(self):
         return "Config(%s)" % ", ".join("%s=%s" % kv for kv in self.as_dict().items())

@@ -8,6 +8,8 @@
 // about 0.1 ms, the same order as the operator itself, so this library never
 // synchronises).
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <math.h>
 #include <stdint.h>
 
@@ -23,6 +25,12 @@ namespace {
 constexpr int64_t kVectorBytes = 16;
 // Largest grid launched in one call; bigger jobs loop inside the kernel.
 constexpr int64_t kMaxGrid = int64_t(1) << 20;
+// Workgroup size when rows narrower than half a wave share waves: one wave.
+// Sweeps on MI355X (HIP-graph timing): bf16 [262144, 128] runs in 23.3 us as
+// 16 lanes x 1 vector x 4 rows per 64-lane workgroup, against 62.8 us with a
+// whole wave per row; [524288, 64] 23.7 against 115 us; [131072, 256]
+// 23.3 against 36.3 us; 128- to 512-lane workgroups were 1-6 % slower.
+constexpr int kSubwaveThreads = 64;
 
 struct Problem {
     const void* x;
@@ -160,6 +168,16 @@ rmsnorm_config_t choose(int64_t rows, int64_t hidden, int dtype, bool aligned, b
     c.items_per_lane = per;
     c.rows_per_block = 1;
     c.max_blocks = 0;
+    if (vec && units <= mbr::kLprList[mbr::kNumLpr - 1]) {
+        // a row narrower than half a wave: the smallest lane group that holds
+        // it with one vector per lane, one wave per workgroup
+        const int lpr = round_up_in(mbr::kLprList, mbr::kNumLpr, units);
+        const int64_t per_wave = 64 / lpr;  // rows sharing one wave
+        c.lanes_per_row = lpr;
+        c.items_per_lane = 1;
+        c.rows_per_block = static_cast<int32_t>(
+            std::min<int64_t>(kSubwaveThreads / lpr, std::max<int64_t>(per_wave, ceil_div(rows, per_wave) * per_wave)));
+    }
     return c;
 }
 
@@ -168,7 +186,8 @@ rmsnorm_status_t launch(const Problem& p, const rmsnorm_config_t* user, hipStrea
     const rmsnorm_config_t c = (user && user->path != RMSNORM_PATH_AUTO) ? *user : choose(p.rows, p.hidden, p.dtype, aligned, p.fused, p.qt);
     const int wi = index_of(mbr::kWprList, mbr::kNumWpr, c.waves_per_row);
     if (wi < 0 || c.rows_per_block < 1 || c.max_blocks < 0) return RMSNORM_ERR_INVALID_ARG;
-    const int64_t lanes_per_row = int64_t(64) * c.waves_per_row;
+    const bool whole = c.lanes_per_row == 0 || c.lanes_per_row == 64 * c.waves_per_row;
+    const int64_t lanes_per_row = whole ? int64_t(64) * c.waves_per_row : c.lanes_per_row;
 
     mbr::RowArgs a;
     a.x = p.x;
@@ -187,8 +206,19 @@ rmsnorm_status_t launch(const Problem& p, const rmsnorm_config_t* user, hipStrea
     switch (c.path) {
         case RMSNORM_PATH_VECTOR: {
             if (!aligned || p.hidden % vec_elems(p.dtype) != 0) return RMSNORM_ERR_INVALID_ARG;
-            const int vi = index_of(mbr::kVplList, mbr::kNumVpl, c.items_per_lane);
             const int64_t nvec = p.hidden / vec_elems(p.dtype);
+            if (!whole) {  // several rows per wave, lanes_per_row lanes each
+                const int li = index_of(mbr::kLprList, mbr::kNumLpr, c.lanes_per_row);
+                const int vi = index_of(mbr::kSwVplList, mbr::kNumSwVpl, c.items_per_lane);
+                if (c.waves_per_row != 1 || li < 0 || vi < 0 || lanes_per_row * c.items_per_lane < nvec)
+                    return RMSNORM_ERR_INVALID_ARG;
+                threads = lanes_per_row * c.rows_per_block;
+                if (threads % 64 != 0 || threads > mbr::max_threads_for(1)) return RMSNORM_ERR_INVALID_ARG;
+                fn = mbr::subwave_kernel(p.dtype, p.fused, p.qt, lanes_per_row * c.items_per_lane != nvec, li, vi);
+                a.units = static_cast<int32_t>(nvec);
+                break;
+            }
+            const int vi = index_of(mbr::kVplList, mbr::kNumVpl, c.items_per_lane);
             if (vi < 0 || lanes_per_row * c.items_per_lane < nvec) return RMSNORM_ERR_INVALID_ARG;
             threads = lanes_per_row * c.rows_per_block;
             if (threads > mbr::max_threads_for(c.waves_per_row)) return RMSNORM_ERR_INVALID_ARG;
@@ -199,6 +229,7 @@ rmsnorm_status_t launch(const Problem& p, const rmsnorm_config_t* user, hipStrea
             break;
         }
         case RMSNORM_PATH_ELEMENT: {
+            if (!whole) return RMSNORM_ERR_INVALID_ARG;
             const int ei = index_of(mbr::kEplList, mbr::kNumEpl, c.items_per_lane);
             if (ei < 0 || lanes_per_row * c.items_per_lane < p.hidden) return RMSNORM_ERR_INVALID_ARG;
             threads = lanes_per_row * c.rows_per_block;
@@ -208,7 +239,7 @@ rmsnorm_status_t launch(const Problem& p, const rmsnorm_config_t* user, hipStrea
             break;
         }
         case RMSNORM_PATH_TWO_PASS: {
-            if (c.rows_per_block != 1) return RMSNORM_ERR_INVALID_ARG;
+            if (c.rows_per_block != 1 || !whole) return RMSNORM_ERR_INVALID_ARG;
             const bool vec = aligned && p.hidden % vec_elems(p.dtype) == 0;
             threads = lanes_per_row;
             fn = p.qt ? mbr::qtwopass_kernel(p.dtype, p.qt, p.fused, vec) : mbr::twopass_kernel(p.dtype, p.fused, vec);
@@ -363,6 +394,7 @@ rmsnorm_status_t run_bwd(const BwdProblem& p, const rmsnorm_config_t* user, void
         (user && user->path != RMSNORM_PATH_AUTO) ? *user : choose_bwd(p.rows, p.hidden, p.dtype, aligned);
     const int wi = index_of(mbr::kWprList, mbr::kNumWpr, c.waves_per_row);
     if (wi < 0 || c.rows_per_block != 1 || c.max_blocks < 0) return RMSNORM_ERR_INVALID_ARG;
+    if (c.lanes_per_row != 0 && c.lanes_per_row != 64 * c.waves_per_row) return RMSNORM_ERR_INVALID_ARG;
     const bool dw = p.dw != nullptr;
     const int64_t ws_need = dw ? bwd_workspace_need(p.rows, p.hidden, c) : 0;
     const hipStream_t stream = static_cast<hipStream_t>(stream_arg);
@@ -512,6 +544,7 @@ rmsnorm_status_t run_ln(const LnProblem& p, const rmsnorm_config_t* user, void* 
         (user && user->path != RMSNORM_PATH_AUTO) ? *user : choose_ln(p.rows, p.hidden, p.dtype, aligned);
     const int wi = index_of(mbr::kWprList, mbr::kNumWpr, c.waves_per_row);
     if (wi < 0 || c.rows_per_block != 1 || c.max_blocks < 0) return RMSNORM_ERR_INVALID_ARG;
+    if (c.lanes_per_row != 0 && c.lanes_per_row != 64 * c.waves_per_row) return RMSNORM_ERR_INVALID_ARG;
     const int64_t lanes = int64_t(64) * c.waves_per_row;
     mbr::LnArgs a;
     a.x = p.x;

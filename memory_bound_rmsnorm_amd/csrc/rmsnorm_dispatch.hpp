@@ -43,6 +43,15 @@ const void* qtwopass_kernel(int dtype, int qt, bool fused, bool vec);
 const void* qvec_kernel_bf16(int qt, bool fused, bool masked, int wi, int vi);
 const void* qvec_kernel_f32(int qt, bool fused, bool masked, int wi, int vi);
 
+// Rows narrower than a wave: LPR lanes per row (a row per lane group), one or
+// two 16-byte vectors per lane; every form (plain, fused, quantised).
+constexpr int kLprList[] = {8, 16, 32};
+constexpr int kSwVplList[] = {1, 2};
+constexpr int kNumLpr = sizeof(kLprList) / sizeof(int);
+constexpr int kNumSwVpl = sizeof(kSwVplList) / sizeof(int);
+// qt: 0 = normalised output, 1 = int8, 2 = fp8 e4m3fn.
+const void* subwave_kernel(int dtype, bool fused, int qt, bool masked, int lpr_index, int vpl_index);
+
 // Backward (dx, and dweight through per-workgroup partial rows): the lane
 // holds x, dy and the weight slice (plus fp32 column sums when dweight is
 // wanted), so the vector path carries at most 8 vectors per lane (4 in a

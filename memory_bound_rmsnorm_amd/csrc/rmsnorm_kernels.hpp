@@ -145,6 +145,27 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// Sum over each aligned group of L lanes (L = 8, 16, 32 or 64): the first
+// steps of wave_sum, stopped at the group width; every lane of a group returns
+// the same bits.
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(L == 8 || L == 16 || L == 32 || L == 64, "group width");
+    if constexpr (L == 64) {
+        return wave_sum(v);
+    } else {
+        v += dpp_mov<0xB1>(v);
+        v += dpp_mov<0x4E>(v);
+        v += dpp_mov<0x141>(v);
+        if constexpr (L >= 16) v += dpp_mov<0x140>(v);
+        if constexpr (L == 32) {
+            auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+            v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+        }
+        return v;
+    }
+}
+
 // Maximum over the 64 lanes of a wave, same pattern as wave_sum (fmaxf is
 // commutative, so every lane returns the same bits).
 __device__ __forceinline__ float wave_max(float v) {
@@ -161,6 +182,24 @@ __device__ __forceinline__ float wave_max(float v) {
         v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
     }
     return v;
+}
+
+// Maximum over each aligned group of L lanes, as group_sum.
+template <int L>
+__device__ __forceinline__ float group_max(float v) {
+    if constexpr (L == 64) {
+        return wave_max(v);
+    } else {
+        v = fmaxf(v, dpp_mov<0xB1>(v));
+        v = fmaxf(v, dpp_mov<0x4E>(v));
+        v = fmaxf(v, dpp_mov<0x141>(v));
+        if constexpr (L >= 16) v = fmaxf(v, dpp_mov<0x140>(v));
+        if constexpr (L == 32) {
+            auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+            v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+        }
+        return v;
+    }
 }
 
 // ---------------------------------------------------------------- quantised output
@@ -238,15 +277,21 @@ constexpr bool row_pipelined() { return VPL * (FUSED ? 2 : 1) <= 4; }
 // covers 1 KiB of contiguous memory.  MASKED: the row has fewer than
 // 64*WPR*VPL vectors; loads are clamped in bounds (the extra values are
 // excluded from the sum) and stores skipped.
-template <class E, int WPR, int VPL, bool MASKED, bool FUSED, int QT = 0>
+//
+// LPR < 64 (with WPR 1): rows narrower than a wave share it, each row owning
+// an aligned group of LPR lanes (8, 16 or 32); the row sums are group sums,
+// with no LDS and no barrier.  A bf16 row of 128 (16 vectors) then keeps all
+// 64 lanes busy with 4 rows instead of leaving 48 lanes idle.
+template <class E, int WPR, int VPL, bool MASKED, bool FUSED, int QT = 0, int LPR = 64>
 __global__ void __launch_bounds__(max_threads<WPR>()) rms_vec_kernel(const RowArgs a) {
-    constexpr int LANES = 64 * WPR;
+    static_assert(LPR == 64 || WPR == 1, "sub-wave rows use one wave");
+    constexpr int LANES = LPR < 64 ? LPR : 64 * WPR;
     constexpr int V = E::kVec;
     constexpr int NR = FUSED ? VPL : 1;  // residual registers
     constexpr bool WRES = QT != 0 || weight_resident<WPR, VPL, FUSED>();
     constexpr bool PIPE = row_pipelined<VPL, FUSED>();
     const int wave = wave_id();
-    const int slot = wave / WPR;  // row within the workgroup
+    const int slot = LPR < 64 ? static_cast<int>(threadIdx.x) / LPR : wave / WPR;  // row within the workgroup
     const int lane_row = static_cast<int>(threadIdx.x) - slot * LANES;
     const int nvec = a.units;
     const int64_t rpb = a.rows_per_block;
@@ -329,8 +374,8 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_vec_kernel(const RowAr
                 }
             }
         }
-        ss = wave_sum(ss);
-        if constexpr (QT != 0) mx = wave_max(mx);
+        ss = group_sum<LPR>(ss);
+        if constexpr (QT != 0) mx = group_max<LPR>(mx);
         if constexpr (WPR > 1) {
             if ((threadIdx.x & 63) == 0) {
                 part[it & 1][wave] = ss;

@@ -100,7 +100,7 @@ def test_bad_forced_configs():
                 mbr.Config(mbr.PATH_VECTOR, 8, 2, 1, -1), mbr.Config(mbr.PATH_VECTOR, 1, 2, 1, 0),
                 mbr.Config(mbr.PATH_VECTOR, 16, 5, 1, 0), mbr.Config(mbr.PATH_VECTOR, 8, 9, 1, 0),
                 mbr.Config(mbr.PATH_ELEMENT, 4, 3, 1, 0), mbr.Config(mbr.PATH_ELEMENT, 1, 8, 1, 0),
-                mbr.Config(7, 8, 2, 1, 0)]:
+                mbr.Config(7, 8, 2, 1, 0), mbr.Config(mbr.PATH_VECTOR, 1, 1, 1, 0, 16)]:
         n = mbr.rmsnorm_bwd_workspace_size(rows, hidden, torch.bfloat16, cfg) if cfg.max_blocks >= 0 else 0
         st = L.rmsnorm_bwd_ex(X, W, G, D, DW, rows, hidden, 1e-5, 1, WS, n, ctypes.byref(cfg), None)
         assert st == INV, cfg

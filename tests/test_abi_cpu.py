@@ -152,6 +152,19 @@ def test_bad_forced_configs_rejected():
     assert call(1, 1, 4, 0) == INV            # zero rows per block
     assert call(1, 1, 4, 1, mb=-1) == INV
 
+    def sub(lpr, wpr, per, rpb, hidden=128, path=1):
+        cfg = mbr.Config(path, wpr, per, rpb, 0, lpr)
+        return L.rmsnorm_fwd_ex(A, W, O, 8, hidden, 1e-5, 1, ctypes.byref(cfg), None)
+
+    assert sub(12, 1, 1, 16) == INV           # lanes per row not built
+    assert sub(16, 2, 1, 8) == INV            # several rows per wave need waves_per_row 1
+    assert sub(16, 1, 3, 16) == INV           # 1 or 2 vectors per lane only
+    assert sub(8, 1, 1, 8) == INV             # 8 lanes x 1 vector do not cover 16 vectors
+    assert sub(16, 1, 1, 3) == INV            # 48 lanes: not whole waves
+    assert sub(16, 1, 1, 64) == INV           # 1024 lanes over the 512-lane bound
+    assert sub(16, 1, 1, 4, path=2) == INV    # element path has whole-wave rows only
+    assert sub(16, 1, 1, 4, path=3) == INV    # so has the two-pass path
+
 
 @pytest.mark.parametrize("name", list(inputs.WORKLOADS))
 def test_selection_for_the_workloads(name):
@@ -164,8 +177,8 @@ def test_selection_for_the_workloads(name):
     assert 64 * cfg.waves_per_row * cfg.rows_per_block <= (1024 if cfg.waves_per_row == 16 else 512)
 
 
-@pytest.mark.parametrize("hidden", [1, 3, 7, 8, 9, 127, 769, 2048, 4095, 5120, 5121, 8192, 8193, 16384,
-                                    65536, 81920, 131072, 1 << 20])
+@pytest.mark.parametrize("hidden", [1, 3, 7, 8, 9, 64, 96, 127, 128, 256, 264, 769, 2048, 4095, 5120, 5121, 8192,
+                                    8193, 16384, 65536, 81920, 131072, 1 << 20])
 @pytest.mark.parametrize("rows", [1, 5, 4096, 12289])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("aligned", [True, False])
@@ -174,6 +187,15 @@ def test_selection_is_always_a_built_covering_config(hidden, rows, dtype, aligne
     cfg = mbr.rmsnorm_select_config(rows, hidden, dtype, aligned, fused)
     vec = 4 if dtype == torch.float32 else 8
     assert cfg.waves_per_row in (1, 2, 4, 8, 16) and cfg.rows_per_block >= 1
+    if cfg.lanes_per_row:  # several rows per wave
+        lpr = cfg.lanes_per_row
+        assert cfg.path == mbr.PATH_VECTOR and aligned and hidden % vec == 0 and hidden // vec <= 32
+        assert lpr in (8, 16, 32) and cfg.waves_per_row == 1 and cfg.items_per_lane in (1, 2)
+        assert lpr * cfg.items_per_lane >= hidden // vec
+        assert (lpr * cfg.rows_per_block) % 64 == 0 and lpr * cfg.rows_per_block <= 512
+        per_wave = 64 // lpr
+        assert cfg.rows_per_block <= max(-(-rows // per_wave) * per_wave, per_wave)
+        return
     if cfg.path == mbr.PATH_VECTOR:
         assert aligned and hidden % vec == 0
         assert 64 * cfg.waves_per_row * cfg.items_per_lane >= hidden // vec

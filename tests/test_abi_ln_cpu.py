@@ -61,6 +61,6 @@ def test_pointer_validation_and_forced_configs():
     for cfg in [mbr.Config(mbr.PATH_VECTOR, 3, 2, 1, 0), mbr.Config(mbr.PATH_VECTOR, 4, 2, 2, 0),
                 mbr.Config(mbr.PATH_VECTOR, 16, 5, 1, 0), mbr.Config(mbr.PATH_VECTOR, 1, 2, 1, 0),
                 mbr.Config(mbr.PATH_ELEMENT, 4, 3, 1, 0), mbr.Config(mbr.PATH_VECTOR, 4, 2, 1, -1),
-                mbr.Config(9, 4, 2, 1, 0)]:
+                mbr.Config(9, 4, 2, 1, 0), mbr.Config(mbr.PATH_VECTOR, 1, 1, 1, 0, 32)]:
         import ctypes
         assert L.layernorm_fwd_ex(X, G, B, O, 4, 4096, 1e-5, 1, ctypes.byref(cfg), None) == INV, cfg

@@ -108,14 +108,21 @@ def test_odd_row_counts(dtype, fused):
         check_workload(w, inputs.make(w, seed=rows))
 
 
-def test_many_rows_in_kernel_loop():
-    """More row groups than the largest grid: workgroups loop over rows."""
-    rows = (1 << 20) * 4 + 3
-    w = inputs.custom(rows, 8, "bf16", False)
-    cfg = mbr.rmsnorm_select_config(rows, 8, BF16)
+@pytest.mark.parametrize("subwave", [False, True])
+def test_many_rows_in_kernel_loop(subwave):
+    """More row groups than the largest grid (2^20 workgroups): workgroups loop
+    over rows, with a whole wave per row and with 8 rows per wave."""
+    if subwave:
+        rows = (1 << 20) * 8 + 3
+        cfg = mbr.rmsnorm_select_config(rows, 8, BF16)
+        assert cfg.lanes_per_row == 8
+    else:
+        rows = (1 << 20) * 4 + 3
+        cfg = mbr.Config(mbr.PATH_VECTOR, 1, 1, 1, 0)
     assert (rows + cfg.rows_per_block - 1) // cfg.rows_per_block > (1 << 20)
+    w = inputs.custom(rows, 8, "bf16", False)
     say("many rows", rows, cfg)
-    check_workload(w, inputs.make(w, seed=5))
+    check_workload(w, inputs.make(w, seed=5), cfg)
 
 
 # ---------------------------------------------------------------- every built configuration
@@ -414,3 +421,47 @@ def test_hbm_copy_copies():
     mbr.hbm_copy(src, dst)
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
+
+
+# ---------------------------------------------------------------- rows narrower than a wave
+
+
+def subwave_configs():
+    """(lanes per row, vectors per lane, rows per workgroup) for every built
+    sub-wave kernel, at the smallest and the largest workgroup."""
+    out = []
+    for lpr in (8, 16, 32):
+        for vpl in (1, 2):
+            for rpb in (64 // lpr, 512 // lpr):
+                out.append((lpr, vpl, rpb))
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("fused", [False, True])
+def test_every_subwave_config(dtype, fused):
+    """Several rows per wave: exact and partial rows, a partial last group of
+    rows, and a capped grid that walks row groups."""
+    vecw = 8 if dtype == "bf16" else 4
+    n = 0
+    for lpr, vpl, rpb in subwave_configs():
+        for nvec in sorted({lpr * vpl, max(1, lpr * vpl - 3), lpr * (vpl - 1) + 1}):
+            for mb in (0, 2):
+                rows = 2 * rpb + 3
+                cfg = mbr.Config(mbr.PATH_VECTOR, 1, vpl, rpb, mb, lpr)
+                w = inputs.custom(rows, nvec * vecw, dtype, fused)
+                say("subwave", dtype, fused, cfg, "hidden", nvec * vecw, "rows", rows)
+                check_workload(w, inputs.make(w, seed=n), cfg)
+                n += 1
+    assert n > 50
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("hidden", [8, 16, 64, 96, 128, 200, 256])
+def test_narrow_rows_automatic(dtype, hidden):
+    """Narrow rows (per-head norms) at many rows take the sub-wave path."""
+    rows = 20001
+    cfg = mbr.rmsnorm_select_config(rows, hidden, BF16 if dtype == "bf16" else F32, True, False)
+    say("narrow", dtype, hidden, cfg)
+    w = inputs.custom(rows, hidden, dtype, False)
+    check_workload(w, inputs.make(w, seed=hidden))

@@ -175,3 +175,20 @@ def test_quant_rejects_overlaps_on_device_buffers():
                                      4, 256, 1e-5, 1, 0, torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert st == mbr.RMSNORM_ERR_INVALID_ARG and torch.count_nonzero(x) == 0
+
+
+@pytest.mark.parametrize("q", ["int8", "fp8"])
+@pytest.mark.parametrize("fused", [False, True])
+def test_every_subwave_quant_config(fused, q):
+    """Quantised output with several rows per wave (lanes_per_row 8, 16, 32)."""
+    n = 0
+    for dtype, vecw in (("bf16", 8), ("f32", 4)):
+        for lpr in (8, 16, 32):
+            for vpl in (1, 2):
+                for nvec, rpb in ((lpr * vpl, 64 // lpr), (max(1, lpr * vpl - 3), 512 // lpr)):
+                    cfg = mbr.Config(mbr.PATH_VECTOR, 1, vpl, rpb, 0, lpr)
+                    w = inputs.custom(2 * rpb + 3, nvec * vecw, dtype, fused)
+                    say("quant subwave", q, dtype, fused, cfg, "hidden", nvec * vecw)
+                    check(w, inputs.make(w, seed=n), QT[q], cfg)
+                    n += 1
+    assert n == 24
