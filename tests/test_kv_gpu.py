@@ -202,3 +202,16 @@ def test_kv_overlap_rejected_on_device_buffers():
         a = list(args)
         a[i] = bad
         assert L.kv_rmsnorm_rope_cache(*a) == INV, i
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_kv_non_finite_values(dtype):
+    """A NaN in a token's norm part makes that token's normalised row NaN and
+    leaves its rotated part alone; an Inf in the rotated part propagates through
+    the rotation of its own pair only."""
+    w, t, nc0, rc0 = _custom(dtype, 16, 2, 512, 64, 40, 256, 6, mbr.ROPE_PAIRS)
+    t["kv"][3, 1, 10] = float("nan")
+    t["kv"][7, 0, 512 + 5] = float("inf")
+    nc, rc = nc0.clone(), rc0.clone()
+    run_gpu(t, nc, rc, 1e-5, mbr.ROPE_PAIRS)
+    check(t, 1e-5, mbr.ROPE_PAIRS, dtype, nc0, rc0, nc, rc)

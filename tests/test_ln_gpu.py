@@ -203,3 +203,15 @@ def test_pages_layernorm_test_case_on_gpu():
     want = oracle_y = parity.oracle_ln(x, g, b, eps)
     parity.compare_ln(y, oracle_y, x, g, b, eps, mbr.layernorm_select_config(rows, hidden, F32, True))
     assert float(np.max(np.abs(y - want))) <= float(gd["f32_atol"])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ln_non_finite_rows(dtype):
+    """A NaN or an Inf in a row makes that row NaN (as in the oracle: the mean
+    and the variance are non-finite) and leaves the other rows alone."""
+    w = inputs.custom(9, 4096, dtype, layernorm=True)
+    for bad in (float("nan"), float("inf"), -float("inf")):
+        t = inputs.make(w, seed=5)
+        t["x"][4, 100] = bad
+        say("ln non-finite", dtype, bad)
+        check(w, t)
