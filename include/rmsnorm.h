@@ -272,8 +272,11 @@ RMSNORM_API rmsnorm_status_t rmsnorm_bwd(const void* x, const void* weight, cons
                                          void* stream);
 
 /* rmsnorm_bwd with a launch configuration (NULL or path AUTO = automatic).
- * rows_per_block must be 1; max_blocks caps the grid and is the number of
- * partial dweight rows (0 = no cap). */
+ * rows_per_block > 1 is accepted on path VECTOR only (64 * waves_per_row *
+ * rows_per_block threads within the limit of rmsnorm_config_t; with dweight,
+ * hidden * 4 bytes of LDS at most 60 KiB): the rows of a workgroup's slots then
+ * share one partial dweight row.  max_blocks caps the grid and is the number
+ * of partial dweight rows (0 = no cap). */
 RMSNORM_API rmsnorm_status_t rmsnorm_bwd_ex(const void* x, const void* weight, const void* dy, void* dx,
                                             void* dweight, int64_t rows, int64_t hidden, float eps,
                                             rmsnorm_dtype_t dtype, void* workspace, size_t workspace_bytes,
@@ -281,7 +284,8 @@ RMSNORM_API rmsnorm_status_t rmsnorm_bwd_ex(const void* x, const void* weight, c
 
 /* Bytes of workspace rmsnorm_bwd (cfg NULL or AUTO: any pointer alignment) or
  * rmsnorm_bwd_ex with cfg needs to produce dweight:
- * min(rows, partial rows) * round_up(hidden, 64) * 4.  No HIP call. */
+ * min(ceil(rows / rows_per_block), max_blocks) * round_up(hidden, 64) * 4.
+ * No HIP call. */
 RMSNORM_API rmsnorm_status_t rmsnorm_bwd_workspace_size(int64_t rows, int64_t hidden, rmsnorm_dtype_t dtype,
                                                         const rmsnorm_config_t* cfg, size_t* bytes);
 

@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdlib>
 #include <math.h>
 #include <stdint.h>
 
@@ -293,16 +294,22 @@ struct BwdProblem {
 // Floats per partial dweight row: hidden rounded up to 64 (256-byte rows).
 int64_t bwd_ld(int64_t hidden) { return (hidden + 63) / 64 * 64; }
 
-// Default grid of the backward walk: 512 workgroups (two per CU on MI355X),
-// the best of the sweeps on MI355X for every measured shape.  Fixed, not read
-// from the device, so that a shape's results (and its workspace size) are the
-// same on any GPU.
+// Grid cap of the backward walk with few rows and on the element and two-pass
+// paths: 512 workgroups (two per CU on MI355X).  Fixed, not read from the
+// device, so that a shape's results (and its workspace size) are the same on
+// any GPU.
 constexpr int64_t kBwdGrid = 512;
 
-// Partial dweight rows (= workgroups of the walk) for a configuration.
+// LDS the backward vector kernel may take for combining its row slots' sums
+// (the rest of the 64 KiB a workgroup can address holds its row totals).
+constexpr size_t kBwdCombineLds = 60 * 1024;
+
+// Partial dweight rows (= workgroups of the walk) for a configuration: one per
+// group of rows_per_block rows, at most max_blocks.
 int64_t bwd_partials(int64_t rows, const rmsnorm_config_t& c) {
     const int64_t cap = c.max_blocks > 0 ? c.max_blocks : kMaxGrid;
-    return rows < cap ? rows : cap;
+    const int64_t groups = ceil_div(rows, int64_t(c.rows_per_block > 0 ? c.rows_per_block : 1));
+    return groups < cap ? groups : cap;
 }
 
 bool bwd_vector_aligned(const BwdProblem& p) {
@@ -313,11 +320,21 @@ bool bwd_vector_aligned(const BwdProblem& p) {
     return true;
 }
 
-// With a capped grid the waves in flight are grid x waves per row, so a row
-// gets at least four waves (when it has two vectors or elements per lane to
-// spread) and lanes hold up to four 16-byte vectors (eight elements), more
-// waves when rows are few.  Sweeps on MI355X: bf16 hidden 8192 runs fastest as
-// 4 waves x 4 vectors, hidden 2048 as 4 x 1, both on 512 workgroups.
+// Vector path (sweeps on MI355X over bf16 / fp32, hidden 1024..8192, rows
+// 1024..16384), by the number of rows:
+//   * fewer than 1024: one row per workgroup, spread over more waves (up to
+//     2048 waves in all);
+//   * 1024 .. 8191, rows of at most 512 vectors: one wave per row holding the
+//     whole row (up to eight vectors per lane), four row slots per workgroup
+//     (eight for rows of at most 128 vectors) and 256 workgroups: few partial
+//     dweight rows, and every lane's loads in flight at once;
+//   * otherwise: the waves per row that leave the fewest lanes past the row
+//     end with at most six vectors per lane, ties going to four vectors per
+//     lane (bf16 hidden 5120: 2 waves x 5, not 4 x 3 with a sixth of the
+//     lanes idle, 9% faster); workgroups of four waves filled with row
+//     slots; 512 workgroups.
+// Element path: at least four waves per row (when a row has two elements per
+// lane to spread), up to eight elements per lane.
 rmsnorm_config_t choose_bwd(int64_t rows, int64_t hidden, int dtype, bool aligned) {
     rmsnorm_config_t c = {RMSNORM_PATH_TWO_PASS, 16, 0, 1, static_cast<int32_t>(kBwdGrid)};
     const bool vec = aligned && hidden % vec_elems(dtype) == 0;
@@ -325,15 +342,33 @@ rmsnorm_config_t choose_bwd(int64_t rows, int64_t hidden, int dtype, bool aligne
     const int* list = vec ? mbr::kBwdVplList : mbr::kBwdEplList;
     const int nlist = vec ? mbr::kNumBwdVpl : mbr::kNumBwdEpl;
     const int cap = vec ? 4 : 8;
+    const bool few = rows < 1024;
     auto fit = [&](int wpr) {
         const int per = round_up_in(list, nlist, ceil_div(units, int64_t(64) * wpr));
         if (per < 0) return -1;
         return (!vec || mbr::bwd_vec_built(wpr, per)) ? per : -1;
     };
+    const bool whole_row = vec && !few && rows < 8192 && units <= 512;
+    const bool balanced = vec && !few && !whole_row;
     int wpr = 1;
-    while (wpr < 16 && ceil_div(units, int64_t(64) * wpr) > cap) wpr *= 2;
-    while (wpr < 4 && units >= int64_t(64) * wpr * 2) wpr *= 2;
-    while (wpr < 16 && rows < 2048 / wpr && units >= int64_t(64) * wpr * 2) wpr *= 2;
+    if (balanced) {
+        int64_t best_pad = -1;
+        int best_v = 0;
+        for (int w = 1; w <= 16; w *= 2) {
+            const int v = fit(w);
+            if (v < 0 || v > 6) continue;
+            const int64_t pad = int64_t(64) * w * v - units;
+            if (best_pad < 0 || pad < best_pad || (pad == best_pad && std::abs(v - 4) < std::abs(best_v - 4))) {
+                wpr = w;
+                best_pad = pad;
+                best_v = v;
+            }
+        }
+    } else if (!whole_row) {
+        while (wpr < 16 && ceil_div(units, int64_t(64) * wpr) > cap) wpr *= 2;
+        while (!vec && wpr < 4 && units >= int64_t(64) * wpr * 2) wpr *= 2;
+        while (wpr < 16 && rows < 2048 / wpr && units >= int64_t(64) * wpr * 2) wpr *= 2;
+    }
     int per = fit(wpr);
     while (per < 0 && wpr < 16) {
         wpr *= 2;
@@ -343,6 +378,13 @@ rmsnorm_config_t choose_bwd(int64_t rows, int64_t hidden, int dtype, bool aligne
     c.path = vec ? RMSNORM_PATH_VECTOR : RMSNORM_PATH_ELEMENT;
     c.waves_per_row = wpr;
     c.items_per_lane = per;
+    if (whole_row) {
+        c.rows_per_block = units <= 128 ? 8 : 4;
+        c.max_blocks = 256;
+    } else if (balanced) {
+        c.rows_per_block = wpr < 4 ? 4 / wpr : 1;
+        c.max_blocks = 512;
+    }
     return c;
 }
 
@@ -375,10 +417,11 @@ rmsnorm_status_t validate_bwd_pointers(const BwdProblem& p, int64_t ws_need) {
     return RMSNORM_OK;
 }
 
-rmsnorm_status_t launch_checked(const void* fn, int64_t grid, int64_t threads, void* arg, hipStream_t stream) {
+rmsnorm_status_t launch_checked(const void* fn, int64_t grid, int64_t threads, void* arg, hipStream_t stream,
+                                size_t lds_bytes = 0) {
     void* args[] = {arg};
     const hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(grid)), dim3(static_cast<unsigned>(threads)),
-                                         args, 0, stream);
+                                         args, lds_bytes, stream);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         return RMSNORM_ERR_RUNTIME;
@@ -393,7 +436,8 @@ rmsnorm_status_t run_bwd(const BwdProblem& p, const rmsnorm_config_t* user, void
     const rmsnorm_config_t c =
         (user && user->path != RMSNORM_PATH_AUTO) ? *user : choose_bwd(p.rows, p.hidden, p.dtype, aligned);
     const int wi = index_of(mbr::kWprList, mbr::kNumWpr, c.waves_per_row);
-    if (wi < 0 || c.rows_per_block != 1 || c.max_blocks < 0) return RMSNORM_ERR_INVALID_ARG;
+    if (wi < 0 || c.rows_per_block < 1 || c.max_blocks < 0) return RMSNORM_ERR_INVALID_ARG;
+    if (c.rows_per_block > 1 && c.path != RMSNORM_PATH_VECTOR) return RMSNORM_ERR_INVALID_ARG;
     if (c.lanes_per_row != 0 && c.lanes_per_row != 64 * c.waves_per_row) return RMSNORM_ERR_INVALID_ARG;
     const bool dw = p.dw != nullptr;
     const int64_t ws_need = dw ? bwd_workspace_need(p.rows, p.hidden, c) : 0;
@@ -403,7 +447,7 @@ rmsnorm_status_t run_bwd(const BwdProblem& p, const rmsnorm_config_t* user, void
         if (!dw) return RMSNORM_OK;
         if (reinterpret_cast<uintptr_t>(p.dw) % elem_size(p.dtype) != 0) return RMSNORM_ERR_INVALID_ARG;
         mbr::DwArgs d = {nullptr, p.dw, bwd_ld(p.hidden), 0, static_cast<int32_t>(p.hidden)};
-        return launch_checked(mbr::bwd_dw_kernel(p.dtype), ceil_div(d.ld, mbr::kDwCols), 1024, &d, stream);
+        return launch_checked(mbr::bwd_dw_kernel(p.dtype), ceil_div(d.ld, mbr::kDwCols), mbr::kDwThreads, &d, stream);
     }
     s = validate_bwd_pointers(p, ws_need);
     if (s != RMSNORM_OK) return s;
@@ -416,11 +460,14 @@ rmsnorm_status_t run_bwd(const BwdProblem& p, const rmsnorm_config_t* user, void
     a.dx = p.dx;
     a.part = static_cast<float*>(p.ws);
     a.rows = p.rows;
+    a.rows_per_block = c.rows_per_block;
+    a.n_groups = ceil_div(p.rows, int64_t(c.rows_per_block));
     a.ld = bwd_ld(p.hidden);
     a.hidden_f = static_cast<float>(p.hidden);
     a.eps = p.eps;
     const void* fn = nullptr;
-    int64_t threads = lanes;
+    const int64_t threads = lanes * c.rows_per_block;
+    size_t lds = 0;
     switch (c.path) {
         case RMSNORM_PATH_VECTOR: {
             if (!aligned || p.hidden % vec_elems(p.dtype) != 0) return RMSNORM_ERR_INVALID_ARG;
@@ -430,6 +477,9 @@ rmsnorm_status_t run_bwd(const BwdProblem& p, const rmsnorm_config_t* user, void
             if (threads > mbr::max_threads_for(c.waves_per_row)) return RMSNORM_ERR_INVALID_ARG;
             fn = mbr::bwd_vec_kernel(p.dtype, dw, lanes * c.items_per_lane != nvec, wi, vi);
             a.units = static_cast<int32_t>(nvec);
+            // several row slots combine their dweight sums in LDS: hidden floats
+            if (dw && c.rows_per_block > 1) lds = static_cast<size_t>(p.hidden) * 4;
+            if (lds > kBwdCombineLds) return RMSNORM_ERR_INVALID_ARG;
             break;
         }
         case RMSNORM_PATH_ELEMENT: {
@@ -451,7 +501,7 @@ rmsnorm_status_t run_bwd(const BwdProblem& p, const rmsnorm_config_t* user, void
     }
     if (!fn) return RMSNORM_ERR_INVALID_ARG;
     const int64_t grid = bwd_partials(p.rows, c);
-    s = launch_checked(fn, grid, threads, &a, stream);
+    s = launch_checked(fn, grid, threads, &a, stream, lds);
     if (s != RMSNORM_OK) return s;
     if (dw) {
         mbr::DwArgs d;
@@ -460,7 +510,7 @@ rmsnorm_status_t run_bwd(const BwdProblem& p, const rmsnorm_config_t* user, void
         d.ld = a.ld;
         d.n_part = static_cast<int32_t>(grid);
         d.hidden = static_cast<int32_t>(p.hidden);
-        s = launch_checked(mbr::bwd_dw_kernel(p.dtype), ceil_div(a.ld, mbr::kDwCols), 1024, &d, stream);
+        s = launch_checked(mbr::bwd_dw_kernel(p.dtype), ceil_div(a.ld, mbr::kDwCols), mbr::kDwThreads, &d, stream);
     }
     return s;
 }

@@ -34,8 +34,10 @@ struct BwdArgs {
     void* dx;
     float* part;     // DW: [gridDim.x][ld] fp32 partial dweight rows
     int64_t rows;
-    int64_t ld;      // floats per partial row (a multiple of 64, >= hidden)
-    int32_t units;   // per row: 16-byte vectors (vector path) or elements
+    int64_t n_groups;        // ceil(rows / rows_per_block)
+    int64_t ld;              // floats per partial row (a multiple of 64, >= hidden)
+    int32_t units;           // per row: 16-byte vectors (vector path) or elements
+    int32_t rows_per_block;  // vector path: rows a workgroup works on at once
     float hidden_f;
     float eps;
 };
@@ -48,10 +50,12 @@ struct DwArgs {
     int32_t hidden;
 };
 
-// Row totals of both sums, identical bits in every lane of the row.
+// Row totals of both sums, identical bits in every lane of the row; the row
+// occupies waves slot*WPR .. slot*WPR + WPR - 1 of the workgroup.  Every wave
+// of the workgroup reaches the barrier once per call.
 template <int WPR>
 __device__ __forceinline__ void row_sums(float& ss, float& cc, float (&ps)[2][16], float (&pc)[2][16], int it,
-                                         int wave) {
+                                         int wave, int slot = 0) {
     ss = wave_sum(ss);
     cc = wave_sum(cc);
     if constexpr (WPR > 1) {
@@ -64,8 +68,8 @@ __device__ __forceinline__ void row_sums(float& ss, float& cc, float (&ps)[2][16
         cc = 0.f;
 #pragma unroll
         for (int i = 0; i < WPR; ++i) {
-            ss += ps[it & 1][i];
-            cc += pc[it & 1][i];
+            ss += ps[it & 1][slot * WPR + i];
+            cc += pc[it & 1][slot * WPR + i];
         }
     }
 }
@@ -87,19 +91,23 @@ __device__ __forceinline__ void store_partial(float* p, const float* acc, F32) {
     reinterpret_cast<f32x4*>(p)[0] = a;
 }
 
-// Vector path: WPR waves per row (one row per workgroup at a time), VPL
-// 16-byte vectors per lane, lane l owning vectors l, l + 64*WPR, ... of both
-// x and dy; the weight slice stays in registers for the whole walk.  When the
-// row slice is small the next row's x and dy are loaded before the current
-// row is reduced, so memory stays busy across the barrier.
+// Vector path: WPR waves per row, VPL 16-byte vectors per lane, lane l of a
+// row owning vectors l, l + 64*WPR, ... of both x and dy; the weight slice
+// stays in registers for the whole walk.  A workgroup holds rows_per_block
+// row slots; in each step of its walk slot s takes row group*rows_per_block +
+// s.  With several slots, the slots' dweight sums are combined in LDS, in slot
+// order, into the workgroup's single partial row: fewer partial rows for the
+// same number of waves in flight.  (A conditional next-row prefetch measured
+// the same as none: the compiler waits for every load after the branch.)
 template <class E, int WPR, int VPL, bool MASKED, bool DW>
 __global__ void __launch_bounds__(max_threads<WPR>()) rms_bwd_vec_kernel(const BwdArgs a) {
     constexpr int LANES = 64 * WPR;
     constexpr int V = E::kVec;
-    constexpr bool PIPE = VPL <= 2;
     const int wave = wave_id();
-    const int lane = static_cast<int>(threadIdx.x);
+    const int slot = wave / WPR;
+    const int lane = static_cast<int>(threadIdx.x) - slot * LANES;
     const int nvec = a.units;
+    const int rpb = a.rows_per_block;
     __shared__ float ps[2][16], pc[2][16];
 
     // Byte offset of a lane's k-th vector within a row: unsigned 32-bit, so
@@ -114,14 +122,6 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_bwd_vec_kernel(const B
     };
     auto in_row = [&](int k) { return !MASKED || k * LANES + lane < nvec; };
     const int64_t row_bytes = static_cast<int64_t>(nvec) * 16;
-    auto load_row = [&](int64_t row, u32x4 (&xv)[VPL], u32x4 (&gv)[VPL]) {
-        const char* xr = static_cast<const char*>(a.x) + row * row_bytes;
-        const char* gr = static_cast<const char*>(a.dy) + row * row_bytes;
-#pragma unroll
-        for (int k = 0; k < VPL; ++k) xv[k] = load_stream(at(xr, voff(k)));
-#pragma unroll
-        for (int k = 0; k < VPL; ++k) gv[k] = load_stream(at(gr, voff(k)));
-    };
 
     u32x4 wv[VPL];
 #pragma unroll
@@ -132,40 +132,37 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_bwd_vec_kernel(const B
         for (int i = 0; i < VPL * V; ++i) acc[i] = 0.f;
     }
 
-    int64_t row = blockIdx.x;
-    u32x4 nx[PIPE ? VPL : 1], ng[PIPE ? VPL : 1];
-    if constexpr (PIPE) {
-        if (row < a.rows) load_row(row, nx, ng);
-    }
-    for (int it = 0; row < a.rows; row += gridDim.x, ++it) {
+    int it = 0;
+    for (int64_t grp = blockIdx.x; grp < a.n_groups; grp += gridDim.x, ++it) {
+        const int64_t row = grp * rpb + slot;
+        const bool valid = row < a.rows;
         u32x4 xv[VPL], gv[VPL];
-        if constexpr (PIPE) {
+        float ss = 0.f, cc = 0.f;
+        if (valid) {
+            const char* xr = static_cast<const char*>(a.x) + row * row_bytes;
+            const char* gr = static_cast<const char*>(a.dy) + row * row_bytes;
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) xv[k] = load_stream(at(xr, voff(k)));
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) gv[k] = load_stream(at(gr, voff(k)));
 #pragma unroll
             for (int k = 0; k < VPL; ++k) {
-                xv[k] = nx[k];
-                gv[k] = ng[k];
-            }
-            if (row + gridDim.x < a.rows) load_row(row + gridDim.x, nx, ng);
-        } else {
-            load_row(row, xv, gv);
-        }
-        float ss = 0.f, cc = 0.f;
+                float fx[V], fg[V], fw[V];
+                widen(xv[k], fx, E{});
+                widen(gv[k], fg, E{});
+                widen(wv[k], fw, E{});
+                float s = 0.f, c = 0.f;
 #pragma unroll
-        for (int k = 0; k < VPL; ++k) {
-            float fx[V], fg[V], fw[V];
-            widen(xv[k], fx, E{});
-            widen(gv[k], fg, E{});
-            widen(wv[k], fw, E{});
-            float s = 0.f, c = 0.f;
-#pragma unroll
-            for (int i = 0; i < V; ++i) {
-                s += fx[i] * fx[i];
-                c += (fg[i] * fw[i]) * fx[i];
+                for (int i = 0; i < V; ++i) {
+                    s += fx[i] * fx[i];
+                    c += (fg[i] * fw[i]) * fx[i];
+                }
+                ss += in_row(k) ? s : 0.f;
+                cc += in_row(k) ? c : 0.f;
             }
-            ss += in_row(k) ? s : 0.f;
-            cc += in_row(k) ? c : 0.f;
         }
-        row_sums<WPR>(ss, cc, ps, pc, it, wave);
+        row_sums<WPR>(ss, cc, ps, pc, it, wave, slot);
+        if (!valid) continue;
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             repack(xv[k]);
@@ -193,9 +190,30 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_bwd_vec_kernel(const B
     }
     if constexpr (DW) {
         float* pr = a.part + static_cast<int64_t>(blockIdx.x) * a.ld;
+        if (rpb == 1) {
 #pragma unroll
-        for (int k = 0; k < VPL; ++k)
-            if (in_row(k)) store_partial(pr + static_cast<int64_t>(k * LANES + lane) * V, acc + k * V, E{});
+            for (int k = 0; k < VPL; ++k)
+                if (in_row(k)) store_partial(pr + static_cast<int64_t>(k * LANES + lane) * V, acc + k * V, E{});
+            return;
+        }
+        // slots add their sums into one LDS row in slot order, then the whole
+        // workgroup writes it out
+        extern __shared__ float comb[];  // nvec * V floats
+        for (int s = 0; s < rpb; ++s) {
+            if (slot == s) {
+#pragma unroll
+                for (int k = 0; k < VPL; ++k) {
+                    if (!in_row(k)) continue;
+                    float* c = comb + (k * LANES + lane) * V;
+#pragma unroll
+                    for (int i = 0; i < V; ++i) c[i] = s == 0 ? acc[k * V + i] : c[i] + acc[k * V + i];
+                }
+            }
+            __syncthreads();
+        }
+        const int nq = nvec * V / 4;
+        for (int j = static_cast<int>(threadIdx.x); j < nq; j += blockDim.x)
+            reinterpret_cast<f32x4*>(pr)[j] = reinterpret_cast<const f32x4*>(comb)[j];
     }
 }
 
@@ -342,18 +360,32 @@ __global__ void __launch_bounds__(1024) rms_bwd_twopass_kernel(const BwdArgs a) 
 }
 
 // Second stage of dweight: workgroup b sums the columns of kDwQuads column
-// quads (4 fp32 columns each) over the n_part partial rows.  Thread (s, q),
-// s = tid / kDwQuads, q = tid % kDwQuads, adds partial rows s, s + S, s + 2S,
-// ... (S = 1024 / kDwQuads slices) of its quad in that order; the S slice sums
-// are then combined by a fixed pairwise tree in LDS, and the total is rounded
-// once to the tensor dtype.  n_part == 0 writes zeros.
+// quads (4 fp32 columns each) over the n_part partial rows.  Thread t of the
+// workgroup takes quad q = t % kDwQuads and slice s = t / kDwQuads, and adds
+// partial rows s, s + S, s + 2S, ... (S = kDwSlices) of its quad in that
+// order (loads issued four at a time).  The S slice sums are then combined
+// by a fixed tree: a butterfly over the slices held by one wave (lane
+// exchanges at distances kDwQuads, 2 kDwQuads, ..., 32), then the waves'
+// totals added in wave order through LDS; the total is rounded once to the
+// tensor dtype.  n_part == 0 writes zeros.  A workgroup reads 128 bytes of
+// each partial row: narrower tiles measured slower on MI355X, since
+// neighbouring workgroups (usually on different XCDs) then fetch the same
+// cache lines.
+constexpr int kDwThreads = 512;
 constexpr int kDwQuads = 8;
-constexpr int kDwSlices = 1024 / kDwQuads;
+constexpr int kDwSlices = kDwThreads / kDwQuads;
 constexpr int kDwCols = 4 * kDwQuads;  // columns per workgroup
 static_assert(64 % kDwCols == 0, "a workgroup's columns must not cross the end of a 64-float partial row");
 
+__device__ __forceinline__ f32x4 shfl_xor4(f32x4 v, int m) {
+    f32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = __shfl_xor(v[i], m);
+    return r;
+}
+
 template <class E>
-__global__ void __launch_bounds__(1024) rms_bwd_dw_kernel(const DwArgs a) {
+__global__ void __launch_bounds__(kDwThreads) rms_bwd_dw_kernel(const DwArgs a) {
     using S = typename E::scalar;
     const int q = threadIdx.x % kDwQuads;
     const int s = threadIdx.x / kDwQuads;
@@ -361,17 +393,29 @@ __global__ void __launch_bounds__(1024) rms_bwd_dw_kernel(const DwArgs a) {
     const f32x4* col = reinterpret_cast<const f32x4*>(a.part) + quad;
     const int64_t stride = a.ld / 4;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int p = s; p < a.n_part; p += kDwSlices) acc += col[p * stride];
-    __shared__ f32x4 sm[kDwSlices][kDwQuads];
-    sm[s][q] = acc;
-    __syncthreads();
-#pragma unroll
-    for (int st = kDwSlices / 2; st >= 1; st >>= 1) {
-        if (s < st) sm[s][q] += sm[s + st][q];
-        __syncthreads();
+    int p = s;
+    for (; p + 3 * kDwSlices < a.n_part; p += 4 * kDwSlices) {
+        const f32x4 v0 = col[p * stride];
+        const f32x4 v1 = col[(p + kDwSlices) * stride];
+        const f32x4 v2 = col[(p + 2 * kDwSlices) * stride];
+        const f32x4 v3 = col[(p + 3 * kDwSlices) * stride];
+        acc += v0;
+        acc += v1;
+        acc += v2;
+        acc += v3;
     }
-    if (s == 0) {
-        const f32x4 t = sm[0][q];
+    for (; p < a.n_part; p += kDwSlices) acc += col[p * stride];
+#pragma unroll
+    for (int m = kDwQuads; m < 64; m <<= 1) acc += shfl_xor4(acc, m);
+    constexpr int kWaves = kDwThreads / 64;
+    __shared__ f32x4 sm[kWaves][kDwQuads];
+    const int lane = threadIdx.x & 63;
+    if (lane < kDwQuads) sm[threadIdx.x / 64][lane] = acc;
+    __syncthreads();
+    if (threadIdx.x < kDwQuads) {
+        f32x4 t = sm[0][q];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) t += sm[w][q];
         S* out = static_cast<S*>(a.dw);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {

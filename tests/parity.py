@@ -214,11 +214,12 @@ def oracle_quant(x, w, eps, qtype, residual=None):
 #     gamma = (2L + 16)*u.  The two terms can cancel, so the bound is on M_k,
 #     not on |dx_k|; both sides then round once, which adds at most one unit
 #     in the last place of the dtype.
-#   * dw_j = sum_i dy_ij*x_ij*r_i is summed per lane over ceil(rows/G) rows (G
-#     partial rows), then over ceil(G/64) partial rows per slice and a 6-level
+#   * dw_j = sum_i dy_ij*x_ij*r_i is summed per lane over ceil(ceil(rows/R)/G)
+#     rows (R row slots per workgroup, G partial rows), the R slot sums are
+#     added in slot order, then ceil(G/64) partial rows per slice and a 7-level
 #     tree: absolute error below gamma_w * A_j, A_j = sum_i |dy_ij*x_ij|*r_i,
-#     gamma_w = 2*(ceil(rows/G) + ceil(G/64) + L/2 + 12)*u (factor 2 for the
-#     per-term errors and margin); plus one unit in the last place.
+#     gamma_w = 2*(ceil(ceil(rows/R)/G) + R + ceil(G/64) + L/2 + 12)*u (factor
+#     2 for the per-term errors and margin); plus one unit in the last place.
 # M and A are magnitudes computed here in fp64 for the bound only; the values
 # compared against are the oracle's.
 
@@ -300,7 +301,8 @@ def compare_bwd(dx_gpu, dw_gpu, dx_want, dw_want, x, w, dy, eps, cfg, n_part) ->
     check_magnitude(dx_gpu, dx_want, M, (2 * L + 16) * U, bf16, "dx", stats)
     if dw_want is not None:
         g = max(1, n_part)
-        gamma_w = 2 * (-(-rows // g) + -(-g // 64) + L / 2 + 12) * U
+        R = max(1, getattr(cfg, "rows_per_block", 1))
+        gamma_w = 2 * (-(-(-(-rows // R)) // g) + R + -(-g // 64) + L / 2 + 12) * U
         check_magnitude(dw_gpu, dw_want, A, gamma_w, bf16, "dw", stats)
     return stats
 

@@ -39,10 +39,15 @@ def test_workspace_size_formula():
                              (16384, 8192, torch.bfloat16), (5, 131080, torch.float32), (70000, 96, torch.float32)]:
         need = mbr.rmsnorm_bwd_workspace_size(rows, hidden, dt)
         ld = (hidden + 63) // 64 * 64
-        caps = [mbr.rmsnorm_select_bwd_config(rows, hidden, dt, a).max_blocks for a in (True, False)]
-        assert need == max(min(rows, c) for c in caps) * ld * 4
+        cfgs = [mbr.rmsnorm_select_bwd_config(rows, hidden, dt, a) for a in (True, False)]
+        assert need == max(min(-(-rows // c.rows_per_block), c.max_blocks) for c in cfgs) * ld * 4
         cfg = mbr.Config(mbr.PATH_ELEMENT, 4, 8, 1, 3)
         assert mbr.rmsnorm_bwd_workspace_size(rows, hidden, dt, cfg) == min(rows, 3) * ld * 4
+        # row slots share a partial row: one per group of rows_per_block rows
+        for rpb, mb in ((4, 3), (4, 0), (2, 1000)):
+            cfg = mbr.Config(mbr.PATH_VECTOR, 2, 2, rpb, mb)
+            groups = -(-rows // rpb)
+            assert mbr.rmsnorm_bwd_workspace_size(rows, hidden, dt, cfg) == (min(groups, mb) if mb else groups) * ld * 4
     assert mbr.lib().rmsnorm_bwd_workspace_size(4, 16, 1, None, None) == INV
     bad = mbr.Config(mbr.PATH_VECTOR, 4, 2, 1, -1)
     assert mbr.lib().rmsnorm_bwd_workspace_size(4, 16, 1, ctypes.byref(bad), ctypes.byref(ctypes.c_size_t())) == INV
@@ -51,8 +56,14 @@ def test_workspace_size_formula():
 def test_headline_choice():
     c = mbr.rmsnorm_select_bwd_config(16384, 8192, torch.bfloat16, True)
     assert (c.path, c.waves_per_row, c.items_per_lane, c.rows_per_block, c.max_blocks) == (mbr.PATH_VECTOR, 4, 4, 1, 512)
+    # narrower rows: four vectors per lane, four row slots, 256 partial rows
     c = mbr.rmsnorm_select_bwd_config(4096, 2048, torch.bfloat16, True)
-    assert (c.path, c.waves_per_row, c.items_per_lane, c.max_blocks) == (mbr.PATH_VECTOR, 4, 1, 512)
+    assert (c.path, c.waves_per_row, c.items_per_lane, c.rows_per_block, c.max_blocks) == (mbr.PATH_VECTOR, 1, 4, 4, 256)
+    c = mbr.rmsnorm_select_bwd_config(16384, 4096, torch.bfloat16, True)
+    assert (c.path, c.waves_per_row, c.items_per_lane, c.rows_per_block, c.max_blocks) == (mbr.PATH_VECTOR, 2, 4, 2, 512)
+    # few rows: one row per workgroup, spread over more waves
+    c = mbr.rmsnorm_select_bwd_config(64, 2048, torch.float32, True)
+    assert (c.path, c.waves_per_row, c.items_per_lane, c.rows_per_block) == (mbr.PATH_VECTOR, 8, 1, 1)
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
@@ -63,7 +74,9 @@ def test_choice_is_built_and_covering(dtype, aligned, rows):
     for hidden in [1, 7, 8, 64, 100, 1000, 2048, 4095, 4096, 5120, 8192, 16384, 32768, 32776, 65536, 131080]:
         c = mbr.rmsnorm_select_bwd_config(rows, hidden, dtype, aligned)
         lanes = 64 * c.waves_per_row
-        assert c.rows_per_block == 1 and c.max_blocks >= 1 and c.waves_per_row in (1, 2, 4, 8, 16)
+        assert c.max_blocks >= 1 and c.waves_per_row in (1, 2, 4, 8, 16)
+        assert c.rows_per_block == 1 or (c.path == mbr.PATH_VECTOR and lanes * c.rows_per_block <= 512
+                                         and hidden * 4 <= 60 * 1024)
         if c.path == mbr.PATH_VECTOR:
             assert aligned and hidden % v == 0
             assert c.items_per_lane in range(1, 9) and (c.waves_per_row < 16 or c.items_per_lane <= 4)
@@ -100,10 +113,18 @@ def test_bad_forced_configs():
                 mbr.Config(mbr.PATH_VECTOR, 8, 2, 1, -1), mbr.Config(mbr.PATH_VECTOR, 1, 2, 1, 0),
                 mbr.Config(mbr.PATH_VECTOR, 16, 5, 1, 0), mbr.Config(mbr.PATH_VECTOR, 8, 9, 1, 0),
                 mbr.Config(mbr.PATH_ELEMENT, 4, 3, 1, 0), mbr.Config(mbr.PATH_ELEMENT, 1, 8, 1, 0),
-                mbr.Config(7, 8, 2, 1, 0), mbr.Config(mbr.PATH_VECTOR, 1, 1, 1, 0, 16)]:
+                mbr.Config(7, 8, 2, 1, 0), mbr.Config(mbr.PATH_VECTOR, 1, 1, 1, 0, 16),
+                # row slots: vector path only, within the thread limit
+                mbr.Config(mbr.PATH_VECTOR, 4, 2, 0, 0), mbr.Config(mbr.PATH_VECTOR, 4, 2, 3, 0),
+                mbr.Config(mbr.PATH_VECTOR, 2, 4, 8, 0), mbr.Config(mbr.PATH_ELEMENT, 4, 8, 2, 0),
+                mbr.Config(mbr.PATH_TWO_PASS, 16, 0, 2, 0)]:
         n = mbr.rmsnorm_bwd_workspace_size(rows, hidden, torch.bfloat16, cfg) if cfg.max_blocks >= 0 else 0
         st = L.rmsnorm_bwd_ex(X, W, G, D, DW, rows, hidden, 1e-5, 1, WS, n, ctypes.byref(cfg), None)
         assert st == INV, cfg
+    # slots combine dweight in LDS: hidden * 4 bytes, at most 60 KiB
+    cfg = mbr.Config(mbr.PATH_VECTOR, 4, 8, 2, 0)
+    n = mbr.rmsnorm_bwd_workspace_size(rows, 16384, torch.bfloat16, cfg)
+    assert L.rmsnorm_bwd_ex(X, W, G, D, DW, rows, 16384, 1e-5, 1, WS, n, ctypes.byref(cfg), None) == INV
     # vector path on an unaligned buffer
     cfg = mbr.Config(mbr.PATH_VECTOR, 8, 1, 1, 0)
     st = L.rmsnorm_bwd_ex(X + 2, W, G, D, None, rows, hidden, 1e-5, 1, None, 0, ctypes.byref(cfg), None)

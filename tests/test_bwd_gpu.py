@@ -47,7 +47,7 @@ def effective_config(rows, hidden, dtype, cfg=None, aligned=True):
 
 def n_partials(rows, cfg):
     cap = cfg.max_blocks if cfg.max_blocks > 0 else 1 << 20
-    return min(rows, cap)
+    return min(-(-rows // max(1, cfg.rows_per_block)), cap)
 
 
 def check(w, t, cfg=None, eps=None, want_dw=True):
@@ -120,6 +120,43 @@ def test_bwd_every_vector_config(dtype):
                 check(w, inputs.make(w, seed=n), cfg, want_dw=(n % 3 != 2))
                 n += 1
     assert n > 150
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_rows_per_block_configs(dtype):
+    """Several row slots per workgroup on every built vector configuration
+    that fits the thread limit: rows not a multiple of the slot count, slots
+    with no row at all, masked rows, and caps that make each workgroup walk
+    several groups; dx-only calls every third case."""
+    vecw = 8 if dtype == "bf16" else 4
+    n = 0
+    for wpr, vpl in _built_vec():
+        for rpb in {1: (2, 3, 8), 2: (2, 4), 4: (2,)}.get(wpr, ()):
+            lanes = 64 * wpr
+            for nvec in sorted({lanes * vpl, max(1, lanes * (vpl - 1) + 3)}):
+                if nvec * vecw * 4 > 60 * 1024:
+                    continue  # the LDS combine limit (checked on the CPU)
+                for mb, rows in ((0, rpb + 1), (2, 5 * rpb + 2), (0, 1)):
+                    cfg = mbr.Config(mbr.PATH_VECTOR, wpr, vpl, rpb, mb)
+                    w = inputs.custom(rows, nvec * vecw, dtype, backward=True)
+                    say("bwd slots", dtype, cfg, "hidden", nvec * vecw, "rows", rows)
+                    check(w, inputs.make(w, seed=1000 + n), cfg, want_dw=(n % 3 != 2))
+                    n += 1
+    assert n > 100
+
+
+def test_bwd_rows_per_block_many_groups_deterministic():
+    """A capped grid over many rows with row slots: parity, and the same bits
+    on a second call."""
+    w = inputs.custom(20000, 2048, "bf16", backward=True)
+    cfg = mbr.Config(mbr.PATH_VECTOR, 2, 2, 4, 128)
+    say("bwd slots many groups", cfg)
+    t = inputs.make(w, seed=7)
+    check(w, t, cfg)
+    dev = {k: v.cuda() for k, v in t.items()}
+    a = run_bwd(dev["x"], dev["weight"], dev["dy"], w.eps, cfg)
+    b = run_bwd(dev["x"], dev["weight"], dev["dy"], w.eps, cfg)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -237,7 +274,7 @@ def test_bwd_workspace_checked_on_device_buffers():
     dw = torch.empty_like(wt)
     need = mbr.rmsnorm_bwd_workspace_size(rows, hidden, BF16)
     cfg = effective_config(rows, hidden, "bf16")
-    assert need == min(rows, cfg.max_blocks) * 1024 * 4
+    assert need == n_partials(rows, cfg) * 1024 * 4
     ws = torch.empty(need + 64, dtype=torch.uint8, device="cuda")
     L, s = mbr.lib(), torch.cuda.current_stream().cuda_stream
     args = (x.data_ptr(), wt.data_ptr(), dy.data_ptr(), dx.data_ptr(), dw.data_ptr(), rows, hidden, 1e-5, 1)
