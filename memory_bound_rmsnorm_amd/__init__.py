@@ -59,7 +59,8 @@ class Config(ctypes.Structure):
     """rmsnorm_config_t."""
     _fields_ = [("path", ctypes.c_int32), ("waves_per_row", ctypes.c_int32),
                 ("items_per_lane", ctypes.c_int32), ("rows_per_block", ctypes.c_int32),
-                ("max_blocks", ctypes.c_int32), ("lanes_per_row", ctypes.c_int32)]
+                ("max_blocks", ctypes.c_int32), ("lanes_per_row", ctypes.c_int32),
+                ("weight_lds", ctypes.c_int32)]
 
     def as_dict(self):
         d = {"path": PATH_NAMES.get(self.path, self.path), "waves_per_row": self.waves_per_row,
@@ -67,6 +68,8 @@ class Config(ctypes.Structure):
              "max_blocks": self.max_blocks}
         if self.lanes_per_row:
             d["lanes_per_row"] = self.lanes_per_row
+        if self.weight_lds:
+            d["weight_lds"] = self.weight_lds
         return d
 
     def __repr__(self):

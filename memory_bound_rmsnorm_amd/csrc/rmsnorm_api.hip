@@ -26,6 +26,9 @@ namespace {
 constexpr int64_t kVectorBytes = 16;
 // Largest grid launched in one call; bigger jobs loop inside the kernel.
 constexpr int64_t kMaxGrid = int64_t(1) << 20;
+// Most LDS a forward workgroup may take for a staged weight (the rest of the
+// 64 KiB it can address holds its row totals).
+constexpr size_t kWeightLdsMax = 60 * 1024;
 // Workgroup size when rows narrower than half a wave share waves: one wave.
 // Sweeps on MI355X (HIP-graph timing): bf16 [262144, 128] runs in 23.3 us as
 // 16 lanes x 1 vector x 4 rows per 64-lane workgroup, against 62.8 us with a
@@ -164,11 +167,45 @@ rmsnorm_config_t choose(int64_t rows, int64_t hidden, int dtype, bool aligned, b
         per = fit(wpr);
     }
     if (per < 0) return c;
+    if (vec && !fused && !qt && rows >= 1024 && int64_t(64) * wpr * per > units) {
+        // plain rows the cap leaves padded (bf16 hidden 3072, 5120, 6144):
+        // the fewest idle lanes with at most five vectors per lane, ties kept
+        // as chosen.  Sweeps on MI355X: [8192, 5120] 2 x 5 28.6 us against
+        // 31.6 as 8 x 2, [4096, 6144] 4 x 3 18.3 against 19.5.
+        int64_t pad = int64_t(64) * wpr * per - units;
+        for (int w = 1; w <= 16; w *= 2) {
+            const int v = fit(w);
+            if (v < 0 || v > 5) continue;
+            const int64_t q = int64_t(64) * w * v - units;
+            if (q < pad) {
+                pad = q;
+                wpr = w;
+                per = v;
+            }
+        }
+    }
     c.path = vec ? RMSNORM_PATH_VECTOR : RMSNORM_PATH_ELEMENT;
     c.waves_per_row = wpr;
     c.items_per_lane = per;
     c.rows_per_block = 1;
     c.max_blocks = 0;
+    if (vec && !fused && !qt && units >= 384 && units * kVectorBytes <= int64_t(kWeightLdsMax)) {
+        // A plain job that fits one residency round (3072 to 4096 waves of
+        // rows at up to eight vectors per lane): four rows per workgroup
+        // (two at two waves a row) sharing one LDS copy of the weight, which
+        // leaves each lane 6-8 fewer global loads.  Sweeps on MI355X: bf16
+        // [2048, 8192] 11.7 us against 13.8, [2048, 5120] 7.5 against 10.1,
+        // [4096, 3072] 9.1 against 11.2; no gain outside that window.
+        int w1 = 1;
+        while (ceil_div(units, int64_t(64) * w1) > 8) w1 *= 2;
+        const int v1 = fit(w1);
+        if (v1 > 0 && rows * w1 >= 3072 && rows * w1 <= 4096 && w1 <= 2) {
+            c.waves_per_row = w1;
+            c.items_per_lane = v1;
+            c.rows_per_block = 4;
+            c.weight_lds = 1;
+        }
+    }
     if (vec && units <= mbr::kLprList[mbr::kNumLpr - 1]) {
         // a row narrower than half a wave: the smallest lane group that holds
         // it with one vector per lane, one wave per workgroup
@@ -187,7 +224,9 @@ rmsnorm_status_t launch(const Problem& p, const rmsnorm_config_t* user, hipStrea
     const rmsnorm_config_t c = (user && user->path != RMSNORM_PATH_AUTO) ? *user : choose(p.rows, p.hidden, p.dtype, aligned, p.fused, p.qt);
     const int wi = index_of(mbr::kWprList, mbr::kNumWpr, c.waves_per_row);
     if (wi < 0 || c.rows_per_block < 1 || c.max_blocks < 0) return RMSNORM_ERR_INVALID_ARG;
+    if (c.weight_lds != 0 && c.weight_lds != 1) return RMSNORM_ERR_INVALID_ARG;
     const bool whole = c.lanes_per_row == 0 || c.lanes_per_row == 64 * c.waves_per_row;
+    if (c.weight_lds && (c.path != RMSNORM_PATH_VECTOR || !whole || p.qt)) return RMSNORM_ERR_INVALID_ARG;
     const int64_t lanes_per_row = whole ? int64_t(64) * c.waves_per_row : c.lanes_per_row;
 
     mbr::RowArgs a;
@@ -201,6 +240,8 @@ rmsnorm_status_t launch(const Problem& p, const rmsnorm_config_t* user, hipStrea
     a.hidden_f = static_cast<float>(p.hidden);
     a.eps = p.eps;
     a.scale = p.scale;
+    a.w_lds = c.weight_lds;
+    size_t lds_bytes = 0;
 
     const void* fn = nullptr;
     int64_t threads = 0;
@@ -227,6 +268,10 @@ rmsnorm_status_t launch(const Problem& p, const rmsnorm_config_t* user, hipStrea
             fn = p.qt ? mbr::qvec_kernel(p.dtype, p.qt, p.fused, masked, wi, vi)
                       : mbr::vec_kernel(p.dtype, p.fused, masked, wi, vi);
             a.units = static_cast<int32_t>(nvec);
+            if (c.weight_lds) {
+                lds_bytes = static_cast<size_t>(nvec) * kVectorBytes;
+                if (lds_bytes > kWeightLdsMax) return RMSNORM_ERR_INVALID_ARG;
+            }
             break;
         }
         case RMSNORM_PATH_ELEMENT: {
@@ -258,7 +303,7 @@ rmsnorm_status_t launch(const Problem& p, const rmsnorm_config_t* user, hipStrea
     if (p.rows == 0) return RMSNORM_OK;
     void* args[] = {&a};
     hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(grid)), dim3(static_cast<unsigned>(threads)),
-                                   args, 0, stream);
+                                   args, lds_bytes, stream);
     if (e != hipSuccess) {
         (void)hipGetLastError();  // do not leave a sticky error for the caller's next HIP call
         return RMSNORM_ERR_RUNTIME;
@@ -438,6 +483,7 @@ rmsnorm_status_t run_bwd(const BwdProblem& p, const rmsnorm_config_t* user, void
     const int wi = index_of(mbr::kWprList, mbr::kNumWpr, c.waves_per_row);
     if (wi < 0 || c.rows_per_block < 1 || c.max_blocks < 0) return RMSNORM_ERR_INVALID_ARG;
     if (c.rows_per_block > 1 && c.path != RMSNORM_PATH_VECTOR) return RMSNORM_ERR_INVALID_ARG;
+    if (c.weight_lds != 0) return RMSNORM_ERR_INVALID_ARG;
     if (c.lanes_per_row != 0 && c.lanes_per_row != 64 * c.waves_per_row) return RMSNORM_ERR_INVALID_ARG;
     const bool dw = p.dw != nullptr;
     const int64_t ws_need = dw ? bwd_workspace_need(p.rows, p.hidden, c) : 0;
@@ -593,7 +639,7 @@ rmsnorm_status_t run_ln(const LnProblem& p, const rmsnorm_config_t* user, void* 
     const rmsnorm_config_t c =
         (user && user->path != RMSNORM_PATH_AUTO) ? *user : choose_ln(p.rows, p.hidden, p.dtype, aligned);
     const int wi = index_of(mbr::kWprList, mbr::kNumWpr, c.waves_per_row);
-    if (wi < 0 || c.rows_per_block != 1 || c.max_blocks < 0) return RMSNORM_ERR_INVALID_ARG;
+    if (wi < 0 || c.rows_per_block != 1 || c.max_blocks < 0 || c.weight_lds != 0) return RMSNORM_ERR_INVALID_ARG;
     if (c.lanes_per_row != 0 && c.lanes_per_row != 64 * c.waves_per_row) return RMSNORM_ERR_INVALID_ARG;
     const int64_t lanes = int64_t(64) * c.waves_per_row;
     mbr::LnArgs a;

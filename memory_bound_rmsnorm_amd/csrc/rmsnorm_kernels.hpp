@@ -56,6 +56,7 @@ struct RowArgs {
     float hidden_f;      // hidden as fp32, the mean's divisor
     float eps;
     float* scale;        // quantised forms: one fp32 scale per row
+    int32_t w_lds;       // vector path, normalised output: weight staged in LDS
 };
 
 // ---------------------------------------------------------------- dtypes
@@ -315,10 +316,22 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_vec_kernel(const RowAr
     };
 
     const u32x4* wr = static_cast<const u32x4*>(a.w);
+    // w_lds: the workgroup copies the weight into LDS once (dynamic LDS of
+    // units * 16 bytes) and every row slot reads its slice from there, in place
+    // of per-lane global loads; published by the first row barrier (or by an
+    // explicit one when rows take a single wave).
+    extern __shared__ u32x4 wlds[];
+    const bool use_lds = QT == 0 && LPR == 64 && a.w_lds != 0;
     u32x4 wv[WRES ? VPL : 1];
     if constexpr (WRES) {
+        if (!use_lds) {
 #pragma unroll
-        for (int k = 0; k < VPL; ++k) wv[k] = load_keep(wr + vidx(k));
+            for (int k = 0; k < VPL; ++k) wv[k] = load_keep(wr + vidx(k));
+        }
+    }
+    if (use_lds) {
+        for (int j = static_cast<int>(threadIdx.x); j < nvec; j += static_cast<int>(blockDim.x)) wlds[j] = load_keep(wr + j);
+        if constexpr (WPR == 1) __syncthreads();
     }
 
     int64_t g = blockIdx.x;
@@ -414,7 +427,9 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_vec_kernel(const RowAr
                 if (!in_row(k)) continue;
                 float f[V], fw[V];
                 widen(d[k], f, E{});
-                if constexpr (WRES)
+                if (use_lds)
+                    widen(wlds[k * LANES + lane_row], fw, E{});
+                else if constexpr (WRES)
                     widen(wv[k], fw, E{});
                 else
                     widen(load_keep(wr + k * LANES + lane_row), fw, E{});

@@ -123,6 +123,9 @@ WORKLOADS: Dict[str, Workload] = {
                  note="large hidden, 8 outlier channels x100; headline bandwidth case"),
         Workload("bf16_residual_12289x5120", "bf16", 12289, 5120, 1e-5, True, N01, W_N,
                  residual=N01, note="fused residual add; odd row count"),
+        Workload("bf16_shard_2048x8192", "bf16", 2048, 8192, 1e-5, False, N01, W_N,
+                 outlier_columns=OUTLIER_COLUMNS, outlier_scale=100.0,
+                 note="one GPU's rows of the 16384 x 8192 case split by tokens over 8 GPUs"),
     ]
 }
 

@@ -217,10 +217,17 @@ def resources(args):
         elif w.layernorm:
             mangled = "ln_vec_kernelINS_%d%sELi%dELi%dELb%dEEEv" % (len(e), e, cfg.waves_per_row, per, int(masked))
         else:
-            fam = {1: "rms_vec_kernel", 2: "rms_elem_kernel", 3: "rms_twopass_kernel"}[cfg.path]
             qt = {None: 0, "int8": 1, "fp8": 2}[w.quant]
-            mangled = "%sINS_%d%sELi%dELi%dELb%dELb%dELi%dEEEv" % (fam, len(e), e, cfg.waves_per_row, per,
-                                                                   int(masked), int(w.fused), qt)
+            if cfg.path == 1:  # rms_vec_kernel<E, WPR, VPL, MASKED, FUSED, QT, LPR>
+                lpr = cfg.lanes_per_row or 64
+                masked = (lpr if lpr < 64 else 64 * cfg.waves_per_row) * per != units
+                mangled = "rms_vec_kernelINS_%d%sELi%dELi%dELb%dELb%dELi%dELi%dEEEv" % (
+                    len(e), e, cfg.waves_per_row, per, int(masked), int(w.fused), qt, lpr)
+            elif cfg.path == 2:  # rms_elem_kernel<E, WPR, EPL, FUSED, QT>
+                mangled = "rms_elem_kernelINS_%d%sELi%dELi%dELb%dELi%dEEEv" % (len(e), e, cfg.waves_per_row, per,
+                                                                              int(w.fused), qt)
+            else:  # rms_twopass_kernel<E, VEC, FUSED, QT>
+                mangled = "rms_twopass_kernelINS_%d%sELb1ELb%dELi%dEEEv" % (len(e), e, int(w.fused), qt)
         hit = [l for l in lines if mangled in l]
         out.append("%s -> %s | %s" % (name, cfg.as_dict(), hit[0].split("|", 1)[1].strip() if hit else "?"))
     for name, w in inputs.KV_WORKLOADS.items():

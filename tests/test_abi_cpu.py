@@ -165,6 +165,26 @@ def test_bad_forced_configs_rejected():
     assert sub(16, 1, 1, 4, path=2) == INV    # element path has whole-wave rows only
     assert sub(16, 1, 1, 4, path=3) == INV    # so has the two-pass path
 
+    def lds(path, wpr, per, rpb, flag=1, hidden=2048, lpr=0):
+        cfg = mbr.Config(path, wpr, per, rpb, 0, lpr, flag)
+        return L.rmsnorm_fwd_ex(A, W, O, 8, hidden, 1e-5, 1, ctypes.byref(cfg), None)
+
+    assert lds(1, 2, 1, 2, flag=2) == INV                # weight_lds is 0 or 1
+    assert lds(2, 4, 8, 1) == INV                        # element path: no staged weight
+    assert lds(3, 16, 0, 1) == INV                       # nor the two-pass path
+    assert lds(1, 1, 1, 8, hidden=128, lpr=16) == INV    # nor rows sharing a wave
+    assert lds(1, 16, 4, 1, hidden=32768) == INV         # 64 KiB of weight: over the 60 KiB bound
+    # the quantised, backward and LayerNorm entry points take no staged weight
+    cfg = mbr.Config(1, 2, 1, 2, 0, 0, 1)
+    Q, S = 0x7F0030000000, 0x7F0040000000
+    assert L.rmsnorm_dynamic_quant_fwd_ex(A, None, W, None, Q, S, 8, 2048, 1e-5, 1, 0, ctypes.byref(cfg),
+                                          None) == INV
+    assert L.layernorm_fwd_ex(A, W, None, O, 8, 2048, 1e-5, 1, ctypes.byref(mbr.Config(1, 1, 4, 1, 0, 0, 1)),
+                              None) == INV
+    G, D = 0x7F0050000000, 0x7F0060000000
+    assert L.rmsnorm_bwd_ex(A, W, G, D, None, 8, 2048, 1e-5, 1, None, 0, ctypes.byref(mbr.Config(1, 4, 1, 1, 0, 0, 1)),
+                            None) == INV
+
 
 @pytest.mark.parametrize("name", list(inputs.WORKLOADS))
 def test_selection_for_the_workloads(name):
@@ -175,6 +195,9 @@ def test_selection_for_the_workloads(name):
     vec = 4 if w.dtype == "f32" else 8
     assert 64 * cfg.waves_per_row * cfg.items_per_lane >= w.hidden // vec
     assert 64 * cfg.waves_per_row * cfg.rows_per_block <= (1024 if cfg.waves_per_row == 16 else 512)
+    # one GPU's share of the token-split headline fits one residency round:
+    # four rows per workgroup share an LDS copy of the weight
+    assert cfg.weight_lds == (1 if name == "bf16_shard_2048x8192" else 0)
 
 
 @pytest.mark.parametrize("hidden", [1, 3, 7, 8, 9, 64, 96, 127, 128, 256, 264, 769, 2048, 4095, 5120, 5121, 8192,
@@ -210,6 +233,9 @@ def test_selection_is_always_a_built_covering_config(hidden, rows, dtype, aligne
         assert hidden > 8192  # everything narrower fits a register-resident path
     assert 64 * cfg.waves_per_row * cfg.rows_per_block <= (1024 if cfg.waves_per_row == 16 else 512)
     assert cfg.rows_per_block <= max(rows, 1)
+    if cfg.weight_lds:
+        assert cfg.weight_lds == 1 and cfg.path == mbr.PATH_VECTOR and not fused and not cfg.lanes_per_row
+        assert (hidden // vec) * 16 <= 60 * 1024
 
 
 def test_hbm_copy_rejects_bad_arguments():

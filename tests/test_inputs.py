@@ -30,6 +30,7 @@ def test_algorithmic_bytes():
     assert w["bf16_decode_256x4096"].algorithmic_bytes == 4_202_496
     assert w[inputs.HEADLINE].algorithmic_bytes == 536_887_296
     assert w["bf16_residual_12289x5120"].algorithmic_bytes == 503_367_680
+    assert w["bf16_shard_2048x8192"].algorithmic_bytes == (2 * 2048 * 8192 + 8192) * 2
 
 
 def test_quant_workload_bytes():

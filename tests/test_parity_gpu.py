@@ -191,6 +191,43 @@ def test_every_two_pass_config(dtype, fused):
             check_workload(w, inputs.make(w, seed=wpr + hidden), cfg)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("fused", [False, True])
+def test_weight_in_lds_matches_bitwise(dtype, fused):
+    """weight_lds = 1 (the workgroup stages the weight in LDS once) on every
+    built vector configuration, with one and with the most row slots, full and
+    masked rows, and a capped grid whose workgroups walk several row groups:
+    bitwise equal to the same configuration reading the weight from global
+    memory, and within the oracle's bound."""
+    vecw = 8 if dtype == "bf16" else 4
+    n = 0
+    for wpr, vpl in _configs(mbr.PATH_VECTOR, dtype, fused):
+        lanes = 64 * wpr
+        max_rpb = (1024 if wpr == 16 else 512) // lanes
+        for nvec in sorted({lanes * vpl, max(1, lanes * vpl - 37)}):
+            if nvec * 16 > 60 * 1024:
+                continue
+            for rpb, mb in sorted({(1, 0), (max_rpb, 0), (max_rpb, 2)}):
+                rows = 2 * rpb + 1
+                w = inputs.custom(rows, nvec * vecw, dtype, fused)
+                t = inputs.make(w, seed=500 + n)
+                dev = {k: v.cuda() for k, v in t.items()}
+                on = mbr.Config(mbr.PATH_VECTOR, wpr, vpl, rpb, mb, 0, 1)
+                off = mbr.Config(mbr.PATH_VECTOR, wpr, vpl, rpb, mb, 0, 0)
+                say("weight in LDS", dtype, fused, on, "hidden", nvec * vecw, "rows", rows)
+                if fused:
+                    a = run_fused(dev["x"], dev["residual"], dev["weight"], w.eps, on)
+                    b = run_fused(dev["x"], dev["residual"], dev["weight"], w.eps, off)
+                    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+                else:
+                    assert torch.equal(run_plain(dev["x"], dev["weight"], w.eps, on),
+                                       run_plain(dev["x"], dev["weight"], w.eps, off))
+                if n % 4 == 0:
+                    check_workload(w, t, on)
+                n += 1
+    assert n > 60
+
+
 @pytest.mark.parametrize("fused", [False, True])
 def test_persistent_grid_matches_bitwise(fused):
     """Capping the grid (workgroups loop over row groups) changes nothing."""
