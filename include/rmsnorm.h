@@ -146,8 +146,9 @@ typedef struct {
                                with whole-wave rows only; each workgroup copies the weight
                                into LDS once (hidden * size bytes, at most 60 KiB) and its
                                rows read it from there instead of from global memory.  The
-                               results are bitwise the same either way.  Must be 0 for the
-                               quantised, backward and LayerNorm entry points */
+                               results are bitwise the same either way.  layernorm_fwd_ex:
+                               gamma and beta staged the same way.  Must be 0 for the
+                               quantised and backward entry points */
 } rmsnorm_config_t;
 
 /*
@@ -325,8 +326,11 @@ RMSNORM_API rmsnorm_status_t layernorm_fwd(const void* x, const void* gamma, con
                                            void* stream);
 
 /* layernorm_fwd with a launch configuration (NULL or path AUTO = automatic;
- * path TWO_PASS selects the three-pass wide-row kernel); rows_per_block must
- * be 1. */
+ * path TWO_PASS selects the three-pass wide-row kernel).  weight_lds (gamma
+ * and beta staged in LDS once per workgroup, hidden * size bytes each, at most
+ * 60 KiB together) is taken on path VECTOR only; rows_per_block > 1 requires
+ * it (the row slots share that copy), with 64 * waves_per_row *
+ * rows_per_block within the limit of rmsnorm_config_t. */
 RMSNORM_API rmsnorm_status_t layernorm_fwd_ex(const void* x, const void* gamma, const void* beta, void* out,
                                               int64_t rows, int64_t hidden, float eps, rmsnorm_dtype_t dtype,
                                               const rmsnorm_config_t* cfg, void* stream);

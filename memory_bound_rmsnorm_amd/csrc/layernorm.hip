@@ -7,18 +7,25 @@
 namespace mbr {
 namespace {
 
-template <class E, int WPR, int VPL, bool MASKED>
+template <class E, int WPR, int VPL, bool MASKED, bool GBL>
 const void* lvec_ptr() {
     if constexpr (ln_vec_built(WPR, VPL))
-        return reinterpret_cast<const void*>(&ln_vec_kernel<E, WPR, VPL, MASKED>);
+        return reinterpret_cast<const void*>(&ln_vec_kernel<E, WPR, VPL, MASKED, GBL>);
     else
         return nullptr;
 }
 
-template <class E, bool MASKED, size_t... I>
+template <class E, bool MASKED, bool GBL, size_t... I>
 const void* const* lvec_table(std::index_sequence<I...>) {
-    static const void* const table[] = {lvec_ptr<E, kWprList[I / kNumLnVpl], kLnVplList[I % kNumLnVpl], MASKED>()...};
+    static const void* const table[] = {
+        lvec_ptr<E, kWprList[I / kNumLnVpl], kLnVplList[I % kNumLnVpl], MASKED, GBL>()...};
     return table;
+}
+
+template <class E, size_t... I>
+const void* const* lvec_table_for(bool masked, bool gbl, std::index_sequence<I...> seq) {
+    if (gbl) return masked ? lvec_table<E, true, true>(seq) : lvec_table<E, false, true>(seq);
+    return masked ? lvec_table<E, true, false>(seq) : lvec_table<E, false, false>(seq);
 }
 
 template <class E, size_t... I>
@@ -30,14 +37,11 @@ const void* const* lelem_table(std::index_sequence<I...>) {
 
 }  // namespace
 
-const void* ln_vec_kernel_ptr(int dtype, bool masked, int wi, int vi) {
+const void* ln_vec_kernel_ptr(int dtype, bool masked, bool gamma_beta_lds, int wi, int vi) {
     using Seq = std::make_index_sequence<kNumWpr * kNumLnVpl>;
     if (wi < 0 || wi >= kNumWpr || vi < 0 || vi >= kNumLnVpl) return nullptr;
-    const void* const* t;
-    if (dtype == 1)
-        t = masked ? lvec_table<Bf16, true>(Seq{}) : lvec_table<Bf16, false>(Seq{});
-    else
-        t = masked ? lvec_table<F32, true>(Seq{}) : lvec_table<F32, false>(Seq{});
+    const void* const* t = dtype == 1 ? lvec_table_for<Bf16>(masked, gamma_beta_lds, Seq{})
+                                      : lvec_table_for<F32>(masked, gamma_beta_lds, Seq{});
     return t[wi * kNumLnVpl + vi];
 }
 

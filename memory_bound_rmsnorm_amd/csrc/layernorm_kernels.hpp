@@ -33,7 +33,9 @@ struct LnArgs {
     const void* b;  // beta, or nullptr (no bias)
     void* out;
     int64_t rows;
-    int32_t units;  // per row: 16-byte vectors (vector path) or elements
+    int64_t n_groups;        // vector path: ceil(rows / rows_per_block)
+    int32_t units;           // per row: 16-byte vectors (vector path) or elements
+    int32_t rows_per_block;  // vector path: row slots per workgroup
     float hidden_f;
     float eps;
 };
@@ -42,8 +44,11 @@ struct LnArgs {
 // and value, one barrier, fixed-order sums of the slots.  The first call of a
 // row uses slot set 0 and the second set 1; a set is written again only after
 // the other set's barrier, so single buffers suffice.
+// The row's waves are wave0 .. wave0 + NWAVES - 1 of the workgroup (several
+// row slots share a workgroup on the vector path).
 template <int NWAVES, int N>
-__device__ __forceinline__ void block_sums(float (&v)[N], float (&slots)[N][16], int wave, int nwaves_rt = NWAVES) {
+__device__ __forceinline__ void block_sums(float (&v)[N], float (&slots)[N][16], int wave, int nwaves_rt = NWAVES,
+                                           int wave0 = 0) {
 #pragma unroll
     for (int k = 0; k < N; ++k) v[k] = wave_sum(v[k]);
     if (NWAVES == 1 || nwaves_rt == 1) return;
@@ -57,7 +62,7 @@ __device__ __forceinline__ void block_sums(float (&v)[N], float (&slots)[N][16],
         float t = 0.f;
         if constexpr (NWAVES > 0) {
 #pragma unroll
-            for (int i = 0; i < NWAVES; ++i) t += slots[k][i];
+            for (int i = 0; i < NWAVES; ++i) t += slots[k][wave0 + i];
         } else {
             for (int i = 0; i < nwaves_rt; ++i) t += slots[k][i];
         }
@@ -78,19 +83,29 @@ __device__ __forceinline__ LnMoments ln_moments(float m0, const float (&tq)[2], 
     return {m0, c, rsqrtf(var + a.eps)};
 }
 
-// Vector path: WPR waves per row, one row per workgroup at a time, lane l
-// owning 16-byte vectors l, l + 64*WPR, ... (VPL of them).  MASKED: the row
-// has fewer than 64*WPR*VPL vectors; loads are clamped in bounds, the extra
-// values excluded from both sums, stores skipped.
-template <class E, int WPR, int VPL, bool MASKED>
+// Vector path: WPR waves per row, lane l of a row owning 16-byte vectors l,
+// l + 64*WPR, ... (VPL of them).  MASKED: the row has fewer than 64*WPR*VPL
+// vectors; loads are clamped in bounds, the extra values excluded from both
+// sums, stores skipped.  GBL: the workgroup copies gamma (and beta) into LDS
+// once, published by the first row barrier (or an explicit one when a row
+// takes one wave), and holds rows_per_block row slots that read them from
+// there: in each step of its walk slot s takes row group*rows_per_block + s
+// (a slot past the last row reads the last row again and stores nothing).
+// Without GBL a workgroup works on one row at a time and loads gamma and beta
+// per row; the slot terms fold away at compile time.
+template <class E, int WPR, int VPL, bool MASKED, bool GBL>
 __global__ void __launch_bounds__(max_threads<WPR>()) ln_vec_kernel(const LnArgs a) {
     constexpr int LANES = 64 * WPR;
     constexpr int V = E::kVec;
     const int wave = wave_id();
-    const int lane = static_cast<int>(threadIdx.x);
+    const int slot = GBL ? wave / WPR : 0;
+    const int lane = static_cast<int>(threadIdx.x) - slot * LANES;
     const int nvec = a.units;
+    const int64_t rpb = GBL ? a.rows_per_block : 1;
+    const int64_t n_groups = GBL ? a.n_groups : a.rows;
     const bool bias = a.b != nullptr;
     __shared__ float s1[1][16], s2[2][16];
+    extern __shared__ u32x4 gb[];  // GBL: gamma [nvec], then beta [nvec]
 
     auto vidx = [&](int k) {
         const int v = k * LANES + lane;
@@ -98,8 +113,18 @@ __global__ void __launch_bounds__(max_threads<WPR>()) ln_vec_kernel(const LnArgs
     };
     auto in_row = [&](int k) { return !MASKED || k * LANES + lane < nvec; };
 
-    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
-        const u32x4* xr = static_cast<const u32x4*>(a.x) + row * nvec;
+    if constexpr (GBL) {
+        for (int j = static_cast<int>(threadIdx.x); j < nvec; j += static_cast<int>(blockDim.x)) {
+            gb[j] = load_keep(static_cast<const u32x4*>(a.g) + j);
+            if (bias) gb[nvec + j] = load_keep(static_cast<const u32x4*>(a.b) + j);
+        }
+        if constexpr (WPR == 1) __syncthreads();
+    }
+
+    for (int64_t grp = blockIdx.x; grp < n_groups; grp += gridDim.x) {
+        const int64_t row = grp * rpb + slot;
+        const bool valid = !GBL || row < a.rows;
+        const u32x4* xr = static_cast<const u32x4*>(a.x) + (valid ? row : a.rows - 1) * nvec;
         u32x4 d[VPL];
 #pragma unroll
         for (int k = 0; k < VPL; ++k) d[k] = load_stream(xr + vidx(k));
@@ -113,13 +138,15 @@ __global__ void __launch_bounds__(max_threads<WPR>()) ln_vec_kernel(const LnArgs
             for (int i = 0; i < V; ++i) t += f[i];
             s[0] += in_row(k) ? t : 0.f;
         }
-        block_sums<WPR>(s, s1, wave);
+        block_sums<WPR>(s, s1, wave, WPR, slot * WPR);
         const float m0 = s[0] / a.hidden_f;
-        u32x4 gv[VPL], bv[VPL];
+        u32x4 gv[GBL ? 1 : VPL], bv[GBL ? 1 : VPL];
+        if constexpr (!GBL) {
 #pragma unroll
-        for (int k = 0; k < VPL; ++k) {
-            gv[k] = load_keep(static_cast<const u32x4*>(a.g) + vidx(k));
-            if (bias) bv[k] = load_keep(static_cast<const u32x4*>(a.b) + vidx(k));
+            for (int k = 0; k < VPL; ++k) {
+                gv[k] = load_keep(static_cast<const u32x4*>(a.g) + vidx(k));
+                if (bias) bv[k] = load_keep(static_cast<const u32x4*>(a.b) + vidx(k));
+            }
         }
         float tq[2] = {0.f, 0.f};
 #pragma unroll
@@ -136,7 +163,8 @@ __global__ void __launch_bounds__(max_threads<WPR>()) ln_vec_kernel(const LnArgs
             tq[0] += in_row(k) ? t : 0.f;
             tq[1] += in_row(k) ? q : 0.f;
         }
-        block_sums<WPR>(tq, s2, wave);
+        block_sums<WPR>(tq, s2, wave, WPR, slot * WPR);
+        if (!valid) continue;  // GBL only: a slot past the last row
         const LnMoments m = ln_moments(m0, tq, a);
         u32x4* outr = static_cast<u32x4*>(a.out) + row * nvec;
 #pragma unroll
@@ -144,10 +172,14 @@ __global__ void __launch_bounds__(max_threads<WPR>()) ln_vec_kernel(const LnArgs
             if (!in_row(k)) continue;
             float f[V], fg[V], fb[V];
             widen(d[k], f, E{});
-            widen(gv[k], fg, E{});
-            if (bias) {
-                widen(bv[k], fb, E{});
+            if constexpr (GBL) {
+                widen(gb[k * LANES + lane], fg, E{});
+                if (bias) widen(gb[nvec + k * LANES + lane], fb, E{});
             } else {
+                widen(gv[k], fg, E{});
+                if (bias) widen(bv[k], fb, E{});
+            }
+            if (!bias) {
 #pragma unroll
                 for (int i = 0; i < V; ++i) fb[i] = 0.f;
             }

@@ -585,9 +585,11 @@ bool ln_vector_aligned(const LnProblem& p) {
 // Each LayerNorm row needs two workgroup reductions, so rows take as few
 // waves as registers allow: up to eight 16-byte vectors (or elements) per lane,
 // more waves per row only when rows are few; one row per workgroup, uncapped
-// grid.  Sweeps on MI355X, bf16 [8192, 4096]: 1 wave x 8 vectors 25.9 us,
-// 2 x 4 26.1, 4 x 2 28.3, 8 x 1 31.8.  Rows beyond every built register
-// configuration take the multi-pass path.
+// grid.  Sweeps on MI355X with per-row gamma/beta loads, bf16 [8192, 4096]:
+// 1 wave x 8 vectors 25.9 us, 2 x 4 26.1, 4 x 2 28.3, 8 x 1 31.8.  Wide rows
+// with enough of them then move to row slots sharing gamma/beta in LDS
+// (below).  Rows beyond every built register configuration take the
+// multi-pass path.
 rmsnorm_config_t choose_ln(int64_t rows, int64_t hidden, int dtype, bool aligned) {
     rmsnorm_config_t c = {RMSNORM_PATH_TWO_PASS, 16, 0, 1, 0};
     const bool vec = aligned && hidden % vec_elems(dtype) == 0;
@@ -612,6 +614,40 @@ rmsnorm_config_t choose_ln(int64_t rows, int64_t hidden, int dtype, bool aligned
     c.path = vec ? RMSNORM_PATH_VECTOR : RMSNORM_PATH_ELEMENT;
     c.waves_per_row = wpr;
     c.items_per_lane = per;
+    // Rows of 384 vectors or more, gamma and beta fitting LDS (sized for a
+    // beta): row slots sharing one LDS copy of them.  From 4096 rows, the
+    // waves per row with the fewest idle lanes at up to five vectors per lane
+    // (ties: closest to four) and 512-lane workgroups; at 2048..4095 rows of
+    // more than 512 vectors, two waves per row and four slots, so that the
+    // job is one round of workgroups.  Sweeps on MI355X (HIP-graph timing,
+    // bf16 with beta): [8192, 4096] 25.0 us as 2 x 4 x 4 slots against 26.4,
+    // [4096, 4096] 12.5 against 14.5, [4096, 8192] 25.7 (4 x 4 x 2) against
+    // 28.8, [2048, 8192] 11.9 (2 x 8 x 4) against 16.5.
+    if (vec && units >= 384 && units * kVectorBytes * 2 <= int64_t(kWeightLdsMax)) {
+        int w = 0, v = 0;
+        if (rows >= 4096) {
+            int64_t best_pad = -1;
+            for (int ww = 1; ww <= 16; ww *= 2) {
+                const int vv = fit(ww);
+                if (vv < 0 || vv > 5) continue;
+                const int64_t pad = int64_t(64) * ww * vv - units;
+                if (best_pad < 0 || pad < best_pad || (pad == best_pad && std::abs(vv - 4) < std::abs(v - 4))) {
+                    best_pad = pad;
+                    w = ww;
+                    v = vv;
+                }
+            }
+        } else if (rows >= 2048 && units > 512) {
+            w = 2;
+            v = fit(2);
+        }
+        if (w > 0 && v > 0 && w <= 8) {
+            c.waves_per_row = w;
+            c.items_per_lane = v;
+            c.rows_per_block = 512 / (64 * w);
+            c.weight_lds = 1;
+        }
+    }
     return c;
 }
 
@@ -639,27 +675,38 @@ rmsnorm_status_t run_ln(const LnProblem& p, const rmsnorm_config_t* user, void* 
     const rmsnorm_config_t c =
         (user && user->path != RMSNORM_PATH_AUTO) ? *user : choose_ln(p.rows, p.hidden, p.dtype, aligned);
     const int wi = index_of(mbr::kWprList, mbr::kNumWpr, c.waves_per_row);
-    if (wi < 0 || c.rows_per_block != 1 || c.max_blocks < 0 || c.weight_lds != 0) return RMSNORM_ERR_INVALID_ARG;
+    if (wi < 0 || c.rows_per_block < 1 || c.max_blocks < 0) return RMSNORM_ERR_INVALID_ARG;
+    if (c.weight_lds != 0 && c.weight_lds != 1) return RMSNORM_ERR_INVALID_ARG;
+    if ((c.rows_per_block != 1 || c.weight_lds) && c.path != RMSNORM_PATH_VECTOR) return RMSNORM_ERR_INVALID_ARG;
+    if (c.rows_per_block != 1 && !c.weight_lds) return RMSNORM_ERR_INVALID_ARG;  // slots share the LDS copy
     if (c.lanes_per_row != 0 && c.lanes_per_row != 64 * c.waves_per_row) return RMSNORM_ERR_INVALID_ARG;
     const int64_t lanes = int64_t(64) * c.waves_per_row;
+    const int64_t threads = lanes * c.rows_per_block;
     mbr::LnArgs a;
     a.x = p.x;
     a.g = p.g;
     a.b = p.b;
     a.out = p.out;
     a.rows = p.rows;
+    a.rows_per_block = c.rows_per_block;
+    a.n_groups = ceil_div(p.rows, int64_t(c.rows_per_block));
     a.hidden_f = static_cast<float>(p.hidden);
     a.eps = p.eps;
     const void* fn = nullptr;
+    size_t lds = 0;
     switch (c.path) {
         case RMSNORM_PATH_VECTOR: {
             if (!aligned || p.hidden % vec_elems(p.dtype) != 0) return RMSNORM_ERR_INVALID_ARG;
             const int vi = index_of(mbr::kLnVplList, mbr::kNumLnVpl, c.items_per_lane);
             const int64_t nvec = p.hidden / vec_elems(p.dtype);
             if (vi < 0 || lanes * c.items_per_lane < nvec) return RMSNORM_ERR_INVALID_ARG;
-            if (lanes > mbr::max_threads_for(c.waves_per_row)) return RMSNORM_ERR_INVALID_ARG;
-            fn = mbr::ln_vec_kernel_ptr(p.dtype, lanes * c.items_per_lane != nvec, wi, vi);
+            if (threads > mbr::max_threads_for(c.waves_per_row)) return RMSNORM_ERR_INVALID_ARG;
+            fn = mbr::ln_vec_kernel_ptr(p.dtype, lanes * c.items_per_lane != nvec, c.weight_lds != 0, wi, vi);
             a.units = static_cast<int32_t>(nvec);
+            if (c.weight_lds) {
+                lds = static_cast<size_t>(nvec) * kVectorBytes * (p.b ? 2 : 1);
+                if (lds > kWeightLdsMax) return RMSNORM_ERR_INVALID_ARG;
+            }
             break;
         }
         case RMSNORM_PATH_ELEMENT: {
@@ -680,9 +727,9 @@ rmsnorm_status_t run_ln(const LnProblem& p, const rmsnorm_config_t* user, void* 
             return RMSNORM_ERR_INVALID_ARG;
     }
     if (!fn) return RMSNORM_ERR_INVALID_ARG;
-    int64_t grid = p.rows < kMaxGrid ? p.rows : kMaxGrid;
+    int64_t grid = a.n_groups < kMaxGrid ? a.n_groups : kMaxGrid;
     if (c.max_blocks > 0 && grid > c.max_blocks) grid = c.max_blocks;
-    return launch_checked(fn, grid, lanes, &a, static_cast<hipStream_t>(stream));
+    return launch_checked(fn, grid, threads, &a, static_cast<hipStream_t>(stream), lds);
 }
 
 // ---------------------------------------------------------------- KV RMSNorm + RoPE + cache

@@ -77,7 +77,7 @@ constexpr int kLnEplList[] = {1, 2, 4, 8};
 constexpr int kNumLnVpl = sizeof(kLnVplList) / sizeof(int);
 constexpr int kNumLnEpl = sizeof(kLnEplList) / sizeof(int);
 
-const void* ln_vec_kernel_ptr(int dtype, bool masked, int wpr_index, int vpl_index);
+const void* ln_vec_kernel_ptr(int dtype, bool masked, bool gamma_beta_lds, int wpr_index, int vpl_index);
 const void* ln_elem_kernel_ptr(int dtype, int wpr_index, int epl_index);
 const void* ln_multipass_kernel_ptr(int dtype, bool vec);
 

@@ -215,7 +215,8 @@ def resources(args):
             fam = {1: "rms_bwd_vec_kernel", 2: "rms_bwd_elem_kernel", 3: "rms_bwd_twopass_kernel"}[cfg.path]
             mangled = "%sINS_%d%sELi%dELi%dELb%dELb1EEEv" % (fam, len(e), e, cfg.waves_per_row, per, int(masked))
         elif w.layernorm:
-            mangled = "ln_vec_kernelINS_%d%sELi%dELi%dELb%dEEEv" % (len(e), e, cfg.waves_per_row, per, int(masked))
+            mangled = "ln_vec_kernelINS_%d%sELi%dELi%dELb%dELb%dEEEv" % (len(e), e, cfg.waves_per_row, per, int(masked),
+                                                                   int(bool(cfg.weight_lds)))
         else:
             qt = {None: 0, "int8": 1, "fp8": 2}[w.quant]
             if cfg.path == 1:  # rms_vec_kernel<E, WPR, VPL, MASKED, FUSED, QT, LPR>

@@ -28,13 +28,18 @@ def test_bad_sizes_rejected(rows, hidden, eps, dtype, want):
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("aligned", [True, False])
-@pytest.mark.parametrize("rows", [1, 100, 100000])
+@pytest.mark.parametrize("rows", [1, 100, 2048, 4096, 100000])
 def test_choice_is_built_and_covering(dtype, aligned, rows):
     v = 8 if dtype == torch.bfloat16 else 4
     for hidden in [1, 7, 8, 64, 100, 768, 1000, 2048, 4095, 4096, 5120, 8192, 16384, 32768, 32776, 65536, 131080]:
         c = mbr.layernorm_select_config(rows, hidden, dtype, aligned)
         lanes = 64 * c.waves_per_row
-        assert c.rows_per_block == 1 and c.max_blocks == 0 and c.waves_per_row in (1, 2, 4, 8, 16)
+        assert c.max_blocks == 0 and c.waves_per_row in (1, 2, 4, 8, 16)
+        if c.weight_lds:  # gamma and beta (sized for both) in LDS, shared by the row slots
+            assert c.path == mbr.PATH_VECTOR and (hidden // v) * 32 <= 60 * 1024
+            assert c.rows_per_block >= 1 and lanes * c.rows_per_block <= 512
+        else:
+            assert c.rows_per_block == 1
         if c.path == mbr.PATH_VECTOR:
             assert aligned and hidden % v == 0 and lanes * c.items_per_lane >= hidden // v
             assert c.items_per_lane in range(1, 9) and (c.waves_per_row < 16 or c.items_per_lane <= 4)
@@ -45,8 +50,17 @@ def test_choice_is_built_and_covering(dtype, aligned, rows):
 
 
 def test_stated_choices():
+    # many rows of 512 vectors: 2 waves x 4 vectors, four row slots sharing gamma/beta in LDS
     c = mbr.layernorm_select_config(8192, 4096, torch.bfloat16, True)
-    assert (c.path, c.waves_per_row, c.items_per_lane) == (mbr.PATH_VECTOR, 1, 8)
+    assert (c.path, c.waves_per_row, c.items_per_lane, c.rows_per_block, c.weight_lds) == (mbr.PATH_VECTOR, 2, 4, 4, 1)
+    c = mbr.layernorm_select_config(4096, 8192, torch.bfloat16, True)
+    assert (c.waves_per_row, c.items_per_lane, c.rows_per_block, c.weight_lds) == (4, 4, 2, 1)
+    # one round of workgroups at 2048 rows of 1024 vectors
+    c = mbr.layernorm_select_config(2048, 8192, torch.bfloat16, True)
+    assert (c.waves_per_row, c.items_per_lane, c.rows_per_block, c.weight_lds) == (2, 8, 4, 1)
+    # narrower rows keep one row per workgroup and per-row gamma/beta loads
+    c = mbr.layernorm_select_config(8192, 2048, torch.bfloat16, True)
+    assert (c.waves_per_row, c.items_per_lane, c.rows_per_block, c.weight_lds) == (1, 4, 1, 0)
     c = mbr.layernorm_select_config(64, 768, torch.float32, True)
     assert (c.path, c.waves_per_row, c.items_per_lane) == (mbr.PATH_VECTOR, 2, 2)  # few rows: spread
 
@@ -58,9 +72,18 @@ def test_pointer_validation_and_forced_configs():
     for args in [(None, G, B, O), (X, None, B, O), (X, G, B, None), (X + 1, G, B, O), (X, G, B + 1, O),
                  (X, G, B, X + 2), (X, G, B, G), (X, G, B, B - 16)]:
         assert L.layernorm_fwd(*args, 4, 256, 1e-5, 1, None) == INV, args
-    for cfg in [mbr.Config(mbr.PATH_VECTOR, 3, 2, 1, 0), mbr.Config(mbr.PATH_VECTOR, 4, 2, 2, 0),
+    for cfg in [mbr.Config(mbr.PATH_VECTOR, 3, 2, 1, 0), mbr.Config(mbr.PATH_VECTOR, 4, 2, 4, 0),
                 mbr.Config(mbr.PATH_VECTOR, 16, 5, 1, 0), mbr.Config(mbr.PATH_VECTOR, 1, 2, 1, 0),
                 mbr.Config(mbr.PATH_ELEMENT, 4, 3, 1, 0), mbr.Config(mbr.PATH_VECTOR, 4, 2, 1, -1),
-                mbr.Config(9, 4, 2, 1, 0), mbr.Config(mbr.PATH_VECTOR, 1, 1, 1, 0, 32)]:
+                mbr.Config(9, 4, 2, 1, 0), mbr.Config(mbr.PATH_VECTOR, 1, 1, 1, 0, 32),
+                mbr.Config(mbr.PATH_VECTOR, 4, 2, 0, 0),            # no row slots
+                mbr.Config(mbr.PATH_VECTOR, 4, 2, 2, 0),            # row slots need the LDS copy
+                mbr.Config(mbr.PATH_VECTOR, 4, 2, 2, 0, 0, 2),      # weight_lds is 0 or 1
+                mbr.Config(mbr.PATH_ELEMENT, 4, 16, 2, 0),          # row slots: vector path only
+                mbr.Config(mbr.PATH_ELEMENT, 4, 16, 1, 0, 0, 1),    # so is the LDS copy
+                mbr.Config(mbr.PATH_TWO_PASS, 16, 0, 1, 0, 0, 1)]:
         import ctypes
         assert L.layernorm_fwd_ex(X, G, B, O, 4, 4096, 1e-5, 1, ctypes.byref(cfg), None) == INV, cfg
+    # gamma and beta in LDS: 2 * 4096 vectors * 16 bytes, over the 60 KiB bound
+    cfg = mbr.Config(mbr.PATH_VECTOR, 16, 4, 1, 0, 0, 1)
+    assert L.layernorm_fwd_ex(X, G, B, O, 4, 32768, 1e-5, 1, ctypes.byref(cfg), None) == INV

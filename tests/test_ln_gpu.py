@@ -90,6 +90,41 @@ def test_ln_every_vector_config(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ln_gamma_beta_in_lds(dtype):
+    """weight_lds = 1 (gamma and beta copied into LDS once per workgroup, which
+    then holds rows_per_block row slots) on every built vector configuration:
+    one slot and the most slots, full and masked rows, with and without beta,
+    and a capped grid whose workgroups walk several row groups.  Bitwise equal
+    to the per-row-load kernel, and within the oracle's bound."""
+    vecw = 8 if dtype == "bf16" else 4
+    n = 0
+    for wpr in (1, 2, 4, 8, 16):
+        for vpl in range(1, 9):
+            if wpr == 16 and vpl > 4:
+                continue
+            lanes = 64 * wpr
+            max_rpb = (1024 if wpr == 16 else 512) // lanes
+            for nvec in sorted({lanes * vpl, max(1, lanes * vpl - 37)}):
+                for rpb, mb in sorted({(1, 0), (max_rpb, 0), (max_rpb, 2)}):
+                    bias = n % 2 == 0
+                    if nvec * 16 * (2 if bias else 1) > 60 * 1024:
+                        continue
+                    rows = 2 * rpb + 1
+                    w = inputs.custom(rows, nvec * vecw, dtype, layernorm=True)
+                    t = inputs.make(w, seed=700 + n)
+                    on = mbr.Config(mbr.PATH_VECTOR, wpr, vpl, rpb, mb, 0, 1)
+                    off = mbr.Config(mbr.PATH_VECTOR, wpr, vpl, 1, 0)
+                    say("ln gamma/beta in LDS", dtype, on, "hidden", nvec * vecw, "bias", bias)
+                    x, g = t["x"].cuda(), t["weight"].cuda()
+                    b = t["beta"].cuda() if bias else None
+                    assert torch.equal(run_ln(x, g, b, w.eps, on), run_ln(x, g, b, w.eps, off))
+                    if n % 4 == 0:
+                        check(w, t, on, bias=bias)
+                    n += 1
+    assert n > 60
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_ln_every_element_and_multipass_config(dtype):
     n = 0
     for wpr in (1, 2, 4, 8, 16):
