@@ -142,13 +142,12 @@ typedef struct {
                                waves_per_row 1 and items_per_lane 1 or 2, several rows
                                sharing a wave; lanes_per_row * rows_per_block must then be
                                a multiple of 64 and at most 512 */
-    int32_t weight_lds;     /* 0 or 1.  1: VECTOR path of rmsnorm_fwd / rmsnorm_residual_fwd
-                               with whole-wave rows only; each workgroup copies the weight
-                               into LDS once (hidden * size bytes, at most 60 KiB) and its
-                               rows read it from there instead of from global memory.  The
-                               results are bitwise the same either way.  layernorm_fwd_ex:
-                               gamma and beta staged the same way.  Must be 0 for the
-                               quantised and backward entry points */
+    int32_t weight_lds;     /* 0 or 1.  1: VECTOR path with whole-wave rows only; each
+                               workgroup copies the weight into LDS once (hidden * size
+                               bytes, at most 60 KiB) and its rows take it from there
+                               instead of from global memory.  The results are bitwise the
+                               same either way.  layernorm_fwd_ex: gamma and beta staged
+                               the same way.  Must be 0 for rmsnorm_bwd_ex */
 } rmsnorm_config_t;
 
 /*

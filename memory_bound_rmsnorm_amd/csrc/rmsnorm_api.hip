@@ -226,7 +226,7 @@ rmsnorm_status_t launch(const Problem& p, const rmsnorm_config_t* user, hipStrea
     if (wi < 0 || c.rows_per_block < 1 || c.max_blocks < 0) return RMSNORM_ERR_INVALID_ARG;
     if (c.weight_lds != 0 && c.weight_lds != 1) return RMSNORM_ERR_INVALID_ARG;
     const bool whole = c.lanes_per_row == 0 || c.lanes_per_row == 64 * c.waves_per_row;
-    if (c.weight_lds && (c.path != RMSNORM_PATH_VECTOR || !whole || p.qt)) return RMSNORM_ERR_INVALID_ARG;
+    if (c.weight_lds && (c.path != RMSNORM_PATH_VECTOR || !whole)) return RMSNORM_ERR_INVALID_ARG;
     const int64_t lanes_per_row = whole ? int64_t(64) * c.waves_per_row : c.lanes_per_row;
 
     mbr::RowArgs a;

@@ -317,21 +317,21 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_vec_kernel(const RowAr
 
     const u32x4* wr = static_cast<const u32x4*>(a.w);
     // w_lds: the workgroup copies the weight into LDS once (dynamic LDS of
-    // units * 16 bytes) and every row slot reads its slice from there, in place
-    // of per-lane global loads; published by the first row barrier (or by an
+    // units * 16 bytes) and every row slot takes its slice from there, in place
+    // of per-lane global loads.  Lanes that hold the weight (WRES, and every
+    // quantised form) fill their registers from LDS after a barrier; the
+    // others read LDS at the output, after the first row barrier (or an
     // explicit one when rows take a single wave).
     extern __shared__ u32x4 wlds[];
-    const bool use_lds = QT == 0 && LPR == 64 && a.w_lds != 0;
+    const bool use_lds = LPR == 64 && a.w_lds != 0;
     u32x4 wv[WRES ? VPL : 1];
-    if constexpr (WRES) {
-        if (!use_lds) {
-#pragma unroll
-            for (int k = 0; k < VPL; ++k) wv[k] = load_keep(wr + vidx(k));
-        }
-    }
     if (use_lds) {
         for (int j = static_cast<int>(threadIdx.x); j < nvec; j += static_cast<int>(blockDim.x)) wlds[j] = load_keep(wr + j);
-        if constexpr (WPR == 1) __syncthreads();
+        if (WRES || WPR == 1) __syncthreads();
+    }
+    if constexpr (WRES) {
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) wv[k] = use_lds ? wlds[vidx(k)] : load_keep(wr + vidx(k));
     }
 
     int64_t g = blockIdx.x;
@@ -427,10 +427,10 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_vec_kernel(const RowAr
                 if (!in_row(k)) continue;
                 float f[V], fw[V];
                 widen(d[k], f, E{});
-                if (use_lds)
-                    widen(wlds[k * LANES + lane_row], fw, E{});
-                else if constexpr (WRES)
+                if constexpr (WRES)
                     widen(wv[k], fw, E{});
+                else if (use_lds)
+                    widen(wlds[k * LANES + lane_row], fw, E{});
                 else
                     widen(load_keep(wr + k * LANES + lane_row), fw, E{});
 #pragma unroll

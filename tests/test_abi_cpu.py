@@ -174,8 +174,9 @@ def test_bad_forced_configs_rejected():
     assert lds(3, 16, 0, 1) == INV                       # nor the two-pass path
     assert lds(1, 1, 1, 8, hidden=128, lpr=16) == INV    # nor rows sharing a wave
     assert lds(1, 16, 4, 1, hidden=32768) == INV         # 64 KiB of weight: over the 60 KiB bound
-    # the quantised and backward entry points take no staged weight
-    cfg = mbr.Config(1, 2, 1, 2, 0, 0, 1)
+    # the quantised forms take a staged weight on the vector path only; the
+    # backward entry point takes none
+    cfg = mbr.Config(2, 4, 8, 1, 0, 0, 1)
     Q, S = 0x7F0030000000, 0x7F0040000000
     assert L.rmsnorm_dynamic_quant_fwd_ex(A, None, W, None, Q, S, 8, 2048, 1e-5, 1, 0, ctypes.byref(cfg),
                                           None) == INV

@@ -118,6 +118,39 @@ def test_every_quant_config(dtype, fused, q):
 
 
 @pytest.mark.parametrize("q", ["int8", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("fused", [False, True])
+def test_weight_in_lds_matches_bitwise(dtype, fused, q):
+    """weight_lds = 1 on every built quantised vector configuration (the lanes
+    fill their weight registers from the workgroup's LDS copy): one and the
+    most row slots, full and masked rows, a capped grid.  Codes, scales and h
+    bitwise equal to the global-weight kernel, and within the oracle's rule."""
+    vecw = 8 if dtype == "bf16" else 4
+    n = 0
+    for wpr, vpl in _qconfigs(mbr.PATH_VECTOR):
+        lanes = 64 * wpr
+        max_rpb = (1024 if wpr == 16 else 512) // lanes
+        for nvec in sorted({lanes * vpl, max(1, lanes * vpl - 37)}):
+            if nvec * 16 > 60 * 1024:
+                continue
+            for rpb, mb in sorted({(1, 0), (max_rpb, 0), (max_rpb, 2)}):
+                rows = 2 * rpb + 1
+                w = inputs.custom(rows, nvec * vecw, dtype, fused)
+                t = inputs.make(w, seed=900 + n)
+                on = mbr.Config(mbr.PATH_VECTOR, wpr, vpl, rpb, mb, 0, 1)
+                off = mbr.Config(mbr.PATH_VECTOR, wpr, vpl, rpb, mb, 0, 0)
+                say("quant weight in LDS", q, dtype, fused, on, "hidden", nvec * vecw)
+                a, b = run_quant(t, QT[q], w.eps, on), run_quant(t, QT[q], w.eps, off)
+                assert np.array_equal(a[1], b[1]) and np.array_equal(a[2].view(np.uint32), b[2].view(np.uint32))
+                if fused:
+                    assert torch.equal(a[0], b[0])
+                if n % 5 == 0:
+                    check(w, t, QT[q], on)
+                n += 1
+    assert n > 40
+
+
+@pytest.mark.parametrize("q", ["int8", "fp8"])
 def test_zero_rows_and_degenerate(q):
     """A zero row gets scale 0 and zero codes; a row with one non-zero element
     maps it to full scale."""
