@@ -114,6 +114,7 @@ __global__ void __launch_bounds__(max_threads<WPR>()) ln_vec_kernel(const LnArgs
     auto in_row = [&](int k) { return !MASKED || k * LANES + lane < nvec; };
 
     if constexpr (GBL) {
+        // gamma and beta vectors fetched together: one round trip per step
         for (int j = static_cast<int>(threadIdx.x); j < nvec; j += static_cast<int>(blockDim.x)) {
             gb[j] = load_keep(static_cast<const u32x4*>(a.g) + j);
             if (bias) gb[nvec + j] = load_keep(static_cast<const u32x4*>(a.b) + j);

@@ -252,6 +252,30 @@ __device__ __forceinline__ void store_codes(void* q_row, int v, const float (&t)
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// Copy n 16-byte vectors from global memory into LDS with the whole
+// workgroup.  Each step covers up to 4 * blockDim vectors: the number of loads
+// per thread (m) is the same for every thread, so the loads go out back to
+// back, and only the last one can fall past the end (then it is skipped).  The
+// copy costs about one memory round trip instead of one per loop step; the
+// caller places the barrier that publishes it.
+__device__ __forceinline__ void stage_to_lds(const u32x4* src, u32x4* dst, int n) {
+    const int t = static_cast<int>(threadIdx.x), nt = static_cast<int>(blockDim.x);
+    for (int j0 = 0; j0 < n; j0 += 4 * nt) {
+        const int m = min(4, (n - j0 + nt - 1) / nt);  // uniform
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = j0 + u * nt + t;
+            if (u < m && j < n) v[u] = load_keep(src + j);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = j0 + u * nt + t;
+            if (u < m && j < n) dst[j] = v[u];
+        }
+    }
+}
+
 // ---------------------------------------------------------------- vector path
 
 template <int WPR>
@@ -326,12 +350,19 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_vec_kernel(const RowAr
     const bool use_lds = LPR == 64 && a.w_lds != 0;
     u32x4 wv[WRES ? VPL : 1];
     if (use_lds) {
-        for (int j = static_cast<int>(threadIdx.x); j < nvec; j += static_cast<int>(blockDim.x)) wlds[j] = load_keep(wr + j);
+        stage_to_lds(wr, wlds, nvec);
         if (WRES || WPR == 1) __syncthreads();
     }
     if constexpr (WRES) {
+        // one branch around each whole block, so each path issues its loads
+        // back to back
+        if (use_lds) {
 #pragma unroll
-        for (int k = 0; k < VPL; ++k) wv[k] = use_lds ? wlds[vidx(k)] : load_keep(wr + vidx(k));
+            for (int k = 0; k < VPL; ++k) wv[k] = wlds[vidx(k)];
+        } else {
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) wv[k] = load_keep(wr + vidx(k));
+        }
     }
 
     int64_t g = blockIdx.x;
