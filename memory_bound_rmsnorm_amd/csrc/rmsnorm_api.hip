@@ -135,10 +135,11 @@ bool vector_aligned(const Problem& p) {
 
 // The automatic choice, from launch-shape sweeps on MI355X.  Vector path:
 // spread a row over the fewest waves (one row per workgroup) that keep at most
-// two 16-byte vectors of it per lane (three for the fused form, whose lanes
+// two 16-byte vectors of it per lane (four for the fused form, whose lanes
 // then keep the weight resident) -- many short waves keep more requests in
 // flight than a few long ones; e.g. bf16 hidden 8192 runs as 8 waves x 2
-// vectors, the fused bf16 hidden 5120 as 4 waves x 3.  The quantised forms
+// vectors, the fused bf16 hidden 5120 as 4 waves x 3 and 8192 as 4 x 4
+// (fused [12289, 8192]: 128.5 us against 132.3 as 8 x 2).  The quantised forms
 // store half as many bytes per vector and hold the weight anyway; they run
 // fastest with up to four (five fused) vectors per lane: 4 x 4 for hidden
 // 8192, 2 x 5 for the fused 5120.  Element path: at most 8 elements per lane.  When rows are few,
@@ -150,7 +151,7 @@ rmsnorm_config_t choose(int64_t rows, int64_t hidden, int dtype, bool aligned, b
     const int64_t units = vec ? hidden / vec_elems(dtype) : hidden;
     const int* list = vec ? mbr::kVplList : mbr::kEplList;
     const int nlist = vec ? mbr::kNumVpl : mbr::kNumEpl;
-    const int cap = vec ? (qt ? (fused ? 5 : 4) : (fused ? 3 : 2)) : 8;
+    const int cap = vec ? (qt ? (fused ? 5 : 4) : (fused ? 4 : 2)) : 8;
     auto fit = [&](int wpr) {
         const int per = round_up_in(list, nlist, ceil_div(units, int64_t(64) * wpr));
         if (per < 0) return -1;
@@ -167,11 +168,12 @@ rmsnorm_config_t choose(int64_t rows, int64_t hidden, int dtype, bool aligned, b
         per = fit(wpr);
     }
     if (per < 0) return c;
-    if (vec && !fused && !qt && rows >= 1024 && int64_t(64) * wpr * per > units) {
-        // plain rows the cap leaves padded (bf16 hidden 3072, 5120, 6144):
-        // the fewest idle lanes with at most five vectors per lane, ties kept
-        // as chosen.  Sweeps on MI355X: [8192, 5120] 2 x 5 28.6 us against
-        // 31.6 as 8 x 2, [4096, 6144] 4 x 3 18.3 against 19.5.
+    if (vec && !qt && rows >= 1024 && (!fused || rows < 4096) && int64_t(64) * wpr * per > units) {
+        // rows the cap leaves padded (bf16 hidden 3072, 5120, 6144; fused
+        // 5120 below 4096 rows): the fewest idle lanes with at most five
+        // vectors per lane, ties kept as chosen.  Sweeps on MI355X: [8192,
+        // 5120] 2 x 5 28.6 us against 31.6 as 8 x 2, [4096, 6144] 4 x 3 18.3
+        // against 19.5, fused [1024, 5120] 2 x 5 7.6 against 9.0 as 4 x 3.
         int64_t pad = int64_t(64) * wpr * per - units;
         for (int w = 1; w <= 16; w *= 2) {
             const int v = fit(w);
