@@ -245,6 +245,35 @@ def resources(args):
     print("\n".join(out))
 
 
+def occupancy(args):
+    """Runtime occupancy of a workload's kernels from two rocprofv3 --pmc runs
+    (the derived counters OccupancyPercent and MeanOccupancyPerCU), next to the
+    copy kernel measured in the same process."""
+    w = inputs.EVERY_WORKLOAD[args.workload]
+    pm, pn = _counter_means(args.percent, "OccupancyPercent")
+    mm, _ = _counter_means(args.mean, "MeanOccupancyPerCU")
+    out = ["# rocprofv3 --pmc summary: runtime occupancy of %s" % _title(w),
+           "# OccupancyPercent command: %s" % args.command_percent,
+           "# MeanOccupancyPerCU command: %s" % args.command_mean,
+           "# OccupancyPercent: resident wave-cycles as a share of the maximum (32 waves per CU on gfx950);",
+           "# MeanOccupancyPerCU: mean resident waves per CU; both averaged over the dispatches counted."]
+    for i, pred in enumerate(_step_kernels(w)):
+        n, pv = _pick(pm, pred)
+        _, mv = _pick(mm, pred)
+        out += ["kernel_%d: %s" % (i, n.replace(":", ";")),
+                "kernel_%d_dispatches_counted: %d" % (i, pn[n]),
+                "kernel_%d_occupancy_percent: %.1f" % (i, pv),
+                "kernel_%d_mean_waves_per_cu: %.2f" % (i, mv)]
+    cn, cp = _pick(pm, lambda k: COPY_KERNEL_TAG in k)
+    _, cm = _pick(mm, lambda k: COPY_KERNEL_TAG in k)
+    out += ["copy_kernel: %s" % COPY_KERNEL_TAG,
+            "copy_occupancy_percent: %.1f" % cp,
+            "copy_mean_waves_per_cu: %.2f" % cm,
+            "launch_config: %s" % _launch_config(w),
+            "source_sha256: %s" % _build.source_digest(_family(w))]
+    print("\n".join(out))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -258,11 +287,17 @@ def main(argv=None):
     p.add_argument("--workload", default=inputs.HEADLINE)
     p.add_argument("--command-fetch", required=True)
     p.add_argument("--command-write", required=True)
+    o = sub.add_parser("occupancy")
+    o.add_argument("--percent", required=True)
+    o.add_argument("--mean", required=True)
+    o.add_argument("--workload", default=inputs.HEADLINE)
+    o.add_argument("--command-percent", required=True)
+    o.add_argument("--command-mean", required=True)
     r = sub.add_parser("resources")
     r.add_argument("--command", default="python -m memory_bound_rmsnorm_amd._build && "
                                         "python -m memory_bound_rmsnorm_amd.profile_summary resources")
     a = ap.parse_args(argv)
-    {"stats": stats, "pmc": pmc, "resources": resources}[a.cmd](a)
+    {"stats": stats, "pmc": pmc, "occupancy": occupancy, "resources": resources}[a.cmd](a)
 
 
 if __name__ == "__main__":
