@@ -138,7 +138,8 @@ typedef struct {
     int32_t max_blocks;     /* >= 0; 0: one workgroup per group of rows_per_block rows;
                                n > 0: at most n workgroups, each looping over row groups */
     int32_t lanes_per_row;  /* 0: 64 * waves_per_row (whole waves).  VECTOR path of the
-                               forward entry points only: 8, 16 or 32 lanes per row with
+                               forward entry points and of rmsnorm_bwd_ex only (not
+                               layernorm_fwd_ex): 8, 16 or 32 lanes per row with
                                waves_per_row 1 and items_per_lane 1 or 2, several rows
                                sharing a wave; lanes_per_row * rows_per_block must then be
                                a multiple of 64 and at most 512 */
@@ -282,7 +283,11 @@ RMSNORM_API rmsnorm_status_t rmsnorm_bwd(const void* x, const void* weight, cons
  * rows_per_block threads within the limit of rmsnorm_config_t; with dweight,
  * hidden * 4 bytes of LDS at most 60 KiB): the rows of a workgroup's slots then
  * share one partial dweight row.  max_blocks caps the grid and is the number
- * of partial dweight rows (0 = no cap). */
+ * of partial dweight rows (0 = no cap).  lanes_per_row 8, 16 or 32 (rows of at
+ * most 2 * lanes_per_row vectors; waves_per_row 1, items_per_lane 1 or 2;
+ * lanes_per_row * rows_per_block a multiple of 64, at most 512): several rows
+ * per wave, each taking one row slot; with dweight and more than one wave per
+ * workgroup, hidden * 4 bytes of LDS, at most 60 KiB. */
 RMSNORM_API rmsnorm_status_t rmsnorm_bwd_ex(const void* x, const void* weight, const void* dy, void* dx,
                                             void* dweight, int64_t rows, int64_t hidden, float eps,
                                             rmsnorm_dtype_t dtype, void* workspace, size_t workspace_bytes,

@@ -29,6 +29,19 @@ const void* const* bvec_tables(bool masked, bool dw, std::index_sequence<I...> s
                   : (dw ? bvec_table<E, false, true>(s) : bvec_table<E, false, false>(s));
 }
 
+template <class E, bool MASKED, bool DW, size_t... I>
+const void* const* bsub_table(std::index_sequence<I...>) {
+    static const void* const table[] = {reinterpret_cast<const void*>(
+        &rms_bwd_vec_kernel<E, 1, kSwVplList[I % kNumSwVpl], MASKED, DW, kLprList[I / kNumSwVpl]>)...};
+    return table;
+}
+
+template <class E, size_t... I>
+const void* const* bsub_tables(bool masked, bool dw, std::index_sequence<I...> s) {
+    return masked ? (dw ? bsub_table<E, true, true>(s) : bsub_table<E, true, false>(s))
+                  : (dw ? bsub_table<E, false, true>(s) : bsub_table<E, false, false>(s));
+}
+
 template <class E, bool DW, size_t... I>
 const void* const* belem_table(std::index_sequence<I...>) {
     static const void* const table[] = {reinterpret_cast<const void*>(
@@ -51,6 +64,13 @@ const void* bwd_vec_kernel(int dtype, bool dw, bool masked, int wi, int vi) {
     if (wi < 0 || wi >= kNumWpr || vi < 0 || vi >= kNumBwdVpl) return nullptr;
     const void* const* t = dtype == 1 ? bvec_tables<Bf16>(masked, dw, Seq{}) : bvec_tables<F32>(masked, dw, Seq{});
     return t[wi * kNumBwdVpl + vi];
+}
+
+const void* bwd_subwave_kernel(int dtype, bool dw, bool masked, int li, int vi) {
+    using Seq = std::make_index_sequence<kNumLpr * kNumSwVpl>;
+    if (li < 0 || li >= kNumLpr || vi < 0 || vi >= kNumSwVpl) return nullptr;
+    const void* const* t = dtype == 1 ? bsub_tables<Bf16>(masked, dw, Seq{}) : bsub_tables<F32>(masked, dw, Seq{});
+    return t[li * kNumSwVpl + vi];
 }
 
 const void* bwd_elem_kernel(int dtype, bool dw, int wi, int ei) {

@@ -74,6 +74,23 @@ __device__ __forceinline__ void row_sums(float& ss, float& cc, float (&ps)[2][16
     }
 }
 
+// Sum over the 64 / L lanes of a wave that hold the same position in their
+// aligned L-lane groups (L = 8, 16 or 32).  row_ror:8 pairs lane i with lane
+// i ^ 8 inside each 16-lane row, and the two permlane swaps pair lanes i ^ 16
+// and i ^ 32; both partners add the same two values, so every lane returns
+// the same bits as its partners.
+template <int L>
+__device__ __forceinline__ float across_groups_sum(float v) {
+    static_assert(L == 8 || L == 16 || L == 32, "group width");
+    if constexpr (L == 8) v += dpp_mov<0x128>(v);
+    if constexpr (L <= 16) {
+        auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    }
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 // Makes the compiler treat a packed vector as redefined here (no instruction
 // is emitted), so values widened from it before this point are recomputed
 // after it instead of being held: a row's x, dy and w then stay packed across
@@ -99,12 +116,19 @@ __device__ __forceinline__ void store_partial(float* p, const float* acc, F32) {
 // order, into the workgroup's single partial row: fewer partial rows for the
 // same number of waves in flight.  (A conditional next-row prefetch measured
 // the same as none: the compiler waits for every load after the branch.)
-template <class E, int WPR, int VPL, bool MASKED, bool DW>
+//
+// LPR < 64 (with WPR 1): rows narrower than a wave share it, each row owning
+// an aligned group of LPR lanes (8, 16 or 32) and being one row slot; the row
+// sums are group sums with no LDS and no barrier.  A wave's groups add their
+// dweight sums among themselves first, and the LDS combine then runs over
+// waves instead of slots.
+template <class E, int WPR, int VPL, bool MASKED, bool DW, int LPR = 64>
 __global__ void __launch_bounds__(max_threads<WPR>()) rms_bwd_vec_kernel(const BwdArgs a) {
-    constexpr int LANES = 64 * WPR;
+    static_assert(LPR == 64 || WPR == 1, "sub-wave rows use one wave");
+    constexpr int LANES = LPR < 64 ? LPR : 64 * WPR;
     constexpr int V = E::kVec;
     const int wave = wave_id();
-    const int slot = wave / WPR;
+    const int slot = LPR < 64 ? static_cast<int>(threadIdx.x) / LPR : wave / WPR;
     const int lane = static_cast<int>(threadIdx.x) - slot * LANES;
     const int nvec = a.units;
     const int rpb = a.rows_per_block;
@@ -138,13 +162,19 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_bwd_vec_kernel(const B
         const bool valid = row < a.rows;
         u32x4 xv[VPL], gv[VPL];
         float ss = 0.f, cc = 0.f;
-        if (valid) {
-            const char* xr = static_cast<const char*>(a.x) + row * row_bytes;
-            const char* gr = static_cast<const char*>(a.dy) + row * row_bytes;
+        // Sub-wave rows address from the group's first row (wave-uniform)
+        // plus a 32-bit offset per lane group; a group past the last row
+        // loads the last row again instead of branching around the loads,
+        // and its sums are dropped.
+        const int64_t brow = LPR < 64 ? grp * rpb : row;
+        const unsigned soff = LPR < 64 ? static_cast<unsigned>(((valid ? row : a.rows - 1) - brow) * row_bytes) : 0u;
+        if (LPR < 64 || valid) {
+            const char* xr = static_cast<const char*>(a.x) + brow * row_bytes;
+            const char* gr = static_cast<const char*>(a.dy) + brow * row_bytes;
 #pragma unroll
-            for (int k = 0; k < VPL; ++k) xv[k] = load_stream(at(xr, voff(k)));
+            for (int k = 0; k < VPL; ++k) xv[k] = load_stream(at(xr, soff + voff(k)));
 #pragma unroll
-            for (int k = 0; k < VPL; ++k) gv[k] = load_stream(at(gr, voff(k)));
+            for (int k = 0; k < VPL; ++k) gv[k] = load_stream(at(gr, soff + voff(k)));
 #pragma unroll
             for (int k = 0; k < VPL; ++k) {
                 float fx[V], fg[V], fw[V];
@@ -161,7 +191,12 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_bwd_vec_kernel(const B
                 cc += in_row(k) ? c : 0.f;
             }
         }
-        row_sums<WPR>(ss, cc, ps, pc, it, wave, slot);
+        if constexpr (LPR < 64) {
+            ss = group_sum<LPR>(ss);
+            cc = group_sum<LPR>(cc);
+        } else {
+            row_sums<WPR>(ss, cc, ps, pc, it, wave, slot);
+        }
         if (!valid) continue;
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
@@ -171,7 +206,7 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_bwd_vec_kernel(const B
         }
         const float r = rsqrtf(ss / a.hidden_f + a.eps);
         const float k2 = r * r * cc / a.hidden_f;
-        char* dxr = static_cast<char*>(a.dx) + row * row_bytes;
+        char* dxr = static_cast<char*>(a.dx) + brow * row_bytes;
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             if (!in_row(k)) continue;
@@ -181,7 +216,7 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_bwd_vec_kernel(const B
             widen(wv[k], fw, E{});
 #pragma unroll
             for (int i = 0; i < V; ++i) d[i] = r * (fg[i] * fw[i] - fx[i] * k2);
-            store_stream(reinterpret_cast<u32x4*>(dxr + voff(k)), narrow(d, E{}));
+            store_stream(reinterpret_cast<u32x4*>(dxr + soff + voff(k)), narrow(d, E{}));
             if constexpr (DW) {
 #pragma unroll
                 for (int i = 0; i < V; ++i) acc[k * V + i] += (fg[i] * fx[i]) * r;
@@ -190,17 +225,28 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_bwd_vec_kernel(const B
     }
     if constexpr (DW) {
         float* pr = a.part + static_cast<int64_t>(blockIdx.x) * a.ld;
-        if (rpb == 1) {
+        // Rows narrower than a wave: the lane groups of a wave first add their
+        // sums across groups (every group ends with the same bits) and group 0
+        // then stands for the wave.
+        if constexpr (LPR < 64) {
+#pragma unroll
+            for (int i = 0; i < VPL * V; ++i) acc[i] = across_groups_sum<LPR>(acc[i]);
+        }
+        const int parties = LPR < 64 ? static_cast<int>(blockDim.x) / 64 : rpb;
+        const int party = LPR < 64 ? wave : slot;
+        const bool speaks = LPR == 64 || (threadIdx.x & 63) < LPR;
+        if (parties == 1) {
+            if (!speaks) return;
 #pragma unroll
             for (int k = 0; k < VPL; ++k)
                 if (in_row(k)) store_partial(pr + static_cast<int64_t>(k * LANES + lane) * V, acc + k * V, E{});
             return;
         }
-        // slots add their sums into one LDS row in slot order, then the whole
-        // workgroup writes it out
+        // the parties add their sums into one LDS row in order, then the
+        // whole workgroup writes it out
         extern __shared__ float comb[];  // nvec * V floats
-        for (int s = 0; s < rpb; ++s) {
-            if (slot == s) {
+        for (int s = 0; s < parties; ++s) {
+            if (party == s && speaks) {
 #pragma unroll
                 for (int k = 0; k < VPL; ++k) {
                     if (!in_row(k)) continue;

@@ -64,6 +64,9 @@ constexpr bool bwd_vec_built(int wpr, int vpl) { return wpr < 16 || vpl <= 4; }
 
 const void* bwd_vec_kernel(int dtype, bool dw, bool masked, int wpr_index, int vpl_index);
 const void* bwd_elem_kernel(int dtype, bool dw, int wpr_index, int epl_index);
+// Backward vector kernel with rows narrower than a wave (kLprList lanes per
+// row, kSwVplList vectors per lane, one wave per row slot group).
+const void* bwd_subwave_kernel(int dtype, bool dw, bool masked, int lpr_index, int vpl_index);
 const void* bwd_twopass_kernel(int dtype, bool dw, bool vec);
 const void* bwd_dw_kernel(int dtype);
 

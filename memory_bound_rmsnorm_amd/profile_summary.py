@@ -212,8 +212,14 @@ def resources(args):
         units = w.hidden // (4 if w.dtype == "f32" else 8)
         masked = 64 * cfg.waves_per_row * per != units
         if w.backward:
-            fam = {1: "rms_bwd_vec_kernel", 2: "rms_bwd_elem_kernel", 3: "rms_bwd_twopass_kernel"}[cfg.path]
-            mangled = "%sINS_%d%sELi%dELi%dELb%dELb1EEEv" % (fam, len(e), e, cfg.waves_per_row, per, int(masked))
+            if cfg.path == 1:  # rms_bwd_vec_kernel<E, WPR, VPL, MASKED, DW, LPR>
+                lpr = cfg.lanes_per_row or 64
+                masked = (lpr if lpr < 64 else 64 * cfg.waves_per_row) * per != units
+                mangled = "rms_bwd_vec_kernelINS_%d%sELi%dELi%dELb%dELb1ELi%dEEEv" % (
+                    len(e), e, cfg.waves_per_row, per, int(masked), lpr)
+            else:  # rms_bwd_elem_kernel<E, WPR, EPL, DW>, rms_bwd_twopass_kernel<E, VEC, DW>
+                fam = {2: "rms_bwd_elem_kernel", 3: "rms_bwd_twopass_kernel"}[cfg.path]
+                mangled = "%sINS_%d%sELi%dELi%dELb%dELb1EEEv" % (fam, len(e), e, cfg.waves_per_row, per, int(masked))
         elif w.layernorm:
             mangled = "ln_vec_kernelINS_%d%sELi%dELi%dELb%dELb%dEEEv" % (len(e), e, cfg.waves_per_row, per, int(masked),
                                                                    int(bool(cfg.weight_lds)))

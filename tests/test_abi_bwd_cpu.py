@@ -44,8 +44,8 @@ def test_workspace_size_formula():
         cfg = mbr.Config(mbr.PATH_ELEMENT, 4, 8, 1, 3)
         assert mbr.rmsnorm_bwd_workspace_size(rows, hidden, dt, cfg) == min(rows, 3) * ld * 4
         # row slots share a partial row: one per group of rows_per_block rows
-        for rpb, mb in ((4, 3), (4, 0), (2, 1000)):
-            cfg = mbr.Config(mbr.PATH_VECTOR, 2, 2, rpb, mb)
+        for rpb, mb, lpr in ((4, 3, 0), (4, 0, 0), (2, 1000, 0), (16, 7, 16), (8, 0, 8)):
+            cfg = mbr.Config(mbr.PATH_VECTOR, 1 if lpr else 2, 2, rpb, mb, lpr)
             groups = -(-rows // rpb)
             assert mbr.rmsnorm_bwd_workspace_size(rows, hidden, dt, cfg) == (min(groups, mb) if mb else groups) * ld * 4
     assert mbr.lib().rmsnorm_bwd_workspace_size(4, 16, 1, None, None) == INV
@@ -64,6 +64,18 @@ def test_headline_choice():
     # few rows: one row per workgroup, spread over more waves
     c = mbr.rmsnorm_select_bwd_config(64, 2048, torch.float32, True)
     assert (c.path, c.waves_per_row, c.items_per_lane, c.rows_per_block) == (mbr.PATH_VECTOR, 8, 1, 1)
+    # narrow rows: lane groups of 8, 16 or 32 with at most two vectors per lane,
+    # four waves per workgroup (eight with one vector per lane), fewer slots
+    # when the rows would make under 256 groups
+    for rows, hidden, dt, want in [(262144, 128, torch.bfloat16, (8, 2, 32)), (262144, 64, torch.bfloat16, (8, 1, 64)),
+                                   (131072, 256, torch.bfloat16, (16, 2, 16)), (65536, 512, torch.bfloat16, (32, 2, 8)),
+                                   (131072, 128, torch.float32, (16, 2, 16)), (4096, 128, torch.bfloat16, (8, 2, 16)),
+                                   (1024, 128, torch.bfloat16, (8, 2, 8)), (65536, 24, torch.bfloat16, (8, 1, 64))]:
+        c = mbr.rmsnorm_select_bwd_config(rows, hidden, dt, True)
+        assert (c.path, c.waves_per_row, c.max_blocks) == (mbr.PATH_VECTOR, 1, 512), (rows, hidden)
+        assert (c.lanes_per_row, c.items_per_lane, c.rows_per_block) == want, (rows, hidden, c.as_dict())
+    c = mbr.rmsnorm_select_bwd_config(1023, 128, torch.bfloat16, True)
+    assert c.lanes_per_row == 0
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
@@ -73,10 +85,14 @@ def test_choice_is_built_and_covering(dtype, aligned, rows):
     v = 8 if dtype == torch.bfloat16 else 4
     for hidden in [1, 7, 8, 64, 100, 1000, 2048, 4095, 4096, 5120, 8192, 16384, 32768, 32776, 65536, 131080]:
         c = mbr.rmsnorm_select_bwd_config(rows, hidden, dtype, aligned)
-        lanes = 64 * c.waves_per_row
+        lanes = c.lanes_per_row or 64 * c.waves_per_row
         assert c.max_blocks >= 1 and c.waves_per_row in (1, 2, 4, 8, 16)
         assert c.rows_per_block == 1 or (c.path == mbr.PATH_VECTOR and lanes * c.rows_per_block <= 512
                                          and hidden * 4 <= 60 * 1024)
+        if c.lanes_per_row:  # rows narrower than a wave: whole waves per workgroup
+            assert c.path == mbr.PATH_VECTOR and c.lanes_per_row in (8, 16, 32) and c.waves_per_row == 1
+            assert c.items_per_lane in (1, 2) and lanes * c.rows_per_block % 64 == 0
+            assert rows >= 1024 and hidden // v <= 64
         if c.path == mbr.PATH_VECTOR:
             assert aligned and hidden % v == 0
             assert c.items_per_lane in range(1, 9) and (c.waves_per_row < 16 or c.items_per_lane <= 4)
@@ -121,6 +137,15 @@ def test_bad_forced_configs():
         n = mbr.rmsnorm_bwd_workspace_size(rows, hidden, torch.bfloat16, cfg) if cfg.max_blocks >= 0 else 0
         st = L.rmsnorm_bwd_ex(X, W, G, D, DW, rows, hidden, 1e-5, 1, WS, n, ctypes.byref(cfg), None)
         assert st == INV, cfg
+    # rows narrower than a wave: 8, 16 or 32 lanes, one wave per row group,
+    # one or two vectors per lane covering the row, whole waves per workgroup
+    for cfg in [mbr.Config(mbr.PATH_VECTOR, 2, 1, 8, 0, 16), mbr.Config(mbr.PATH_VECTOR, 1, 3, 4, 0, 16),
+                mbr.Config(mbr.PATH_VECTOR, 1, 1, 2, 0, 16), mbr.Config(mbr.PATH_VECTOR, 1, 1, 64, 0, 16),
+                mbr.Config(mbr.PATH_VECTOR, 1, 1, 8, 0, 12), mbr.Config(mbr.PATH_ELEMENT, 1, 1, 4, 0, 16),
+                mbr.Config(mbr.PATH_VECTOR, 1, 1, 8, 0, 8), mbr.Config(mbr.PATH_TWO_PASS, 1, 0, 1, 0, 32)]:
+        n = mbr.rmsnorm_bwd_workspace_size(rows, 128, torch.bfloat16, cfg)
+        st = L.rmsnorm_bwd_ex(X, W, G, D, DW, rows, 128, 1e-5, 1, WS, n, ctypes.byref(cfg), None)
+        assert st == INV, cfg.as_dict()
     # slots combine dweight in LDS: hidden * 4 bytes, at most 60 KiB
     cfg = mbr.Config(mbr.PATH_VECTOR, 4, 8, 2, 0)
     n = mbr.rmsnorm_bwd_workspace_size(rows, 16384, torch.bfloat16, cfg)

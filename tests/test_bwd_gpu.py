@@ -93,6 +93,22 @@ def test_bwd_ragged_shapes(rows, hidden, dtype):
     check(w, inputs.make(w, seed=rows * 5 + hidden))
 
 
+NARROW = [(1024, 8), (1027, 64), (4096, 128), (3001, 256), (2050, 384), (1500, 512), (20000, 128), (9000, 24)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,hidden", NARROW)
+def test_bwd_narrow_rows_automatic(rows, hidden, dtype):
+    """Per-head widths from 1024 rows take several rows per wave when they
+    are whole vectors; checked through the automatic choice."""
+    w = inputs.custom(rows, hidden, dtype, backward=True)
+    cfg = effective_config(rows, hidden, dtype)
+    say("bwd narrow", rows, hidden, dtype, cfg.as_dict())
+    if hidden % (8 if dtype == "bf16" else 4) == 0 and hidden // (8 if dtype == "bf16" else 4) <= 64:
+        assert cfg.lanes_per_row in (8, 16, 32)
+    check(w, inputs.make(w, seed=rows + 3 * hidden))
+
+
 def test_bwd_many_rows_per_workgroup():
     """Far more rows than partial rows: every workgroup walks ~100 rows."""
     w = inputs.custom(40000, 1024, "bf16", backward=True)
@@ -143,6 +159,41 @@ def test_bwd_rows_per_block_configs(dtype):
                     check(w, inputs.make(w, seed=1000 + n), cfg, want_dw=(n % 3 != 2))
                     n += 1
     assert n > 100
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_subwave_configs(dtype):
+    """Rows narrower than a wave (8, 16 or 32 lanes per row): one wave and
+    several waves per workgroup, full and masked rows, rows that leave part
+    of a wave or of the last group idle, capped grids; dx-only calls every
+    third case."""
+    vecw = 8 if dtype == "bf16" else 4
+    n = 0
+    for lpr in (8, 16, 32):
+        for vpl in (1, 2):
+            for rpb in (64 // lpr, 128 // lpr, 512 // lpr):
+                for nvec in sorted({lpr * vpl, max(1, lpr * (vpl - 1) + 3)}):
+                    for mb, rows in ((0, rpb + 1), (3, 7 * rpb + 5), (0, 3), (0, 1)):
+                        cfg = mbr.Config(mbr.PATH_VECTOR, 1, vpl, rpb, mb, lpr)
+                        w = inputs.custom(rows, nvec * vecw, dtype, backward=True)
+                        say("bwd sub-wave", dtype, cfg.as_dict(), "hidden", nvec * vecw, "rows", rows)
+                        check(w, inputs.make(w, seed=2000 + n), cfg, want_dw=(n % 3 != 2))
+                        n += 1
+    assert n > 100
+
+
+def test_bwd_subwave_many_groups_deterministic():
+    """Per-head rows (bf16, hidden 128) over a capped grid: parity, and the
+    same bits on a second call."""
+    w = inputs.custom(40000, 128, "bf16", backward=True)
+    cfg = mbr.Config(mbr.PATH_VECTOR, 1, 1, 32, 64, 16)
+    say("bwd sub-wave many groups", cfg.as_dict())
+    t = inputs.make(w, seed=9)
+    check(w, t, cfg)
+    dev = {k: v.cuda() for k, v in t.items()}
+    a = run_bwd(dev["x"], dev["weight"], dev["dy"], w.eps, cfg)
+    b = run_bwd(dev["x"], dev["weight"], dev["dy"], w.eps, cfg)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
 def test_bwd_rows_per_block_many_groups_deterministic():
