@@ -137,9 +137,8 @@ typedef struct {
                                (1024 when waves_per_row == 16); TWO_PASS: must be 1 */
     int32_t max_blocks;     /* >= 0; 0: one workgroup per group of rows_per_block rows;
                                n > 0: at most n workgroups, each looping over row groups */
-    int32_t lanes_per_row;  /* 0: 64 * waves_per_row (whole waves).  VECTOR path of the
-                               forward entry points and of rmsnorm_bwd_ex only (not
-                               layernorm_fwd_ex): 8, 16 or 32 lanes per row with
+    int32_t lanes_per_row;  /* 0: 64 * waves_per_row (whole waves).  VECTOR path of every
+                               entry point with a configuration: 8, 16 or 32 lanes per row with
                                waves_per_row 1 and items_per_lane 1 or 2, several rows
                                sharing a wave; lanes_per_row * rows_per_block must then be
                                a multiple of 64 and at most 512 */
@@ -334,7 +333,9 @@ RMSNORM_API rmsnorm_status_t layernorm_fwd(const void* x, const void* gamma, con
  * and beta staged in LDS once per workgroup, hidden * size bytes each, at most
  * 60 KiB together) is taken on path VECTOR only; rows_per_block > 1 requires
  * it (the row slots share that copy), with 64 * waves_per_row *
- * rows_per_block within the limit of rmsnorm_config_t. */
+ * rows_per_block within the limit of rmsnorm_config_t.  lanes_per_row 8, 16
+ * or 32 (weight_lds 0): several rows per wave, each taking one row slot and
+ * holding its gamma / beta slice in registers. */
 RMSNORM_API rmsnorm_status_t layernorm_fwd_ex(const void* x, const void* gamma, const void* beta, void* out,
                                               int64_t rows, int64_t hidden, float eps, rmsnorm_dtype_t dtype,
                                               const rmsnorm_config_t* cfg, void* stream);

@@ -28,6 +28,13 @@ const void* const* lvec_table_for(bool masked, bool gbl, std::index_sequence<I..
     return masked ? lvec_table<E, true, false>(seq) : lvec_table<E, false, false>(seq);
 }
 
+template <class E, bool MASKED, size_t... I>
+const void* const* lsub_table(std::index_sequence<I...>) {
+    static const void* const table[] = {reinterpret_cast<const void*>(
+        &ln_vec_kernel<E, 1, kSwVplList[I % kNumSwVpl], MASKED, false, kLprList[I / kNumSwVpl]>)...};
+    return table;
+}
+
 template <class E, size_t... I>
 const void* const* lelem_table(std::index_sequence<I...>) {
     static const void* const table[] = {
@@ -43,6 +50,14 @@ const void* ln_vec_kernel_ptr(int dtype, bool masked, bool gamma_beta_lds, int w
     const void* const* t = dtype == 1 ? lvec_table_for<Bf16>(masked, gamma_beta_lds, Seq{})
                                       : lvec_table_for<F32>(masked, gamma_beta_lds, Seq{});
     return t[wi * kNumLnVpl + vi];
+}
+
+const void* ln_subwave_kernel_ptr(int dtype, bool masked, int li, int vi) {
+    using Seq = std::make_index_sequence<kNumLpr * kNumSwVpl>;
+    if (li < 0 || li >= kNumLpr || vi < 0 || vi >= kNumSwVpl) return nullptr;
+    const void* const* t = dtype == 1 ? (masked ? lsub_table<Bf16, true>(Seq{}) : lsub_table<Bf16, false>(Seq{}))
+                                      : (masked ? lsub_table<F32, true>(Seq{}) : lsub_table<F32, false>(Seq{}));
+    return t[li * kNumSwVpl + vi];
 }
 
 const void* ln_elem_kernel_ptr(int dtype, int wi, int ei) {

@@ -93,16 +93,23 @@ __device__ __forceinline__ LnMoments ln_moments(float m0, const float (&tq)[2], 
 // (a slot past the last row reads the last row again and stores nothing).
 // Without GBL a workgroup works on one row at a time and loads gamma and beta
 // per row; the slot terms fold away at compile time.
-template <class E, int WPR, int VPL, bool MASKED, bool GBL>
+//
+// LPR < 64 (one wave, no GBL): rows narrower than a wave share it, each row
+// owning an aligned group of LPR lanes (8, 16 or 32) and being one row slot;
+// both reductions are group sums with no LDS and no barrier, and each lane
+// loads its gamma / beta slice once for the whole walk.
+template <class E, int WPR, int VPL, bool MASKED, bool GBL, int LPR = 64>
 __global__ void __launch_bounds__(max_threads<WPR>()) ln_vec_kernel(const LnArgs a) {
-    constexpr int LANES = 64 * WPR;
+    static_assert(LPR == 64 || (WPR == 1 && !GBL), "sub-wave rows use one wave and per-lane gamma / beta");
+    constexpr bool SUB = LPR < 64;
+    constexpr int LANES = SUB ? LPR : 64 * WPR;
     constexpr int V = E::kVec;
     const int wave = wave_id();
-    const int slot = GBL ? wave / WPR : 0;
+    const int slot = SUB ? static_cast<int>(threadIdx.x) / LPR : GBL ? wave / WPR : 0;
     const int lane = static_cast<int>(threadIdx.x) - slot * LANES;
     const int nvec = a.units;
-    const int64_t rpb = GBL ? a.rows_per_block : 1;
-    const int64_t n_groups = GBL ? a.n_groups : a.rows;
+    const int64_t rpb = GBL || SUB ? a.rows_per_block : 1;
+    const int64_t n_groups = GBL || SUB ? a.n_groups : a.rows;
     const bool bias = a.b != nullptr;
     __shared__ float s1[1][16], s2[2][16];
     extern __shared__ u32x4 gb[];  // GBL: gamma [nvec], then beta [nvec]
@@ -122,13 +129,26 @@ __global__ void __launch_bounds__(max_threads<WPR>()) ln_vec_kernel(const LnArgs
         if constexpr (WPR == 1) __syncthreads();
     }
 
+    u32x4 gs[SUB ? VPL : 1], bs[SUB ? VPL : 1];
+    if constexpr (SUB) {
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            gs[k] = load_keep(static_cast<const u32x4*>(a.g) + vidx(k));
+            if (bias) bs[k] = load_keep(static_cast<const u32x4*>(a.b) + vidx(k));
+        }
+    }
+
     for (int64_t grp = blockIdx.x; grp < n_groups; grp += gridDim.x) {
         const int64_t row = grp * rpb + slot;
-        const bool valid = !GBL || row < a.rows;
-        const u32x4* xr = static_cast<const u32x4*>(a.x) + (valid ? row : a.rows - 1) * nvec;
+        const bool valid = !(GBL || SUB) || row < a.rows;
+        // sub-wave rows address from the group's first row (wave-uniform)
+        // plus a per-lane-group vector offset
+        const int64_t brow = SUB ? grp * rpb : valid ? row : a.rows - 1;
+        const int soff = SUB ? static_cast<int>(((valid ? row : a.rows - 1) - brow) * nvec) : 0;
+        const u32x4* xr = static_cast<const u32x4*>(a.x) + brow * nvec;
         u32x4 d[VPL];
 #pragma unroll
-        for (int k = 0; k < VPL; ++k) d[k] = load_stream(xr + vidx(k));
+        for (int k = 0; k < VPL; ++k) d[k] = load_stream(xr + (soff + vidx(k)));
         float s[1] = {0.f};
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
@@ -139,10 +159,14 @@ __global__ void __launch_bounds__(max_threads<WPR>()) ln_vec_kernel(const LnArgs
             for (int i = 0; i < V; ++i) t += f[i];
             s[0] += in_row(k) ? t : 0.f;
         }
-        block_sums<WPR>(s, s1, wave, WPR, slot * WPR);
+        if constexpr (SUB) {
+            s[0] = group_sum<LPR>(s[0]);
+        } else {
+            block_sums<WPR>(s, s1, wave, WPR, slot * WPR);
+        }
         const float m0 = s[0] / a.hidden_f;
-        u32x4 gv[GBL ? 1 : VPL], bv[GBL ? 1 : VPL];
-        if constexpr (!GBL) {
+        u32x4 gv[GBL || SUB ? 1 : VPL], bv[GBL || SUB ? 1 : VPL];
+        if constexpr (!GBL && !SUB) {
 #pragma unroll
             for (int k = 0; k < VPL; ++k) {
                 gv[k] = load_keep(static_cast<const u32x4*>(a.g) + vidx(k));
@@ -164,10 +188,15 @@ __global__ void __launch_bounds__(max_threads<WPR>()) ln_vec_kernel(const LnArgs
             tq[0] += in_row(k) ? t : 0.f;
             tq[1] += in_row(k) ? q : 0.f;
         }
-        block_sums<WPR>(tq, s2, wave, WPR, slot * WPR);
-        if (!valid) continue;  // GBL only: a slot past the last row
+        if constexpr (SUB) {
+            tq[0] = group_sum<LPR>(tq[0]);
+            tq[1] = group_sum<LPR>(tq[1]);
+        } else {
+            block_sums<WPR>(tq, s2, wave, WPR, slot * WPR);
+        }
+        if (!valid) continue;  // GBL or sub-wave only: a slot past the last row
         const LnMoments m = ln_moments(m0, tq, a);
-        u32x4* outr = static_cast<u32x4*>(a.out) + row * nvec;
+        u32x4* outr = static_cast<u32x4*>(a.out) + (SUB ? brow * nvec + soff : row * nvec);
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             if (!in_row(k)) continue;
@@ -176,6 +205,9 @@ __global__ void __launch_bounds__(max_threads<WPR>()) ln_vec_kernel(const LnArgs
             if constexpr (GBL) {
                 widen(gb[k * LANES + lane], fg, E{});
                 if (bias) widen(gb[nvec + k * LANES + lane], fb, E{});
+            } else if constexpr (SUB) {
+                widen(gs[k], fg, E{});
+                if (bias) widen(bs[k], fb, E{});
             } else {
                 widen(gv[k], fg, E{});
                 if (bias) widen(bv[k], fb, E{});

@@ -623,11 +623,32 @@ bool ln_vector_aligned(const LnProblem& p) {
 // 1 wave x 8 vectors 25.9 us, 2 x 4 26.1, 4 x 2 28.3, 8 x 1 31.8.  Wide rows
 // with enough of them then move to row slots sharing gamma/beta in LDS
 // (below).  Rows beyond every built register configuration take the
-// multi-pass path.
+// multi-pass path.  Narrow rows (at most 64 vectors, from 1024 rows) share
+// waves in lane groups of 8, 16 or 32 with at most two vectors per lane:
+// workgroups of four waves and an uncapped grid, or eight waves and 1024
+// workgroups with one vector per lane; fewer row slots while there would be
+// under 256 groups of rows.  HIP-graph sweeps on MI355X: bf16 [262144, 128]
+// 23.2 us against 70.4 with a wave per row, [131072, 256] 23.2 against 40.1,
+// [262144, 64] 14.4 against 68.2.
 rmsnorm_config_t choose_ln(int64_t rows, int64_t hidden, int dtype, bool aligned) {
     rmsnorm_config_t c = {RMSNORM_PATH_TWO_PASS, 16, 0, 1, 0, 0, 0};
     const bool vec = aligned && hidden % vec_elems(dtype) == 0;
     const int64_t units = vec ? hidden / vec_elems(dtype) : hidden;
+    if (vec && units <= 64 && rows >= 1024) {
+        int lpr = 0;
+        for (int i = 0; i < mbr::kNumLpr && !lpr; ++i)
+            if (ceil_div(units, int64_t(mbr::kLprList[i])) <= 2) lpr = mbr::kLprList[i];
+        const int vpl = static_cast<int>(ceil_div(units, int64_t(lpr)));
+        int rpb = (vpl == 1 ? 512 : 256) / lpr;
+        while (rpb > 64 / lpr && rows < int64_t(rpb) * 256) rpb /= 2;
+        c.path = RMSNORM_PATH_VECTOR;
+        c.waves_per_row = 1;
+        c.items_per_lane = vpl;
+        c.rows_per_block = rpb;
+        c.max_blocks = vpl == 1 ? 1024 : 0;
+        c.lanes_per_row = lpr;
+        return c;
+    }
     const int* list = vec ? mbr::kLnVplList : mbr::kLnEplList;
     const int nlist = vec ? mbr::kNumLnVpl : mbr::kNumLnEpl;
     const int cap = 8;
@@ -711,10 +732,12 @@ rmsnorm_status_t run_ln(const LnProblem& p, const rmsnorm_config_t* user, void* 
     const int wi = index_of(mbr::kWprList, mbr::kNumWpr, c.waves_per_row);
     if (wi < 0 || c.rows_per_block < 1 || c.max_blocks < 0) return RMSNORM_ERR_INVALID_ARG;
     if (c.weight_lds != 0 && c.weight_lds != 1) return RMSNORM_ERR_INVALID_ARG;
-    if ((c.rows_per_block != 1 || c.weight_lds) && c.path != RMSNORM_PATH_VECTOR) return RMSNORM_ERR_INVALID_ARG;
-    if (c.rows_per_block != 1 && !c.weight_lds) return RMSNORM_ERR_INVALID_ARG;  // slots share the LDS copy
-    if (c.lanes_per_row != 0 && c.lanes_per_row != 64 * c.waves_per_row) return RMSNORM_ERR_INVALID_ARG;
-    const int64_t lanes = int64_t(64) * c.waves_per_row;
+    const bool whole = c.lanes_per_row == 0 || c.lanes_per_row == 64 * c.waves_per_row;
+    if ((c.rows_per_block != 1 || c.weight_lds || !whole) && c.path != RMSNORM_PATH_VECTOR)
+        return RMSNORM_ERR_INVALID_ARG;
+    // whole-wave slots share the LDS copy; sub-wave rows keep gamma / beta per lane
+    if (whole ? c.rows_per_block != 1 && !c.weight_lds : c.weight_lds != 0) return RMSNORM_ERR_INVALID_ARG;
+    const int64_t lanes = whole ? int64_t(64) * c.waves_per_row : c.lanes_per_row;
     const int64_t threads = lanes * c.rows_per_block;
     mbr::LnArgs a;
     a.x = p.x;
@@ -733,9 +756,19 @@ rmsnorm_status_t run_ln(const LnProblem& p, const rmsnorm_config_t* user, void* 
             if (!aligned || p.hidden % vec_elems(p.dtype) != 0) return RMSNORM_ERR_INVALID_ARG;
             const int vi = index_of(mbr::kLnVplList, mbr::kNumLnVpl, c.items_per_lane);
             const int64_t nvec = p.hidden / vec_elems(p.dtype);
-            if (vi < 0 || lanes * c.items_per_lane < nvec) return RMSNORM_ERR_INVALID_ARG;
-            if (threads > mbr::max_threads_for(c.waves_per_row)) return RMSNORM_ERR_INVALID_ARG;
-            fn = mbr::ln_vec_kernel_ptr(p.dtype, lanes * c.items_per_lane != nvec, c.weight_lds != 0, wi, vi);
+            const bool masked = lanes * c.items_per_lane != nvec;
+            if (whole) {
+                if (vi < 0 || lanes * c.items_per_lane < nvec) return RMSNORM_ERR_INVALID_ARG;
+                if (threads > mbr::max_threads_for(c.waves_per_row)) return RMSNORM_ERR_INVALID_ARG;
+                fn = mbr::ln_vec_kernel_ptr(p.dtype, masked, c.weight_lds != 0, wi, vi);
+            } else {  // several rows per wave, lanes_per_row lanes each
+                const int li = index_of(mbr::kLprList, mbr::kNumLpr, c.lanes_per_row);
+                const int si = index_of(mbr::kSwVplList, mbr::kNumSwVpl, c.items_per_lane);
+                if (c.waves_per_row != 1 || li < 0 || si < 0 || lanes * c.items_per_lane < nvec)
+                    return RMSNORM_ERR_INVALID_ARG;
+                if (threads % 64 != 0 || threads > mbr::max_threads_for(1)) return RMSNORM_ERR_INVALID_ARG;
+                fn = mbr::ln_subwave_kernel_ptr(p.dtype, masked, li, si);
+            }
             a.units = static_cast<int32_t>(nvec);
             if (c.weight_lds) {
                 lds = static_cast<size_t>(nvec) * kVectorBytes * (p.b ? 2 : 1);

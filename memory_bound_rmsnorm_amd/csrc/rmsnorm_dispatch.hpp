@@ -81,6 +81,9 @@ constexpr int kNumLnVpl = sizeof(kLnVplList) / sizeof(int);
 constexpr int kNumLnEpl = sizeof(kLnEplList) / sizeof(int);
 
 const void* ln_vec_kernel_ptr(int dtype, bool masked, bool gamma_beta_lds, int wpr_index, int vpl_index);
+// LayerNorm vector kernel with rows narrower than a wave (kLprList lanes per
+// row, kSwVplList vectors per lane, per-lane gamma / beta).
+const void* ln_subwave_kernel_ptr(int dtype, bool masked, int lpr_index, int vpl_index);
 const void* ln_elem_kernel_ptr(int dtype, int wpr_index, int epl_index);
 const void* ln_multipass_kernel_ptr(int dtype, bool vec);
 

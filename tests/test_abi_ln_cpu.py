@@ -33,9 +33,15 @@ def test_choice_is_built_and_covering(dtype, aligned, rows):
     v = 8 if dtype == torch.bfloat16 else 4
     for hidden in [1, 7, 8, 64, 100, 768, 1000, 2048, 4095, 4096, 5120, 8192, 16384, 32768, 32776, 65536, 131080]:
         c = mbr.layernorm_select_config(rows, hidden, dtype, aligned)
-        lanes = 64 * c.waves_per_row
-        assert c.max_blocks == 0 and c.waves_per_row in (1, 2, 4, 8, 16)
-        if c.weight_lds:  # gamma and beta (sized for both) in LDS, shared by the row slots
+        lanes = c.lanes_per_row or 64 * c.waves_per_row
+        assert c.waves_per_row in (1, 2, 4, 8, 16)
+        assert c.max_blocks == (1024 if c.lanes_per_row and c.items_per_lane == 1 else 0)
+        if c.lanes_per_row:  # rows narrower than a wave, several per wave, whole waves per workgroup
+            assert c.path == mbr.PATH_VECTOR and c.lanes_per_row in (8, 16, 32) and c.waves_per_row == 1
+            assert c.items_per_lane in (1, 2) and lanes * c.rows_per_block % 64 == 0
+            assert lanes * c.rows_per_block <= 512 and not c.weight_lds
+            assert rows >= 1024 and hidden // v <= 64
+        elif c.weight_lds:  # gamma and beta (sized for both) in LDS, shared by the row slots
             assert c.path == mbr.PATH_VECTOR and (hidden // v) * 32 <= 60 * 1024
             assert c.rows_per_block >= 1 and lanes * c.rows_per_block <= 512
         else:
@@ -63,6 +69,17 @@ def test_stated_choices():
     assert (c.waves_per_row, c.items_per_lane, c.rows_per_block, c.weight_lds) == (1, 4, 1, 0)
     c = mbr.layernorm_select_config(64, 768, torch.float32, True)
     assert (c.path, c.waves_per_row, c.items_per_lane) == (mbr.PATH_VECTOR, 2, 2)  # few rows: spread
+    # narrow rows: lane groups of 8, 16 or 32 with at most two vectors per lane
+    for rows, hidden, dt, want in [(262144, 128, torch.bfloat16, (8, 2, 32, 0)),
+                                   (262144, 64, torch.bfloat16, (8, 1, 64, 1024)),
+                                   (131072, 256, torch.bfloat16, (16, 2, 16, 0)),
+                                   (65536, 512, torch.bfloat16, (32, 2, 8, 0)),
+                                   (131072, 128, torch.float32, (16, 2, 16, 0)),
+                                   (4096, 128, torch.bfloat16, (8, 2, 16, 0)), (1024, 128, torch.bfloat16, (8, 2, 8, 0))]:
+        c = mbr.layernorm_select_config(rows, hidden, dt, True)
+        assert (c.path, c.waves_per_row, c.weight_lds) == (mbr.PATH_VECTOR, 1, 0), (rows, hidden)
+        assert (c.lanes_per_row, c.items_per_lane, c.rows_per_block, c.max_blocks) == want, (rows, hidden)
+    assert mbr.layernorm_select_config(1023, 128, torch.bfloat16, True).lanes_per_row == 0
 
 
 @fake_only
@@ -84,6 +101,13 @@ def test_pointer_validation_and_forced_configs():
                 mbr.Config(mbr.PATH_TWO_PASS, 16, 0, 1, 0, 0, 1)]:
         import ctypes
         assert L.layernorm_fwd_ex(X, G, B, O, 4, 4096, 1e-5, 1, ctypes.byref(cfg), None) == INV, cfg
+    # rows narrower than a wave (hidden 128 bf16: 16 vectors)
+    for cfg in [mbr.Config(mbr.PATH_VECTOR, 2, 1, 8, 0, 16), mbr.Config(mbr.PATH_VECTOR, 1, 3, 4, 0, 16),
+                mbr.Config(mbr.PATH_VECTOR, 1, 1, 2, 0, 16), mbr.Config(mbr.PATH_VECTOR, 1, 1, 64, 0, 16),
+                mbr.Config(mbr.PATH_VECTOR, 1, 1, 8, 0, 12), mbr.Config(mbr.PATH_ELEMENT, 1, 1, 4, 0, 16),
+                mbr.Config(mbr.PATH_VECTOR, 1, 1, 8, 0, 8), mbr.Config(mbr.PATH_VECTOR, 1, 1, 4, 0, 16, 1),
+                mbr.Config(mbr.PATH_TWO_PASS, 1, 0, 1, 0, 32)]:
+        assert L.layernorm_fwd_ex(X, G, B, O, 4, 128, 1e-5, 1, ctypes.byref(cfg), None) == INV, cfg.as_dict()
     # gamma and beta in LDS: 2 * 4096 vectors * 16 bytes, over the 60 KiB bound
     cfg = mbr.Config(mbr.PATH_VECTOR, 16, 4, 1, 0, 0, 1)
     assert L.layernorm_fwd_ex(X, G, B, O, 4, 32768, 1e-5, 1, ctypes.byref(cfg), None) == INV

@@ -124,6 +124,43 @@ def test_ln_gamma_beta_in_lds(dtype):
     assert n > 60
 
 
+NARROW = [(1024, 8), (1027, 64), (4096, 128), (3001, 256), (2050, 384), (1500, 512), (20000, 128), (9000, 24)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,hidden", NARROW)
+def test_ln_narrow_rows_automatic(rows, hidden, dtype):
+    """Per-head widths from 1024 rows take several rows per wave when they
+    are whole vectors; checked through the automatic choice."""
+    w = inputs.custom(rows, hidden, dtype, layernorm=True)
+    cfg = mbr.layernorm_select_config(rows, hidden, tdt(dtype), True)
+    say("ln narrow", rows, hidden, dtype, cfg.as_dict())
+    if hidden % (8 if dtype == "bf16" else 4) == 0 and hidden // (8 if dtype == "bf16" else 4) <= 64:
+        assert cfg.lanes_per_row in (8, 16, 32)
+    check(w, inputs.make(w, seed=rows + 5 * hidden), bias=rows % 2 == 0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ln_subwave_configs(dtype):
+    """Rows narrower than a wave (8, 16 or 32 lanes per row): one, two and
+    eight waves per workgroup, full and masked rows, rows that leave part of
+    a wave or of the last group idle, capped grids; without beta every third
+    case."""
+    vecw = 8 if dtype == "bf16" else 4
+    n = 0
+    for lpr in (8, 16, 32):
+        for vpl in (1, 2):
+            for rpb in (64 // lpr, 128 // lpr, 512 // lpr):
+                for nvec in sorted({lpr * vpl, max(1, lpr * (vpl - 1) + 3)}):
+                    for mb, rows in ((0, rpb + 1), (3, 7 * rpb + 5), (0, 3), (0, 1)):
+                        cfg = mbr.Config(mbr.PATH_VECTOR, 1, vpl, rpb, mb, lpr)
+                        w = inputs.custom(rows, nvec * vecw, dtype, layernorm=True)
+                        say("ln sub-wave", dtype, cfg.as_dict(), "hidden", nvec * vecw, "rows", rows)
+                        check(w, inputs.make(w, seed=3000 + n), cfg, bias=(n % 3 != 2))
+                        n += 1
+    assert n > 100
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_ln_every_element_and_multipass_config(dtype):
     n = 0
