@@ -208,15 +208,33 @@ rmsnorm_config_t choose(int64_t rows, int64_t hidden, int dtype, bool aligned, b
             c.weight_lds = 1;
         }
     }
-    if (vec && units <= mbr::kLprList[mbr::kNumLpr - 1]) {
-        // a row narrower than half a wave: the smallest lane group that holds
-        // it with one vector per lane, one wave per workgroup
+    if (vec && !fused && !qt && units <= mbr::kLprList[mbr::kNumLpr - 1]) {
+        // a plain row narrower than half a wave: the smallest lane group that
+        // holds it with one vector per lane, one wave per workgroup
         const int lpr = round_up_in(mbr::kLprList, mbr::kNumLpr, units);
         const int64_t per_wave = 64 / lpr;  // rows sharing one wave
         c.lanes_per_row = lpr;
         c.items_per_lane = 1;
         c.rows_per_block = static_cast<int32_t>(
             std::min<int64_t>(kSubwaveThreads / lpr, std::max<int64_t>(per_wave, ceil_div(rows, per_wave) * per_wave)));
+    } else if (vec && units <= 2 * mbr::kLprList[mbr::kNumLpr - 1] && (fused || qt || units % 64 != 0)) {
+        // Fused and quantised rows of at most 64 vectors, and plain ones of
+        // 33..63 (a whole wave would leave lanes idle): the smallest lane group
+        // that holds the row with at most two vectors per lane, two waves per
+        // workgroup (one while there would be under 256 workgroups).  HIP-graph
+        // sweeps on MI355X, against one wave per row or one vector per lane:
+        // int8 [262144, 128] 19.6-20.3 us against 25.6, int8 [65536, 512] 20.0-20.3
+        // against 26.8, fused [262144, 128] 44.9 against 46.9, plain
+        // [65536, 384] 18.9 against 22.1.
+        int lpr = 0;
+        for (int i = 0; i < mbr::kNumLpr && !lpr; ++i)
+            if (ceil_div(units, int64_t(mbr::kLprList[i])) <= 2) lpr = mbr::kLprList[i];
+        int rpb = 128 / lpr;
+        if (rows < int64_t(rpb) * 256) rpb = 64 / lpr;
+        c.waves_per_row = 1;
+        c.items_per_lane = static_cast<int>(ceil_div(units, int64_t(lpr)));
+        c.rows_per_block = rpb;
+        c.lanes_per_row = lpr;
     }
     return c;
 }

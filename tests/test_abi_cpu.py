@@ -211,12 +211,14 @@ def test_selection_is_always_a_built_covering_config(hidden, rows, dtype, aligne
     assert cfg.waves_per_row in (1, 2, 4, 8, 16) and cfg.rows_per_block >= 1
     if cfg.lanes_per_row:  # several rows per wave
         lpr = cfg.lanes_per_row
-        assert cfg.path == mbr.PATH_VECTOR and aligned and hidden % vec == 0 and hidden // vec <= 32
+        assert cfg.path == mbr.PATH_VECTOR and aligned and hidden % vec == 0 and hidden // vec <= 64
         assert lpr in (8, 16, 32) and cfg.waves_per_row == 1 and cfg.items_per_lane in (1, 2)
-        assert lpr * cfg.items_per_lane >= hidden // vec
-        assert (lpr * cfg.rows_per_block) % 64 == 0 and lpr * cfg.rows_per_block <= 512
+        assert lpr * cfg.items_per_lane >= hidden // vec > lpr * (cfg.items_per_lane - 1)
+        assert (lpr * cfg.rows_per_block) % 64 == 0 and lpr * cfg.rows_per_block <= 128
         per_wave = 64 // lpr
-        assert cfg.rows_per_block <= max(-(-rows // per_wave) * per_wave, per_wave)
+        assert cfg.rows_per_block == per_wave or rows >= 256 * cfg.rows_per_block
+        if not fused:  # plain rows of 64 vectors fill a whole wave exactly
+            assert hidden // vec != 64
         return
     if cfg.path == mbr.PATH_VECTOR:
         assert aligned and hidden % vec == 0
@@ -235,6 +237,29 @@ def test_selection_is_always_a_built_covering_config(hidden, rows, dtype, aligne
     if cfg.weight_lds:
         assert cfg.weight_lds == 1 and cfg.path == mbr.PATH_VECTOR and not fused and not cfg.lanes_per_row
         assert (hidden // vec) * 16 <= 60 * 1024
+
+
+def test_narrow_row_choices():
+    """Rows narrower than a wave: plain rows of up to 32 vectors take one
+    vector per lane in the smallest lane group that holds them; fused and
+    quantised rows of up to 64 vectors, and plain ones of 33..63, take at
+    most two vectors per lane in the smallest lane group, two waves per
+    workgroup from 256 workgroups on."""
+    B = torch.bfloat16
+    for rows, hidden, fused, want in [(262144, 128, False, (16, 1, 4)), (262144, 64, False, (8, 1, 8)),
+                                      (131072, 256, False, (32, 1, 2)), (65536, 384, False, (32, 2, 4)),
+                                      (262144, 128, True, (8, 2, 16)), (65536, 512, True, (32, 2, 4)),
+                                      (65536, 256, True, (16, 2, 8)), (100, 128, True, (8, 2, 8))]:
+        c = mbr.rmsnorm_select_config(rows, hidden, B, True, fused)
+        assert (c.path, c.waves_per_row) == (mbr.PATH_VECTOR, 1)
+        assert (c.lanes_per_row, c.items_per_lane, c.rows_per_block) == want, (rows, hidden, fused, c.as_dict())
+    c = mbr.rmsnorm_select_config(65536, 512, B, True, False)
+    assert (c.lanes_per_row, c.waves_per_row, c.items_per_lane) == (0, 1, 1)  # 64 vectors: a whole wave
+    for fused in (False, True):  # the quantised forms (int8 and fp8 share the choice)
+        c = mbr.rmsnorm_select_quant_config(262144, 128, B, True, fused)
+        assert (c.lanes_per_row, c.items_per_lane, c.rows_per_block) == (8, 2, 16)
+        c = mbr.rmsnorm_select_quant_config(65536, 512, B, True, fused)
+        assert (c.lanes_per_row, c.items_per_lane, c.rows_per_block) == (32, 2, 4)
 
 
 def test_hbm_copy_rejects_bad_arguments():

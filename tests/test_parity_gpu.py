@@ -494,11 +494,12 @@ def test_every_subwave_config(dtype, fused):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("hidden", [8, 16, 64, 96, 128, 200, 256])
-def test_narrow_rows_automatic(dtype, hidden):
+@pytest.mark.parametrize("hidden", [8, 16, 64, 96, 128, 200, 256, 384, 512])
+@pytest.mark.parametrize("fused", [False, True])
+def test_narrow_rows_automatic(dtype, hidden, fused):
     """Narrow rows (per-head norms) at many rows take the sub-wave path."""
     rows = 20001
-    cfg = mbr.rmsnorm_select_config(rows, hidden, BF16 if dtype == "bf16" else F32, True, False)
-    say("narrow", dtype, hidden, cfg)
-    w = inputs.custom(rows, hidden, dtype, False)
+    cfg = mbr.rmsnorm_select_config(rows, hidden, BF16 if dtype == "bf16" else F32, True, fused)
+    say("narrow", dtype, hidden, fused, cfg)
+    w = inputs.custom(rows, hidden, dtype, fused)
     check_workload(w, inputs.make(w, seed=hidden))

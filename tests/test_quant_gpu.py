@@ -212,6 +212,24 @@ def test_quant_rejects_overlaps_on_device_buffers():
 
 @pytest.mark.parametrize("q", ["int8", "fp8"])
 @pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("dtype,hidden", [("bf16", 64), ("bf16", 128), ("bf16", 200), ("bf16", 384), ("bf16", 512),
+                                          ("f32", 96), ("f32", 256)])
+def test_narrow_rows_automatic_quant(dtype, hidden, fused, q):
+    """Per-head widths through the automatic choice: lane groups with up to
+    two vectors per lane wherever the row is whole vectors."""
+    rows = 20001
+    cfg = mbr.rmsnorm_select_quant_config(rows, hidden, torch.bfloat16 if dtype == "bf16" else torch.float32,
+                                          True, fused)
+    vecw = 8 if dtype == "bf16" else 4
+    if hidden % vecw == 0:
+        assert cfg.lanes_per_row in (8, 16, 32) and cfg.items_per_lane in (1, 2)
+    say("quant narrow", q, dtype, hidden, fused, cfg.as_dict())
+    w = inputs.custom(rows, hidden, dtype, fused)
+    check(w, inputs.make(w, seed=hidden + 7), QT[q])
+
+
+@pytest.mark.parametrize("q", ["int8", "fp8"])
+@pytest.mark.parametrize("fused", [False, True])
 def test_every_subwave_quant_config(fused, q):
     """Quantised output with several rows per wave (lanes_per_row 8, 16, 32)."""
     n = 0
