@@ -390,6 +390,30 @@ RMSNORM_API rmsnorm_status_t kv_rmsnorm_rope_cache(const void* kv, const void* g
                                                    int64_t rope_dim, int64_t max_pos, int64_t num_slots, float eps,
                                                    int32_t rope_style, rmsnorm_dtype_t dtype, void* stream);
 
+/* kv_rmsnorm_rope_cache with a launch configuration (NULL or path AUTO =
+ * automatic).  path VECTOR (16-byte aligned buffers and a vector shape as
+ * above): lanes_per_row 0 (a whole wave per row) with items_per_lane 1, 2, 4
+ * or 8 norm vectors per lane, or lanes_per_row 16 or 32 (several rows per
+ * wave) with items_per_lane 1 or 2; the rotated part must fit the row's
+ * lanes.  path ELEMENT: the element kernel (lanes_per_row 0).  waves_per_row
+ * and rows_per_block must be 1, max_blocks and weight_lds 0.  INVALID_ARG
+ * otherwise; the results do not depend on the configuration beyond the
+ * rounding of the row sum. */
+RMSNORM_API rmsnorm_status_t kv_rmsnorm_rope_cache_ex(const void* kv, const void* gamma, const float* cos_table,
+                                                      const float* sin_table, const int32_t* positions,
+                                                      const int64_t* slots, void* norm_cache, void* rope_cache,
+                                                      int64_t tokens, int64_t heads, int64_t norm_dim,
+                                                      int64_t rope_dim, int64_t max_pos, int64_t num_slots,
+                                                      float eps, int32_t rope_style, rmsnorm_dtype_t dtype,
+                                                      const rmsnorm_config_t* cfg, void* stream);
+
+/* The configuration kv_rmsnorm_rope_cache would use for this shape
+ * (vector_aligned != 0: every buffer will be 16-byte aligned).  INVALID_ARG
+ * for cfg == NULL or bad sizes; no HIP call. */
+RMSNORM_API rmsnorm_status_t kv_select_config(int64_t tokens, int64_t heads, int64_t norm_dim, int64_t rope_dim,
+                                              int32_t rope_style, rmsnorm_dtype_t dtype, int32_t vector_aligned,
+                                              rmsnorm_config_t* cfg);
+
 #ifdef __cplusplus
 }
 #endif

@@ -113,13 +113,16 @@ def lib() -> ctypes.CDLL:
         L.layernorm_select_config.argtypes = [i64, i64, i32, i32, cfgp]
         L.kv_rmsnorm_rope_cache.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32,
                                             i32, vp]
+        L.kv_rmsnorm_rope_cache_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32,
+                                               i32, i32, cfgp, vp]
+        L.kv_select_config.argtypes = [i64, i64, i64, i64, i32, i32, i32, cfgp]
         L.rmsnorm_status_string.argtypes = [i32]
         L.rmsnorm_status_string.restype = ctypes.c_char_p
         for fn in (L.rmsnorm_fwd, L.rmsnorm_residual_fwd, L.rmsnorm_fwd_ex, L.rmsnorm_residual_fwd_ex,
                    L.rmsnorm_select_config, L.rmsnorm_select_quant_config, L.rmsnorm_dynamic_quant_fwd,
                    L.rmsnorm_dynamic_quant_fwd_ex, L.rmsnorm_bwd, L.rmsnorm_bwd_ex, L.rmsnorm_bwd_workspace_size,
                    L.rmsnorm_select_bwd_config, L.layernorm_fwd, L.layernorm_fwd_ex, L.layernorm_select_config,
-                   L.kv_rmsnorm_rope_cache):
+                   L.kv_rmsnorm_rope_cache, L.kv_rmsnorm_rope_cache_ex, L.kv_select_config):
             fn.restype = i32
         _lib = L
     return _lib
@@ -381,6 +384,24 @@ def kv_rmsnorm_rope_cache(kv, gamma, cos_table, sin_table, positions, slots, nor
     kv[..., norm_dim:] into rope_cache[slot] (C: kv_rmsnorm_rope_cache).
     kv [tokens, heads, norm_dim + rope_dim]; caches [num_slots, heads, dim];
     tables float32 [max_pos, rope_dim / 2]; positions int32, slots int64."""
+    return kv_rmsnorm_rope_cache_ex(kv, gamma, cos_table, sin_table, positions, slots, norm_cache, rope_cache,
+                                    eps, rope_style, None, stream)
+
+
+def kv_select_config(tokens: int, heads: int, norm_dim: int, rope_dim: int, rope_style: int, dtype,
+                     vector_aligned: bool = True) -> Config:
+    """The configuration kv_rmsnorm_rope_cache uses for this shape."""
+    code = dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype)
+    cfg = Config()
+    _check(lib().kv_select_config(int(tokens), int(heads), int(norm_dim), int(rope_dim), int(rope_style), code,
+                                  int(bool(vector_aligned)), ctypes.byref(cfg)), "kv_select_config")
+    return cfg
+
+
+def kv_rmsnorm_rope_cache_ex(kv, gamma, cos_table, sin_table, positions, slots, norm_cache, rope_cache,
+                             eps: float = 1e-6, rope_style: int = ROPE_PAIRS, config: Optional[Config] = None,
+                             stream=None):
+    """kv_rmsnorm_rope_cache with a forced configuration (None: automatic)."""
     for t, n in ((kv, "kv"), (gamma, "gamma"), (positions, "positions"), (slots, "slots"),
                  (norm_cache, "norm_cache"), (rope_cache, "rope_cache"), (cos_table, "cos_table"),
                  (sin_table, "sin_table")):
@@ -403,11 +424,13 @@ def kv_rmsnorm_rope_cache(kv, gamma, cos_table, sin_table, positions, slots, nor
     if positions.dtype != torch.int32 or slots.dtype != torch.int64 or positions.numel() != tokens or \
             slots.numel() != tokens:
         raise ValueError("positions (int32) and slots (int64) need one entry per token")
-    st = lib().kv_rmsnorm_rope_cache(kv.data_ptr(), gamma.data_ptr(), cos_table.data_ptr(), sin_table.data_ptr(),
-                                     positions.data_ptr(), slots.data_ptr(), norm_cache.data_ptr(),
-                                     rope_cache.data_ptr(), tokens, heads, norm_dim, rope_dim, cos_table.shape[0],
-                                     norm_cache.shape[0], float(eps), int(rope_style), dtype_code(kv.dtype),
-                                     _stream(stream, kv.device))
+    st = lib().kv_rmsnorm_rope_cache_ex(kv.data_ptr(), gamma.data_ptr(), cos_table.data_ptr(),
+                                        sin_table.data_ptr(), positions.data_ptr(), slots.data_ptr(),
+                                        norm_cache.data_ptr(), rope_cache.data_ptr(), tokens, heads, norm_dim,
+                                        rope_dim, cos_table.shape[0], norm_cache.shape[0], float(eps),
+                                        int(rope_style), dtype_code(kv.dtype),
+                                        ctypes.byref(config) if config is not None else None,
+                                        _stream(stream, kv.device))
     _check(st, "kv_rmsnorm_rope_cache")
     return norm_cache, rope_cache
 

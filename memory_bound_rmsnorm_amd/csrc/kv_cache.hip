@@ -22,7 +22,33 @@ const void* kv_vec_for(int vi, bool masked) {
     }
 }
 
+template <class E, int STYLE, int LPR>
+const void* kv_sub_for(int vi, bool masked) {
+    switch (vi) {
+        case 0: return masked ? reinterpret_cast<const void*>(&kv_vec_kernel<E, 1, true, STYLE, LPR>)
+                              : reinterpret_cast<const void*>(&kv_vec_kernel<E, 1, false, STYLE, LPR>);
+        case 1: return masked ? reinterpret_cast<const void*>(&kv_vec_kernel<E, 2, true, STYLE, LPR>)
+                              : reinterpret_cast<const void*>(&kv_vec_kernel<E, 2, false, STYLE, LPR>);
+        default: return nullptr;
+    }
+}
+
+template <class E, int STYLE>
+const void* kv_sub_lpr(int li, int vi, bool masked) {
+    switch (li) {
+        case 0: return kv_sub_for<E, STYLE, 8>(vi, masked);
+        case 1: return kv_sub_for<E, STYLE, 16>(vi, masked);
+        case 2: return kv_sub_for<E, STYLE, 32>(vi, masked);
+        default: return nullptr;
+    }
+}
+
 }  // namespace
+
+const void* kv_subwave_kernel_ptr(int dtype, int style, bool masked, int li, int vi) {
+    if (dtype == 1) return style ? kv_sub_lpr<Bf16, 1>(li, vi, masked) : kv_sub_lpr<Bf16, 0>(li, vi, masked);
+    return style ? kv_sub_lpr<F32, 1>(li, vi, masked) : kv_sub_lpr<F32, 0>(li, vi, masked);
+}
 
 const void* kv_vec_kernel_ptr(int dtype, int style, bool masked, int vi) {
     if (dtype == 1) return style ? kv_vec_for<Bf16, 1>(vi, masked) : kv_vec_for<Bf16, 0>(vi, masked);

@@ -71,11 +71,19 @@ __device__ __forceinline__ void load_table(const float* row, int j0, float (&out
 // they are issued before the token's slot and position are read; the
 // range check on those (wave-uniform) then guards every table read and every
 // cache store, and a skipped token's loaded values are simply dropped.
-template <class E, int NVPL, bool MASKED, int STYLE>
+//
+// LPR < 64: 64 / LPR rows share a wave, each owning an aligned group of LPR
+// lanes (8, 16 or 32; the rotated part must fit them).  A group past the last
+// row loads the last row again; the range check is then per group, taken
+// after the group sum (which every lane of the wave joins) and before the
+// stores, and a skipped group reads no table.
+template <class E, int NVPL, bool MASKED, int STYLE, int LPR = 64>
 __global__ void __launch_bounds__(256) kv_vec_kernel(const KvArgs a) {
     constexpr int V = E::kVec;
     constexpr int NT = STYLE == 1 ? V / 2 : V;  // table entries per rope lane
-    const int lane = static_cast<int>(threadIdx.x) & 63;
+    constexpr int G = 64 / LPR;                 // rows per wave
+    const int lane = static_cast<int>(threadIdx.x) & (LPR - 1);
+    const int grp = G > 1 ? (static_cast<int>(threadIdx.x) & 63) / LPR : 0;
     const int nv = a.norm_dim / V;               // norm vectors per row
     const int rv = a.rope_dim / V;               // rope vectors per row
     const int d_vec = nv + rv;                   // vectors per kv row
@@ -84,17 +92,20 @@ __global__ void __launch_bounds__(256) kv_vec_kernel(const KvArgs a) {
     const bool rope_lane = lane < rlanes;
     const int64_t waves = static_cast<int64_t>(gridDim.x) * (blockDim.x >> 6);
     auto vidx = [&](int k) {
-        const int v = k * 64 + lane;
+        const int v = k * LPR + lane;
         return MASKED ? (v < nv ? v : nv - 1) : v;
     };
-    auto in_row = [&](int k) { return !MASKED || k * 64 + lane < nv; };
+    auto in_row = [&](int k) { return !MASKED || k * LPR + lane < nv; };
 
     u32x4 gv[NVPL];
 #pragma unroll
     for (int k = 0; k < NVPL; ++k) gv[k] = load_keep(static_cast<const u32x4*>(a.gamma) + vidx(k));
 
-    for (int64_t row = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + wave_id(); row < a.rows;
-         row += waves) {
+    for (int64_t base = (static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + wave_id()) * G; base < a.rows;
+         base += waves * G) {
+        const int64_t row0 = base + grp;
+        const bool in_rows = G == 1 || row0 < a.rows;
+        const int64_t row = in_rows ? row0 : a.rows - 1;
         const u32x4* xr = static_cast<const u32x4*>(a.kv) + row * d_vec;
         u32x4 xv[NVPL], ra, rb;
 #pragma unroll
@@ -107,9 +118,12 @@ __global__ void __launch_bounds__(256) kv_vec_kernel(const KvArgs a) {
         const int64_t h = row - t * a.heads;
         const int64_t slot = a.slots[t];
         const int64_t p = a.pos[t];
-        if (slot < 0 || slot >= a.num_slots || p < 0 || p >= a.max_pos) continue;  // wave-uniform
+        const bool ok = in_rows && slot >= 0 && slot < a.num_slots && p >= 0 && p < a.max_pos;
+        if constexpr (G == 1) {
+            if (!ok) continue;  // wave-uniform
+        }
         float ct[NT], st[NT];
-        if (rope_lane) {
+        if (rope_lane && (G == 1 || ok)) {
             load_table(a.cos_t + p * half, lane * NT, ct);
             load_table(a.sin_t + p * half, lane * NT, st);
         }
@@ -123,7 +137,10 @@ __global__ void __launch_bounds__(256) kv_vec_kernel(const KvArgs a) {
             for (int i = 0; i < V; ++i) s += f[i] * f[i];
             ss += in_row(k) ? s : 0.f;
         }
-        const float r = rsqrtf(wave_sum(ss) / a.norm_dim_f + a.eps);
+        const float r = rsqrtf(group_sum<LPR>(ss) / a.norm_dim_f + a.eps);
+        if constexpr (G > 1) {
+            if (!ok) continue;  // per lane group, after the group sum
+        }
         u32x4* ncr = static_cast<u32x4*>(a.nc) + (slot * a.heads + h) * nv;
 #pragma unroll
         for (int k = 0; k < NVPL; ++k) {
@@ -133,7 +150,7 @@ __global__ void __launch_bounds__(256) kv_vec_kernel(const KvArgs a) {
             widen(gv[k], fw, E{});
 #pragma unroll
             for (int i = 0; i < V; ++i) f[i] = f[i] * r * fw[i];
-            store_stream(ncr + k * 64 + lane, narrow(f, E{}));
+            store_stream(ncr + k * LPR + lane, narrow(f, E{}));
         }
         if (rope_lane) {
             u32x4* rcr = static_cast<u32x4*>(a.rc) + (slot * a.heads + h) * rv;

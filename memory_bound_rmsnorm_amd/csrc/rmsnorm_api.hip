@@ -881,35 +881,69 @@ rmsnorm_status_t validate_kv_pointers(const KvProblem& p) {
     return RMSNORM_OK;
 }
 
-// The vector kernel needs 16-byte vectors that never straddle the split or a
-// rope pair group, table rows whose per-lane entries are 16-byte (8-byte for
-// fp32 adjacent pairs) aligned, a rotated part no wider than 64 lane slots and
-// a norm part of at most 8 vectors per lane.  Returns the NVPL index or -1.
-int kv_vec_choice(const KvProblem& p, bool* masked) {
-    const int v = vec_elems(p.dtype);
-    const int64_t unit = p.style == 1 ? v : 2 * v;
-    if (p.dn % v != 0 || p.dr % unit != 0) return -1;
+bool kv_aligned(const KvProblem& p) {
     const void* ptrs[] = {p.kv, p.gamma, p.nc, p.rc, p.cos_t, p.sin_t};
     for (const void* q : ptrs)
-        if (q && reinterpret_cast<uintptr_t>(q) % kVectorBytes != 0) return -1;
-    const int64_t rope_lanes = p.style == 1 ? p.dr / v : p.dr / (2 * v);
-    if (rope_lanes > 64) return -1;
-    const int64_t nv = p.dn / v;
-    for (int i = 0; i < mbr::kNumKvVpl; ++i) {
-        if (int64_t(64) * mbr::kKvVplList[i] >= nv) {
-            *masked = int64_t(64) * mbr::kKvVplList[i] != nv;
-            return i;
-        }
-    }
-    return -1;
+        if (q && reinterpret_cast<uintptr_t>(q) % kVectorBytes != 0) return false;
+    return true;
 }
 
-rmsnorm_status_t run_kv(const KvProblem& p, void* stream) {
+// Lanes with rotary work per row, or -1 when the shape cannot take 16-byte
+// vectors: these must never straddle the split or a rope pair group, and
+// table rows need 16-byte (8-byte for fp32 adjacent pairs) aligned per-lane
+// entries.
+int64_t kv_rope_lanes(int64_t dn, int64_t dr, int style, int dtype) {
+    const int v = vec_elems(dtype);
+    const int64_t unit = style == 1 ? v : 2 * v;
+    if (dn % v != 0 || dr % unit != 0) return -1;
+    return style == 1 ? dr / v : dr / (2 * v);
+}
+
+// Automatic KV launch configuration.  Path VECTOR: the smallest lane group
+// of 8, 16 or 32 that holds the norm part with at most two vectors per lane
+// and the rotated part, several rows per wave; else a whole wave per row
+// with up to 8 norm vectors per lane and the rotated part in at most 64
+// lanes.  Otherwise ELEMENT.  HIP-graph sweeps on MI355X: the bf16 prefill
+// (16384 rows of 512 + 64) 9.2 us as 32 lanes x 2 against 11.0 with a wave
+// per row; 16384 tokens x 8 heads of 128 + 64, 19.5 us as 8 lanes x 2
+// against 21.1 as 16 x 1 and 53.9 with a wave per row.
+rmsnorm_config_t choose_kv(int64_t dn, int64_t dr, int style, int dtype, bool aligned) {
+    rmsnorm_config_t c = {RMSNORM_PATH_ELEMENT, 1, 0, 1, 0, 0, 0};
+    const int64_t rope_lanes = kv_rope_lanes(dn, dr, style, dtype);
+    if (!aligned || rope_lanes < 0 || rope_lanes > 64) return c;
+    const int64_t nv = dn / vec_elems(dtype);
+    for (int i = 0; i < mbr::kNumKvLpr; ++i) {
+        const int lpr = mbr::kKvLprList[i];
+        if (ceil_div(nv, int64_t(lpr)) <= 2 && rope_lanes <= lpr) {
+            c.path = RMSNORM_PATH_VECTOR;
+            c.items_per_lane = static_cast<int32_t>(ceil_div(nv, int64_t(lpr)));
+            c.lanes_per_row = lpr;
+            return c;
+        }
+    }
+    for (int i = 0; i < mbr::kNumKvVpl; ++i) {
+        if (int64_t(64) * mbr::kKvVplList[i] >= nv) {
+            c.path = RMSNORM_PATH_VECTOR;
+            c.items_per_lane = mbr::kKvVplList[i];
+            return c;
+        }
+    }
+    return c;
+}
+
+rmsnorm_status_t run_kv(const KvProblem& p, const rmsnorm_config_t* user, void* stream) {
     rmsnorm_status_t s = validate_kv(p);
     if (s != RMSNORM_OK) return s;
     if (p.tokens == 0) return RMSNORM_OK;
     s = validate_kv_pointers(p);
     if (s != RMSNORM_OK) return s;
+    const bool aligned = kv_aligned(p);
+    const rmsnorm_config_t c = (user && user->path != RMSNORM_PATH_AUTO)
+                                   ? *user
+                                   : choose_kv(p.dn, p.dr, p.style, p.dtype, aligned);
+    if (c.waves_per_row != 1 || c.rows_per_block != 1 || c.max_blocks != 0 || c.weight_lds != 0)
+        return RMSNORM_ERR_INVALID_ARG;
+    const bool whole = c.lanes_per_row == 0 || c.lanes_per_row == 64;
     mbr::KvArgs a;
     a.kv = p.kv;
     a.gamma = p.gamma;
@@ -927,17 +961,38 @@ rmsnorm_status_t run_kv(const KvProblem& p, void* stream) {
     a.rope_dim = static_cast<int32_t>(p.dr);
     a.norm_dim_f = static_cast<float>(p.dn);
     a.eps = p.eps;
-    bool masked = false;
-    const int vi = kv_vec_choice(p, &masked);
-    const void* fn = vi >= 0 ? mbr::kv_vec_kernel_ptr(p.dtype, p.style, masked, vi)
-                             : mbr::kv_elem_kernel_ptr(p.dtype, p.style);
+    const void* fn = nullptr;
+    int64_t rows_per_wave = 1;
+    if (c.path == RMSNORM_PATH_VECTOR) {
+        const int64_t rope_lanes = kv_rope_lanes(p.dn, p.dr, p.style, p.dtype);
+        const int64_t lanes = whole ? 64 : c.lanes_per_row;
+        const int64_t nv = p.dn / vec_elems(p.dtype);
+        if (!aligned || rope_lanes < 0 || rope_lanes > lanes || lanes * c.items_per_lane < nv)
+            return RMSNORM_ERR_INVALID_ARG;
+        const bool masked = lanes * c.items_per_lane != nv;
+        if (whole) {
+            const int vi = index_of(mbr::kKvVplList, mbr::kNumKvVpl, c.items_per_lane);
+            if (vi < 0) return RMSNORM_ERR_INVALID_ARG;
+            fn = mbr::kv_vec_kernel_ptr(p.dtype, p.style, masked, vi);
+        } else {
+            const int li = index_of(mbr::kKvLprList, mbr::kNumKvLpr, c.lanes_per_row);
+            const int vi = index_of(mbr::kKvSwVplList, mbr::kNumKvSwVpl, c.items_per_lane);
+            if (li < 0 || vi < 0) return RMSNORM_ERR_INVALID_ARG;
+            fn = mbr::kv_subwave_kernel_ptr(p.dtype, p.style, masked, li, vi);
+            rows_per_wave = 64 / c.lanes_per_row;
+        }
+    } else if (c.path == RMSNORM_PATH_ELEMENT) {
+        if (!whole) return RMSNORM_ERR_INVALID_ARG;
+        fn = mbr::kv_elem_kernel_ptr(p.dtype, p.style);
+    }
     if (!fn) return RMSNORM_ERR_INVALID_ARG;
-    // One row per wave, four waves per workgroup.  Sweeps on MI355X (bf16
-    // prefill, 16384 rows of 512 + 64): two or eight waves per workgroup within
-    // noise; two or four rows per wave, all loaded before any is reduced,
-    // slower (13.4 us against 12.1), since fewer waves are in flight.
+    // Four waves per workgroup.  Sweeps on MI355X (bf16 prefill, 16384 rows
+    // of 512 + 64, one row per wave): two or eight waves per workgroup within
+    // noise; two or four rows per wave one after another, all loaded before
+    // any is reduced, slower (13.4 us against 12.1), since fewer waves are in
+    // flight.
     constexpr int64_t kWavesPerBlock = 4;
-    int64_t grid = ceil_div(a.rows, kWavesPerBlock);
+    int64_t grid = ceil_div(a.rows, kWavesPerBlock * rows_per_wave);
     if (grid > kMaxGrid) grid = kMaxGrid;
     return launch_checked(fn, grid, 64 * kWavesPerBlock, &a, static_cast<hipStream_t>(stream));
 }
@@ -1089,10 +1144,34 @@ RMSNORM_API rmsnorm_status_t kv_rmsnorm_rope_cache(const void* kv, const void* g
                                                    int64_t tokens, int64_t heads, int64_t norm_dim,
                                                    int64_t rope_dim, int64_t max_pos, int64_t num_slots, float eps,
                                                    int32_t rope_style, rmsnorm_dtype_t dtype, void* stream) {
+    return kv_rmsnorm_rope_cache_ex(kv, gamma, cos_table, sin_table, positions, slots, norm_cache, rope_cache, tokens,
+                                    heads, norm_dim, rope_dim, max_pos, num_slots, eps, rope_style, dtype, nullptr,
+                                    stream);
+}
+
+RMSNORM_API rmsnorm_status_t kv_rmsnorm_rope_cache_ex(const void* kv, const void* gamma, const float* cos_table,
+                                                      const float* sin_table, const int32_t* positions,
+                                                      const int64_t* slots, void* norm_cache, void* rope_cache,
+                                                      int64_t tokens, int64_t heads, int64_t norm_dim,
+                                                      int64_t rope_dim, int64_t max_pos, int64_t num_slots,
+                                                      float eps, int32_t rope_style, rmsnorm_dtype_t dtype,
+                                                      const rmsnorm_config_t* cfg, void* stream) {
     const KvProblem p = {kv,       gamma,     cos_table, sin_table, positions, slots,
                          norm_cache, rope_cache, tokens, heads,     norm_dim,  rope_dim,
                          max_pos,  num_slots, eps,       rope_style, static_cast<int>(dtype)};
-    return run_kv(p, stream);
+    return run_kv(p, cfg, stream);
+}
+
+RMSNORM_API rmsnorm_status_t kv_select_config(int64_t tokens, int64_t heads, int64_t norm_dim, int64_t rope_dim,
+                                              int32_t rope_style, rmsnorm_dtype_t dtype,
+                                              int32_t vector_aligned_flag, rmsnorm_config_t* cfg) {
+    if (!cfg) return RMSNORM_ERR_INVALID_ARG;
+    const KvProblem p = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, tokens, heads,
+                         norm_dim, rope_dim, 0, 0, 0.0f, rope_style, static_cast<int>(dtype)};
+    const rmsnorm_status_t s = validate_kv(p);
+    if (s != RMSNORM_OK) return s;
+    *cfg = choose_kv(norm_dim, rope_dim, rope_style, static_cast<int>(dtype), vector_aligned_flag != 0);
+    return RMSNORM_OK;
 }
 
 RMSNORM_API const char* rmsnorm_status_string(rmsnorm_status_t status) {

@@ -91,7 +91,13 @@ const void* ln_multipass_kernel_ptr(int dtype, bool vec);
 // 16-byte vectors per lane (index 0..3), rope style 0 (halves) or 1 (pairs).
 constexpr int kKvVplList[] = {1, 2, 4, 8};
 constexpr int kNumKvVpl = sizeof(kKvVplList) / sizeof(int);
+// Rows narrower than a wave: lanes per row, and norm vectors per lane.
+constexpr int kKvLprList[] = {8, 16, 32};
+constexpr int kNumKvLpr = sizeof(kKvLprList) / sizeof(int);
+constexpr int kKvSwVplList[] = {1, 2};
+constexpr int kNumKvSwVpl = sizeof(kKvSwVplList) / sizeof(int);
 const void* kv_vec_kernel_ptr(int dtype, int style, bool masked, int vpl_index);
+const void* kv_subwave_kernel_ptr(int dtype, int style, bool masked, int lpr_index, int vpl_index);
 const void* kv_elem_kernel_ptr(int dtype, int style);
 
 // Per-unit getters defined in the instantiation files.

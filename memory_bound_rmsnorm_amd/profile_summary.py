@@ -163,15 +163,16 @@ def pmc(args):
 
 def kv_launch(w):
     """The kernel kv_rmsnorm_rope_cache runs for workload w on 16-byte-aligned
-    buffers (its host-side choice, restated for reporting)."""
-    v = 4 if w.dtype == "f32" else 8
-    unit = v if w.rope_style == 1 else 2 * v
-    rope_lanes = w.rope_dim // unit if w.rope_style == 1 else w.rope_dim // (2 * v)
-    nv = w.norm_dim // v
-    per = next((k for k in (1, 2, 4, 8) if 64 * k >= nv), None)
-    vec = w.norm_dim % v == 0 and w.rope_dim % unit == 0 and rope_lanes <= 64 and per is not None
-    return {"path": "vector" if vec else "element", "norm_vectors_per_lane": per if vec else 0,
-            "rope_style": "pairs" if w.rope_style == 1 else "halves", "rows_per_workgroup": 4}
+    buffers (the library's own choice, kv_select_config)."""
+    import torch
+    import memory_bound_rmsnorm_amd as mbr
+    c = mbr.kv_select_config(w.tokens, w.heads, w.norm_dim, w.rope_dim, w.rope_style,
+                             torch.float32 if w.dtype == "f32" else torch.bfloat16, True)
+    vec = c.path == mbr.PATH_VECTOR
+    lanes = c.lanes_per_row or 64
+    return {"path": "vector" if vec else "element", "norm_vectors_per_lane": c.items_per_lane if vec else 0,
+            "lanes_per_row": lanes if vec else 64, "rope_style": "pairs" if w.rope_style == 1 else "halves",
+            "rows_per_workgroup": 4 * (64 // lanes) if vec else 4}
 
 
 def launch_config(w):
@@ -241,9 +242,9 @@ def resources(args):
         k = kv_launch(w)
         e = "F32" if w.dtype == "f32" else "Bf16"
         if k["path"] == "vector":
-            masked = 64 * k["norm_vectors_per_lane"] != w.norm_dim // (4 if w.dtype == "f32" else 8)
-            mangled = "kv_vec_kernelINS_%d%sELi%dELb%dELi%dEEEv" % (len(e), e, k["norm_vectors_per_lane"],
-                                                                   int(masked), w.rope_style)
+            masked = k["lanes_per_row"] * k["norm_vectors_per_lane"] != w.norm_dim // (4 if w.dtype == "f32" else 8)
+            mangled = "kv_vec_kernelINS_%d%sELi%dELb%dELi%dELi%dEEEv" % (len(e), e, k["norm_vectors_per_lane"],
+                                                                        int(masked), w.rope_style, k["lanes_per_row"])
         else:
             mangled = "kv_elem_kernelINS_%d%sELi%dEEEv" % (len(e), e, w.rope_style)
         hit = [l for l in lines if mangled in l]

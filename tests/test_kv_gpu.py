@@ -36,10 +36,10 @@ def bits(t):
     return inputs.bits(t.reshape(-1)).reshape(tuple(t.shape))
 
 
-def run_gpu(t, nc, rc, eps, style):
+def run_gpu(t, nc, rc, eps, style, cfg=None):
     d = {k: v.cuda() for k, v in t.items() if k in ("kv", "gamma", "cos", "sin", "positions", "slots")}
-    mbr.kv_rmsnorm_rope_cache(d["kv"], d["gamma"], d["cos"], d["sin"], d["positions"], d["slots"], nc, rc, eps,
-                              style)
+    mbr.kv_rmsnorm_rope_cache_ex(d["kv"], d["gamma"], d["cos"], d["sin"], d["positions"], d["slots"], nc, rc, eps,
+                                 style, cfg)
     torch.cuda.synchronize()
 
 
@@ -138,6 +138,39 @@ def test_kv_shapes(dn, dr, heads, style, dtype):
     say("kv shape", dtype, style, dn, dr, heads)
     run_gpu(t, nc, rc, 1e-5, style)
     check(t, 1e-5, style, dtype, nc0, rc0, nc, rc)
+
+
+KV_CONFIGS = [(0, 1), (0, 2), (0, 4), (0, 8), (8, 1), (8, 2), (16, 1), (16, 2), (32, 1),
+              (32, 2)]  # (lanes per row, vectors per lane)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("style", [mbr.ROPE_HALVES, mbr.ROPE_PAIRS])
+@pytest.mark.parametrize("lpr,nvpl", KV_CONFIGS)
+def test_kv_every_vector_config(lpr, nvpl, style, dtype):
+    """Every built vector configuration, forced: full and masked norm parts,
+    a rotated part filling the row's lanes or a few of them, none at all;
+    rows that leave part of the last wave idle, several heads, and padding,
+    out-of-range slots and positions among the tokens."""
+    v = 8 if dtype == "bf16" else 4
+    lanes = lpr or 64
+    unit = v if style == mbr.ROPE_PAIRS else 2 * v
+    n = 0
+    for nv in sorted({lanes * nvpl, max(1, lanes * (nvpl - 1) + 3)}):
+        for dr in sorted({0, unit, min(lanes, 16) * unit}):
+            for tokens, heads in ((1, 1), (37, 2), (9, 3)):
+                w, t, nc0, rc0 = _custom(dtype, tokens, heads, nv * v, dr, 101, 512, 100 * n + tokens, style)
+                if tokens > 4:
+                    t["slots"][1] = -1
+                    t["slots"][3] = 101
+                    t["positions"][2] = 512
+                cfg = mbr.Config(mbr.PATH_VECTOR, 1, nvpl, 1, 0, lpr)
+                nc, rc = nc0.clone(), rc0.clone()
+                say("kv config", dtype, style, cfg.as_dict(), "dn", nv * v, "dr", dr, "tokens", tokens, "heads", heads)
+                run_gpu(t, nc, rc, 1e-5, style, cfg)
+                check(t, 1e-5, style, dtype, nc0, rc0, nc, rc)
+                n += 1
+    assert n >= 9
 
 
 def test_kv_padding_and_out_of_range_tokens_write_nothing():
