@@ -46,6 +46,9 @@ int main(void) {
     expect("bwd_max_blocks", c.max_blocks, 512);
     expect("select_ln", layernorm_select_config(8192, 4096, RMSNORM_DTYPE_BF16, 1, &c), RMSNORM_OK);
     expect("ln_weight_lds", c.weight_lds, 1);
+    expect("select_kv", kv_select_config(16384, 1, 512, 64, 1, RMSNORM_DTYPE_BF16, 1, &c), RMSNORM_OK);
+    expect("kv_lanes_per_row", c.lanes_per_row, 32);
+    expect("kv_items_per_lane", c.items_per_lane, 2);
 
     /* workspace of the backward: min(ceil(rows / rows_per_block), partials) * round_up(hidden, 64) * 4 */
     size_t ws = 0;
@@ -81,6 +84,9 @@ int main(void) {
     expect("kv_odd_rope", kv_rmsnorm_rope_cache(NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 4, 1, 512, 63, 16,
                                                 16, 1e-6f, 1, RMSNORM_DTYPE_BF16, NULL),
            RMSNORM_ERR_INVALID_ARG);
+    expect("kv_ex_tokens0", kv_rmsnorm_rope_cache_ex(NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, 1, 512, 64,
+                                                     16, 16, 1e-6f, 1, RMSNORM_DTYPE_BF16, &c, NULL),
+           RMSNORM_OK);
     expect("copy_null", hbm_copy(NULL, NULL, 16, 0, NULL) != 0, 1);
     return failures;
 }
