@@ -97,6 +97,16 @@ __device__ __forceinline__ float across_groups_sum(float v) {
 // the reduction (12 VGPRs per bf16 vector instead of 24 widened fp32 ones).
 __device__ __forceinline__ void repack(u32x4& v) { asm volatile("" : "+v"(v)); }
 
+// Where the row kernel needs it: the widened values would otherwise spill
+// (8 vectors per lane, or 4 and more in a 1024-lane workgroup, 128 VGPRs).
+// Elsewhere holding them saves a third of the widening work (the 4 x 4 kernel:
+// 633 -> 569 VALU instructions per row, 156 VGPRs, still 3 waves per SIMD
+// against the 2 its 512-workgroup grid keeps resident): bf16 [4096, 2048]
+// 16.0 -> 15.7 us, fp32 [16384, 2048] 69.2 -> 67.7, [16384, 8192] 134.9 ->
+// 134.5.  With it the 1 x 8 kernel keeps [2048, 4096] at 18.6 us (22.2 spilling).
+template <int WPR, int VPL>
+constexpr bool kBwdRepack = VPL >= 8 || (WPR == 16 && VPL >= 4);
+
 // One partial row: V consecutive fp32 sums per 16-byte input vector.
 __device__ __forceinline__ void store_partial(float* p, const float* acc, Bf16) {
     f32x4 a = {acc[0], acc[1], acc[2], acc[3]}, b = {acc[4], acc[5], acc[6], acc[7]};
@@ -198,11 +208,13 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_bwd_vec_kernel(const B
             row_sums<WPR>(ss, cc, ps, pc, it, wave, slot);
         }
         if (!valid) continue;
+        if constexpr (kBwdRepack<WPR, VPL>) {
 #pragma unroll
-        for (int k = 0; k < VPL; ++k) {
-            repack(xv[k]);
-            repack(gv[k]);
-            repack(wv[k]);
+            for (int k = 0; k < VPL; ++k) {
+                repack(xv[k]);
+                repack(gv[k]);
+                repack(wv[k]);
+            }
         }
         const float r = rsqrtf(ss / a.hidden_f + a.eps);
         const float k2 = r * r * cc / a.hidden_f;
