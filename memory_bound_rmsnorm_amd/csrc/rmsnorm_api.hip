@@ -550,7 +550,7 @@ rmsnorm_status_t run_bwd(const BwdProblem& p, const rmsnorm_config_t* user, void
     a.rows_per_block = c.rows_per_block;
     a.n_groups = ceil_div(p.rows, int64_t(c.rows_per_block));
     a.ld = bwd_ld(p.hidden);
-    a.hidden_f = static_cast<float>(p.hidden);
+    a.inv_hidden = static_cast<float>(1.0 / static_cast<double>(p.hidden));
     a.eps = p.eps;
     const void* fn = nullptr;
     const int64_t threads = lanes * c.rows_per_block;

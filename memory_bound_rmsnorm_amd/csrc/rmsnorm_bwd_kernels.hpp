@@ -38,7 +38,8 @@ struct BwdArgs {
     int64_t ld;              // floats per partial row (a multiple of 64, >= hidden)
     int32_t units;           // per row: 16-byte vectors (vector path) or elements
     int32_t rows_per_block;  // vector path: rows a workgroup works on at once
-    float hidden_f;
+    float inv_hidden;        // 1 / hidden rounded once on the host (exact for powers of two):
+                             // the row sums multiply by it instead of dividing
     float eps;
 };
 
@@ -216,8 +217,8 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_bwd_vec_kernel(const B
                 repack(wv[k]);
             }
         }
-        const float r = rsqrtf(ss / a.hidden_f + a.eps);
-        const float k2 = r * r * cc / a.hidden_f;
+        const float r = rsqrtf(mul_rn(ss, a.inv_hidden) + a.eps);
+        const float k2 = mul_rn(r * r * cc, a.inv_hidden);
         char* dxr = static_cast<char*>(a.dx) + brow * row_bytes;
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
@@ -313,8 +314,8 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_bwd_elem_kernel(const 
             cc += in_row(k) ? (fg[k] * fw[k]) * fx[k] : 0.f;
         }
         row_sums<WPR>(ss, cc, ps, pc, it, wave);
-        const float r = rsqrtf(ss / a.hidden_f + a.eps);
-        const float k2 = r * r * cc / a.hidden_f;
+        const float r = rsqrtf(mul_rn(ss, a.inv_hidden) + a.eps);
+        const float k2 = mul_rn(r * r * cc, a.inv_hidden);
         S* dxr = static_cast<S*>(a.dx) + row * H;
 #pragma unroll
         for (int k = 0; k < EPL; ++k) {
@@ -383,8 +384,8 @@ __global__ void __launch_bounds__(1024) rms_bwd_twopass_kernel(const BwdArgs a) 
             ss += ps[it & 1][i];
             cc += pc[it & 1][i];
         }
-        const float r = rsqrtf(ss / a.hidden_f + a.eps);
-        const float k2 = r * r * cc / a.hidden_f;
+        const float r = rsqrtf(mul_rn(ss, a.inv_hidden) + a.eps);
+        const float k2 = mul_rn(r * r * cc, a.inv_hidden);
         for (int j = threadIdx.x; j < n; j += blockDim.x) {
             if constexpr (VEC) {
                 float fx[V], fg[V], fw[V], d[V];

@@ -116,6 +116,14 @@ __device__ __forceinline__ u32x4 load_stream(const u32x4* p) { return __builtin_
 __device__ __forceinline__ void store_stream(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 __device__ __forceinline__ u32x4 load_keep(const u32x4* p) { return *p; }
 
+// A product the compiler may not fuse into a following add (device code is
+// built with contraction on): where a kernel family must give the same bits
+// in every launch configuration, such a product is rounded on its own.
+__device__ __forceinline__ float mul_rn(float a, float b) {
+#pragma clang fp contract(off)
+    return a * b;
+}
+
 // ---------------------------------------------------------------- reduction
 
 template <int CTRL>
