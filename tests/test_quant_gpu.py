@@ -243,3 +243,20 @@ def test_every_subwave_quant_config(fused, q):
                     check(w, inputs.make(w, seed=n), QT[q], cfg)
                     n += 1
     assert n == 24
+
+
+@pytest.mark.parametrize("q", ["int8", "fp8"])
+def test_non_finite_rows_stay_in_their_row(q):
+    """A NaN or an infinity in one row leaves that row's scale non-finite and
+    every other row exactly as the oracle has it."""
+    w = inputs.custom(9, 512, "bf16", False)
+    t = inputs.make(w, seed=31)
+    t["x"][2, 5] = float("nan")
+    t["x"][6, 7] = float("inf")
+    _, q_g, s_g = run_quant(t, QT[q], w.eps, residual=False)
+    assert not np.isfinite(s_g[2]) and not np.isfinite(s_g[6])
+    keep = np.array([r for r in range(9) if r not in (2, 6)])
+    xb, wb = inputs.bits(t["x"])[keep], inputs.bits(t["weight"])
+    _, q_o, s_o = parity.oracle_quant(xb, wb, w.eps, QT[q])
+    q_gk = q_g[keep].view(np.int8) if QT[q] == 0 else q_g[keep]
+    say(parity.compare_quant(q_gk, q_o, s_g[keep], s_o, parity.quant_t(xb, wb, QT[q]), QT[q]))
