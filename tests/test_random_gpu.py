@@ -1,0 +1,53 @@
+"""Seeded random shapes through every entry point's automatic choice: rows,
+widths (whole 16-byte vectors or not), dtypes and forms drawn from one fixed
+generator, each compared with the oracle under the same bounds as the
+dedicated suites.  A wide net over the launch-configuration rules."""
+import numpy as np
+import pytest
+import torch
+
+import memory_bound_rmsnorm_amd as mbr
+from memory_bound_rmsnorm_amd import inputs
+from tests import parity
+from tests.test_bwd_gpu import check as check_bwd
+from tests.test_ln_gpu import check as check_ln
+from tests.test_parity_gpu import check_workload
+from tests.test_quant_gpu import QT, check as check_quant
+
+pytestmark = pytest.mark.gpu
+
+
+def _cases(n=240, seed=20261202):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dtype = "bf16" if rng.random() < 0.7 else "f32"
+        v = 8 if dtype == "bf16" else 4
+        r = rng.random()
+        if r < 0.35:
+            hidden = int(rng.integers(1, 65)) * v          # narrow, whole vectors
+        elif r < 0.75:
+            hidden = int(rng.integers(9, 1200)) * v        # wide, whole vectors
+        else:
+            hidden = int(rng.integers(1, 9000))            # any width
+        rows = int(rng.integers(1, max(2, min(6000, 2_000_000 // hidden))))
+        kind = ["fwd", "fused", "int8", "fp8", "bwd", "ln"][i % 6]
+        out.append((i, kind, dtype, rows, hidden))
+    return out
+
+
+@pytest.mark.parametrize("i,kind,dtype,rows,hidden", _cases())
+def test_random_shape(i, kind, dtype, rows, hidden):
+    print("random case", i, kind, dtype, rows, hidden, flush=True)
+    if kind in ("fwd", "fused"):
+        w = inputs.custom(rows, hidden, dtype, kind == "fused")
+        check_workload(w, inputs.make(w, seed=i))
+    elif kind in ("int8", "fp8"):
+        w = inputs.custom(rows, hidden, dtype, i % 4 == 0)
+        check_quant(w, inputs.make(w, seed=i), QT[kind])
+    elif kind == "bwd":
+        w = inputs.custom(rows, hidden, dtype, backward=True)
+        check_bwd(w, inputs.make(w, seed=i), want_dw=i % 5 != 0)
+    else:
+        w = inputs.custom(rows, hidden, dtype, layernorm=True)
+        check_ln(w, inputs.make(w, seed=i), bias=i % 3 != 0)
