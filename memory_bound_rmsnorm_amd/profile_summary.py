@@ -94,6 +94,25 @@ def stats(args):
             out.append("rmsnorm_kernel_avg_us: %.3f" % t)
         out.append("rmsnorm_gbps_from_avg: %.1f" % (w.algorithmic_bytes / t / 1e3))
         out.append("rmsnorm_frac_of_8TBps: %.4f" % (w.algorithmic_bytes / t / 1e3 / 8000.0))
+    # The average above covers every dispatch of the run: warm-up, the eager
+    # pass and the graph replays.  bench.py's timed steps are the last
+    # args.steps dispatches of each kernel (the timed graph replay); their
+    # average, from the per-dispatch trace next to the stats file, is the
+    # figure to set beside the bench line's own HIP-event reading.
+    trace = os.path.join(os.path.dirname(args.csv), os.path.basename(args.csv).replace("kernel_stats", "kernel_trace"))
+    if os.path.exists(trace) and trace != args.csv and len(step_avg) == len(preds):
+        with open(trace) as f:
+            disp = list(csv.DictReader(f))
+        timed = []
+        for pred in preds:
+            d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in disp if pred(r["Kernel_Name"])]
+            if len(d) >= args.steps:
+                timed.append(sum(d[-args.steps:]) / args.steps)
+        if len(timed) == len(preds):
+            t = sum(timed)
+            out.append("timed_steps: the last %d dispatches of each kernel (the timed graph replay)" % args.steps)
+            out.append("timed_steps_avg_us: %.3f" % t)
+            out.append("timed_steps_gbps: %.1f" % (w.algorithmic_bytes / t / 1e3))
     print("\n".join(out))
 
 
@@ -285,6 +304,7 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
+    s.add_argument("--steps", type=int, default=200, help="timed steps of the traced bench run")
     s.add_argument("--csv", required=True)
     s.add_argument("--workload", default=inputs.HEADLINE, choices=sorted(inputs.EVERY_WORKLOAD))
     s.add_argument("--command", required=True)
