@@ -124,7 +124,11 @@ typedef enum {
     RMSNORM_PATH_AUTO = 0,     /* let the library choose (the other fields are ignored) */
     RMSNORM_PATH_VECTOR = 1,   /* row in VGPRs, 16-byte loads/stores; needs 16-byte alignment */
     RMSNORM_PATH_ELEMENT = 2,  /* row in VGPRs, one element per access; any alignment */
-    RMSNORM_PATH_TWO_PASS = 3  /* row too large for registers: second read of x (and residual) */
+    RMSNORM_PATH_TWO_PASS = 3, /* row too large for registers: second read of x (and residual) */
+    RMSNORM_PATH_VECTOR_ANY = 4 /* rmsnorm_fwd_ex / rmsnorm_residual_fwd_ex only: any width of at
+                                   least one vector and any element alignment; the row's full
+                                   16-byte vectors at whatever alignment it has, then its last
+                                   hidden % (16 / size) elements one by one; rows_per_block 1 */
 } rmsnorm_path_t;
 
 typedef struct {

@@ -148,15 +148,20 @@ bool vector_aligned(const Problem& p) {
 rmsnorm_config_t choose(int64_t rows, int64_t hidden, int dtype, bool aligned, bool fused, int qt) {
     rmsnorm_config_t c = {RMSNORM_PATH_TWO_PASS, 16, 0, 1, 0, 0, 0};
     const bool vec = aligned && hidden % vec_elems(dtype) == 0;
-    const int64_t units = vec ? hidden / vec_elems(dtype) : hidden;
-    const int* list = vec ? mbr::kVplList : mbr::kEplList;
-    const int nlist = vec ? mbr::kNumVpl : mbr::kNumEpl;
-    const int cap = vec ? (qt ? (fused ? 5 : 4) : (fused ? 4 : 2)) : 8;
+    // any other width or alignment: full vectors at the row's own alignment
+    // plus a tail of single elements (plain and fused forms)
+    const bool any = !vec && !qt && hidden >= vec_elems(dtype);
+    const int64_t units = vec || any ? hidden / vec_elems(dtype) : hidden;
+    const int* list = vec ? mbr::kVplList : any ? mbr::kAnyVplList : mbr::kEplList;
+    const int nlist = vec ? mbr::kNumVpl : any ? mbr::kNumAnyVpl : mbr::kNumEpl;
+    const int cap = vec || any ? (qt ? (fused ? 5 : 4) : (fused ? 4 : 2)) : 8;
     auto fit = [&](int wpr) {
         const int per = round_up_in(list, nlist, ceil_div(units, int64_t(64) * wpr));
         if (per < 0) return -1;
         const bool built = qt ? (vec ? mbr::qvec_built(wpr, per) : mbr::qelem_built(wpr, per))
-                              : (vec ? mbr::vec_built(wpr, per, fused) : mbr::elem_built(wpr, per));
+                         : vec ? mbr::vec_built(wpr, per, fused)
+                         : any ? mbr::any_built(wpr, per, fused)
+                               : mbr::elem_built(wpr, per);
         return built ? per : -1;
     };
     int wpr = 1;
@@ -168,7 +173,7 @@ rmsnorm_config_t choose(int64_t rows, int64_t hidden, int dtype, bool aligned, b
         per = fit(wpr);
     }
     if (per < 0) return c;
-    if (vec && !qt && rows >= 1024 && (!fused || rows < 4096) && int64_t(64) * wpr * per > units) {
+    if ((vec || any) && !qt && rows >= 1024 && (!fused || rows < 4096) && int64_t(64) * wpr * per > units) {
         // rows the cap leaves padded (bf16 hidden 3072, 5120, 6144; fused
         // 5120 below 4096 rows): the fewest idle lanes with at most five
         // vectors per lane, ties kept as chosen.  Sweeps on MI355X: [8192,
@@ -186,7 +191,7 @@ rmsnorm_config_t choose(int64_t rows, int64_t hidden, int dtype, bool aligned, b
             }
         }
     }
-    c.path = vec ? RMSNORM_PATH_VECTOR : RMSNORM_PATH_ELEMENT;
+    c.path = vec ? RMSNORM_PATH_VECTOR : any ? RMSNORM_PATH_VECTOR_ANY : RMSNORM_PATH_ELEMENT;
     c.waves_per_row = wpr;
     c.items_per_lane = per;
     c.rows_per_block = 1;
@@ -261,6 +266,7 @@ rmsnorm_status_t launch(const Problem& p, const rmsnorm_config_t* user, hipStrea
     a.eps = p.eps;
     a.scale = p.scale;
     a.w_lds = c.weight_lds;
+    a.tail = 0;
     size_t lds_bytes = 0;
 
     const void* fn = nullptr;
@@ -292,6 +298,18 @@ rmsnorm_status_t launch(const Problem& p, const rmsnorm_config_t* user, hipStrea
                 lds_bytes = static_cast<size_t>(nvec) * kVectorBytes;
                 if (lds_bytes > kWeightLdsMax) return RMSNORM_ERR_INVALID_ARG;
             }
+            break;
+        }
+        case RMSNORM_PATH_VECTOR_ANY: {
+            if (!whole || p.qt || c.rows_per_block != 1 || c.weight_lds) return RMSNORM_ERR_INVALID_ARG;
+            const int64_t nvec = p.hidden / vec_elems(p.dtype);
+            const int vi = index_of(mbr::kAnyVplList, mbr::kNumAnyVpl, c.items_per_lane);
+            if (nvec < 1 || vi < 0 || lanes_per_row * c.items_per_lane < nvec) return RMSNORM_ERR_INVALID_ARG;
+            threads = lanes_per_row;
+            if (threads > mbr::max_threads_for(c.waves_per_row)) return RMSNORM_ERR_INVALID_ARG;
+            fn = mbr::any_kernel(p.dtype, p.fused, lanes_per_row * c.items_per_lane != nvec, wi, vi);
+            a.units = static_cast<int32_t>(nvec);
+            a.tail = static_cast<int32_t>(p.hidden - nvec * vec_elems(p.dtype));
             break;
         }
         case RMSNORM_PATH_ELEMENT: {

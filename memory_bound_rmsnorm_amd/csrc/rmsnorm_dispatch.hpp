@@ -30,11 +30,18 @@ constexpr bool elem_built(int wpr, int epl) { return wpr < 16 || epl <= 8; }
 constexpr bool qvec_built(int wpr, int vpl) { return vpl <= 8 && (wpr < 16 || vpl <= 4); }
 constexpr bool qelem_built(int wpr, int epl) { return epl <= 8 && (wpr < 16 || epl <= 4); }
 
+// Any-alignment vector path (rows of any width at any element alignment):
+// full 16-byte vectors per lane, plus a tail of single elements.
+constexpr int kAnyVplList[] = {1, 2, 3, 4, 5, 6, 7, 8};
+constexpr int kNumAnyVpl = sizeof(kAnyVplList) / sizeof(int);
+constexpr bool any_built(int wpr, int vpl, bool fused) { return wpr < 16 || vpl <= (fused ? 4 : 6); }
+
 // Host-side kernel handles (addresses of the __global__ stubs), or nullptr.
 // dtype: 0 = f32, 1 = bf16.
 const void* vec_kernel(int dtype, bool fused, bool masked, int wpr_index, int vpl_index);
 const void* elem_kernel(int dtype, bool fused, int wpr_index, int epl_index);
 const void* twopass_kernel(int dtype, bool fused, bool vec);
+const void* any_kernel(int dtype, bool fused, bool masked, int wpr_index, int vpl_index);
 
 // Quantised forms; qt: 1 = int8, 2 = fp8 e4m3fn.
 const void* qvec_kernel(int dtype, int qt, bool fused, bool masked, int wpr_index, int vpl_index);

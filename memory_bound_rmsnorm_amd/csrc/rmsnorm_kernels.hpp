@@ -57,6 +57,7 @@ struct RowArgs {
     float eps;
     float* scale;        // quantised forms: one fp32 scale per row
     int32_t w_lds;       // vector path, normalised output: weight staged in LDS
+    int32_t tail;        // any-alignment vector path: elements after the full vectors (< kVec)
 };
 
 // ---------------------------------------------------------------- dtypes
@@ -488,6 +489,117 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_vec_kernel(const RowAr
                 for (int i = 0; i < V; ++i) f[i] = f[i] * r * fw[i];
                 store_stream(outr + k * LANES + lane_row, narrow(f, E{}));
             }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- any-alignment vector path
+
+// A 16-byte vector at any element alignment.  The HSA ABI runs gfx950 in
+// unaligned-access mode, so a global load or store of 16 bytes needs only the
+// alignment of the access's own elements; the compiler then issues one
+// global_load/store_dwordx4 as for an aligned vector.
+typedef u32x4 u32x4_any2 __attribute__((aligned(2)));
+
+__device__ __forceinline__ u32x4 load_stream_any(const char* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_any2*>(p));
+}
+__device__ __forceinline__ u32x4 load_keep_any(const char* p) { return *reinterpret_cast<const u32x4_any2*>(p); }
+__device__ __forceinline__ void store_stream_any(char* p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_any2*>(p));
+}
+
+// Rows of any width and any element alignment (plain and fused forms): a row
+// of H elements is H / V full 16-byte vectors, moved at whatever alignment the
+// row starts at, and then H % V tail elements moved one by one.  Lane l of a
+// row owns vectors l, l + 64*WPR, ... (VPL of them) and, if l < H % V, tail
+// element l.  Every access stays inside the row, so nothing is read or
+// written past a row's end or the tensor's.  One row per workgroup at a
+// time; otherwise the vector path's reduction, rounding and output order.
+template <class E, int WPR, int VPL, bool MASKED, bool FUSED>
+__global__ void __launch_bounds__(max_threads<WPR>()) rms_any_kernel(const RowArgs a) {
+    using S = typename E::scalar;
+    constexpr int LANES = 64 * WPR;
+    constexpr int V = E::kVec;
+    constexpr int NR = FUSED ? VPL : 1;
+    const int wave = wave_id();
+    const int lane = static_cast<int>(threadIdx.x);
+    const int nvec = a.units;  // full vectors per row
+    const int tail = a.tail;
+    const int64_t row_bytes = (static_cast<int64_t>(nvec) * V + tail) * static_cast<int64_t>(sizeof(S));
+    __shared__ float part[2][16];
+
+    auto voff = [&](int k) {
+        const int v = k * LANES + lane;
+        return static_cast<int64_t>(MASKED ? (v < nvec ? v : nvec - 1) : v) * 16;
+    };
+    auto in_row = [&](int k) { return !MASKED || k * LANES + lane < nvec; };
+    const bool has_tail = lane < tail;
+    const int64_t toff = (static_cast<int64_t>(nvec) * V + lane) * static_cast<int64_t>(sizeof(S));
+
+    const char* wr = static_cast<const char*>(a.w);
+    int it = 0;
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x, ++it) {
+        const char* xr = static_cast<const char*>(a.x) + row * row_bytes;
+        u32x4 d[VPL], rv[NR];
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) d[k] = load_stream_any(xr + voff(k));
+        float xt = 0.f;
+        if (has_tail) xt = widen1(*reinterpret_cast<const S*>(xr + toff));
+        if constexpr (FUSED) {
+            const char* rr = static_cast<const char*>(a.res) + row * row_bytes;
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) rv[k] = load_stream_any(rr + voff(k));
+            char* hr = static_cast<char*>(a.h) + row * row_bytes;
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) {
+                float fx[V], fr[V];
+                widen(d[k], fx, E{});
+                widen(rv[k], fr, E{});
+#pragma unroll
+                for (int i = 0; i < V; ++i) fx[i] += fr[i];
+                d[k] = narrow(fx, E{});  // h rounded once; the norm sees this value
+                if (in_row(k)) store_stream_any(hr + voff(k), d[k]);
+            }
+            if (has_tail) {
+                const S ht = narrow1(xt + widen1(*reinterpret_cast<const S*>(rr + toff)), E{});
+                *reinterpret_cast<S*>(hr + toff) = ht;
+                xt = widen1(ht);
+            }
+        }
+        float ss = xt * xt;
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            float f[V];
+            widen(d[k], f, E{});
+            float s = 0.f;
+#pragma unroll
+            for (int i = 0; i < V; ++i) s += f[i] * f[i];
+            ss += in_row(k) ? s : 0.f;
+        }
+        ss = wave_sum(ss);
+        if constexpr (WPR > 1) {
+            if ((threadIdx.x & 63) == 0) part[it & 1][wave] = ss;
+            __syncthreads();
+            ss = 0.f;
+#pragma unroll
+            for (int i = 0; i < WPR; ++i) ss += part[it & 1][i];
+        }
+        const float r = rsqrtf(ss / a.hidden_f + a.eps);
+        char* outr = static_cast<char*>(a.out) + row * row_bytes;
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            if (!in_row(k)) continue;
+            float f[V], fw[V];
+            widen(d[k], f, E{});
+            widen(load_keep_any(wr + voff(k)), fw, E{});
+#pragma unroll
+            for (int i = 0; i < V; ++i) f[i] = f[i] * r * fw[i];
+            store_stream_any(outr + voff(k), narrow(f, E{}));
+        }
+        if (has_tail) {
+            const float wt = widen1(*reinterpret_cast<const S*>(wr + toff));
+            *reinterpret_cast<S*>(outr + toff) = narrow1(xt * r * wt, E{});
         }
     }
 }

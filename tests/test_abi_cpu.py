@@ -151,6 +151,19 @@ def test_bad_forced_configs_rejected():
     assert call(7, 1, 4, 1) == INV            # unknown path
     assert call(1, 1, 4, 0) == INV            # zero rows per block
     assert call(1, 1, 4, 1, mb=-1) == INV
+    # any-alignment vectors: whole-wave rows, one row per workgroup, vectors covering the full ones
+    assert call(4, 1, 2, 1, hidden=2049) == INV   # 64 x 2 vectors do not cover 256
+    assert call(4, 1, 9, 1, hidden=2049) == INV   # vectors per lane not built
+    assert call(4, 1, 4, 2, hidden=2049) == INV   # one row per workgroup
+    assert call(4, 16, 8, 1, hidden=65537) == INV  # not built (would spill)
+    assert call(4, 1, 1, 1, hidden=7) == INV      # no full vector: the element path
+    cfg = mbr.Config(4, 1, 4, 1, 0, 0, 1)           # no LDS weight on this path
+    assert L.rmsnorm_fwd_ex(A + 2, W, O, 8, 2049, 1e-5, 1, ctypes.byref(cfg), None) == INV
+    cfg = mbr.Config(4, 1, 4, 1, 0, 16)             # nor rows sharing a wave
+    assert L.rmsnorm_fwd_ex(A + 2, W, O, 8, 2049, 1e-5, 1, ctypes.byref(cfg), None) == INV
+    cfg = mbr.Config(4, 1, 4, 1, 0)                 # nor the quantised forms
+    assert L.rmsnorm_dynamic_quant_fwd_ex(A, None, W, None, O, 0x7F0030000000, 8, 2049, 1e-5, 1, 0,
+                                          ctypes.byref(cfg), None) == INV
 
     def sub(lpr, wpr, per, rpb, hidden=128, path=1):
         cfg = mbr.Config(path, wpr, per, rpb, 0, lpr)
@@ -226,9 +239,18 @@ def test_selection_is_always_a_built_covering_config(hidden, rows, dtype, aligne
         assert cfg.items_per_lane in (1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16)
         if cfg.waves_per_row == 16:
             assert cfg.items_per_lane <= (6 if fused else 10)
+    elif cfg.path == mbr.PATH_VECTOR_ANY:
+        # any width of at least one vector, any element alignment: full
+        # vectors per lane, the rest as a tail of single elements
+        assert not (aligned and hidden % vec == 0) and hidden >= vec
+        assert 64 * cfg.waves_per_row * cfg.items_per_lane >= hidden // vec
+        assert cfg.items_per_lane in range(1, 9) and cfg.rows_per_block == 1 and cfg.max_blocks == 0
+        if cfg.waves_per_row == 16:
+            assert cfg.items_per_lane <= (4 if fused else 6)
     elif cfg.path == mbr.PATH_ELEMENT:
         assert 64 * cfg.waves_per_row * cfg.items_per_lane >= hidden
         assert cfg.items_per_lane in (1, 2, 4, 8, 16)
+        assert hidden < vec  # a row of at least one vector takes a vector path
     else:
         assert cfg.path == mbr.PATH_TWO_PASS and cfg.rows_per_block == 1
         assert hidden > 8192  # everything narrower fits a register-resident path

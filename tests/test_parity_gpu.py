@@ -256,7 +256,8 @@ def _raw_plain(xp, wp, op, rows, hidden, eps, dt):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("which", ["x", "weight", "out"])
 def test_misaligned_pointers(dtype, which):
-    """Element-aligned but not 16-byte-aligned buffers take the element path."""
+    """Element-aligned but not 16-byte-aligned buffers take the any-alignment
+    vector path (full vectors at the buffer's own alignment)."""
     rows, hidden, eps = 33, 2048, 1e-5
     w = inputs.custom(rows, hidden, dtype, False)
     t = inputs.make(w, seed=11)
@@ -277,6 +278,71 @@ def test_misaligned_pointers(dtype, which):
     # nothing outside the output was written
     assert torch.count_nonzero(obuf[:off["out"]]) == 0
     assert torch.count_nonzero(obuf[off["out"] + rows * hidden:]) == 0
+
+
+def _run_any(dtype, rows, hidden, fused, cfg, off, seed):
+    """Forced configuration on buffers that start `off` elements past a
+    16-byte boundary, inside guard space: parity with the oracle, and no byte
+    outside the outputs written."""
+    w = inputs.custom(rows, hidden, dtype, fused)
+    t = inputs.make(w, seed=seed)
+    td = BF16 if dtype == "bf16" else F32
+    es = 2 if dtype == "bf16" else 4
+    n = rows * hidden
+    g = 64  # guard elements around every region
+    bases = [g + off + i * (n + 2 * g) for i in range(4)]  # x, residual, h, out
+    buf = torch.zeros(4 * (n + 2 * g) + 2 * g, dtype=td, device="cuda")
+    buf[bases[0]:bases[0] + n] = t["x"].reshape(-1).cuda()
+    if fused:
+        buf[bases[1]:bases[1] + n] = t["residual"].reshape(-1).cuda()
+    wt = t["weight"].cuda()
+    p = buf.data_ptr()
+    ptr = [p + es * b for b in bases]
+    L = mbr.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    code = mbr.dtype_code(td)
+    if fused:
+        st = L.rmsnorm_residual_fwd_ex(ptr[0], ptr[1], wt.data_ptr(), ptr[2], ptr[3], rows, hidden, w.eps, code,
+                                       ctypes.byref(cfg), stream)
+    else:
+        st = L.rmsnorm_fwd_ex(ptr[0], wt.data_ptr(), ptr[3], rows, hidden, w.eps, code, ctypes.byref(cfg), stream)
+    torch.cuda.synchronize()
+    assert st == mbr.RMSNORM_OK, mbr.rmsnorm_status_string(st)
+    cpu = inputs.bits(buf.cpu())
+    xb, wb = inputs.bits(t["x"]), inputs.bits(t["weight"])
+    if fused:
+        h_want, y_want = parity.oracle_residual(xb, inputs.bits(t["residual"]), wb, w.eps)
+        assert np.array_equal(cpu[bases[2]:bases[2] + n].reshape(rows, hidden), h_want), "residual sum differs"
+    else:
+        y_want = parity.oracle_fwd(xb, wb, w.eps)
+    parity.compare(cpu[bases[3]:bases[3] + n].reshape(rows, hidden), y_want)
+    written = np.zeros(cpu.shape, bool)
+    for i in (0, 1, 2, 3) if fused else (0, 3):
+        written[bases[i]:bases[i] + n] = True
+    assert not np.any(cpu[~written] != 0), "a byte outside the buffers changed"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("fused", [False, True])
+def test_every_any_alignment_config(dtype, fused):
+    """Every built any-alignment vector configuration, forced: full and
+    masked vector sets, tails of 0, 1 and V - 1 elements, rows starting 0, 1
+    and V - 1 elements past a 16-byte boundary."""
+    v = 8 if dtype == "bf16" else 4
+    n = 0
+    for wpr in (1, 2, 4, 8, 16):
+        for vpl in range(1, 9):
+            if wpr == 16 and vpl > (4 if fused else 6):
+                continue
+            lanes = 64 * wpr
+            for nvec in sorted({lanes * vpl, max(1, lanes * (vpl - 1) + 3)}):
+                tail = (0, 1, v - 1)[n % 3]
+                off = (1, v - 1, 0)[n % 3]
+                cfg = mbr.Config(mbr.PATH_VECTOR_ANY, wpr, vpl, 1, 2 if n % 4 == 3 else 0)
+                say("any", dtype, fused, cfg, "hidden", nvec * v + tail, "offset", off)
+                _run_any(dtype, 5, nvec * v + tail, fused, cfg, off, 4000 + n)
+                n += 1
+    assert n > 70
 
 
 def test_misaligned_fused():
