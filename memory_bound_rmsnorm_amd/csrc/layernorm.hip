@@ -35,6 +35,20 @@ const void* const* lsub_table(std::index_sequence<I...>) {
     return table;
 }
 
+template <class E, int WPR, int VPL, bool MASKED>
+const void* lany_ptr() {
+    if constexpr (ln_any_built(WPR, VPL))
+        return reinterpret_cast<const void*>(&ln_any_kernel<E, WPR, VPL, MASKED>);
+    else
+        return nullptr;
+}
+
+template <class E, bool MASKED, size_t... I>
+const void* const* lany_table(std::index_sequence<I...>) {
+    static const void* const table[] = {lany_ptr<E, kWprList[I / kNumAnyVpl], kAnyVplList[I % kNumAnyVpl], MASKED>()...};
+    return table;
+}
+
 template <class E, size_t... I>
 const void* const* lelem_table(std::index_sequence<I...>) {
     static const void* const table[] = {
@@ -58,6 +72,14 @@ const void* ln_subwave_kernel_ptr(int dtype, bool masked, int li, int vi) {
     const void* const* t = dtype == 1 ? (masked ? lsub_table<Bf16, true>(Seq{}) : lsub_table<Bf16, false>(Seq{}))
                                       : (masked ? lsub_table<F32, true>(Seq{}) : lsub_table<F32, false>(Seq{}));
     return t[li * kNumSwVpl + vi];
+}
+
+const void* ln_any_kernel_ptr(int dtype, bool masked, int wi, int vi) {
+    using Seq = std::make_index_sequence<kNumWpr * kNumAnyVpl>;
+    if (wi < 0 || wi >= kNumWpr || vi < 0 || vi >= kNumAnyVpl) return nullptr;
+    const void* const* t = dtype == 1 ? (masked ? lany_table<Bf16, true>(Seq{}) : lany_table<Bf16, false>(Seq{}))
+                                      : (masked ? lany_table<F32, true>(Seq{}) : lany_table<F32, false>(Seq{}));
+    return t[wi * kNumAnyVpl + vi];
 }
 
 const void* ln_elem_kernel_ptr(int dtype, int wi, int ei) {

@@ -38,6 +38,7 @@ struct LnArgs {
     int32_t rows_per_block;  // vector path: row slots per workgroup
     float hidden_f;
     float eps;
+    int32_t tail;            // any-alignment vector path: elements after the full vectors (< kVec)
 };
 
 // Workgroup totals of N per-lane values: wave sums, one LDS slot per wave
@@ -219,6 +220,102 @@ __global__ void __launch_bounds__(max_threads<WPR>()) ln_vec_kernel(const LnArgs
 #pragma unroll
             for (int i = 0; i < V; ++i) f[i] = fg[i] * (((f[i] - m.m0) - m.c) * m.inv) + fb[i];
             store_stream(outr + k * LANES + lane, narrow(f, E{}));
+        }
+    }
+}
+
+// Any width and any element alignment, in vectors: a row of H elements is
+// H / V full 16-byte vectors moved at the row's own alignment (unaligned
+// 16-byte accesses, as the RMSNorm any-alignment kernel), then H % V tail
+// elements, tail element l owned by lane l.  One row per workgroup at a time;
+// gamma and beta are read per row like the vector path's per-row loads.  The
+// moments are the vector path's corrected two-pass sums, with the tail
+// element added first in each lane.
+template <class E, int WPR, int VPL, bool MASKED>
+__global__ void __launch_bounds__(max_threads<WPR>()) ln_any_kernel(const LnArgs a) {
+    using S = typename E::scalar;
+    constexpr int LANES = 64 * WPR;
+    constexpr int V = E::kVec;
+    const int wave = wave_id();
+    const int lane = static_cast<int>(threadIdx.x);
+    const int nvec = a.units;
+    const int tail = a.tail;
+    const int64_t row_bytes = (static_cast<int64_t>(nvec) * V + tail) * static_cast<int64_t>(sizeof(S));
+    const bool bias = a.b != nullptr;
+    __shared__ float s1[1][16], s2[2][16];
+    auto voff = [&](int k) {
+        const int v = k * LANES + lane;
+        return static_cast<int64_t>(MASKED ? (v < nvec ? v : nvec - 1) : v) * 16;
+    };
+    auto in_row = [&](int k) { return !MASKED || k * LANES + lane < nvec; };
+    const bool has_tail = lane < tail;
+    const int64_t toff = (static_cast<int64_t>(nvec) * V + lane) * static_cast<int64_t>(sizeof(S));
+    const char* gr = static_cast<const char*>(a.g);
+    const char* br = static_cast<const char*>(a.b);
+
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+        const char* xr = static_cast<const char*>(a.x) + row * row_bytes;
+        u32x4 d[VPL];
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) d[k] = load_stream_any(xr + voff(k));
+        const float xt = has_tail ? widen1(*reinterpret_cast<const S*>(xr + toff)) : 0.f;
+        float s[1] = {xt};
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            float f[V];
+            widen(d[k], f, E{});
+            float t = 0.f;
+#pragma unroll
+            for (int i = 0; i < V; ++i) t += f[i];
+            s[0] += in_row(k) ? t : 0.f;
+        }
+        block_sums<WPR>(s, s1, wave);
+        const float m0 = s[0] / a.hidden_f;
+        u32x4 gv[VPL], bv[VPL];
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            gv[k] = load_keep_any(gr + voff(k));
+            if (bias) bv[k] = load_keep_any(br + voff(k));
+        }
+        const float et = has_tail ? xt - m0 : 0.f;
+        float tq[2] = {et, et * et};
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            float f[V];
+            widen(d[k], f, E{});
+            float t = 0.f, q = 0.f;
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                const float e = f[i] - m0;
+                t += e;
+                q += e * e;
+            }
+            tq[0] += in_row(k) ? t : 0.f;
+            tq[1] += in_row(k) ? q : 0.f;
+        }
+        block_sums<WPR>(tq, s2, wave);
+        const LnMoments m = ln_moments(m0, tq, a);
+        char* outr = static_cast<char*>(a.out) + row * row_bytes;
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            if (!in_row(k)) continue;
+            float f[V], fg[V], fb[V];
+            widen(d[k], f, E{});
+            widen(gv[k], fg, E{});
+            if (bias) {
+                widen(bv[k], fb, E{});
+            } else {
+#pragma unroll
+                for (int i = 0; i < V; ++i) fb[i] = 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < V; ++i) f[i] = fg[i] * (((f[i] - m.m0) - m.c) * m.inv) + fb[i];
+            store_stream_any(outr + voff(k), narrow(f, E{}));
+        }
+        if (has_tail) {
+            const float gt = widen1(*reinterpret_cast<const S*>(gr + toff));
+            const float bt = bias ? widen1(*reinterpret_cast<const S*>(br + toff)) : 0.f;
+            *reinterpret_cast<S*>(outr + toff) = narrow1(gt * (((xt - m.m0) - m.c) * m.inv) + bt, E{});
         }
     }
 }

@@ -669,7 +669,10 @@ bool ln_vector_aligned(const LnProblem& p) {
 rmsnorm_config_t choose_ln(int64_t rows, int64_t hidden, int dtype, bool aligned) {
     rmsnorm_config_t c = {RMSNORM_PATH_TWO_PASS, 16, 0, 1, 0, 0, 0};
     const bool vec = aligned && hidden % vec_elems(dtype) == 0;
-    const int64_t units = vec ? hidden / vec_elems(dtype) : hidden;
+    // any other width or alignment: full vectors at the row's own alignment,
+    // then a tail of single elements
+    const bool any = !vec && hidden >= vec_elems(dtype);
+    const int64_t units = vec || any ? hidden / vec_elems(dtype) : hidden;
     if (vec && units <= 64 && rows >= 1024) {
         int lpr = 0;
         for (int i = 0; i < mbr::kNumLpr && !lpr; ++i)
@@ -685,13 +688,13 @@ rmsnorm_config_t choose_ln(int64_t rows, int64_t hidden, int dtype, bool aligned
         c.lanes_per_row = lpr;
         return c;
     }
-    const int* list = vec ? mbr::kLnVplList : mbr::kLnEplList;
-    const int nlist = vec ? mbr::kNumLnVpl : mbr::kNumLnEpl;
+    const int* list = vec ? mbr::kLnVplList : any ? mbr::kAnyVplList : mbr::kLnEplList;
+    const int nlist = vec ? mbr::kNumLnVpl : any ? mbr::kNumAnyVpl : mbr::kNumLnEpl;
     const int cap = 8;
     auto fit = [&](int wpr) {
         const int per = round_up_in(list, nlist, ceil_div(units, int64_t(64) * wpr));
         if (per < 0) return -1;
-        return (!vec || mbr::ln_vec_built(wpr, per)) ? per : -1;
+        return (vec ? mbr::ln_vec_built(wpr, per) : !any || mbr::ln_any_built(wpr, per)) ? per : -1;
     };
     int wpr = 1;
     while (wpr < 16 && ceil_div(units, int64_t(64) * wpr) > cap) wpr *= 2;
@@ -702,7 +705,7 @@ rmsnorm_config_t choose_ln(int64_t rows, int64_t hidden, int dtype, bool aligned
         per = fit(wpr);
     }
     if (per < 0) return c;
-    c.path = vec ? RMSNORM_PATH_VECTOR : RMSNORM_PATH_ELEMENT;
+    c.path = vec ? RMSNORM_PATH_VECTOR : any ? RMSNORM_PATH_VECTOR_ANY : RMSNORM_PATH_ELEMENT;
     c.waves_per_row = wpr;
     c.items_per_lane = per;
     // Rows of 384 vectors or more, gamma and beta fitting LDS (sized for a
@@ -785,6 +788,7 @@ rmsnorm_status_t run_ln(const LnProblem& p, const rmsnorm_config_t* user, void* 
     a.n_groups = ceil_div(p.rows, int64_t(c.rows_per_block));
     a.hidden_f = static_cast<float>(p.hidden);
     a.eps = p.eps;
+    a.tail = 0;
     const void* fn = nullptr;
     size_t lds = 0;
     switch (c.path) {
@@ -810,6 +814,17 @@ rmsnorm_status_t run_ln(const LnProblem& p, const rmsnorm_config_t* user, void* 
                 lds = static_cast<size_t>(nvec) * kVectorBytes * (p.b ? 2 : 1);
                 if (lds > kWeightLdsMax) return RMSNORM_ERR_INVALID_ARG;
             }
+            break;
+        }
+        case RMSNORM_PATH_VECTOR_ANY: {
+            if (!whole || c.rows_per_block != 1 || c.weight_lds) return RMSNORM_ERR_INVALID_ARG;
+            const int64_t nvec = p.hidden / vec_elems(p.dtype);
+            const int vi = index_of(mbr::kAnyVplList, mbr::kNumAnyVpl, c.items_per_lane);
+            if (nvec < 1 || vi < 0 || lanes * c.items_per_lane < nvec) return RMSNORM_ERR_INVALID_ARG;
+            if (lanes > mbr::max_threads_for(c.waves_per_row)) return RMSNORM_ERR_INVALID_ARG;
+            fn = mbr::ln_any_kernel_ptr(p.dtype, lanes * c.items_per_lane != nvec, wi, vi);
+            a.units = static_cast<int32_t>(nvec);
+            a.tail = static_cast<int32_t>(p.hidden - nvec * vec_elems(p.dtype));
             break;
         }
         case RMSNORM_PATH_ELEMENT: {

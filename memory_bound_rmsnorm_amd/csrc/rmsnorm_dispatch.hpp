@@ -91,6 +91,10 @@ const void* ln_vec_kernel_ptr(int dtype, bool masked, bool gamma_beta_lds, int w
 // LayerNorm vector kernel with rows narrower than a wave (kLprList lanes per
 // row, kSwVplList vectors per lane, per-lane gamma / beta).
 const void* ln_subwave_kernel_ptr(int dtype, bool masked, int lpr_index, int vpl_index);
+// LayerNorm at any width and element alignment, in vectors (kAnyVplList);
+// x, gamma and beta are live together, so a 1024-lane workgroup takes 3.
+constexpr bool ln_any_built(int wpr, int vpl) { return wpr < 16 || vpl <= 3; }
+const void* ln_any_kernel_ptr(int dtype, bool masked, int wpr_index, int vpl_index);
 const void* ln_elem_kernel_ptr(int dtype, int wpr_index, int epl_index);
 const void* ln_multipass_kernel_ptr(int dtype, bool vec);
 

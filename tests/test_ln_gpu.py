@@ -225,7 +225,7 @@ def test_ln_misaligned_pointers(dtype):
     y = inputs.bits(obuf[1:1 + rows * hidden].reshape(rows, hidden).cpu())
     xb, gb, bb = inputs.bits(t["x"]), inputs.bits(t["weight"]), inputs.bits(t["beta"])
     cfg = mbr.layernorm_select_config(rows, hidden, td, False)
-    assert cfg.path == mbr.PATH_ELEMENT
+    assert cfg.path == mbr.PATH_VECTOR_ANY  # vectors at the buffers' own alignment
     parity.compare_ln(y, parity.oracle_ln(xb, gb, bb, eps), xb, gb, bb, eps, cfg)
     assert obuf[0].item() == 0 and torch.count_nonzero(obuf[1 + rows * hidden:]) == 0
 
@@ -287,3 +287,65 @@ def test_ln_non_finite_rows(dtype):
         t["x"][4, 100] = bad
         say("ln non-finite", dtype, bad)
         check(w, t)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ln_every_any_alignment_config(dtype):
+    """Every built any-alignment LayerNorm configuration, forced: full and
+    masked vector sets, tails of 0, 1 and V - 1 elements, x and out starting
+    0, 1 or V - 1 elements past a 16-byte boundary inside guard space, with
+    and without beta; parity with the oracle and no byte outside out written."""
+    import ctypes
+    v = 8 if dtype == "bf16" else 4
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    es = 2 if dtype == "bf16" else 4
+    L = mbr.lib()
+    n = 0
+    for wpr in (1, 2, 4, 8, 16):
+        for vpl in range(1, 9):
+            if wpr == 16 and vpl > 3:
+                continue
+            lanes = 64 * wpr
+            for nvec in sorted({lanes * vpl, max(1, lanes * (vpl - 1) + 3)}):
+                tail = (0, 1, v - 1)[n % 3]
+                off = (1, v - 1, 0)[n % 3]
+                bias = n % 2 == 0
+                rows, hidden = 5, nvec * v + tail
+                w = inputs.custom(rows, hidden, dtype, layernorm=True)
+                t = inputs.make(w, seed=5000 + n)
+                cnt, g = rows * hidden, 64
+                buf = torch.zeros(2 * (cnt + 2 * g) + 2 * g, dtype=td, device="cuda")
+                xb, ob = g + off, g + off + cnt + 2 * g
+                buf[xb:xb + cnt] = t["x"].reshape(-1).cuda()
+                gam, bet = t["weight"].cuda(), t["beta"].cuda()
+                cfg = mbr.Config(mbr.PATH_VECTOR_ANY, wpr, vpl, 1, 2 if n % 4 == 3 else 0)
+                say("ln any", dtype, cfg, "hidden", hidden, "offset", off, "bias", bias)
+                p = buf.data_ptr()
+                st = L.layernorm_fwd_ex(p + es * xb, gam.data_ptr(), bet.data_ptr() if bias else None, p + es * ob,
+                                        rows, hidden, w.eps, mbr.dtype_code(td), ctypes.byref(cfg),
+                                        torch.cuda.current_stream().cuda_stream)
+                torch.cuda.synchronize()
+                assert st == mbr.RMSNORM_OK
+                cpu = inputs.bits(buf.cpu())
+                xbits, gbits = inputs.bits(t["x"]), inputs.bits(t["weight"])
+                bbits = inputs.bits(t["beta"]) if bias else None
+                got = cpu[ob:ob + cnt].reshape(rows, hidden)
+                parity.compare_ln(got, parity.oracle_ln(xbits, gbits, bbits, w.eps), xbits, gbits, bbits, w.eps, cfg)
+                written = np.zeros(cpu.shape, bool)
+                written[xb:xb + cnt] = True
+                written[ob:ob + cnt] = True
+                assert not np.any(cpu[~written] != 0), "a byte outside the buffers changed"
+                n += 1
+    assert n == 70
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,hidden", [(300, 4097), (1027, 769), (64, 5121), (2000, 100), (5, 9)])
+def test_ln_odd_widths_automatic(rows, hidden, dtype):
+    """Widths that are not whole vectors take the any-alignment path."""
+    w = inputs.custom(rows, hidden, dtype, layernorm=True)
+    cfg = mbr.layernorm_select_config(rows, hidden, tdt(dtype), True)
+    say("ln odd", rows, hidden, dtype, cfg)
+    if hidden % (8 if dtype == "bf16" else 4):
+        assert cfg.path == mbr.PATH_VECTOR_ANY
+    check(w, inputs.make(w, seed=rows + hidden), bias=rows % 2 == 0)
