@@ -125,8 +125,9 @@ typedef enum {
     RMSNORM_PATH_VECTOR = 1,   /* row in VGPRs, 16-byte loads/stores; needs 16-byte alignment */
     RMSNORM_PATH_ELEMENT = 2,  /* row in VGPRs, one element per access; any alignment */
     RMSNORM_PATH_TWO_PASS = 3, /* row too large for registers: second read of x (and residual) */
-    RMSNORM_PATH_VECTOR_ANY = 4 /* rmsnorm_fwd_ex / rmsnorm_residual_fwd_ex only: any width of at
-                                   least one vector and any element alignment; the row's full
+    RMSNORM_PATH_VECTOR_ANY = 4 /* rmsnorm_fwd_ex / rmsnorm_residual_fwd_ex /
+                                   rmsnorm_dynamic_quant_fwd_ex: any width of at least one
+                                   vector and any element alignment; the row's full
                                    16-byte vectors at whatever alignment it has, then its last
                                    hidden % (16 / size) elements one by one; rows_per_block 1 */
 } rmsnorm_path_t;
@@ -216,8 +217,9 @@ typedef enum {
  *   scale_out      [rows] float32, 4-byte aligned.
  *   qtype          rmsnorm_quant_t; anything else -> RMSNORM_ERR_UNSUPPORTED_DTYPE.
  * q_out and scale_out may not overlap any other buffer or each other.  The
- * 16-byte vector path additionally needs q_out 16-byte aligned.  Other rules
- * and errors as rmsnorm_fwd.
+ * 16-byte vector path additionally needs q_out 16-byte aligned; otherwise (or
+ * for widths that are not whole vectors) the any-alignment path writes the
+ * codes at any byte offset.  Other rules and errors as rmsnorm_fwd.
  */
 RMSNORM_API rmsnorm_status_t rmsnorm_dynamic_quant_fwd(const void* x, const void* residual,
                                                       const void* weight, void* residual_out,
@@ -227,7 +229,7 @@ RMSNORM_API rmsnorm_status_t rmsnorm_dynamic_quant_fwd(const void* x, const void
 
 /* As rmsnorm_dynamic_quant_fwd with an explicit launch configuration; the
  * quantised kernels are built for at most 8 vectors (or elements) per lane,
- * 4 with 16 waves per row. */
+ * 4 with 16 waves per row (VECTOR_ANY: 1-8 vectors, 4 with 16 waves). */
 RMSNORM_API rmsnorm_status_t rmsnorm_dynamic_quant_fwd_ex(const void* x, const void* residual,
                                                          const void* weight, void* residual_out,
                                                          void* q_out, float* scale_out, int64_t rows,

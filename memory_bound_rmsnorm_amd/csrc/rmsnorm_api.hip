@@ -149,8 +149,8 @@ rmsnorm_config_t choose(int64_t rows, int64_t hidden, int dtype, bool aligned, b
     rmsnorm_config_t c = {RMSNORM_PATH_TWO_PASS, 16, 0, 1, 0, 0, 0};
     const bool vec = aligned && hidden % vec_elems(dtype) == 0;
     // any other width or alignment: full vectors at the row's own alignment
-    // plus a tail of single elements (plain and fused forms)
-    const bool any = !vec && !qt && hidden >= vec_elems(dtype);
+    // plus a tail of single elements (every form)
+    const bool any = !vec && hidden >= vec_elems(dtype);
     const int64_t units = vec || any ? hidden / vec_elems(dtype) : hidden;
     const int* list = vec ? mbr::kVplList : any ? mbr::kAnyVplList : mbr::kEplList;
     const int nlist = vec ? mbr::kNumVpl : any ? mbr::kNumAnyVpl : mbr::kNumEpl;
@@ -158,7 +158,9 @@ rmsnorm_config_t choose(int64_t rows, int64_t hidden, int dtype, bool aligned, b
     auto fit = [&](int wpr) {
         const int per = round_up_in(list, nlist, ceil_div(units, int64_t(64) * wpr));
         if (per < 0) return -1;
-        const bool built = qt ? (vec ? mbr::qvec_built(wpr, per) : mbr::qelem_built(wpr, per))
+        const bool built = qt ? (vec ? mbr::qvec_built(wpr, per)
+                                 : any ? mbr::qany_built(wpr, per)
+                                       : mbr::qelem_built(wpr, per))
                          : vec ? mbr::vec_built(wpr, per, fused)
                          : any ? mbr::any_built(wpr, per, fused)
                                : mbr::elem_built(wpr, per);
@@ -301,13 +303,15 @@ rmsnorm_status_t launch(const Problem& p, const rmsnorm_config_t* user, hipStrea
             break;
         }
         case RMSNORM_PATH_VECTOR_ANY: {
-            if (!whole || p.qt || c.rows_per_block != 1 || c.weight_lds) return RMSNORM_ERR_INVALID_ARG;
+            if (!whole || c.rows_per_block != 1 || c.weight_lds) return RMSNORM_ERR_INVALID_ARG;
             const int64_t nvec = p.hidden / vec_elems(p.dtype);
             const int vi = index_of(mbr::kAnyVplList, mbr::kNumAnyVpl, c.items_per_lane);
             if (nvec < 1 || vi < 0 || lanes_per_row * c.items_per_lane < nvec) return RMSNORM_ERR_INVALID_ARG;
             threads = lanes_per_row;
             if (threads > mbr::max_threads_for(c.waves_per_row)) return RMSNORM_ERR_INVALID_ARG;
-            fn = mbr::any_kernel(p.dtype, p.fused, lanes_per_row * c.items_per_lane != nvec, wi, vi);
+            const bool masked = lanes_per_row * c.items_per_lane != nvec;
+            fn = p.qt ? mbr::qany_kernel(p.dtype, p.qt, p.fused, masked, wi, vi)
+                      : mbr::any_kernel(p.dtype, p.fused, masked, wi, vi);
             a.units = static_cast<int32_t>(nvec);
             a.tail = static_cast<int32_t>(p.hidden - nvec * vec_elems(p.dtype));
             break;

@@ -35,6 +35,8 @@ constexpr bool qelem_built(int wpr, int epl) { return epl <= 8 && (wpr < 16 || e
 constexpr int kAnyVplList[] = {1, 2, 3, 4, 5, 6, 7, 8};
 constexpr int kNumAnyVpl = sizeof(kAnyVplList) / sizeof(int);
 constexpr bool any_built(int wpr, int vpl, bool fused) { return wpr < 16 || vpl <= (fused ? 4 : 6); }
+// Its quantised forms hold the weight slice as well, as on the vector path.
+constexpr bool qany_built(int wpr, int vpl) { return wpr < 16 || vpl <= 4; }
 
 // Host-side kernel handles (addresses of the __global__ stubs), or nullptr.
 // dtype: 0 = f32, 1 = bf16.
@@ -45,6 +47,7 @@ const void* any_kernel(int dtype, bool fused, bool masked, int wpr_index, int vp
 
 // Quantised forms; qt: 1 = int8, 2 = fp8 e4m3fn.
 const void* qvec_kernel(int dtype, int qt, bool fused, bool masked, int wpr_index, int vpl_index);
+const void* qany_kernel(int dtype, int qt, bool fused, bool masked, int wpr_index, int vpl_index);
 const void* qelem_kernel(int dtype, int qt, bool fused, int wpr_index, int epl_index);
 const void* qtwopass_kernel(int dtype, int qt, bool fused, bool vec);
 const void* qvec_kernel_bf16(int qt, bool fused, bool masked, int wi, int vi);

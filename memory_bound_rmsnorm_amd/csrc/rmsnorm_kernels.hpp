@@ -509,14 +509,32 @@ __device__ __forceinline__ void store_stream_any(char* p, u32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4_any2*>(p));
 }
 
-// Rows of any width and any element alignment (plain and fused forms): a row
-// of H elements is H / V full 16-byte vectors, moved at whatever alignment the
-// row starts at, and then H % V tail elements moved one by one.  Lane l of a
-// row owns vectors l, l + 64*WPR, ... (VPL of them) and, if l < H % V, tail
+// Codes of one input vector at any byte offset: 8 bytes for bf16, 4 for fp32.
+typedef u32x2 u32x2_any1 __attribute__((aligned(1)));
+typedef unsigned u32_any1 __attribute__((aligned(1)));
+template <int QT>
+__device__ __forceinline__ void store_codes_any(char* p, const float (&t)[8], Bf16) {
+    u32x2 c;
+    c[0] = quant_pack4<QT>(t[0], t[1], t[2], t[3]);
+    c[1] = quant_pack4<QT>(t[4], t[5], t[6], t[7]);
+    __builtin_nontemporal_store(c, reinterpret_cast<u32x2_any1*>(p));
+}
+template <int QT>
+__device__ __forceinline__ void store_codes_any(char* p, const float (&t)[4], F32) {
+    __builtin_nontemporal_store(quant_pack4<QT>(t[0], t[1], t[2], t[3]), reinterpret_cast<u32_any1*>(p));
+}
+
+// Rows of any width and any element alignment (every form): a row of H
+// elements is H / V full 16-byte vectors, moved at whatever alignment the row
+// starts at, and then H % V tail elements moved one by one.  Lane l of a row
+// owns vectors l, l + 64*WPR, ... (VPL of them) and, if l < H % V, tail
 // element l.  Every access stays inside the row, so nothing is read or
 // written past a row's end or the tensor's.  One row per workgroup at a
 // time; otherwise the vector path's reduction, rounding and output order.
-template <class E, int WPR, int VPL, bool MASKED, bool FUSED>
+// The quantised forms (QT) hold the weight slice from the start, as on the
+// vector path, and write their codes at the row's byte offset in the code
+// tensor.
+template <class E, int WPR, int VPL, bool MASKED, bool FUSED, int QT = 0>
 __global__ void __launch_bounds__(max_threads<WPR>()) rms_any_kernel(const RowArgs a) {
     using S = typename E::scalar;
     constexpr int LANES = 64 * WPR;
@@ -526,8 +544,10 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_any_kernel(const RowAr
     const int lane = static_cast<int>(threadIdx.x);
     const int nvec = a.units;  // full vectors per row
     const int tail = a.tail;
-    const int64_t row_bytes = (static_cast<int64_t>(nvec) * V + tail) * static_cast<int64_t>(sizeof(S));
+    const int64_t row_elems = static_cast<int64_t>(nvec) * V + tail;
+    const int64_t row_bytes = row_elems * static_cast<int64_t>(sizeof(S));
     __shared__ float part[2][16];
+    __shared__ float mpart[QT ? 2 : 1][QT ? 16 : 1];
 
     auto voff = [&](int k) {
         const int v = k * LANES + lane;
@@ -538,6 +558,13 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_any_kernel(const RowAr
     const int64_t toff = (static_cast<int64_t>(nvec) * V + lane) * static_cast<int64_t>(sizeof(S));
 
     const char* wr = static_cast<const char*>(a.w);
+    u32x4 wv[QT ? VPL : 1];
+    float wt = 0.f;
+    if constexpr (QT != 0) {
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) wv[k] = load_keep_any(wr + voff(k));
+        if (has_tail) wt = widen1(*reinterpret_cast<const S*>(wr + toff));
+    }
     int it = 0;
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x, ++it) {
         const char* xr = static_cast<const char*>(a.x) + row * row_bytes;
@@ -568,6 +595,7 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_any_kernel(const RowAr
             }
         }
         float ss = xt * xt;
+        float mx = QT != 0 ? fabsf(xt * wt) : 0.f;
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             float f[V];
@@ -576,16 +604,50 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_any_kernel(const RowAr
 #pragma unroll
             for (int i = 0; i < V; ++i) s += f[i] * f[i];
             ss += in_row(k) ? s : 0.f;
+            if constexpr (QT != 0) {
+                float fw[V];
+                widen(wv[k], fw, E{});
+                float m = 0.f;
+#pragma unroll
+                for (int i = 0; i < V; ++i) m = fmaxf(m, fabsf(f[i] * fw[i]));
+                mx = in_row(k) ? fmaxf(mx, m) : mx;
+            }
         }
         ss = wave_sum(ss);
+        if constexpr (QT != 0) mx = wave_max(mx);
         if constexpr (WPR > 1) {
-            if ((threadIdx.x & 63) == 0) part[it & 1][wave] = ss;
+            if ((threadIdx.x & 63) == 0) {
+                part[it & 1][wave] = ss;
+                if constexpr (QT != 0) mpart[it & 1][wave] = mx;
+            }
             __syncthreads();
             ss = 0.f;
 #pragma unroll
             for (int i = 0; i < WPR; ++i) ss += part[it & 1][i];
+            if constexpr (QT != 0) {
+                mx = 0.f;
+#pragma unroll
+                for (int i = 0; i < WPR; ++i) mx = fmaxf(mx, mpart[it & 1][i]);
+            }
         }
         const float r = rsqrtf(ss / a.hidden_f + a.eps);
+        if constexpr (QT != 0) {
+            const float inv = mx > 0.f ? quant_max<QT>() / mx : 0.f;
+            if (lane == 0) a.scale[row] = r * mx / quant_max<QT>();
+            char* qr = static_cast<char*>(a.out) + row * row_elems;  // one byte per element
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) {
+                if (!in_row(k)) continue;
+                float f[V], fw[V];
+                widen(d[k], f, E{});
+                widen(wv[k], fw, E{});
+#pragma unroll
+                for (int i = 0; i < V; ++i) f[i] = (f[i] * fw[i]) * inv;
+                store_codes_any<QT>(qr + voff(k) / static_cast<int64_t>(sizeof(S)), f, E{});
+            }
+            if (has_tail) qr[nvec * V + lane] = static_cast<char>(quant_code<QT>((xt * wt) * inv));
+            continue;
+        }
         char* outr = static_cast<char*>(a.out) + row * row_bytes;
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {

@@ -161,7 +161,10 @@ def test_bad_forced_configs_rejected():
     assert L.rmsnorm_fwd_ex(A + 2, W, O, 8, 2049, 1e-5, 1, ctypes.byref(cfg), None) == INV
     cfg = mbr.Config(4, 1, 4, 1, 0, 16)             # nor rows sharing a wave
     assert L.rmsnorm_fwd_ex(A + 2, W, O, 8, 2049, 1e-5, 1, ctypes.byref(cfg), None) == INV
-    cfg = mbr.Config(4, 1, 4, 1, 0)                 # nor the quantised forms
+    cfg = mbr.Config(4, 16, 5, 1, 0)                # quantised forms: at most 4 vectors at 16 waves
+    assert L.rmsnorm_dynamic_quant_fwd_ex(A, None, W, None, O, 0x7F0030000000, 8, 16 * 64 * 5 * 8 - 3, 1e-5, 1, 0,
+                                          ctypes.byref(cfg), None) == INV
+    cfg = mbr.Config(4, 1, 4, 2, 0)                 # and one row per workgroup
     assert L.rmsnorm_dynamic_quant_fwd_ex(A, None, W, None, O, 0x7F0030000000, 8, 2049, 1e-5, 1, 0,
                                           ctypes.byref(cfg), None) == INV
 
@@ -346,6 +349,11 @@ def test_quant_selection_is_always_built(hidden, rows, dtype, fused):
     if cfg.path == mbr.PATH_VECTOR:
         assert cfg.items_per_lane <= (4 if cfg.waves_per_row == 16 else 8)
         assert 64 * cfg.waves_per_row * cfg.items_per_lane * (4 if dtype == torch.float32 else 8) >= hidden
+    elif cfg.path == mbr.PATH_VECTOR_ANY:
+        v = 4 if dtype == torch.float32 else 8
+        assert hidden % v != 0 and hidden >= v and cfg.rows_per_block == 1 and cfg.lanes_per_row == 0
+        assert cfg.items_per_lane <= (4 if cfg.waves_per_row == 16 else 8)
+        assert 64 * cfg.waves_per_row * cfg.items_per_lane >= hidden // v
     elif cfg.path == mbr.PATH_ELEMENT:
         assert cfg.items_per_lane <= (4 if cfg.waves_per_row == 16 else 8)
         assert 64 * cfg.waves_per_row * cfg.items_per_lane >= hidden

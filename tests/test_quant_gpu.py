@@ -3,6 +3,7 @@
 Codes must equal the oracle's except where Q*v*w/max|v*w| lies within float32
 error of a tie between two codes (tests/parity.py::compare_quant); scales
 within 1e-5 relative; the residual sum h bitwise."""
+import ctypes
 import sys
 
 import numpy as np
@@ -260,3 +261,84 @@ def test_non_finite_rows_stay_in_their_row(q):
     _, q_o, s_o = parity.oracle_quant(xb, wb, w.eps, QT[q])
     q_gk = q_g[keep].view(np.int8) if QT[q] == 0 else q_g[keep]
     say(parity.compare_quant(q_gk, q_o, s_g[keep], s_o, parity.quant_t(xb, wb, QT[q]), QT[q]))
+
+
+def _run_any_quant(dtype, rows, hidden, fused, qtype, cfg, off, qoff, seed):
+    """Forced configuration with x (residual, h) starting `off` elements and
+    the codes `qoff` bytes past a 16-byte boundary, inside guard space: parity
+    with the oracle, and no byte outside the outputs written."""
+    w = inputs.custom(rows, hidden, dtype, fused)
+    t = inputs.make(w, seed=seed)
+    td = BF16 if dtype == "bf16" else F32
+    es = 2 if dtype == "bf16" else 4
+    n = rows * hidden
+    g = 64
+    bases = [g + off + i * (n + 2 * g) for i in range(3)]  # x, residual, h
+    buf = torch.zeros(3 * (n + 2 * g) + 2 * g, dtype=td, device="cuda")
+    buf[bases[0]:bases[0] + n] = t["x"].reshape(-1).cuda()
+    if fused:
+        buf[bases[1]:bases[1] + n] = t["residual"].reshape(-1).cuda()
+    qbuf = torch.zeros(n + 2 * g, dtype=torch.uint8, device="cuda")
+    sbuf = torch.zeros(rows + 2, dtype=torch.float32, device="cuda")
+    wt = t["weight"].cuda()
+    p = buf.data_ptr()
+    ptr = [p + es * b for b in bases]
+    st = mbr.lib().rmsnorm_dynamic_quant_fwd_ex(
+        ptr[0], ptr[1] if fused else None, wt.data_ptr(), ptr[2] if fused else None, qbuf.data_ptr() + g + qoff,
+        sbuf.data_ptr() + 4, rows, hidden, w.eps, mbr.dtype_code(td), qtype, ctypes.byref(cfg),
+        torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == mbr.RMSNORM_OK, mbr.rmsnorm_status_string(st)
+    cpu, q_all, s_all = inputs.bits(buf.cpu()), qbuf.cpu().numpy(), sbuf.cpu().numpy()
+    xb, wb = inputs.bits(t["x"]), inputs.bits(t["weight"])
+    rb = inputs.bits(t["residual"]) if fused else None
+    h_o, q_o, s_o = parity.oracle_quant(xb, wb, w.eps, qtype, residual=rb)
+    if fused:
+        assert np.array_equal(cpu[bases[2]:bases[2] + n].reshape(rows, hidden), h_o), "residual sum differs"
+    q_g = q_all[g + qoff:g + qoff + n].reshape(rows, hidden)
+    v = h_o if fused else xb
+    say(parity.compare_quant(q_g.view(np.int8) if qtype == 0 else q_g, q_o, s_all[1:1 + rows], s_o,
+                             parity.quant_t(v, wb, qtype), qtype))
+    written = np.zeros(cpu.shape, bool)
+    for i in (0, 1, 2) if fused else (0,):
+        written[bases[i]:bases[i] + n] = True
+    assert not np.any(cpu[~written] != 0), "a byte outside x, residual and h changed"
+    assert not np.any(q_all[:g + qoff] != 0) and not np.any(q_all[g + qoff + n:] != 0), "a code outside q changed"
+    assert s_all[0] == 0 and s_all[-1] == 0, "a scale outside the row range changed"
+
+
+@pytest.mark.parametrize("q", ["int8", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("fused", [False, True])
+def test_every_any_alignment_quant_config(dtype, fused, q):
+    """Every built quantised any-alignment configuration, forced: full and
+    masked vector sets, tails of 0, 1 and V - 1 elements, inputs and codes
+    at several offsets from a 16-byte boundary."""
+    v = 8 if dtype == "bf16" else 4
+    n = 0
+    for wpr in (1, 2, 4, 8, 16):
+        for vpl in range(1, 9):
+            if wpr == 16 and vpl > 4:
+                continue
+            lanes = 64 * wpr
+            for nvec in sorted({lanes * vpl, max(1, lanes * (vpl - 1) + 3)}):
+                tail = (0, 1, v - 1)[n % 3]
+                off = (1, v - 1, 0)[n % 3]
+                qoff = (3, 0, 1, 7)[n % 4]
+                cfg = mbr.Config(mbr.PATH_VECTOR_ANY, wpr, vpl, 1, 2 if n % 4 == 3 else 0)
+                say("quant any", q, dtype, fused, cfg, "hidden", nvec * v + tail, "offsets", off, qoff)
+                _run_any_quant(dtype, 5, nvec * v + tail, fused, QT[q], cfg, off, qoff, 5000 + n)
+                n += 1
+    assert n == 72
+
+
+@pytest.mark.parametrize("q", ["int8", "fp8"])
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("hidden", [8191, 5121, 4097, 1031])
+def test_odd_widths_automatic_quant(hidden, fused, q):
+    """Widths that are not whole vectors take the any-alignment path by
+    themselves, at the sizes of the workloads."""
+    cfg = mbr.rmsnorm_select_quant_config(4096, hidden, BF16, True, fused)
+    assert cfg.path == mbr.PATH_VECTOR_ANY
+    say("quant odd width", q, hidden, fused, cfg.as_dict())
+    _run_any_quant("bf16", 2048 if hidden > 5000 else 4096, hidden, fused, QT[q], cfg, 1, 5, hidden)
