@@ -3,8 +3,9 @@
  *
  * It is the measuring stick for the RMSNorm kernels, not part of the RMSNorm
  * operation: the bandwidth a kernel that reads N bytes and writes N bytes can
- * reach on this GPU ("spec versus achievable": the TileLang tutorial ch. 02,
- * section 2.2, notes that a copy mix reaches only part of the quoted HBM
+ * reach on this GPU (the TileLang tutorial ch. 02, section 2.2, sets datasheet
+ * against attainable bandwidth;
+ * it notes that a copy mix reaches only part of the quoted HBM
  * bandwidth), and the known-size kernel used to scale the FETCH_SIZE and
  * WRITE_SIZE hardware counters into bytes.
  */
