@@ -126,7 +126,8 @@ typedef enum {
     RMSNORM_PATH_ELEMENT = 2,  /* row in VGPRs, one element per access; any alignment */
     RMSNORM_PATH_TWO_PASS = 3, /* row too large for registers: second read of x (and residual) */
     RMSNORM_PATH_VECTOR_ANY = 4 /* rmsnorm_fwd_ex / rmsnorm_residual_fwd_ex /
-                                   rmsnorm_dynamic_quant_fwd_ex: any width of at least one
+                                   rmsnorm_dynamic_quant_fwd_ex / rmsnorm_bwd_ex /
+                                   layernorm_fwd_ex: any width of at least one
                                    vector and any element alignment; the row's full
                                    16-byte vectors at whatever alignment it has, then its last
                                    hidden % (16 / size) elements one by one; rows_per_block 1 */

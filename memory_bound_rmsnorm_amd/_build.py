@@ -24,7 +24,7 @@ RESOURCE_USAGE = os.path.join(BUILD, "resource_usage.txt")
 
 RMSNORM_SOURCES = ["rmsnorm_api.hip", "rmsnorm_misc.hip", "rmsnorm_vec_bf16.hip", "rmsnorm_vec_f32.hip", "rmsnorm_any.hip",
                    "rmsnorm_any_quant.hip", "rmsnorm_quant_bf16.hip", "rmsnorm_quant_f32.hip", "rmsnorm_quant_misc.hip",
-                   "rmsnorm_subwave.hip", "rmsnorm_bwd.hip", "layernorm.hip", "kv_cache.hip"]
+                   "rmsnorm_subwave.hip", "rmsnorm_bwd.hip", "rmsnorm_bwd_any.hip", "layernorm.hip", "kv_cache.hip"]
 COPY_SOURCES = ["hbm_copy.hip"]
 
 # Packed-fp32 VALU forms are disabled: hipcc emits them from plain float code
@@ -112,7 +112,8 @@ KERNEL_SOURCES = {
     "fwd": ["rmsnorm_kernels.hpp", "rmsnorm_vec_bf16.hip", "rmsnorm_vec_f32.hip", "rmsnorm_misc.hip",
             "rmsnorm_quant_bf16.hip", "rmsnorm_quant_f32.hip", "rmsnorm_quant_misc.hip", "rmsnorm_subwave.hip",
             "rmsnorm_any.hip", "rmsnorm_any_quant.hip", "hbm_copy.hip"],
-    "bwd": ["rmsnorm_kernels.hpp", "rmsnorm_bwd_kernels.hpp", "rmsnorm_bwd.hip", "hbm_copy.hip"],
+    "bwd": ["rmsnorm_kernels.hpp", "rmsnorm_bwd_kernels.hpp", "rmsnorm_bwd.hip", "rmsnorm_bwd_any.hip",
+            "hbm_copy.hip"],
     "ln": ["rmsnorm_kernels.hpp", "layernorm_kernels.hpp", "layernorm.hip", "hbm_copy.hip"],
     "kv": ["rmsnorm_kernels.hpp", "kv_kernels.hpp", "kv_cache.hip", "hbm_copy.hip"],
 }

@@ -430,10 +430,14 @@ bool bwd_vector_aligned(const BwdProblem& p) {
 rmsnorm_config_t choose_bwd(int64_t rows, int64_t hidden, int dtype, bool aligned) {
     rmsnorm_config_t c = {RMSNORM_PATH_TWO_PASS, 16, 0, 1, static_cast<int32_t>(kBwdGrid), 0, 0};
     const bool vec = aligned && hidden % vec_elems(dtype) == 0;
-    const int64_t units = vec ? hidden / vec_elems(dtype) : hidden;
-    const int* list = vec ? mbr::kBwdVplList : mbr::kBwdEplList;
-    const int nlist = vec ? mbr::kNumBwdVpl : mbr::kNumBwdEpl;
-    const int cap = vec ? 4 : 8;
+    // any other width or alignment: full vectors at the row's own alignment
+    // plus a tail of single elements, one row per workgroup
+    const bool any = !vec && hidden >= vec_elems(dtype);
+    const bool vlike = vec || any;
+    const int64_t units = vlike ? hidden / vec_elems(dtype) : hidden;
+    const int* list = vlike ? mbr::kBwdVplList : mbr::kBwdEplList;
+    const int nlist = vlike ? mbr::kNumBwdVpl : mbr::kNumBwdEpl;
+    const int cap = vlike ? 4 : 8;
     const bool few = rows < 1024;
     if (vec && !few && units <= 64) {
         int lpr = 0;
@@ -453,10 +457,11 @@ rmsnorm_config_t choose_bwd(int64_t rows, int64_t hidden, int dtype, bool aligne
     auto fit = [&](int wpr) {
         const int per = round_up_in(list, nlist, ceil_div(units, int64_t(64) * wpr));
         if (per < 0) return -1;
-        return (!vec || mbr::bwd_vec_built(wpr, per)) ? per : -1;
+        const bool built = vec ? mbr::bwd_vec_built(wpr, per) : !any || mbr::bwd_any_built(wpr, per);
+        return built ? per : -1;
     };
     const bool whole_row = vec && !few && rows < 8192 && units <= 512;
-    const bool balanced = vec && !few && !whole_row;
+    const bool balanced = vlike && !few && !whole_row;
     int wpr = 1;
     if (balanced) {
         int64_t best_pad = -1;
@@ -473,7 +478,7 @@ rmsnorm_config_t choose_bwd(int64_t rows, int64_t hidden, int dtype, bool aligne
         }
     } else if (!whole_row) {
         while (wpr < 16 && ceil_div(units, int64_t(64) * wpr) > cap) wpr *= 2;
-        while (!vec && wpr < 4 && units >= int64_t(64) * wpr * 2) wpr *= 2;
+        while (!vlike && wpr < 4 && units >= int64_t(64) * wpr * 2) wpr *= 2;
         while (wpr < 16 && rows < 2048 / wpr && units >= int64_t(64) * wpr * 2) wpr *= 2;
     }
     int per = fit(wpr);
@@ -482,14 +487,14 @@ rmsnorm_config_t choose_bwd(int64_t rows, int64_t hidden, int dtype, bool aligne
         per = fit(wpr);
     }
     if (per < 0) return c;
-    c.path = vec ? RMSNORM_PATH_VECTOR : RMSNORM_PATH_ELEMENT;
+    c.path = vec ? RMSNORM_PATH_VECTOR : any ? RMSNORM_PATH_VECTOR_ANY : RMSNORM_PATH_ELEMENT;
     c.waves_per_row = wpr;
     c.items_per_lane = per;
     if (whole_row) {
         c.rows_per_block = units <= 128 ? 8 : 4;
         c.max_blocks = 256;
     } else if (balanced) {
-        c.rows_per_block = wpr < 4 ? 4 / wpr : 1;
+        c.rows_per_block = wpr < 4 && vec ? 4 / wpr : 1;
         c.max_blocks = 512;
     }
     return c;
@@ -574,6 +579,7 @@ rmsnorm_status_t run_bwd(const BwdProblem& p, const rmsnorm_config_t* user, void
     a.ld = bwd_ld(p.hidden);
     a.inv_hidden = static_cast<float>(1.0 / static_cast<double>(p.hidden));
     a.eps = p.eps;
+    a.tail = 0;
     const void* fn = nullptr;
     const int64_t threads = lanes * c.rows_per_block;
     size_t lds = 0;
@@ -600,6 +606,17 @@ rmsnorm_status_t run_bwd(const BwdProblem& p, const rmsnorm_config_t* user, void
             // combine their dweight sums in LDS: hidden floats
             if (dw && (whole ? c.rows_per_block > 1 : threads > 64)) lds = static_cast<size_t>(p.hidden) * 4;
             if (lds > kBwdCombineLds) return RMSNORM_ERR_INVALID_ARG;
+            break;
+        }
+        case RMSNORM_PATH_VECTOR_ANY: {
+            if (!whole) return RMSNORM_ERR_INVALID_ARG;  // rows_per_block 1: checked above
+            const int64_t nvec = p.hidden / vec_elems(p.dtype);
+            const int vi = index_of(mbr::kBwdVplList, mbr::kNumBwdVpl, c.items_per_lane);
+            if (nvec < 1 || vi < 0 || lanes * c.items_per_lane < nvec) return RMSNORM_ERR_INVALID_ARG;
+            if (threads > mbr::max_threads_for(c.waves_per_row)) return RMSNORM_ERR_INVALID_ARG;
+            fn = mbr::bwd_any_kernel(p.dtype, dw, lanes * c.items_per_lane != nvec, wi, vi);
+            a.units = static_cast<int32_t>(nvec);
+            a.tail = static_cast<int32_t>(p.hidden - nvec * vec_elems(p.dtype));
             break;
         }
         case RMSNORM_PATH_ELEMENT: {

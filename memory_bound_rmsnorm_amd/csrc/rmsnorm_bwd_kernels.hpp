@@ -41,6 +41,7 @@ struct BwdArgs {
     float inv_hidden;        // 1 / hidden rounded once on the host (exact for powers of two):
                              // the row sums multiply by it instead of dividing
     float eps;
+    int32_t tail;            // any-alignment path: elements after the row's full vectors
 };
 
 struct DwArgs {
@@ -329,6 +330,122 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_bwd_elem_kernel(const 
 #pragma unroll
         for (int k = 0; k < EPL; ++k)
             if (in_row(k)) pr[k * LANES + lane] = acc[k];
+    }
+}
+
+// The any-alignment kernel also holds its tail values: it repacks from 5
+// vectors per lane (3 in a 1024-lane workgroup) to stay clear of spills.
+template <int WPR, int VPL>
+constexpr bool kBwdAnyRepack = VPL >= 5 || (WPR == 16 && VPL >= 3);
+
+// Any width and any element alignment, in vectors: a row of H elements is
+// H / V full 16-byte vectors, moved at whatever alignment the row starts at,
+// and then H % V tail elements moved one by one.  Lane l owns vectors l,
+// l + 64*WPR, ... (VPL of them) and, if l < H % V, tail element l; every
+// access stays inside its row.  One row per workgroup at a time; otherwise the
+// vector path's sums, rounding and dweight partial rows (columns of the tail
+// land in the partial row's last H % V places).
+template <class E, int WPR, int VPL, bool MASKED, bool DW>
+__global__ void __launch_bounds__(max_threads<WPR>()) rms_bwd_any_kernel(const BwdArgs a) {
+    using S = typename E::scalar;
+    constexpr int LANES = 64 * WPR;
+    constexpr int V = E::kVec;
+    const int wave = wave_id();
+    const int lane = static_cast<int>(threadIdx.x);
+    const int nvec = a.units;
+    const int tail = a.tail;
+    const int64_t row_bytes = (static_cast<int64_t>(nvec) * V + tail) * static_cast<int64_t>(sizeof(S));
+    __shared__ float ps[2][16], pc[2][16];
+
+    // 32-bit byte offsets within a row on a wave-uniform row base, as on the
+    // vector path
+    auto voff = [&](int k) {
+        const int v = k * LANES + lane;
+        return static_cast<unsigned>(MASKED ? (v < nvec ? v : nvec - 1) : v) * 16u;
+    };
+    auto in_row = [&](int k) { return !MASKED || k * LANES + lane < nvec; };
+    const bool has_tail = lane < tail;
+    const unsigned toff = static_cast<unsigned>((nvec * V + lane) * static_cast<int>(sizeof(S)));
+
+    const char* wr = static_cast<const char*>(a.w);
+    u32x4 wv[VPL];
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) wv[k] = load_keep_any(wr + voff(k));
+    const float wt = has_tail ? widen1(*reinterpret_cast<const S*>(wr + toff)) : 0.f;
+    float acc[DW ? VPL * V : 1], acct = 0.f;
+    if constexpr (DW) {
+#pragma unroll
+        for (int i = 0; i < VPL * V; ++i) acc[i] = 0.f;
+    }
+
+    int it = 0;
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x, ++it) {
+        const char* xr = static_cast<const char*>(a.x) + row * row_bytes;
+        const char* gr = static_cast<const char*>(a.dy) + row * row_bytes;
+        u32x4 xv[VPL], gv[VPL];
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) xv[k] = load_stream_any(xr + voff(k));
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) gv[k] = load_stream_any(gr + voff(k));
+        float xt = 0.f, gt = 0.f;
+        if (has_tail) {
+            xt = widen1(*reinterpret_cast<const S*>(xr + toff));
+            gt = widen1(*reinterpret_cast<const S*>(gr + toff));
+        }
+        float ss = xt * xt, cc = (gt * wt) * xt;
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            float fx[V], fg[V], fw[V];
+            widen(xv[k], fx, E{});
+            widen(gv[k], fg, E{});
+            widen(wv[k], fw, E{});
+            float s = 0.f, c = 0.f;
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                s += fx[i] * fx[i];
+                c += (fg[i] * fw[i]) * fx[i];
+            }
+            ss += in_row(k) ? s : 0.f;
+            cc += in_row(k) ? c : 0.f;
+        }
+        row_sums<WPR>(ss, cc, ps, pc, it, wave);
+        if constexpr (kBwdAnyRepack<WPR, VPL>) {
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) {
+                repack(xv[k]);
+                repack(gv[k]);
+                repack(wv[k]);
+            }
+        }
+        const float r = rsqrtf(mul_rn(ss, a.inv_hidden) + a.eps);
+        const float k2 = mul_rn(r * r * cc, a.inv_hidden);
+        char* dxr = static_cast<char*>(a.dx) + row * row_bytes;
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            if (!in_row(k)) continue;
+            float fx[V], fg[V], fw[V], d[V];
+            widen(xv[k], fx, E{});
+            widen(gv[k], fg, E{});
+            widen(wv[k], fw, E{});
+#pragma unroll
+            for (int i = 0; i < V; ++i) d[i] = r * (fg[i] * fw[i] - fx[i] * k2);
+            store_stream_any(dxr + voff(k), narrow(d, E{}));
+            if constexpr (DW) {
+#pragma unroll
+                for (int i = 0; i < V; ++i) acc[k * V + i] += (fg[i] * fx[i]) * r;
+            }
+        }
+        if (has_tail) {
+            *reinterpret_cast<S*>(dxr + toff) = narrow1(r * (gt * wt - xt * k2), E{});
+            if constexpr (DW) acct += (gt * xt) * r;
+        }
+    }
+    if constexpr (DW) {
+        float* pr = a.part + static_cast<int64_t>(blockIdx.x) * a.ld;
+#pragma unroll
+        for (int k = 0; k < VPL; ++k)
+            if (in_row(k)) store_partial(pr + static_cast<int64_t>(k * LANES + lane) * V, acc + k * V, E{});
+        if (has_tail) pr[nvec * V + lane] = acct;
     }
 }
 

@@ -74,6 +74,10 @@ constexpr bool bwd_vec_built(int wpr, int vpl) { return wpr < 16 || vpl <= 4; }
 
 const void* bwd_vec_kernel(int dtype, bool dw, bool masked, int wpr_index, int vpl_index);
 const void* bwd_elem_kernel(int dtype, bool dw, int wpr_index, int epl_index);
+// Any width and element alignment, in vectors (kBwdVplList); it also holds
+// its tail values, so 16 waves per row take at most 3 vectors per lane.
+constexpr bool bwd_any_built(int wpr, int vpl) { return wpr < 16 || vpl <= 3; }
+const void* bwd_any_kernel(int dtype, bool dw, bool masked, int wpr_index, int vpl_index);
 // Backward vector kernel with rows narrower than a wave (kLprList lanes per
 // row, kSwVplList vectors per lane, one wave per row slot group).
 const void* bwd_subwave_kernel(int dtype, bool dw, bool masked, int lpr_index, int vpl_index);

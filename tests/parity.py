@@ -243,6 +243,8 @@ def bwd_chain(cfg, hidden: int, bf16: bool) -> int:
         per_lane = cfg.items_per_lane * v
     elif cfg.path == 2:    # element
         per_lane = cfg.items_per_lane
+    elif cfg.path == 4:    # any alignment: the lane's vectors plus one tail element
+        per_lane = cfg.items_per_lane * v + 1
     else:                  # two-pass: every lane strides over the row
         vec = hidden % v == 0
         units = hidden // v if vec else hidden

@@ -97,8 +97,13 @@ def test_choice_is_built_and_covering(dtype, aligned, rows):
             assert aligned and hidden % v == 0
             assert c.items_per_lane in range(1, 9) and (c.waves_per_row < 16 or c.items_per_lane <= 4)
             assert lanes * c.items_per_lane >= hidden // v
+        elif c.path == mbr.PATH_VECTOR_ANY:
+            assert (not aligned or hidden % v != 0) and hidden >= v and c.rows_per_block == 1
+            assert c.items_per_lane in range(1, 9) and (c.waves_per_row < 16 or c.items_per_lane <= 3)
+            assert lanes * c.items_per_lane >= hidden // v
         elif c.path == mbr.PATH_ELEMENT:
             assert c.items_per_lane in (1, 2, 4, 8) and lanes * c.items_per_lane >= hidden
+            assert hidden < v
         else:
             assert c.path == mbr.PATH_TWO_PASS and hidden > 8 * 1024
 
@@ -133,7 +138,10 @@ def test_bad_forced_configs():
                 # row slots: vector path only, within the thread limit
                 mbr.Config(mbr.PATH_VECTOR, 4, 2, 0, 0), mbr.Config(mbr.PATH_VECTOR, 4, 2, 3, 0),
                 mbr.Config(mbr.PATH_VECTOR, 2, 4, 8, 0), mbr.Config(mbr.PATH_ELEMENT, 4, 8, 2, 0),
-                mbr.Config(mbr.PATH_TWO_PASS, 16, 0, 2, 0)]:
+                mbr.Config(mbr.PATH_TWO_PASS, 16, 0, 2, 0),
+                # any alignment: one row per workgroup, whole waves, built and covering
+                mbr.Config(mbr.PATH_VECTOR_ANY, 1, 4, 2, 0), mbr.Config(mbr.PATH_VECTOR_ANY, 1, 4, 1, 0, 32),
+                mbr.Config(mbr.PATH_VECTOR_ANY, 1, 2, 1, 0), mbr.Config(mbr.PATH_VECTOR_ANY, 1, 9, 1, 0)]:
         n = mbr.rmsnorm_bwd_workspace_size(rows, hidden, torch.bfloat16, cfg) if cfg.max_blocks >= 0 else 0
         st = L.rmsnorm_bwd_ex(X, W, G, D, DW, rows, hidden, 1e-5, 1, WS, n, ctypes.byref(cfg), None)
         assert st == INV, cfg

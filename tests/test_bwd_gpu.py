@@ -9,6 +9,7 @@ last vector or lane, grid caps that make workgroups walk many rows, ragged
 widths, rows == 0, dx-only calls, in-place dx, misaligned buffers, workspace
 checks, determinism, non-finite rows and HIP-graph replays.
 """
+import ctypes
 import sys
 
 import numpy as np
@@ -311,7 +312,7 @@ def test_bwd_misaligned_pointers(dtype):
     xb, wb, gb = inputs.bits(t["x"]), inputs.bits(t["weight"]), inputs.bits(t["dy"])
     dx_want, dw_want = parity.oracle_bwd(xb, wb, gb, eps)
     cfg = effective_config(rows, hidden, dtype, aligned=False)
-    assert cfg.path == mbr.PATH_ELEMENT
+    assert cfg.path == mbr.PATH_VECTOR_ANY
     parity.compare_bwd(dx, dw, dx_want, dw_want, xb, wb, gb, eps, cfg, n_partials(rows, cfg))
     assert bufs["dx"][0].item() == 0 and torch.count_nonzero(bufs["dx"][1 + rows * hidden:]) == 0
     assert dwbuf[0].item() == 0 and torch.count_nonzero(dwbuf[1 + hidden:]) == 0
@@ -386,3 +387,80 @@ def test_bwd_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(dx_g, dx_e) and torch.equal(dw_g, dw_e), "replay %d differs" % rep
         run_bwd(t["x"], t["weight"], t["dy"], 1e-5)
+
+
+def _run_bwd_any(dtype, rows, hidden, cfg, off, woff, seed, want_dw=True):
+    """Forced configuration with x, dy and dx starting `off` elements and the
+    weight and dweight `woff` elements past a 16-byte boundary, inside guard
+    space: parity with the oracle, and no element outside dx and dweight
+    written."""
+    w = inputs.custom(rows, hidden, dtype, backward=True)
+    t = inputs.make(w, seed=seed)
+    td = tdt(dtype)
+    es = 2 if dtype == "bf16" else 4
+    n, g = rows * hidden, 64
+    bases = [g + off + i * (n + 2 * g) for i in range(3)]  # x, dy, dx
+    buf = torch.zeros(3 * (n + 2 * g) + 2 * g, dtype=td, device="cuda")
+    buf[bases[0]:bases[0] + n] = t["x"].reshape(-1).cuda()
+    buf[bases[1]:bases[1] + n] = t["dy"].reshape(-1).cuda()
+    wbuf = torch.zeros(2 * (hidden + 2 * g), dtype=td, device="cuda")  # weight, dweight
+    wb0, wb1 = g + woff, hidden + 3 * g + woff
+    wbuf[wb0:wb0 + hidden] = t["weight"].cuda()
+    nbytes = mbr.rmsnorm_bwd_workspace_size(rows, hidden, td, cfg)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    p, q = buf.data_ptr(), wbuf.data_ptr()
+    st = mbr.lib().rmsnorm_bwd_ex(p + es * bases[0], q + es * wb0, p + es * bases[1], p + es * bases[2],
+                                  q + es * wb1 if want_dw else None, rows, hidden, w.eps, mbr.dtype_code(td),
+                                  ws.data_ptr() if want_dw else None, nbytes if want_dw else 0,
+                                  ctypes.byref(cfg), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == mbr.RMSNORM_OK, mbr.rmsnorm_status_string(st)
+    cpu, wcpu = inputs.bits(buf.cpu()), inputs.bits(wbuf.cpu())
+    xb, wb, gb = inputs.bits(t["x"]), inputs.bits(t["weight"]), inputs.bits(t["dy"])
+    dx_want, dw_want = parity.oracle_bwd(xb, wb, gb, w.eps, want_dw)
+    dx = cpu[bases[2]:bases[2] + n].reshape(rows, hidden)
+    dw = wcpu[wb1:wb1 + hidden] if want_dw else None
+    say(parity.compare_bwd(dx, dw, dx_want, dw_want, xb, wb, gb, w.eps, cfg, n_partials(rows, cfg)))
+    written = np.zeros(cpu.shape, bool)
+    for i in range(3):
+        written[bases[i]:bases[i] + n] = True
+    assert not np.any(cpu[~written] != 0), "an element outside x, dy and dx changed"
+    wwritten = np.zeros(wcpu.shape, bool)
+    wwritten[wb0:wb0 + hidden] = True
+    if want_dw:
+        wwritten[wb1:wb1 + hidden] = True
+    assert not np.any(wcpu[~wwritten] != 0), "an element outside weight and dweight changed"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_every_any_alignment_config(dtype):
+    """Every built any-alignment backward configuration, forced: full and
+    masked vector sets, tails of 0, 1 and V - 1 elements, buffers at several
+    offsets from a 16-byte boundary, with and without dweight and a grid cap."""
+    v = 8 if dtype == "bf16" else 4
+    n = 0
+    for wpr in (1, 2, 4, 8, 16):
+        for vpl in range(1, 9):
+            if wpr == 16 and vpl > 3:
+                continue
+            lanes = 64 * wpr
+            for nvec in sorted({lanes * vpl, max(1, lanes * (vpl - 1) + 3)}):
+                tail = (0, 1, v - 1)[n % 3]
+                off = (1, v - 1, 0)[n % 3]
+                woff = (0, 1, v - 1, 2)[n % 4]
+                cfg = mbr.Config(mbr.PATH_VECTOR_ANY, wpr, vpl, 1, 2 if n % 4 == 3 else 0)
+                say("bwd any", dtype, cfg.as_dict(), "hidden", nvec * v + tail, "offsets", off, woff)
+                _run_bwd_any(dtype, 5, nvec * v + tail, cfg, off, woff, 6000 + n, want_dw=n % 5 != 4)
+                n += 1
+    assert n == 70
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,hidden", [(4096, 8191), (2048, 5121), (4096, 4097), (4096, 2049), (300, 1031)])
+def test_bwd_odd_widths_automatic(rows, hidden, dtype):
+    """Widths that are not whole vectors take the any-alignment path by themselves."""
+    td = tdt(dtype)
+    cfg = mbr.rmsnorm_select_bwd_config(rows, hidden, td, True)
+    assert cfg.path == mbr.PATH_VECTOR_ANY
+    say("bwd odd width", dtype, rows, hidden, cfg.as_dict())
+    _run_bwd_any(dtype, rows, hidden, cfg, 1, 1, hidden)
