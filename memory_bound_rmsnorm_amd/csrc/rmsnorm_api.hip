@@ -437,7 +437,14 @@ rmsnorm_config_t choose_bwd(int64_t rows, int64_t hidden, int dtype, bool aligne
     const int64_t units = vlike ? hidden / vec_elems(dtype) : hidden;
     const int* list = vlike ? mbr::kBwdVplList : mbr::kBwdEplList;
     const int nlist = vlike ? mbr::kNumBwdVpl : mbr::kNumBwdEpl;
-    const int cap = vlike ? 4 : 8;
+    // The any-alignment kernel takes one row per workgroup: below 12288 rows it
+    // runs fastest with at most two vectors per lane and more waves per row.
+    // Sweeps on MI355X (bf16, 512 workgroups): [4096, 4097] 4 x 2 27.5 us
+    // against 29.5 as 2 x 4, [4096, 2049] 2 x 2 19.4 against 22.6 as 1 x 4;
+    // from 12288 rows on the balanced rule below holds ([12289, 5121] 2 x 5
+    // 88.8 us, [16384, 8191] 4 x 4 179.6; the element kernel 114.2 and 179.0).
+    const bool any_short = any && rows < 12288;
+    const int cap = vlike ? (any_short ? 2 : 4) : 8;
     const bool few = rows < 1024;
     if (vec && !few && units <= 64) {
         int lpr = 0;
@@ -461,7 +468,7 @@ rmsnorm_config_t choose_bwd(int64_t rows, int64_t hidden, int dtype, bool aligne
         return built ? per : -1;
     };
     const bool whole_row = vec && !few && rows < 8192 && units <= 512;
-    const bool balanced = vlike && !few && !whole_row;
+    const bool balanced = vlike && !few && !whole_row && !any_short;
     int wpr = 1;
     if (balanced) {
         int64_t best_pad = -1;
