@@ -44,6 +44,12 @@ int main(void) {
     expect("quant_path", c.path, RMSNORM_PATH_VECTOR);
     expect("select_bwd", rmsnorm_select_bwd_config(16384, 8192, RMSNORM_DTYPE_BF16, 1, &c), RMSNORM_OK);
     expect("bwd_max_blocks", c.max_blocks, 512);
+    /* odd widths: full vectors at the row's own alignment plus a tail */
+    expect("select_quant_odd", rmsnorm_select_quant_config(16384, 8191, RMSNORM_DTYPE_BF16, 1, 0, &c), RMSNORM_OK);
+    expect("quant_odd_path", c.path, RMSNORM_PATH_VECTOR_ANY);
+    expect("select_bwd_odd", rmsnorm_select_bwd_config(16384, 8191, RMSNORM_DTYPE_BF16, 1, &c), RMSNORM_OK);
+    expect("bwd_odd_path", c.path, RMSNORM_PATH_VECTOR_ANY);
+    expect("bwd_odd_rows_per_block", c.rows_per_block, 1);
     expect("select_ln", layernorm_select_config(8192, 4096, RMSNORM_DTYPE_BF16, 1, &c), RMSNORM_OK);
     expect("ln_weight_lds", c.weight_lds, 1);
     expect("select_kv", kv_select_config(16384, 1, 512, 64, 1, RMSNORM_DTYPE_BF16, 1, &c), RMSNORM_OK);
