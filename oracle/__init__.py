@@ -20,6 +20,13 @@ the forward, closed forms, invariants) and ``tests/test_oracle_ln_pins.py``
 The only unpinned choice is which bf16 neighbour is returned when the exact
 result lies within the fp64 evaluation error (about 1e-12 relative) of a
 rounding midpoint.
+
+``unrounded=True`` on the normalising functions returns the float64 value each
+output has before its one rounding (the same arithmetic, stopped short of the
+store).  Comparisons use it to check that a result is a correct rounding of a
+value within the evaluation error of the exact one, which tells nearest-even
+apart from truncation or double rounding; ``round_bf16_array`` and
+``round_f32_array`` apply the oracle's roundings to such arrays.
 """
 import ctypes
 import os
@@ -30,6 +37,7 @@ from . import build as _build
 
 F32 = 0
 BF16 = 1
+F64 = 2  # output only: unrounded
 
 _lib = None
 
@@ -41,9 +49,9 @@ def _load():
             _build.build()
         lib = ctypes.CDLL(_build.LIB)
         vp, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
-        lib.oracle_rmsnorm_fwd.argtypes = [vp, vp, vp, i64, i64, f32, i32]
+        lib.oracle_rmsnorm_fwd.argtypes = [vp, vp, vp, i64, i64, f32, i32, i32]
         lib.oracle_rmsnorm_fwd.restype = i32
-        lib.oracle_rmsnorm_residual_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, i32]
+        lib.oracle_rmsnorm_residual_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, i32, i32]
         lib.oracle_rmsnorm_residual_fwd.restype = i32
         lib.oracle_round_bf16.argtypes = [ctypes.c_double]
         lib.oracle_round_bf16.restype = ctypes.c_uint16
@@ -51,14 +59,18 @@ def _load():
         lib.oracle_round_f32.restype = ctypes.c_float
         lib.oracle_round_e4m3.argtypes = [ctypes.c_double]
         lib.oracle_round_e4m3.restype = ctypes.c_uint8
+        lib.oracle_round_bf16_n.argtypes = [vp, vp, i64]
+        lib.oracle_round_bf16_n.restype = None
+        lib.oracle_round_f32_n.argtypes = [vp, vp, i64]
+        lib.oracle_round_f32_n.restype = None
         lib.oracle_rmsnorm_dynamic_quant_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, i32]
         lib.oracle_rmsnorm_dynamic_quant_fwd.restype = i32
-        lib.oracle_rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, i32]
+        lib.oracle_rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, i32, i32]
         lib.oracle_rmsnorm_bwd.restype = i32
-        lib.oracle_layernorm_fwd.argtypes = [vp, vp, vp, vp, i64, i64, f32, i32]
+        lib.oracle_layernorm_fwd.argtypes = [vp, vp, vp, vp, i64, i64, f32, i32, i32]
         lib.oracle_layernorm_fwd.restype = i32
         lib.oracle_kv_rmsnorm_rope_cache.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
-                                                     f32, i32, i32]
+                                                     f32, i32, i32, i32]
         lib.oracle_kv_rmsnorm_rope_cache.restype = i32
         _lib = lib
     return _lib
@@ -78,23 +90,30 @@ def _check(a: np.ndarray, name: str) -> np.ndarray:
     return np.ascontiguousarray(a)
 
 
-def rmsnorm_fwd(x: np.ndarray, weight: np.ndarray, eps: float) -> np.ndarray:
-    """RMSNorm of every row of ``x`` (float32 or bf16-bits), same dtype out."""
+def _out(like: np.ndarray, unrounded: bool) -> np.ndarray:
+    return np.empty(like.shape, np.float64) if unrounded else np.empty_like(like)
+
+
+def rmsnorm_fwd(x: np.ndarray, weight: np.ndarray, eps: float, unrounded: bool = False) -> np.ndarray:
+    """RMSNorm of every row of ``x`` (float32 or bf16-bits), same dtype out
+    (float64 before the rounding with ``unrounded``)."""
     x = _check(x, "x")
     weight = np.ascontiguousarray(weight).reshape(-1)
     code = _dtype_code(x)
     if weight.dtype != x.dtype or weight.shape[0] != x.shape[1]:
         raise ValueError("weight must be [hidden] with the dtype of x")
-    out = np.empty_like(x)
+    out = _out(x, unrounded)
     rc = _load().oracle_rmsnorm_fwd(x.ctypes.data, weight.ctypes.data, out.ctypes.data,
-                                    x.shape[0], x.shape[1], float(eps), code)
+                                    x.shape[0], x.shape[1], float(eps), code, F64 if unrounded else code)
     if rc != 0:
         raise RuntimeError("oracle_rmsnorm_fwd failed")
     return out
 
 
-def rmsnorm_residual_fwd(x: np.ndarray, residual: np.ndarray, weight: np.ndarray, eps: float):
-    """Returns ``(h, y)``: h = round(x + residual), y = RMSNorm(h)."""
+def rmsnorm_residual_fwd(x: np.ndarray, residual: np.ndarray, weight: np.ndarray, eps: float,
+                         unrounded: bool = False):
+    """Returns ``(h, y)``: h = round(x + residual), y = RMSNorm(h) (y in
+    float64 before its rounding with ``unrounded``; h is always rounded)."""
     x = _check(x, "x")
     residual = _check(residual, "residual")
     weight = np.ascontiguousarray(weight).reshape(-1)
@@ -104,10 +123,10 @@ def rmsnorm_residual_fwd(x: np.ndarray, residual: np.ndarray, weight: np.ndarray
     if weight.dtype != x.dtype or weight.shape[0] != x.shape[1]:
         raise ValueError("weight must be [hidden] with the dtype of x")
     h = np.empty_like(x)
-    y = np.empty_like(x)
+    y = _out(x, unrounded)
     rc = _load().oracle_rmsnorm_residual_fwd(x.ctypes.data, residual.ctypes.data,
                                              weight.ctypes.data, h.ctypes.data, y.ctypes.data,
-                                             x.shape[0], x.shape[1], float(eps), code)
+                                             x.shape[0], x.shape[1], float(eps), code, F64 if unrounded else code)
     if rc != 0:
         raise RuntimeError("oracle_rmsnorm_residual_fwd failed")
     return h, y
@@ -145,9 +164,10 @@ def rmsnorm_dynamic_quant_fwd(x: np.ndarray, weight: np.ndarray, eps: float, qty
 
 
 def rmsnorm_bwd(x: np.ndarray, weight: np.ndarray, dy: np.ndarray, eps: float, want_dw: bool = True,
-                want_dx: bool = True):
+                want_dx: bool = True, unrounded: bool = False):
     """Returns ``(dx, dw)`` of y = RMSNorm(x) * weight for upstream gradient dy
-    (either is None when not wanted)."""
+    (either is None when not wanted; float64 before the rounding with
+    ``unrounded``)."""
     x = _check(x, "x")
     dy = _check(dy, "dy")
     weight = np.ascontiguousarray(weight).reshape(-1)
@@ -156,20 +176,21 @@ def rmsnorm_bwd(x: np.ndarray, weight: np.ndarray, dy: np.ndarray, eps: float, w
         raise ValueError("dy must match x")
     if weight.dtype != x.dtype or weight.shape[0] != x.shape[1]:
         raise ValueError("weight must be [hidden] with the dtype of x")
-    dx = np.empty_like(x) if want_dx else None
-    dw = np.empty_like(weight) if want_dw else None
+    dx = _out(x, unrounded) if want_dx else None
+    dw = _out(weight, unrounded) if want_dw else None
     rc = _load().oracle_rmsnorm_bwd(x.ctypes.data, weight.ctypes.data, dy.ctypes.data,
                                     dx.ctypes.data if dx is not None else None,
                                     dw.ctypes.data if dw is not None else None, x.shape[0], x.shape[1],
-                                    float(eps), code)
+                                    float(eps), code, F64 if unrounded else code)
     if rc != 0:
         raise RuntimeError("oracle_rmsnorm_bwd failed")
     return dx, dw
 
 
-def layernorm_fwd(x: np.ndarray, gamma: np.ndarray, beta, eps: float) -> np.ndarray:
+def layernorm_fwd(x: np.ndarray, gamma: np.ndarray, beta, eps: float, unrounded: bool = False) -> np.ndarray:
     """LayerNorm of every row of ``x``: gamma * (x - mean) / sqrt(var + eps) + beta
-    (beta None: no bias), same dtype out."""
+    (beta None: no bias), same dtype out (float64 before the rounding with
+    ``unrounded``)."""
     x = _check(x, "x")
     gamma = np.ascontiguousarray(gamma).reshape(-1)
     code = _dtype_code(x)
@@ -179,10 +200,10 @@ def layernorm_fwd(x: np.ndarray, gamma: np.ndarray, beta, eps: float) -> np.ndar
         beta = np.ascontiguousarray(beta).reshape(-1)
         if beta.dtype != x.dtype or beta.shape[0] != x.shape[1]:
             raise ValueError("beta must be [hidden] with the dtype of x")
-    out = np.empty_like(x)
+    out = _out(x, unrounded)
     rc = _load().oracle_layernorm_fwd(x.ctypes.data, gamma.ctypes.data,
                                       beta.ctypes.data if beta is not None else None, out.ctypes.data,
-                                      x.shape[0], x.shape[1], float(eps), code)
+                                      x.shape[0], x.shape[1], float(eps), code, F64 if unrounded else code)
     if rc != 0:
         raise RuntimeError("oracle_layernorm_fwd failed")
     return out
@@ -197,7 +218,8 @@ def kv_rmsnorm_rope_cache(kv: np.ndarray, gamma: np.ndarray, cos_t: np.ndarray, 
                           eps: float, rope_style: int) -> None:
     """Writes RMSNorm(kv[..., :Dn]) * gamma into norm_cache[slot] and the RoPE of
     kv[..., Dn:] into rope_cache[slot], in place.  kv [tokens, heads, Dn + Dr];
-    caches [num_slots, heads, Dn] and [num_slots, heads, Dr] (same dtype as kv);
+    caches [num_slots, heads, Dn] and [num_slots, heads, Dr] (same dtype as kv,
+    or both float64 for the values before their rounding);
     cos_t / sin_t float32 [max_pos, Dr / 2]; positions int32 [tokens]; slots
     int64 [tokens]."""
     if kv.ndim != 3 or norm_cache.ndim != 3 or rope_cache.ndim != 3:
@@ -209,9 +231,10 @@ def kv_rmsnorm_rope_cache(kv: np.ndarray, gamma: np.ndarray, cos_t: np.ndarray, 
         raise ValueError("cache shapes do not match kv")
     if norm_cache.shape[0] != rope_cache.shape[0]:
         raise ValueError("the two caches must have the same number of slots")
-    for a in (kv, norm_cache, rope_cache):
-        if a.dtype != kv.dtype or not a.flags.c_contiguous:
-            raise ValueError("kv and the caches must be contiguous with one dtype")
+    unrounded = norm_cache.dtype == np.float64
+    for a in (norm_cache, rope_cache):
+        if a.dtype != (np.float64 if unrounded else kv.dtype) or not a.flags.c_contiguous:
+            raise ValueError("the caches must be contiguous, both with the dtype of kv or both float64")
     gamma = np.ascontiguousarray(gamma).reshape(-1)
     if gamma.dtype != kv.dtype or gamma.shape[0] != norm_dim:
         raise ValueError("gamma must be [norm_dim] with the dtype of kv")
@@ -227,7 +250,7 @@ def kv_rmsnorm_rope_cache(kv: np.ndarray, gamma: np.ndarray, cos_t: np.ndarray, 
     rc = _load().oracle_kv_rmsnorm_rope_cache(
         kv.ctypes.data, gamma.ctypes.data, cos_t.ctypes.data, sin_t.ctypes.data, positions.ctypes.data,
         slots.ctypes.data, norm_cache.ctypes.data, rope_cache.ctypes.data, tokens, heads, norm_dim, rope_dim,
-        cos_t.shape[0], norm_cache.shape[0], float(eps), int(rope_style), code)
+        cos_t.shape[0], norm_cache.shape[0], float(eps), int(rope_style), code, F64 if unrounded else code)
     if rc != 0:
         raise RuntimeError("oracle_kv_rmsnorm_rope_cache failed")
 
@@ -244,3 +267,19 @@ def round_bf16(v: float) -> int:
 
 def round_f32(v: float) -> float:
     return float(_load().oracle_round_f32(float(v)))
+
+
+def round_bf16_array(v: np.ndarray) -> np.ndarray:
+    """Nearest-even bf16 bit patterns of a float64 array, one rounding each."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(v.shape, np.uint16)
+    _load().oracle_round_bf16_n(v.ctypes.data, out.ctypes.data, v.size)
+    return out
+
+
+def round_f32_array(v: np.ndarray) -> np.ndarray:
+    """Nearest-even float32 values of a float64 array."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(v.shape, np.float32)
+    _load().oracle_round_f32_n(v.ctypes.data, out.ctypes.data, v.size)
+    return out

@@ -42,7 +42,12 @@
  *   - NaN/Inf inputs propagate as IEEE arithmetic dictates.
  *
  * dtype codes (private to this file): 0 = float32, 1 = bfloat16 (stored as the
- * upper 16 bits of the float32 pattern).
+ * upper 16 bits of the float32 pattern).  The normalised outputs can also be
+ * written unrounded (out_dtype 2 = float64): the exact-up-to-fp64 value before
+ * the one rounding, which is what a comparison needs to tell a correctly
+ * rounded result from a truncated or doubly rounded one.  Every other output
+ * (the fused residual sum h, which the norm itself consumes rounded, and the
+ * quantised codes) is always rounded.
  */
 #include <math.h>
 #include <stdint.h>
@@ -51,6 +56,7 @@
 
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
+#define ORACLE_F64 2 /* output only: the value before rounding */
 #define ORACLE_QUANT_INT8 0
 #define ORACLE_QUANT_FP8_E4M3 1
 
@@ -137,8 +143,27 @@ uint8_t oracle_round_e4m3(double v) {
  * floating-point environment). */
 float oracle_round_f32(double v) { return (float)v; }
 
+/* The two roundings above over arrays (for comparisons against unrounded
+ * values). */
+void oracle_round_bf16_n(const double *v, uint16_t *out, int64_t n) {
+    int64_t i;
+    for (i = 0; i < n; ++i) out[i] = oracle_round_bf16(v[i]);
+}
+
+void oracle_round_f32_n(const double *v, float *out, int64_t n) {
+    int64_t i;
+    for (i = 0; i < n; ++i) out[i] = oracle_round_f32(v[i]);
+}
+
+/* An output type is the input type or, for the normalised outputs, float64. */
+static int bad_types(int dtype, int out_dtype) {
+    return (dtype != ORACLE_F32 && dtype != ORACLE_BF16) || (out_dtype != dtype && out_dtype != ORACLE_F64);
+}
+
 static void store_elem(void *base, int64_t i, double v, int dtype) {
-    if (dtype == ORACLE_F32) {
+    if (dtype == ORACLE_F64) {
+        memcpy((char *)base + 8 * i, &v, 8);
+    } else if (dtype == ORACLE_F32) {
         float f = oracle_round_f32(v);
         memcpy((char *)base + 4 * i, &f, 4);
     } else {
@@ -149,30 +174,31 @@ static void store_elem(void *base, int64_t i, double v, int dtype) {
 
 /* Normalise one row already widened to double: v[0..hidden) -> out row. */
 static void normalise_row(const double *v, const void *w, void *out, int64_t out_off,
-                          int64_t hidden, float eps, int dtype) {
+                          int64_t hidden, float eps, int dtype, int out_dtype) {
     double s = 0.0, mean, r;
     int64_t j;
     for (j = 0; j < hidden; ++j) s += v[j] * v[j];
     mean = s / (double)hidden;
     r = 1.0 / sqrt(mean + (double)eps);
     for (j = 0; j < hidden; ++j)
-        store_elem(out, out_off + j, v[j] * r * load_elem(w, j, dtype), dtype);
+        store_elem(out, out_off + j, v[j] * r * load_elem(w, j, dtype), out_dtype);
 }
 
 /*
- * out[i, :] = RMSNorm(x[i, :]) for i < rows; row-major, contiguous.
+ * out[i, :] = RMSNorm(x[i, :]) for i < rows; row-major, contiguous.  out has
+ * the dtype of x, or float64 (unrounded) when out_dtype is ORACLE_F64.
  * Returns 0 on success, -1 on a bad argument or allocation failure.
  */
 int oracle_rmsnorm_fwd(const void *x, const void *w, void *out, int64_t rows, int64_t hidden,
-                       float eps, int dtype) {
+                       float eps, int dtype, int out_dtype) {
     double *v;
     int64_t i, j;
-    if (rows < 0 || hidden <= 0 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16)) return -1;
+    if (rows < 0 || hidden <= 0 || bad_types(dtype, out_dtype)) return -1;
     v = (double *)malloc(sizeof(double) * (size_t)hidden);
     if (!v) return -1;
     for (i = 0; i < rows; ++i) {
         for (j = 0; j < hidden; ++j) v[j] = load_elem(x, i * hidden + j, dtype);
-        normalise_row(v, w, out, i * hidden, hidden, eps, dtype);
+        normalise_row(v, w, out, i * hidden, hidden, eps, dtype, out_dtype);
     }
     free(v);
     return 0;
@@ -181,13 +207,13 @@ int oracle_rmsnorm_fwd(const void *x, const void *w, void *out, int64_t rows, in
 /*
  * h[i, :] = round(x[i, :] + residual[i, :]) and out[i, :] = RMSNorm(h[i, :]).
  * The sum is formed in fp64, rounded once to the dtype and written to h_out;
- * the rounded value is what the norm sees.
+ * the rounded value is what the norm sees.  out_dtype applies to out only.
  */
 int oracle_rmsnorm_residual_fwd(const void *x, const void *residual, const void *w, void *h_out,
-                                void *out, int64_t rows, int64_t hidden, float eps, int dtype) {
+                                void *out, int64_t rows, int64_t hidden, float eps, int dtype, int out_dtype) {
     double *v;
     int64_t i, j;
-    if (rows < 0 || hidden <= 0 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16)) return -1;
+    if (rows < 0 || hidden <= 0 || bad_types(dtype, out_dtype)) return -1;
     v = (double *)malloc(sizeof(double) * (size_t)hidden);
     if (!v) return -1;
     for (i = 0; i < rows; ++i) {
@@ -197,7 +223,7 @@ int oracle_rmsnorm_residual_fwd(const void *x, const void *residual, const void 
             store_elem(h_out, k, sum, dtype);
             v[j] = load_elem(h_out, k, dtype);
         }
-        normalise_row(v, w, out, i * hidden, hidden, eps, dtype);
+        normalise_row(v, w, out, i * hidden, hidden, eps, dtype, out_dtype);
     }
     free(v);
     return 0;
@@ -282,14 +308,15 @@ int oracle_rmsnorm_dynamic_quant_fwd(const void *x, const void *residual, const 
  *   dx_k    = r dy_k w_k - x_k r^3 c / H
  *   dw_j    = sum_i dy_ij x_ij r_i        (over all rows, fp64)
  *
- * dx and dw are each rounded once to the dtype.  Either may be NULL (not
- * wanted); the other is unaffected.
+ * dx and dw are each rounded once to the dtype (or written unrounded when
+ * out_dtype is ORACLE_F64).  Either may be NULL (not wanted); the other is
+ * unaffected.
  */
 int oracle_rmsnorm_bwd(const void *x, const void *w, const void *dy, void *dx, void *dw, int64_t rows,
-                       int64_t hidden, float eps, int dtype) {
+                       int64_t hidden, float eps, int dtype, int out_dtype) {
     double *acc = NULL;
     int64_t i, j;
-    if (rows < 0 || hidden <= 0 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16)) return -1;
+    if (rows < 0 || hidden <= 0 || bad_types(dtype, out_dtype)) return -1;
     if (dw) {
         acc = (double *)calloc((size_t)hidden, sizeof(double));
         if (!acc) return -1;
@@ -307,12 +334,12 @@ int oracle_rmsnorm_bwd(const void *x, const void *w, const void *dy, void *dx, v
             double g = load_elem(dy, i * hidden + j, dtype);
             if (dx)
                 store_elem(dx, i * hidden + j, r * g * load_elem(w, j, dtype) - v * r * r * r * c / (double)hidden,
-                           dtype);
+                           out_dtype);
             if (acc) acc[j] += g * v * r;
         }
     }
     if (acc) {
-        for (j = 0; j < hidden; ++j) store_elem(dw, j, acc[j], dtype);
+        for (j = 0; j < hidden; ++j) store_elem(dw, j, acc[j], out_dtype);
         free(acc);
     }
     return 0;
@@ -328,13 +355,13 @@ int oracle_rmsnorm_bwd(const void *x, const void *w, const void *dy, void *dx, v
  * header comment and docs/04-transformer-kernels.md "LayerNorm"; the CPU
  * reference cpu_layernorm in crates/xserv-kernels/tests/ops_test.rs divides the
  * centred sum of squares by hidden).  Plain two-pass definition in fp64: the
- * mean first, then the centred squares, then one rounding per output.
- * beta may be NULL (no bias).
+ * mean first, then the centred squares, then one rounding per output (none
+ * when out_dtype is ORACLE_F64).  beta may be NULL (no bias).
  */
 int oracle_layernorm_fwd(const void *x, const void *gamma, const void *beta, void *out, int64_t rows,
-                         int64_t hidden, float eps, int dtype) {
+                         int64_t hidden, float eps, int dtype, int out_dtype) {
     int64_t i, j;
-    if (rows < 0 || hidden <= 0 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16)) return -1;
+    if (rows < 0 || hidden <= 0 || bad_types(dtype, out_dtype)) return -1;
     for (i = 0; i < rows; ++i) {
         double s = 0.0, q = 0.0, mu, inv;
         for (j = 0; j < hidden; ++j) s += load_elem(x, i * hidden + j, dtype);
@@ -347,7 +374,7 @@ int oracle_layernorm_fwd(const void *x, const void *gamma, const void *beta, voi
         for (j = 0; j < hidden; ++j) {
             double v = load_elem(gamma, j, dtype) * (load_elem(x, i * hidden + j, dtype) - mu) * inv;
             if (beta) v += load_elem(beta, j, dtype);
-            store_elem(out, i * hidden + j, v, dtype);
+            store_elem(out, i * hidden + j, v, out_dtype);
         }
     }
     return 0;
@@ -370,16 +397,17 @@ int oracle_layernorm_fwd(const void *x, const void *gamma, const void *beta, voi
  *   scatter: token t writes both results at cache row slots[t] (caches
  *   [num_slots, heads, norm_dim] and [num_slots, heads, rope_dim]); a token
  *   whose slot or position is out of range (negative included) writes nothing.
- * fp64 arithmetic, one rounding per output element.
+ * fp64 arithmetic, one rounding per output element (none when out_dtype is
+ * ORACLE_F64: both caches are then float64).
  */
 int oracle_kv_rmsnorm_rope_cache(const void *kv, const void *gamma, const float *cos_t, const float *sin_t,
                                  const int32_t *positions, const int64_t *slots, void *norm_cache,
                                  void *rope_cache, int64_t tokens, int64_t heads, int64_t norm_dim,
                                  int64_t rope_dim, int64_t max_pos, int64_t num_slots, float eps, int rope_style,
-                                 int dtype) {
+                                 int dtype, int out_dtype) {
     int64_t t, h, j, d = norm_dim + rope_dim, half = rope_dim / 2;
     if (tokens < 0 || heads <= 0 || norm_dim <= 0 || rope_dim < 0 || rope_dim % 2 != 0 || max_pos < 0 ||
-        num_slots < 0 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16) || (rope_style != 0 && rope_style != 1))
+        num_slots < 0 || bad_types(dtype, out_dtype) || (rope_style != 0 && rope_style != 1))
         return -1;
     for (t = 0; t < tokens; ++t) {
         const int64_t slot = slots[t];
@@ -395,15 +423,15 @@ int oracle_kv_rmsnorm_rope_cache(const void *kv, const void *gamma, const float 
             r = 1.0 / sqrt(s / (double)norm_dim + (double)eps);
             for (j = 0; j < norm_dim; ++j)
                 store_elem(norm_cache, (slot * heads + h) * norm_dim + j,
-                           load_elem(kv, in + j, dtype) * r * load_elem(gamma, j, dtype), dtype);
+                           load_elem(kv, in + j, dtype) * r * load_elem(gamma, j, dtype), out_dtype);
             for (j = 0; j < half; ++j) {
                 const int64_t ia = rope_style ? 2 * j : j, ib = rope_style ? 2 * j + 1 : j + half;
                 const double a = load_elem(kv, in + norm_dim + ia, dtype);
                 const double b = load_elem(kv, in + norm_dim + ib, dtype);
                 const double c = (double)cos_t[pos * half + j], sn = (double)sin_t[pos * half + j];
                 const int64_t out = (slot * heads + h) * rope_dim;
-                store_elem(rope_cache, out + ia, a * c - b * sn, dtype);
-                store_elem(rope_cache, out + ib, a * sn + b * c, dtype);
+                store_elem(rope_cache, out + ia, a * c - b * sn, out_dtype);
+                store_elem(rope_cache, out + ib, a * sn + b * c, out_dtype);
             }
         }
     }

@@ -18,6 +18,7 @@ from tests import test_oracle_quant_pins as qpins
 from tests import test_oracle_bwd_pins as bpins
 from tests import test_oracle_ln_pins as lpins
 from tests import test_oracle_kv_pins as kpins
+from tests import test_oracle_unrounded_pins as upins
 
 MUTANTS = [
     ("eps dropped", "sqrt(mean + (double)eps)", "sqrt(mean)"),
@@ -37,10 +38,10 @@ MUTANTS = [
      "load_elem(x, k, dtype) - load_elem(residual, k, dtype)"),
     ("unrounded residual sum normalised", "v[j] = load_elem(h_out, k, dtype);", "v[j] = sum;"),
     ("rounded before the weight multiply",
-     "store_elem(out, out_off + j, v[j] * r * load_elem(w, j, dtype), dtype);",
+     "store_elem(out, out_off + j, v[j] * r * load_elem(w, j, dtype), out_dtype);",
      "store_elem(out, out_off + j, (dtype == ORACLE_BF16 ? "
      "(double)oracle_bf16_back(oracle_round_bf16(v[j] * r)) : (double)(float)(v[j] * r)) "
-     "* load_elem(w, j, dtype), dtype);"),
+     "* load_elem(w, j, dtype), out_dtype);"),
 ]
 
 MUTANTS += [
@@ -96,8 +97,8 @@ MUTANTS += [
 ]
 
 MUTANTS += [
-    ("kv rotation sign", "store_elem(rope_cache, out + ia, a * c - b * sn, dtype);",
-     "store_elem(rope_cache, out + ia, a * c + b * sn, dtype);"),
+    ("kv rotation sign", "store_elem(rope_cache, out + ia, a * c - b * sn, out_dtype);",
+     "store_elem(rope_cache, out + ia, a * c + b * sn, out_dtype);"),
     ("kv cos and sin swapped", "const double c = (double)cos_t[pos * half + j], sn = (double)sin_t[pos * half + j];",
      "const double c = (double)sin_t[pos * half + j], sn = (double)cos_t[pos * half + j];"),
     ("kv halves paired as adjacent elements",
@@ -109,9 +110,26 @@ MUTANTS += [
     ("kv slot ignored", "store_elem(norm_cache, (slot * heads + h) * norm_dim + j,",
      "store_elem(norm_cache, (t * heads + h) * norm_dim + j,"),
     ("kv eps dropped", "r = 1.0 / sqrt(s / (double)norm_dim + (double)eps);", "r = 1.0 / sqrt(s / (double)norm_dim);"),
-    ("kv gamma dropped", "load_elem(kv, in + j, dtype) * r * load_elem(gamma, j, dtype), dtype);",
-     "load_elem(kv, in + j, dtype) * r, dtype);"),
+    ("kv gamma dropped", "load_elem(kv, in + j, dtype) * r * load_elem(gamma, j, dtype), out_dtype);",
+     "load_elem(kv, in + j, dtype) * r, out_dtype);"),
     ("kv every head read from head 0", "const int64_t in = (t * heads + h) * d;", "const int64_t in = t * heads * d;"),
+]
+
+MUTANTS += [
+    ("unrounded output passed through float32", "memcpy((char *)base + 8 * i, &v, 8);",
+     "v = (double)(float)v;\n        memcpy((char *)base + 8 * i, &v, 8);"),
+    ("array bf16 rounding via float32", "for (i = 0; i < n; ++i) out[i] = oracle_round_bf16(v[i]);",
+     "for (i = 0; i < n; ++i) out[i] = oracle_round_bf16((double)(float)v[i]);"),
+    ("unrounded output without the weight", "store_elem(out, out_off + j, v[j] * r * load_elem(w, j, dtype), out_dtype);",
+     "store_elem(out, out_off + j, out_dtype == ORACLE_F64 ? v[j] * r : v[j] * r * load_elem(w, j, dtype), out_dtype);"),
+    ("unrounded dx without the radial term",
+     "r * g * load_elem(w, j, dtype) - v * r * r * r * c / (double)hidden,\n                           out_dtype);",
+     "r * g * load_elem(w, j, dtype) - (out_dtype == ORACLE_F64 ? 0.0 : v * r * r * r * c / (double)hidden),\n"
+     "                           out_dtype);"),
+    ("unrounded layernorm without beta", "if (beta) v += load_elem(beta, j, dtype);",
+     "if (beta && out_dtype != ORACLE_F64) v += load_elem(beta, j, dtype);"),
+    ("unrounded rope sign", "store_elem(rope_cache, out + ib, a * sn + b * c, out_dtype);",
+     "store_elem(rope_cache, out + ib, out_dtype == ORACLE_F64 ? b * c - a * sn : a * sn + b * c, out_dtype);"),
 ]
 
 HELPER = """
@@ -169,6 +187,13 @@ PIN_TESTS = [
     (kpins.test_quarter_turn_moves_exactly_one_pair, dict(style=1)),
     (kpins.test_rotation_preserves_pair_lengths, {}),
     (kpins.test_scatter_rows_and_skips, dict(dtype="bf16")),
+    (upins.test_round_arrays_match_exact_rational_rounding, {}),
+    (upins.test_unrounded_hand_example, dict(dtype="f32")),
+    (upins.test_unrounded_brute_force_tiny_rows, dict(dtype="bf16")),
+    (upins.test_rounding_the_unrounded_output_gives_the_rounded_output, dict(dtype="bf16")),
+    (upins.test_unrounded_backward_matches_decimal_central_differences, {}),
+    (upins.test_unrounded_layernorm_two_columns, {}),
+    (upins.test_unrounded_kv_parts, dict(style=oracle.ROPE_PAIRS)),
 ]
 
 

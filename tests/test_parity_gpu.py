@@ -1,7 +1,9 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle, on the GPU.
 
 Every test compares element by element on seeded inputs: bf16 within 1 ulp,
-fp32 within 1e-5 relative, the fused residual sum h bitwise (tests/parity.py).
+fp32 within 1e-5 relative, the fused residual sum h bitwise, and every output a
+nearest-even rounding of a value within the launch configuration's fp32
+evaluation bound of the oracle's unrounded result (tests/parity.py).
 Covered: the five stated workloads at full size in the automatically chosen
 launch configuration (the one bench.py times), every built kernel
 configuration on shapes that span several workgroups and a partial last one,
@@ -49,18 +51,36 @@ def run_fused(x, r, w, eps, cfg=None, h=None, out=None):
     return h, out
 
 
+def auto(rows, hidden, td, aligned=True, fused=False):
+    return mbr.rmsnorm_select_config(rows, hidden, td, aligned, fused)
+
+
+def expect(xb, wb, eps, cfg, res=None):
+    """(h, y, y unrounded, gamma): the oracle's residual sum (None without a
+    residual), its rounded and unrounded output, and the relative fp32
+    evaluation bound of the launch configuration cfg."""
+    gamma = parity.fwd_gamma(cfg, xb.shape[1], xb.dtype == np.uint16)
+    if res is None:
+        want, e = parity.oracle_fwd(xb, wb, eps, unrounded=True)
+        return None, want, e, gamma
+    h, want, e = parity.oracle_residual(xb, res, wb, eps, unrounded=True)
+    return h, want, e, gamma
+
+
 def check_workload(w, t, cfg=None, eps=None):
     """Run workload tensors t (CPU) on the GPU and compare with the oracle."""
     eps = w.eps if eps is None else eps
+    eff = cfg if cfg is not None else auto(w.rows, w.hidden, tdtype(w), True, w.fused)
     dev = {k: v.cuda() for k, v in t.items()}
     xb, wb = inputs.bits(t["x"]), inputs.bits(t["weight"])
     if w.fused:
         h, y = run_fused(dev["x"], dev["residual"], dev["weight"], eps, cfg)
-        h_want, y_want = parity.oracle_residual(xb, inputs.bits(t["residual"]), wb, eps)
+        h_want, y_want, e, gamma = expect(xb, wb, eps, eff, inputs.bits(t["residual"]))
         assert np.array_equal(inputs.bits(h), h_want), "residual sum differs"
-        return parity.compare(inputs.bits(y), y_want)
+        return parity.compare(inputs.bits(y), y_want, e, gamma)
     y = run_plain(dev["x"], dev["weight"], eps, cfg)
-    return parity.compare(inputs.bits(y), parity.oracle_fwd(xb, wb, eps))
+    _, y_want, e, gamma = expect(xb, wb, eps, eff)
+    return parity.compare(inputs.bits(y), y_want, e, gamma)
 
 
 # ---------------------------------------------------------------- stated workloads
@@ -274,7 +294,8 @@ def test_misaligned_pointers(dtype, which):
                     obuf.data_ptr() + es * off["out"], rows, hidden, eps, mbr.dtype_code(td))
     assert st == mbr.RMSNORM_OK
     got = inputs.bits(obuf[off["out"]:off["out"] + rows * hidden].reshape(rows, hidden).cpu())
-    parity.compare(got, parity.oracle_fwd(inputs.bits(t["x"]), inputs.bits(t["weight"]), eps))
+    _, want, e, gamma = expect(inputs.bits(t["x"]), inputs.bits(t["weight"]), eps, auto(rows, hidden, td, False))
+    parity.compare(got, want, e, gamma)
     # nothing outside the output was written
     assert torch.count_nonzero(obuf[:off["out"]]) == 0
     assert torch.count_nonzero(obuf[off["out"] + rows * hidden:]) == 0
@@ -310,12 +331,10 @@ def _run_any(dtype, rows, hidden, fused, cfg, off, seed):
     assert st == mbr.RMSNORM_OK, mbr.rmsnorm_status_string(st)
     cpu = inputs.bits(buf.cpu())
     xb, wb = inputs.bits(t["x"]), inputs.bits(t["weight"])
+    h_want, y_want, e, gamma = expect(xb, wb, w.eps, cfg, inputs.bits(t["residual"]) if fused else None)
     if fused:
-        h_want, y_want = parity.oracle_residual(xb, inputs.bits(t["residual"]), wb, w.eps)
         assert np.array_equal(cpu[bases[2]:bases[2] + n].reshape(rows, hidden), h_want), "residual sum differs"
-    else:
-        y_want = parity.oracle_fwd(xb, wb, w.eps)
-    parity.compare(cpu[bases[3]:bases[3] + n].reshape(rows, hidden), y_want)
+    parity.compare(cpu[bases[3]:bases[3] + n].reshape(rows, hidden), y_want, e, gamma)
     written = np.zeros(cpu.shape, bool)
     for i in (0, 1, 2, 3) if fused else (0, 3):
         written[bases[i]:bases[i] + n] = True
@@ -360,29 +379,29 @@ def test_misaligned_fused():
                                         eps, 1, torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert st == mbr.RMSNORM_OK
-    h_want, y_want = parity.oracle_residual(inputs.bits(t["x"]), inputs.bits(t["residual"]),
-                                            inputs.bits(t["weight"]), eps)
+    h_want, y_want, e, gamma = expect(inputs.bits(t["x"]), inputs.bits(t["weight"]), eps,
+                                      auto(rows, hidden, BF16, False, True), inputs.bits(t["residual"]))
     cpu = inputs.bits(buf.cpu())
     assert np.array_equal(cpu[ho:ho + n].reshape(rows, hidden), h_want)
-    parity.compare(cpu[oo:oo + n].reshape(rows, hidden), y_want)
+    parity.compare(cpu[oo:oo + n].reshape(rows, hidden), y_want, e, gamma)
 
 
 @pytest.mark.parametrize("hidden", [4096, 4100])
 def test_in_place_plain(hidden):
     w = inputs.custom(300, hidden, "bf16", False)
     t = inputs.make(w, seed=13)
-    want = parity.oracle_fwd(inputs.bits(t["x"]), inputs.bits(t["weight"]), 1e-5)
+    _, want, e, gamma = expect(inputs.bits(t["x"]), inputs.bits(t["weight"]), 1e-5, auto(300, hidden, BF16))
     x = t["x"].cuda()
     run_plain(x, t["weight"].cuda(), 1e-5, out=x)
-    parity.compare(inputs.bits(x), want)
+    parity.compare(inputs.bits(x), want, e, gamma)
 
 
 @pytest.mark.parametrize("alias", ["h=residual", "h=x", "out=x", "out=residual", "h=x,out=residual"])
 def test_in_place_fused(alias):
     w = inputs.custom(257, 5120, "bf16", True)
     t = inputs.make(w, seed=14)
-    h_want, y_want = parity.oracle_residual(inputs.bits(t["x"]), inputs.bits(t["residual"]),
-                                            inputs.bits(t["weight"]), 1e-5)
+    h_want, y_want, e, gamma = expect(inputs.bits(t["x"]), inputs.bits(t["weight"]), 1e-5,
+                                      auto(257, 5120, BF16, True, True), inputs.bits(t["residual"]))
     x, r, wt = t["x"].cuda(), t["residual"].cuda(), t["weight"].cuda()
     named = {"x": x, "residual": r}
     h = torch.empty_like(x)
@@ -395,7 +414,7 @@ def test_in_place_fused(alias):
             out = named[v]
     run_fused(x, r, wt, 1e-5, h=h, out=out)
     assert np.array_equal(inputs.bits(h), h_want)
-    parity.compare(inputs.bits(out), y_want)
+    parity.compare(inputs.bits(out), y_want, e, gamma)
 
 
 def test_overlap_rejected_on_device_buffers():
@@ -418,7 +437,8 @@ def test_non_default_stream():
         out = torch.empty_like(x)
         mbr.rmsnorm_fwd(x, wt, out, w.eps)
     s.synchronize()
-    parity.compare(inputs.bits(out), parity.oracle_fwd(inputs.bits(t["x"]), inputs.bits(t["weight"]), w.eps))
+    _, want, e, gamma = expect(inputs.bits(t["x"]), inputs.bits(t["weight"]), w.eps, auto(w.rows, w.hidden, BF16))
+    parity.compare(inputs.bits(out), want, e, gamma)
 
 
 # ---------------------------------------------------------------- determinism and degenerate rows
@@ -461,11 +481,11 @@ def test_degenerate_rows(dtype):
     for eps in (1e-5, 0.0):
         xs = x if eps > 0 else x[1:]
         y = run_plain(xs.cuda(), wt.cuda(), eps)
-        want = parity.oracle_fwd(inputs.bits(xs), inputs.bits(wt), eps)
+        _, want, e, gamma = expect(inputs.bits(xs), inputs.bits(wt), eps, auto(xs.shape[0], H, td))
         got = inputs.bits(y)
         if eps > 0:
             assert np.all(got[0].astype(np.float64) == 0) if dtype == "f32" else np.all(got[0] & 0x7FFF == 0)
-        parity.compare(got, want)
+        parity.compare(got, want, e, gamma)
 
 
 def test_pages_rmsnorm_test_case_on_gpu():
@@ -480,7 +500,8 @@ def test_pages_rmsnorm_test_case_on_gpu():
     for td, tol in ((F32, 1e-4), (BF16, 0.05)):
         xt, gt = torch.from_numpy(x).to(td), torch.from_numpy(g).to(td)
         y = run_plain(xt.cuda(), gt.cuda(), eps)
-        parity.compare(inputs.bits(y), parity.oracle_fwd(inputs.bits(xt), inputs.bits(gt), eps))
+        _, want, e, gamma = expect(inputs.bits(xt), inputs.bits(gt), eps, auto(rows, hidden, td))
+        parity.compare(inputs.bits(y), want, e, gamma)
         err = float(np.max(np.abs(y.float().cpu().numpy() - ref)))
         say("pages' test case", td, "max_err vs f32 reference on unrounded inputs", err)
         assert err <= tol
