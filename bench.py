@@ -24,10 +24,28 @@ replay), the way a serving loop issues them; the same K steps as eager
 launches are timed first and reported as eager_us_per_call.  --eager times the
 eager launches instead.  For the large workloads both give the same per-call
 time once the GPU is warm; the small ones finish faster than Python can issue
-eager launches.  The default warm-up is 300 steps: measured on MI355X, the
-first ~20 ms of a burst of launches run slower than the steady state (bf16
-[16384, 8192]: 87.2 us per call after 20 warm-up steps, 84.7 after 300).  Parity of this launch configuration at this
-size with the CPU oracle is the job of the GPU test suite, not of this script.
+eager launches.  After the timed region the same graph is replayed S more
+times, each replay timed on its own, for the spread of the per-call time
+(median, minimum, 90th percentile).
+
+Default run (the headline workload): before the headline's own warm-up the
+other four stated configurations are measured -- fp32 [64, 2048], bf16
+[4096, 2048], bf16 [256, 4096] and the fused bf16 [12289, 5120] -- each with
+its launches captured in a HIP graph that cycles through enough rotating sets
+to stay HBM-cold, 20 replays timed one by one (median, minimum, p90 per call);
+then the copy ceiling.  They go into the line as per_config.  Measured on
+MI355X, the first ~20 ms of a burst of launches run slower than the steady
+state (bf16 [16384, 8192]: 87.2 us per call after 20 launches, 84.7 after
+300), so this order also means the headline's W warm-up steps start on a GPU
+that has been busy for seconds.  Parity of every launch configuration timed
+here, at these sizes, with the CPU oracle is the job of the GPU test suite,
+not of this script.
+
+CPU baseline: the oracle (as it stands) over a bounded sample of the
+headline's rows, with the rows split over every CPU this process may use
+(its affinity mask capped by its cgroup CPU quota) and again on one thread;
+one warm-up pass, then timed runs of at least a second each, the median
+reported.
 
 Prints ONE JSON line on stdout.  With --all, one JSON record per other
 workload is written to stderr (lines starting with '#'); those also carry the
@@ -39,6 +57,7 @@ import concurrent.futures
 import json
 import os
 import platform
+import statistics
 import sys
 import time
 
@@ -64,6 +83,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=300,
                     help="untimed warm-up steps (default 300: on MI355X the first ~20 ms of a burst of "
                          "launches run up to 3%% slower, 12%% for the quantised forms, than the steady state)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other stated configurations (per_config) in the default run")
+    ap.add_argument("--spread", type=int, default=20,
+                    help="extra timed replays of the headline graph for the per-call spread (0: none)")
     ap.add_argument("--workload", default=inputs.HEADLINE, choices=sorted(inputs.EVERY_WORKLOAD))
     ap.add_argument("--all", action="store_true", help="also time every other workload (stderr)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline budget; 0 disables it")
@@ -74,12 +97,39 @@ def parse():
     return ap.parse_args()
 
 
-def host_threads() -> int:
+def cgroup_cpu_quota():
+    """CPUs this process's cgroup may use (cgroup v2 cpu.max or v1 cfs quota),
+    or None when unlimited or unknown."""
     try:
-        n = len(os.sched_getaffinity(0))
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            q, per = f.read().split()[:2]
+            return None if q == "max" else int(q) / int(per)
+    except (OSError, ValueError):
+        pass
+    try:
+        with open("/sys/fs/cgroup/cpu/cpu.cfs_quota_us") as f:
+            q = int(f.read())
+        with open("/sys/fs/cgroup/cpu/cpu.cfs_period_us") as f:
+            per = int(f.read())
+        return None if q <= 0 else q / per
+    except (OSError, ValueError):
+        return None
+
+
+def host_cpus():
+    """(threads, detail): every CPU this process may use -- its affinity mask,
+    capped by its cgroup CPU quota when there is one."""
+    try:
+        aff = len(os.sched_getaffinity(0))
     except AttributeError:
-        n = os.cpu_count() or 1
-    return max(1, min(16, n))
+        aff = os.cpu_count() or 1
+    quota = cgroup_cpu_quota()
+    n = aff if quota is None else max(1, min(aff, int(quota)))
+    return n, {"affinity_cpus": aff, "cgroup_cpu_quota": quota}
+
+
+def host_threads() -> int:
+    return host_cpus()[0]
 
 
 def cpu_model() -> str:
@@ -176,12 +226,42 @@ def n_sets_for(w) -> int:
     return max(2, -(-MIN_FOOTPRINT // per_set))
 
 
-def time_steps_graph(fn, steps, warmup):
+def percentile(vals, q):
+    """Nearest-rank percentile q (0-100) of a non-empty list."""
+    v = sorted(vals)
+    k = max(0, min(len(v) - 1, -(-len(v) * q // 100) - 1))
+    return v[int(k)]
+
+
+def spread_us(per_call_s, launches):
+    """Median, minimum and 90th percentile of per-call times (seconds), in us."""
+    return {"us_median": round(statistics.median(per_call_s) * 1e6, 3), "us_min": round(min(per_call_s) * 1e6, 3),
+            "us_p90": round(percentile(per_call_s, 90) * 1e6, 3), "samples": len(per_call_s),
+            "launches_per_sample": launches}
+
+
+def replay_samples(g, launches, samples):
+    """Replay a captured graph `samples` times, each replay between its own HIP
+    events on the current stream; per-call seconds of each replay."""
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(samples)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) / 1e3 / launches for a, b in ev]
+
+
+def time_steps_graph(fn, steps, warmup, spread=0):
     """Exactly `steps` calls, captured once in a HIP graph and replayed once
     between a device synchronise and HIP events on the launch stream.  Before
     that: W eager warm-up calls and one untimed replay, which uploads the
     graph.  Consecutive calls stay ordered (a captured stream is a chain of
-    dependent nodes); what a replay leaves out is the per-launch host work."""
+    dependent nodes); what a replay leaves out is the per-launch host work.
+    After the timed replay, `spread` more replays are timed one by one.
+    Returns (wall seconds, event seconds, per-call seconds of the extra replays)."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -199,8 +279,9 @@ def time_steps_graph(fn, steps, warmup):
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    extra = replay_samples(g, steps, spread) if spread > 0 else []
     del g
-    return wall, start.elapsed_time(end) / 1e3
+    return wall, start.elapsed_time(end) / 1e3, extra
 
 
 def time_steps(fn, steps, warmup):
@@ -217,15 +298,17 @@ def time_steps(fn, steps, warmup):
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, start.elapsed_time(end) / 1e3
+    return wall, start.elapsed_time(end) / 1e3, []
 
 
-def graph_time(fn, n_sets, replays=10):
-    """Per-launch time with the launches captured once in a HIP graph and
-    replayed, which removes Python and launch-call overhead from the GPU
-    timeline (the kernels allocate nothing and memset nothing, so they capture
-    cleanly)."""
-    launches = min(4096, max(64, n_sets))  # one pass over every rotation set
+def graph_samples(fn, n_sets, samples=20):
+    """Per-launch times with the launches captured once in a HIP graph that
+    cycles through every rotation set (at least 64 launches), replayed
+    `samples` times, each replay timed on its own.  The graph removes Python
+    and launch-call overhead from the GPU timeline (the kernels allocate and
+    memset nothing, so they capture cleanly).  Returns (per-call seconds of each
+    replay, launches per replay)."""
+    launches = min(4096, max(64, n_sets))
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -233,13 +316,15 @@ def graph_time(fn, n_sets, replays=10):
             fn(i % n_sets)
     g.replay()
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(replays):
-        g.replay()
-    end.record()
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / 1e3 / (launches * replays)
+    per = replay_samples(g, launches, samples)
+    del g
+    return per, launches
+
+
+def graph_time(fn, n_sets, replays=10):
+    """Median per-launch time over `replays` timed graph replays."""
+    per, _ = graph_samples(fn, n_sets, replays)
+    return statistics.median(per)
 
 
 def copy_ceiling(w, steps, warmup, graph=False):
@@ -250,7 +335,7 @@ def copy_ceiling(w, steps, warmup, graph=False):
     src = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(i % 251) for i in range(n)]
     dst = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(n)]
     timer = time_steps_graph if graph else time_steps
-    wall, ev = timer(lambda i: mbr.hbm_copy(src[i % n], dst[i % n]), steps, warmup)
+    wall, ev, _ = timer(lambda i: mbr.hbm_copy(src[i % n], dst[i % n]), steps, warmup)
     del src, dst
     torch.cuda.empty_cache()
     return 2 * nbytes / (ev / steps) / 1e9
@@ -292,21 +377,58 @@ def load_traffic(w, launch):
         return None
 
 
+def _cpu_rates(one_pass, sample_bytes, threads, runs, min_s):
+    """One warm-up pass, then `runs` timed runs of at least min_s seconds each
+    (whole passes); GB/s of each run."""
+    one_pass(threads)
+    rates = []
+    for _ in range(runs):
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            one_pass(threads)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= min_s:
+                break
+        rates.append(sample_bytes * reps / el / 1e9)
+    return rates
+
+
+def _cpu_record(one_pass, sample_bytes, seconds, sample_desc):
+    """The oracle on every usable CPU and on one thread: median of 5 and of 3
+    timed runs; `seconds` is the whole budget."""
+    T, detail = host_cpus()
+    min_s = max(0.2, seconds / 8)
+    rates = _cpu_rates(one_pass, sample_bytes, T, 5, min_s)
+    one = _cpu_rates(one_pass, sample_bytes, 1, 3, min_s) if T > 1 else rates
+    med = statistics.median(rates)
+    return {"value": round(med, 4), "unit": "GB/s", "cores": T, "kind": "oracle",
+            "sample": "%s; rows split over %d threads (every CPU this process may use), median of %d timed runs "
+                      "of >= %.1f s after a warm-up pass" % (sample_desc, T, len(rates), min_s),
+            "runs_gbps": [round(r, 4) for r in rates],
+            "one_thread": {"value": round(statistics.median(one), 4), "unit": "GB/s", "threads": 1,
+                           "runs_gbps": [round(r, 4) for r in one]},
+            "host": dict({"cpu_model": cpu_model(), "os_cpu_count": os.cpu_count()}, **detail)}
+
+
+def _split(n, T):
+    return [(i * n // T, (i + 1) * n // T) for i in range(T)]
+
+
 def cpu_baseline_kv(w, t, seconds):
     """The oracle over the first tokens of a KV workload, tokens split across
     the host's threads, each thread writing compact caches of its own."""
     import numpy as np
     import oracle  # the CPU checker; timed here as a reported baseline only
-    T = host_threads()
     tokens = min(w.tokens, 2048)
     kvb = inputs.bits(t["kv"])[:tokens]
     gb = inputs.bits(t["gamma"])
     cos_t, sin_t = t["cos"].numpy(), t["sin"].numpy()
     pos = t["positions"].numpy()[:tokens]
     np_dtype = np.uint16 if w.dtype == "bf16" else np.float32
-    per_thread = [(i * tokens // T, (i + 1) * tokens // T) for i in range(T)]
 
-    def one_pass():
+    def one_pass(T):
         with concurrent.futures.ThreadPoolExecutor(T) as ex:
             def job(r):
                 n = r[1] - r[0]
@@ -316,40 +438,28 @@ def cpu_baseline_kv(w, t, seconds):
                 rc = np.empty((n, w.heads, w.rope_dim), np_dtype)
                 oracle.kv_rmsnorm_rope_cache(kvb[r[0]:r[1]], gb, cos_t, sin_t, pos[r[0]:r[1]],
                                              np.arange(n, dtype=np.int64), nc, rc, w.eps, w.rope_style)
-            list(ex.map(job, per_thread))
+            list(ex.map(job, _split(tokens, T)))
 
-    one_pass()
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        one_pass()
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
     sample_bytes = w.algorithmic_bytes * tokens // w.tokens
-    return {"value": round(sample_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": T, "kind": "oracle",
-            "sample": "first %d of %d tokens, %d passes in %.1f s on %d threads (%s)"
-                      % (tokens, w.tokens, reps, el, T, cpu_model())}
+    return _cpu_record(one_pass, sample_bytes, seconds, "first %d of %d tokens" % (tokens, w.tokens))
 
 
 def cpu_baseline(w, t, seconds):
-    """The oracle, as it stands, over a bounded sample of the workload's rows,
-    rows split across the host's threads; GB/s with the same byte ledger."""
+    """The oracle, as it stands, over a bounded sample of the workload's rows
+    (about 64 MiB of algorithmic bytes), rows split across the host's threads;
+    GB/s with the same byte ledger."""
     if is_kv(w):
         return cpu_baseline_kv(w, t, seconds)
     import oracle  # the CPU checker; timed here as a reported baseline only
-    T = host_threads()
-    rows = min(w.rows, 512 if w.hidden >= 4096 else 2048)
+    rows = max(1, min(w.rows, (64 << 20) * w.rows // w.algorithmic_bytes))
     xb = inputs.bits(t["x"])[:rows]
     wb = inputs.bits(t["weight"])
     rb = inputs.bits(t["residual"])[:rows] if w.fused else None
     gb = inputs.bits(t["dy"])[:rows] if w.backward else None
     bb = inputs.bits(t["beta"]) if w.layernorm else None
-    per_thread = [(i * rows // T, (i + 1) * rows // T) for i in range(T)]
     qt = {"int8": oracle.QUANT_INT8, "fp8": oracle.QUANT_FP8_E4M3}.get(w.quant)
 
-    def one_pass():
+    def one_pass(T):
         with concurrent.futures.ThreadPoolExecutor(T) as ex:
             def job(r):
                 if r[0] == r[1]:
@@ -365,44 +475,40 @@ def cpu_baseline(w, t, seconds):
                     oracle.rmsnorm_residual_fwd(xb[r[0]:r[1]], rb[r[0]:r[1]], wb, w.eps)
                 else:
                     oracle.rmsnorm_fwd(xb[r[0]:r[1]], wb, w.eps)
-            list(ex.map(job, per_thread))
+            list(ex.map(job, _split(rows, T)))
 
-    one_pass()  # warm-up
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        one_pass()
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
     sample_bytes = inputs.Workload(w.name, w.dtype, rows, w.hidden, w.eps, w.fused, w.x, w.weight, w.residual,
                                    quant=w.quant, grad=w.grad, beta=w.beta).algorithmic_bytes
-    return {"value": round(sample_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": T, "kind": "oracle",
-            "sample": "first %d of %d rows, %d passes in %.1f s on %d threads (%s)"
-                      % (rows, w.rows, reps, el, T, cpu_model())}
+    return _cpu_record(one_pass, sample_bytes, seconds, "first %d of %d rows" % (rows, w.rows))
 
 
-def bench_workload(w, steps, warmup, seed, with_copy=True, graph=False, timed_graph=False):
+def setup_workload(w, seed):
+    """(host tensors, rotating device sets, number of sets, shape fields)."""
     if is_kv(w):
         t = inputs.make_kv(w, seed=seed)
         n_sets = n_sets_for(w)
-        sets = KvSets(w, t, n_sets)
-        shape = {"tokens": w.tokens, "heads": w.heads, "norm_dim": w.norm_dim, "rope_dim": w.rope_dim,
-                 "num_slots": w.num_slots}
-    else:
-        t = inputs.make(w, seed=seed)
-        n_sets = n_sets_for(w)
-        sets = Sets(w, t, n_sets)
-        shape = {"rows": w.rows, "hidden": w.hidden, "fused": w.fused, "quant": w.quant, "backward": w.backward}
+        return t, KvSets(w, t, n_sets), n_sets, {"tokens": w.tokens, "heads": w.heads, "norm_dim": w.norm_dim,
+                                                 "rope_dim": w.rope_dim, "num_slots": w.num_slots}
+    t = inputs.make(w, seed=seed)
+    n_sets = n_sets_for(w)
+    return t, Sets(w, t, n_sets), n_sets, {"rows": w.rows, "hidden": w.hidden, "fused": w.fused, "quant": w.quant,
+                                           "backward": w.backward}
+
+
+def bench_workload(w, steps, warmup, seed, with_copy=True, graph=False, timed_graph=False, spread=0):
+    t, sets, n_sets, shape = setup_workload(w, seed)
     nbytes = w.algorithmic_bytes
     rec = dict({"workload": w.name, "dtype": w.dtype}, **shape)
+    if with_copy:
+        # the copy ceiling first: the same read/write byte count, rotated and timed the same way
+        rec["copy_ceiling_gbps"] = copy_ceiling(w, max(20, steps // 2), max(2, warmup // 2), graph=timed_graph)
     if timed_graph:
         # eager launches first, for the record; the timed steps are a graph replay
-        _, ev_e = time_steps(sets.launch, steps, warmup)
+        _, ev_e, _ = time_steps(sets.launch, steps, warmup)
         rec["eager_us_per_call"] = ev_e / steps * 1e6
         rec["eager_gbps"] = nbytes / (ev_e / steps) / 1e9
-    wall, ev = (time_steps_graph if timed_graph else time_steps)(sets.launch, steps, warmup)
+    wall, ev, extra = (time_steps_graph(sets.launch, steps, warmup, spread) if timed_graph
+                       else time_steps(sets.launch, steps, warmup))
     kern_s = ev / steps
     rec.update({
         "timing": "graph" if timed_graph else "eager",
@@ -411,15 +517,40 @@ def bench_workload(w, steps, warmup, seed, with_copy=True, graph=False, timed_gr
         "gbps_wall": nbytes * steps / wall / 1e9, "gbps_kernel": nbytes / kern_s / 1e9,
         "kernel_config": launch_dict(w),
     })
+    if extra:
+        rec["spread"] = spread_us(extra, steps)
     if graph:
         gs = graph_time(sets.launch, n_sets)
         rec["us_per_call_graph"] = gs * 1e6
         rec["gbps_graph"] = nbytes / gs / 1e9
     if with_copy:
-        cc = copy_ceiling(w, max(20, steps // 2), max(2, warmup // 2), graph=timed_graph)
-        rec["copy_ceiling_gbps"] = cc
-        rec["frac_of_copy_ceiling"] = rec["gbps_kernel"] / cc
+        rec["frac_of_copy_ceiling"] = rec["gbps_kernel"] / rec["copy_ceiling_gbps"]
+    del sets
+    torch.cuda.empty_cache()
     return t, rec
+
+
+# The other stated configurations, measured in the default run (per_config).
+STATED = {"C1": "fp32_64x2048", "C2": "bf16_prefill_4096x2048", "C3": "bf16_decode_256x4096",
+          "C4": inputs.HEADLINE, "C5": "bf16_residual_12289x5120"}
+
+
+def measure_config(w, seed, samples=20):
+    """One stated configuration, HBM-cold: its launches captured in a HIP graph
+    that cycles through the rotating sets, `samples` replays timed one by one;
+    per-call median, minimum and p90, and GB/s and roofline fraction at the
+    median."""
+    t, sets, n_sets, shape = setup_workload(w, seed)
+    for i in range(2 * n_sets):  # first launches: module load, clocks
+        sets.launch(i)
+    per, launches = graph_samples(sets.launch, n_sets, samples)
+    del sets, t
+    torch.cuda.empty_cache()
+    med = statistics.median(per)
+    gbps = w.algorithmic_bytes / med / 1e9
+    return dict({"workload": w.name, "dtype": w.dtype}, **shape, algorithmic_bytes=w.algorithmic_bytes,
+                rotation_sets=n_sets, gbps=round(gbps, 2), frac=round(gbps / HBM_PEAK_GBPS, 4),
+                launch=launch_dict(w), **spread_us(per, launches))
 
 
 def describe(w):
@@ -465,7 +596,15 @@ def main():
     mbr.lib()  # fail loudly if the HIP library is not built
     w = inputs.EVERY_WORKLOAD[args.workload]
     log("# device:", torch.cuda.get_device_name(0), "| workload:", w.name, "| steps", args.steps, "warmup", args.warmup)
-    t, rec = bench_workload(w, args.steps, args.warmup, args.seed, not args.no_copy, timed_graph=not args.eager)
+    per_config = {}
+    if w.name == inputs.HEADLINE and not args.no_configs:
+        for label, name in STATED.items():
+            if name == w.name:
+                continue
+            per_config[label] = measure_config(inputs.WORKLOADS[name], args.seed)
+            log("# %s:" % label, json.dumps(per_config[label]))
+    t, rec = bench_workload(w, args.steps, args.warmup, args.seed, not args.no_copy, timed_graph=not args.eager,
+                            spread=0 if args.eager else args.spread)
     log("# timed:", json.dumps(rec))
 
     achieved = rec["gbps_kernel"]
@@ -495,12 +634,19 @@ def main():
         "timing": ("the K steps captured in one HIP graph and replayed once between synchronisations"
                    if rec["timing"] == "graph" else "K eager launches between synchronisations"),
     }
+    if "spread" in rec:
+        line["spread"] = dict(rec["spread"], note="the same K-step graph replayed again, each replay timed on its "
+                                                  "own with HIP events")
     if "eager_us_per_call" in rec:
         line["eager_us_per_call"] = round(rec["eager_us_per_call"], 3)
         line["eager_gbps"] = round(rec["eager_gbps"], 2)
     if "copy_ceiling_gbps" in rec:
         line["copy_ceiling_gbps"] = round(rec["copy_ceiling_gbps"], 2)
         line["frac_of_copy_ceiling"] = round(rec["frac_of_copy_ceiling"], 4)
+    if per_config:
+        line["per_config"] = dict(per_config, note="measured before the headline: graph replays over rotating "
+                                                   "sets (HBM-cold), per call; parity by tests/test_parity_gpu.py::"
+                                                   "test_stated_workloads_full_size")
     if args.all:
         for name, other in inputs.EVERY_WORKLOAD.items():
             if name == w.name:

@@ -43,3 +43,28 @@ def test_traffic_is_read_only_while_sources_match(monkeypatch):
     monkeypatch.setattr(_build, "source_digest", lambda family="fwd": "0" * 64)
     assert bench.load_traffic(w, launch) is None
     assert bench.load_traffic(w, dict(launch, path="two_pass")) is None
+
+
+def test_cpu_baseline_uses_every_usable_cpu_and_one_thread():
+    """The oracle timed on all CPUs this process may use and on one thread,
+    medians of several timed runs, with the host recorded."""
+    w = inputs.custom(256, 1024, "bf16", False)
+    t = inputs.make(w, seed=0)
+    rec = bench.cpu_baseline(w, t, 0.8)
+    n, detail = bench.host_cpus()
+    assert rec["cores"] == n and rec["kind"] == "oracle" and rec["unit"] == "GB/s"
+    assert len(rec["runs_gbps"]) == 5 and rec["value"] > 0
+    assert rec["one_thread"]["threads"] == 1 and len(rec["one_thread"]["runs_gbps"]) == (3 if n > 1 else 5)
+    assert rec["host"]["affinity_cpus"] >= n
+
+
+def test_spread_statistics():
+    s = bench.spread_us([3e-6, 1e-6, 2e-6, 4e-6, 10e-6], 7)
+    assert s["us_median"] == 3.0 and s["us_min"] == 1.0 and s["us_p90"] == 10.0
+    assert s["samples"] == 5 and s["launches_per_sample"] == 7
+    assert bench.percentile(list(range(1, 101)), 90) == 90
+
+
+def test_stated_configurations_are_the_five_workloads():
+    assert set(bench.STATED.values()) == set(inputs.WORKLOADS) - {"bf16_shard_2048x8192"}
+    assert bench.STATED["C4"] == inputs.HEADLINE
