@@ -33,11 +33,12 @@ other four stated configurations are measured -- fp32 [64, 2048], bf16
 [4096, 2048], bf16 [256, 4096] and the fused bf16 [12289, 5120] -- each with
 its launches captured in a HIP graph that cycles through enough rotating sets
 to stay HBM-cold, 20 replays timed one by one (median, minimum, p90 per call);
-then the copy ceiling.  They go into the line as per_config.  Measured on
-MI355X, the first ~20 ms of a burst of launches run slower than the steady
-state (bf16 [16384, 8192]: 87.2 us per call after 20 launches, 84.7 after
-300), so this order also means the headline's W warm-up steps start on a GPU
-that has been busy for seconds.  Parity of every launch configuration timed
+then the copy ceiling, after 100 ms of copies.  They go into the line as
+per_config.  Measured on MI355X, the first ~20 ms of a burst of launches run
+slower than the steady state (bf16 [16384, 8192]: 87.2 us per call after 20
+launches, 84.7 after 300); the ceiling is a steady-state figure, and taking it
+right before the headline means the headline's W warm-up steps also start on
+a GPU at steady clocks.  Parity of every launch configuration timed
 here, at these sizes, with the CPU oracle is the job of the GPU test suite,
 not of this script.
 
@@ -327,15 +328,37 @@ def graph_time(fn, n_sets, replays=10):
     return statistics.median(per)
 
 
+def warm_for(fn, seconds):
+    """Launch fn in batches of 16 until `seconds` of wall time have passed,
+    synchronising after each batch; returns the number of launches."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    i = 0
+    while True:
+        for _ in range(16):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return i
+
+
+COPY_WARM_SECONDS = 0.1
+
+
 def copy_ceiling(w, steps, warmup, graph=False):
     """hbm_copy of the same read/write byte count as one step, rotated the same
-    way and timed the same way (eager launches or one graph replay)."""
+    way and timed the same way (eager launches or one graph replay), after
+    100 ms of copies: on MI355X the first ~20 ms of a burst of launches run
+    slower than the steady state, and the ceiling is a steady-state figure."""
     nbytes = w.copy_bytes
     n = max(2, -(-MIN_FOOTPRINT // (2 * nbytes)))
     src = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(i % 251) for i in range(n)]
     dst = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(n)]
     timer = time_steps_graph if graph else time_steps
-    wall, ev, _ = timer(lambda i: mbr.hbm_copy(src[i % n], dst[i % n]), steps, warmup)
+    copy = lambda i: mbr.hbm_copy(src[i % n], dst[i % n])  # noqa: E731
+    warm_for(copy, COPY_WARM_SECONDS)
+    wall, ev, _ = timer(copy, steps, warmup)
     del src, dst
     torch.cuda.empty_cache()
     return 2 * nbytes / (ev / steps) / 1e9
