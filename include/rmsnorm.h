@@ -19,7 +19,8 @@
  *   - Pointers are DEVICE pointers (HIP device memory, e.g. torch CUDA-tensor
  *     storage).  The caller owns every buffer; the library allocates nothing
  *     and keeps no per-call state.  Only the backward's weight gradient needs
- *     scratch memory, which the caller passes in as a workspace.
+ *     scratch memory, which the caller passes in as a workspace (or, with
+ *     rmsnorm_bwd_noalloc, the library's fixed per-GPU scratch array).
  *   - Tensors are contiguous and row-major; weight is [hidden]; all tensors
  *     share one dtype.  Any element-aligned address is accepted; 16-byte
  *     vector accesses are used only when every pointer is 16-byte aligned and
@@ -298,6 +299,26 @@ RMSNORM_API rmsnorm_status_t rmsnorm_bwd_ex(const void* x, const void* weight, c
                                             void* dweight, int64_t rows, int64_t hidden, float eps,
                                             rmsnorm_dtype_t dtype, void* workspace, size_t workspace_bytes,
                                             const rmsnorm_config_t* cfg, void* stream);
+
+/* rmsnorm_bwd for callers that cannot allocate device memory -- code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc: no
+ * workspace argument, and no allocation inside.  The partial dweight rows live
+ * in a 16 MiB array the library holds in device memory (one per GPU, kept
+ * until the process ends).  Arguments and results as rmsnorm_bwd; the launch
+ * configuration is rmsnorm_bwd's automatic choice, with the number of partial
+ * dweight rows capped at what the array holds, 16 MiB / (round_up(hidden, 64)
+ * * 4) (512 rows at hidden 8192): below the cap the results equal
+ * rmsnorm_bwd's bitwise, above it only the dweight summation order differs.
+ * hidden above 4194304 with dweight is INVALID_ARG (one partial row would not
+ * fit).  Runs on the current device (the stream must belong to it); the
+ * array's address is looked up there on the first call (RUNTIME if HIP
+ * fails).  Every call on one GPU shares that GPU's array: calls that may run
+ * at the same time on one GPU (other streams, other host threads) race and
+ * must be ordered by the caller.  Nothing in the array needs clearing between
+ * calls: each call writes every partial row it reads. */
+RMSNORM_API rmsnorm_status_t rmsnorm_bwd_noalloc(const void* x, const void* weight, const void* dy, void* dx,
+                                                 void* dweight, int64_t rows, int64_t hidden, float eps,
+                                                 rmsnorm_dtype_t dtype, void* stream);
 
 /* Bytes of workspace rmsnorm_bwd (cfg NULL or AUTO: any pointer alignment) or
  * rmsnorm_bwd_ex with cfg needs to produce dweight:

@@ -108,6 +108,7 @@ def lib() -> ctypes.CDLL:
         L.rmsnorm_dynamic_quant_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, f32, i32, i32, cfgp, vp]
         L.rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, i32, vp, ctypes.c_size_t, vp]
         L.rmsnorm_bwd_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, i32, vp, ctypes.c_size_t, cfgp, vp]
+        L.rmsnorm_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, i32, vp]
         L.rmsnorm_bwd_workspace_size.argtypes = [i64, i64, i32, cfgp, ctypes.POINTER(ctypes.c_size_t)]
         L.rmsnorm_select_bwd_config.argtypes = [i64, i64, i32, i32, cfgp]
         L.layernorm_fwd.argtypes = [vp, vp, vp, vp, i64, i64, f32, i32, vp]
@@ -122,7 +123,8 @@ def lib() -> ctypes.CDLL:
         L.rmsnorm_status_string.restype = ctypes.c_char_p
         for fn in (L.rmsnorm_fwd, L.rmsnorm_residual_fwd, L.rmsnorm_fwd_ex, L.rmsnorm_residual_fwd_ex,
                    L.rmsnorm_select_config, L.rmsnorm_select_quant_config, L.rmsnorm_dynamic_quant_fwd,
-                   L.rmsnorm_dynamic_quant_fwd_ex, L.rmsnorm_bwd, L.rmsnorm_bwd_ex, L.rmsnorm_bwd_workspace_size,
+                   L.rmsnorm_dynamic_quant_fwd_ex, L.rmsnorm_bwd, L.rmsnorm_bwd_ex, L.rmsnorm_bwd_noalloc,
+                   L.rmsnorm_bwd_workspace_size,
                    L.rmsnorm_select_bwd_config, L.layernorm_fwd, L.layernorm_fwd_ex, L.layernorm_select_config,
                    L.kv_rmsnorm_rope_cache, L.kv_rmsnorm_rope_cache_ex, L.kv_select_config):
             fn.restype = i32
@@ -342,6 +344,29 @@ def rmsnorm_bwd_ex(x, weight, dy, dx, dweight=None, eps: float = 1e-5, workspace
 def rmsnorm_bwd(x, weight, dy, dx, dweight=None, eps: float = 1e-5, workspace=None, stream=None):
     """RMSNorm backward (C: rmsnorm_bwd)."""
     return rmsnorm_bwd_ex(x, weight, dy, dx, dweight, eps, workspace, None, stream)
+
+
+def rmsnorm_bwd_noalloc(x, weight, dy, dx, dweight=None, eps: float = 1e-5, stream=None):
+    """RMSNorm backward with no workspace and no allocation (C:
+    rmsnorm_bwd_noalloc): the partial dweight rows live in the library's
+    per-GPU scratch array, so calls on one GPU must not overlap in time."""
+    for t, n in ((x, "x"), (weight, "weight"), (dy, "dy"), (dx, "dx")):
+        _device_tensor(t, n)
+    for t, n in ((dy, "dy"), (dx, "dx")):
+        if t.shape != x.shape or t.dtype != x.dtype:
+            raise ValueError("%s must match x in shape and dtype" % n)
+    if weight.dtype != x.dtype:
+        raise ValueError("weight must match x in dtype")
+    rows, hidden = _shape(x, weight)
+    if dweight is not None:
+        _device_tensor(dweight, "dweight")
+        if dweight.shape != weight.shape or dweight.dtype != x.dtype:
+            raise ValueError("dweight must match weight in shape and dtype")
+    st = lib().rmsnorm_bwd_noalloc(x.data_ptr(), weight.data_ptr(), dy.data_ptr(), dx.data_ptr(),
+                                   dweight.data_ptr() if dweight is not None else None, rows, hidden, float(eps),
+                                   dtype_code(x.dtype), _stream(stream, x.device))
+    _check(st, "rmsnorm_bwd_noalloc")
+    return dx, dweight
 
 
 def layernorm_fwd_ex(x, gamma, beta, out, eps: float = 1e-5, config: Optional[Config] = None, stream=None):

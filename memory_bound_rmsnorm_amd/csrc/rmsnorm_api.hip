@@ -10,8 +10,10 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdlib>
 #include <math.h>
+#include <mutex>
 #include <stdint.h>
 
 #include "../../include/rmsnorm.h"
@@ -659,6 +661,68 @@ rmsnorm_status_t run_bwd(const BwdProblem& p, const rmsnorm_config_t* user, void
     return s;
 }
 
+// ---------------------------------------------------------------- allocation-free backward
+
+// The allocation-free backward keeps its partial dweight rows in this fixed
+// device array instead of a caller workspace.  Each GPU the library runs on
+// holds its own copy (16 MiB) until the process ends.  In host code the name
+// is only a host-side stand-in: the array's device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::atomic<float*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// This device's copy of the scratch array, looked up on its first use with
+// the device current; nullptr if HIP reports an error.
+float* scratch_on_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    float* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        void* q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        p = static_cast<float*>(q);
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
+rmsnorm_status_t run_bwd_noalloc(BwdProblem p, void* stream) {
+    rmsnorm_status_t s = validate_sizes(p.rows, p.hidden, p.eps, p.dtype);
+    if (s != RMSNORM_OK) return s;
+    if (p.rows == 0) return run_bwd(p, nullptr, stream);  // dweight zeroed, no partial rows
+    const bool aligned = p.x && p.w && p.dy && p.dx && bwd_vector_aligned(p);
+    rmsnorm_config_t c = choose_bwd(p.rows, p.hidden, p.dtype, aligned);
+    if (p.dw) {
+        // as many partial rows as the scratch array holds, at most the
+        // automatic choice's (then the results equal rmsnorm_bwd's bitwise)
+        const int64_t cap = static_cast<int64_t>(kScratchBytes) / (bwd_ld(p.hidden) * 4);
+        if (cap < 1) return RMSNORM_ERR_INVALID_ARG;
+        if (bwd_partials(p.rows, c) > cap) c.max_blocks = static_cast<int32_t>(cap);
+    }
+    s = validate_bwd_pointers(p, 0);  // every argument error before the first HIP call
+    if (s != RMSNORM_OK) return s;
+    if (p.dw) {
+        float* ws = scratch_on_current_device();
+        if (!ws) return RMSNORM_ERR_RUNTIME;
+        p.ws = ws;
+        p.ws_bytes = kScratchBytes;
+    }
+    return run_bwd(p, &c, stream);
+}
+
 // ---------------------------------------------------------------- LayerNorm
 
 struct LnProblem {
@@ -1147,6 +1211,13 @@ RMSNORM_API rmsnorm_status_t rmsnorm_bwd(const void* x, const void* weight, cons
                                          void* workspace, size_t workspace_bytes, void* stream) {
     return rmsnorm_bwd_ex(x, weight, dy, dx, dweight, rows, hidden, eps, dtype, workspace, workspace_bytes, nullptr,
                           stream);
+}
+
+RMSNORM_API rmsnorm_status_t rmsnorm_bwd_noalloc(const void* x, const void* weight, const void* dy, void* dx,
+                                                 void* dweight, int64_t rows, int64_t hidden, float eps,
+                                                 rmsnorm_dtype_t dtype, void* stream) {
+    const BwdProblem p = {x, weight, dy, dx, dweight, rows, hidden, eps, static_cast<int>(dtype), nullptr, 0};
+    return run_bwd_noalloc(p, stream);
 }
 
 RMSNORM_API rmsnorm_status_t rmsnorm_bwd_workspace_size(int64_t rows, int64_t hidden, rmsnorm_dtype_t dtype,

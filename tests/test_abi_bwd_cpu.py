@@ -162,3 +162,25 @@ def test_bad_forced_configs():
     cfg = mbr.Config(mbr.PATH_VECTOR, 8, 1, 1, 0)
     st = L.rmsnorm_bwd_ex(X + 2, W, G, D, None, rows, hidden, 1e-5, 1, None, 0, ctypes.byref(cfg), None)
     assert st == INV
+
+
+def test_noalloc_argument_errors_before_any_hip_call():
+    """rmsnorm_bwd_noalloc rejects bad sizes, null or overlapping pointers and a
+    hidden size whose one partial dweight row would not fit its 16 MiB scratch
+    array, all before its first HIP call (here there is no GPU: a HIP call
+    would give RUNTIME, not INVALID_ARG)."""
+    L = mbr.lib()
+    INV = mbr.RMSNORM_ERR_INVALID_ARG
+    base = 1 << 44
+    assert L.rmsnorm_bwd_noalloc(None, None, None, None, None, 4, 64, 1e-5, 1, None) == INV
+    assert L.rmsnorm_bwd_noalloc(base, base + (1 << 30), base + (2 << 30), base + (3 << 30), None, -1, 64, 1e-5, 1,
+                                 None) == INV
+    assert L.rmsnorm_bwd_noalloc(base, base + (1 << 30), base + (2 << 30), base + (3 << 30), None, 4, 64, 1e-5, 7,
+                                 None) == mbr.RMSNORM_ERR_UNSUPPORTED_DTYPE
+    # dx partially overlapping x
+    assert L.rmsnorm_bwd_noalloc(base, base + (1 << 30), base + (2 << 30), base + 16, None, 4, 64, 1e-5, 1,
+                                 None) == INV
+    # one partial row of hidden 4194305 (round_up 4194368 floats) exceeds 16 MiB
+    h = 4194305
+    assert L.rmsnorm_bwd_noalloc(base, base + (1 << 36), base + (2 << 36), base + (3 << 36), base + (4 << 36), 2, h,
+                                 1e-5, 0, None) == INV
