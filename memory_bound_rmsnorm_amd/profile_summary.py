@@ -21,32 +21,79 @@ from collections import defaultdict
 
 from memory_bound_rmsnorm_amd import _build, inputs
 
-RMS_KERNEL_TAGS = ("rms_vec_kernel", "rms_elem_kernel", "rms_twopass_kernel")
-BWD_KERNEL_TAGS = ("rms_bwd_vec_kernel", "rms_bwd_elem_kernel", "rms_bwd_twopass_kernel")
-BWD_DW_TAG = "rms_bwd_dw_kernel"
-LN_KERNEL_TAGS = ("ln_vec_kernel", "ln_elem_kernel", "ln_multipass_kernel")
-KV_KERNEL_TAGS = ("kv_vec_kernel", "kv_elem_kernel")
+COPY_KERNEL_TAG = "hbm_copy_kernel"
 
 
 def _is_kv(w):
     return isinstance(w, inputs.KvWorkload)
-COPY_KERNEL_TAG = "hbm_copy_kernel"
 
 
-def _is_rms(name):
-    return any(t in name for t in RMS_KERNEL_TAGS)
+def _targ(kind, v):
+    """One template argument: (demangled text, Itanium-mangled text)."""
+    if kind == "class":
+        return "mbr::" + v, "NS_%d%sE" % (len(v), v)
+    if kind == "bool":
+        return ("true" if v else "false"), "Lb%dE" % int(bool(v))
+    return str(v), ("Li%dE" % v if v >= 0 else "Lin%dE" % -v)
+
+
+def _instance(name, args):
+    """(demangled 'mbr::name<...>' prefix, mangled fragment) of one kernel instance."""
+    parts = [_targ(k, v) for k, v in args]
+    return ("mbr::%s<%s>" % (name, ", ".join(d for d, _ in parts)),
+            "%sI%sEEv" % (name, "".join(m for _, m in parts)))
+
+
+def kernel_instances(w):
+    """The kernel instances one step of workload w launches with the library's
+    automatic configuration on 16-byte-aligned buffers, in launch order."""
+    e = ("class", "F32" if w.dtype == "f32" else "Bf16")
+    if _is_kv(w):
+        k = kv_launch(w)
+        if k["path"] == "vector":
+            nv = w.norm_dim // (4 if w.dtype == "f32" else 8)
+            masked = k["lanes_per_row"] * k["norm_vectors_per_lane"] != nv
+            return [_instance("kv_vec_kernel", [e, ("int", k["norm_vectors_per_lane"]), ("bool", masked),
+                                                ("int", w.rope_style), ("int", k["lanes_per_row"])])]
+        return [_instance("kv_elem_kernel", [e, ("int", w.rope_style)])]
+    cfg = launch_config(w)
+    v = 4 if w.dtype == "f32" else 8
+    units = w.hidden // v
+    lpr = cfg.lanes_per_row or 64
+    lanes = lpr if lpr < 64 else 64 * cfg.waves_per_row
+    per = cfg.items_per_lane
+    masked = lanes * per != units
+    wpr, path = cfg.waves_per_row, cfg.path
+    if w.backward:
+        if path == 1:
+            row = _instance("rms_bwd_vec_kernel", [e, ("int", wpr), ("int", per), ("bool", masked), ("bool", True),
+                                                   ("int", lpr)])
+        elif path == 2:
+            row = _instance("rms_bwd_elem_kernel", [e, ("int", wpr), ("int", per), ("bool", True)])
+        else:
+            row = _instance("rms_bwd_twopass_kernel", [e, ("bool", True), ("bool", True)])
+        return [row, _instance("rms_bwd_dw_kernel", [e])]
+    if w.layernorm:
+        if path == 1:
+            return [_instance("ln_vec_kernel", [e, ("int", wpr), ("int", per), ("bool", masked),
+                                                ("bool", bool(cfg.weight_lds)), ("int", lpr)])]
+        if path == 2:
+            return [_instance("ln_elem_kernel", [e, ("int", wpr), ("int", per)])]
+        return [_instance("ln_multipass_kernel", [e, ("bool", True)])]
+    qt = {None: 0, "int8": 1, "fp8": 2}[w.quant]
+    if path == 1:
+        return [_instance("rms_vec_kernel", [e, ("int", wpr), ("int", per), ("bool", masked), ("bool", w.fused),
+                                             ("int", qt), ("int", lpr)])]
+    if path == 2:
+        return [_instance("rms_elem_kernel", [e, ("int", wpr), ("int", per), ("bool", w.fused), ("int", qt)])]
+    return [_instance("rms_twopass_kernel", [e, ("bool", True), ("bool", w.fused), ("int", qt)])]
 
 
 def _step_kernels(w):
-    """Predicates for the kernels one step of workload w launches, once each:
-    the forward kernel, or the backward row kernel plus the dweight reduction."""
-    if _is_kv(w):
-        return [lambda k: any(t in k for t in KV_KERNEL_TAGS)]
-    if w.backward:
-        return [lambda k: any(t in k for t in BWD_KERNEL_TAGS), lambda k: BWD_DW_TAG in k]
-    if w.layernorm:
-        return [lambda k: any(t in k for t in LN_KERNEL_TAGS)]
-    return [_is_rms]
+    """Predicates for the kernels one step of workload w launches, once each
+    (the exact template instances of its automatic configuration): the
+    forward kernel, or the backward row kernel plus the dweight reduction."""
+    return [(lambda k, d=d: d in k) for d, _ in kernel_instances(w)]
 
 
 def _family(w):
@@ -95,24 +142,29 @@ def stats(args):
         out.append("rmsnorm_gbps_from_avg: %.1f" % (w.algorithmic_bytes / t / 1e3))
         out.append("rmsnorm_frac_of_8TBps: %.4f" % (w.algorithmic_bytes / t / 1e3 / 8000.0))
     # The average above covers every dispatch of the run: warm-up, the eager
-    # pass and the graph replays.  bench.py's timed steps are the last
-    # args.steps dispatches of each kernel (the timed graph replay); their
-    # average, from the per-dispatch trace next to the stats file, is the
-    # figure to set beside the bench line's own HIP-event reading.
+    # pass and the graph replays.  The window below picks the dispatches that
+    # a bench line's own HIP events timed (counted from the end of the run,
+    # in launch order), from the per-dispatch trace next to the stats file.
     trace = os.path.join(os.path.dirname(args.csv), os.path.basename(args.csv).replace("kernel_stats", "kernel_trace"))
-    if os.path.exists(trace) and trace != args.csv and len(step_avg) == len(preds):
+    if os.path.exists(trace) and trace != args.csv and len(step_avg) == len(preds) and args.window_count > 0:
         with open(trace) as f:
-            disp = list(csv.DictReader(f))
+            disp = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
         timed = []
         for pred in preds:
             d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in disp if pred(r["Kernel_Name"])]
-            if len(d) >= args.steps:
-                timed.append(sum(d[-args.steps:]) / args.steps)
+            a = len(d) - args.window_from_end
+            if a >= 0 and a + args.window_count <= len(d):
+                win = d[a:a + args.window_count]
+                timed.append((sum(win) / len(win), sorted(win)[len(win) // 2]))
         if len(timed) == len(preds):
-            t = sum(timed)
-            out.append("timed_steps: the last %d dispatches of each kernel (the timed graph replay)" % args.steps)
-            out.append("timed_steps_avg_us: %.3f" % t)
-            out.append("timed_steps_gbps: %.1f" % (w.algorithmic_bytes / t / 1e3))
+            t = sum(x[0] for x in timed)
+            out.append("timed_window: %s" % args.window_note)
+            out.append("timed_window_dispatches: %d (from %d before the end)" % (args.window_count,
+                                                                                 args.window_from_end))
+            out.append("timed_window_avg_us: %.3f" % t)
+            out.append("timed_window_median_us: %.3f" % sum(x[1] for x in timed))
+            out.append("timed_window_gbps: %.1f" % (w.algorithmic_bytes / t / 1e3))
+            out.append("timed_window_frac_of_8TBps: %.4f" % (w.algorithmic_bytes / t / 1e3 / 8000.0))
     print("\n".join(out))
 
 
@@ -148,7 +200,8 @@ def pmc(args):
     rname = " + ".join(rname)
     cname, cfetch = _pick(fm, lambda k: COPY_KERNEL_TAG in k)
     _, cwrite = _pick(wm, lambda k: COPY_KERNEL_TAG in k)
-    copy_bytes = w.copy_bytes  # read == written per dispatch, as bench.py's copy ceiling
+    # read == written per dispatch: the copy ceiling of the workload the run was for
+    copy_bytes = inputs.EVERY_WORKLOAD[args.copy_workload or args.workload].copy_bytes
     fscale = copy_bytes / (cfetch * 1024.0)
     wscale = copy_bytes / (cwrite * 1024.0)
     read_alg = w.read_bytes
@@ -163,7 +216,7 @@ def pmc(args):
            "rmsnorm_dispatches_counted: %d" % min(ndisp),
            "rmsnorm_fetch_kib_per_dispatch: %.1f" % rfetch,
            "rmsnorm_write_kib_per_dispatch: %.1f" % rwrite,
-           "copy_kernel: %s" % COPY_KERNEL_TAG,
+           "copy_kernel: %s (the copy ceiling of %s)" % (COPY_KERNEL_TAG, args.copy_workload or args.workload),
            "copy_bytes_read_and_written_per_dispatch: %d" % copy_bytes,
            "copy_fetch_kib_per_dispatch: %.1f" % cfetch,
            "copy_write_kib_per_dispatch: %.1f" % cwrite,
@@ -225,49 +278,11 @@ def resources(args):
            "# command: %s" % args.command,
            "kernels_built: %d" % len(lines),
            "kernels_with_scratch_or_spills: %d" % len(spill)]
-    for name, w in inputs.ALL_WORKLOADS.items():
-        cfg = launch_config(w)
-        e = "F32" if w.dtype == "f32" else "Bf16"
-        per = cfg.items_per_lane
-        units = w.hidden // (4 if w.dtype == "f32" else 8)
-        masked = 64 * cfg.waves_per_row * per != units
-        if w.backward:
-            if cfg.path == 1:  # rms_bwd_vec_kernel<E, WPR, VPL, MASKED, DW, LPR>
-                lpr = cfg.lanes_per_row or 64
-                masked = (lpr if lpr < 64 else 64 * cfg.waves_per_row) * per != units
-                mangled = "rms_bwd_vec_kernelINS_%d%sELi%dELi%dELb%dELb1ELi%dEEEv" % (
-                    len(e), e, cfg.waves_per_row, per, int(masked), lpr)
-            else:  # rms_bwd_elem_kernel<E, WPR, EPL, DW>, rms_bwd_twopass_kernel<E, VEC, DW>
-                fam = {2: "rms_bwd_elem_kernel", 3: "rms_bwd_twopass_kernel"}[cfg.path]
-                mangled = "%sINS_%d%sELi%dELi%dELb%dELb1EEEv" % (fam, len(e), e, cfg.waves_per_row, per, int(masked))
-        elif w.layernorm:
-            mangled = "ln_vec_kernelINS_%d%sELi%dELi%dELb%dELb%dEEEv" % (len(e), e, cfg.waves_per_row, per, int(masked),
-                                                                   int(bool(cfg.weight_lds)))
-        else:
-            qt = {None: 0, "int8": 1, "fp8": 2}[w.quant]
-            if cfg.path == 1:  # rms_vec_kernel<E, WPR, VPL, MASKED, FUSED, QT, LPR>
-                lpr = cfg.lanes_per_row or 64
-                masked = (lpr if lpr < 64 else 64 * cfg.waves_per_row) * per != units
-                mangled = "rms_vec_kernelINS_%d%sELi%dELi%dELb%dELb%dELi%dELi%dEEEv" % (
-                    len(e), e, cfg.waves_per_row, per, int(masked), int(w.fused), qt, lpr)
-            elif cfg.path == 2:  # rms_elem_kernel<E, WPR, EPL, FUSED, QT>
-                mangled = "rms_elem_kernelINS_%d%sELi%dELi%dELb%dELi%dEEEv" % (len(e), e, cfg.waves_per_row, per,
-                                                                              int(w.fused), qt)
-            else:  # rms_twopass_kernel<E, VEC, FUSED, QT>
-                mangled = "rms_twopass_kernelINS_%d%sELb1ELb%dELi%dEEEv" % (len(e), e, int(w.fused), qt)
-        hit = [l for l in lines if mangled in l]
-        out.append("%s -> %s | %s" % (name, cfg.as_dict(), hit[0].split("|", 1)[1].strip() if hit else "?"))
-    for name, w in inputs.KV_WORKLOADS.items():
-        k = kv_launch(w)
-        e = "F32" if w.dtype == "f32" else "Bf16"
-        if k["path"] == "vector":
-            masked = k["lanes_per_row"] * k["norm_vectors_per_lane"] != w.norm_dim // (4 if w.dtype == "f32" else 8)
-            mangled = "kv_vec_kernelINS_%d%sELi%dELb%dELi%dELi%dEEEv" % (len(e), e, k["norm_vectors_per_lane"],
-                                                                        int(masked), w.rope_style, k["lanes_per_row"])
-        else:
-            mangled = "kv_elem_kernelINS_%d%sELi%dEEEv" % (len(e), e, w.rope_style)
-        hit = [l for l in lines if mangled in l]
-        out.append("%s -> %s | %s" % (name, k, hit[0].split("|", 1)[1].strip() if hit else "?"))
+    for name, w in list(inputs.ALL_WORKLOADS.items()) + list(inputs.KV_WORKLOADS.items()):
+        for _, mangled in kernel_instances(w):
+            hit = [l for l in lines if mangled in l]
+            out.append("%s -> %s | %s | %s" % (name, launch_dict(w), mangled.split("I", 1)[0],
+                                               hit[0].split("|", 1)[1].strip() if hit else "?"))
     print("\n".join(out))
 
 
@@ -304,7 +319,10 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
-    s.add_argument("--steps", type=int, default=200, help="timed steps of the traced bench run")
+    s.add_argument("--window-from-end", type=int, default=0,
+                   help="first dispatch of the timed window, counted from the end of each kernel's dispatches")
+    s.add_argument("--window-count", type=int, default=0, help="dispatches in the timed window (0: none)")
+    s.add_argument("--window-note", default="", help="what the timed window is")
     s.add_argument("--csv", required=True)
     s.add_argument("--workload", default=inputs.HEADLINE, choices=sorted(inputs.EVERY_WORKLOAD))
     s.add_argument("--command", required=True)
@@ -312,6 +330,8 @@ def main(argv=None):
     p.add_argument("--fetch", required=True)
     p.add_argument("--write", required=True)
     p.add_argument("--workload", default=inputs.HEADLINE)
+    p.add_argument("--copy-workload", default=None,
+                   help="workload whose copy ceiling the run's copy kernel moved (default: --workload)")
     p.add_argument("--command-fetch", required=True)
     p.add_argument("--command-write", required=True)
     o = sub.add_parser("occupancy")
