@@ -125,13 +125,20 @@ typedef enum {
     RMSNORM_PATH_AUTO = 0,     /* let the library choose (the other fields are ignored) */
     RMSNORM_PATH_VECTOR = 1,   /* row in VGPRs, 16-byte loads/stores; needs 16-byte alignment */
     RMSNORM_PATH_ELEMENT = 2,  /* row in VGPRs, one element per access; any alignment */
-    RMSNORM_PATH_TWO_PASS = 3, /* row too large for registers: second read of x (and residual) */
-    RMSNORM_PATH_VECTOR_ANY = 4 /* rmsnorm_fwd_ex / rmsnorm_residual_fwd_ex /
+    RMSNORM_PATH_TWO_PASS = 3, /* row too large for registers and LDS, or an unaligned row too
+                                  large for registers: second read of x (and residual) */
+    RMSNORM_PATH_VECTOR_ANY = 4, /* rmsnorm_fwd_ex / rmsnorm_residual_fwd_ex /
                                    rmsnorm_dynamic_quant_fwd_ex / rmsnorm_bwd_ex /
                                    layernorm_fwd_ex: any width of at least one
                                    vector and any element alignment; the row's full
                                    16-byte vectors at whatever alignment it has, then its last
                                    hidden % (16 / size) elements one by one; rows_per_block 1 */
+    RMSNORM_PATH_VECTOR_LDS = 5 /* rmsnorm_fwd_ex / rmsnorm_residual_fwd_ex: rows wider than
+                                   the register path holds, still read once: 1024 lanes
+                                   (waves_per_row 16, rows_per_block 1), items_per_lane
+                                   vectors per lane in VGPRs (10 plain; 6 or 7 fused), the
+                                   row's remaining vectors staged in LDS, at most 162816
+                                   bytes of them; needs 16-byte alignment */
 } rmsnorm_path_t;
 
 typedef struct {
@@ -139,6 +146,7 @@ typedef struct {
     int32_t waves_per_row;  /* 64-lane waves cooperating on one row: 1, 2, 4, 8 or 16 */
     int32_t items_per_lane; /* VECTOR: 16-byte vectors per lane, one of 1-8, 10, 12, 14, 16;
                                ELEMENT: elements per lane, one of 1, 2, 4, 8, 16;
+                               VECTOR_LDS: vectors per lane held in VGPRs (see above);
                                TWO_PASS: ignored (0) */
     int32_t rows_per_block; /* rows per workgroup; 64 * waves_per_row * rows_per_block <= 512
                                (1024 when waves_per_row == 16); TWO_PASS: must be 1 */

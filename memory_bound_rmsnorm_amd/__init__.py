@@ -53,8 +53,9 @@ PATH_VECTOR = 1
 PATH_ELEMENT = 2
 PATH_TWO_PASS = 3
 PATH_VECTOR_ANY = 4
+PATH_VECTOR_LDS = 5
 PATH_NAMES = {PATH_AUTO: "auto", PATH_VECTOR: "vector", PATH_ELEMENT: "element", PATH_TWO_PASS: "two_pass",
-              PATH_VECTOR_ANY: "vector_any"}
+              PATH_VECTOR_ANY: "vector_any", PATH_VECTOR_LDS: "vector_lds"}
 
 
 class Config(ctypes.Structure):

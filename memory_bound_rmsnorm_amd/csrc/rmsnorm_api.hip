@@ -135,6 +135,23 @@ bool vector_aligned(const Problem& p) {
     return true;  // codes: a 16-byte-aligned base keeps every row's 8- (4-) byte stores aligned
 }
 
+// Vectors per lane the register + LDS path holds in registers for a row of
+// nvec vectors, or 0 when the row does not fit it: the register part must
+// leave at least one vector for LDS, and the rest must fit the LDS limit.
+int stage_rv(int64_t nvec, bool fused) {
+    const int64_t lds_vectors = mbr::kStageLdsMax / kVectorBytes;
+    int rv = 0;
+    if (!fused) {
+        rv = mbr::kStageRvPlain;
+    } else {
+        for (int v : mbr::kStageRvFused)  // ascending: the most registers that leave a staged part
+            if (nvec > int64_t(mbr::kStageLanes) * v) rv = v;
+    }
+    if (rv == 0) return 0;
+    const int64_t staged = nvec - int64_t(mbr::kStageLanes) * rv;
+    return staged >= 1 && staged <= lds_vectors ? rv : 0;
+}
+
 // The automatic choice, from launch-shape sweeps on MI355X.  Vector path:
 // spread a row over the fewest waves (one row per workgroup) that keep at most
 // two 16-byte vectors of it per lane (four for the fused form, whose lanes
@@ -176,7 +193,20 @@ rmsnorm_config_t choose(int64_t rows, int64_t hidden, int dtype, bool aligned, b
         wpr *= 2;
         per = fit(wpr);
     }
-    if (per < 0) return c;
+    if (per < 0) {
+        // Wider than every register configuration.  Aligned rows that fit
+        // 1024 lanes' registers plus LDS are still read once (register + LDS
+        // path); the rest take two passes.
+        if (vec && !qt) {
+            const int rv = stage_rv(units, fused);
+            if (rv > 0) {
+                c.path = RMSNORM_PATH_VECTOR_LDS;
+                c.waves_per_row = 16;
+                c.items_per_lane = rv;
+            }
+        }
+        return c;
+    }
     if ((vec || any) && !qt && rows >= 1024 && (!fused || rows < 4096) && int64_t(64) * wpr * per > units) {
         // rows the cap leaves padded (bf16 hidden 3072, 5120, 6144; fused
         // 5120 below 4096 rows): the fewest idle lanes with at most five
@@ -326,6 +356,18 @@ rmsnorm_status_t launch(const Problem& p, const rmsnorm_config_t* user, hipStrea
             if (threads > mbr::max_threads_for(c.waves_per_row)) return RMSNORM_ERR_INVALID_ARG;
             fn = p.qt ? mbr::qelem_kernel(p.dtype, p.qt, p.fused, wi, ei) : mbr::elem_kernel(p.dtype, p.fused, wi, ei);
             a.units = static_cast<int32_t>(p.hidden);
+            break;
+        }
+        case RMSNORM_PATH_VECTOR_LDS: {
+            if (!aligned || p.hidden % vec_elems(p.dtype) != 0 || p.qt) return RMSNORM_ERR_INVALID_ARG;
+            if (c.waves_per_row != 16 || !whole || c.rows_per_block != 1 || c.weight_lds) return RMSNORM_ERR_INVALID_ARG;
+            const int64_t nvec = p.hidden / vec_elems(p.dtype);
+            const int64_t staged = nvec - int64_t(mbr::kStageLanes) * c.items_per_lane;
+            if (staged < 1 || staged * kVectorBytes > mbr::kStageLdsMax) return RMSNORM_ERR_INVALID_ARG;
+            fn = mbr::stage_kernel(p.dtype, p.fused, c.items_per_lane);
+            threads = mbr::kStageLanes;
+            lds_bytes = static_cast<size_t>(staged * kVectorBytes);
+            a.units = static_cast<int32_t>(nvec);
             break;
         }
         case RMSNORM_PATH_TWO_PASS: {

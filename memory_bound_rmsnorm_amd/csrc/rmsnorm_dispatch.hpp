@@ -43,7 +43,18 @@ constexpr bool qany_built(int wpr, int vpl) { return wpr < 16 || vpl <= 4; }
 const void* vec_kernel(int dtype, bool fused, bool masked, int wpr_index, int vpl_index);
 const void* elem_kernel(int dtype, bool fused, int wpr_index, int epl_index);
 const void* twopass_kernel(int dtype, bool fused, bool vec);
+
 const void* any_kernel(int dtype, bool fused, bool masked, int wpr_index, int vpl_index);
+
+// Register + LDS path (rows wider than the register configurations): vectors
+// per lane held in VGPRs, the rest of the row staged in dynamic LDS of at
+// most kStageLdsMax bytes (160 KiB per gfx950 workgroup, less 1 KiB for the
+// kernel's own row totals).
+constexpr int kStageRvPlain = 10;
+constexpr int kStageRvFused[] = {6, 7};
+constexpr int kStageLanes = 1024;
+constexpr long kStageLdsMax = 160 * 1024 - 1024;
+const void* stage_kernel(int dtype, bool fused, int rv);
 
 // Quantised forms; qt: 1 = int8, 2 = fp8 e4m3fn.
 const void* qvec_kernel(int dtype, int qt, bool fused, bool masked, int wpr_index, int vpl_index);

@@ -7,13 +7,17 @@
 // with a single rounding at write-back and exactly one global read and one
 // global write of every row (gollamago README, "RMSNorm 优化（TileLang）").
 //
-// Three kernel families, all one row per group of 64*WPR lanes:
+// Kernel families, all one row per group of 64*WPR lanes:
 //   rms_vec_kernel      the row lives in VGPRs as packed 16-byte vectors
 //                       (bf16x8 / f32x4); coalesced 16-byte loads and stores.
+//   rms_any_kernel      the same at any element alignment (full vectors plus
+//                       a tail of single elements).
 //   rms_elem_kernel     the row lives in VGPRs as fp32 scalars, one element per
 //                       access: any hidden, any element alignment.
-//   rms_twopass_kernel  rows larger than the register budget of a 1024-lane
-//                       workgroup: pass 1 sums squares, pass 2 re-reads x.
+//   rms_stage_kernel    rows larger than the register budget of a 1024-lane
+//                       workgroup: part in VGPRs, the rest staged in LDS.
+//   rms_twopass_kernel  rows larger than that, or unaligned wide rows: pass 1
+//                       sums squares, pass 2 re-reads x.
 //
 // QT != 0 selects the dynamic-quantisation form (the Add + RmsNorm +
 // DynamicQuant fusion the TileLang tutorial ch. 02, section 4.2, cites from
@@ -758,6 +762,127 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_elem_kernel(const RowA
                 const int j = k * LANES + lane_row;
                 if (j < H) outr[j] = narrow1(d[k] * r * widen1(wr[j]), E{});
             }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- register + LDS path
+
+// Rows wider than any register-resident configuration, still read once and
+// written once (the one-read-per-row point of the gollamago README, "RMSNorm
+// 优化（TileLang）"): 1024 lanes per row; the first 1024 * RV vectors of the
+// row stay in VGPRs as on the vector path (lane l owns vectors l, l + 1024,
+// ...), and the remaining nl = units - 1024 * RV vectors are staged in
+// dynamic LDS, nl * 16 bytes (up to nearly the 160 KiB a gfx950 workgroup
+// can take).  Lane l stages vectors R + l, R + l + 1024, ... in LDS slots l,
+// l + 1024, ...: it alone writes and reads its slots, so the staged part
+// needs no barrier of its own.  The staged vectors pass through registers CH
+// per lane at a time, issued right after the register part's loads; their
+// squares join the same per-lane sum.  The reduction (one LDS slot per wave,
+// one barrier, every wave adding the 16 slots in order) and the rounding are
+// the vector path's.  Aligned rows only, one row per workgroup at a time.
+template <class E, int RV, int CH, bool FUSED>
+__global__ void __launch_bounds__(1024) rms_stage_kernel(const RowArgs a) {
+    constexpr int LANES = 1024;
+    constexpr int V = E::kVec;
+    constexpr int R = LANES * RV;
+    const int lane = static_cast<int>(threadIdx.x);
+    const int wave = wave_id();
+    const int nvec = a.units;
+    const int nl = nvec - R;                     // staged vectors, > 0
+    const int ml = (nl + LANES - 1) / LANES;     // staged slots per lane (uniform)
+    __shared__ float part[2][16];
+    extern __shared__ u32x4 stage[];
+    const u32x4* wr = static_cast<const u32x4*>(a.w);
+
+    auto add_round = [&](u32x4 xv, u32x4 rv) {  // h = round(x + residual)
+        float fx[V], fr[V];
+        widen(xv, fx, E{});
+        widen(rv, fr, E{});
+#pragma unroll
+        for (int i = 0; i < V; ++i) fx[i] += fr[i];
+        return narrow(fx, E{});
+    };
+    auto sumsq = [&](u32x4 v) {
+        float f[V];
+        widen(v, f, E{});
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < V; ++i) s += f[i] * f[i];
+        return s;
+    };
+    auto scaled = [&](u32x4 v, u32x4 w, float r) {
+        // widen the packed vector again here: without this (empty) register
+        // constraint the compiler reuses the fp32 values of the sum of squares
+        // and keeps them live across the barrier, twice the registers of the
+        // packed row, and spills
+        asm volatile("" : "+v"(v));
+        float f[V], fw[V];
+        widen(v, f, E{});
+        widen(w, fw, E{});
+#pragma unroll
+        for (int i = 0; i < V; ++i) f[i] = f[i] * r * fw[i];
+        return narrow(f, E{});
+    };
+
+    int it = 0;
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x, ++it) {
+        const u32x4* xr = static_cast<const u32x4*>(a.x) + row * nvec;
+        const u32x4* rr = static_cast<const u32x4*>(a.res) + row * nvec;  // fused only
+        u32x4* hr = static_cast<u32x4*>(a.h) + row * nvec;               // fused only
+        u32x4 d[RV], rv[FUSED ? RV : 1];
+#pragma unroll
+        for (int k = 0; k < RV; ++k) d[k] = load_stream(xr + k * LANES + lane);
+        if constexpr (FUSED) {
+#pragma unroll
+            for (int k = 0; k < RV; ++k) rv[k] = load_stream(rr + k * LANES + lane);
+        }
+        float ss = 0.f;
+        for (int m0 = 0; m0 < ml; m0 += CH) {
+            u32x4 t[CH], tr[FUSED ? CH : 1];
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const int u = (m0 + c) * LANES + lane;
+                if (u < nl) {
+                    t[c] = load_stream(xr + R + u);
+                    if constexpr (FUSED) tr[c] = load_stream(rr + R + u);
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const int u = (m0 + c) * LANES + lane;
+                if (u < nl) {
+                    if constexpr (FUSED) {
+                        t[c] = add_round(t[c], tr[c]);  // h rounded once; the norm sees this value
+                        store_stream(hr + R + u, t[c]);
+                    }
+                    ss += sumsq(t[c]);
+                    stage[u] = t[c];
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < RV; ++k) {
+            if constexpr (FUSED) {
+                d[k] = add_round(d[k], rv[k]);
+                store_stream(hr + k * LANES + lane, d[k]);
+            }
+            ss += sumsq(d[k]);
+        }
+        ss = wave_sum(ss);
+        if ((lane & 63) == 0) part[it & 1][wave] = ss;
+        __syncthreads();
+        ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ss += part[it & 1][i];
+        const float r = rsqrtf(ss / a.hidden_f + a.eps);
+        u32x4* outr = static_cast<u32x4*>(a.out) + row * nvec;
+#pragma unroll
+        for (int k = 0; k < RV; ++k)
+            store_stream(outr + k * LANES + lane, scaled(d[k], load_keep(wr + k * LANES + lane), r));
+        for (int m = 0; m < ml; ++m) {
+            const int u = m * LANES + lane;
+            if (u < nl) store_stream(outr + R + u, scaled(stage[u], load_keep(wr + R + u), r));
         }
     }
 }

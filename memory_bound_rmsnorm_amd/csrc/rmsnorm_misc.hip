@@ -39,6 +39,23 @@ const void* elem_kernel(int dtype, bool fused, int wi, int ei) {
     return t[wi * kNumEpl + ei];
 }
 
+const void* stage_kernel(int dtype, bool fused, int rv) {
+    // chunk of staged vectors per lane through registers: the largest that
+    // stays spill-free at 128 VGPRs (1024-lane workgroups)
+    if (!fused) {
+        if (rv != kStageRvPlain) return nullptr;
+        return dtype == 1 ? reinterpret_cast<const void*>(&rms_stage_kernel<Bf16, 10, 10, false>)
+                          : reinterpret_cast<const void*>(&rms_stage_kernel<F32, 10, 10, false>);
+    }
+    if (rv == 6)
+        return dtype == 1 ? reinterpret_cast<const void*>(&rms_stage_kernel<Bf16, 6, 5, true>)
+                          : reinterpret_cast<const void*>(&rms_stage_kernel<F32, 6, 5, true>);
+    if (rv == 7)
+        return dtype == 1 ? reinterpret_cast<const void*>(&rms_stage_kernel<Bf16, 7, 4, true>)
+                          : reinterpret_cast<const void*>(&rms_stage_kernel<F32, 7, 4, true>);
+    return nullptr;
+}
+
 const void* twopass_kernel(int dtype, bool fused, bool vec) {
     if (dtype == 1) {
         if (vec) return fused ? reinterpret_cast<const void*>(&rms_twopass_kernel<Bf16, true, true>)

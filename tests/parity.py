@@ -175,6 +175,9 @@ def chain(cfg, hidden: int, bf16: bool) -> int:
         per_lane = cfg.items_per_lane
     elif cfg.path == 4:    # any alignment: the lane's vectors plus one tail element
         per_lane = cfg.items_per_lane * v + 1
+    elif cfg.path == 5:    # register + LDS: the lane's register vectors plus its staged ones
+        staged = hidden // v - 1024 * cfg.items_per_lane
+        per_lane = (cfg.items_per_lane + -(-staged // 1024)) * v
     else:                  # two-pass: every lane strides over the row
         vec = hidden % v == 0
         units = hidden // v if vec else hidden

@@ -254,9 +254,19 @@ def test_selection_is_always_a_built_covering_config(hidden, rows, dtype, aligne
         assert 64 * cfg.waves_per_row * cfg.items_per_lane >= hidden
         assert cfg.items_per_lane in (1, 2, 4, 8, 16)
         assert hidden < vec  # a row of at least one vector takes a vector path
+    elif cfg.path == mbr.PATH_VECTOR_LDS:
+        # past the register path: 1024 lanes, a register part plus at least
+        # one staged vector, the staged part within LDS
+        assert aligned and hidden % vec == 0 and cfg.waves_per_row == 16 and cfg.rows_per_block == 1
+        assert cfg.items_per_lane == (10 if not fused else cfg.items_per_lane) and cfg.items_per_lane in (6, 7, 10)
+        staged = hidden // vec - 1024 * cfg.items_per_lane
+        assert 1 <= staged and staged * 16 <= 160 * 1024 - 1024
+        assert hidden // vec > 1024 * (6 if fused else 10)  # the register path cannot hold it
     else:
         assert cfg.path == mbr.PATH_TWO_PASS and cfg.rows_per_block == 1
         assert hidden > 8192  # everything narrower fits a register-resident path
+        if aligned and hidden % vec == 0:  # aligned rows take two passes only past registers + LDS
+            assert hidden // vec > 1024 * (7 if fused else 10) + (160 * 1024 - 1024) // 16
     assert 64 * cfg.waves_per_row * cfg.rows_per_block <= (1024 if cfg.waves_per_row == 16 else 512)
     assert cfg.rows_per_block <= max(rows, 1)
     if cfg.weight_lds:

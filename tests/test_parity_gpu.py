@@ -264,6 +264,89 @@ def test_persistent_grid_matches_bitwise(fused):
     check_workload(w, inputs.make(w, seed=3), capped)
 
 
+# ---------------------------------------------------------------- rows wider than the registers
+
+
+STAGED_WIDTHS = [81928, 98304, 131072, 131080, 163328]
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("hidden", STAGED_WIDTHS)
+def test_staged_rows_automatic(hidden, fused):
+    """bf16 rows past the register budget: part in VGPRs, the rest in LDS, read
+    once (fused rows past what registers plus LDS hold take two passes)."""
+    rows = 37
+    cfg = auto(rows, hidden, BF16, True, fused)
+    say("staged", hidden, "fused" if fused else "plain", cfg)
+    if not fused or hidden <= 138752:
+        assert cfg.path == mbr.PATH_VECTOR_LDS
+    check_workload(inputs.custom(rows, hidden, "bf16", fused), inputs.make(inputs.custom(rows, hidden, "bf16", fused),
+                                                                            seed=hidden + fused))
+
+
+def _staged_cases(dtype, fused):
+    """(items_per_lane, staged vectors) for every built register + LDS kernel:
+    one staged vector, a partial last slot, whole slots, and the LDS limit."""
+    v = 8 if dtype == "bf16" else 4
+    top = (160 * 1024 - 1024) // 16
+    for rv in ((6, 7) if fused else (10,)):
+        for staged in sorted({1, 1023, 1024, 1025, 5000, top - 1, top}):
+            yield rv, (1024 * rv + staged) * v
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("fused", [False, True])
+def test_every_staged_config(dtype, fused):
+    """Forced register + LDS configurations at every staged-part shape, with a
+    capped grid whose workgroups walk several rows (the LDS slots reused)."""
+    n = 0
+    for rv, hidden in _staged_cases(dtype, fused):
+        for mb in (0, 2):
+            rows = 5
+            cfg = mbr.Config(mbr.PATH_VECTOR_LDS, 16, rv, 1, mb)
+            w = inputs.custom(rows, hidden, dtype, fused)
+            say("staged config", dtype, fused, cfg, "hidden", hidden)
+            check_workload(w, inputs.make(w, seed=900 + n), cfg)
+            n += 1
+    assert n >= 14
+
+
+def test_staged_in_place_and_rejections():
+    """out == x and h == residual on the register + LDS path; configurations
+    that would leave nothing for LDS, overflow it, or lack alignment are
+    refused before launch."""
+    rows, hidden = 9, 131072
+    w = inputs.custom(rows, hidden, "bf16", True)
+    t = inputs.make(w, seed=77)
+    cfg = auto(rows, hidden, BF16, True, True)
+    h_want, y_want, e, gamma = expect(inputs.bits(t["x"]), inputs.bits(t["weight"]), w.eps, cfg,
+                                      inputs.bits(t["residual"]))
+    x, r, wt = t["x"].cuda(), t["residual"].cuda(), t["weight"].cuda()
+    run_fused(x, r, wt, w.eps, h=r, out=x)
+    assert np.array_equal(inputs.bits(r), h_want)
+    parity.compare(inputs.bits(x), y_want, e, gamma)
+    x = torch.zeros(2, 81920, dtype=BF16, device="cuda")
+    wt = torch.ones(81920, dtype=BF16, device="cuda")
+    out = torch.empty_like(x)
+    L, s = mbr.lib(), torch.cuda.current_stream().cuda_stream
+    INV = mbr.RMSNORM_ERR_INVALID_ARG
+    for c in (mbr.Config(mbr.PATH_VECTOR_LDS, 16, 10, 1, 0),     # nothing left for LDS
+              mbr.Config(mbr.PATH_VECTOR_LDS, 16, 8, 1, 0),      # not built
+              mbr.Config(mbr.PATH_VECTOR_LDS, 8, 10, 1, 0),      # 16 waves per row only
+              mbr.Config(mbr.PATH_VECTOR_LDS, 16, 10, 2, 0)):    # one row per workgroup
+        assert L.rmsnorm_fwd_ex(x.data_ptr(), wt.data_ptr(), out.data_ptr(), 2, 81920, 1e-5, 1, ctypes.byref(c),
+                                s) == INV
+    big = torch.zeros(1, 163336, dtype=BF16, device="cuda")
+    wb = torch.ones(163336, dtype=BF16, device="cuda")
+    ob = torch.empty_like(big)
+    c = mbr.Config(mbr.PATH_VECTOR_LDS, 16, 10, 1, 0)  # one vector past the LDS limit
+    assert L.rmsnorm_fwd_ex(big.data_ptr(), wb.data_ptr(), ob.data_ptr(), 1, 163336, 1e-5, 1, ctypes.byref(c),
+                            s) == INV
+    assert L.rmsnorm_fwd_ex(big.data_ptr() + 2, wb.data_ptr(), ob.data_ptr(), 1, 163328, 1e-5, 1, ctypes.byref(c),
+                            s) == INV  # not 16-byte aligned
+    torch.cuda.synchronize()
+
+
 # ---------------------------------------------------------------- pointers
 
 
