@@ -66,7 +66,7 @@ import torch
 
 import memory_bound_rmsnorm_amd as mbr
 from memory_bound_rmsnorm_amd import _build, inputs
-from memory_bound_rmsnorm_amd.profile_summary import kv_launch, launch_dict
+from memory_bound_rmsnorm_amd.profile_summary import kernel_instances, launch_dict
 
 HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 MIN_FOOTPRINT = 2 << 30
@@ -364,19 +364,10 @@ def copy_ceiling(w, steps, warmup, graph=False):
     return 2 * nbytes / (ev / steps) / 1e9
 
 
-KERNEL_FAMILY = {"vector": "rms_vec_kernel", "element": "rms_elem_kernel", "two_pass": "rms_twopass_kernel"}
-BWD_KERNEL_FAMILY = {"vector": "rms_bwd_vec_kernel", "element": "rms_bwd_elem_kernel",
-                     "two_pass": "rms_bwd_twopass_kernel"}
-LN_KERNEL_FAMILY = {"vector": "ln_vec_kernel", "element": "ln_elem_kernel", "two_pass": "ln_multipass_kernel"}
-
-
 def load_traffic(w, launch):
     """HBM bytes per step from the committed counter summary, if it was taken
     on the current kernel sources in the current launch configuration; else None."""
-    if is_kv(w):
-        fam = {"vector": "kv_vec_kernel", "element": "kv_elem_kernel"}[launch["path"]]
-    else:
-        fam = (BWD_KERNEL_FAMILY if w.backward else LN_KERNEL_FAMILY if w.layernorm else KERNEL_FAMILY)[launch["path"]]
+    fam = kernel_instances(w)[0][0].split("<")[0].split("::")[1]
     path = os.path.join(PROFILE_DIR, "pmc_traffic_%s_%s.txt" % (fam, w.name))
     if not os.path.exists(path):
         return None

@@ -165,7 +165,19 @@ LN_WORKLOADS: Dict[str, Workload] = {
                  note="LayerNorm, small fp32 case at hidden 768"),
     ]
 }
-ALL_WORKLOADS: Dict[str, Workload] = dict(WORKLOADS, **QUANT_WORKLOADS, **BWD_WORKLOADS, **LN_WORKLOADS)
+# Rows wider than the register path holds (131072 elements, 256 KiB per bf16
+# row), plain and fused: the register + LDS path, read once.
+WIDE_WORKLOADS: Dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("bf16_wide_2048x131072", "bf16", 2048, 131072, 1e-5, False, N01, W_N,
+                 note="rows past the register budget"),
+        Workload("bf16_wide_residual_2048x131072", "bf16", 2048, 131072, 1e-5, True, N01, W_N, residual=N01,
+                 note="fused rows past the register budget"),
+    ]
+}
+ALL_WORKLOADS: Dict[str, Workload] = dict(WORKLOADS, **QUANT_WORKLOADS, **BWD_WORKLOADS, **LN_WORKLOADS,
+                                          **WIDE_WORKLOADS)
 
 
 def _draw(rng: np.random.Generator, d: Dist, shape) -> np.ndarray:

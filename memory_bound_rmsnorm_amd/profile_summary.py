@@ -86,6 +86,9 @@ def kernel_instances(w):
                                              ("int", qt), ("int", lpr)])]
     if path == 2:
         return [_instance("rms_elem_kernel", [e, ("int", wpr), ("int", per), ("bool", w.fused), ("int", qt)])]
+    if path == 5:  # rms_stage_kernel<E, RV, CH, FUSED>, CH as rmsnorm_misc.hip instantiates it
+        ch = {(False, 10): 10, (True, 6): 5, (True, 7): 4}[(w.fused, per)]
+        return [_instance("rms_stage_kernel", [e, ("int", per), ("int", ch), ("bool", w.fused)])]
     return [_instance("rms_twopass_kernel", [e, ("bool", True), ("bool", w.fused), ("int", qt)])]
 
 
