@@ -159,7 +159,7 @@ typedef struct {
                                a multiple of 64 and at most 512 */
     int32_t weight_lds;     /* 0 or 1.  1: VECTOR path with whole-wave rows only; each
                                workgroup copies the weight into LDS once (hidden * size
-                               bytes, at most 60 KiB) and its rows take it from there
+                               bytes, at most 159 KiB) and its rows take it from there
                                instead of from global memory.  The results are bitwise the
                                same either way.  layernorm_fwd_ex: gamma and beta staged
                                the same way.  Must be 0 for rmsnorm_bwd_ex */
@@ -296,13 +296,13 @@ RMSNORM_API rmsnorm_status_t rmsnorm_bwd(const void* x, const void* weight, cons
 /* rmsnorm_bwd with a launch configuration (NULL or path AUTO = automatic).
  * rows_per_block > 1 is accepted on path VECTOR only (64 * waves_per_row *
  * rows_per_block threads within the limit of rmsnorm_config_t; with dweight,
- * hidden * 4 bytes of LDS at most 60 KiB): the rows of a workgroup's slots then
+ * hidden * 4 bytes of LDS at most 159 KiB): the rows of a workgroup's slots then
  * share one partial dweight row.  max_blocks caps the grid and is the number
  * of partial dweight rows (0 = no cap).  lanes_per_row 8, 16 or 32 (rows of at
  * most 2 * lanes_per_row vectors; waves_per_row 1, items_per_lane 1 or 2;
  * lanes_per_row * rows_per_block a multiple of 64, at most 512): several rows
  * per wave, each taking one row slot; with dweight and more than one wave per
- * workgroup, hidden * 4 bytes of LDS, at most 60 KiB. */
+ * workgroup, hidden * 4 bytes of LDS, at most 159 KiB. */
 RMSNORM_API rmsnorm_status_t rmsnorm_bwd_ex(const void* x, const void* weight, const void* dy, void* dx,
                                             void* dweight, int64_t rows, int64_t hidden, float eps,
                                             rmsnorm_dtype_t dtype, void* workspace, size_t workspace_bytes,
@@ -367,7 +367,7 @@ RMSNORM_API rmsnorm_status_t layernorm_fwd(const void* x, const void* gamma, con
 /* layernorm_fwd with a launch configuration (NULL or path AUTO = automatic;
  * path TWO_PASS selects the three-pass wide-row kernel).  weight_lds (gamma
  * and beta staged in LDS once per workgroup, hidden * size bytes each, at most
- * 60 KiB together) is taken on path VECTOR only; rows_per_block > 1 requires
+ * 159 KiB together) is taken on path VECTOR only; rows_per_block > 1 requires
  * it (the row slots share that copy), with 64 * waves_per_row *
  * rows_per_block within the limit of rmsnorm_config_t.  lanes_per_row 8, 16
  * or 32 (weight_lds 0): several rows per wave, each taking one row slot and

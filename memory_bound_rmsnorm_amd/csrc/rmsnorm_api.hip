@@ -28,9 +28,14 @@ namespace {
 constexpr int64_t kVectorBytes = 16;
 // Largest grid launched in one call; bigger jobs loop inside the kernel.
 constexpr int64_t kMaxGrid = int64_t(1) << 20;
-// Most LDS a forward workgroup may take for a staged weight (the rest of the
-// 64 KiB it can address holds its row totals).
-constexpr size_t kWeightLdsMax = 60 * 1024;
+// Most dynamic LDS a workgroup may take for a staged weight (gamma and beta
+// for LayerNorm) or the backward's slot combine: a gfx950 workgroup can take
+// 160 KiB (the device reports 163840 bytes per block), less 1 KiB kept for
+// the kernels' own row totals.
+constexpr size_t kWeightLdsMax = 160 * 1024 - 1024;
+// The LayerNorm automatic choice stages gamma and beta only within the window
+// its sweeps covered (60 KiB together).
+constexpr size_t kLnStageAutoMax = 60 * 1024;
 // Workgroup size when rows narrower than half a wave share waves: one wave.
 // Sweeps on MI355X (HIP-graph timing): bf16 [262144, 128] runs in 23.3 us as
 // 16 lanes x 1 vector x 4 rows per 64-lane workgroup, against 62.8 us with a
@@ -432,8 +437,8 @@ int64_t bwd_ld(int64_t hidden) { return (hidden + 63) / 64 * 64; }
 constexpr int64_t kBwdGrid = 512;
 
 // LDS the backward vector kernel may take for combining its row slots' sums
-// (the rest of the 64 KiB a workgroup can address holds its row totals).
-constexpr size_t kBwdCombineLds = 60 * 1024;
+// (the 160 KiB a gfx950 workgroup can take, less 1 KiB for its row totals).
+constexpr size_t kBwdCombineLds = 160 * 1024 - 1024;
 
 // Partial dweight rows (= workgroups of the walk) for a configuration: one per
 // group of rows_per_block rows, at most max_blocks.
@@ -851,7 +856,7 @@ rmsnorm_config_t choose_ln(int64_t rows, int64_t hidden, int dtype, bool aligned
     // bf16 with beta): [8192, 4096] 25.0 us as 2 x 4 x 4 slots against 26.4,
     // [4096, 4096] 12.5 against 14.5, [4096, 8192] 25.7 (4 x 4 x 2) against
     // 28.8, [2048, 8192] 11.9 (2 x 8 x 4) against 16.5.
-    if (vec && units >= 384 && units * kVectorBytes * 2 <= int64_t(kWeightLdsMax)) {
+    if (vec && units >= 384 && units * kVectorBytes * 2 <= int64_t(kLnStageAutoMax)) {
         int w = 0, v = 0;
         if (rows >= 4096) {
             int64_t best_pad = -1;

@@ -88,7 +88,7 @@ def test_choice_is_built_and_covering(dtype, aligned, rows):
         lanes = c.lanes_per_row or 64 * c.waves_per_row
         assert c.max_blocks >= 1 and c.waves_per_row in (1, 2, 4, 8, 16)
         assert c.rows_per_block == 1 or (c.path == mbr.PATH_VECTOR and lanes * c.rows_per_block <= 512
-                                         and hidden * 4 <= 60 * 1024)
+                                         and hidden * 4 <= 159 * 1024)
         if c.lanes_per_row:  # rows narrower than a wave: whole waves per workgroup
             assert c.path == mbr.PATH_VECTOR and c.lanes_per_row in (8, 16, 32) and c.waves_per_row == 1
             assert c.items_per_lane in (1, 2) and lanes * c.rows_per_block % 64 == 0
@@ -154,10 +154,8 @@ def test_bad_forced_configs():
         n = mbr.rmsnorm_bwd_workspace_size(rows, 128, torch.bfloat16, cfg)
         st = L.rmsnorm_bwd_ex(X, W, G, D, DW, rows, 128, 1e-5, 1, WS, n, ctypes.byref(cfg), None)
         assert st == INV, cfg.as_dict()
-    # slots combine dweight in LDS: hidden * 4 bytes, at most 60 KiB
-    cfg = mbr.Config(mbr.PATH_VECTOR, 4, 8, 2, 0)
-    n = mbr.rmsnorm_bwd_workspace_size(rows, 16384, torch.bfloat16, cfg)
-    assert L.rmsnorm_bwd_ex(X, W, G, D, DW, rows, 16384, 1e-5, 1, WS, n, ctypes.byref(cfg), None) == INV
+    # slots combine dweight in LDS (hidden * 4 bytes, at most 159 KiB): every
+    # built multi-slot configuration fits (512 lanes of at most 8 vectors: 64 KiB)
     # vector path on an unaligned buffer
     cfg = mbr.Config(mbr.PATH_VECTOR, 8, 1, 1, 0)
     st = L.rmsnorm_bwd_ex(X + 2, W, G, D, None, rows, hidden, 1e-5, 1, None, 0, ctypes.byref(cfg), None)

@@ -151,7 +151,7 @@ def test_bwd_rows_per_block_configs(dtype):
         for rpb in {1: (2, 3, 8), 2: (2, 4), 4: (2,)}.get(wpr, ()):
             lanes = 64 * wpr
             for nvec in sorted({lanes * vpl, max(1, lanes * (vpl - 1) + 3)}):
-                if nvec * vecw * 4 > 60 * 1024:
+                if nvec * vecw * 4 > 159 * 1024:
                     continue  # the LDS combine limit (checked on the CPU)
                 for mb, rows in ((0, rpb + 1), (2, 5 * rpb + 2), (0, 1)):
                     cfg = mbr.Config(mbr.PATH_VECTOR, wpr, vpl, rpb, mb)

@@ -107,7 +107,7 @@ def test_ln_gamma_beta_in_lds(dtype):
             for nvec in sorted({lanes * vpl, max(1, lanes * vpl - 37)}):
                 for rpb, mb in sorted({(1, 0), (max_rpb, 0), (max_rpb, 2)}):
                     bias = n % 2 == 0
-                    if nvec * 16 * (2 if bias else 1) > 60 * 1024:
+                    if nvec * 16 * (2 if bias else 1) > 159 * 1024:
                         continue
                     rows = 2 * rpb + 1
                     w = inputs.custom(rows, nvec * vecw, dtype, layernorm=True)

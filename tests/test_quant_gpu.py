@@ -132,7 +132,7 @@ def test_weight_in_lds_matches_bitwise(dtype, fused, q):
         lanes = 64 * wpr
         max_rpb = (1024 if wpr == 16 else 512) // lanes
         for nvec in sorted({lanes * vpl, max(1, lanes * vpl - 37)}):
-            if nvec * 16 > 60 * 1024:
+            if nvec * 16 > 159 * 1024:
                 continue
             for rpb, mb in sorted({(1, 0), (max_rpb, 0), (max_rpb, 2)}):
                 rows = 2 * rpb + 1
