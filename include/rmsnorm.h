@@ -144,8 +144,14 @@ typedef enum {
 typedef struct {
     int32_t path;           /* rmsnorm_path_t */
     int32_t waves_per_row;  /* 64-lane waves cooperating on one row: 1, 2, 4, 8 or 16 */
-    int32_t items_per_lane; /* VECTOR: 16-byte vectors per lane, one of 1-8, 10, 12, 14, 16;
-                               ELEMENT: elements per lane, one of 1, 2, 4, 8, 16;
+    int32_t items_per_lane; /* VECTOR: 16-byte vectors per lane.  Built for
+                               rmsnorm_fwd_ex: 1-8, and 10 at 16 waves per row;
+                               rmsnorm_residual_fwd_ex: 1-5, 1-6 at 16 waves.
+                               VECTOR_ANY: vectors per lane, 1-5; at 16 waves 1-6
+                               (1-4 fused).  ELEMENT: elements per lane; only rows
+                               narrower than one 16-byte vector take this path, so
+                               only 1 element with waves_per_row 1 is built.  The
+                               other entry points state their own built sets;
                                VECTOR_LDS: vectors per lane held in VGPRs (see above);
                                TWO_PASS: ignored (0) */
     int32_t rows_per_block; /* rows per workgroup; 64 * waves_per_row * rows_per_block <= 512
@@ -238,8 +244,8 @@ RMSNORM_API rmsnorm_status_t rmsnorm_dynamic_quant_fwd(const void* x, const void
                                                       rmsnorm_quant_t qtype, void* stream);
 
 /* As rmsnorm_dynamic_quant_fwd with an explicit launch configuration; the
- * quantised kernels are built for at most 8 vectors (or elements) per lane,
- * 4 with 16 waves per row (VECTOR_ANY: 1-8 vectors, 4 with 16 waves). */
+ * quantised kernels are built for 1-5 vectors per lane, 1-4 with 16 waves per
+ * row (VECTOR and VECTOR_ANY), and ELEMENT 1 element with waves_per_row 1. */
 RMSNORM_API rmsnorm_status_t rmsnorm_dynamic_quant_fwd_ex(const void* x, const void* residual,
                                                          const void* weight, void* residual_out,
                                                          void* q_out, float* scale_out, int64_t rows,
@@ -302,7 +308,9 @@ RMSNORM_API rmsnorm_status_t rmsnorm_bwd(const void* x, const void* weight, cons
  * most 2 * lanes_per_row vectors; waves_per_row 1, items_per_lane 1 or 2;
  * lanes_per_row * rows_per_block a multiple of 64, at most 512): several rows
  * per wave, each taking one row slot; with dweight and more than one wave per
- * workgroup, hidden * 4 bytes of LDS, at most 159 KiB. */
+ * workgroup, hidden * 4 bytes of LDS, at most 159 KiB.  Built: VECTOR 1-8
+ * vectors per lane with one wave per row, 1-6 with 2-8 waves, 1-4 with 16;
+ * VECTOR_ANY 1-6, 1-3 with 16 waves; ELEMENT 1 element with waves_per_row 1. */
 RMSNORM_API rmsnorm_status_t rmsnorm_bwd_ex(const void* x, const void* weight, const void* dy, void* dx,
                                             void* dweight, int64_t rows, int64_t hidden, float eps,
                                             rmsnorm_dtype_t dtype, void* workspace, size_t workspace_bytes,
@@ -371,7 +379,9 @@ RMSNORM_API rmsnorm_status_t layernorm_fwd(const void* x, const void* gamma, con
  * it (the row slots share that copy), with 64 * waves_per_row *
  * rows_per_block within the limit of rmsnorm_config_t.  lanes_per_row 8, 16
  * or 32 (weight_lds 0): several rows per wave, each taking one row slot and
- * holding its gamma / beta slice in registers. */
+ * holding its gamma / beta slice in registers.  Built: VECTOR and VECTOR_ANY
+ * 1-8 vectors per lane (16 waves per row: 1-4 and 1-3); ELEMENT 1 element with
+ * waves_per_row 1. */
 RMSNORM_API rmsnorm_status_t layernorm_fwd_ex(const void* x, const void* gamma, const void* beta, void* out,
                                               int64_t rows, int64_t hidden, float eps, rmsnorm_dtype_t dtype,
                                               const rmsnorm_config_t* cfg, void* stream);

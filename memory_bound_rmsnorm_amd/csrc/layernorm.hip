@@ -49,10 +49,17 @@ const void* const* lany_table(std::index_sequence<I...>) {
     return table;
 }
 
+template <class E, int WPR, int EPL>
+const void* lelem_ptr() {
+    if constexpr (ln_elem_built(WPR, EPL))
+        return reinterpret_cast<const void*>(&ln_elem_kernel<E, WPR, EPL>);
+    else
+        return nullptr;
+}
+
 template <class E, size_t... I>
 const void* const* lelem_table(std::index_sequence<I...>) {
-    static const void* const table[] = {
-        reinterpret_cast<const void*>(&ln_elem_kernel<E, kWprList[I / kNumLnEpl], kLnEplList[I % kNumLnEpl]>)...};
+    static const void* const table[] = {lelem_ptr<E, kWprList[I / kNumLnEpl], kLnEplList[I % kNumLnEpl]>()...};
     return table;
 }
 

@@ -166,7 +166,8 @@ int stage_rv(int64_t nvec, bool fused) {
 // (fused [12289, 8192]: 128.5 us against 132.3 as 8 x 2).  The quantised forms
 // store half as many bytes per vector and hold the weight anyway; they run
 // fastest with up to four (five fused) vectors per lane: 4 x 4 for hidden
-// 8192, 2 x 5 for the fused 5120.  Element path: at most 8 elements per lane.  When rows are few,
+// 8192, 2 x 5 for the fused 5120.  Element path (rows narrower than one
+// vector): one wave, one element per lane.  When rows are few,
 // each row gets more waves so the whole GPU has work.  Rows that no built
 // register-resident configuration covers take the two-pass path.
 rmsnorm_config_t choose(int64_t rows, int64_t hidden, int dtype, bool aligned, bool fused, int qt) {
@@ -474,8 +475,8 @@ bool bwd_vector_aligned(const BwdProblem& p) {
 // several rows per wave; workgroups of four waves (eight with one vector per
 // lane), fewer row slots while there would be under 256 groups of rows; 512
 // workgroups.  bf16 [262144, 128]: 37.7 us against 151.7 with a wave per row.
-// Element path: at least four waves per row (when a row has two elements per
-// lane to spread), up to eight elements per lane.
+// Element path (rows narrower than one vector): one wave, one element per
+// lane.
 rmsnorm_config_t choose_bwd(int64_t rows, int64_t hidden, int dtype, bool aligned) {
     rmsnorm_config_t c = {RMSNORM_PATH_TWO_PASS, 16, 0, 1, static_cast<int32_t>(kBwdGrid), 0, 0};
     const bool vec = aligned && hidden % vec_elems(dtype) == 0;

@@ -42,10 +42,17 @@ const void* const* bsub_tables(bool masked, bool dw, std::index_sequence<I...> s
                   : (dw ? bsub_table<E, false, true>(s) : bsub_table<E, false, false>(s));
 }
 
+template <class E, int WPR, int EPL, bool DW>
+const void* belem_ptr() {
+    if constexpr (bwd_elem_built(WPR, EPL))
+        return reinterpret_cast<const void*>(&rms_bwd_elem_kernel<E, WPR, EPL, DW>);
+    else
+        return nullptr;
+}
+
 template <class E, bool DW, size_t... I>
 const void* const* belem_table(std::index_sequence<I...>) {
-    static const void* const table[] = {reinterpret_cast<const void*>(
-        &rms_bwd_elem_kernel<E, kWprList[I / kNumBwdEpl], kBwdEplList[I % kNumBwdEpl], DW>)...};
+    static const void* const table[] = {belem_ptr<E, kWprList[I / kNumBwdEpl], kBwdEplList[I % kNumBwdEpl], DW>()...};
     return table;
 }
 

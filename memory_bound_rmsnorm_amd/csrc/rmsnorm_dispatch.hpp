@@ -6,11 +6,18 @@
 
 namespace mbr {
 
-// Built configurations.  Vector path: waves per row x 16-byte vectors per lane
-// (1-8 plus the multiples that make common hidden sizes exact: 640 vectors =
-// 64 x 10 for bf16 5120, 896 = 64 x 14 for 7168, 768 = 64 x 12 for 6144).
+// Built configurations: the ones the automatic choices (forward, quantised,
+// backward, LayerNorm) can pick, plus one sweep set -- the plain forward
+// vector kernels at every waves-per-row below 16 with up to 8 vectors per
+// lane -- for launch-shape sweeps of the hot path through the _ex entry
+// points.  A lane of a 1024-lane workgroup has 128 VGPRs, of a narrower one
+// 256; nothing is built that would spill.
+//
+// Vector path: waves per row x 16-byte vectors per lane.  Below 16 waves the
+// choice keeps at most 5 vectors per lane (plain rows up to 8 when four rows
+// share an LDS copy of the weight); 16 waves take what registers allow.
 constexpr int kWprList[] = {1, 2, 4, 8, 16};
-constexpr int kVplList[] = {1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16};
+constexpr int kVplList[] = {1, 2, 3, 4, 5, 6, 7, 8, 10};
 constexpr int kEplList[] = {1, 2, 4, 8, 16};
 constexpr int kNumWpr = sizeof(kWprList) / sizeof(int);
 constexpr int kNumVpl = sizeof(kVplList) / sizeof(int);
@@ -18,25 +25,24 @@ constexpr int kNumEpl = sizeof(kEplList) / sizeof(int);
 
 constexpr int max_threads_for(int wpr) { return wpr == 16 ? 1024 : 512; }
 
-// A 1024-lane workgroup leaves each lane 128 VGPRs, narrower ones 256; the
-// configurations below are the ones whose registers fit without scratch
-// spills (the others are not built).
 constexpr bool vec_built(int wpr, int vpl, bool fused) {
-    return wpr < 16 ? !(fused && vpl == 16) : vpl <= (fused ? 6 : 10);
+    return fused ? vpl <= (wpr < 16 ? 5 : 6) : vpl <= (wpr < 16 ? 8 : 10);
 }
-constexpr bool elem_built(int wpr, int epl) { return wpr < 16 || epl <= 8; }
+// Element path: only rows narrower than one 16-byte vector take it, as one
+// wave with one element per lane.
+constexpr bool elem_built(int wpr, int epl) { return wpr == 1 && epl == 1; }
 // Quantised forms (int8 / fp8 codes plus a per-row scale) also hold the weight
-// slice, so lanes carry at most 8 vectors (4 in a 1024-lane workgroup).
-constexpr bool qvec_built(int wpr, int vpl) { return vpl <= 8 && (wpr < 16 || vpl <= 4); }
-constexpr bool qelem_built(int wpr, int epl) { return epl <= 8 && (wpr < 16 || epl <= 4); }
+// slice; the choice keeps at most 5 vectors per lane (4 at 16 waves).
+constexpr bool qvec_built(int wpr, int vpl) { return vpl <= (wpr < 16 ? 5 : 4); }
+constexpr bool qelem_built(int wpr, int epl) { return elem_built(wpr, epl); }
 
 // Any-alignment vector path (rows of any width at any element alignment):
 // full 16-byte vectors per lane, plus a tail of single elements.
 constexpr int kAnyVplList[] = {1, 2, 3, 4, 5, 6, 7, 8};
 constexpr int kNumAnyVpl = sizeof(kAnyVplList) / sizeof(int);
-constexpr bool any_built(int wpr, int vpl, bool fused) { return wpr < 16 || vpl <= (fused ? 4 : 6); }
+constexpr bool any_built(int wpr, int vpl, bool fused) { return vpl <= (wpr < 16 ? 5 : fused ? 4 : 6); }
 // Its quantised forms hold the weight slice as well, as on the vector path.
-constexpr bool qany_built(int wpr, int vpl) { return wpr < 16 || vpl <= 4; }
+constexpr bool qany_built(int wpr, int vpl) { return vpl <= (wpr < 16 ? 5 : 4); }
 
 // Host-side kernel handles (addresses of the __global__ stubs), or nullptr.
 // dtype: 0 = f32, 1 = bf16.
@@ -76,18 +82,22 @@ const void* subwave_kernel(int dtype, bool fused, int qt, bool masked, int lpr_i
 // Backward (dx, and dweight through per-workgroup partial rows): the lane
 // holds x, dy and the weight slice (plus fp32 column sums when dweight is
 // wanted), so the vector path carries at most 8 vectors per lane (4 in a
-// 1024-lane workgroup) and the element path at most 8 elements.
+// 1024-lane workgroup); the element path, as in the forward, only takes rows
+// narrower than one vector.
 constexpr int kBwdVplList[] = {1, 2, 3, 4, 5, 6, 7, 8};
 constexpr int kBwdEplList[] = {1, 2, 4, 8};
 constexpr int kNumBwdVpl = sizeof(kBwdVplList) / sizeof(int);
 constexpr int kNumBwdEpl = sizeof(kBwdEplList) / sizeof(int);
-constexpr bool bwd_vec_built(int wpr, int vpl) { return wpr < 16 || vpl <= 4; }
+// One wave holds a whole row of up to 8 vectors; the balanced rule keeps at
+// most 6 per lane.
+constexpr bool bwd_vec_built(int wpr, int vpl) { return vpl <= (wpr == 1 ? 8 : wpr < 16 ? 6 : 4); }
+constexpr bool bwd_elem_built(int wpr, int epl) { return wpr == 1 && epl == 1; }
 
 const void* bwd_vec_kernel(int dtype, bool dw, bool masked, int wpr_index, int vpl_index);
 const void* bwd_elem_kernel(int dtype, bool dw, int wpr_index, int epl_index);
 // Any width and element alignment, in vectors (kBwdVplList); it also holds
 // its tail values, so 16 waves per row take at most 3 vectors per lane.
-constexpr bool bwd_any_built(int wpr, int vpl) { return wpr < 16 || vpl <= 3; }
+constexpr bool bwd_any_built(int wpr, int vpl) { return vpl <= (wpr < 16 ? 6 : 3); }
 const void* bwd_any_kernel(int dtype, bool dw, bool masked, int wpr_index, int vpl_index);
 // Backward vector kernel with rows narrower than a wave (kLprList lanes per
 // row, kSwVplList vectors per lane, one wave per row slot group).
@@ -97,11 +107,12 @@ const void* bwd_dw_kernel(int dtype);
 
 // LayerNorm: the row and the per-vector gamma / beta live in registers; up to
 // 8 vectors per lane (4 in a 1024-lane workgroup, whose lanes have 128 VGPRs)
-// are built spill-free, elements up to 8 per lane; wider rows take the
-// multi-pass path.
+// are built spill-free; wider rows take the multi-pass path, rows narrower
+// than one vector the one-element-per-lane kernel.
 constexpr int kLnVplList[] = {1, 2, 3, 4, 5, 6, 7, 8};
 constexpr bool ln_vec_built(int wpr, int vpl) { return wpr < 16 || vpl <= 4; }
 constexpr int kLnEplList[] = {1, 2, 4, 8};
+constexpr bool ln_elem_built(int wpr, int epl) { return wpr == 1 && epl == 1; }
 constexpr int kNumLnVpl = sizeof(kLnVplList) / sizeof(int);
 constexpr int kNumLnEpl = sizeof(kLnEplList) / sizeof(int);
 

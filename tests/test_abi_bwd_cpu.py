@@ -8,6 +8,7 @@ import torch
 
 import memory_bound_rmsnorm_amd as mbr
 from tests.test_abi_cpu import HEADERS, _declared, fake_only
+from tests import built
 
 INV = mbr.RMSNORM_ERR_INVALID_ARG
 
@@ -95,14 +96,14 @@ def test_choice_is_built_and_covering(dtype, aligned, rows):
             assert rows >= 1024 and hidden // v <= 64
         if c.path == mbr.PATH_VECTOR:
             assert aligned and hidden % v == 0
-            assert c.items_per_lane in range(1, 9) and (c.waves_per_row < 16 or c.items_per_lane <= 4)
+            assert c.lanes_per_row or built.bwd_vec(c.waves_per_row, c.items_per_lane)
             assert lanes * c.items_per_lane >= hidden // v
         elif c.path == mbr.PATH_VECTOR_ANY:
             assert (not aligned or hidden % v != 0) and hidden >= v and c.rows_per_block == 1
-            assert c.items_per_lane in range(1, 9) and (c.waves_per_row < 16 or c.items_per_lane <= 3)
+            assert built.bwd_any(c.waves_per_row, c.items_per_lane)
             assert lanes * c.items_per_lane >= hidden // v
         elif c.path == mbr.PATH_ELEMENT:
-            assert c.items_per_lane in (1, 2, 4, 8) and lanes * c.items_per_lane >= hidden
+            assert built.elem(c.waves_per_row, c.items_per_lane) and lanes * c.items_per_lane >= hidden
             assert hidden < v
         else:
             assert c.path == mbr.PATH_TWO_PASS and hidden > 8 * 1024

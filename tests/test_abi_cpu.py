@@ -11,6 +11,7 @@ import torch
 
 import memory_bound_rmsnorm_amd as mbr
 from memory_bound_rmsnorm_amd import _build, inputs
+from tests import built
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
@@ -239,20 +240,17 @@ def test_selection_is_always_a_built_covering_config(hidden, rows, dtype, aligne
     if cfg.path == mbr.PATH_VECTOR:
         assert aligned and hidden % vec == 0
         assert 64 * cfg.waves_per_row * cfg.items_per_lane >= hidden // vec
-        assert cfg.items_per_lane in (1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16)
-        if cfg.waves_per_row == 16:
-            assert cfg.items_per_lane <= (6 if fused else 10)
+        assert built.vec(cfg.waves_per_row, cfg.items_per_lane, fused)
     elif cfg.path == mbr.PATH_VECTOR_ANY:
         # any width of at least one vector, any element alignment: full
         # vectors per lane, the rest as a tail of single elements
         assert not (aligned and hidden % vec == 0) and hidden >= vec
         assert 64 * cfg.waves_per_row * cfg.items_per_lane >= hidden // vec
-        assert cfg.items_per_lane in range(1, 9) and cfg.rows_per_block == 1 and cfg.max_blocks == 0
-        if cfg.waves_per_row == 16:
-            assert cfg.items_per_lane <= (4 if fused else 6)
+        assert built.any_(cfg.waves_per_row, cfg.items_per_lane, fused)
+        assert cfg.rows_per_block == 1 and cfg.max_blocks == 0
     elif cfg.path == mbr.PATH_ELEMENT:
         assert 64 * cfg.waves_per_row * cfg.items_per_lane >= hidden
-        assert cfg.items_per_lane in (1, 2, 4, 8, 16)
+        assert built.elem(cfg.waves_per_row, cfg.items_per_lane)
         assert hidden < vec  # a row of at least one vector takes a vector path
     elif cfg.path == mbr.PATH_VECTOR_LDS:
         # past the register path: 1024 lanes, a register part plus at least
@@ -357,15 +355,15 @@ def test_quant_argument_validation():
 def test_quant_selection_is_always_built(hidden, rows, dtype, fused):
     cfg = mbr.rmsnorm_select_quant_config(rows, hidden, dtype, True, fused)
     if cfg.path == mbr.PATH_VECTOR:
-        assert cfg.items_per_lane <= (4 if cfg.waves_per_row == 16 else 8)
+        assert cfg.lanes_per_row or built.qvec(cfg.waves_per_row, cfg.items_per_lane)
         assert 64 * cfg.waves_per_row * cfg.items_per_lane * (4 if dtype == torch.float32 else 8) >= hidden
     elif cfg.path == mbr.PATH_VECTOR_ANY:
         v = 4 if dtype == torch.float32 else 8
         assert hidden % v != 0 and hidden >= v and cfg.rows_per_block == 1 and cfg.lanes_per_row == 0
-        assert cfg.items_per_lane <= (4 if cfg.waves_per_row == 16 else 8)
+        assert built.qany(cfg.waves_per_row, cfg.items_per_lane)
         assert 64 * cfg.waves_per_row * cfg.items_per_lane >= hidden // v
     elif cfg.path == mbr.PATH_ELEMENT:
-        assert cfg.items_per_lane <= (4 if cfg.waves_per_row == 16 else 8)
+        assert built.elem(cfg.waves_per_row, cfg.items_per_lane)
         assert 64 * cfg.waves_per_row * cfg.items_per_lane >= hidden
     else:
         assert cfg.path == mbr.PATH_TWO_PASS

@@ -4,6 +4,7 @@ import torch
 
 import memory_bound_rmsnorm_amd as mbr
 from tests.test_abi_cpu import HEADERS, _declared, fake_only
+from tests import built
 
 INV = mbr.RMSNORM_ERR_INVALID_ARG
 
@@ -48,14 +49,14 @@ def test_choice_is_built_and_covering(dtype, aligned, rows):
             assert c.rows_per_block == 1
         if c.path == mbr.PATH_VECTOR:
             assert aligned and hidden % v == 0 and lanes * c.items_per_lane >= hidden // v
-            assert c.items_per_lane in range(1, 9) and (c.waves_per_row < 16 or c.items_per_lane <= 4)
+            assert c.lanes_per_row or built.ln_vec(c.waves_per_row, c.items_per_lane)
         elif c.path == mbr.PATH_VECTOR_ANY:
             # any width of at least one vector, any element alignment
             assert not (aligned and hidden % v == 0) and hidden >= v
             assert lanes * c.items_per_lane >= hidden // v and c.rows_per_block == 1 and not c.weight_lds
-            assert c.items_per_lane in range(1, 9) and (c.waves_per_row < 16 or c.items_per_lane <= 3)
+            assert built.ln_any(c.waves_per_row, c.items_per_lane)
         elif c.path == mbr.PATH_ELEMENT:
-            assert c.items_per_lane in (1, 2, 4, 8) and lanes * c.items_per_lane >= hidden
+            assert built.elem(c.waves_per_row, c.items_per_lane) and lanes * c.items_per_lane >= hidden
             assert hidden < v  # a row of at least one vector takes a vector path
         else:
             assert c.path == mbr.PATH_TWO_PASS and hidden > 8 * 1024

@@ -19,6 +19,7 @@ import torch
 import memory_bound_rmsnorm_amd as mbr
 from memory_bound_rmsnorm_amd import inputs
 from tests import parity
+from tests import built
 
 pytestmark = pytest.mark.gpu
 
@@ -120,7 +121,7 @@ def test_bwd_many_rows_per_workgroup():
 
 
 def _built_vec():
-    return [(wpr, vpl) for wpr in (1, 2, 4, 8, 16) for vpl in range(1, 9) if wpr < 16 or vpl <= 4]
+    return [(wpr, vpl) for wpr in built.WPR for vpl in built.BWD_VPL if built.bwd_vec(wpr, vpl)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -136,7 +137,7 @@ def test_bwd_every_vector_config(dtype):
                 say("bwd vector", dtype, cfg, "hidden", nvec * vecw, "rows", rows)
                 check(w, inputs.make(w, seed=n), cfg, want_dw=(n % 3 != 2))
                 n += 1
-    assert n > 150
+    assert n == 180
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -213,17 +214,21 @@ def test_bwd_rows_per_block_many_groups_deterministic():
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_bwd_every_element_config(dtype):
+    """The one built element configuration (one wave, one element per lane)
+    at every width it covers that matters: below one vector, as chosen, and
+    up to a whole wave."""
     n = 0
-    for wpr in (1, 2, 4, 8, 16):
-        for epl in (1, 2, 4, 8):
-            lanes = 64 * wpr
-            for hidden in sorted({lanes * epl, max(1, lanes * epl - 5), lanes * (epl - 1) + 1 if epl > 1 else 3}):
+    for wpr in built.WPR:
+        for epl in built.BWD_EPL:
+            if not built.elem(wpr, epl):
+                continue
+            for hidden in (1, 2, 3, 5, 7, 33, 59, 64):
                 cfg = mbr.Config(mbr.PATH_ELEMENT, wpr, epl, 1, 2 if n % 2 else 0)
                 w = inputs.custom(5, hidden, dtype, backward=True)
                 say("bwd element", dtype, cfg, "hidden", hidden)
                 check(w, inputs.make(w, seed=n), cfg, want_dw=(n % 4 != 3))
                 n += 1
-    assert n > 40
+    assert n == 8
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -439,9 +444,9 @@ def test_bwd_every_any_alignment_config(dtype):
     offsets from a 16-byte boundary, with and without dweight and a grid cap."""
     v = 8 if dtype == "bf16" else 4
     n = 0
-    for wpr in (1, 2, 4, 8, 16):
-        for vpl in range(1, 9):
-            if wpr == 16 and vpl > 3:
+    for wpr in built.WPR:
+        for vpl in built.BWD_VPL:
+            if not built.bwd_any(wpr, vpl):
                 continue
             lanes = 64 * wpr
             for nvec in sorted({lanes * vpl, max(1, lanes * (vpl - 1) + 3)}):
@@ -452,7 +457,7 @@ def test_bwd_every_any_alignment_config(dtype):
                 say("bwd any", dtype, cfg.as_dict(), "hidden", nvec * v + tail, "offsets", off, woff)
                 _run_bwd_any(dtype, 5, nvec * v + tail, cfg, off, woff, 6000 + n, want_dw=n % 5 != 4)
                 n += 1
-    assert n == 70
+    assert n == 54
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])

@@ -20,6 +20,7 @@ import memory_bound_rmsnorm_amd as mbr
 from memory_bound_rmsnorm_amd import inputs
 from tests import parity
 from tests.test_oracle_pins import _read_golden
+from tests import built
 
 pytestmark = pytest.mark.gpu
 
@@ -75,9 +76,9 @@ def test_ln_ragged_shapes(rows, hidden, dtype):
 def test_ln_every_vector_config(dtype):
     vecw = 8 if dtype == "bf16" else 4
     n = 0
-    for wpr in (1, 2, 4, 8, 16):
-        for vpl in range(1, 9):
-            if wpr == 16 and vpl > 4:
+    for wpr in built.WPR:
+        for vpl in built.LN_VPL:
+            if not built.ln_vec(wpr, vpl):
                 continue
             lanes = 64 * wpr
             for nvec in sorted({lanes * vpl, max(1, lanes * vpl - 37), lanes * (vpl - 1) + 1}):
@@ -98,9 +99,9 @@ def test_ln_gamma_beta_in_lds(dtype):
     to the per-row-load kernel, and within the oracle's bound."""
     vecw = 8 if dtype == "bf16" else 4
     n = 0
-    for wpr in (1, 2, 4, 8, 16):
-        for vpl in range(1, 9):
-            if wpr == 16 and vpl > 4:
+    for wpr in built.WPR:
+        for vpl in built.LN_VPL:
+            if not built.ln_vec(wpr, vpl):
                 continue
             lanes = 64 * wpr
             max_rpb = (1024 if wpr == 16 else 512) // lanes
@@ -164,10 +165,13 @@ def test_ln_subwave_configs(dtype):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_ln_every_element_and_multipass_config(dtype):
     n = 0
-    for wpr in (1, 2, 4, 8, 16):
-        lanes = 64 * wpr
-        for epl in (1, 2, 4, 8):
-            for hidden in sorted({lanes * epl, max(1, lanes * epl - 5), lanes * (epl - 1) + 1 if epl > 1 else 3}):
+    for wpr in built.WPR:
+        for epl in built.LN_EPL:
+            if not built.elem(wpr, epl):
+                continue
+            # the one built element configuration: below one vector (as
+            # chosen) and up to the whole wave it covers
+            for hidden in (1, 2, 3, 5, 7, 33, 59, 64):
                 cfg = mbr.Config(mbr.PATH_ELEMENT, wpr, epl, 1, 2 if n % 2 else 0)
                 w = inputs.custom(5, hidden, dtype, layernorm=True)
                 say("ln element", dtype, cfg, "hidden", hidden)
@@ -301,9 +305,9 @@ def test_ln_every_any_alignment_config(dtype):
     es = 2 if dtype == "bf16" else 4
     L = mbr.lib()
     n = 0
-    for wpr in (1, 2, 4, 8, 16):
-        for vpl in range(1, 9):
-            if wpr == 16 and vpl > 3:
+    for wpr in built.WPR:
+        for vpl in built.ANY_VPL:
+            if not built.ln_any(wpr, vpl):
                 continue
             lanes = 64 * wpr
             for nvec in sorted({lanes * vpl, max(1, lanes * (vpl - 1) + 3)}):

@@ -21,6 +21,7 @@ import torch
 import memory_bound_rmsnorm_amd as mbr
 from memory_bound_rmsnorm_amd import inputs
 from tests import parity
+from tests import built
 
 pytestmark = pytest.mark.gpu
 
@@ -150,14 +151,10 @@ def test_many_rows_in_kernel_loop(subwave):
 
 def _configs(path, dtype, fused):
     vec = path == mbr.PATH_VECTOR
-    per_list = (1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16) if vec else (1, 2, 4, 8, 16)
-    for wpr in (1, 2, 4, 8, 16):
-        for per in per_list:
-            if wpr == 16 and per > ((6 if fused else 10) if vec else 8):
-                continue
-            if vec and fused and per == 16:
-                continue
-            yield wpr, per
+    for wpr in built.WPR:
+        for per in (built.VEC_VPL if vec else built.EPL):
+            if built.vec(wpr, per, fused) if vec else built.elem(wpr, per):
+                yield wpr, per
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -189,7 +186,9 @@ def test_every_element_config(dtype, fused):
     for wpr, epl in _configs(mbr.PATH_ELEMENT, dtype, fused):
         lanes = 64 * wpr
         max_rpb = (1024 if wpr == 16 else 512) // lanes
-        for hidden in sorted({lanes * epl, max(1, lanes * epl - 5), lanes * (epl - 1) + 1 if epl > 1 else 3}):
+        # the one built element configuration: below one vector (as chosen)
+        # and up to the whole wave it covers
+        for hidden in (1, 2, 3, 5, 7, 33, 59, 64):
             rpb = max_rpb if n % 2 else 1
             rows = 2 * rpb + 1
             cfg = mbr.Config(mbr.PATH_ELEMENT, wpr, epl, rpb, 0)
@@ -197,7 +196,7 @@ def test_every_element_config(dtype, fused):
             say("element", dtype, fused, cfg, "hidden", hidden, "rows", rows)
             check_workload(w, inputs.make(w, seed=n), cfg)
             n += 1
-    assert n > 40
+    assert n == 8
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -432,9 +431,9 @@ def test_every_any_alignment_config(dtype, fused):
     and V - 1 elements past a 16-byte boundary."""
     v = 8 if dtype == "bf16" else 4
     n = 0
-    for wpr in (1, 2, 4, 8, 16):
-        for vpl in range(1, 9):
-            if wpr == 16 and vpl > (4 if fused else 6):
+    for wpr in built.WPR:
+        for vpl in built.ANY_VPL:
+            if not built.any_(wpr, vpl, fused):
                 continue
             lanes = 64 * wpr
             for nvec in sorted({lanes * vpl, max(1, lanes * (vpl - 1) + 3)}):
@@ -444,7 +443,7 @@ def test_every_any_alignment_config(dtype, fused):
                 say("any", dtype, fused, cfg, "hidden", nvec * v + tail, "offset", off)
                 _run_any(dtype, 5, nvec * v + tail, fused, cfg, off, 4000 + n)
                 n += 1
-    assert n > 70
+    assert n == (48 if fused else 52)
 
 
 def test_misaligned_fused():

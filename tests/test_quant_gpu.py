@@ -13,6 +13,7 @@ import torch
 import memory_bound_rmsnorm_amd as mbr
 from memory_bound_rmsnorm_amd import inputs
 from tests import parity
+from tests import built
 
 pytestmark = pytest.mark.gpu
 BF16, F32 = torch.bfloat16, torch.float32
@@ -76,11 +77,10 @@ def test_ragged_shapes(rows, hidden, dtype, fused, q):
 
 def _qconfigs(path):
     vec = path == mbr.PATH_VECTOR
-    for wpr in (1, 2, 4, 8, 16):
-        for per in ((1, 2, 3, 4, 5, 6, 7, 8) if vec else (1, 2, 4, 8)):
-            if wpr == 16 and per > 4:
-                continue
-            yield wpr, per
+    for wpr in built.WPR:
+        for per in (built.VEC_VPL if vec else built.EPL):
+            if built.qvec(wpr, per) if vec else built.elem(wpr, per):
+                yield wpr, per
 
 
 @pytest.mark.parametrize("q", ["int8", "fp8"])
@@ -101,13 +101,12 @@ def test_every_quant_config(dtype, fused, q):
                 check(w, inputs.make(w, seed=n), QT[q], cfg)
                 n += 1
     for wpr, epl in _qconfigs(mbr.PATH_ELEMENT):
-        lanes = 64 * wpr
-        hidden = max(1, lanes * epl - 5)
-        cfg = mbr.Config(mbr.PATH_ELEMENT, wpr, epl, 1, 0)
-        w = inputs.custom(3, hidden, dtype, fused)
-        say("quant element", q, dtype, fused, cfg, "hidden", hidden)
-        check(w, inputs.make(w, seed=n), QT[q], cfg)
-        n += 1
+        for hidden in (3, 7, 59):
+            cfg = mbr.Config(mbr.PATH_ELEMENT, wpr, epl, 1, 0)
+            w = inputs.custom(3, hidden, dtype, fused)
+            say("quant element", q, dtype, fused, cfg, "hidden", hidden)
+            check(w, inputs.make(w, seed=n), QT[q], cfg)
+            n += 1
     for wpr in (1, 4, 16):
         for hidden in (4096, 4099):
             cfg = mbr.Config(mbr.PATH_TWO_PASS, wpr, 0, 1, 0)
@@ -316,9 +315,9 @@ def test_every_any_alignment_quant_config(dtype, fused, q):
     at several offsets from a 16-byte boundary."""
     v = 8 if dtype == "bf16" else 4
     n = 0
-    for wpr in (1, 2, 4, 8, 16):
-        for vpl in range(1, 9):
-            if wpr == 16 and vpl > 4:
+    for wpr in built.WPR:
+        for vpl in built.ANY_VPL:
+            if not built.qany(wpr, vpl):
                 continue
             lanes = 64 * wpr
             for nvec in sorted({lanes * vpl, max(1, lanes * (vpl - 1) + 3)}):
@@ -329,7 +328,7 @@ def test_every_any_alignment_quant_config(dtype, fused, q):
                 say("quant any", q, dtype, fused, cfg, "hidden", nvec * v + tail, "offsets", off, qoff)
                 _run_any_quant(dtype, 5, nvec * v + tail, fused, QT[q], cfg, off, qoff, 5000 + n)
                 n += 1
-    assert n == 72
+    assert n == 48
 
 
 @pytest.mark.parametrize("q", ["int8", "fp8"])
