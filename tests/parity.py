@@ -114,11 +114,26 @@ def _round_keys(v: np.ndarray, bf16: bool) -> np.ndarray:
     return _keys(r)
 
 
+def _half_ulp(v: np.ndarray, bf16: bool) -> np.ndarray:
+    """Half the spacing of the output format at |v| (the spacing above v at a
+    power of two), subnormals included."""
+    mant, lo = (7, -133) if bf16 else (23, -149)
+    a = np.abs(v)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return 0.5 * np.maximum(2.0 ** (e - mant), 2.0 ** lo)
+
+
 def check_rounded(got: np.ndarray, exact: np.ndarray, tol, hidden: int, what: str = "y",
                   stats: dict = None) -> dict:
     """Every element of got (bf16 patterns or float32) must be the nearest-even
     rounding of some value within tol (absolute, scalar or per element) plus the
-    oracle's own fp64 error of exact (the oracle's unrounded value)."""
+    oracle's own fp64 error of exact (the oracle's unrounded value).
+
+    Besides the counts, the result reports max_bound_used: over all elements,
+    how much of the bound the element needed, (|got - exact| - half an ulp of
+    got) / bound, floored at 0 -- an element that is exactly the nearest-even
+    rounding of exact needs none of it."""
     bf16 = got.dtype == np.uint16
     g = np.ascontiguousarray(got).reshape(-1)
     e = np.ascontiguousarray(exact, dtype=np.float64).reshape(-1)
@@ -128,6 +143,7 @@ def check_rounded(got: np.ndarray, exact: np.ndarray, tol, hidden: int, what: st
     n_bad = n_diff = 0
     first = None
     worst = 0.0
+    used = 0.0
     for a in range(0, g.size, _CHUNK):
         gc, ec, tc = g[a:a + _CHUNK], e[a:a + _CHUNK], t_all[a:a + _CHUNK]
         gnan = _bf16_is_nan(gc) if bf16 else np.isnan(gc)
@@ -153,7 +169,12 @@ def check_rounded(got: np.ndarray, exact: np.ndarray, tol, hidden: int, what: st
         with np.errstate(invalid="ignore", divide="ignore"):
             d = np.abs(kg - kw)
             worst = max(worst, float(d.max()) if d.size else 0.0)
-    res = {"n": int(g.size), "differ_from_nearest_even": n_diff, "max_ulp_from_nearest_even": int(worst)}
+            gv = _values(gc)
+            need = np.maximum(np.abs(gv - ec) - _half_ulp(gv, bf16), 0.0)
+            u = np.where(need > 0, need / np.where(t > 0, t, np.inf), 0.0)
+            used = max(used, float(u.max()) if u.size else 0.0)
+    res = {"n": int(g.size), "differ_from_nearest_even": n_diff, "max_ulp_from_nearest_even": int(worst),
+           "max_bound_used": round(used, 4)}
     if stats is not None:
         stats[what + "_rounding"] = res
     if n_bad:
