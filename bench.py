@@ -32,9 +32,13 @@ Default run (the headline workload): before the headline's own warm-up the
 other four stated configurations are measured -- fp32 [64, 2048], bf16
 [4096, 2048], bf16 [256, 4096] and the fused bf16 [12289, 5120] -- each with
 its launches captured in a HIP graph that cycles through enough rotating sets
-to stay HBM-cold, 20 replays timed one by one (median, minimum, p90 per call);
-then the copy ceiling, after 100 ms of copies.  They go into the line as
-per_config.  Measured on MI355X, the first ~20 ms of a burst of launches run
+to stay HBM-cold, 20 replays timed one by one (median, minimum, p90 per call),
+plus, for those whose bytes fit the cache easily (C1-C3), a cache-resident
+figure with one set reused by every launch (labelled as such, never an HBM
+figure); then the copy ceiling, after 100 ms of copies, and the runtime's own
+device-to-device copy (hipMemcpyAsync) of the same bytes as a second ceiling.
+The configurations go into the line as per_config; the device (name, arch,
+compute units, torch and HIP versions) as device.  Measured on MI355X, the first ~20 ms of a burst of launches run
 slower than the steady state (bf16 [16384, 8192]: 87.2 us per call after 20
 launches, 84.7 after 300); the ceiling is a steady-state figure, and taking it
 right before the headline means the headline's W warm-up steps also start on
@@ -364,6 +368,30 @@ def copy_ceiling(w, steps, warmup, graph=False):
     return 2 * nbytes / (ev / steps) / 1e9
 
 
+def memcpy_ceiling(w, steps, warmup):
+    """The runtime's own device-to-device copy (hipMemcpyAsync, through torch's
+    copy_ of contiguous same-type tensors) of the same byte count, rotated the
+    same way, timed as eager calls between HIP events: a second ceiling beside
+    the hand-written copy kernel."""
+    nbytes = w.copy_bytes
+    n = max(2, -(-MIN_FOOTPRINT // (2 * nbytes)))
+    src = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(i % 251) for i in range(n)]
+    dst = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(n)]
+    copy = lambda i: dst[i % n].copy_(src[i % n])  # noqa: E731
+    warm_for(copy, COPY_WARM_SECONDS)
+    _, ev, _ = time_steps(copy, steps, warmup)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ev / steps) / 1e9
+
+
+def device_info():
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2 ** 30, 1), "torch": torch.__version__,
+            "hip": getattr(torch.version, "hip", None)}
+
+
 def load_traffic(w, launch):
     """HBM bytes per step from the committed counter summary, if it was taken
     on the current kernel sources in the current launch configuration; else None."""
@@ -516,6 +544,7 @@ def bench_workload(w, steps, warmup, seed, with_copy=True, graph=False, timed_gr
     if with_copy:
         # the copy ceiling first: the same read/write byte count, rotated and timed the same way
         rec["copy_ceiling_gbps"] = copy_ceiling(w, max(20, steps // 2), max(2, warmup // 2), graph=timed_graph)
+        rec["memcpy_ceiling_gbps"] = memcpy_ceiling(w, max(20, steps // 2), max(2, warmup // 2))
     if timed_graph:
         # eager launches first, for the record; the timed steps are a graph replay
         _, ev_e, _ = time_steps(sets.launch, steps, warmup)
@@ -539,10 +568,15 @@ def bench_workload(w, steps, warmup, seed, with_copy=True, graph=False, timed_gr
         rec["gbps_graph"] = nbytes / gs / 1e9
     if with_copy:
         rec["frac_of_copy_ceiling"] = rec["gbps_kernel"] / rec["copy_ceiling_gbps"]
+        rec["frac_of_memcpy_ceiling"] = rec["gbps_kernel"] / rec["memcpy_ceiling_gbps"]
     del sets
     torch.cuda.empty_cache()
     return t, rec
 
+
+# Workloads whose bytes fit comfortably in the 256 MB last-level cache also
+# get a cache-resident figure in per_config.
+CACHE_RESIDENT_MAX = 64 << 20
 
 # The other stated configurations, measured in the default run (per_config).
 STATED = {"C1": "fp32_64x2048", "C2": "bf16_prefill_4096x2048", "C3": "bf16_decode_256x4096",
@@ -558,13 +592,22 @@ def measure_config(w, seed, samples=20):
     for i in range(2 * n_sets):  # first launches: module load, clocks
         sets.launch(i)
     per, launches = graph_samples(sets.launch, n_sets, samples)
+    warm = None
+    if w.algorithmic_bytes <= CACHE_RESIDENT_MAX:
+        # the same buffers every launch: cache-resident, not an HBM figure
+        wper, wl = graph_samples(lambda i: sets.launch(0), 1, samples)
+        warm = {"us_median": round(statistics.median(wper) * 1e6, 3), "launches_per_sample": wl,
+                "note": "one input/output set reused by every launch: cache-resident, not HBM bandwidth"}
     del sets, t
     torch.cuda.empty_cache()
     med = statistics.median(per)
     gbps = w.algorithmic_bytes / med / 1e9
-    return dict({"workload": w.name, "dtype": w.dtype}, **shape, algorithmic_bytes=w.algorithmic_bytes,
-                rotation_sets=n_sets, gbps=round(gbps, 2), frac=round(gbps / HBM_PEAK_GBPS, 4),
-                launch=launch_dict(w), **spread_us(per, launches))
+    rec = dict({"workload": w.name, "dtype": w.dtype}, **shape, algorithmic_bytes=w.algorithmic_bytes,
+               rotation_sets=n_sets, gbps=round(gbps, 2), frac=round(gbps / HBM_PEAK_GBPS, 4),
+               launch=launch_dict(w), **spread_us(per, launches))
+    if warm:
+        rec["cache_resident"] = warm
+    return rec
 
 
 def describe(w):
@@ -657,6 +700,9 @@ def main():
     if "copy_ceiling_gbps" in rec:
         line["copy_ceiling_gbps"] = round(rec["copy_ceiling_gbps"], 2)
         line["frac_of_copy_ceiling"] = round(rec["frac_of_copy_ceiling"], 4)
+        line["memcpy_ceiling_gbps"] = round(rec["memcpy_ceiling_gbps"], 2)
+        line["frac_of_memcpy_ceiling"] = round(rec["frac_of_memcpy_ceiling"], 4)
+    line["device"] = device_info()
     if per_config:
         line["per_config"] = dict(per_config, note="measured before the headline: graph replays over rotating "
                                                    "sets (HBM-cold), per call; parity by tests/test_parity_gpu.py::"
