@@ -51,18 +51,28 @@
 
 #define RMSNORM_API __attribute__((visibility("default")))
 
+/* The enums below are 32-bit integers at the boundary.  C++ sees them with a
+ * fixed int32_t underlying type, so any 32-bit value a caller passes is a
+ * value of the type (rejected by validation when unknown) rather than an
+ * out-of-range enum, whose mere load C++ leaves undefined. */
+#ifdef __cplusplus
+#define RMSNORM_ENUM_BASE : int32_t
+#else
+#define RMSNORM_ENUM_BASE
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-typedef enum {
+typedef enum RMSNORM_ENUM_BASE {
     RMSNORM_OK = 0,
     RMSNORM_ERR_INVALID_ARG = 1,       /* null pointer, bad size, bad eps, bad overlap, bad config */
     RMSNORM_ERR_UNSUPPORTED_DTYPE = 2, /* dtype not one of rmsnorm_dtype_t */
     RMSNORM_ERR_RUNTIME = 3            /* the HIP launch reported an error */
 } rmsnorm_status_t;
 
-typedef enum {
+typedef enum RMSNORM_ENUM_BASE {
     RMSNORM_DTYPE_F32 = 0, /* IEEE binary32 */
     RMSNORM_DTYPE_BF16 = 1 /* bfloat16: upper 16 bits of a binary32 */
 } rmsnorm_dtype_t;
@@ -121,7 +131,7 @@ RMSNORM_API const char* rmsnorm_status_string(rmsnorm_status_t status);
  * may differ in the last bit through the fp32 reduction order.
  * ---------------------------------------------------------------------- */
 
-typedef enum {
+typedef enum RMSNORM_ENUM_BASE {
     RMSNORM_PATH_AUTO = 0,     /* let the library choose (the other fields are ignored) */
     RMSNORM_PATH_VECTOR = 1,   /* row in VGPRs, 16-byte loads/stores; needs 16-byte alignment */
     RMSNORM_PATH_ELEMENT = 2,  /* row in VGPRs, one element per access; any alignment */
@@ -202,7 +212,7 @@ RMSNORM_API rmsnorm_status_t rmsnorm_residual_fwd_ex(const void* x, const void* 
  * RMSNorm with dynamic per-row quantisation of its output.
  * ---------------------------------------------------------------------- */
 
-typedef enum {
+typedef enum RMSNORM_ENUM_BASE {
     RMSNORM_QUANT_INT8 = 0,     /* signed 8-bit codes in [-127, 127], Q = 127 */
     RMSNORM_QUANT_FP8_E4M3 = 1  /* OCP fp8 e4m3fn codes (bias 7, max 448, no inf), Q = 448 */
 } rmsnorm_quant_t;
