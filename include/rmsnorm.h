@@ -142,7 +142,13 @@ typedef enum RMSNORM_ENUM_BASE {
                                    layernorm_fwd_ex: any width of at least one
                                    vector and any element alignment; the row's full
                                    16-byte vectors at whatever alignment it has, then its last
-                                   hidden % (16 / size) elements one by one; rows_per_block 1 */
+                                   hidden % (16 / size) elements one by one; rows_per_block 1.
+                                   bf16 normalised output: a row that starts 2 bytes past a
+                                   4-byte boundary moves as the row one element earlier
+                                   (when x, out, residual and h share their offset modulo 4
+                                   and the configuration covers hidden + 1 elements); the
+                                   two bytes before the row, in the same 4-byte word, are
+                                   then read but never written */
     RMSNORM_PATH_VECTOR_LDS = 5 /* rmsnorm_fwd_ex / rmsnorm_residual_fwd_ex: rows wider than
                                    the register path holds, still read once: 1024 lanes
                                    (waves_per_row 16, rows_per_block 1), items_per_lane

@@ -140,6 +140,19 @@ bool vector_aligned(const Problem& p) {
     return true;  // codes: a 16-byte-aligned base keeps every row's 8- (4-) byte stores aligned
 }
 
+// Whether the any-alignment path's shifted frame can apply: normalised bf16
+// output, and x, out (and residual, h) at the same offset modulo 4 bytes, so
+// that every row's tensors share it; some row must start 2 bytes past a
+// 4-byte boundary (an odd width, or a base there).
+bool shifted_frame(const Problem& p) {
+    if (p.qt || p.dtype != RMSNORM_DTYPE_BF16) return false;
+    const uintptr_t m = reinterpret_cast<uintptr_t>(p.x) & 3;
+    if ((reinterpret_cast<uintptr_t>(p.out) & 3) != m) return false;
+    if (p.fused && ((reinterpret_cast<uintptr_t>(p.res) & 3) != m || (reinterpret_cast<uintptr_t>(p.h) & 3) != m))
+        return false;
+    return m != 0 || p.hidden % 2 != 0;
+}
+
 // Vectors per lane the register + LDS path holds in registers for a row of
 // nvec vectors, or 0 when the row does not fit it: the register part must
 // leave at least one vector for LDS, and the rest must fit the LDS limit.
@@ -176,7 +189,10 @@ rmsnorm_config_t choose(int64_t rows, int64_t hidden, int dtype, bool aligned, b
     // any other width or alignment: full vectors at the row's own alignment
     // plus a tail of single elements (every form)
     const bool any = !vec && hidden >= vec_elems(dtype);
-    const int64_t units = vec || any ? hidden / vec_elems(dtype) : hidden;
+    // the any-alignment path's shifted frame (bf16 rows that start 2 bytes
+    // past a 4-byte boundary) moves one more element per row
+    const int64_t frame_extra = any && !qt && dtype == RMSNORM_DTYPE_BF16 ? 1 : 0;
+    const int64_t units = vec || any ? (hidden + frame_extra) / vec_elems(dtype) : hidden;
     const int* list = vec ? mbr::kVplList : any ? mbr::kAnyVplList : mbr::kEplList;
     const int nlist = vec ? mbr::kNumVpl : any ? mbr::kNumAnyVpl : mbr::kNumEpl;
     const int cap = vec || any ? (qt ? (fused ? 5 : 4) : (fused ? 4 : 2)) : 8;
@@ -307,6 +323,7 @@ rmsnorm_status_t launch(const Problem& p, const rmsnorm_config_t* user, hipStrea
     a.scale = p.scale;
     a.w_lds = c.weight_lds;
     a.tail = 0;
+    a.frame = 0;
     size_t lds_bytes = 0;
 
     const void* fn = nullptr;
@@ -347,7 +364,11 @@ rmsnorm_status_t launch(const Problem& p, const rmsnorm_config_t* user, hipStrea
             if (nvec < 1 || vi < 0 || lanes_per_row * c.items_per_lane < nvec) return RMSNORM_ERR_INVALID_ARG;
             threads = lanes_per_row;
             if (threads > mbr::max_threads_for(c.waves_per_row)) return RMSNORM_ERR_INVALID_ARG;
-            const bool masked = lanes_per_row * c.items_per_lane != nvec;
+            // bf16 rows that start 2 bytes past a 4-byte boundary move in the
+            // shifted frame (one more element per row) when every row tensor
+            // shares that offset and the configuration covers the longer row
+            a.frame = shifted_frame(p) && lanes_per_row * c.items_per_lane >= (p.hidden + 1) / vec_elems(p.dtype);
+            const bool masked = a.frame || lanes_per_row * c.items_per_lane != nvec;
             fn = p.qt ? mbr::qany_kernel(p.dtype, p.qt, p.fused, masked, wi, vi)
                       : mbr::any_kernel(p.dtype, p.fused, masked, wi, vi);
             a.units = static_cast<int32_t>(nvec);

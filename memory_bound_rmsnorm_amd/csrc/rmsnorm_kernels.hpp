@@ -62,6 +62,9 @@ struct RowArgs {
     float* scale;        // quantised forms: one fp32 scale per row
     int32_t w_lds;       // vector path, normalised output: weight staged in LDS
     int32_t tail;        // any-alignment vector path: elements after the full vectors (< kVec)
+    int32_t frame;       // any-alignment vector path, bf16, normalised output: rows that
+                         // start 2 bytes past a 4-byte boundary move as the dword-aligned
+                         // row one element earlier (every row tensor shares that offset)
 };
 
 // ---------------------------------------------------------------- dtypes
@@ -513,6 +516,7 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_vec_kernel(const RowAr
 // alignment of the access's own elements; the compiler then issues one
 // global_load/store_dwordx4 as for an aligned vector.
 typedef u32x4 u32x4_any2 __attribute__((aligned(2)));
+typedef unsigned u32_any2 __attribute__((aligned(2)));
 
 __device__ __forceinline__ u32x4 load_stream_any(const char* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4_any2*>(p));
@@ -520,6 +524,17 @@ __device__ __forceinline__ u32x4 load_stream_any(const char* p) {
 __device__ __forceinline__ u32x4 load_keep_any(const char* p) { return *reinterpret_cast<const u32x4_any2*>(p); }
 __device__ __forceinline__ void store_stream_any(char* p, u32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4_any2*>(p));
+}
+
+// The 16 bytes of a vector at a 4-byte-aligned address except its first
+// element slot (two bytes): the shifted frame's first vector, whose first slot
+// lies before the row.
+__device__ __forceinline__ void store_after_first_slot(char* p, u32x4 v) {
+    *reinterpret_cast<uint16_t*>(p + 2) = static_cast<uint16_t>(v[0] >> 16);
+    unsigned* q = reinterpret_cast<unsigned*>(p + 4);
+    q[0] = v[1];
+    q[1] = v[2];
+    q[2] = v[3];
 }
 
 // Codes of one input vector at any byte offset: 8 bytes for bf16, 4 for fp32.
@@ -541,12 +556,20 @@ __device__ __forceinline__ void store_codes_any(char* p, const float (&t)[4], F3
 // elements is H / V full 16-byte vectors, moved at whatever alignment the row
 // starts at, and then H % V tail elements moved one by one.  Lane l of a row
 // owns vectors l, l + 64*WPR, ... (VPL of them) and, if l < H % V, tail
-// element l.  Every access stays inside the row, so nothing is read or
-// written past a row's end or the tensor's.  One row per workgroup at a
-// time; otherwise the vector path's reduction, rounding and output order.
-// The quantised forms (QT) hold the weight slice from the start, as on the
-// vector path, and write their codes at the row's byte offset in the code
-// tensor.
+// element l.  Nothing is written outside the row, nor read past a row's end
+// or the tensor's.  One row per workgroup at a time; otherwise the vector
+// path's reduction, rounding and output order.  The quantised forms (QT) hold
+// the weight slice from the start, as on the vector path, and write their
+// codes at the row's byte offset in the code tensor.
+//
+// Shifted frame (a.frame; bf16 normalised output, masked launches): 16-byte
+// accesses 2 bytes past a 4-byte boundary run far slower on gfx950 than
+// 4-byte-aligned ones, so a row that starts there is moved as the virtual row
+// of H + 1 elements one slot earlier, which starts 4-byte aligned.  The
+// virtual first slot is the two bytes before the row, in the same 4-byte word
+// as the row's first element: it is read, zeroed, and never written.  The
+// weight keeps its own alignment: each virtual vector takes the weight's own
+// vector and the two elements before it, shifted up one slot in registers.
 template <class E, int WPR, int VPL, bool MASKED, bool FUSED, int QT = 0>
 __global__ void __launch_bounds__(max_threads<WPR>()) rms_any_kernel(const RowArgs a) {
     using S = typename E::scalar;
@@ -555,6 +578,7 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_any_kernel(const RowAr
     constexpr int NR = FUSED ? VPL : 1;
     const int wave = wave_id();
     const int lane = static_cast<int>(threadIdx.x);
+    constexpr bool kFrame = QT == 0 && MASKED && sizeof(S) == 2;
     const int nvec = a.units;  // full vectors per row
     const int tail = a.tail;
     const int64_t row_elems = static_cast<int64_t>(nvec) * V + tail;
@@ -562,13 +586,16 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_any_kernel(const RowAr
     __shared__ float part[2][16];
     __shared__ float mpart[QT ? 2 : 1][QT ? 16 : 1];
 
+    // per row: sh = 1 in the shifted frame, nv full vectors, tl tail elements
+    int sh = 0, nv = nvec, tl = tail;
     auto voff = [&](int k) {
         const int v = k * LANES + lane;
-        return static_cast<int64_t>(MASKED ? (v < nvec ? v : nvec - 1) : v) * 16;
+        return static_cast<int64_t>(MASKED ? (v < nv ? v : nv - 1) : v) * 16;
     };
-    auto in_row = [&](int k) { return !MASKED || k * LANES + lane < nvec; };
-    const bool has_tail = lane < tail;
-    const int64_t toff = (static_cast<int64_t>(nvec) * V + lane) * static_cast<int64_t>(sizeof(S));
+    auto in_row = [&](int k) { return !MASKED || k * LANES + lane < nv; };
+    auto toff = [&]() { return (static_cast<int64_t>(nv) * V + lane) * static_cast<int64_t>(sizeof(S)); };
+    const bool has_tail_q = lane < tail;
+    const int64_t toff_q = (static_cast<int64_t>(nvec) * V + lane) * static_cast<int64_t>(sizeof(S));
 
     const char* wr = static_cast<const char*>(a.w);
     u32x4 wv[QT ? VPL : 1];
@@ -576,21 +603,31 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_any_kernel(const RowAr
     if constexpr (QT != 0) {
 #pragma unroll
         for (int k = 0; k < VPL; ++k) wv[k] = load_keep_any(wr + voff(k));
-        if (has_tail) wt = widen1(*reinterpret_cast<const S*>(wr + toff));
+        if (has_tail_q) wt = widen1(*reinterpret_cast<const S*>(wr + toff_q));
     }
     int it = 0;
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x, ++it) {
-        const char* xr = static_cast<const char*>(a.x) + row * row_bytes;
+        const char* xrow = static_cast<const char*>(a.x) + row * row_bytes;
+        if constexpr (kFrame) {
+            sh = a.frame && (reinterpret_cast<uintptr_t>(xrow) & 2) ? 1 : 0;
+            nv = static_cast<int>((row_elems + sh) / V);
+            tl = static_cast<int>((row_elems + sh) % V);
+        }
+        const int64_t back = sh * static_cast<int64_t>(sizeof(S));  // virtual row start, bytes before the row
+        const bool has_tail = lane < tl;
+        const char* xr = xrow - back;
         u32x4 d[VPL], rv[NR];
 #pragma unroll
         for (int k = 0; k < VPL; ++k) d[k] = load_stream_any(xr + voff(k));
+        if (sh && lane == 0) d[0][0] &= 0xffff0000u;  // the slot before the row
         float xt = 0.f;
-        if (has_tail) xt = widen1(*reinterpret_cast<const S*>(xr + toff));
+        if (has_tail) xt = widen1(*reinterpret_cast<const S*>(xr + toff()));
         if constexpr (FUSED) {
-            const char* rr = static_cast<const char*>(a.res) + row * row_bytes;
+            const char* rr = static_cast<const char*>(a.res) + row * row_bytes - back;
 #pragma unroll
             for (int k = 0; k < VPL; ++k) rv[k] = load_stream_any(rr + voff(k));
-            char* hr = static_cast<char*>(a.h) + row * row_bytes;
+            if (sh && lane == 0) rv[0][0] &= 0xffff0000u;
+            char* hr = static_cast<char*>(a.h) + row * row_bytes - back;
 #pragma unroll
             for (int k = 0; k < VPL; ++k) {
                 float fx[V], fr[V];
@@ -599,11 +636,15 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_any_kernel(const RowAr
 #pragma unroll
                 for (int i = 0; i < V; ++i) fx[i] += fr[i];
                 d[k] = narrow(fx, E{});  // h rounded once; the norm sees this value
-                if (in_row(k)) store_stream_any(hr + voff(k), d[k]);
+                if (!in_row(k)) continue;
+                if (k == 0 && sh && lane == 0)
+                    store_after_first_slot(hr, d[k]);
+                else
+                    store_stream_any(hr + voff(k), d[k]);
             }
             if (has_tail) {
-                const S ht = narrow1(xt + widen1(*reinterpret_cast<const S*>(rr + toff)), E{});
-                *reinterpret_cast<S*>(hr + toff) = ht;
+                const S ht = narrow1(xt + widen1(*reinterpret_cast<const S*>(rr + toff())), E{});
+                *reinterpret_cast<S*>(hr + toff()) = ht;
                 xt = widen1(ht);
             }
         }
@@ -661,20 +702,37 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_any_kernel(const RowAr
             if (has_tail) qr[nvec * V + lane] = static_cast<char>(quant_code<QT>((xt * wt) * inv));
             continue;
         }
-        char* outr = static_cast<char*>(a.out) + row * row_bytes;
+        char* outr = static_cast<char*>(a.out) + row * row_bytes - back;
+        const char* wv0 = wr - back;  // the weight one element back in the shifted frame
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             if (!in_row(k)) continue;
+            const bool first = k == 0 && sh && lane == 0;
+            // shifted frame: the weight's own vector v and the last two
+            // elements before it, moved up one slot in registers (both loads
+            // at the weight's alignment)
+            const u32x4 wa = load_keep_any(wr + voff(k));
+            u32x4 wk = wa;
+            if (sh) {
+                const unsigned before = first ? 0u : *reinterpret_cast<const u32_any2*>(wr + voff(k) - 4);
+                wk[0] = __builtin_amdgcn_alignbyte(wa[0], before, 2);
+                wk[1] = __builtin_amdgcn_alignbyte(wa[1], wa[0], 2);
+                wk[2] = __builtin_amdgcn_alignbyte(wa[2], wa[1], 2);
+                wk[3] = __builtin_amdgcn_alignbyte(wa[3], wa[2], 2);
+            }
             float f[V], fw[V];
             widen(d[k], f, E{});
-            widen(load_keep_any(wr + voff(k)), fw, E{});
+            widen(wk, fw, E{});
 #pragma unroll
             for (int i = 0; i < V; ++i) f[i] = f[i] * r * fw[i];
-            store_stream_any(outr + voff(k), narrow(f, E{}));
+            if (first)
+                store_after_first_slot(outr, narrow(f, E{}));
+            else
+                store_stream_any(outr + voff(k), narrow(f, E{}));
         }
         if (has_tail) {
-            const float wt = widen1(*reinterpret_cast<const S*>(wr + toff));
-            *reinterpret_cast<S*>(outr + toff) = narrow1(xt * r * wt, E{});
+            const float wt = widen1(*reinterpret_cast<const S*>(wv0 + toff()));
+            *reinterpret_cast<S*>(outr + toff()) = narrow1(xt * r * wt, E{});
         }
     }
 }

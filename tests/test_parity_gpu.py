@@ -446,6 +446,81 @@ def test_every_any_alignment_config(dtype, fused):
     assert n == (48 if fused else 52)
 
 
+def _run_any_offsets(rows, hidden, fused, offs, cfg=None, inplace=False, seed=0):
+    """bf16 rows through the any-alignment path with x, residual, h and out at
+    their own element offsets past a 16-byte boundary (inplace: out = x and
+    h = residual), automatic or forced configuration: parity with the oracle
+    and no byte outside the outputs written."""
+    w = inputs.custom(rows, hidden, "bf16", fused)
+    t = inputs.make(w, seed=seed)
+    n = rows * hidden
+    g = 64
+    bases = [g + offs[i] + i * (n + 2 * g) for i in range(4)]  # x, residual, h, out
+    if inplace:
+        bases[3], bases[2] = bases[0], bases[1]
+    buf = torch.zeros(4 * (n + 2 * g) + 2 * g, dtype=BF16, device="cuda")
+    buf[bases[0]:bases[0] + n] = t["x"].reshape(-1).cuda()
+    if fused:
+        buf[bases[1]:bases[1] + n] = t["residual"].reshape(-1).cuda()
+    wt = t["weight"].cuda()
+    ptr = [buf.data_ptr() + 2 * b for b in bases]
+    L = mbr.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    cfgp = ctypes.byref(cfg) if cfg is not None else None
+    if fused:
+        st = L.rmsnorm_residual_fwd_ex(ptr[0], ptr[1], wt.data_ptr(), ptr[2], ptr[3], rows, hidden, w.eps, 1, cfgp,
+                                       stream)
+    else:
+        st = L.rmsnorm_fwd_ex(ptr[0], wt.data_ptr(), ptr[3], rows, hidden, w.eps, 1, cfgp, stream)
+    torch.cuda.synchronize()
+    assert st == mbr.RMSNORM_OK, mbr.rmsnorm_status_string(st)
+    used = cfg if cfg is not None else mbr.rmsnorm_select_config(rows, hidden, BF16, False, fused)
+    cpu = inputs.bits(buf.cpu())
+    xb, wb = inputs.bits(t["x"]), inputs.bits(t["weight"])
+    h_want, y_want, e, gamma = expect(xb, wb, w.eps, used, inputs.bits(t["residual"]) if fused else None)
+    if fused:
+        assert np.array_equal(cpu[bases[2]:bases[2] + n].reshape(rows, hidden), h_want), "residual sum differs"
+    parity.compare(cpu[bases[3]:bases[3] + n].reshape(rows, hidden), y_want, e, gamma)
+    written = np.zeros(cpu.shape, bool)
+    for i in ((0, 1, 2, 3) if fused else (0, 3)):
+        written[bases[i]:bases[i] + n] = True
+    assert not np.any(cpu[~written] != 0), "a byte outside the buffers changed"
+
+
+# element offsets of (x, residual, h, out) past a 16-byte boundary: every row
+# tensor 2 bytes past a 4-byte boundary (shifted frame), 4-byte aligned but
+# not 16 (no shift), and mixed (x and out at different offsets modulo 4: the
+# frame is off and rows move at their own alignment)
+ANY_OFFSETS = [(0, 0, 0, 0), (1, 1, 1, 1), (3, 5, 7, 1), (2, 2, 6, 4), (1, 0, 0, 0), (0, 3, 1, 2), (5, 1, 1, 4)]
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("hidden", [9, 15, 17, 2049, 4095, 5121, 8191, 8193])
+def test_any_alignment_shifted_frame(hidden, fused):
+    """The any-alignment path's shifted frame: rows that start 2 bytes past a
+    4-byte boundary move as the dword-aligned row one element earlier.  Odd
+    widths (rows alternate between the two cases), every mix of tensor
+    offsets, in place, the automatic choice and forced configurations that
+    do and do not cover the longer shifted row."""
+    rows = 7
+    n = 0
+    for offs in ANY_OFFSETS:
+        say("any frame", hidden, fused, offs)
+        _run_any_offsets(rows, hidden, fused, offs, seed=hidden + n)
+        n += 1
+    say("any frame in place", hidden, fused)
+    _run_any_offsets(rows, hidden, fused, (1, 1, 1, 1), inplace=True, seed=hidden + 99)
+    _run_any_offsets(rows, hidden, fused, (0, 2, 2, 0), inplace=True, seed=hidden + 98)
+    nv = hidden // 8
+    for wpr in (1, 2, 4):
+        per = -(-nv // (64 * wpr))
+        if per < 1 or not built.any_(wpr, per, fused):
+            continue
+        cfg = mbr.Config(mbr.PATH_VECTOR_ANY, wpr, per, 1, 2)
+        say("any frame forced", hidden, fused, cfg)
+        _run_any_offsets(rows, hidden, fused, (1, 1, 1, 1), cfg=cfg, seed=hidden + 50 + wpr)
+
+
 def test_misaligned_fused():
     rows, hidden, eps = 17, 1024, 1e-5
     w = inputs.custom(rows, hidden, "bf16", True)
