@@ -140,14 +140,14 @@ bool vector_aligned(const Problem& p) {
     return true;  // codes: a 16-byte-aligned base keeps every row's 8- (4-) byte stores aligned
 }
 
-// Whether the any-alignment path's shifted frame can apply: normalised bf16
-// output, and x, out (and residual, h) at the same offset modulo 4 bytes, so
-// that every row's tensors share it; some row must start 2 bytes past a
-// 4-byte boundary (an odd width, or a base there).
+// Whether the any-alignment path's shifted frame can apply: bf16, and x (and
+// residual, h, and a normalised out; codes have no alignment) at the same
+// offset modulo 4 bytes, so that every row's tensors share it; some row must
+// start 2 bytes past a 4-byte boundary (an odd width, or a base there).
 bool shifted_frame(const Problem& p) {
-    if (p.qt || p.dtype != RMSNORM_DTYPE_BF16) return false;
+    if (p.dtype != RMSNORM_DTYPE_BF16) return false;
     const uintptr_t m = reinterpret_cast<uintptr_t>(p.x) & 3;
-    if ((reinterpret_cast<uintptr_t>(p.out) & 3) != m) return false;
+    if (!p.qt && (reinterpret_cast<uintptr_t>(p.out) & 3) != m) return false;
     if (p.fused && ((reinterpret_cast<uintptr_t>(p.res) & 3) != m || (reinterpret_cast<uintptr_t>(p.h) & 3) != m))
         return false;
     return m != 0 || p.hidden % 2 != 0;
@@ -191,7 +191,7 @@ rmsnorm_config_t choose(int64_t rows, int64_t hidden, int dtype, bool aligned, b
     const bool any = !vec && hidden >= vec_elems(dtype);
     // the any-alignment path's shifted frame (bf16 rows that start 2 bytes
     // past a 4-byte boundary) moves one more element per row
-    const int64_t frame_extra = any && !qt && dtype == RMSNORM_DTYPE_BF16 ? 1 : 0;
+    const int64_t frame_extra = any && dtype == RMSNORM_DTYPE_BF16 ? 1 : 0;
     const int64_t units = vec || any ? (hidden + frame_extra) / vec_elems(dtype) : hidden;
     const int* list = vec ? mbr::kVplList : any ? mbr::kAnyVplList : mbr::kEplList;
     const int nlist = vec ? mbr::kNumVpl : any ? mbr::kNumAnyVpl : mbr::kNumEpl;

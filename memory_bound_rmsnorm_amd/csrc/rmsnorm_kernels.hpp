@@ -547,6 +547,17 @@ __device__ __forceinline__ void store_codes_any(char* p, const float (&t)[8], Bf
     c[1] = quant_pack4<QT>(t[4], t[5], t[6], t[7]);
     __builtin_nontemporal_store(c, reinterpret_cast<u32x2_any1*>(p));
 }
+// The shifted frame's first vector of codes: every code but the first, whose
+// slot lies before the row.
+template <int QT>
+__device__ __forceinline__ void store_codes_after_first(char* p, const float (&t)[8]) {
+    const unsigned c0 = quant_pack4<QT>(t[0], t[1], t[2], t[3]);
+    const unsigned c1 = quant_pack4<QT>(t[4], t[5], t[6], t[7]);
+#pragma unroll
+    for (int b = 1; b < 4; ++b) p[b] = static_cast<char>(c0 >> (8 * b));
+#pragma unroll
+    for (int b = 0; b < 4; ++b) p[4 + b] = static_cast<char>(c1 >> (8 * b));
+}
 template <int QT>
 __device__ __forceinline__ void store_codes_any(char* p, const float (&t)[4], F32) {
     __builtin_nontemporal_store(quant_pack4<QT>(t[0], t[1], t[2], t[3]), reinterpret_cast<u32_any1*>(p));
@@ -578,7 +589,7 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_any_kernel(const RowAr
     constexpr int NR = FUSED ? VPL : 1;
     const int wave = wave_id();
     const int lane = static_cast<int>(threadIdx.x);
-    constexpr bool kFrame = QT == 0 && MASKED && sizeof(S) == 2;
+    constexpr bool kFrame = MASKED && sizeof(S) == 2;
     const int nvec = a.units;  // full vectors per row
     const int tail = a.tail;
     const int64_t row_elems = static_cast<int64_t>(nvec) * V + tail;
@@ -594,16 +605,57 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_any_kernel(const RowAr
     };
     auto in_row = [&](int k) { return !MASKED || k * LANES + lane < nv; };
     auto toff = [&]() { return (static_cast<int64_t>(nv) * V + lane) * static_cast<int64_t>(sizeof(S)); };
-    const bool has_tail_q = lane < tail;
-    const int64_t toff_q = (static_cast<int64_t>(nvec) * V + lane) * static_cast<int64_t>(sizeof(S));
-
     const char* wr = static_cast<const char*>(a.w);
+    const int64_t wbytes = row_elems * static_cast<int64_t>(sizeof(S));
+    // The weight's own 16-byte vector at byte offset wo.  In the shifted frame
+    // the last virtual vector of a row with H = 7 (mod 8) takes the weight's
+    // vector H / 8, which ends 2 bytes past the weight: its last two bytes are
+    // not read (and not used).
+    auto weight_vec = [&](int64_t wo) {
+        if (!kFrame || wo + 16 <= wbytes) return load_keep_any(wr + wo);
+        const u32_any2* p = reinterpret_cast<const u32_any2*>(wr + wo);
+        u32x4 v;
+        v[0] = p[0];
+        v[1] = p[1];
+        v[2] = p[2];
+        v[3] = *reinterpret_cast<const uint16_t*>(wr + wo + 12);
+        return v;
+    };
+    // ... moved up one element behind the last two elements before it (b: the
+    // 4 bytes before the vector, 0 for the first)
+    auto shift_weight = [](u32x4 w, unsigned b) {
+        u32x4 r;
+        r[0] = __builtin_amdgcn_alignbyte(w[0], b, 2);
+        r[1] = __builtin_amdgcn_alignbyte(w[1], w[0], 2);
+        r[2] = __builtin_amdgcn_alignbyte(w[2], w[1], 2);
+        r[3] = __builtin_amdgcn_alignbyte(w[3], w[2], 2);
+        return r;
+    };
+    auto weight_before = [&](int64_t wo) {
+        return wo == 0 ? 0u : *reinterpret_cast<const u32_any2*>(wr + wo - 4);
+    };
+
+    // Quantised forms hold the weight slice from the start: its own vectors
+    // (and, in the shifted frame, the 4 bytes before each and the tail weight
+    // of both frames), for every vector the longer virtual row can take.
+    const int nvw = kFrame && a.frame ? static_cast<int>((row_elems + 1) / V) : nvec;
+    auto woff = [&](int k) {
+        const int v = k * LANES + lane;
+        return static_cast<int64_t>(MASKED ? (v < nvw ? v : nvw - 1) : v) * 16;
+    };
     u32x4 wv[QT ? VPL : 1];
-    float wt = 0.f;
+    unsigned wb[QT && kFrame ? VPL : 1];
+    float wt0 = 0.f, wt1 = 0.f;
     if constexpr (QT != 0) {
 #pragma unroll
-        for (int k = 0; k < VPL; ++k) wv[k] = load_keep_any(wr + voff(k));
-        if (has_tail_q) wt = widen1(*reinterpret_cast<const S*>(wr + toff_q));
+        for (int k = 0; k < VPL; ++k) {
+            wv[k] = weight_vec(woff(k));
+            if constexpr (kFrame) wb[k] = a.frame ? weight_before(woff(k)) : 0u;
+        }
+        const int64_t t0 = static_cast<int64_t>(nvec) * V + lane;       // tail element, unshifted row
+        const int64_t t1 = static_cast<int64_t>(nvw) * V + lane - 1;    // and in the shifted frame
+        if (lane < tail) wt0 = widen1(reinterpret_cast<const S*>(wr)[t0]);
+        if (kFrame && a.frame && lane < (row_elems + 1) % V) wt1 = widen1(reinterpret_cast<const S*>(wr)[t1]);
     }
     int it = 0;
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x, ++it) {
@@ -648,8 +700,13 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_any_kernel(const RowAr
                 xt = widen1(ht);
             }
         }
+        const float wt = sh ? wt1 : wt0;
         float ss = xt * xt;
         float mx = QT != 0 ? fabsf(xt * wt) : 0.f;
+        auto qweight = [&](int k) {  // quantised forms: this row's weight vector k
+            if constexpr (QT != 0 && kFrame) return sh ? shift_weight(wv[k], wb[k]) : wv[k];
+            return wv[k];
+        };
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             float f[V];
@@ -660,7 +717,7 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_any_kernel(const RowAr
             ss += in_row(k) ? s : 0.f;
             if constexpr (QT != 0) {
                 float fw[V];
-                widen(wv[k], fw, E{});
+                widen(qweight(k), fw, E{});
                 float m = 0.f;
 #pragma unroll
                 for (int i = 0; i < V; ++i) m = fmaxf(m, fabsf(f[i] * fw[i]));
@@ -688,18 +745,24 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_any_kernel(const RowAr
         if constexpr (QT != 0) {
             const float inv = mx > 0.f ? quant_max<QT>() / mx : 0.f;
             if (lane == 0) a.scale[row] = r * mx / quant_max<QT>();
-            char* qr = static_cast<char*>(a.out) + row * row_elems;  // one byte per element
+            char* qr = static_cast<char*>(a.out) + row * row_elems - sh;  // one byte per element
 #pragma unroll
             for (int k = 0; k < VPL; ++k) {
                 if (!in_row(k)) continue;
                 float f[V], fw[V];
                 widen(d[k], f, E{});
-                widen(wv[k], fw, E{});
+                widen(qweight(k), fw, E{});
 #pragma unroll
                 for (int i = 0; i < V; ++i) f[i] = (f[i] * fw[i]) * inv;
+                if constexpr (kFrame) {
+                    if (k == 0 && sh && lane == 0) {
+                        store_codes_after_first<QT>(qr, f);
+                        continue;
+                    }
+                }
                 store_codes_any<QT>(qr + voff(k) / static_cast<int64_t>(sizeof(S)), f, E{});
             }
-            if (has_tail) qr[nvec * V + lane] = static_cast<char>(quant_code<QT>((xt * wt) * inv));
+            if (has_tail) qr[static_cast<int64_t>(nv) * V + lane] = static_cast<char>(quant_code<QT>((xt * wt) * inv));
             continue;
         }
         char* outr = static_cast<char*>(a.out) + row * row_bytes - back;
@@ -711,15 +774,8 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_any_kernel(const RowAr
             // shifted frame: the weight's own vector v and the last two
             // elements before it, moved up one slot in registers (both loads
             // at the weight's alignment)
-            const u32x4 wa = load_keep_any(wr + voff(k));
-            u32x4 wk = wa;
-            if (sh) {
-                const unsigned before = first ? 0u : *reinterpret_cast<const u32_any2*>(wr + voff(k) - 4);
-                wk[0] = __builtin_amdgcn_alignbyte(wa[0], before, 2);
-                wk[1] = __builtin_amdgcn_alignbyte(wa[1], wa[0], 2);
-                wk[2] = __builtin_amdgcn_alignbyte(wa[2], wa[1], 2);
-                wk[3] = __builtin_amdgcn_alignbyte(wa[3], wa[2], 2);
-            }
+            const u32x4 wa = weight_vec(voff(k));
+            const u32x4 wk = sh ? shift_weight(wa, weight_before(voff(k))) : wa;
             float f[V], fw[V];
             widen(d[k], f, E{});
             widen(wk, fw, E{});

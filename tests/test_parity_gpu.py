@@ -394,7 +394,9 @@ def _run_any(dtype, rows, hidden, fused, cfg, off, seed):
     n = rows * hidden
     g = 64  # guard elements around every region
     bases = [g + off + i * (n + 2 * g) for i in range(4)]  # x, residual, h, out
-    buf = torch.zeros(4 * (n + 2 * g) + 2 * g, dtype=td, device="cuda")
+    # guard space holds a non-zero pattern, so that a stray write of a zero
+    # (the value the shifted frame's slot before a row computes to) shows
+    buf = torch.full((4 * (n + 2 * g) + 2 * g,), 1.0, dtype=td, device="cuda")
     buf[bases[0]:bases[0] + n] = t["x"].reshape(-1).cuda()
     if fused:
         buf[bases[1]:bases[1] + n] = t["residual"].reshape(-1).cuda()
@@ -420,7 +422,7 @@ def _run_any(dtype, rows, hidden, fused, cfg, off, seed):
     written = np.zeros(cpu.shape, bool)
     for i in (0, 1, 2, 3) if fused else (0, 3):
         written[bases[i]:bases[i] + n] = True
-    assert not np.any(cpu[~written] != 0), "a byte outside the buffers changed"
+    assert np.all(cpu[~written] == inputs.bits(torch.ones(1, dtype=td))[0]), "a byte outside the buffers changed"
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -458,7 +460,7 @@ def _run_any_offsets(rows, hidden, fused, offs, cfg=None, inplace=False, seed=0)
     bases = [g + offs[i] + i * (n + 2 * g) for i in range(4)]  # x, residual, h, out
     if inplace:
         bases[3], bases[2] = bases[0], bases[1]
-    buf = torch.zeros(4 * (n + 2 * g) + 2 * g, dtype=BF16, device="cuda")
+    buf = torch.full((4 * (n + 2 * g) + 2 * g,), 1.0, dtype=BF16, device="cuda")  # non-zero guard pattern
     buf[bases[0]:bases[0] + n] = t["x"].reshape(-1).cuda()
     if fused:
         buf[bases[1]:bases[1] + n] = t["residual"].reshape(-1).cuda()
@@ -484,7 +486,7 @@ def _run_any_offsets(rows, hidden, fused, offs, cfg=None, inplace=False, seed=0)
     written = np.zeros(cpu.shape, bool)
     for i in ((0, 1, 2, 3) if fused else (0, 3)):
         written[bases[i]:bases[i] + n] = True
-    assert not np.any(cpu[~written] != 0), "a byte outside the buffers changed"
+    assert np.all(cpu[~written] == inputs.bits(torch.ones(1, dtype=BF16))[0]), "a byte outside the buffers changed"
 
 
 # element offsets of (x, residual, h, out) past a 16-byte boundary: every row

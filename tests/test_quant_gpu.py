@@ -273,12 +273,14 @@ def _run_any_quant(dtype, rows, hidden, fused, qtype, cfg, off, qoff, seed):
     n = rows * hidden
     g = 64
     bases = [g + off + i * (n + 2 * g) for i in range(3)]  # x, residual, h
-    buf = torch.zeros(3 * (n + 2 * g) + 2 * g, dtype=td, device="cuda")
+    # guard space holds non-zero patterns, so that a stray write of a zero
+    # (code or value) shows
+    buf = torch.full((3 * (n + 2 * g) + 2 * g,), 1.0, dtype=td, device="cuda")
     buf[bases[0]:bases[0] + n] = t["x"].reshape(-1).cuda()
     if fused:
         buf[bases[1]:bases[1] + n] = t["residual"].reshape(-1).cuda()
-    qbuf = torch.zeros(n + 2 * g, dtype=torch.uint8, device="cuda")
-    sbuf = torch.zeros(rows + 2, dtype=torch.float32, device="cuda")
+    qbuf = torch.full((n + 2 * g,), 0xA5, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((rows + 2,), -1.0, dtype=torch.float32, device="cuda")
     wt = t["weight"].cuda()
     p = buf.data_ptr()
     ptr = [p + es * b for b in bases]
@@ -301,9 +303,9 @@ def _run_any_quant(dtype, rows, hidden, fused, qtype, cfg, off, qoff, seed):
     written = np.zeros(cpu.shape, bool)
     for i in (0, 1, 2) if fused else (0,):
         written[bases[i]:bases[i] + n] = True
-    assert not np.any(cpu[~written] != 0), "a byte outside x, residual and h changed"
-    assert not np.any(q_all[:g + qoff] != 0) and not np.any(q_all[g + qoff + n:] != 0), "a code outside q changed"
-    assert s_all[0] == 0 and s_all[-1] == 0, "a scale outside the row range changed"
+    assert np.all(cpu[~written] == inputs.bits(torch.ones(1, dtype=td))[0]), "a byte outside x, residual and h changed"
+    assert np.all(q_all[:g + qoff] == 0xA5) and np.all(q_all[g + qoff + n:] == 0xA5), "a code outside q changed"
+    assert s_all[0] == -1.0 and s_all[-1] == -1.0, "a scale outside the row range changed"
 
 
 @pytest.mark.parametrize("q", ["int8", "fp8"])
