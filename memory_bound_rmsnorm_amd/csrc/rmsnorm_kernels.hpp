@@ -607,32 +607,26 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_any_kernel(const RowAr
     auto toff = [&]() { return (static_cast<int64_t>(nv) * V + lane) * static_cast<int64_t>(sizeof(S)); };
     const char* wr = static_cast<const char*>(a.w);
     const int64_t wbytes = row_elems * static_cast<int64_t>(sizeof(S));
-    // The weight's own 16-byte vector at byte offset wo.  In the shifted frame
-    // the last virtual vector of a row with H = 7 (mod 8) takes the weight's
-    // vector H / 8, which ends 2 bytes past the weight: its last two bytes are
-    // not read (and not used).
-    auto weight_vec = [&](int64_t wo) {
-        if (!kFrame || wo + 16 <= wbytes) return load_keep_any(wr + wo);
-        const u32_any2* p = reinterpret_cast<const u32_any2*>(wr + wo);
-        u32x4 v;
-        v[0] = p[0];
-        v[1] = p[1];
-        v[2] = p[2];
-        v[3] = *reinterpret_cast<const uint16_t*>(wr + wo + 12);
-        return v;
+    // Weight access in the shifted frame, without branches (a load inside a
+    // branch makes the compiler wait for every load in flight where the
+    // branch ends).  A virtual vector takes the weight's own vector at byte
+    // offset wo moved up one element behind the 4 bytes before it (0 for the
+    // first).  The last virtual vector of an H = 7 (mod 8) row would take a
+    // vector ending 2 bytes past the weight ("over"): the 16 bytes that end at
+    // the weight's end are already its virtual vector.
+    auto over_end = [&](int64_t wo) { return kFrame && wo + 16 > wbytes; };
+    auto weight_vec = [&](int64_t wo) { return load_keep_any(wr + (over_end(wo) ? wbytes - 16 : wo)); };
+    auto weight_before = [&](int64_t wo) {
+        const unsigned b = *reinterpret_cast<const u32_any2*>(wr + (wo >= 4 ? wo - 4 : 0));
+        return wo >= 4 ? b : 0u;
     };
-    // ... moved up one element behind the last two elements before it (b: the
-    // 4 bytes before the vector, 0 for the first)
-    auto shift_weight = [](u32x4 w, unsigned b) {
+    auto shift_weight = [&](u32x4 w, unsigned b, bool over) {
         u32x4 r;
         r[0] = __builtin_amdgcn_alignbyte(w[0], b, 2);
         r[1] = __builtin_amdgcn_alignbyte(w[1], w[0], 2);
         r[2] = __builtin_amdgcn_alignbyte(w[2], w[1], 2);
         r[3] = __builtin_amdgcn_alignbyte(w[3], w[2], 2);
-        return r;
-    };
-    auto weight_before = [&](int64_t wo) {
-        return wo == 0 ? 0u : *reinterpret_cast<const u32_any2*>(wr + wo - 4);
+        return over ? w : r;
     };
 
     // Quantised forms hold the weight slice from the start: its own vectors
@@ -649,8 +643,19 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_any_kernel(const RowAr
     if constexpr (QT != 0) {
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
-            wv[k] = weight_vec(woff(k));
-            if constexpr (kFrame) wb[k] = a.frame ? weight_before(woff(k)) : 0u;
+            const int64_t wo = woff(k);
+            if (!over_end(wo)) {
+                wv[k] = load_keep_any(wr + wo);
+            } else {
+                // the weight's vector H / 8 ends 2 bytes past the weight: its
+                // last element (never used) is not read
+                const u32_any2* p = reinterpret_cast<const u32_any2*>(wr + wo);
+                wv[k][0] = p[0];
+                wv[k][1] = p[1];
+                wv[k][2] = p[2];
+                wv[k][3] = *reinterpret_cast<const uint16_t*>(wr + wo + 12);
+            }
+            if constexpr (kFrame) wb[k] = a.frame && wo >= 4 ? *reinterpret_cast<const u32_any2*>(wr + wo - 4) : 0u;
         }
         const int64_t t0 = static_cast<int64_t>(nvec) * V + lane;       // tail element, unshifted row
         const int64_t t1 = static_cast<int64_t>(nvw) * V + lane - 1;    // and in the shifted frame
@@ -704,7 +709,7 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_any_kernel(const RowAr
         float ss = xt * xt;
         float mx = QT != 0 ? fabsf(xt * wt) : 0.f;
         auto qweight = [&](int k) {  // quantised forms: this row's weight vector k
-            if constexpr (QT != 0 && kFrame) return sh ? shift_weight(wv[k], wb[k]) : wv[k];
+            if constexpr (QT != 0 && kFrame) return sh ? shift_weight(wv[k], wb[k], false) : wv[k];
             return wv[k];
         };
 #pragma unroll
@@ -775,7 +780,7 @@ __global__ void __launch_bounds__(max_threads<WPR>()) rms_any_kernel(const RowAr
             // elements before it, moved up one slot in registers (both loads
             // at the weight's alignment)
             const u32x4 wa = weight_vec(voff(k));
-            const u32x4 wk = sh ? shift_weight(wa, weight_before(voff(k))) : wa;
+            const u32x4 wk = sh ? shift_weight(wa, weight_before(voff(k)), over_end(voff(k))) : wa;
             float f[V], fw[V];
             widen(d[k], f, E{});
             widen(wk, fw, E{});

@@ -318,7 +318,8 @@ def test_ln_every_any_alignment_config(dtype):
                 w = inputs.custom(rows, hidden, dtype, layernorm=True)
                 t = inputs.make(w, seed=5000 + n)
                 cnt, g = rows * hidden, 64
-                buf = torch.zeros(2 * (cnt + 2 * g) + 2 * g, dtype=td, device="cuda")
+                # non-zero guard pattern: a stray write of a zero would show
+                buf = torch.full((2 * (cnt + 2 * g) + 2 * g,), 1.0, dtype=td, device="cuda")
                 xb, ob = g + off, g + off + cnt + 2 * g
                 buf[xb:xb + cnt] = t["x"].reshape(-1).cuda()
                 gam, bet = t["weight"].cuda(), t["beta"].cuda()
@@ -338,9 +339,51 @@ def test_ln_every_any_alignment_config(dtype):
                 written = np.zeros(cpu.shape, bool)
                 written[xb:xb + cnt] = True
                 written[ob:ob + cnt] = True
-                assert not np.any(cpu[~written] != 0), "a byte outside the buffers changed"
+                assert np.all(cpu[~written] == inputs.bits(torch.ones(1, dtype=td))[0]), \
+                    "a byte outside the buffers changed"
                 n += 1
     assert n == 70
+
+
+@pytest.mark.parametrize("hidden", [9, 17, 2049, 4095, 4097, 8191])
+def test_ln_any_alignment_offsets(hidden):
+    """bf16 LayerNorm at odd widths through the automatic choice, x and out
+    at several offsets past a 16-byte boundary (the same and different ones
+    modulo 4 bytes), in place, with and without beta: parity with the oracle
+    and a guard pattern that must stay untouched."""
+    import ctypes
+    L = mbr.lib()
+    rows, g = 7, 64
+    cnt = rows * hidden
+    n = 0
+    for xo, oo, inplace in ((1, 1, False), (3, 5, False), (1, 0, False), (2, 6, False), (0, 0, False), (1, 1, True),
+                            (0, 0, True)):
+        bias = n % 2 == 0
+        w = inputs.custom(rows, hidden, "bf16", layernorm=True)
+        t = inputs.make(w, seed=7000 + hidden + n)
+        buf = torch.full((2 * (cnt + 2 * g) + 2 * g,), 1.0, dtype=torch.bfloat16, device="cuda")
+        xb = g + xo
+        ob = xb if inplace else g + oo + cnt + 2 * g
+        buf[xb:xb + cnt] = t["x"].reshape(-1).cuda()
+        gam, bet = t["weight"].cuda(), t["beta"].cuda()
+        say("ln any offsets", hidden, xo, oo, inplace, bias)
+        p = buf.data_ptr()
+        st = L.layernorm_fwd(p + 2 * xb, gam.data_ptr(), bet.data_ptr() if bias else None, p + 2 * ob, rows, hidden,
+                             w.eps, 1, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        assert st == mbr.RMSNORM_OK
+        cfg = mbr.layernorm_select_config(rows, hidden, torch.bfloat16, False)
+        cpu = inputs.bits(buf.cpu())
+        xbits, gbits = inputs.bits(t["x"]), inputs.bits(t["weight"])
+        bbits = inputs.bits(t["beta"]) if bias else None
+        got = cpu[ob:ob + cnt].reshape(rows, hidden)
+        parity.compare_ln(got, parity.oracle_ln(xbits, gbits, bbits, w.eps), xbits, gbits, bbits, w.eps, cfg)
+        written = np.zeros(cpu.shape, bool)
+        written[xb:xb + cnt] = True
+        written[ob:ob + cnt] = True
+        assert np.all(cpu[~written] == inputs.bits(torch.ones(1, dtype=torch.bfloat16))[0]), \
+            "a byte outside the buffers changed"
+        n += 1
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
