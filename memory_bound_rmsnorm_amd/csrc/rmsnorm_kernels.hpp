@@ -11,9 +11,11 @@
 //   rms_vec_kernel      the row lives in VGPRs as packed 16-byte vectors
 //                       (bf16x8 / f32x4); coalesced 16-byte loads and stores.
 //   rms_any_kernel      the same at any element alignment (full vectors plus
-//                       a tail of single elements).
+//                       a tail of single elements; bf16 rows 2 bytes past a
+//                       4-byte boundary move one element earlier, 4-byte
+//                       aligned).
 //   rms_elem_kernel     the row lives in VGPRs as fp32 scalars, one element per
-//                       access: any hidden, any element alignment.
+//                       access: rows narrower than one 16-byte vector.
 //   rms_stage_kernel    rows larger than the register budget of a 1024-lane
 //                       workgroup: part in VGPRs, the rest staged in LDS.
 //   rms_twopass_kernel  rows larger than that, or unaligned wide rows: pass 1
