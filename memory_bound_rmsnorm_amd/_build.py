@@ -119,17 +119,42 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments and trailing blanks: what the compiler
+    sees (string and character literals are kept as they are)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return "\n".join(l.rstrip() for l in "".join(out).splitlines() if l.strip())
+
+
 def source_digest(family: str = "fwd") -> str:
-    """sha256 over one kernel family's device sources, so that counter readings
-    taken on one version of the kernels are not quoted for another.  Host-side
-    selection is checked separately through the launch configuration recorded
-    next to the counters."""
+    """sha256 over one kernel family's device sources, comments left out, so
+    that counter readings taken on one version of the kernels are not quoted
+    for another.  Host-side selection is checked separately through the launch
+    configuration recorded next to the counters."""
     import hashlib
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[family]:
         h.update(name.encode())
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 
