@@ -476,7 +476,8 @@ def _run_any_offsets(rows, hidden, fused, offs, cfg=None, inplace=False, seed=0)
         st = L.rmsnorm_fwd_ex(ptr[0], wt.data_ptr(), ptr[3], rows, hidden, w.eps, 1, cfgp, stream)
     torch.cuda.synchronize()
     assert st == mbr.RMSNORM_OK, mbr.rmsnorm_status_string(st)
-    used = cfg if cfg is not None else mbr.rmsnorm_select_config(rows, hidden, BF16, False, fused)
+    aligned = hidden % 8 == 0 and all(b % 8 == 0 for b in (bases if fused else bases[::3]))
+    used = cfg if cfg is not None else mbr.rmsnorm_select_config(rows, hidden, BF16, aligned, fused)
     cpu = inputs.bits(buf.cpu())
     xb, wb = inputs.bits(t["x"]), inputs.bits(t["weight"])
     h_want, y_want, e, gamma = expect(xb, wb, w.eps, used, inputs.bits(t["residual"]) if fused else None)

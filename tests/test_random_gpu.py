@@ -51,3 +51,33 @@ def test_random_shape(i, kind, dtype, rows, hidden):
     else:
         w = inputs.custom(rows, hidden, dtype, layernorm=True)
         check_ln(w, inputs.make(w, seed=i), bias=i % 3 != 0)
+
+
+def _offset_cases(n=72, seed=20261203):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        hidden = int(rng.integers(8, 9000))
+        rows = int(rng.integers(1, max(2, min(3000, 1_000_000 // hidden))))
+        offs = tuple(int(o) for o in rng.integers(0, 8, 4))
+        if rng.random() < 0.5:  # x, residual, h and out at one offset modulo 4 bytes: the shifted frame applies
+            offs = tuple((offs[0] % 2) + 2 * (o // 2) for o in offs)
+        kind = ["fwd", "fused", "int8", "fp8"][i % 4]
+        out.append((i, kind, rows, hidden, offs, rng.random() < 0.2))
+    return out
+
+
+@pytest.mark.parametrize("i,kind,rows,hidden,offs,inplace", _offset_cases())
+def test_random_offsets(i, kind, rows, hidden, offs, inplace):
+    """bf16 rows of random widths with x, residual, h and out (or the codes)
+    at random element offsets past a 16-byte boundary, through the automatic
+    choice: half of the cases put every row tensor at one offset modulo 4
+    bytes, where rows 2 bytes past a 4-byte boundary take the shifted frame."""
+    from tests.test_parity_gpu import _run_any_offsets
+    from tests.test_quant_gpu import _run_any_quant
+    print("random offsets case", i, kind, rows, hidden, offs, inplace, flush=True)
+    if kind in ("fwd", "fused"):
+        _run_any_offsets(rows, hidden, kind == "fused", offs, inplace=inplace, seed=9000 + i)
+    else:
+        cfg = mbr.rmsnorm_select_quant_config(rows, hidden, torch.bfloat16, False, i % 8 == 2)
+        _run_any_quant("bf16", rows, hidden, i % 8 == 2, QT[kind], cfg, offs[0], offs[3], 9000 + i)
