@@ -18,15 +18,20 @@ Timing protocol: inputs are resident in HBM before the timed region; several
 copies of the input/output set are rotated so that the footprint of a pass
 (>= 2 GiB) exceeds the 256 MB last-level cache and every step reads from HBM;
 W untimed warm-up steps; then exactly K steps between a device synchronise and
-HIP events on the launch stream.  By default the K steps are captured once in
-a HIP graph and replayed once inside the timed region (after an untimed
-replay), the way a serving loop issues them; the same K steps as eager
-launches are timed first and reported as eager_us_per_call.  --eager times the
-eager launches instead.  For the large workloads both give the same per-call
-time once the GPU is warm; the small ones finish faster than Python can issue
-eager launches.  After the timed region the same graph is replayed S more
-times, each replay timed on its own, for the spread of the per-call time
-(median, minimum, 90th percentile).
+HIP events on the launch stream.  A step of at least 128 MiB (the headline;
+the fused, quantised and backward forms at [16384, 8192] or [12289, 5120];
+LayerNorm [8192, 4096]; the wide rows) takes >= 20 us, more than twice as
+long as one call takes to issue (8-12 us), so the K steps are K
+eager calls of the C-ABI entry point through the Python binding, the way a
+caller issues them; before the copy ceiling the same K steps are also captured
+in a HIP graph and timed as one replay, for the record (graph_us_per_call).
+Smaller steps would time the host, so they are captured in a HIP graph
+(before the warm-up, with an untimed upload replay) and replayed once inside
+the timed region, with K eager calls timed before the capture, for the
+record (eager_us_per_call).  --graph and --eager force either.  After the timed
+region, S more batches of K steps are timed one by one (eager batches queued
+back to back, or graph replays), for the spread of the per-call time (median,
+minimum, 90th percentile).
 
 Default run (the headline workload): before the headline's own warm-up the
 other four stated configurations are measured -- fp32 [64, 2048], bf16
@@ -35,16 +40,20 @@ its launches captured in a HIP graph that cycles through enough rotating sets
 to stay HBM-cold, 20 replays timed one by one (median, minimum, p90 per call),
 plus, for those whose bytes fit the cache easily (C1-C3), a cache-resident
 figure with one set reused by every launch (labelled as such, never an HBM
-figure); then the copy ceiling, after 100 ms of copies, and the runtime's own
-device-to-device copy (hipMemcpyAsync) of the same bytes as a second ceiling.
+figure), each after 50 ms of back-to-back replays of its graph; then the
+runtime's own device-to-device copy (hipMemcpyAsync) of the headline's bytes
+as one ceiling; then the headline's graph record; then the copy ceiling (the
+hand-written 16-byte copy kernel on the same bytes, after 100 ms of copies,
+timed the same way as the headline), right before the headline's warm-up.
 The configurations go into the line as per_config; the device (name, arch,
-compute units, torch and HIP versions) as device.  Measured on MI355X, the first ~20 ms of a burst of launches run
-slower than the steady state (bf16 [16384, 8192]: 87.2 us per call after 20
-launches, 84.7 after 300); the ceiling is a steady-state figure, and taking it
-right before the headline means the headline's W warm-up steps also start on
-a GPU at steady clocks.  Parity of every launch configuration timed
-here, at these sizes, with the CPU oracle is the job of the GPU test suite,
-not of this script.
+compute units, torch and HIP versions) as device.  Measured on MI355X, the
+first ~20 ms of a burst of launches after an idle spell (a graph capture, a
+buffer release) run slower than the steady state (bf16 [16384, 8192]: 87.2 us
+per call after 20 launches, 84.7 after 300); the ceilings are steady-state
+figures, and with nothing but the W warm-up steps and a synchronise between
+the copies and the timed steps, the headline's steps run at steady state too.
+Parity of every launch configuration timed here, at these sizes, with the CPU
+oracle is the job of the GPU test suite, not of this script.
 
 CPU baseline: the oracle (as it stands) over a bounded sample of the
 headline's rows, with the rows split over every CPU this process may use
@@ -97,8 +106,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline budget; 0 disables it")
     ap.add_argument("--no-copy", action="store_true", help="skip the copy-ceiling measurement")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--graph", action="store_true",
+                    help="time the K steps as one HIP-graph replay, whatever the step's size")
     ap.add_argument("--eager", action="store_true",
-                    help="time the K steps as eager launches instead of one HIP-graph replay")
+                    help="time the K steps as K eager calls, whatever the step's size")
     return ap.parse_args()
 
 
@@ -259,22 +270,40 @@ def replay_samples(g, launches, samples):
     return [a.elapsed_time(b) / 1e3 / launches for a, b in ev]
 
 
-def time_steps_graph(fn, steps, warmup, spread=0):
-    """Exactly `steps` calls, captured once in a HIP graph and replayed once
-    between a device synchronise and HIP events on the launch stream.  Before
-    that: W eager warm-up calls and one untimed replay, which uploads the
-    graph.  Consecutive calls stay ordered (a captured stream is a chain of
-    dependent nodes); what a replay leaves out is the per-launch host work.
-    After the timed replay, `spread` more replays are timed one by one.
-    Returns (wall seconds, event seconds, per-call seconds of the extra replays)."""
-    for i in range(warmup):
-        fn(i)
+COPY_WARM_SECONDS = 0.1
+GRAPH_WARM_SECONDS = 0.05
+
+
+def capture(fn, steps, first):
+    """fn(first), ..., fn(first + steps - 1) captured once in a HIP graph, then
+    one untimed replay, which uploads it."""
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(steps):
-            fn(warmup + i)
+            fn(first + i)
     g.replay()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_steps_graph(fn, steps, warmup, spread=0, before=None):
+    """Exactly `steps` calls, captured once in a HIP graph and replayed once
+    between a device synchronise and HIP events on the launch stream.  Before
+    that, in this order: one untimed call outside the capture (module load),
+    the capture and its untimed upload replay, `before()` if given, and W eager
+    warm-up calls.  The capture is host work that leaves the GPU idle, so it
+    comes first: between the warm-up and the timed replay there is only a
+    synchronise.  Consecutive calls stay ordered (a captured stream is a chain
+    of dependent nodes); what a replay leaves out is the per-launch host work.
+    After the timed replay, `spread` more replays are timed one by one.
+    Returns (wall seconds, event seconds, per-call seconds of the extra replays)."""
+    fn(0)
+    g = capture(fn, steps, warmup)
+    if before is not None:
+        before()
+    for i in range(warmup):
+        fn(i)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -289,13 +318,19 @@ def time_steps_graph(fn, steps, warmup, spread=0):
     return wall, start.elapsed_time(end) / 1e3, extra
 
 
-def time_steps(fn, steps, warmup):
+def time_steps(fn, steps, warmup, spread=0, before=None):
+    """Exactly `steps` eager calls between a device synchronise and HIP events
+    on the launch stream, after `before()` if given and W warm-up calls.  After
+    the timed region, `spread` more batches of `steps` calls, queued back to
+    back, are timed one by one, each between its own events.
+    Returns (wall seconds, event seconds, per-call seconds of the extra batches)."""
+    if before is not None:
+        before()
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
     for i in range(steps):
@@ -303,24 +338,32 @@ def time_steps(fn, steps, warmup):
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, start.elapsed_time(end) / 1e3, []
+    extra = []
+    if spread > 0:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(spread)]
+        for j, (a, b) in enumerate(ev):
+            a.record(stream)
+            for i in range(steps):
+                fn(warmup + (j + 1) * steps + i)
+            b.record(stream)
+        torch.cuda.synchronize()
+        extra = [a.elapsed_time(b) / 1e3 / steps for a, b in ev]
+    return wall, start.elapsed_time(end) / 1e3, extra
 
 
-def graph_samples(fn, n_sets, samples=20):
+def graph_samples(fn, n_sets, samples=20, warm_s=GRAPH_WARM_SECONDS):
     """Per-launch times with the launches captured once in a HIP graph that
     cycles through every rotation set (at least 64 launches), replayed
-    `samples` times, each replay timed on its own.  The graph removes Python
-    and launch-call overhead from the GPU timeline (the kernels allocate and
-    memset nothing, so they capture cleanly).  Returns (per-call seconds of each
-    replay, launches per replay)."""
+    `samples` times, each replay timed on its own.  Before the timed replays
+    the graph is replayed back to back for `warm_s` seconds (steady state:
+    the capture leaves the GPU idle, and the first ~20 ms of a burst of
+    launches after an idle spell run slower).  The graph removes Python and
+    launch-call overhead from the GPU timeline (the kernels allocate and
+    memset nothing, so they capture cleanly).  Returns (per-call seconds of
+    each replay, launches per replay)."""
     launches = min(4096, max(64, n_sets))
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for i in range(launches):
-            fn(i % n_sets)
-    g.replay()
-    torch.cuda.synchronize()
+    g = capture(fn, launches, 0)
+    warm_for(lambda i: g.replay(), warm_s, batch=4)
     per = replay_samples(g, launches, samples)
     del g
     return per, launches
@@ -332,14 +375,14 @@ def graph_time(fn, n_sets, replays=10):
     return statistics.median(per)
 
 
-def warm_for(fn, seconds):
-    """Launch fn in batches of 16 until `seconds` of wall time have passed,
-    synchronising after each batch; returns the number of launches."""
+def warm_for(fn, seconds, batch=16):
+    """Launch fn in batches of `batch` until `seconds` of wall time have
+    passed, synchronising after each batch; returns the number of launches."""
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     i = 0
     while True:
-        for _ in range(16):
+        for _ in range(batch):
             fn(i)
             i += 1
         torch.cuda.synchronize()
@@ -347,25 +390,35 @@ def warm_for(fn, seconds):
             return i
 
 
-COPY_WARM_SECONDS = 0.1
-
-
-def copy_ceiling(w, steps, warmup, graph=False):
+class CopyCeiling:
     """hbm_copy of the same read/write byte count as one step, rotated the same
     way and timed the same way (eager launches or one graph replay), after
-    100 ms of copies: on MI355X the first ~20 ms of a burst of launches run
-    slower than the steady state, and the ceiling is a steady-state figure."""
-    nbytes = w.copy_bytes
-    n = max(2, -(-MIN_FOOTPRINT // (2 * nbytes)))
-    src = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(i % 251) for i in range(n)]
-    dst = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(n)]
-    timer = time_steps_graph if graph else time_steps
-    copy = lambda i: mbr.hbm_copy(src[i % n], dst[i % n])  # noqa: E731
-    warm_for(copy, COPY_WARM_SECONDS)
-    wall, ev, _ = timer(copy, steps, warmup)
-    del src, dst
-    torch.cuda.empty_cache()
-    return 2 * nbytes / (ev / steps) / 1e9
+    100 ms of copies: the ceiling is a steady-state figure.  The buffers live
+    until free(), so that no deallocation idles the GPU between this and the
+    headline steps that follow it."""
+
+    def __init__(self, w):
+        self.nbytes = w.copy_bytes
+        self.n = max(2, -(-MIN_FOOTPRINT // (2 * self.nbytes)))
+        self.src = [torch.empty(self.nbytes, dtype=torch.uint8, device="cuda").fill_(i % 251) for i in range(self.n)]
+        self.dst = [torch.empty(self.nbytes, dtype=torch.uint8, device="cuda") for _ in range(self.n)]
+
+    def launch(self, i):
+        mbr.hbm_copy(self.src[i % self.n], self.dst[i % self.n])
+
+    def measure(self, steps, warmup, graph=False):
+        def warm():
+            warm_for(self.launch, COPY_WARM_SECONDS)
+        if graph:
+            _, ev, _ = time_steps_graph(self.launch, steps, warmup, before=warm)
+        else:
+            warm()
+            _, ev, _ = time_steps(self.launch, steps, warmup)
+        return 2 * self.nbytes / (ev / steps) / 1e9
+
+    def free(self):
+        self.src, self.dst = [], []
+        torch.cuda.empty_cache()
 
 
 def memcpy_ceiling(w, steps, warmup):
@@ -537,21 +590,52 @@ def setup_workload(w, seed):
                                            "backward": w.backward}
 
 
+# Steps of at least this many algorithmic bytes take >= 20 us even at 6.4 TB/s,
+# more than twice what the Python binding and the C ABI need to issue one call
+# (8-12 us measured on the GPU machine), so K eager calls keep the GPU busy from the
+# first to the last and are timed as such; smaller steps would time the host,
+# so they are captured in a HIP graph and replayed.
+EAGER_MIN_BYTES = 128 << 20
+
+
+def timed_as_graph(w, args) -> bool:
+    if args.graph or args.eager:
+        return bool(args.graph)
+    return w.algorithmic_bytes < EAGER_MIN_BYTES
+
+
 def bench_workload(w, steps, warmup, seed, with_copy=True, graph=False, timed_graph=False, spread=0):
     t, sets, n_sets, shape = setup_workload(w, seed)
     nbytes = w.algorithmic_bytes
     rec = dict({"workload": w.name, "dtype": w.dtype}, **shape)
+    copy = None
     if with_copy:
-        # the copy ceiling first: the same read/write byte count, rotated and timed the same way
-        rec["copy_ceiling_gbps"] = copy_ceiling(w, max(20, steps // 2), max(2, warmup // 2), graph=timed_graph)
         rec["memcpy_ceiling_gbps"] = memcpy_ceiling(w, max(20, steps // 2), max(2, warmup // 2))
+        copy = CopyCeiling(w)
+
+    def ceiling():
+        rec["copy_ceiling_gbps"] = copy.measure(max(20, steps // 2), max(2, warmup // 2), graph=timed_graph)
+    before = ceiling if copy is not None else None
+    sets.launch(0)  # first launch: module load
     if timed_graph:
-        # eager launches first, for the record; the timed steps are a graph replay
-        _, ev_e, _ = time_steps(sets.launch, steps, warmup)
-        rec["eager_us_per_call"] = ev_e / steps * 1e6
-        rec["eager_gbps"] = nbytes / (ev_e / steps) / 1e9
-    wall, ev, extra = (time_steps_graph(sets.launch, steps, warmup, spread) if timed_graph
-                       else time_steps(sets.launch, steps, warmup))
+        # the eager record first; the graph is captured before the copy
+        # ceiling, which runs right before the headline's warm-up
+        _, ev2, _ = time_steps(sets.launch, steps, warmup)
+        rec["eager_us_per_call"] = ev2 / steps * 1e6
+        rec["eager_gbps"] = nbytes / (ev2 / steps) / 1e9
+        wall, ev, extra = time_steps_graph(sets.launch, steps, warmup, spread, before=before)
+    else:
+        # the same K steps as one graph replay first, for the record (after
+        # 50 ms of replays: the capture idles the GPU); then the copy ceiling,
+        # then the headline's warm-up and timed steps with nothing between
+        # them but a synchronise
+        _, ev2, _ = time_steps_graph(sets.launch, steps, warmup,
+                                     before=lambda: warm_for(sets.launch, GRAPH_WARM_SECONDS))
+        rec["graph_us_per_call"] = ev2 / steps * 1e6
+        rec["graph_gbps"] = nbytes / (ev2 / steps) / 1e9
+        wall, ev, extra = time_steps(sets.launch, steps, warmup, spread, before=before)
+    if copy is not None:
+        copy.free()
     kern_s = ev / steps
     rec.update({
         "timing": "graph" if timed_graph else "eager",
@@ -587,17 +671,18 @@ def measure_config(w, seed, samples=20):
     """One stated configuration, HBM-cold: its launches captured in a HIP graph
     that cycles through the rotating sets, `samples` replays timed one by one;
     per-call median, minimum and p90, and GB/s and roofline fraction at the
-    median."""
+    median.  A cache-resident figure, where there is one, is taken first, so
+    that the HBM-cold replays are the configuration's last dispatches."""
     t, sets, n_sets, shape = setup_workload(w, seed)
     for i in range(2 * n_sets):  # first launches: module load, clocks
         sets.launch(i)
-    per, launches = graph_samples(sets.launch, n_sets, samples)
     warm = None
     if w.algorithmic_bytes <= CACHE_RESIDENT_MAX:
         # the same buffers every launch: cache-resident, not an HBM figure
         wper, wl = graph_samples(lambda i: sets.launch(0), 1, samples)
         warm = {"us_median": round(statistics.median(wper) * 1e6, 3), "launches_per_sample": wl,
                 "note": "one input/output set reused by every launch: cache-resident, not HBM bandwidth"}
+    per, launches = graph_samples(sets.launch, n_sets, samples)
     del sets, t
     torch.cuda.empty_cache()
     med = statistics.median(per)
@@ -660,8 +745,8 @@ def main():
                 continue
             per_config[label] = measure_config(inputs.WORKLOADS[name], args.seed)
             log("# %s:" % label, json.dumps(per_config[label]))
-    t, rec = bench_workload(w, args.steps, args.warmup, args.seed, not args.no_copy, timed_graph=not args.eager,
-                            spread=0 if args.eager else args.spread)
+    t, rec = bench_workload(w, args.steps, args.warmup, args.seed, not args.no_copy,
+                            timed_graph=timed_as_graph(w, args), spread=args.spread)
     log("# timed:", json.dumps(rec))
 
     achieved = rec["gbps_kernel"]
@@ -689,14 +774,20 @@ def main():
                      "traffic": load_traffic(w, rec["kernel_config"])},
         "parity": "checked against the CPU oracle at this size and launch configuration by " + parity,
         "timing": ("the K steps captured in one HIP graph and replayed once between synchronisations"
-                   if rec["timing"] == "graph" else "K eager launches between synchronisations"),
+                   if rec["timing"] == "graph" else
+                   "K eager calls of the C-ABI entry point (through the Python binding) between synchronisations"),
     }
     if "spread" in rec:
-        line["spread"] = dict(rec["spread"], note="the same K-step graph replayed again, each replay timed on its "
-                                                  "own with HIP events")
+        line["spread"] = dict(rec["spread"], note=(
+            "the same K-step graph replayed again, each replay timed on its own with HIP events"
+            if rec["timing"] == "graph" else
+            "more batches of K eager calls, queued back to back, each batch timed on its own with HIP events"))
     if "eager_us_per_call" in rec:
         line["eager_us_per_call"] = round(rec["eager_us_per_call"], 3)
         line["eager_gbps"] = round(rec["eager_gbps"], 2)
+    if "graph_us_per_call" in rec:
+        line["graph_us_per_call"] = round(rec["graph_us_per_call"], 3)
+        line["graph_gbps"] = round(rec["graph_gbps"], 2)
     if "copy_ceiling_gbps" in rec:
         line["copy_ceiling_gbps"] = round(rec["copy_ceiling_gbps"], 2)
         line["frac_of_copy_ceiling"] = round(rec["frac_of_copy_ceiling"], 4)
@@ -711,7 +802,8 @@ def main():
         for name, other in inputs.EVERY_WORKLOAD.items():
             if name == w.name:
                 continue
-            _, r = bench_workload(other, args.steps, args.warmup, args.seed, graph=True)
+            _, r = bench_workload(other, args.steps, args.warmup, args.seed, graph=True,
+                                  timed_graph=timed_as_graph(other, args))
             log("# workload:", json.dumps(r))
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(w, t, args.cpu_seconds)

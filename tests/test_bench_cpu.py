@@ -68,3 +68,18 @@ def test_spread_statistics():
 def test_stated_configurations_are_the_five_workloads():
     assert set(bench.STATED.values()) == set(inputs.WORKLOADS) - {"bf16_shard_2048x8192"}
     assert bench.STATED["C4"] == inputs.HEADLINE
+
+
+def test_timing_method_follows_the_step_size():
+    """K eager calls for steps of >= 128 MiB (the headline among them), one
+    graph replay for smaller ones; --graph and --eager force either."""
+    from types import SimpleNamespace as NS
+    plain = NS(graph=False, eager=False)
+    w = inputs.EVERY_WORKLOAD
+    assert not bench.timed_as_graph(w[inputs.HEADLINE], plain)
+    assert not bench.timed_as_graph(w["bf16_residual_12289x5120"], plain)
+    assert not bench.timed_as_graph(w["bf16_ln_8192x4096"], plain)
+    assert bench.timed_as_graph(w["bf16_prefill_4096x2048"], plain)
+    assert bench.timed_as_graph(w["bf16_kv_prefill_4x4096_576"], plain)
+    assert bench.timed_as_graph(w[inputs.HEADLINE], NS(graph=True, eager=False))
+    assert not bench.timed_as_graph(w["fp32_64x2048"], NS(graph=False, eager=True))
