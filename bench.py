@@ -59,7 +59,10 @@ CPU baseline: the oracle (as it stands) over a bounded sample of the
 headline's rows, with the rows split over every CPU this process may use
 (its affinity mask capped by its cgroup CPU quota) and again on one thread;
 one warm-up pass, then timed runs of at least a second each, the median
-reported.
+reported.  One more, untimed, pass of the oracle over the sample is set
+beside the GPU's output for the same rows in the timed launch configuration
+(cpu_baseline.oracle_vs_gpu: ulp histogram, bitwise-equal fraction, largest
+errors); a report only, since the GPU test suite is the parity gate.
 
 Prints ONE JSON line on stdout.  With --all, one JSON record per other
 workload is written to stderr (lines starting with '#'); those also carry the
@@ -539,6 +542,61 @@ def cpu_baseline_kv(w, t, seconds):
     return _cpu_record(one_pass, sample_bytes, seconds, "first %d of %d tokens" % (tokens, w.tokens))
 
 
+def sample_rows(w) -> int:
+    """Rows of the CPU baseline's bounded sample: about 64 MiB of algorithmic bytes."""
+    return max(1, min(w.rows, (64 << 20) * w.rows // w.algorithmic_bytes))
+
+
+def gpu_sample(w, sets):
+    """The timed launch configuration's outputs for the sample rows of
+    rotation set 0 (whose inputs are the host tensors), as host arrays."""
+    if is_kv(w):
+        return None
+    rows = sample_rows(w)
+    s = sets.sets[0]
+    torch.cuda.synchronize()
+    if w.backward:
+        return {"dx": inputs.bits(s["dx"][:rows])}
+    if w.quant:
+        d = {"q": s["q"][:rows].cpu().numpy(), "scale": s["scale"][:rows].cpu().numpy()}
+        if w.fused:
+            d["h"] = inputs.bits(s["h"][:rows])
+        return d
+    d = {"y": inputs.bits(s["out"][:rows])}
+    if w.fused:
+        d["h"] = inputs.bits(s["h"][:rows])
+    return d
+
+
+def _agreement(gpu, ref, kind):
+    """How the GPU's sample outputs compare with the oracle's: bf16 distance
+    on the monotone line of bit patterns (+0 = -0), fp32 relative error,
+    codes by count of differing codes."""
+    import numpy as np
+    n = int(ref.size)
+    if kind == "codes":
+        diff = np.ascontiguousarray(gpu).view(np.uint8).reshape(-1) != np.ascontiguousarray(ref).view(np.uint8).reshape(-1)
+        return {"n": n, "n_differing": int(diff.sum())}
+    if kind == "scale":
+        rel = np.abs(gpu.astype(np.float64) - ref) / np.maximum(np.abs(ref.astype(np.float64)), 1e-300)
+        return {"n": n, "max_rel_err": float(rel.max()) if n else 0.0}
+    if kind == "bf16":
+        def mono(p):
+            p = p.astype(np.int32)
+            return np.where(p & 0x8000, -(p & 0x7FFF), p)
+        d = np.abs(mono(gpu) - mono(ref)).reshape(-1)
+        gf = (gpu.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        rf = (ref.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        return {"n": n, "max_ulp": int(d.max()) if n else 0, "frac_bitwise_equal": float((d == 0).mean()) if n else 1.0,
+                "ulp_histogram": {"0": int((d == 0).sum()), "1": int((d == 1).sum()), ">1": int((d > 1).sum())},
+                "max_abs_err": float(np.abs(gf - rf).max()) if n else 0.0}
+    g, r = gpu.astype(np.float64).reshape(-1), ref.astype(np.float64).reshape(-1)
+    rel = np.abs(g - r) / np.maximum(np.abs(r), 1e-300)
+    return {"n": n, "max_rel_err": float(rel.max()) if n else 0.0,
+            "frac_bitwise_equal": float((gpu.reshape(-1) == ref.reshape(-1)).mean()) if n else 1.0,
+            "max_abs_err": float(np.abs(g - r).max()) if n else 0.0}
+
+
 def cpu_baseline(w, t, seconds):
     """The oracle, as it stands, over a bounded sample of the workload's rows
     (about 64 MiB of algorithmic bytes), rows split across the host's threads;
@@ -546,7 +604,7 @@ def cpu_baseline(w, t, seconds):
     if is_kv(w):
         return cpu_baseline_kv(w, t, seconds)
     import oracle  # the CPU checker; timed here as a reported baseline only
-    rows = max(1, min(w.rows, (64 << 20) * w.rows // w.algorithmic_bytes))
+    rows = sample_rows(w)
     xb = inputs.bits(t["x"])[:rows]
     wb = inputs.bits(t["weight"])
     rb = inputs.bits(t["residual"])[:rows] if w.fused else None
@@ -574,7 +632,36 @@ def cpu_baseline(w, t, seconds):
 
     sample_bytes = inputs.Workload(w.name, w.dtype, rows, w.hidden, w.eps, w.fused, w.x, w.weight, w.residual,
                                    quant=w.quant, grad=w.grad, beta=w.beta).algorithmic_bytes
-    return _cpu_record(one_pass, sample_bytes, seconds, "first %d of %d rows" % (rows, w.rows))
+    rec = _cpu_record(one_pass, sample_bytes, seconds, "first %d of %d rows" % (rows, w.rows))
+    gpu = t.get("gpu_sample")
+    if gpu is not None:
+        # one more (untimed) pass of the oracle over the sample, set beside
+        # the GPU's output of the same rows in the timed launch configuration
+        kind = w.dtype
+        if w.backward:
+            dx, _ = oracle.rmsnorm_bwd(xb, wb, gb, w.eps, want_dw=False)
+            outs = {"dx": _agreement(gpu["dx"], dx, kind)}
+        elif w.layernorm:
+            outs = {"y": _agreement(gpu["y"], oracle.layernorm_fwd(xb, wb, bb, w.eps), kind)}
+        elif qt is not None:
+            h, q, sc = oracle.rmsnorm_dynamic_quant_fwd(xb, wb, w.eps, qt, residual=rb if w.fused else None)
+            outs = {"codes": _agreement(gpu["q"], q, "codes"), "scale": _agreement(gpu["scale"], sc, "scale")}
+            if w.fused:
+                outs["h"] = _agreement(gpu["h"], h, kind)
+        elif w.fused:
+            h, y = oracle.rmsnorm_residual_fwd(xb, rb, wb, w.eps)
+            outs = {"h": _agreement(gpu["h"], h, kind), "y": _agreement(gpu["y"], y, kind)}
+        else:
+            outs = {"y": _agreement(gpu["y"], oracle.rmsnorm_fwd(xb, wb, w.eps), kind)}
+        note = ("the oracle's output for the sample rows against the GPU's output for the same rows of rotation "
+                "set 0 in the timed launch configuration; a report: the GPU test suite is the parity gate")
+        if qt is not None:
+            note += " (it checks that every differing code sits at a rounding tie)"
+        elif w.backward or w.layernorm:
+            note += (" (these outputs cancel: their bound is on magnitude, so an output near zero may lie several "
+                     "ulps from the oracle's and still be within it)")
+        rec["oracle_vs_gpu"] = dict(outs, rows=rows, note=note)
+    return rec
 
 
 def setup_workload(w, seed):
@@ -653,6 +740,7 @@ def bench_workload(w, steps, warmup, seed, with_copy=True, graph=False, timed_gr
     if with_copy:
         rec["frac_of_copy_ceiling"] = rec["gbps_kernel"] / rec["copy_ceiling_gbps"]
         rec["frac_of_memcpy_ceiling"] = rec["gbps_kernel"] / rec["memcpy_ceiling_gbps"]
+    t["gpu_sample"] = gpu_sample(w, sets)
     del sets
     torch.cuda.empty_cache()
     return t, rec

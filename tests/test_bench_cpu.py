@@ -83,3 +83,32 @@ def test_timing_method_follows_the_step_size():
     assert bench.timed_as_graph(w["bf16_kv_prefill_4x4096_576"], plain)
     assert bench.timed_as_graph(w[inputs.HEADLINE], NS(graph=True, eager=False))
     assert not bench.timed_as_graph(w["fp32_64x2048"], NS(graph=False, eager=True))
+
+
+def test_agreement_report():
+    import numpy as np
+    a = np.array([0x3F80, 0x3F81, 0xBF80, 0x8000, 0x0000], np.uint16)
+    b = np.array([0x3F80, 0x3F80, 0xBF81, 0x0000, 0x0001], np.uint16)
+    r = bench._agreement(a, b, "bf16")
+    assert r["max_ulp"] == 1 and r["ulp_histogram"] == {"0": 2, "1": 3, ">1": 0}
+    assert bench._agreement(np.array([1, 255], np.uint8), np.array([1, -1], np.int8), "codes")["n_differing"] == 0
+    assert bench._agreement(np.array([1, 254], np.uint8), np.array([1, -1], np.int8), "codes")["n_differing"] == 1
+
+
+def test_cpu_baseline_sets_the_oracle_beside_the_gpu_sample():
+    """The CPU-baseline leg compares its oracle output with the sample the
+    bench took from the GPU; here the 'GPU' sample is the oracle's own output
+    with one element moved by one ulp."""
+    import oracle
+    w = inputs.custom(64, 512, "bf16", True)
+    t = inputs.make(w, seed=0)
+    rows = bench.sample_rows(w)
+    xb, rb, wb = (inputs.bits(t[k]) for k in ("x", "residual", "weight"))
+    h, y = oracle.rmsnorm_residual_fwd(xb[:rows], rb[:rows], wb, w.eps)
+    y = y.copy()
+    y[3, 7] += 1
+    t["gpu_sample"] = {"h": h, "y": y}
+    rec = bench.cpu_baseline(w, t, 0.4)
+    agree = rec["oracle_vs_gpu"]
+    assert agree["rows"] == rows and agree["h"]["max_ulp"] == 0
+    assert agree["y"]["max_ulp"] == 1 and agree["y"]["ulp_histogram"]["1"] == 1
