@@ -2,6 +2,8 @@
 widths (whole 16-byte vectors or not), dtypes and forms drawn from one fixed
 generator, each compared with the oracle under the same bounds as the
 dedicated suites.  A wide net over the launch-configuration rules."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -15,6 +17,11 @@ from tests.test_parity_gpu import check_workload
 from tests.test_quant_gpu import QT, check as check_quant
 
 pytestmark = pytest.mark.gpu
+
+# A wider net on demand: RMSNORM_RANDOM_CASES=N (shape cases; a third as many
+# offset cases) and RMSNORM_RANDOM_SEED=S replace the defaults below.
+_N = int(os.environ.get("RMSNORM_RANDOM_CASES", "0"))
+_SEED = int(os.environ.get("RMSNORM_RANDOM_SEED", "0"))
 
 
 def _cases(n=240, seed=20261202):
@@ -36,7 +43,7 @@ def _cases(n=240, seed=20261202):
     return out
 
 
-@pytest.mark.parametrize("i,kind,dtype,rows,hidden", _cases())
+@pytest.mark.parametrize("i,kind,dtype,rows,hidden", _cases(_N or 240, _SEED or 20261202))
 def test_random_shape(i, kind, dtype, rows, hidden):
     print("random case", i, kind, dtype, rows, hidden, flush=True)
     if kind in ("fwd", "fused"):
@@ -67,7 +74,8 @@ def _offset_cases(n=72, seed=20261203):
     return out
 
 
-@pytest.mark.parametrize("i,kind,rows,hidden,offs,inplace", _offset_cases())
+@pytest.mark.parametrize("i,kind,rows,hidden,offs,inplace",
+                         _offset_cases(_N // 3 or 72, _SEED + 1 if _SEED else 20261203))
 def test_random_offsets(i, kind, rows, hidden, offs, inplace):
     """bf16 rows of random widths with x, residual, h and out (or the codes)
     at random element offsets past a 16-byte boundary, through the automatic
