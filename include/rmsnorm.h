@@ -22,9 +22,13 @@
  *     scratch memory, which the caller passes in as a workspace (or, with
  *     rmsnorm_bwd_noalloc, the library's fixed per-GPU scratch array).
  *   - Tensors are contiguous and row-major; weight is [hidden]; all tensors
- *     share one dtype.  Any element-aligned address is accepted; 16-byte
- *     vector accesses are used only when every pointer is 16-byte aligned and
- *     hidden * dtype_size is a multiple of 16.
+ *     share one dtype.  Any element-aligned address is accepted.  With every
+ *     pointer 16-byte aligned and hidden * dtype_size a multiple of 16, rows
+ *     move as aligned 16-byte vectors; otherwise a row of at least one vector
+ *     moves as 16-byte vectors at its own alignment plus its last few
+ *     elements one by one (see RMSNORM_PATH_VECTOR_ANY for the one read
+ *     outside a row: two bytes in the same 4-byte word as its first element),
+ *     and a narrower row one element per access.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
  *     work and return without synchronising; results are ready when the stream
  *     reaches that point.
