@@ -17,11 +17,14 @@ fallback -- if the library is not built, every call raises.
     rmsnorm_bwd_ex(..., config)                                forced launch configuration
     rmsnorm_bwd_workspace_size(rows, hidden, dtype, config)    -> bytes
     rmsnorm_select_bwd_config(rows, hidden, dtype, vector_aligned) -> Config
+    rmsnorm_bwd_noalloc(x, weight, dy, dx, dweight, eps)       -> (dx, dweight), no workspace (fixed per-GPU scratch)
     layernorm_fwd(x, gamma, beta, out, eps)                    -> out (beta may be None)
     layernorm_fwd_ex(..., config)                              forced launch configuration
     layernorm_select_config(rows, hidden, dtype, vector_aligned) -> Config
     kv_rmsnorm_rope_cache(kv, gamma, cos, sin, positions, slots, norm_cache, rope_cache, eps, rope_style)
+    kv_rmsnorm_rope_cache_ex(..., config), kv_select_config(...) forced / reported configuration
     rmsnorm_status_string(status)                              -> str
+    hbm_copy(src, dst)                                         16-byte copy (libhbm_copy.so), the bandwidth ceiling
 
 The backward's weight gradient needs a workspace; when none is passed, a
 torch byte tensor of the queried size is allocated for the call (device
