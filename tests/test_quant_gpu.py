@@ -343,3 +343,41 @@ def test_odd_widths_automatic_quant(hidden, fused, q):
     assert cfg.path == mbr.PATH_VECTOR_ANY
     say("quant odd width", q, hidden, fused, cfg.as_dict())
     _run_any_quant("bf16", 2048 if hidden > 5000 else 4096, hidden, fused, QT[q], cfg, 1, 5, hidden)
+
+
+@pytest.mark.parametrize("qname", ["int8", "fp8"])
+def test_quant_graph_capture_replays_match_eager(qname):
+    """The fused quantised form (and a plain odd-width call on the
+    any-alignment path) captured in one HIP graph: every replay, with eager
+    work and synchronisations in between, equals the eager results bitwise."""
+    qt = QT[qname]
+    w = inputs.custom(3000, 5120, "bf16", True)
+    t = {k: v.cuda() for k, v in inputs.make(w, seed=31).items()}
+    w2 = inputs.custom(777, 4097, "bf16", False)
+    t2 = {k: v.cuda() for k, v in inputs.make(w2, seed=32).items()}
+
+    def outputs():
+        return (torch.empty_like(t["x"]), torch.empty(t["x"].shape, dtype=torch.uint8, device="cuda"),
+                torch.empty(t["x"].shape[0], dtype=torch.float32, device="cuda"),
+                torch.empty(t2["x"].shape, dtype=torch.uint8, device="cuda"),
+                torch.empty(t2["x"].shape[0], dtype=torch.float32, device="cuda"))
+
+    def call(o):
+        mbr.rmsnorm_dynamic_quant_fwd(t["x"], t["weight"], o[1], o[2], 1e-5, qt, t["residual"], o[0])
+        mbr.rmsnorm_dynamic_quant_fwd(t2["x"], t2["weight"], o[3], o[4], 1e-5, qt)
+
+    eager = outputs()
+    call(eager)
+    graphed = outputs()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(graphed)
+    for rep in range(3):
+        for o in graphed:
+            o.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(eager, graphed):
+            assert torch.equal(a, b), "replay %d differs" % rep
+        call(outputs())  # eager work between replays
