@@ -808,6 +808,7 @@ def describe(w):
     parity = ("tests/test_bwd_gpu.py::test_bwd_workloads_full_size" if w.backward else
               "tests/test_ln_gpu.py::test_ln_workloads_full_size" if w.layernorm else
               "tests/test_quant_gpu.py" if w.quant else
+              "tests/test_parity_gpu.py::test_shape_workloads_full_size" if w.name in inputs.SHAPE_WORKLOADS else
               "tests/test_parity_gpu.py::test_stated_workloads_full_size")
     return metric, desc, fields, parity
 

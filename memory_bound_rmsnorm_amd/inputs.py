@@ -176,8 +176,21 @@ WIDE_WORKLOADS: Dict[str, Workload] = {
                  note="fused rows past the register budget"),
     ]
 }
+# Two shapes that exercise the forward's other launch forms at full scale:
+# per-head rows narrower than a wave (several rows share a wave in lane
+# groups), and an odd width (16-byte vectors at the row's own alignment, every
+# other row in the shifted frame, plus a tail element).
+SHAPE_WORKLOADS: Dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("bf16_narrow_262144x128", "bf16", 262144, 128, 1e-5, False, N01, W_N,
+                 note="per-head width: rows narrower than a wave"),
+        Workload("bf16_odd_16384x8191", "bf16", 16384, 8191, 1e-5, False, N01, W_N,
+                 note="odd width: rows at any element alignment, tail element"),
+    ]
+}
 ALL_WORKLOADS: Dict[str, Workload] = dict(WORKLOADS, **QUANT_WORKLOADS, **BWD_WORKLOADS, **LN_WORKLOADS,
-                                          **WIDE_WORKLOADS)
+                                          **WIDE_WORKLOADS, **SHAPE_WORKLOADS)
 
 
 def _draw(rng: np.random.Generator, d: Dist, shape) -> np.ndarray:

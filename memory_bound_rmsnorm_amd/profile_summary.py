@@ -86,6 +86,13 @@ def kernel_instances(w):
                                              ("int", qt), ("int", lpr)])]
     if path == 2:
         return [_instance("rms_elem_kernel", [e, ("int", wpr), ("int", per), ("bool", w.fused), ("int", qt)])]
+    if path == 4:
+        # any alignment; bf16 rows of an odd width on aligned buffers take the
+        # shifted frame when the launch covers one more element, which always
+        # launches the masked kernel
+        frame = w.dtype == "bf16" and w.hidden % 2 != 0 and lanes * per >= (w.hidden + 1) // v
+        return [_instance("rms_any_kernel", [e, ("int", wpr), ("int", per), ("bool", frame or lanes * per != units),
+                                             ("bool", w.fused), ("int", qt)])]
     if path == 5:  # rms_stage_kernel<E, RV, CH, FUSED>, CH as rmsnorm_misc.hip instantiates it
         ch = {(False, 10): 10, (True, 6): 5, (True, 7): 4}[(w.fused, per)]
         return [_instance("rms_stage_kernel", [e, ("int", per), ("int", ch), ("bool", w.fused)])]

@@ -95,6 +95,15 @@ def test_stated_workloads_full_size(name):
     say(name, stats)
 
 
+@pytest.mark.parametrize("name", list(inputs.SHAPE_WORKLOADS))
+def test_shape_workloads_full_size(name):
+    """The narrow-row and odd-width shapes bench.py also times."""
+    w = inputs.SHAPE_WORKLOADS[name]
+    say("workload", name, "seed 0", "config", mbr.rmsnorm_select_config(w.rows, w.hidden, tdtype(w), True, w.fused))
+    stats = check_workload(w, inputs.make(w, seed=0))
+    say(name, stats)
+
+
 @pytest.mark.parametrize("name", ["bf16_prefill_4096x2048", "bf16_residual_12289x5120"])
 @pytest.mark.parametrize("seed", [1, 2])
 def test_stated_workloads_other_seeds(name, seed):
