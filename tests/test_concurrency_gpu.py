@@ -86,3 +86,14 @@ def test_threads_on_separate_streams_match_serial_calls_bitwise():
         for rep, o in enumerate(outs):
             for a, b in zip(w, o):
                 assert torch.equal(a, b), "job %d (%s), repetition %d differs" % (j, jobs[j].__name__, rep)
+
+
+def test_calls_go_to_the_callers_current_stream():
+    """The binding passes the caller's current stream: the default stream, or
+    the one a `torch.cuda.stream` context selects, in this thread."""
+    x = torch.zeros(1, device="cuda")
+    assert mbr._stream(None, x.device) == torch.cuda.current_stream().cuda_stream
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        assert mbr._stream(None, x.device) == s.cuda_stream
+    assert mbr._stream(s, x.device) == s.cuda_stream
